@@ -1,0 +1,239 @@
+"""Benchmark of the fused RNN-T joint + transducer loss (forward + backward).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload short]
+                    [--tile-t T --tile-u U --tile-v V] [--no-cpu-baseline]
+
+One step = one forward + one backward over a whole synthetic batch (every
+kernel of the path: validation, W_out transpose, fused joint + projection +
+online log-sum-exp, lattice recursions, logit gradients, the dh and dW GEMMs
+and the lattice reductions), with the inputs already resident in HBM and all
+output / state buffers allocated once before timing.  The line printed is
+
+    value = B*T*U lattice cells of the workload per second (padded maxima,
+            the metric's definition), whole job, one GPU.
+
+`roofline` describes the kernel with the largest share of step time: its
+algorithmic flops (2*H*V per valid lattice cell for each MFMA pass) or bytes
+per launch over its mean launch duration, measured with HIP events that the
+library records on the launch stream around each of its kernels.
+`cpu_baseline` times the float64 oracle on a bounded sample of the same
+workload on the host cores and scales it to the same unit.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "lattice cells/sec (B·T·U) fused joint+loss fwd+bwd"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
+PEAK_HBM_GBS = 8000.0
+MFMA_KERNELS = ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
+DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (64, 64, 128),
+                 "medium_lv": (64, 64, 128), "long": (64, 64, 128)}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="short",
+                    choices=["tiny", "short", "medium", "medium_lv", "long"])
+    ap.add_argument("--tile-t", type=int, default=None)
+    ap.add_argument("--tile-u", type=int, default=None)
+    ap.add_argument("--tile-v", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def cpu_baseline(inp, target_s):
+    """Float64 oracle (fwd+bwd, one utterance at a time, NumPy BLAS on all host
+    threads) on a bounded sample of the workload: whole utterances in order
+    until about target_s seconds are spent, or the first utterance cut to its
+    first t_s frames when even one utterance would take longer (t_s from a
+    4-frame pilot).  Scaled to B*T*U cells/s of the whole workload by the
+    ratio of valid lattice cells."""
+    import numpy as np
+    from oracle import rnnt
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+
+    def run(b, t_s):
+        t0 = time.perf_counter()
+        rnnt.utterance_loss_and_grads(inp.enc_f64[b, :t_s], inp.pred_f64[b], inp.W_f64,
+                                      inp.b_f64, inp.labels[b], t_s, int(inp.U_lens[b]),
+                                      inp.blank)
+        return time.perf_counter() - t0
+
+    Tl0, Ul0 = int(inp.T_lens[0]), int(inp.U_lens[0])
+    pilot_t = min(Tl0, 4)
+    pt = run(0, pilot_t)
+    if pt * Tl0 / pilot_t > target_s:
+        t_s = int(min(Tl0, max(pilot_t, round(pilot_t * target_s / max(pt, 1e-6)))))
+        el = run(0, t_s)
+        sample_cells = t_s * (Ul0 + 1)
+        desc = f"utterance 0 (T'={Tl0}, U'={Ul0}) cut to its first {t_s} frames"
+    else:
+        el, sample_cells, nb = 0.0, 0, 0
+        for b in range(inp.B):
+            el += run(b, int(inp.T_lens[b]))
+            sample_cells += int(inp.T_lens[b]) * (int(inp.U_lens[b]) + 1)
+            nb += 1
+            if el >= target_s:
+                break
+        desc = f"utterances 0..{nb - 1} of {inp.B} in full"
+    total_valid = int(np.sum(inp.T_lens.astype(np.int64) * (inp.U_lens.astype(np.int64) + 1)))
+    full_time = el * total_valid / sample_cells
+    value = inp.B * inp.T * inp.U / full_time
+    return {"value": value, "unit": "cells/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{desc}: {sample_cells} valid cells in {el:.2f} s, float64 NumPy "
+                      f"fwd+bwd, scaled by valid cells ({total_valid}) to the B*T*U metric"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the path shards over utterances across GPUs by design, but multi-GPU runs are "
+              "not part of it", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import rnn_joint_transducer_amd as rj
+    from rnn_joint_transducer_amd import _lib
+    from synth import make_config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_config(args.workload)
+    tt, tu, tv = DEFAULT_TILES[args.workload]
+    tt = tt if args.tile_t is None else args.tile_t
+    tu = tu if args.tile_u is None else args.tile_u
+    tv = tv if args.tile_v is None else args.tile_v
+    bf16 = inp.dtype == "bf16"
+    dt = "bf16" if bf16 else "f32"
+
+    def conv(a):
+        if bf16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    tensors = dict(enc=conv(inp.enc), pred=conv(inp.pred), W_out=conv(inp.W), b_out=conv(inp.b),
+                   labels=i32(inp.labels), T_lens=i32(inp.T_lens), U_lens=i32(inp.U_lens))
+    B, T, U, H, V = inp.B, inp.T, inp.U, inp.H, inp.V
+    dc = rj.RNNTJ_BF16 if bf16 else rj.RNNTJ_F32
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_mem = torch.cuda.memory_allocated(dev)
+    saved = torch.empty(rj.rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tt, tu, tv),
+                        dtype=torch.uint8, device=dev)
+    wsb = rj.rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tt, tu, tv, 1)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    costs = torch.empty(B, dtype=torch.float32, device=dev)
+    grads = (torch.empty(B, T, H, device=dev), torch.empty(B, U + 1, H, device=dev),
+             torch.empty(H, V, device=dev), torch.empty(V, device=dev))
+
+    def step():
+        rj.rnnt_joint_loss_fwd(**tensors, tile_t=tt, tile_u=tu, tile_v=tv, costs=costs,
+                               saved=saved)
+        rj.rnnt_joint_loss_bwd(**tensors, saved=saved, tile_t=tt, tile_u=tu, tile_v=tv,
+                               workspace=ws, out=grads)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    peak_gb = torch.cuda.max_memory_allocated(dev) / 1e9
+    extra_gb = (torch.cuda.max_memory_allocated(dev) - base_mem) / 1e9
+    status = rj.rnnt_joint_loss_status(saved)
+
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = B * T * U / (ms / 1e3)
+    print(f"# {args.workload}: {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), "
+          f"{value:.4g} cells/s, peak {peak_gb:.2f} GB, status {status}", file=sys.stderr,
+          flush=True)
+
+    # per-kernel durations from HIP events recorded by the library on its stream
+    _lib.timing(True)
+    kin = max(1, min(args.steps, 10))
+    for _ in range(kin):
+        step()
+    torch.cuda.synchronize()
+    rep = _lib.timing_report()
+    _lib.timing(False)
+    valid = int(np.sum(inp.T_lens.astype(np.int64) * (inp.U_lens.astype(np.int64) + 1)))
+    kernels = {}
+    for name, (n, tot) in rep.items():
+        per_launch_ms = tot / n
+        k = {"launches_per_step": n / kin, "ms_per_step": tot / kin, "ms_per_launch": per_launch_ms}
+        if name in MFMA_KERNELS:
+            flops_step = 2.0 * H * V * valid
+            k["tflops"] = flops_step / (tot / kin / 1e3) / 1e12
+        kernels[name] = k
+        print(f"#   {name:16s} {n / kin:5.1f} launches/step {tot / kin:9.4f} ms/step", file=sys.stderr)
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    kd = kernels[dom]
+    launches = kd["launches_per_step"]
+    if dom in MFMA_KERNELS:
+        per_launch = 2.0 * H * V * valid / launches
+        achieved = per_launch / (kd["ms_per_launch"] / 1e3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[dt],
+                "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[dt], "traffic": None,
+                "algorithmic_per_launch": per_launch}
+    else:
+        # lattice: 32 B per valid cell (alpha and beta chains each read LB, LE and
+        # write one float64); grad_inplace: read + write the logits
+        elem = 2 if bf16 else 4
+        per_cell = 32.0 if dom == "lattice" else (2.0 * elem * V if dom == "grad_inplace" else 0.0)
+        per_launch = per_cell * valid / launches
+        achieved = per_launch / (kd["ms_per_launch"] / 1e3) / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                "algorithmic_per_launch": per_launch}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
+    line = {
+        "metric": METRIC, "value": value, "unit": "cells/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "T": T, "U": U, "H": H, "V": V,
+                   "mode": mode, "tile_t": tt, "tile_u": tu, "tile_v": tv,
+                   "valid_cells": valid, "valid_cells_per_s": valid / (ms / 1e3),
+                   "peak_gb": round(peak_gb, 3), "peak_gb_above_inputs": round(extra_gb, 3)},
+        "roofline": roof,
+        "kernels": {k: {kk: round(vv, 6) for kk, vv in v.items()} for k, v in kernels.items()},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

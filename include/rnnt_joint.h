@@ -1,0 +1,165 @@
+/*
+ * rnnt_joint.h -- C ABI of the fused RNN-T joint network + transducer loss
+ * (forward and backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed ("Flash RNN-T: Memory-Efficient Joint Network and
+ * Transducer Loss Computation", Abstract: the joint and the loss are evaluated
+ * over the full alignment space and the full vocabulary, untiled or with tiled
+ * recomputation; "Daily Papers" page, Transformer-Transducer abstract: one
+ * label distribution per (frame, label history) from a feed-forward
+ * combination of the two encodings; "Daily Papers" page, abstract on sequence
+ * transduction with recurrent networks: the loss sums over every alignment):
+ *
+ *   for every utterance b and lattice cell (t, u), t < T'_b, u <= U'_b:
+ *     h      = tanh(enc[b,t,:] + pred[b,u,:])                  [H]
+ *     z      = h @ W_out + b_out                               [V]
+ *     LB     = log_softmax(z)[blank],  LE = log_softmax(z)[labels[b,u]]  (u < U')
+ *   alpha/beta recursions over the lattice (blank: t -> t+1, label: u -> u+1,
+ *   final blank at (T'-1, U')),  costs[b] = -log P(labels_b | enc_b, pred_b);
+ *   backward: gradients of sum_b grad_costs[b] * costs[b] with respect to
+ *   enc, pred, W_out and b_out.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller: contiguous,
+ *     row-major, 16-byte aligned.  The library never allocates, frees or keeps
+ *     device memory between calls and is reentrant; its only global state is
+ *     the optional kernel-timing record (rnnt_joint_loss_timing, below).
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     on it and the call returns without synchronising, except
+ *     rnnt_joint_loss_status, which synchronises `stream`.
+ *   - Shapes: enc [B,T,H], pred [B,U+1,H] (row 0 = state before any label,
+ *     row u = state after u labels), W_out [H,V], b_out [V], labels int32
+ *     [B,U] (labels[b,u] is the (u+1)-th label), T_lens / U_lens int32 [B].
+ *     enc, pred, W_out and b_out all have type `dtype`; costs and every
+ *     gradient are float32 whatever `dtype` is.
+ *   - Modes: tile_t == 0 and tile_u == 0 selects the UNTILED mode: the forward
+ *     stores the logits (dtype) in `saved` and the backward turns them into
+ *     logit gradients in place, so one forward feeds exactly one backward.
+ *     Otherwise the TILED mode stores only per-cell scalars and recomputes the
+ *     joint and logits in the backward, one lattice chunk of tile_t frames x
+ *     tile_u label positions (all utterances) at a time; 0 on one axis means
+ *     the whole axis.  tile_t must be a multiple of 16 and tile_u of 8.
+ *     tile_v is the vocabulary tile over which the online max / log-sum-exp is
+ *     carried: 0 selects the default (128); 128 is supported.
+ *   - Limits (else RNNTJ_ERR_UNSUPPORTED): H a multiple of 16 with
+ *     16 <= H <= 768 for bf16 and H <= 256 for fp32; V a multiple of 8,
+ *     8 <= V; U + 1 <= 512.
+ *   - Host-side argument errors (null pointers, bad shapes, blank outside
+ *     [0,V), unsupported tiles, workspace too small) return a nonzero code
+ *     before anything is enqueued; outputs are untouched.
+ *   - Data errors are detected on the device: T'_b outside [1,T], U'_b outside
+ *     [0,U], or labels[b,u] (u < U'_b) outside [0,V) or equal to blank.  The
+ *     utterance then gets costs[b] = NaN and zero gradients, and a status
+ *     word in `saved` is set; rnnt_joint_loss_status reports it.
+ *   - NaN / Inf in the float inputs propagate to the outputs; they are not
+ *     reported as errors.
+ */
+#ifndef RNNT_JOINT_H_
+#define RNNT_JOINT_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RNNTJ_ABI_VERSION 1
+
+enum rnntj_dtype { RNNTJ_F32 = 0, RNNTJ_BF16 = 1 };
+
+enum rnntj_status {
+  RNNTJ_OK = 0,
+  RNNTJ_ERR_ARG = 1,          /* null pointer, non-positive size, blank out of range */
+  RNNTJ_ERR_UNSUPPORTED = 2,  /* shape or tile outside the limits above */
+  RNNTJ_ERR_WORKSPACE = 3,    /* workspace_bytes smaller than required */
+  RNNTJ_ERR_HIP = 4,          /* a HIP launch or copy failed */
+  RNNTJ_ERR_DATA = 5          /* (status only) invalid lengths or labels seen on the device */
+};
+
+/* Version of this ABI (RNNTJ_ABI_VERSION of the built library). */
+int rnnt_joint_loss_abi_version(void);
+
+/* Human-readable text for a status code; never NULL, static storage. */
+const char* rnnt_joint_loss_strerror(int code);
+
+/*
+ * Bytes of the forward -> backward state `saved` for these sizes and tiles.
+ * saved holds the per-utterance validated lengths, log P and status, a
+ * transposed copy of W_out, and per cell (diagonal-skewed [B, T+U, U+1]):
+ * lse, LB, LE (float32) and alpha, beta (float64).  In the untiled mode it
+ * also holds the logits [B, ceil16(T), ceil8(U+1), V] in dtype.
+ * Writes *out; returns a status code.
+ */
+int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
+                                int tile_t, int tile_u, int tile_v, size_t* out);
+
+/*
+ * Bytes of scratch `workspace` needed by the forward (pass = 0) or the
+ * backward (pass = 1).  The forward needs none.  The tiled backward needs one
+ * chunk of logit gradients [B, tile_t, tile_u, V] in dtype; the untiled
+ * backward needs none.  Writes *out; returns a status code.
+ */
+int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
+                                    int tile_t, int tile_u, int tile_v, int pass,
+                                    size_t* out);
+
+/*
+ * Forward: costs[b] = -log P(labels_b) for every utterance, and the state the
+ * backward needs, written into `saved` (rnnt_joint_loss_saved_bytes bytes,
+ * caller-owned, contents overwritten).  enc/pred/W_out/b_out are read only.
+ * Launch order on `stream`: length/label validation, W_out transpose, fused
+ * joint + projection + online log-sum-exp (+ logit store when untiled),
+ * alpha/beta lattice recursion.  Returns a status code (host-side checks and
+ * launch errors only).
+ */
+int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out,
+                        const void* b_out, int dtype, const int32_t* labels,
+                        const int32_t* T_lens, const int32_t* U_lens, int B, int T,
+                        int U, int H, int V, int blank, int tile_t, int tile_u,
+                        int tile_v, float* costs, void* saved, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * Backward: overwrites d_enc [B,T,H], d_pred [B,U+1,H], d_W_out [H,V] and
+ * d_b_out [V] (float32) with the gradients of sum_b grad_costs[b] * costs[b]
+ * (grad_costs float32 [B] on the device, or NULL for all ones).  Takes the
+ * same inputs, sizes and tiles as the forward that filled `saved`; the whole
+ * batch is handled in one call.  In the untiled mode it consumes the logits
+ * stored in `saved`.  Entries of d_enc / d_pred past each utterance's lengths
+ * are zero.  Returns a status code (host-side checks and launch errors only).
+ */
+int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,
+                        const void* b_out, int dtype, const int32_t* labels,
+                        const int32_t* T_lens, const int32_t* U_lens, int B, int T,
+                        int U, int H, int V, int blank, int tile_t, int tile_u,
+                        int tile_v, const float* grad_costs, void* saved,
+                        float* d_enc, float* d_pred, float* d_W_out, float* d_b_out,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronises `stream`, then copies the data-error word of `saved` to
+ * *data_error: 0 = every utterance valid, else a bit mask (1 = a length out of
+ * range, 2 = a label out of range or equal to blank).  Returns a status code.
+ */
+int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error);
+
+/*
+ * Kernel timing (measurement aid; no counterpart on the pages).
+ * rnnt_joint_loss_timing(1) makes every later call bracket each kernel it
+ * enqueues with a pair of HIP events recorded on that call's `stream`;
+ * rnnt_joint_loss_timing(0) stops it and drops pending events.  Process-wide
+ * and not thread-safe; off by default.  Events are host-side HIP resources,
+ * not device memory.
+ * rnnt_joint_loss_timing_report waits for the recorded events, writes one
+ * line "<kernel> <launches> <total_ms>\n" per kernel name into buf (NUL
+ * terminated, truncated to len), frees the events and clears the record.
+ */
+int rnnt_joint_loss_timing(int enable);
+int rnnt_joint_loss_timing_report(char* buf, size_t len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNNT_JOINT_H_ */

@@ -49,6 +49,7 @@ from __future__ import annotations
 
 import itertools
 import math
+import multiprocessing
 import os
 from concurrent.futures import ProcessPoolExecutor
 
@@ -211,7 +212,9 @@ def loss_and_grads(enc, pred, W, b_out, labels, T_lens, U_lens, blank,
         jobs.append((enc[b], pred[b], W, b_out, np.asarray(labels[b]),
                      int(T_lens[b]), int(U_lens[b]), blank, gcs[b], threads))
     if workers > 1 and B > 1:
-        with ProcessPoolExecutor(max_workers=min(workers, B)) as ex:
+        # spawn, never fork: the caller may have initialised a GPU runtime
+        ctx = multiprocessing.get_context("spawn")
+        with ProcessPoolExecutor(max_workers=min(workers, B), mp_context=ctx) as ex:
             outs = list(ex.map(_utt_job, jobs))
     else:
         outs = [utterance_loss_and_grads(*j[:9]) for j in jobs]

@@ -1,0 +1,181 @@
+"""Fused RNN-T joint network + transducer loss for MI355X (gfx950).
+
+Thin Python binding over the C ABI in ``include/rnnt_joint.h`` (argument
+marshalling only; every step runs in the HIP kernels of librnntjoint.so).
+PyTorch provides device memory and the current stream.
+
+    costs, saved = rnnt_joint_loss_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens)
+    d_enc, d_pred, d_W, d_b = rnnt_joint_loss_bwd(enc, ..., saved=saved)
+    costs = rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens)  # autograd
+
+Tiling (``tile_t``, ``tile_u``, ``tile_v``) follows the C ABI: tile_t = tile_u
+= 0 is the untiled mode (logits stored by the forward); otherwise the backward
+recomputes the joint per lattice chunk of tile_t x tile_u cells.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from ._lib import (RNNTJ_BF16, RNNTJ_F32, RNNTJointError, check, declared_functions,  # noqa: F401
+                   load)
+
+__all__ = ["rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd", "rnnt_joint_loss_status",
+           "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
+           "rnnt_joint_loss", "RNNTJointError", "load"]
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return RNNTJ_F32
+    if t.dtype == torch.bfloat16:
+        return RNNTJ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def rnnt_joint_loss_saved_bytes(B, T, U, H, V, dtype_code, tile_t=0, tile_u=0, tile_v=0) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().rnnt_joint_loss_saved_bytes(B, T, U, H, V, dtype_code, tile_t, tile_u, tile_v,
+                                             ctypes.byref(out)), "rnnt_joint_loss_saved_bytes")
+    return out.value
+
+
+def rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dtype_code, tile_t=0, tile_u=0, tile_v=0,
+                                    pass_=1) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dtype_code, tile_t, tile_u,
+                                                 tile_v, pass_, ctypes.byref(out)),
+          "rnnt_joint_loss_workspace_bytes")
+    return out.value
+
+
+def _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens):
+    import torch
+    B, T, H = enc.shape
+    U = pred.shape[1] - 1
+    V = W_out.shape[1]
+    dt = enc.dtype
+    for name, t, shape in (("pred", pred, (B, U + 1, H)), ("W_out", W_out, (H, V)),
+                           ("b_out", b_out, (V,))):
+        if tuple(t.shape) != shape or t.dtype != dt:
+            raise ValueError(f"{name}: expected shape {shape} dtype {dt}, got "
+                             f"{tuple(t.shape)} {t.dtype}")
+    for name, t, shape in (("labels", labels, (B, U)), ("T_lens", T_lens, (B,)),
+                           ("U_lens", U_lens, (B,))):
+        if tuple(t.shape) != shape or t.dtype != torch.int32:
+            raise ValueError(f"{name}: expected int32 shape {shape}, got {tuple(t.shape)} {t.dtype}")
+    dev = enc.device
+    for t in (enc, pred, W_out, b_out, labels, T_lens, U_lens):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous and on the same GPU")
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on the GPU (no CPU path)")
+    return B, T, U, H, V
+
+
+def rnnt_joint_loss_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, tile_t=0,
+                        tile_u=0, tile_v=0, costs=None, saved=None):
+    """Costs [B] (float32) and the uint8 `saved` state for the backward."""
+    import torch
+    B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
+    dc = _dtype_code(enc)
+    nbytes = rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v)
+    if saved is None:
+        saved = torch.empty(nbytes, dtype=torch.uint8, device=enc.device)
+    elif saved.numel() < nbytes:
+        raise ValueError(f"saved buffer too small ({saved.numel()} < {nbytes})")
+    if costs is None:
+        costs = torch.empty(B, dtype=torch.float32, device=enc.device)
+    rc = load().rnnt_joint_loss_fwd(_ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out), dc,
+                                    _ptr(labels), _ptr(T_lens), _ptr(U_lens), B, T, U, H, V,
+                                    blank, tile_t, tile_u, tile_v, _ptr(costs), _ptr(saved),
+                                    None, 0, _stream(enc.device))
+    check(rc, "rnnt_joint_loss_fwd")
+    return costs, saved
+
+
+def rnnt_joint_loss_bwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, blank=0,
+                        tile_t=0, tile_u=0, tile_v=0, grad_costs=None, workspace=None,
+                        out=None):
+    """(d_enc, d_pred, d_W_out, d_b_out), all float32."""
+    import torch
+    B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
+    dc = _dtype_code(enc)
+    dev = enc.device
+    ws = rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, 1)
+    if workspace is None and ws > 0:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = (torch.empty(B, T, H, dtype=torch.float32, device=dev),
+               torch.empty(B, U + 1, H, dtype=torch.float32, device=dev),
+               torch.empty(H, V, dtype=torch.float32, device=dev),
+               torch.empty(V, dtype=torch.float32, device=dev))
+    if grad_costs is not None:
+        if grad_costs.dtype != torch.float32 or tuple(grad_costs.shape) != (B,):
+            raise ValueError("grad_costs must be float32 [B]")
+        grad_costs = grad_costs.contiguous()
+    d_enc, d_pred, d_W, d_b = out
+    rc = load().rnnt_joint_loss_bwd(_ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out), dc,
+                                    _ptr(labels), _ptr(T_lens), _ptr(U_lens), B, T, U, H, V,
+                                    blank, tile_t, tile_u, tile_v, _ptr(grad_costs),
+                                    _ptr(saved), _ptr(d_enc), _ptr(d_pred), _ptr(d_W),
+                                    _ptr(d_b), _ptr(workspace), ws if workspace is not None else 0,
+                                    _stream(dev))
+    check(rc, "rnnt_joint_loss_bwd")
+    return out
+
+
+def rnnt_joint_loss_status(saved) -> int:
+    """Synchronises the current stream and returns the data-error bit mask."""
+    v = ctypes.c_int32(0)
+    check(load().rnnt_joint_loss_status(_ptr(saved), _stream(saved.device), ctypes.byref(v)),
+          "rnnt_joint_loss_status")
+    return v.value
+
+
+def _make_function():
+    import torch
+
+    class _RNNTJointLoss(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, enc, pred, W_out, b_out, labels, T_lens, U_lens, blank, tile_t, tile_u,
+                    tile_v):
+            costs, saved = rnnt_joint_loss_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens,
+                                               blank, tile_t, tile_u, tile_v)
+            ctx.save_for_backward(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved)
+            ctx.cfg = (blank, tile_t, tile_u, tile_v)
+            return costs
+
+        @staticmethod
+        def backward(ctx, grad_costs):
+            enc, pred, W_out, b_out, labels, T_lens, U_lens, saved = ctx.saved_tensors
+            blank, tile_t, tile_u, tile_v = ctx.cfg
+            d_enc, d_pred, d_W, d_b = rnnt_joint_loss_bwd(
+                enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, blank, tile_t, tile_u,
+                tile_v, grad_costs=grad_costs.float().contiguous())
+            return (d_enc.to(enc.dtype), d_pred.to(pred.dtype), d_W.to(W_out.dtype),
+                    d_b.to(b_out.dtype), None, None, None, None, None, None, None)
+
+    return _RNNTJointLoss
+
+
+_FN = None
+
+
+def rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, tile_t=0,
+                    tile_u=0, tile_v=0):
+    """Per-utterance costs [B] with autograd support (one backward per forward)."""
+    global _FN
+    if _FN is None:
+        _FN = _make_function()
+    return _FN.apply(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank, tile_t, tile_u,
+                     tile_v)

@@ -1,0 +1,445 @@
+// Backward kernels of the fused RNN-T joint + transducer loss.
+//
+// Gradient of sum_b gc_b * cost_b (transducer lattice as defined on the
+// "Daily Papers" page, abstract on sequence transduction with recurrent
+// networks; joint and loss of the "Flash RNN-T" page, Abstract):
+//   dz(t,u)[v] = gc * (occ * softmax(z)[v] - gB [v=blank] - gE [v=y_u])
+//   dW_out = sum_cells h^T dz,   db_out = sum_cells dz
+//   dh = dz @ W_out^T,  dpre = (1 - h^2) * dh,
+//   d_enc[t] = sum_u dpre(t,u),  d_pred[u] = sum_t dpre(t,u)
+//
+// Kernels here:
+//   grad_inplace_kernel : untiled mode, stored logits -> dz in place.
+//   dh_kernel           : MFMA GEMM dz[cells, V] x W_out^T -> [cells, H] for
+//                         one 16x8 cell tile and 128 hidden columns, with the
+//                         (1 - h^2) epilogue and the two lattice reductions
+//                         done in registers before float32 atomics.
+//   dw_kernel           : MFMA GEMM h^T[H, cells] x dz[cells, V] split over
+//                         utterances (split-K), h rebuilt from enc/pred and
+//                         both operands transposed while staged through LDS;
+//                         the hidden-row-0 workgroups also sum dz columns
+//                         into db_out.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace rnntj {
+
+namespace {
+
+constexpr float kInf = __builtin_inff();
+
+// ------------------------------------------------------------ untiled dz
+
+template <typename T>
+__global__ __launch_bounds__(256) void grad_inplace_kernel(T* __restrict__ z, JointArgs a) {
+  __shared__ float row_c[kTileCells], row_b[kTileCells], row_e[kTileCells];
+  __shared__ int row_y[kTileCells];
+  const Dims d = a.d;
+  const int b = blockIdx.y;
+  const int n_tu = d.U1pad / kTileU;
+  const int t0 = (blockIdx.x / n_tu) * kTileT;
+  const int u0 = (blockIdx.x % n_tu) * kTileU;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  if (t0 >= Tl || u0 > Ul) return;
+  const int tid = threadIdx.x;
+  if (tid < kTileCells) {
+    const int t = t0 + (tid >> 3), u = u0 + (tid & 7);
+    float c = kInf, gb = 0.f, ge = 0.f;
+    int y = -1;
+    if (t < Tl && u <= Ul) {
+      const double g = a.gcost ? (double)a.gcost[b] : 1.0;
+      double gB, gE;
+      cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE);
+      const double occ = gB + gE;
+      const double lse = (double)a.lse[skew_idx(d, b, t, u)];
+      c = occ > 0.0 ? (float)(lse - log(occ)) : kInf;
+      gb = (float)(g * gB);
+      ge = (float)(g * gE);
+      if (u < Ul) y = a.labels[(size_t)b * d.U + u];
+    }
+    row_c[tid] = c;
+    row_b[tid] = gb;
+    row_e[tid] = ge;
+    row_y[tid] = y;
+  }
+  __syncthreads();
+  const float gc = a.gcost ? a.gcost[b] : 1.0f;
+  const int V = d.V;
+  const int cpr = V / 8;  // 8-element chunks per row
+  for (int c = tid; c < kTileCells * cpr; c += 256) {
+    const int row = c / cpr, v0 = (c % cpr) * 8;
+    const int t = t0 + (row >> 3), u = u0 + (row & 7);
+    T* zp = z + (((size_t)b * d.Tpad + t) * d.U1pad + u) * V + v0;
+    Frag8<T> f;
+    if (t < Tl && u <= Ul) {
+      f = load_frag(zp);
+      float x[8];
+      const float cr = row_c[row];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float g = gc * __expf(f.get(i) - cr);
+        if (v0 + i == d.blank) g -= row_b[row];
+        if (v0 + i == row_y[row]) g -= row_e[row];
+        x[i] = g;
+      }
+      pack_frag(f, x);
+    } else {
+      zero_frag(f);
+    }
+    store_frag(zp, f);
+  }
+}
+
+// ------------------------------------------------------------ staging config
+
+template <typename T>
+struct Cfg {
+  static constexpr int BK = std::is_same<T, float>::value ? 32 : 64;  // dh: k (vocab) per stage
+  static constexpr int CE = 16 / (int)sizeof(T);
+  static constexpr int LDK = BK + CE;
+  static constexpr int CH = 128 * BK / CE / 256;  // 16 B chunks per thread per operand
+};
+
+// ------------------------------------------------------------ dh GEMM
+
+template <typename T>
+__device__ __forceinline__ void dh_load(const DhArgs& a, int b, int t0, int u0, int Tl, int Ul,
+                                        int n0, int k0, u32x4 (&ra)[Cfg<T>::CH],
+                                        u32x4 (&rb)[Cfg<T>::CH]) {
+  using C = Cfg<T>;
+  const T* g = static_cast<const T*>(a.g);
+  const T* W = static_cast<const T*>(a.W);
+  const Dims& d = a.d;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < C::CH; ++q) {
+    const int c = tid + 256 * q;
+    const int row = c / (C::BK / C::CE);
+    const int col = (c % (C::BK / C::CE)) * C::CE;
+    const int k = k0 + col;
+    // A: dz rows of the cell tile, row = 8*tt + uu
+    const int t = t0 + (row >> 3), u = u0 + (row & 7);
+    if (t < Tl && u <= Ul && k < d.V)
+      ra[q] = *reinterpret_cast<const u32x4*>(
+          g + (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * d.V + k);
+    else
+      ra[q] = u32x4{0u, 0u, 0u, 0u};
+    // B: W_out rows n0 + row (hidden index), contiguous in the vocabulary
+    const int n = n0 + row;
+    if (n < d.H && k < d.V)
+      rb[q] = *reinterpret_cast<const u32x4*>(W + (size_t)n * d.V + k);
+    else
+      rb[q] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void stage_store(T* lds, const u32x4 (&r)[Cfg<T>::CH]) {
+  using C = Cfg<T>;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < C::CH; ++q) {
+    const int c = tid + 256 * q;
+    const int row = c / (C::BK / C::CE);
+    const int col = (c % (C::BK / C::CE)) * C::CE;
+    *reinterpret_cast<u32x4*>(lds + row * C::LDK + col) = r[q];
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dh_kernel(DhArgs a) {
+  using C = Cfg<T>;
+  __shared__ __align__(16) T As[2][128 * C::LDK];
+  __shared__ __align__(16) T Bs[2][128 * C::LDK];
+  const Dims d = a.d;
+  const int b = blockIdx.z;
+  const int t0 = a.ct0 + (blockIdx.x / a.n_tu) * kTileT;
+  const int u0 = a.cu0 + (blockIdx.x % a.n_tu) * kTileU;
+  const int n0 = blockIdx.y * 128;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  if (t0 >= Tl || u0 > Ul) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kh = lane >> 5, lc = lane & 31;
+  const int wm = w >> 1, wn = w & 1;  // 64 rows x 64 cols per wave
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  u32x4 ra[C::CH], rb[C::CH];
+  const int nk = (d.V + C::BK - 1) / C::BK;
+  dh_load<T>(a, b, t0, u0, Tl, Ul, n0, 0, ra, rb);
+  stage_store<T>(As[0], ra);
+  stage_store<T>(Bs[0], rb);
+  __syncthreads();
+  for (int kb = 0; kb < nk; ++kb) {
+    const int cur = kb & 1;
+    const bool has_next = kb + 1 < nk;
+    if (has_next) dh_load<T>(a, b, t0, u0, Tl, Ul, n0, (kb + 1) * C::BK, ra, rb);
+#pragma unroll
+    for (int kk = 0; kk < C::BK / 16; ++kk) {
+      Frag8<T> fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = load_frag(&As[cur][(64 * wm + 32 * i + lc) * C::LDK + kk * 16 + 8 * kh]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = load_frag(&Bs[cur][(64 * wn + 32 * j + lc) * C::LDK + kk * 16 + 8 * kh]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma_step(acc[i][j], fa[i], fb[j]);
+    }
+    if (has_next) {
+      stage_store<T>(As[cur ^ 1], ra);
+      stage_store<T>(Bs[cur ^ 1], rb);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: dpre = (1 - h^2) * dh, h rebuilt from enc / pred
+  const T* enc = static_cast<const T*>(a.enc);
+  const T* pred = static_cast<const T*>(a.pred);
+  // wave rows: 64*wm + 32*i + acc_row(r, kh)  <->  tt = 8*wm + 4*i + r/4, uu = 4*kh + r%4
+  float pred_sum[2][4];  // [j][r%4]: sum over this wave's frames, per label position
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) pred_sum[j][q] = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 64 * wn + 32 * j + lc;
+    const bool nvalid = n < d.H;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {  // frame within the 32-row block
+        const int t = t0 + 8 * wm + 4 * i + q4;
+        float enc_sum = 0.f;
+        const float ev = (nvalid && t < Tl) ? ElemTraits<T>::to_f32(enc[((size_t)b * d.T + t) * d.H + n]) : 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // label position within the half
+          const int r = 4 * q4 + q;
+          const int u = u0 + 4 * kh + q;
+          float v = 0.f;
+          if (nvalid && t < Tl && u <= Ul) {
+            const float pv = ElemTraits<T>::to_f32(pred[((size_t)b * d.U1 + u) * d.H + n]);
+            const float h = fast_tanh(ev + pv);
+            v = (1.0f - h * h) * acc[i][j][r];
+          }
+          enc_sum += v;
+          pred_sum[j][q] += v;
+        }
+        // the other 4 label positions of this frame live in lane l ^ 32
+        enc_sum += __shfl_xor(enc_sum, 32);
+        if (kh == 0 && nvalid && t < Tl)
+          atomicAdd(&a.d_enc[((size_t)b * d.T + t) * d.H + n], enc_sum);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 64 * wn + 32 * j + lc;
+    if (n < d.H) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = u0 + 4 * kh + q;
+        if (u <= Ul) atomicAdd(&a.d_pred[((size_t)b * d.U1 + u) * d.H + n], pred_sum[j][q]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ dW GEMM
+
+// K block = 32 cells = 4 frames x 8 label positions.
+constexpr int kDwK = 32;
+
+template <typename T>
+struct DwCfg {
+  static constexpr int PAD = 16 / (int)sizeof(T);
+  static constexpr int LDK = kDwK + PAD;  // bf16: 80 B rows, fp32: 144 B rows
+};
+
+template <typename T>
+__device__ __forceinline__ bool dw_cell(const DwArgs& a, int Tl, int Ul, int kt, int ku, int c,
+                                        int& t, int& u) {
+  t = kt + (c >> 3);
+  u = ku + (c & 7);
+  return t < Tl && t < a.ct0 + a.CT && u <= Ul && u < a.cu0 + a.CU;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
+  using C = DwCfg<T>;
+  __shared__ __align__(16) T As[2][128 * C::LDK];  // h^T  [hidden][cell]
+  __shared__ __align__(16) T Bs[2][128 * C::LDK];  // dz^T [vocab][cell]
+  __shared__ float dbs[16][128];
+  const Dims d = a.d;
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128, b = blockIdx.z;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  const int nt = min(a.CT, Tl - a.ct0);
+  const int nu = min(a.CU, Ul + 1 - a.cu0);
+  if (nt <= 0 || nu <= 0) return;
+  const int ntb = (nt + 3) / 4, nub = (nu + 7) / 8;
+  const int nkb = ntb * nub;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int kh = lane >> 5, lc = lane & 31;
+  const int wm = w >> 1, wn = w & 1;
+  const bool do_db = (blockIdx.y == 0);
+
+  const T* enc = static_cast<const T*>(a.enc);
+  const T* pred = static_cast<const T*>(a.pred);
+  const T* g = static_cast<const T*>(a.g);
+
+  // staging role: cell pair cp (cells 2cp, 2cp+1 of the K block), group of
+  // 8 hidden rows (A) / 8 vocabulary columns (B)
+  const int cp = tid & 15, grp = tid >> 4;
+  const int mA = m0 + 8 * grp, nB = n0 + 8 * grp;
+  float hv[2][8], gv[2][8];
+  bool hok[2];
+  float dbacc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) dbacc[i] = 0.f;
+
+  auto load_block = [&](int kb) {
+    const int kt = a.ct0 + 4 * (kb / nub), ku = a.cu0 + 8 * (kb % nub);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      int t, u;
+      const bool ok = dw_cell<T>(a, Tl, Ul, kt, ku, 2 * cp + e, t, u);
+      hok[e] = ok && mA < d.H;
+      if (hok[e]) {
+        Frag8<T> fe = load_frag(enc + ((size_t)b * d.T + t) * d.H + mA);
+        Frag8<T> fp = load_frag(pred + ((size_t)b * d.U1 + u) * d.H + mA);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[e][i] = fe.get(i) + fp.get(i);  // tanh applied at store
+      }
+      if (ok && nB < d.V) {
+        Frag8<T> fg = load_frag(g + (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * d.V + nB);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[e][i] = fg.get(i);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gv[e][i] = 0.f;
+      }
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float h0 = hok[0] ? fast_tanh(hv[0][i]) : 0.f;
+      const float h1 = hok[1] ? fast_tanh(hv[1][i]) : 0.f;
+      if constexpr (std::is_same<T, float>::value) {
+        *reinterpret_cast<float2*>(&As[buf][(8 * grp + i) * C::LDK + 2 * cp]) = float2{h0, h1};
+        *reinterpret_cast<float2*>(&Bs[buf][(8 * grp + i) * C::LDK + 2 * cp]) =
+            float2{gv[0][i], gv[1][i]};
+      } else {
+        *reinterpret_cast<uint32_t*>(&As[buf][(8 * grp + i) * C::LDK + 2 * cp]) =
+            (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
+        *reinterpret_cast<uint32_t*>(&Bs[buf][(8 * grp + i) * C::LDK + 2 * cp]) =
+            (uint32_t)f32_to_bf16(gv[0][i]) | ((uint32_t)f32_to_bf16(gv[1][i]) << 16);
+      }
+      dbacc[i] += gv[0][i] + gv[1][i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int cur = kb & 1;
+    const bool has_next = kb + 1 < nkb;
+    if (has_next) load_block(kb + 1);
+#pragma unroll
+    for (int kk = 0; kk < kDwK / 16; ++kk) {
+      Frag8<T> fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        fa[i] = load_frag(&As[cur][(64 * wm + 32 * i + lc) * C::LDK + kk * 16 + 8 * kh]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        fb[j] = load_frag(&Bs[cur][(64 * wn + 32 * j + lc) * C::LDK + kk * 16 + 8 * kh]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma_step(acc[i][j], fa[i], fb[j]);
+    }
+    if (has_next) store_block(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 64 * wn + 32 * j + lc;
+      if (n < d.V) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 64 * wm + 32 * i + acc_row(r, kh);
+          if (m < d.H) atomicAdd(&a.d_W[(size_t)m * d.V + n], acc[i][j][r]);
+        }
+      }
+    }
+
+  if (do_db) {
+    // dbacc of the 16 cell-pair threads sharing a column group
+#pragma unroll
+    for (int i = 0; i < 8; ++i) dbs[cp][8 * grp + i] = dbacc[i];
+    __syncthreads();
+    if (tid < 128) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) s += dbs[q][tid];
+      if (n0 + tid < d.V) atomicAdd(&a.d_b[n0 + tid], s);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, hipStream_t st) {
+  dim3 grid((a.d.Tpad / kTileT) * (a.d.U1pad / kTileU), a.d.B), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(grad_inplace_kernel<uint16_t>, grid, block, 0, st,
+                       static_cast<uint16_t*>(z), a);
+  else
+    hipLaunchKernelGGL(grad_inplace_kernel<float>, grid, block, 0, st, static_cast<float*>(z),
+                       a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh(const DhArgs& a, bool bf16, hipStream_t st) {
+  dim3 grid((a.CT / kTileT) * a.n_tu, (a.d.H + 127) / 128, a.d.B), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(dh_kernel<float>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st) {
+  dim3 grid((a.d.V + 127) / 128, (a.d.H + 127) / 128, a.d.B), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(dw_kernel<uint16_t>, grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL(dw_kernel<float>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace rnntj

@@ -1,0 +1,176 @@
+// Shared device-side definitions for the fused RNN-T joint + transducer loss
+// kernels (gfx950 / CDNA4, wave64).
+//
+// Lattice notation follows the "Flash RNN-T" page (Abstract: joint network and
+// transducer loss over the full alignment space and vocabulary) and the RNN
+// transducer definition on the "Daily Papers" page (abstract on sequence
+// transduction with recurrent networks): a cell is (b, t, u) with t < T'_b and
+// u <= U'_b; pred row u is the prediction state after u labels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rnntj {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Cell tile of the joint kernels: 16 frames x 8 label positions = 128 cells,
+// processed by 4 waves that own 4 frames x 8 label positions (32 rows) each.
+constexpr int kTileT = 16;
+constexpr int kTileU = 8;
+constexpr int kTileCells = kTileT * kTileU;
+constexpr int kVocabTile = 128;  // vocabulary columns per pass of one wave
+
+// Shapes shared by every kernel.
+struct Dims {
+  int B, T, U, H, V, blank;
+  int U1;     // U + 1 (prediction rows)
+  int DG;     // T + U: anti-diagonals t+u of the padded lattice
+  int Tpad;   // T rounded up to kTileT
+  int U1pad;  // U1 rounded up to kTileU
+};
+
+// Per-cell scalars (lse, LB, LE, alpha, beta) are stored diagonal-skewed:
+// diagonal d = t + u is contiguous in u, so the lattice recursion reads and
+// writes whole anti-diagonals with unit stride.
+__device__ __forceinline__ size_t skew_idx(const Dims& d, int b, int t, int u) {
+  return ((size_t)b * d.DG + (size_t)(t + u)) * d.U1 + u;
+}
+
+// ---------------------------------------------------------------- bf16 / f32
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t x) {
+  return __uint_as_float(((uint32_t)x) << 16);
+}
+
+// round-to-nearest-even float -> bf16 (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct ElemTraits;
+template <> struct ElemTraits<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ float to_f32(float x) { return x; }
+  static __device__ __forceinline__ float from_f32(float x) { return x; }
+};
+template <> struct ElemTraits<uint16_t> {
+  static __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
+  static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Eight consecutive elements along the contraction axis: one MFMA operand
+// fragment of one lane for a 16-wide k-step (bf16: 16 bytes; fp32: 32 bytes).
+template <typename T> struct Frag8;
+template <> struct Frag8<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ float get(int i) const {
+    uint32_t w = v[i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+};
+template <> struct Frag8<float> {
+  f32x4 lo, hi;
+  __device__ __forceinline__ float get(int i) const { return i < 4 ? lo[i] : hi[i - 4]; }
+};
+
+__device__ __forceinline__ Frag8<uint16_t> load_frag(const uint16_t* p) {
+  Frag8<uint16_t> f;
+  f.v = *reinterpret_cast<const u32x4*>(p);
+  return f;
+}
+__device__ __forceinline__ Frag8<float> load_frag(const float* p) {
+  Frag8<float> f;
+  f.lo = *reinterpret_cast<const f32x4*>(p);
+  f.hi = *reinterpret_cast<const f32x4*>(p + 4);
+  return f;
+}
+__device__ __forceinline__ void store_frag(uint16_t* p, const Frag8<uint16_t>& f) {
+  *reinterpret_cast<u32x4*>(p) = f.v;
+}
+__device__ __forceinline__ void store_frag(float* p, const Frag8<float>& f) {
+  *reinterpret_cast<f32x4*>(p) = f.lo;
+  *reinterpret_cast<f32x4*>(p + 4) = f.hi;
+}
+__device__ __forceinline__ void zero_frag(Frag8<uint16_t>& f) { f.v = u32x4{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ void zero_frag(Frag8<float>& f) {
+  f.lo = f32x4{0.f, 0.f, 0.f, 0.f};
+  f.hi = f.lo;
+}
+// Build a fragment from 8 floats (bf16: round to nearest even).
+__device__ __forceinline__ void pack_frag(Frag8<uint16_t>& f, const float* x) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    f.v[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+}
+__device__ __forceinline__ void pack_frag(Frag8<float>& f, const float* x) {
+  f.lo = f32x4{x[0], x[1], x[2], x[3]};
+  f.hi = f32x4{x[4], x[5], x[6], x[7]};
+}
+
+// One 16-wide k-step of a 32x32 output block: C += A(32x16) * B(16x32).
+// Lane l supplies A row (l % 32) and B column (l % 32), elements
+// k = 8*(l/32) .. 8*(l/32)+7 of the step.  bf16 uses one 32x32x16 MFMA; fp32
+// uses eight 32x32x2 MFMAs, the s-th pairing element s of both lane halves
+// (the same k permutation on both operands leaves the sum unchanged).
+__device__ __forceinline__ void mma_step(f32x16& acc, const Frag8<uint16_t>& a,
+                                         const Frag8<uint16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                __builtin_bit_cast(bf16x8, b.v), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_step(f32x16& acc, const Frag8<float>& a,
+                                         const Frag8<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.lo[s], b.lo[s], acc, 0, 0, 0);
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[s], b.hi[s], acc, 0, 0, 0);
+}
+
+// Row of accumulator register r of a 32x32 block for lane-half kh = l/32
+// (column is l % 32): rows 8*(r/4) + 4*kh + (r%4).
+__device__ __forceinline__ int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }
+
+// tanh(x) = 1 - 2 / (1 + e^{2x}); saturates correctly at +-inf, absolute
+// error a few 1e-8.  NaN propagates (the clamp is a compare, not fminf).
+__device__ __forceinline__ float fast_tanh(float x) {
+  float y = x * (2.0f * kLog2e);
+  y = y > 126.0f ? 126.0f : y;
+  float e = __builtin_amdgcn_exp2f(y);
+  return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Transition posteriors of cell (t,u) from the float64 forward / backward
+// variables (all diagonal-skewed):
+//   gB(t,u) = exp(alpha(t,u) + LB(t,u) + beta(t+1,u) - logP)  (t < T'-1)
+//   gB(T'-1,U') = exp(alpha + LB - logP),  gB(T'-1,u<U') = 0
+//   gE(t,u) = exp(alpha(t,u) + LE(t,u) + beta(t,u+1) - logP)  (u < U'), else 0
+__device__ __forceinline__ void cell_posteriors(const Dims& d, const double* __restrict__ alpha,
+                                                const double* __restrict__ beta,
+                                                const float* __restrict__ LB,
+                                                const float* __restrict__ LE, double logP,
+                                                int b, int t, int u, int Tl, int Ul,
+                                                double& gB, double& gE) {
+  const size_t ix = skew_idx(d, b, t, u);
+  const double a = alpha[ix];
+  if (t < Tl - 1)
+    gB = exp(a + (double)LB[ix] + beta[skew_idx(d, b, t + 1, u)] - logP);
+  else
+    gB = (u == Ul) ? exp(a + (double)LB[ix] - logP) : 0.0;
+  gE = (u < Ul) ? exp(a + (double)LE[ix] + beta[skew_idx(d, b, t, u + 1)] - logP) : 0.0;
+}
+
+}  // namespace rnntj

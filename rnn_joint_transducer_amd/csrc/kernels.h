@@ -1,0 +1,94 @@
+// Kernel launch interfaces used by the C ABI (api.cpp).  Device code only
+// sees plain pointers and the Dims struct.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace rnntj {
+
+enum JointMode { kLse = 0, kStoreZ = 1, kGrad = 2 };
+
+struct JointArgs {
+  const void* enc;
+  const void* pred;
+  const void* Wt;     // W_out transposed, [V, H], dtype
+  const void* bias;   // [V], dtype
+  const int32_t* labels;
+  const int32_t* Teff;  // validated lengths (0 frames = invalid utterance)
+  const int32_t* Ueff;
+  Dims d;
+  int ct0, cu0;  // chunk origin (frame, label position)
+  int CT, CU;    // chunk extents, multiples of kTileT / kTileU
+  int n_tu;      // CU / kTileU
+  // forward outputs (diagonal-skewed per-cell scalars)
+  float* lse;
+  float* LB;
+  float* LE;
+  void* zout;  // kStoreZ: logits [B, Tpad, U1pad, V]
+  // backward inputs / output
+  const double* alpha;
+  const double* beta;
+  const double* logP;
+  const float* gcost;  // [B] or null
+  void* gout;          // kGrad: logit gradients [B, CT, CU, V]
+};
+
+hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_tiles,
+                             hipStream_t st);
+
+// Length / label validation: writes Teff/Ueff (0 / 0 for an invalid
+// utterance) and ORs a bit mask into *status.
+hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
+                           const int32_t* labels, const Dims& d, int32_t* Teff,
+                           int32_t* Ueff, int32_t* status, hipStream_t st);
+
+// dst[V, H] = transpose(src[H, V])
+hipError_t launch_transpose(const void* src, void* dst, int H, int V, bool bf16,
+                            hipStream_t st);
+
+// Fill n floats / int32s with zero (a kernel, never a memset node).
+hipError_t launch_zero(void* p, size_t n_words, hipStream_t st);
+
+// Alpha / beta recursion over the anti-diagonals; costs[b] = -logP.
+hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
+                          const int32_t* Ueff, const Dims& d, double* alpha, double* beta,
+                          double* logP, float* costs, hipStream_t st);
+
+// Untiled backward: logits [B, Tpad, U1pad, V] turned into logit gradients
+// in place.
+hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, hipStream_t st);
+
+// dh = dz @ W_out^T for one chunk; dpre = (1 - h^2) dh summed into d_enc over
+// u and into d_pred over t.
+struct DhArgs {
+  const void* g;      // [B, CT, CU, V] logit gradients of the chunk
+  const void* W;      // [H, V]
+  const void* enc;
+  const void* pred;
+  const int32_t* Teff;
+  const int32_t* Ueff;
+  Dims d;
+  int ct0, cu0, CT, CU, n_tu;
+  float* d_enc;
+  float* d_pred;
+};
+hipError_t launch_dh(const DhArgs& a, bool bf16, hipStream_t st);
+
+// d_W_out += h^T dz and d_b_out += column sums of dz over one chunk.
+struct DwArgs {
+  const void* g;
+  const void* enc;
+  const void* pred;
+  const int32_t* Teff;
+  const int32_t* Ueff;
+  Dims d;
+  int ct0, cu0, CT, CU;
+  float* d_W;
+  float* d_b;
+};
+hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st);
+
+}  // namespace rnntj

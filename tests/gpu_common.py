@@ -1,0 +1,64 @@
+"""Helpers shared by the GPU tests: move synth inputs to the GPU, run the HIP
+path through the C ABI binding, and compare with the float64 oracle."""
+from __future__ import annotations
+
+import numpy as np
+
+# the benchmark spec tolerances: fp32 |dloss|/loss <= 1e-5 and grad abs err <= 1e-4;
+# bf16 2e-2 relative (loss per utterance, gradients as max-abs error over the
+# tensor's max-abs value).
+FP32_LOSS_REL = 1e-5
+FP32_GRAD_ABS = 1e-4
+BF16_REL = 2e-2
+
+
+def to_device(inp, device="cuda"):
+    import torch
+    if inp.dtype == "fp32":
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to(device)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+    return dict(enc=conv(inp.enc), pred=conv(inp.pred), W_out=conv(inp.W), b_out=conv(inp.b),
+                labels=i32(inp.labels), T_lens=i32(inp.T_lens), U_lens=i32(inp.U_lens))
+
+
+def run_gpu(inp, tile_t=0, tile_u=0, tile_v=0, grad_costs=None, dev=None, bwd=True):
+    import torch
+    import rnn_joint_transducer_amd as rj
+    dev = dev or to_device(inp)
+    costs, saved = rj.rnnt_joint_loss_fwd(**dev, blank=inp.blank, tile_t=tile_t,
+                                          tile_u=tile_u, tile_v=tile_v)
+    out = dict(costs=costs)
+    if bwd:
+        gc = None if grad_costs is None else torch.tensor(grad_costs, dtype=torch.float32,
+                                                          device=costs.device)
+        d_enc, d_pred, d_W, d_b = rj.rnnt_joint_loss_bwd(**dev, saved=saved, blank=inp.blank,
+                                                         tile_t=tile_t, tile_u=tile_u,
+                                                         tile_v=tile_v, grad_costs=gc)
+        out.update(dEnc=d_enc, dPred=d_pred, dW=d_W, db=d_b)
+    out["status"] = rj.rnnt_joint_loss_status(saved)
+    return {k: (v.cpu().double().numpy() if hasattr(v, "cpu") else v) for k, v in out.items()}
+
+
+def check_costs(gpu, ref, dtype, idx=None):
+    idx = range(len(ref)) if idx is None else idx
+    tol = FP32_LOSS_REL if dtype == "fp32" else BF16_REL
+    worst = 0.0
+    for k, b in enumerate(idx):
+        r = abs(gpu[b] - ref[k]) / abs(ref[k])
+        worst = max(worst, r)
+        assert r <= tol, f"utt {b}: gpu {gpu[b]} oracle {ref[k]} rel {r:.3e} > {tol}"
+    return worst
+
+
+def check_grad(name, gpu, ref, dtype):
+    err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    if dtype == "fp32":
+        assert err <= FP32_GRAD_ABS, f"{name}: max abs err {err:.3e} > {FP32_GRAD_ABS}"
+        return err
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    rel = err / scale if scale > 0 else err
+    assert rel <= BF16_REL, f"{name}: rel err {rel:.3e} > {BF16_REL} (abs {err:.3e})"
+    return rel

@@ -1,0 +1,198 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Small workloads are compared element by element on every output; the large
+workloads (at their full sizes and in the tiling the benchmark uses) are
+compared on sampled utterances the oracle computes one by one, on a
+two-utterance sub-batch for the weight gradients, and on closed forms that
+hold at any size.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import rnnt
+from synth import make_config, make_inputs
+
+from gpu_common import BF16_REL, check_costs, check_grad, run_gpu, to_device
+
+pytestmark = pytest.mark.gpu
+
+WORKERS = min(16, os.cpu_count() or 1)
+
+
+def _oracle_full(inp, grad_costs=None):
+    return oracle.loss_and_grads(inp.enc_f64, inp.pred_f64, inp.W_f64, inp.b_f64, inp.labels,
+                                 inp.T_lens, inp.U_lens, inp.blank, grad_costs=grad_costs,
+                                 workers=min(WORKERS, inp.B))
+
+
+def _compare_all(inp, g, ref):
+    check_costs(g["costs"], ref["costs"], inp.dtype)
+    check_grad("d_enc", g["dEnc"], ref["dEnc"], inp.dtype)
+    check_grad("d_pred", g["dPred"], ref["dPred"], inp.dtype)
+    check_grad("d_W_out", g["dW"], ref["dW"], inp.dtype)
+    check_grad("d_b_out", g["db"], ref["db"], inp.dtype)
+
+
+# ------------------------------------------------------------------ small, every output
+
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0), (0, 8, 128)])
+def test_tiny(tiles):
+    inp = make_config("tiny")
+    print(f"[tiny tiles={tiles}]", flush=True)
+    g = run_gpu(inp, *tiles)
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp))
+
+
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (64, 64, 128), (16, 8, 0)])
+def test_short(tiles):
+    inp = make_config("short")
+    print(f"[short tiles={tiles}]", flush=True)
+    g = run_gpu(inp, *tiles)
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ragged_edges(dtype):
+    """T not a multiple of 16, U+1 not a multiple of 8, V not a multiple of
+    128, a one-frame utterance, an utterance without labels, H = 48."""
+    inp = make_inputs(5, 37, 11, 48, 40, dtype=dtype, sigma=0.4, seed=3, t_range=(1, 37),
+                      u_range=(0, 11))
+    inp.T_lens[:] = [37, 1, 20, 5, 33]
+    inp.U_lens[:] = [11, 4, 0, 11, 7]
+    ref = _oracle_full(inp, grad_costs=[1.0, 0.5, 2.0, -1.0, 0.0])
+    for tiles in [(0, 0, 0), (16, 8, 0), (32, 16, 0)]:
+        print(f"[ragged {dtype} tiles={tiles}]", flush=True)
+        g = run_gpu(inp, *tiles, grad_costs=[1.0, 0.5, 2.0, -1.0, 0.0])
+        _compare_all(inp, g, ref)
+        # gradients past each utterance's lengths are exactly zero
+        for b in range(inp.B):
+            assert np.all(g["dEnc"][b, inp.T_lens[b]:] == 0)
+            assert np.all(g["dPred"][b, inp.U_lens[b] + 1:] == 0)
+
+
+def test_data_errors_flagged():
+    inp = make_inputs(4, 12, 5, 32, 24, sigma=0.4, seed=5, t_range=(4, 12), u_range=(1, 5))
+    good = make_inputs(4, 12, 5, 32, 24, sigma=0.4, seed=5, t_range=(4, 12), u_range=(1, 5))
+    inp.labels[1, 0] = 0          # a label equal to blank
+    inp.T_lens[2] = 13            # T' > T
+    g = run_gpu(inp)
+    assert g["status"] == 3
+    assert math.isnan(g["costs"][1]) and math.isnan(g["costs"][2])
+    assert np.all(g["dEnc"][1] == 0) and np.all(g["dEnc"][2] == 0)
+    assert np.all(g["dPred"][1] == 0) and np.all(g["dPred"][2] == 0)
+    # the valid utterances are untouched by their invalid neighbours
+    sub = [0, 3]
+    ref = oracle.loss_and_grads(good.enc_f64[sub], good.pred_f64[sub], good.W_f64, good.b_f64,
+                                good.labels[sub], good.T_lens[sub], good.U_lens[sub], 0)
+    check_costs(g["costs"], ref["costs"], "fp32", idx=sub)
+    check_grad("d_enc", g["dEnc"][sub], ref["dEnc"], "fp32")
+    check_grad("d_W_out", g["dW"], ref["dW"], "fp32")
+
+
+def test_tile_invariance_short():
+    inp = make_config("short")
+    base = run_gpu(inp, 0, 0, 0)
+    for tiles in [(32, 16, 0), (0, 24, 0), (208, 56, 128)]:
+        g = run_gpu(inp, *tiles)
+        np.testing.assert_allclose(g["costs"], base["costs"], rtol=2e-6)
+        for k in ("dEnc", "dPred", "dW", "db"):
+            np.testing.assert_allclose(g[k], base[k], atol=2e-6, rtol=1e-4)
+
+
+def test_autograd_wrapper():
+    import torch
+    import rnn_joint_transducer_amd as rj
+    inp = make_config("tiny")
+    dev = to_device(inp)
+    for k in ("enc", "pred", "W_out", "b_out"):
+        dev[k].requires_grad_(True)
+    costs = rj.rnnt_joint_loss(**dev, tile_t=16, tile_u=8)
+    (costs * torch.tensor([1.0, 3.0], device=costs.device)).sum().backward()
+    ref = _oracle_full(inp, grad_costs=[1.0, 3.0])
+    check_grad("d_enc", dev["enc"].grad.double().cpu().numpy(), ref["dEnc"], "fp32")
+    check_grad("d_W_out", dev["W_out"].grad.double().cpu().numpy(), ref["dW"], "fp32")
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _sampled(inp, tiles, cost_utts, grad_utts):
+    g = run_gpu(inp, *tiles)
+    assert g["status"] == 0
+    refc = []
+    for b in cost_utts:
+        refc.append(rnnt.loss_only(inp.enc_f64[b:b + 1], inp.pred_f64[b:b + 1], inp.W_f64,
+                                   inp.b_f64, inp.labels[b:b + 1], inp.T_lens[b:b + 1],
+                                   inp.U_lens[b:b + 1], 0)[0])
+    check_costs(g["costs"], refc, inp.dtype, idx=cost_utts)
+    for b in grad_utts:
+        o = rnnt.utterance_loss_and_grads(inp.enc_f64[b], inp.pred_f64[b], inp.W_f64, inp.b_f64,
+                                          inp.labels[b], int(inp.T_lens[b]),
+                                          int(inp.U_lens[b]), 0)
+        Tl, Ul = int(inp.T_lens[b]), int(inp.U_lens[b])
+        check_grad(f"d_enc[{b}]", g["dEnc"][b, :Tl], o["dEnc"], inp.dtype)
+        check_grad(f"d_pred[{b}]", g["dPred"][b, :Ul + 1], o["dPred"], inp.dtype)
+    return g
+
+
+def _sub_batch_weights(inp, tiles, utts):
+    """Weight gradients of a two-utterance sub-batch at the full H, V, T, U."""
+    from synth import Inputs
+    import dataclasses
+    sub = dataclasses.replace(
+        inp, B=len(utts), enc=inp.enc[utts], pred=inp.pred[utts], labels=inp.labels[utts],
+        T_lens=inp.T_lens[utts], U_lens=inp.U_lens[utts], enc_f64=inp.enc_f64[utts],
+        pred_f64=inp.pred_f64[utts])
+    g = run_gpu(sub, *tiles)
+    ref = _oracle_full(sub)
+    check_costs(g["costs"], ref["costs"], inp.dtype)
+    check_grad("d_W_out(sub)", g["dW"], ref["dW"], inp.dtype)
+    check_grad("d_b_out(sub)", g["db"], ref["db"], inp.dtype)
+
+
+@pytest.mark.parametrize("tiles", [(64, 64, 0), (0, 0, 0)])
+def test_medium(tiles):
+    inp = make_config("medium")
+    print(f"[medium tiles={tiles}]", flush=True)
+    _sampled(inp, tiles, cost_utts=[0, 7, 15], grad_utts=[7])
+    _sub_batch_weights(inp, tiles, [3, 11])
+
+
+def test_medium_large_vocab():
+    inp = make_config("medium_lv")
+    print("[medium_lv]", flush=True)
+    _sampled(inp, (64, 64, 128), cost_utts=[2, 9], grad_utts=[9])
+
+
+def test_long_tiled():
+    inp = make_config("long")
+    b = int(np.argmin(inp.T_lens.astype(np.int64) * (inp.U_lens + 1)))
+    print(f"[long sampled utt {b}]", flush=True)
+    _sampled(inp, (64, 64, 128), cost_utts=[b], grad_utts=[])
+
+
+@pytest.mark.parametrize("name", ["medium", "long"])
+def test_zero_weights_closed_form_full_size(name):
+    """W_out = 0 at full size: cost = (T'+U') log V - log C(T'+U'-1, U'),
+    d_enc = d_pred = 0, d_b_out from label counts."""
+    inp = make_config(name)
+    inp.W = np.zeros_like(inp.W)
+    g = run_gpu(inp, *((64, 64, 128) if name == "long" else (0, 0, 0)))
+    V = inp.V
+    want = np.array([(Tl + Ul) * math.log(V) - math.log(math.comb(Tl + Ul - 1, Ul))
+                     for Tl, Ul in zip(inp.T_lens.tolist(), inp.U_lens.tolist())])
+    np.testing.assert_allclose(g["costs"], want, rtol=1e-5)
+    assert np.all(g["dEnc"] == 0) and np.all(g["dPred"] == 0)
+    want_db = np.zeros(V)
+    for b in range(inp.B):
+        Tl, Ul = int(inp.T_lens[b]), int(inp.U_lens[b])
+        want_db += (Tl + Ul) / V
+        want_db[0] -= Tl
+        np.add.at(want_db, inp.labels[b, :Ul], -1.0)
+    np.testing.assert_allclose(g["db"], want_db, atol=2e-2 * np.abs(want_db).max())
+    assert abs(g["db"].sum()) <= 1e-3 * np.abs(want_db).max()
