@@ -143,7 +143,7 @@ def main():
     saved = torch.empty(rj.rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tt, tu, tv),
                         dtype=torch.uint8, device=dev)
     wsb = rj.rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tt, tu, tv, 1)
-    ws = torch.empty(wsb, dtype=torch.uint8, device=dev) if wsb else None
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     costs = torch.empty(B, dtype=torch.float32, device=dev)
     grads = (torch.empty(B, T, H, device=dev), torch.empty(B, U + 1, H, device=dev),
              torch.empty(H, V, device=dev), torch.empty(V, device=dev))

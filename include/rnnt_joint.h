@@ -83,6 +83,10 @@ int rnnt_joint_loss_abi_version(void);
 /* Human-readable text for a status code; never NULL, static storage. */
 const char* rnnt_joint_loss_strerror(int code);
 
+/* Text naming the kernel launch and HIP error behind the calling thread's
+ * most recent RNNTJ_ERR_HIP ("" if none); never NULL, thread-local storage. */
+const char* rnnt_joint_loss_last_error(void);
+
 /*
  * Bytes of the forward -> backward state `saved` for these sizes and tiles.
  * saved holds the per-utterance validated lengths, log P and status, a
@@ -96,9 +100,10 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
 
 /*
  * Bytes of scratch `workspace` needed by the forward (pass = 0) or the
- * backward (pass = 1).  The forward needs none.  The tiled backward needs one
- * chunk of logit gradients [B, tile_t, tile_u, V] in dtype; the untiled
- * backward needs none.  Writes *out; returns a status code.
+ * backward (pass = 1).  The forward needs none.  The backward needs a float64
+ * accumulator for d_b_out [V] and, in the tiled mode, one chunk of logit
+ * gradients [B, tile_t, tile_u, V] in dtype.  Writes *out; returns a status
+ * code.
  */
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
                                     int tile_t, int tile_u, int tile_v, int pass,

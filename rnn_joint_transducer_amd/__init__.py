@@ -112,8 +112,10 @@ def rnnt_joint_loss_bwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, 
     dc = _dtype_code(enc)
     dev = enc.device
     ws = rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, 1)
-    if workspace is None and ws > 0:
+    if workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws:
+        raise ValueError(f"workspace too small ({workspace.numel()} < {ws})")
     if out is None:
         out = (torch.empty(B, T, H, dtype=torch.float32, device=dev),
                torch.empty(B, U + 1, H, dtype=torch.float32, device=dev),
@@ -128,7 +130,7 @@ def rnnt_joint_loss_bwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, 
                                     _ptr(labels), _ptr(T_lens), _ptr(U_lens), B, T, U, H, V,
                                     blank, tile_t, tile_u, tile_v, _ptr(grad_costs),
                                     _ptr(saved), _ptr(d_enc), _ptr(d_pred), _ptr(d_W),
-                                    _ptr(d_b), _ptr(workspace), ws if workspace is not None else 0,
+                                    _ptr(d_b), _ptr(workspace), workspace.numel(),
                                     _stream(dev))
     check(rc, "rnnt_joint_loss_bwd")
     return out

@@ -23,6 +23,7 @@ _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 _SIG = {
     "rnnt_joint_loss_abi_version": (_c_int, []),
     "rnnt_joint_loss_strerror": (ctypes.c_char_p, [_c_int]),
+    "rnnt_joint_loss_last_error": (ctypes.c_char_p, []),
     "rnnt_joint_loss_saved_bytes": (_c_int, [_c_int] * 9 + [ctypes.POINTER(_c_size)]),
     "rnnt_joint_loss_workspace_bytes": (_c_int, [_c_int] * 10 + [ctypes.POINTER(_c_size)]),
     "rnnt_joint_loss_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 9
@@ -43,6 +44,8 @@ class RNNTJointError(RuntimeError):
         msg = STATUS.get(code, str(code))
         try:
             msg += ": " + load().rnnt_joint_loss_strerror(code).decode()
+            if code == 4:
+                msg += " [" + load().rnnt_joint_loss_last_error().decode() + "]"
         except Exception:  # pragma: no cover
             pass
         super().__init__(f"{where} failed with {msg}")
@@ -56,6 +59,13 @@ def load(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise OSError(f"{path} is not built; run `python -m rnn_joint_transducer_amd.build` "
                       "(the HIP extension is required: there is no CPU fallback)")
+    # PyTorch ships its own HIP runtime under the same soname.  Load it first so
+    # that this library binds to that one: two HIP runtimes in one process do
+    # not share the device (the one loaded second sees none).
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # a plain C/ctypes user: /opt/rocm's runtime is used
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIG.items():
         fn = getattr(lib, name)

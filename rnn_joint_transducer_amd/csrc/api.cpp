@@ -34,6 +34,7 @@ struct Plan {
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_z;
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
+  size_t o_ws_db, o_ws_g;  // backward workspace layout
 };
 
 int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile_u, int tile_v,
@@ -79,7 +80,11 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   if (q.untiled) o = align_up(o + q.elem * (size_t)B * q.d.Tpad * q.d.U1pad * V);
   q.saved_bytes = o;
   q.ws_fwd = 0;
-  q.ws_bwd = q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V);
+  // backward workspace: float64 d_b_out accumulator [V], then (tiled) one
+  // chunk of logit gradients [B, CT, CU, V]
+  q.o_ws_db = 0;
+  q.o_ws_g = align_up(8 * (size_t)V);
+  q.ws_bwd = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
   return RNNTJ_OK;
 }
 
@@ -99,18 +104,32 @@ std::mutex g_timing_mu;
 bool g_timing = false;
 std::vector<TimedLaunch> g_timed;
 
+// description of the last failed launch on this thread (rnnt_joint_loss_last_error)
+thread_local char g_last_error[256] = "";
+
+hipError_t note_error(const char* name, hipError_t e) {
+  if (e != hipSuccess)
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s (%s)", name, hipGetErrorName(e),
+             hipGetErrorString(e));
+  return e;
+}
+
+// Launch through `launch` (which returns the HIP status of its launches); a
+// stale runtime error left by earlier, unrelated HIP calls is cleared first
+// so that it is not attributed to this library.
 template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
-  if (!g_timing) return launch();
+  (void)hipGetLastError();
+  if (!g_timing) return note_error(name, launch());
   TimedLaunch t{name, nullptr, nullptr};
   if (hipEventCreate(&t.start) != hipSuccess || hipEventCreate(&t.stop) != hipSuccess)
-    return hipErrorOutOfMemory;
+    return note_error(name, hipErrorOutOfMemory);
   hipEventRecord(t.start, st);
   const hipError_t e = launch();
   hipEventRecord(t.stop, st);
   std::lock_guard<std::mutex> lk(g_timing_mu);
   g_timed.push_back(t);
-  return e;
+  return note_error(name, e);
 }
 
 void drop_timed() {
@@ -248,8 +267,8 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   if (blank < 0 || blank >= V) return RNNTJ_ERR_ARG;
   if (misaligned(enc) || misaligned(pred) || misaligned(W_out) || misaligned(saved))
     return RNNTJ_ERR_ARG;
-  if (workspace_bytes < p.ws_bwd || (p.ws_bwd && !workspace)) return RNNTJ_ERR_WORKSPACE;
-  if (p.ws_bwd && misaligned(workspace)) return RNNTJ_ERR_ARG;
+  if (workspace_bytes < p.ws_bwd || !workspace) return RNNTJ_ERR_WORKSPACE;
+  if (misaligned(workspace)) return RNNTJ_ERR_ARG;
   p.d.blank = blank;
   hipStream_t st = static_cast<hipStream_t>(stream);
 
@@ -257,13 +276,15 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   int32_t* Ueff = at<int32_t>(saved, p.o_ueff);
   double* logP = at<double>(saved, p.o_logp);
   void* Wt = at<char>(saved, p.o_wt);
+  double* db64 = at<double>(workspace, p.o_ws_db);
+  void* gchunk = at<char>(workspace, p.o_ws_g);
 
   hipError_t e;
   if ((e = timed("zero", st, [&] {
          hipError_t r = launch_zero(d_enc, (size_t)B * T * H, st);
          if (r == hipSuccess) r = launch_zero(d_pred, (size_t)B * (U + 1) * H, st);
          if (r == hipSuccess) r = launch_zero(d_W_out, (size_t)H * V, st);
-         if (r == hipSuccess) r = launch_zero(d_b_out, (size_t)V, st);
+         if (r == hipSuccess) r = launch_zero(db64, 2 * (size_t)V, st);
          return r;
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
@@ -301,7 +322,10 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   w.Ueff = Ueff;
   w.d = p.d;
   w.d_W = d_W_out;
-  w.d_b = d_b_out;
+  w.d_b64 = db64;
+  auto finalize = [&] {
+    return timed("db_finalize", st, [&] { return launch_db_finalize(db64, d_b_out, V, st); });
+  };
 
   if (p.untiled) {
     void* z = at<char>(saved, p.o_z);
@@ -316,7 +340,7 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    return RNNTJ_OK;
+    return finalize() == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
   }
 
   // tiled: one lattice chunk of CT frames x CU label positions at a time
@@ -327,22 +351,22 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
       a.CT = p.CT;
       a.CU = p.CU;
       a.n_tu = p.CU / kTileU;
-      a.gout = workspace;
+      a.gout = gchunk;
       if ((e = timed("joint_grad", st, [&] {
              return launch_joint_tile(a, kGrad, p.bf16, (p.CT / kTileT) * a.n_tu, st);
            })) != hipSuccess)
         return RNNTJ_ERR_HIP;
-      h.g = workspace;
+      h.g = gchunk;
       h.ct0 = ct0; h.cu0 = cu0; h.CT = p.CT; h.CU = p.CU; h.n_tu = p.CU / kTileU;
       if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, st); })) != hipSuccess)
         return RNNTJ_ERR_HIP;
-      w.g = workspace;
+      w.g = gchunk;
       w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;
       if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
         return RNNTJ_ERR_HIP;
     }
   }
-  return RNNTJ_OK;
+  return finalize() == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
 }
 
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error) {
@@ -354,6 +378,8 @@ int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error)
   *data_error = v;
   return RNNTJ_OK;
 }
+
+const char* rnnt_joint_loss_last_error(void) { return g_last_error; }
 
 int rnnt_joint_loss_timing(int enable) {
   std::lock_guard<std::mutex> lk(g_timing_mu);

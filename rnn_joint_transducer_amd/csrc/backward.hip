@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   using C = DwCfg<T>;
   __shared__ __align__(16) T As[2][128 * C::LDK];  // h^T  [hidden][cell]
   __shared__ __align__(16) T Bs[2][128 * C::LDK];  // dz^T [vocab][cell]
-  __shared__ float dbs[16][128];
+  __shared__ double dbs[16][128];
   const Dims d = a.d;
   const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128, b = blockIdx.z;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
@@ -304,9 +304,9 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   const int mA = m0 + 8 * grp, nB = n0 + 8 * grp;
   float hv[2][8], gv[2][8];
   bool hok[2];
-  float dbacc[8];
+  double dbacc[8];  // float64: d_b_out[blank] reaches ~sum of T' and must keep 1e-4
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dbacc[i] = 0.f;
+  for (int i = 0; i < 8; ++i) dbacc[i] = 0.0;
 
   auto load_block = [&](int kb) {
     const int kt = a.ct0 + 4 * (kb / nub), ku = a.cu0 + 8 * (kb % nub);
@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
         *reinterpret_cast<uint32_t*>(&Bs[buf][(8 * grp + i) * C::LDK + 2 * cp]) =
             (uint32_t)f32_to_bf16(gv[0][i]) | ((uint32_t)f32_to_bf16(gv[1][i]) << 16);
       }
-      dbacc[i] += gv[0][i] + gv[1][i];
+      dbacc[i] += (double)gv[0][i] + (double)gv[1][i];
     }
   };
 
@@ -403,15 +403,25 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
     for (int i = 0; i < 8; ++i) dbs[cp][8 * grp + i] = dbacc[i];
     __syncthreads();
     if (tid < 128) {
-      float s = 0.f;
+      double s = 0.0;
 #pragma unroll
       for (int q = 0; q < 16; ++q) s += dbs[q][tid];
-      if (n0 + tid < d.V) atomicAdd(&a.d_b[n0 + tid], s);
+      if (n0 + tid < d.V) atomicAdd(&a.d_b64[n0 + tid], s);
     }
   }
 }
 
+__global__ void db_finalize_kernel(const double* __restrict__ src, float* __restrict__ dst, int V) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v < V) dst[v] = (float)src[v];
+}
+
 }  // namespace
+
+hipError_t launch_db_finalize(const double* db64, float* d_b, int V, hipStream_t st) {
+  hipLaunchKernelGGL(db_finalize_kernel, dim3((V + 255) / 256), dim3(256), 0, st, db64, d_b, V);
+  return hipGetLastError();
+}
 
 hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, hipStream_t st) {
   dim3 grid((a.d.Tpad / kTileT) * (a.d.U1pad / kTileU), a.d.B), block(256);

@@ -77,7 +77,7 @@ struct DhArgs {
 };
 hipError_t launch_dh(const DhArgs& a, bool bf16, hipStream_t st);
 
-// d_W_out += h^T dz and d_b_out += column sums of dz over one chunk.
+// d_W_out += h^T dz and d_b64 += column sums of dz (float64) over one chunk.
 struct DwArgs {
   const void* g;
   const void* enc;
@@ -87,8 +87,11 @@ struct DwArgs {
   Dims d;
   int ct0, cu0, CT, CU;
   float* d_W;
-  float* d_b;
+  double* d_b64;
 };
 hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st);
+
+// d_b[v] = (float) db64[v]
+hipError_t launch_db_finalize(const double* db64, float* d_b, int V, hipStream_t st);
 
 }  // namespace rnntj

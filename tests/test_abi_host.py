@@ -14,7 +14,7 @@ def test_exports_every_declared_symbol():
     names = _lib.declared_functions()
     assert set(names) == {"rnnt_joint_loss_abi_version", "rnnt_joint_loss_strerror",
                           "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
-                          "rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd",
+                          "rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd", "rnnt_joint_loss_last_error",
                           "rnnt_joint_loss_status", "rnnt_joint_loss_timing",
                           "rnnt_joint_loss_timing_report"}
     for n in names:
@@ -26,6 +26,7 @@ def test_version_and_strerror():
     for code in range(6):
         assert lib.rnnt_joint_loss_strerror(code)
     assert b"unknown" in lib.rnnt_joint_loss_strerror(99)
+    assert lib.rnnt_joint_loss_last_error() == b""
 
 
 def _saved(B, T, U, H, V, dt, tt=0, tu=0, tv=0):
@@ -50,8 +51,8 @@ def test_buffer_sizes():
     rc, untiled = _saved(16, 500, 100, 640, 1024, 1)
     assert rc == 0
     assert untiled - tiled >= 16 * 512 * 104 * 1024 * 2
-    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 16 * 64 * 64 * 1024 * 2)
-    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 0)
+    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + 16 * 64 * 64 * 1024 * 2)
+    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024)
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, 0, 0) == (0, 0)
 
 
@@ -110,9 +111,11 @@ def test_bwd_rejects_before_launch():
     # tiled mode needs a workspace
     rc = lib.rnnt_joint_loss_bwd(*base, 16, 8, 0, None, v(), v(), v(), v(), v(), None, 0, None)
     assert rc == 3
-    rc = lib.rnnt_joint_loss_bwd(*base, 0, 0, 0, None, None, v(), v(), v(), v(), None, 0, None)
+    rc = lib.rnnt_joint_loss_bwd(*base, 0, 0, 0, None, v(), v(), v(), v(), v(), None, 0, None)
+    assert rc == 3
+    rc = lib.rnnt_joint_loss_bwd(*base, 0, 0, 0, None, None, v(), v(), v(), v(), v(), 4096, None)
     assert rc == 1
-    rc = lib.rnnt_joint_loss_bwd(*base, 0, 0, 0, None, v(), v(), None, v(), v(), None, 0, None)
+    rc = lib.rnnt_joint_loss_bwd(*base, 0, 0, 0, None, v(), v(), None, v(), v(), v(), 4096, None)
     assert rc == 1
 
 

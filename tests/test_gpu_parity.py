@@ -102,7 +102,8 @@ def test_tile_invariance_short():
         g = run_gpu(inp, *tiles)
         np.testing.assert_allclose(g["costs"], base["costs"], rtol=2e-6)
         for k in ("dEnc", "dPred", "dW", "db"):
-            np.testing.assert_allclose(g[k], base[k], atol=2e-6, rtol=1e-4)
+            # float32 atomics sum in a different order per tiling
+            np.testing.assert_allclose(g[k], base[k], atol=2e-5, rtol=1e-4)
 
 
 def test_autograd_wrapper():
