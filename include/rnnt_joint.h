@@ -90,9 +90,10 @@ const char* rnnt_joint_loss_last_error(void);
 /*
  * Bytes of the forward -> backward state `saved` for these sizes and tiles.
  * saved holds the per-utterance validated lengths, log P and status, a
- * transposed copy of W_out, and per cell (diagonal-skewed [B, T+U, U+1]):
- * lse, LB, LE (float32) and alpha, beta (float64).  In the untiled mode it
- * also holds the logits [B, ceil16(T), ceil8(U+1), V] in dtype.
+ * transposed copy of W_out, e^{2 enc} and e^{2 pred} (float32), and per cell
+ * (diagonal-skewed [B, T+U, U+1]): lse, LB, LE (float32) and alpha, beta
+ * (float64).  In the untiled mode it also holds the logits
+ * [B, ceil16(T), ceil8(U+1), V] in dtype.
  * Writes *out; returns a status code.
  */
 int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
@@ -101,9 +102,10 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
 /*
  * Bytes of scratch `workspace` needed by the forward (pass = 0) or the
  * backward (pass = 1).  The forward needs none.  The backward needs a float64
- * accumulator for d_b_out [V] and, in the tiled mode, one chunk of logit
- * gradients [B, tile_t, tile_u, V] in dtype.  Writes *out; returns a status
- * code.
+ * accumulator for d_b_out [V], the joint activations h of one lattice chunk
+ * [B, tile_t, tile_u, H] in dtype (the whole padded lattice when untiled)
+ * and, in the tiled mode, that chunk's logit gradients [B, tile_t, tile_u, V]
+ * in dtype.  Writes *out; returns a status code.
  */
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
                                     int tile_t, int tile_u, int tile_v, int pass,

@@ -31,10 +31,11 @@ struct Plan {
   int CT, CU;  // backward chunk extents
   size_t elem;
   // saved layout (byte offsets)
-  size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_z;
+  size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
+      o_z;
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
-  size_t o_ws_db, o_ws_g;  // backward workspace layout
+  size_t o_ws_db, o_ws_g, o_ws_h;  // backward workspace layout
 };
 
 int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile_u, int tile_v,
@@ -76,15 +77,20 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_le = o;     o = align_up(o + 4 * cells);
   q.o_alpha = o;  o = align_up(o + 8 * cells);
   q.o_beta = o;   o = align_up(o + 8 * cells);
+  q.o_E = o;      o = align_up(o + 4 * (size_t)B * T * H);
+  q.o_P = o;      o = align_up(o + 4 * (size_t)B * (U + 1) * H);
   q.o_z = o;
   if (q.untiled) o = align_up(o + q.elem * (size_t)B * q.d.Tpad * q.d.U1pad * V);
   q.saved_bytes = o;
   q.ws_fwd = 0;
   // backward workspace: float64 d_b_out accumulator [V], then (tiled) one
   // chunk of logit gradients [B, CT, CU, V]
+  // joint activations h of the chunk [B, CT, CU, H] (the whole lattice when
+  // untiled)
   q.o_ws_db = 0;
   q.o_ws_g = align_up(8 * (size_t)V);
-  q.ws_bwd = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
+  q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
+  q.ws_bwd = q.o_ws_h + align_up(q.elem * (size_t)B * q.CT * q.CU * H);
   return RNNTJ_OK;
 }
 
@@ -215,6 +221,12 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
          return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
+  float* Eexp = at<float>(saved, p.o_E);
+  float* Pexp = at<float>(saved, p.o_P);
+  if ((e = timed("prep", st, [&] {
+         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Eexp, Pexp, status, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
   if ((e = timed("transpose", st, [&] { return launch_transpose(W_out, Wt, H, V, p.bf16, st); })) !=
       hipSuccess)
     return RNNTJ_ERR_HIP;
@@ -227,6 +239,10 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
   a.labels = labels;
   a.Teff = Teff;
   a.Ueff = Ueff;
+  a.hdr = status;
+  a.Eexp = Eexp;
+  a.Pexp = Pexp;
+  a.vsplit = 1;
   a.d = p.d;
   a.ct0 = 0;
   a.cu0 = 0;
@@ -278,6 +294,7 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   void* Wt = at<char>(saved, p.o_wt);
   double* db64 = at<double>(workspace, p.o_ws_db);
   void* gchunk = at<char>(workspace, p.o_ws_g);
+  void* hchunk = at<char>(workspace, p.o_ws_h);
 
   hipError_t e;
   if ((e = timed("zero", st, [&] {
@@ -297,6 +314,9 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   a.labels = labels;
   a.Teff = Teff;
   a.Ueff = Ueff;
+  a.hdr = at<int32_t>(saved, p.o_status);
+  a.Eexp = at<float>(saved, p.o_E);
+  a.Pexp = at<float>(saved, p.o_P);
   a.d = p.d;
   a.lse = at<float>(saved, p.o_lse);
   a.LB = at<float>(saved, p.o_lb);
@@ -312,12 +332,14 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   h.pred = pred;
   h.Teff = Teff;
   h.Ueff = Ueff;
+  h.hdr = a.hdr;
+  h.Eexp = a.Eexp;
+  h.Pexp = a.Pexp;
   h.d = p.d;
   h.d_enc = d_enc;
   h.d_pred = d_pred;
   DwArgs w = {};
-  w.enc = enc;
-  w.pred = pred;
+  w.h = hchunk;
   w.Teff = Teff;
   w.Ueff = Ueff;
   w.d = p.d;
@@ -338,12 +360,22 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
       return RNNTJ_ERR_HIP;
     w.g = z;
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
+    if ((e = timed("hrow", st, [&] { return launch_hrow(hchunk, p.bf16, a, st); })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
     return finalize() == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
   }
 
-  // tiled: one lattice chunk of CT frames x CU label positions at a time
+  // tiled: one lattice chunk of CT frames x CU label positions at a time.
+  // The logit-gradient kernel splits the vocabulary tiles of each cell tile
+  // over several workgroups when a chunk alone has too few cell tiles to
+  // give every compute unit (256 on gfx950) about four of them.
+  const int chunk_tiles = B * (p.CT / kTileT) * (p.CU / kTileU);
+  const int nvt = (V + kVocabTile - 1) / kVocabTile;
+  int vsplit = 1;
+  while (vsplit < nvt && chunk_tiles * vsplit < 1024) vsplit *= 2;
+  if (vsplit > nvt) vsplit = nvt;
   for (int ct0 = 0; ct0 < p.d.Tpad; ct0 += p.CT) {
     for (int cu0 = 0; cu0 < p.d.U1pad; cu0 += p.CU) {
       a.ct0 = ct0;
@@ -351,7 +383,9 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
       a.CT = p.CT;
       a.CU = p.CU;
       a.n_tu = p.CU / kTileU;
+      a.vsplit = vsplit;
       a.gout = gchunk;
+      a.hout = hchunk;
       if ((e = timed("joint_grad", st, [&] {
              return launch_joint_tile(a, kGrad, p.bf16, (p.CT / kTileT) * a.n_tu, st);
            })) != hipSuccess)

@@ -15,10 +15,11 @@
 //                         (1 - h^2) epilogue and the two lattice reductions
 //                         done in registers before float32 atomics.
 //   dw_kernel           : MFMA GEMM h^T[H, cells] x dz[cells, V] split over
-//                         utterances (split-K), h rebuilt from enc/pred and
-//                         both operands transposed while staged through LDS;
-//                         the hidden-row-0 workgroups also sum dz columns
-//                         into db_out.
+//                         utterances (split-K); h and dz rows are staged
+//                         row-major and read with transposing LDS loads; the
+//                         hidden-row-0 workgroups also sum dz columns into
+//                         db_out (float64).
+//   hrow_kernel         : untiled mode, h = tanh(enc + pred) rows for dw.
 #include <type_traits>
 
 #include "common.h"
@@ -206,6 +207,7 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs a) {
   // ---- epilogue: dpre = (1 - h^2) * dh, h rebuilt from enc / pred
   const T* enc = static_cast<const T*>(a.enc);
   const T* pred = static_cast<const T*>(a.pred);
+  const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
   // wave rows: 64*wm + 32*i + acc_row(r, kh)  <->  tt = 8*wm + 4*i + r/4, uu = 4*kh + r%4
   float pred_sum[2][4];  // [j][r%4]: sum over this wave's frames, per label position
 #pragma unroll
@@ -222,15 +224,19 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs a) {
       for (int q4 = 0; q4 < 4; ++q4) {  // frame within the 32-row block
         const int t = t0 + 8 * wm + 4 * i + q4;
         float enc_sum = 0.f;
-        const float ev = (nvalid && t < Tl) ? ElemTraits<T>::to_f32(enc[((size_t)b * d.T + t) * d.H + n]) : 0.f;
+        const bool tn = nvalid && t < Tl;
+        const size_t ie = ((size_t)b * d.T + t) * d.H + n;
+        const float ev = tn ? (use_ep ? a.Eexp[ie] : ElemTraits<T>::to_f32(enc[ie])) : 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {  // label position within the half
           const int r = 4 * q4 + q;
           const int u = u0 + 4 * kh + q;
           float v = 0.f;
-          if (nvalid && t < Tl && u <= Ul) {
-            const float pv = ElemTraits<T>::to_f32(pred[((size_t)b * d.U1 + u) * d.H + n]);
-            const float h = fast_tanh(ev + pv);
+          if (tn && u <= Ul) {
+            const size_t ip = ((size_t)b * d.U1 + u) * d.H + n;
+            const float h = use_ep
+                                ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + ev * a.Pexp[ip])
+                                : fast_tanh(ev + ElemTraits<T>::to_f32(pred[ip]));
             v = (1.0f - h * h) * acc[i][j][r];
           }
           enc_sum += v;
@@ -258,95 +264,85 @@ __global__ __launch_bounds__(256) void dh_kernel(DhArgs a) {
 
 // ------------------------------------------------------------ dW GEMM
 
-// K block = 32 cells = 4 frames x 8 label positions.
-constexpr int kDwK = 32;
-
+// d_W_out[m0:m0+128, n0:n0+128] += h^T dz over the valid cells of one
+// utterance in the chunk.  h rows [cell][H] and dz rows [cell][V] are staged
+// row-major (16-byte copies) and read as MFMA operands with load_frag_T, so
+// neither operand is transposed in memory.  K block = 8 frames x 8 label
+// positions (bf16) or 4 x 8 (fp32) of one 16x8 cell tile.
 template <typename T>
 struct DwCfg {
-  static constexpr int PAD = 16 / (int)sizeof(T);
-  static constexpr int LDK = kDwK + PAD;  // bf16: 80 B rows, fp32: 144 B rows
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int KB = kBf16 ? 64 : 32;           // cells per stage
+  static constexpr int LD = 128 + (kBf16 ? 16 : 4);    // LDS row (elements): 288 B / 528 B
+  static constexpr int CE = 16 / (int)sizeof(T);       // elements per 16-byte chunk
+  static constexpr int CPR = 128 / CE;                 // chunks per staged row
+  static constexpr int CH = KB * CPR / 256;            // chunks per thread per operand
+  static constexpr int SPT = kTileCells / KB;          // stages per cell tile
 };
-
-template <typename T>
-__device__ __forceinline__ bool dw_cell(const DwArgs& a, int Tl, int Ul, int kt, int ku, int c,
-                                        int& t, int& u) {
-  t = kt + (c >> 3);
-  u = ku + (c & 7);
-  return t < Tl && t < a.ct0 + a.CT && u <= Ul && u < a.cu0 + a.CU;
-}
 
 template <typename T>
 __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   using C = DwCfg<T>;
-  __shared__ __align__(16) T As[2][128 * C::LDK];  // h^T  [hidden][cell]
-  __shared__ __align__(16) T Bs[2][128 * C::LDK];  // dz^T [vocab][cell]
-  __shared__ double dbs[16][128];
+  __shared__ __align__(16) T As[2][C::KB * C::LD];  // h  [cell][hidden]
+  __shared__ __align__(16) T Bs[2][C::KB * C::LD];  // dz [cell][vocab]
+  __shared__ double dbw[4][128];
   const Dims d = a.d;
   const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128, b = blockIdx.z;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  const int nt = min(a.CT, Tl - a.ct0);
-  const int nu = min(a.CU, Ul + 1 - a.cu0);
-  if (nt <= 0 || nu <= 0) return;
-  const int ntb = (nt + 3) / 4, nub = (nu + 7) / 8;
-  const int nkb = ntb * nub;
+  // valid cell tiles of this utterance inside the chunk form a rectangle
+  const int tv = min(a.CT, Tl - a.ct0), uv = min(a.CU, Ul + 1 - a.cu0);
+  if (tv <= 0 || uv <= 0) return;
+  const int ntt = (tv + kTileT - 1) / kTileT, ntu = (uv + kTileU - 1) / kTileU;
+  const int nstage = ntt * ntu * C::SPT;
+  const int n_tu = a.CU / kTileU;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kh = lane >> 5, lc = lane & 31;
+  const int kh = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
   const bool do_db = (blockIdx.y == 0);
+  const T* hsrc = static_cast<const T*>(a.h);
+  const T* gsrc = static_cast<const T*>(a.g);
+  // this thread's staging chunks: row = c / CPR, column chunk = c % CPR
+  // (c = tid + 256 q, so the column chunk is the same for every q)
+  const int ccol = (tid % C::CPR) * C::CE;
+  const bool mok = m0 + ccol < d.H, nok = n0 + ccol < d.V;
+  double dbacc[C::CE];
+#pragma unroll
+  for (int i = 0; i < C::CE; ++i) dbacc[i] = 0.0;
 
-  const T* enc = static_cast<const T*>(a.enc);
-  const T* pred = static_cast<const T*>(a.pred);
-  const T* g = static_cast<const T*>(a.g);
-
-  // staging role: cell pair cp (cells 2cp, 2cp+1 of the K block), group of
-  // 8 hidden rows (A) / 8 vocabulary columns (B)
-  const int cp = tid & 15, grp = tid >> 4;
-  const int mA = m0 + 8 * grp, nB = n0 + 8 * grp;
-  float hv[2][8], gv[2][8];
-  bool hok[2];
-  double dbacc[8];  // float64: d_b_out[blank] reaches ~sum of T' and must keep 1e-4
+  u32x4 ra[C::CH], rb[C::CH];
+  auto load_stage = [&](int s) {
+    const int tile = s / C::SPT, part = s % C::SPT;
+    const int t0 = a.ct0 + (tile / ntu) * kTileT + part * (C::KB / kTileU);
+    const int u0 = a.cu0 + (tile % ntu) * kTileU;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) dbacc[i] = 0.0;
-
-  auto load_block = [&](int kb) {
-    const int kt = a.ct0 + 4 * (kb / nub), ku = a.cu0 + 8 * (kb % nub);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      int t, u;
-      const bool ok = dw_cell<T>(a, Tl, Ul, kt, ku, 2 * cp + e, t, u);
-      hok[e] = ok && mA < d.H;
-      if (hok[e]) {
-        Frag8<T> fe = load_frag(enc + ((size_t)b * d.T + t) * d.H + mA);
-        Frag8<T> fp = load_frag(pred + ((size_t)b * d.U1 + u) * d.H + mA);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hv[e][i] = fe.get(i) + fp.get(i);  // tanh applied at store
-      }
-      if (ok && nB < d.V) {
-        Frag8<T> fg = load_frag(g + (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * d.V + nB);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gv[e][i] = fg.get(i);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gv[e][i] = 0.f;
-      }
+    for (int q = 0; q < C::CH; ++q) {
+      const int row = (tid + 256 * q) / C::CPR;
+      const int t = t0 + row / kTileU, u = u0 + row % kTileU;
+      const bool ok = t < Tl && u <= Ul;
+      const size_t crow = ((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0);
+      ra[q] = (ok && mok) ? *reinterpret_cast<const u32x4*>(hsrc + crow * d.H + m0 + ccol)
+                          : u32x4{0u, 0u, 0u, 0u};
+      rb[q] = (ok && nok) ? *reinterpret_cast<const u32x4*>(gsrc + crow * d.V + n0 + ccol)
+                          : u32x4{0u, 0u, 0u, 0u};
     }
+    (void)n_tu;
   };
-  auto store_block = [&](int buf) {
+  auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float h0 = hok[0] ? fast_tanh(hv[0][i]) : 0.f;
-      const float h1 = hok[1] ? fast_tanh(hv[1][i]) : 0.f;
-      if constexpr (std::is_same<T, float>::value) {
-        *reinterpret_cast<float2*>(&As[buf][(8 * grp + i) * C::LDK + 2 * cp]) = float2{h0, h1};
-        *reinterpret_cast<float2*>(&Bs[buf][(8 * grp + i) * C::LDK + 2 * cp]) =
-            float2{gv[0][i], gv[1][i]};
-      } else {
-        *reinterpret_cast<uint32_t*>(&As[buf][(8 * grp + i) * C::LDK + 2 * cp]) =
-            (uint32_t)f32_to_bf16(h0) | ((uint32_t)f32_to_bf16(h1) << 16);
-        *reinterpret_cast<uint32_t*>(&Bs[buf][(8 * grp + i) * C::LDK + 2 * cp]) =
-            (uint32_t)f32_to_bf16(gv[0][i]) | ((uint32_t)f32_to_bf16(gv[1][i]) << 16);
+    for (int q = 0; q < C::CH; ++q) {
+      const int row = (tid + 256 * q) / C::CPR;
+      *reinterpret_cast<u32x4*>(&As[buf][row * C::LD + ccol]) = ra[q];
+      *reinterpret_cast<u32x4*>(&Bs[buf][row * C::LD + ccol]) = rb[q];
+      if (do_db) {
+        Frag8<T> f;
+        if constexpr (C::kBf16) {
+          f.v = rb[q];
+        } else {
+          f.lo = __builtin_bit_cast(f32x4, rb[q]);
+        }
+#pragma unroll
+        for (int i = 0; i < C::CE; ++i) dbacc[i] += (double)f.get(i);
       }
-      dbacc[i] += (double)gv[0][i] + (double)gv[1][i];
     }
   };
 
@@ -358,28 +354,26 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  load_block(0);
-  store_block(0);
+  load_stage(0);
+  store_stage(0);
   __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int cur = kb & 1;
-    const bool has_next = kb + 1 < nkb;
-    if (has_next) load_block(kb + 1);
+  for (int s = 0; s < nstage; ++s) {
+    const int cur = s & 1;
+    const bool has_next = s + 1 < nstage;
+    if (has_next) load_stage(s + 1);
 #pragma unroll
-    for (int kk = 0; kk < kDwK / 16; ++kk) {
+    for (int kk = 0; kk < C::KB / 16; ++kk) {
       Frag8<T> fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = load_frag(&As[cur][(64 * wm + 32 * i + lc) * C::LDK + kk * 16 + 8 * kh]);
+      for (int i = 0; i < 2; ++i) fa[i] = load_frag_T(As[cur], C::LD, kk * 16, 64 * wm + 32 * i);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = load_frag(&Bs[cur][(64 * wn + 32 * j + lc) * C::LDK + kk * 16 + 8 * kh]);
+      for (int j = 0; j < 2; ++j) fb[j] = load_frag_T(Bs[cur], C::LD, kk * 16, 64 * wn + 32 * j);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma_step(acc[i][j], fa[i], fb[j]);
     }
-    if (has_next) store_block(cur ^ 1);
+    if (has_next) store_stage(cur ^ 1);
     __syncthreads();
   }
 
@@ -387,7 +381,7 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int n = n0 + 64 * wn + 32 * j + lc;
+      const int n = n0 + 64 * wn + 32 * j + (lane & 31);
       if (n < d.V) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -398,16 +392,62 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
     }
 
   if (do_db) {
-    // dbacc of the 16 cell-pair threads sharing a column group
+    // threads with equal tid % CPR share columns: 4 per wave for bf16
+    // (CPR = 16), 2 per wave for fp32 (CPR = 32); then across the 4 waves
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dbs[cp][8 * grp + i] = dbacc[i];
-    __syncthreads();
-    if (tid < 128) {
-      double s = 0.0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) s += dbs[q][tid];
-      if (n0 + tid < d.V) atomicAdd(&a.d_b64[n0 + tid], s);
+    for (int i = 0; i < C::CE; ++i) {
+      double v = dbacc[i];
+      for (int off = C::CPR; off < 64; off <<= 1) v += __shfl_xor(v, off);
+      dbacc[i] = v;
     }
+    if (lane < C::CPR) {
+#pragma unroll
+      for (int i = 0; i < C::CE; ++i) dbw[w][ccol + i] = dbacc[i];
+    }
+    __syncthreads();
+    if (tid < 128 && n0 + tid < d.V)
+      atomicAdd(&a.d_b64[n0 + tid], dbw[0][tid] + dbw[1][tid] + dbw[2][tid] + dbw[3][tid]);
+  }
+}
+
+// h rows of every valid cell of the lattice ([B, Tpad, U1pad, H], untiled
+// backward): h = tanh(enc[b,t] + pred[b,u]); rows of invalid cells are zero.
+template <typename T>
+__global__ __launch_bounds__(256) void hrow_kernel(JointArgs a, T* __restrict__ hout) {
+  const Dims d = a.d;
+  const int b = blockIdx.y;
+  const int n_tu = d.U1pad / kTileU;
+  const int t0 = (blockIdx.x / n_tu) * kTileT;
+  const int u0 = (blockIdx.x % n_tu) * kTileU;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  if (t0 >= Tl || u0 > Ul) return;
+  const T* enc = static_cast<const T*>(a.enc);
+  const T* pred = static_cast<const T*>(a.pred);
+  const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
+  const int cpr = d.H / 8;
+  for (int c = threadIdx.x; c < kTileCells * cpr; c += 256) {
+    const int row = c / cpr, k0 = (c % cpr) * 8;
+    const int t = t0 + (row >> 3), u = u0 + (row & 7);
+    T* hp = hout + (((size_t)b * d.Tpad + t) * d.U1pad + u) * d.H + k0;
+    Frag8<T> f;
+    if (t < Tl && u <= Ul) {
+      const size_t ie = ((size_t)b * d.T + t) * d.H + k0, ip = ((size_t)b * d.U1 + u) * d.H + k0;
+      float x[8];
+      if (use_ep) {
+        const Frag8<float> e = load_frag(a.Eexp + ie), p = load_frag(a.Pexp + ip);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          x[i] = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e.get(i) * p.get(i));
+      } else {
+        const Frag8<T> e = load_frag(enc + ie), p = load_frag(pred + ip);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fast_tanh(e.get(i) + p.get(i));
+      }
+      pack_frag(f, x);
+    } else {
+      zero_frag(f);
+    }
+    store_frag(hp, f);
   }
 }
 
@@ -420,6 +460,15 @@ __global__ void db_finalize_kernel(const double* __restrict__ src, float* __rest
 
 hipError_t launch_db_finalize(const double* db64, float* d_b, int V, hipStream_t st) {
   hipLaunchKernelGGL(db_finalize_kernel, dim3((V + 255) / 256), dim3(256), 0, st, db64, d_b, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st) {
+  dim3 grid((a.d.Tpad / kTileT) * (a.d.U1pad / kTileU), a.d.B), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(hrow_kernel<uint16_t>, grid, block, 0, st, a, static_cast<uint16_t*>(h));
+  else
+    hipLaunchKernelGGL(hrow_kernel<float>, grid, block, 0, st, a, static_cast<float*>(h));
   return hipGetLastError();
 }
 

@@ -58,6 +58,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// float -> bf16 bits with the hardware round-to-nearest-even conversion
+// (v_cvt_pk_bf16_f32 on gfx950; NaN stays NaN)
+__device__ __forceinline__ uint16_t f32_to_bf16_hw(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<float> {
   static __device__ __forceinline__ float load(const float* p) { return *p; }
@@ -66,7 +72,7 @@ template <> struct ElemTraits<float> {
 };
 template <> struct ElemTraits<uint16_t> {
   static __device__ __forceinline__ float to_f32(uint16_t x) { return bf16_to_f32(x); }
-  static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_bf16(x); }
+  static __device__ __forceinline__ uint16_t from_f32(float x) { return f32_to_bf16_hw(x); }
 };
 
 // Eight consecutive elements along the contraction axis: one MFMA operand
@@ -111,7 +117,7 @@ __device__ __forceinline__ void zero_frag(Frag8<float>& f) {
 __device__ __forceinline__ void pack_frag(Frag8<uint16_t>& f, const float* x) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    f.v[i] = (uint32_t)f32_to_bf16(x[2 * i]) | ((uint32_t)f32_to_bf16(x[2 * i + 1]) << 16);
+    f.v[i] = (uint32_t)f32_to_bf16_hw(x[2 * i]) | ((uint32_t)f32_to_bf16_hw(x[2 * i + 1]) << 16);
 }
 __device__ __forceinline__ void pack_frag(Frag8<float>& f, const float* x) {
   f.lo = f32x4{x[0], x[1], x[2], x[3]};
@@ -136,6 +142,44 @@ __device__ __forceinline__ void mma_step(f32x16& acc, const Frag8<float>& a,
 #pragma unroll
   for (int s = 0; s < 4; ++s)
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[s], b.hi[s], acc, 0, 0, 0);
+}
+
+// Fragment of 8 consecutive rows (the contraction axis) of one column of a
+// row-major LDS tile with leading dimension ld (elements): lane l receives
+// tile[row0 + 8*(l/32) + e][col0 + l%32], e = 0..7 -- the operand layout that
+// mma_step expects, read from a tile stored [k][n].
+// bf16 uses two ds_read_tr16_b64: within each 16-lane group, lane i receives
+// element i%4 of the 8-byte words addressed by lanes 4j + i/4 (j = 0..3), so a
+// lane that points at tile[kb + i/4][cb + 4*(i%4)] hands every lane i of the
+// group four consecutive rows kb..kb+3 of column cb + i.  fp32 uses eight
+// scalar reads.
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+__device__ __forceinline__ Frag8<uint16_t> load_frag_T(const uint16_t* tile, int ld, int row0,
+                                                       int col0) {
+  const int l = threadIdx.x & 63;
+  const int g = l >> 4, i = l & 15;
+  const int kb = row0 + 8 * (g >> 1);
+  const int cb = col0 + 16 * (g & 1);
+  const uint16_t* p0 = tile + (kb + (i >> 2)) * ld + cb + 4 * (i & 3);
+  const uint16_t* p1 = p0 + 4 * ld;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
+  Frag8<uint16_t> f;
+  f.v[0] = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
+  f.v[1] = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
+  f.v[2] = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
+  f.v[3] = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+  return f;
+}
+__device__ __forceinline__ Frag8<float> load_frag_T(const float* tile, int ld, int row0,
+                                                    int col0) {
+  const int l = threadIdx.x & 63;
+  const float* p = tile + (row0 + 8 * (l >> 5)) * ld + col0 + (l & 31);
+  Frag8<float> f;
+  f.lo = f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
+  f.hi = f32x4{p[4 * ld], p[5 * ld], p[6 * ld], p[7 * ld]};
+  return f;
 }
 
 // Row of accumulator register r of a 32x32 block for lane-half kh = l/32

@@ -8,21 +8,27 @@
 //     z = h @ W_out + b_out               (MFMA, one 128-column vocab tile
 //                                          at a time)
 // and one of three epilogues per vocabulary tile:
-//   kLse    : online max / sum-exp (base 2) carried across vocabulary tiles;
-//             at the end lse, LB = z[blank] - lse, LE = z[label] - lse.
+//   kLse    : running sum of exp(z) carried across vocabulary tiles (with a
+//             running max unless every |z| is provably below 64); at the end
+//             lse, LB = z[blank] - lse, LE = z[label] - lse.
 //   kStoreZ : kLse plus the logits written to HBM (untiled mode).
 //   kGrad   : logit gradient of the loss (tiled backward), from the per-cell
 //             transition posteriors gB, gE and the stored lse:
 //             dz[v] = gc * (occ * exp(z[v] - lse) - gB [v=blank] - gE [v=y_u]),
-//             occ = gB + gE, written to a chunk buffer.
+//             occ = gB + gE, written to a chunk buffer, plus the h rows.
 //
 // Work decomposition (gfx950, wave64): a workgroup = 4 waves = one tile of
 // 16 frames x 8 label positions of one utterance.  Wave w owns frames
 // t0+4w..t0+4w+3 x label positions u0..u0+7 = 32 rows of a 32x32 MFMA block,
 // row r <-> (t0 + 4w + r/8, u0 + r%8).  The wave keeps its 32 rows of h for
 // the whole H in registers as MFMA A-fragments, and streams W_out^T through
-// LDS in [128 vocab x BK] slices (double buffered); each slice feeds four
-// 32x32 output blocks per wave.
+// LDS in [128 vocab x BK hidden] slices (double buffered); each slice feeds
+// four 32x32 output blocks per wave.
+//
+// h uses tanh(x) = 1 - 2 / (1 + e^{2 enc} e^{2 pred}) from the per-row
+// exponentials the forward precomputes, unless some finite |enc| or |pred|
+// exceeds 40 (then e^{2x} could overflow before the product), in which case
+// it is evaluated directly.  Both give tanh to a few 1e-7.
 #include <type_traits>
 
 #include "common.h"
@@ -36,25 +42,27 @@ constexpr float kInf = __builtin_inff();
 
 template <typename T>
 struct StageCfg {
-  static constexpr int BK = std::is_same<T, float>::value ? 32 : 64;  // k per slice
-  static constexpr int CE = 16 / (int)sizeof(T);                       // elems per 16 B
-  static constexpr int LDK = BK + CE;  // padded LDS row: 144 B, conflict-free b128 reads
-  static constexpr int CHUNKS = kVocabTile * BK / CE / 256;            // 16 B loads/thread
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int BK = kBf16 ? 128 : 64;             // hidden elements per W^T slice
+  static constexpr int CE = 16 / (int)sizeof(T);          // elements per 16-byte chunk
+  static constexpr int LDK = BK + CE;                     // LDS row: 272 B, conflict-free b128
+  static constexpr int CPR = BK / CE;                     // 16 chunks per slice row
+  static constexpr int CHUNKS = kVocabTile * CPR / 256;   // 8 loads of 16 B per thread
+  static constexpr int KK = BK / 16;                      // k-steps per slice
 };
 
-template <typename T>
+// Per-thread part of one W^T slice [vt .. vt+127] x [kc .. kc+BK): chunk q
+// covers slice row tid/16 + 16q, hidden columns (tid%16)*CE .. +CE.
+template <typename T, bool EXACT>
 __device__ __forceinline__ void load_slice(const T* __restrict__ Wt, int H, int V, int vt,
                                            int kc, u32x4 (&regs)[StageCfg<T>::CHUNKS]) {
   using C = StageCfg<T>;
-  const int tid = threadIdx.x;
+  const int row = threadIdx.x / C::CPR, col = (threadIdx.x % C::CPR) * C::CE;
+  const T* p = Wt + (size_t)(vt + row) * H + kc + col;
 #pragma unroll
   for (int q = 0; q < C::CHUNKS; ++q) {
-    const int c = tid + 256 * q;
-    const int row = c / (C::BK / C::CE);
-    const int col = (c % (C::BK / C::CE)) * C::CE;
-    const int n = vt + row, k = kc + col;
-    if (n < V && k < H)
-      regs[q] = *reinterpret_cast<const u32x4*>(Wt + (size_t)n * H + k);
+    if (EXACT || (vt + row + 16 * q < V && kc + col < H))
+      regs[q] = *reinterpret_cast<const u32x4*>(p + (size_t)16 * q * H);
     else
       regs[q] = u32x4{0u, 0u, 0u, 0u};
   }
@@ -63,14 +71,9 @@ __device__ __forceinline__ void load_slice(const T* __restrict__ Wt, int H, int 
 template <typename T>
 __device__ __forceinline__ void store_slice(T* ws, const u32x4 (&regs)[StageCfg<T>::CHUNKS]) {
   using C = StageCfg<T>;
-  const int tid = threadIdx.x;
+  T* p = ws + (threadIdx.x / C::CPR) * C::LDK + (threadIdx.x % C::CPR) * C::CE;
 #pragma unroll
-  for (int q = 0; q < C::CHUNKS; ++q) {
-    const int c = tid + 256 * q;
-    const int row = c / (C::BK / C::CE);
-    const int col = (c % (C::BK / C::CE)) * C::CE;
-    *reinterpret_cast<u32x4*>(ws + row * C::LDK + col) = regs[q];
-  }
+  for (int q = 0; q < C::CHUNKS; ++q) *reinterpret_cast<u32x4*>(p + 16 * q * C::LDK) = regs[q];
 }
 
 __device__ __forceinline__ float sel4(const f32x16 (&acc)[4], int blk, int r) {
@@ -81,13 +84,27 @@ __device__ __forceinline__ float sel4(const f32x16 (&acc)[4], int blk, int r) {
   return v;
 }
 
+// Transposed staging of one wave's 32 rows x 128 columns of bf16 output:
+// Ts[col][row] (64 bytes per column), the 8-byte granules of a column
+// permuted by swz(col) so that both the column writes from the accumulator
+// layout and the transposing row reads are free of bank conflicts.
+__device__ __forceinline__ int swz(int col) {
+  return ((col >> 1) & 7) ^ (((col >> 1) & 1) << 2);
+}
+__device__ __forceinline__ int ts_idx(int col, int row) {
+  return col * 32 + ((((row >> 2) ^ swz(col)) & 7) << 2) + (row & 3);
+}
+
 }  // namespace
 
-template <typename T, int KS, int MODE>
+template <typename T, int KS, int MODE, bool EXACT>
 __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   using C = StageCfg<T>;
+  constexpr bool kBf16 = C::kBf16;
   constexpr int KC_MAX = (KS * 16 + C::BK - 1) / C::BK;
+  constexpr bool kStores = (MODE == kStoreZ || MODE == kGrad) && kBf16;
   __shared__ __align__(16) T Ws[2][kVocabTile * C::LDK];
+  __shared__ __align__(16) uint16_t Ts[kStores ? 4 : 1][kStores ? 128 * 32 : 8];
   __shared__ float cap_blank[kTileCells];
   __shared__ float cap_label[kTileCells];
   __shared__ float row_c[kTileCells];  // kGrad: (lse - ln occ) * log2(e)
@@ -105,33 +122,74 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int kh = lane >> 5, lc = lane & 31;
   const int H = d.H, V = d.V;
-  const int nks = H / 16;
+  const int nks = EXACT ? KS : H / 16;
   const T* __restrict__ enc = static_cast<const T*>(a.enc);
   const T* __restrict__ pred = static_cast<const T*>(a.pred);
   const T* __restrict__ Wt = static_cast<const T*>(a.Wt);
   const T* __restrict__ bias = static_cast<const T*>(a.bias);
+  const int hflags = a.hdr[1];
+  const bool use_ep = (hflags & kFlagEpBad) == 0;
+  const bool bounded = __int_as_float(a.hdr[2]) < 64.0f;  // NaN bound -> false
+
+  // vocabulary tiles of this workgroup (the tiled backward splits them)
+  const int nvt_all = (V + kVocabTile - 1) / kVocabTile;
+  const int vsplit = (MODE == kGrad) ? a.vsplit : 1;
+  const int vr = (MODE == kGrad) ? (int)blockIdx.z : 0;
+  const int vt_begin = (nvt_all * vr) / vsplit, vt_end = (nvt_all * (vr + 1)) / vsplit;
+  const int nkc = EXACT ? KC_MAX : (H + C::BK - 1) / C::BK;
+  const int nstage = (vt_end - vt_begin) * nkc;
+  if (nstage <= 0) return;
 
   // ---- prologue: start the first W^T slice, build h in registers
   u32x4 regs[C::CHUNKS];
-  load_slice<T>(Wt, H, V, 0, 0, regs);
+  load_slice<T, EXACT>(Wt, H, V, vt_begin * kVocabTile, 0, regs);
 
   Frag8<T> hA[KS];
   {
     const int tt = lc >> 3, uu = lc & 7;
     const int t = t0 + 4 * w + tt, u = u0 + uu;
     const bool valid = (t < Tl) && (u <= Ul);
-    const T* er = enc + ((size_t)b * d.T + (valid ? t : 0)) * H + 8 * kh;
-    const T* pr = pred + ((size_t)b * d.U1 + (valid ? u : 0)) * H + 8 * kh;
+    const int tv = valid ? t : 0, uv = valid ? u : 0;
+    if (use_ep) {
+      const float* er = a.Eexp + ((size_t)b * d.T + tv) * H + 8 * kh;
+      const float* pr = a.Pexp + ((size_t)b * d.U1 + uv) * H + 8 * kh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (ks < nks && valid) {
-        Frag8<T> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
-        float x[8];
+      for (int ks = 0; ks < KS; ++ks) {
+        if ((EXACT || ks < nks) && valid) {
+          const Frag8<float> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
+          float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = fast_tanh(e.get(i) + p.get(i));
-        pack_frag(hA[ks], x);
-      } else {
-        zero_frag(hA[ks]);
+          for (int i = 0; i < 8; ++i)
+            x[i] = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e.get(i) * p.get(i));
+          pack_frag(hA[ks], x);
+        } else {
+          zero_frag(hA[ks]);
+        }
+      }
+    } else {
+      const T* er = enc + ((size_t)b * d.T + tv) * H + 8 * kh;
+      const T* pr = pred + ((size_t)b * d.U1 + uv) * H + 8 * kh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if ((EXACT || ks < nks) && valid) {
+          const Frag8<T> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) x[i] = fast_tanh(e.get(i) + p.get(i));
+          pack_frag(hA[ks], x);
+        } else {
+          zero_frag(hA[ks]);
+        }
+      }
+    }
+    if constexpr (MODE == kGrad) {
+      // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H])
+      if (valid && vr == 0) {
+        T* hrow = static_cast<T*>(a.hout) +
+                  (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          if (EXACT || ks < nks) store_frag(hrow + ks * 16, hA[ks]);
       }
     }
   }
@@ -181,35 +239,39 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
     srun[r] = 0.f;
   }
 
-  const int nvt = (V + kVocabTile - 1) / kVocabTile;
-  const int nkc = (H + C::BK - 1) / C::BK;
-  const int nstage = nvt * nkc;
   int s = 0;
-  for (int vti = 0; vti < nvt; ++vti) {
+  for (int vti = vt_begin; vti < vt_end; ++vti) {
     const int vt = vti * kVocabTile;
+    // accumulators start at the bias of their column
     f32x16 acc[4];
+    bool cvalid[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int blk = 0; blk < 4; ++blk) {
+      const int col = vt + blk * 32 + lc;
+      cvalid[blk] = EXACT || col < V;
+      const float bc = cvalid[blk] ? ElemTraits<T>::to_f32(bias[col]) : 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[q][r] = 0.f;
+      for (int r = 0; r < 16; ++r) acc[blk][r] = bc;
+    }
 
 #pragma unroll
     for (int kc = 0; kc < KC_MAX; ++kc) {
-      if (kc < nkc) {
+      if (EXACT || kc < nkc) {
         const int cur = s & 1;
         const bool has_next = (s + 1) < nstage;
         if (has_next) {
           const int ns = s + 1;
-          load_slice<T>(Wt, H, V, (ns / nkc) * kVocabTile, (ns % nkc) * C::BK, regs);
+          load_slice<T, EXACT>(Wt, H, V, (vt_begin + ns / nkc) * kVocabTile,
+                               (ns % nkc) * C::BK, regs);
         }
-        const T* ws = Ws[cur];
+        const T* ws = Ws[cur] + lc * C::LDK + 8 * kh;
 #pragma unroll
-        for (int kk = 0; kk < C::BK / 16; ++kk) {
-          const int ks = kc * (C::BK / 16) + kk;
-          if (ks < KS && ks < nks) {
+        for (int kk = 0; kk < C::KK; ++kk) {
+          const int ks = kc * C::KK + kk;
+          if (ks < KS && (EXACT || ks < nks)) {
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
-              Frag8<T> bf = load_frag(ws + (blk * 32 + lc) * C::LDK + kk * 16 + 8 * kh);
+              const Frag8<T> bf = load_frag(ws + blk * 32 * C::LDK + kk * 16);
               mma_step(acc[blk], hA[ks < KS ? ks : 0], bf);
             }
           }
@@ -221,42 +283,44 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
     }
 
     // ---- epilogue for vocabulary columns vt .. vt+127
-    float bcol[4];
-    bool cvalid[4];
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const int col = vt + blk * 32 + lc;
-      cvalid[blk] = col < V;
-      bcol[blk] = cvalid[blk] ? ElemTraits<T>::to_f32(bias[col]) : 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[blk][r] += bcol[blk];
-    }
-
     if constexpr (MODE == kLse || MODE == kStoreZ) {
+      if (bounded) {
+        // every |z| < 64: sum e^z directly, no running max needed
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x[4];
-        float mx = -kInf;
+        for (int r = 0; r < 16; ++r) {
+          float sum = srun[r];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          x[blk] = cvalid[blk] ? acc[blk][r] * kLog2e : -kInf;
-          mx = fmaxf(mx, x[blk]);
-        }
-        const float mn = fmaxf(mrun[r], mx);
-        if (mn > -kInf) {
-          float sum = srun[r] * exp2_fast(mrun[r] - mn);
-#pragma unroll
-          for (int blk = 0; blk < 4; ++blk) sum += exp2_fast(x[blk] - mn);
+          for (int blk = 0; blk < 4; ++blk)
+            sum += cvalid[blk] ? exp2_fast(acc[blk][r] * kLog2e) : 0.f;
           srun[r] = sum;
-          mrun[r] = mn;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x[4];
+          float mx = -kInf;
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) {
+            x[blk] = cvalid[blk] ? acc[blk][r] * kLog2e : -kInf;
+            mx = fmaxf(mx, x[blk]);
+          }
+          const float mn = fmaxf(mrun[r], mx);
+          if (mn > -kInf) {
+            float sum = srun[r] * exp2_fast(mrun[r] - mn);
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) sum += exp2_fast(x[blk] - mn);
+            srun[r] = sum;
+            mrun[r] = mn;
+          }
         }
       }
       // blank logit
-      if (a.d.blank >= vt && a.d.blank < vt + kVocabTile) {
-        const int bb = a.d.blank - vt;
+      if (d.blank >= vt && d.blank < vt + kVocabTile) {
+        const int bb = d.blank - vt;
         if (lc == (bb & 31)) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) cap_blank[w * 32 + acc_row(r, kh)] = sel4(acc, bb >> 5, r);
+          for (int r = 0; r < 16; ++r)
+            cap_blank[w * 32 + acc_row(r, kh)] = sel4(acc, bb >> 5, r);
         }
       }
       // label logits
@@ -271,39 +335,96 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
           }
         }
       }
-      if constexpr (MODE == kStoreZ) {
-        T* zout = static_cast<T*>(a.zout);
+    } else {  // kGrad: acc <- dz without the one-hot terms
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = t0 + 4 * w + (r >> 2), u = u0 + 4 * kh + (r & 3);
-          if (t < Tl && u <= Ul) {
-            T* zrow = zout + (((size_t)b * d.Tpad + t) * d.U1pad + u) * V;
+      for (int r = 0; r < 16; ++r)
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk)
-              if (cvalid[blk]) zrow[vt + blk * 32 + lc] = ElemTraits<T>::from_f32(acc[blk][r]);
-          }
-        }
-      }
-    } else {  // kGrad
-      T* gout = static_cast<T*>(a.gout);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rowi = w * 32 + acc_row(r, kh);
-        const int t = t0 + 4 * w + (r >> 2), u = u0 + 4 * kh + (r & 3);
-        const bool rvalid = (t < Tl) && (u <= Ul);
-        const int yl = lab[r & 3];
-        T* grow = gout + (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * V;
+        for (int blk = 0; blk < 4; ++blk)
+          acc[blk][r] = gc * exp2_fast(acc[blk][r] * kLog2e - cst[r]);
+    }
+
+    if constexpr (MODE == kStoreZ || MODE == kGrad) {
+      const int RT = MODE == kGrad ? a.CT : d.Tpad, RU = MODE == kGrad ? a.CU : d.U1pad;
+      const int rt0 = MODE == kGrad ? a.ct0 : 0, ru0 = MODE == kGrad ? a.cu0 : 0;
+      T* out = static_cast<T*>(MODE == kGrad ? a.gout : a.zout);
+      if constexpr (kBf16) {
+        // accumulator columns -> Ts[col][row] (8-byte writes of 4 rows) ...
+        uint16_t* ts = Ts[w];
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) {
-          const int col = vt + blk * 32 + lc;
-          if (cvalid[blk]) {
-            float g = 0.f;
-            if (rvalid) {
-              g = gc * exp2_fast(acc[blk][r] * kLog2e - cst[r]);
-              if (col == d.blank) g -= row_b[rowi];
-              if (col == yl) g -= row_e[rowi];
+          const int col = blk * 32 + lc;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            uint2 pk;
+            pk.x = (uint32_t)f32_to_bf16_hw(acc[blk][4 * i]) |
+                   ((uint32_t)f32_to_bf16_hw(acc[blk][4 * i + 1]) << 16);
+            pk.y = (uint32_t)f32_to_bf16_hw(acc[blk][4 * i + 2]) |
+                   ((uint32_t)f32_to_bf16_hw(acc[blk][4 * i + 3]) << 16);
+            *reinterpret_cast<uint2*>(&ts[ts_idx(col, 8 * i + 4 * kh)]) = pk;
+          }
+        }
+        __syncthreads();
+        if constexpr (MODE == kGrad) {
+          // one-hot terms: lane lc of the first half fixes row lc
+          if (kh == 0) {
+            const int rowi = w * 32 + lc;
+            const int u = u0 + (lc & 7);
+            if (d.blank >= vt && d.blank < vt + kVocabTile) {
+              uint16_t* p = &ts[ts_idx(d.blank - vt, lc)];
+              *p = f32_to_bf16_hw(bf16_to_f32(*p) - row_b[rowi]);
             }
-            grow[col] = ElemTraits<T>::from_f32(g);
+            const int y = (u < Ul) ? a.labels[(size_t)b * d.U + u] : -1;
+            if (y >= vt && y < vt + kVocabTile) {
+              uint16_t* p = &ts[ts_idx(y - vt, lc)];
+              *p = f32_to_bf16_hw(bf16_to_f32(*p) - row_e[rowi]);
+            }
+          }
+          __syncthreads();
+        }
+        // ... then rows: each lane gets 8 consecutive columns of row l%32
+        const int row = lc;
+        const int t = t0 + 4 * w + (row >> 3), u = u0 + (row & 7);
+        if (t < Tl && u <= Ul) {
+          T* orow = out + (((size_t)b * RT + (t - rt0)) * RU + (u - ru0)) * V + vt;
+          const int g = lane >> 4, i = lane & 15;
+#pragma unroll
+          for (int f = 0; f < 8; ++f) {
+            const int k0 = 16 * f + 8 * (g >> 1) + (i >> 2);
+            const int cb = 16 * (g & 1) + 4 * (i & 3);
+            const i16x4 lo =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0, cb)]));
+            const i16x4 hi =
+                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0 + 4, cb)]));
+            u32x4 pk;
+            pk[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+            pk[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+            pk[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+            pk[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+            const int colo = 16 * f + 8 * kh;
+            if (EXACT || vt + colo < V) *reinterpret_cast<u32x4*>(orow + colo) = pk;
+          }
+        }
+        // Ts is rewritten only after the next tile's slice barriers
+      } else {
+        // fp32: 32 lanes store 32 consecutive columns of a row (128 B)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rowi = w * 32 + acc_row(r, kh);
+          const int t = t0 + 4 * w + (r >> 2), u = u0 + 4 * kh + (r & 3);
+          if (t < Tl && u <= Ul) {
+            T* orow = out + (((size_t)b * RT + (t - rt0)) * RU + (u - ru0)) * V;
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+              const int col = vt + blk * 32 + lc;
+              if (cvalid[blk]) {
+                float g = acc[blk][r];
+                if constexpr (MODE == kGrad) {
+                  if (col == d.blank) g -= row_b[rowi];
+                  if (col == lab[r & 3]) g -= row_e[rowi];
+                }
+                orow[col] = g;
+              }
+            }
           }
         }
       }
@@ -311,17 +432,26 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   }
 
   if constexpr (MODE == kLse || MODE == kStoreZ) {
-    // combine the per-lane (max, sum) of the 32 lanes that share each row
+    // combine the per-lane partial sums of the 32 lanes that share each row
+    if (bounded) {
 #pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
+      for (int off = 1; off < 32; off <<= 1)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float mo = __shfl_xor(mrun[r], off);
-        const float so = __shfl_xor(srun[r], off);
-        const float mn = fmaxf(mrun[r], mo);
-        if (mn > -kInf) {
-          srun[r] = srun[r] * exp2_fast(mrun[r] - mn) + so * exp2_fast(mo - mn);
-          mrun[r] = mn;
+        for (int r = 0; r < 16; ++r) srun[r] += __shfl_xor(srun[r], off);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mrun[r] = 0.f;
+    } else {
+#pragma unroll
+      for (int off = 1; off < 32; off <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float mo = __shfl_xor(mrun[r], off);
+          const float so = __shfl_xor(srun[r], off);
+          const float mn = fmaxf(mrun[r], mo);
+          if (mn > -kInf) {
+            srun[r] = srun[r] * exp2_fast(mrun[r] - mn) + so * exp2_fast(mo - mn);
+            mrun[r] = mn;
+          }
         }
       }
     }
@@ -350,21 +480,33 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
 
 // ------------------------------------------------------------------ dispatch
 
+template <typename T, int KS, int MODE>
+static void launch_ks(const JointArgs& a, bool exact, dim3 grid, hipStream_t st) {
+  if (exact)
+    hipLaunchKernelGGL((joint_tile_kernel<T, KS, MODE, true>), grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL((joint_tile_kernel<T, KS, MODE, false>), grid, dim3(256), 0, st, a);
+}
+
 template <typename T, int MODE>
 static hipError_t launch_mode(const JointArgs& a, int n_tiles, hipStream_t st) {
+  using C = StageCfg<T>;
   const int nks = a.d.H / 16;
-  dim3 grid(n_tiles, a.d.B), block(256);
+  dim3 grid(n_tiles, a.d.B, MODE == kGrad ? (a.vsplit > 0 ? a.vsplit : 1) : 1);
+  auto exact = [&](int KS) {
+    return nks == KS && a.d.H % C::BK == 0 && a.d.V % kVocabTile == 0;
+  };
   if constexpr (std::is_same<T, float>::value) {
-    if (nks <= 4) hipLaunchKernelGGL((joint_tile_kernel<T, 4, MODE>), grid, block, 0, st, a);
-    else if (nks <= 8) hipLaunchKernelGGL((joint_tile_kernel<T, 8, MODE>), grid, block, 0, st, a);
-    else if (nks <= 16) hipLaunchKernelGGL((joint_tile_kernel<T, 16, MODE>), grid, block, 0, st, a);
+    if (nks <= 4) launch_ks<T, 4, MODE>(a, exact(4), grid, st);
+    else if (nks <= 8) launch_ks<T, 8, MODE>(a, exact(8), grid, st);
+    else if (nks <= 16) launch_ks<T, 16, MODE>(a, exact(16), grid, st);
     else return hipErrorInvalidValue;
   } else {
-    if (nks <= 8) hipLaunchKernelGGL((joint_tile_kernel<T, 8, MODE>), grid, block, 0, st, a);
-    else if (nks <= 16) hipLaunchKernelGGL((joint_tile_kernel<T, 16, MODE>), grid, block, 0, st, a);
-    else if (nks <= 32) hipLaunchKernelGGL((joint_tile_kernel<T, 32, MODE>), grid, block, 0, st, a);
-    else if (nks <= 40) hipLaunchKernelGGL((joint_tile_kernel<T, 40, MODE>), grid, block, 0, st, a);
-    else if (nks <= 48) hipLaunchKernelGGL((joint_tile_kernel<T, 48, MODE>), grid, block, 0, st, a);
+    if (nks <= 8) launch_ks<T, 8, MODE>(a, exact(8), grid, st);
+    else if (nks <= 16) launch_ks<T, 16, MODE>(a, exact(16), grid, st);
+    else if (nks <= 32) launch_ks<T, 32, MODE>(a, exact(32), grid, st);
+    else if (nks <= 40) launch_ks<T, 40, MODE>(a, exact(40), grid, st);
+    else if (nks <= 48) launch_ks<T, 48, MODE>(a, exact(48), grid, st);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -11,6 +11,11 @@ namespace rnntj {
 
 enum JointMode { kLse = 0, kStoreZ = 1, kGrad = 2 };
 
+// Header of the forward -> backward state (int32 words): [0] data-error mask,
+// [1] flags, [2] float bits of max_v (sum_k |W_out[k,v]| + |b_out[v]|), an
+// upper bound on every |z| since |h| <= 1.
+constexpr int kFlagEpBad = 1;  // some finite |enc| or |pred| > 40
+
 struct JointArgs {
   const void* enc;
   const void* pred;
@@ -19,7 +24,11 @@ struct JointArgs {
   const int32_t* labels;
   const int32_t* Teff;  // validated lengths (0 frames = invalid utterance)
   const int32_t* Ueff;
+  const int32_t* hdr;   // state header (flags, logit bound)
+  const float* Eexp;    // e^{2 enc} [B, T, H]
+  const float* Pexp;    // e^{2 pred} [B, U+1, H]
   Dims d;
+  int vsplit;    // kGrad: vocabulary tiles split over this many workgroups
   int ct0, cu0;  // chunk origin (frame, label position)
   int CT, CU;    // chunk extents, multiples of kTileT / kTileU
   int n_tu;      // CU / kTileU
@@ -34,6 +43,7 @@ struct JointArgs {
   const double* logP;
   const float* gcost;  // [B] or null
   void* gout;          // kGrad: logit gradients [B, CT, CU, V]
+  void* hout;          // kGrad: joint activations h [B, CT, CU, H]
 };
 
 hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_tiles,
@@ -44,6 +54,12 @@ hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_tile
 hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
                            int32_t* Ueff, int32_t* status, hipStream_t st);
+
+// Eexp = e^{2 enc}, Pexp = e^{2 pred} (float32), hdr[1] |= kFlagEpBad if some
+// finite |enc| or |pred| exceeds 40; hdr[2] = max_v sum_k |W[k,v]| + |b[v]|.
+hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
+                       bool bf16, const Dims& d, float* Eexp, float* Pexp, int32_t* hdr,
+                       hipStream_t st);
 
 // dst[V, H] = transpose(src[H, V])
 hipError_t launch_transpose(const void* src, void* dst, int H, int V, bool bf16,
@@ -56,6 +72,9 @@ hipError_t launch_zero(void* p, size_t n_words, hipStream_t st);
 hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
                           const int32_t* Ueff, const Dims& d, double* alpha, double* beta,
                           double* logP, float* costs, hipStream_t st);
+
+// Untiled backward: h rows of every cell into h [B, Tpad, U1pad, H].
+hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st);
 
 // Untiled backward: logits [B, Tpad, U1pad, V] turned into logit gradients
 // in place.
@@ -70,6 +89,9 @@ struct DhArgs {
   const void* pred;
   const int32_t* Teff;
   const int32_t* Ueff;
+  const int32_t* hdr;
+  const float* Eexp;
+  const float* Pexp;
   Dims d;
   int ct0, cu0, CT, CU, n_tu;
   float* d_enc;
@@ -79,9 +101,8 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, hipStream_t st);
 
 // d_W_out += h^T dz and d_b64 += column sums of dz (float64) over one chunk.
 struct DwArgs {
-  const void* g;
-  const void* enc;
-  const void* pred;
+  const void* g;  // dz rows [B, CT, CU, V]
+  const void* h;  // h rows  [B, CT, CU, H]
   const int32_t* Teff;
   const int32_t* Ueff;
   Dims d;

@@ -222,6 +222,41 @@ __global__ void transpose_kernel(const E* __restrict__ src, E* __restrict__ dst,
   }
 }
 
+// e^{2x} of every enc and pred element (accurate expf), and the flag that
+// some finite |x| exceeds 40, where e^{2x} alone could overflow although the
+// joint's sum enc + pred is moderate.
+template <typename E>
+__global__ void ep_kernel(const E* __restrict__ enc, const E* __restrict__ pred, Dims d,
+                          float* __restrict__ Eexp, float* __restrict__ Pexp,
+                          int32_t* __restrict__ hdr) {
+  const size_t ne = (size_t)d.B * d.T * d.H, np = (size_t)d.B * d.U1 * d.H;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  bool bad = false;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < ne + np; i += stride) {
+    const float x = i < ne ? ElemTraits<E>::to_f32(enc[i]) : ElemTraits<E>::to_f32(pred[i - ne]);
+    const float ax = fabsf(x);
+    if (ax > 40.0f && ax != __builtin_inff()) bad = true;
+    const float e = expf(2.0f * x);
+    if (i < ne)
+      Eexp[i] = e;
+    else
+      Pexp[i - ne] = e;
+  }
+  if (bad) atomicOr(&hdr[1], kFlagEpBad);
+}
+
+// hdr[2] = max_v (|b[v]| + sum_k |W[k,v]|) as float bits (non-negative, so
+// integer max orders them; a NaN column bound wins and disables the bound).
+template <typename E>
+__global__ void colbound_kernel(const E* __restrict__ W, const E* __restrict__ bias, Dims d,
+                                int32_t* __restrict__ hdr) {
+  const int v = blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= d.V) return;
+  float s = fabsf(ElemTraits<E>::to_f32(bias[v]));
+  for (int k = 0; k < d.H; ++k) s += fabsf(ElemTraits<E>::to_f32(W[(size_t)k * d.V + v]));
+  atomicMax(&hdr[2], __float_as_int(s));
+}
+
 __global__ void zero_kernel(uint32_t* __restrict__ p, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
@@ -272,6 +307,29 @@ hipError_t launch_transpose(const void* src, void* dst, int H, int V, bool bf16,
   else
     hipLaunchKernelGGL(transpose_kernel<float>, grid, block, 0, st,
                        static_cast<const float*>(src), static_cast<float*>(dst), H, V);
+  return hipGetLastError();
+}
+
+hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
+                       bool bf16, const Dims& d, float* Eexp, float* Pexp, int32_t* hdr,
+                       hipStream_t st) {
+  const size_t n = (size_t)d.B * (d.T + d.U1) * d.H;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  const dim3 gb((d.V + 255) / 256);
+  if (bf16) {
+    hipLaunchKernelGGL(ep_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(enc), static_cast<const uint16_t*>(pred), d,
+                       Eexp, Pexp, hdr);
+    hipLaunchKernelGGL(colbound_kernel<uint16_t>, gb, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(bias), d, hdr);
+  } else {
+    hipLaunchKernelGGL(ep_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
+                       static_cast<const float*>(enc), static_cast<const float*>(pred), d, Eexp,
+                       Pexp, hdr);
+    hipLaunchKernelGGL(colbound_kernel<float>, gb, dim3(256), 0, st,
+                       static_cast<const float*>(W), static_cast<const float*>(bias), d, hdr);
+  }
   return hipGetLastError();
 }
 

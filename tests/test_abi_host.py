@@ -43,16 +43,19 @@ def _ws(B, T, U, H, V, dt, tt=0, tu=0, tv=0, p=1):
 
 def test_buffer_sizes():
     # medium workload, bf16: per cell lse/LB/LE (12 B) + alpha/beta (16 B) over
-    # the skewed [B, T+U, U+1] layout, plus W^T; untiled adds the logits.
+    # the skewed [B, T+U, U+1] layout, W^T, and e^{2 enc}, e^{2 pred} (float32);
+    # untiled adds the logits.
     rc, tiled = _saved(16, 500, 100, 640, 1024, 1, 64, 64, 0)
     assert rc == 0
     cells = 16 * 600 * 101
-    assert cells * 28 <= tiled <= cells * 28 + 640 * 1024 * 2 + 64 * 1024
+    fixed = cells * 28 + 640 * 1024 * 2 + 4 * 16 * (500 + 101) * 640
+    assert fixed <= tiled <= fixed + 64 * 1024
     rc, untiled = _saved(16, 500, 100, 640, 1024, 1)
     assert rc == 0
     assert untiled - tiled >= 16 * 512 * 104 * 1024 * 2
-    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + 16 * 64 * 64 * 1024 * 2)
-    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024)
+    chunk = 16 * 64 * 64
+    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + chunk * (1024 + 640) * 2)
+    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024 + 16 * 512 * 104 * 640 * 2)
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, 0, 0) == (0, 0)
 
 
