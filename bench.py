@@ -52,7 +52,48 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device-to-device copies of BYTES bytes (the "
+                         "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def kernel_source_digest():
+    """sha256 over the HIP/C++ sources of the library (sorted by name)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "rnn_joint_transducer_amd", "csrc", "*"))):
+        h.update(os.path.basename(f).encode())
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kernel, mode):
+    """HBM bytes per launch recorded in profiles/traffic.json by rocprofv3
+    FETCH_SIZE / WRITE_SIZE passes (scaled by the copy calibration), or None
+    when no entry exists or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        entries = json.load(open(path))["entries"]
+    except (OSError, ValueError, KeyError):
+        return None
+    digest = kernel_source_digest()
+    for e in entries:
+        if (e.get("workload") == workload and e.get("kernel") == kernel
+                and e.get("mode") == mode and e.get("source_sha256") == digest):
+            return e.get("bytes_per_launch")
+    return None
+
+
+def calibrate_copy(nbytes):
+    import torch
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 5}))
 
 
 def cpu_baseline(inp, target_s):
@@ -104,6 +145,9 @@ def cpu_baseline(inp, target_s):
 
 def main():
     args = parse()
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the path shards over utterances across GPUs by design, but multi-GPU runs are "
@@ -214,11 +258,12 @@ def main():
                 "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
                 "algorithmic_per_launch": per_launch}
 
+    mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
+    roof["traffic"] = measured_traffic(args.workload, dom, mode)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds)
 
-    mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
     line = {
         "metric": METRIC, "value": value, "unit": "cells/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,

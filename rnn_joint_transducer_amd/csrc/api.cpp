@@ -345,6 +345,13 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   w.d = p.d;
   w.d_W = d_W_out;
   w.d_b64 = db64;
+  // split-K so that the weight-gradient GEMM has >= 1024 workgroups
+  auto set_ksplit = [&](int CT, int CU) {
+    const int tiles = B * ((H + 127) / 128) * ((V + 127) / 128);
+    const int max_stages = (CT / kTileT) * (CU / kTileU) * 2;
+    int k = (1024 + tiles - 1) / tiles;
+    w.ksplit = k < 1 ? 1 : (k > max_stages ? max_stages : k);
+  };
   auto finalize = [&] {
     return timed("db_finalize", st, [&] { return launch_db_finalize(db64, d_b_out, V, st); });
   };
@@ -360,6 +367,7 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
       return RNNTJ_ERR_HIP;
     w.g = z;
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
+    set_ksplit(w.CT, w.CU);
     if ((e = timed("hrow", st, [&] { return launch_hrow(hchunk, p.bf16, a, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
@@ -396,6 +404,7 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
         return RNNTJ_ERR_HIP;
       w.g = gchunk;
       w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;
+      set_ksplit(w.CT, w.CU);
       if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
         return RNNTJ_ERR_HIP;
     }

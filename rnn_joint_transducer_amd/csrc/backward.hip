@@ -287,13 +287,19 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   __shared__ __align__(16) T Bs[2][C::KB * C::LD];  // dz [cell][vocab]
   __shared__ double dbw[4][128];
   const Dims d = a.d;
-  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128, b = blockIdx.z;
+  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128;
+  const int b = blockIdx.z / a.ksplit, kpart = blockIdx.z % a.ksplit;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  // valid cell tiles of this utterance inside the chunk form a rectangle
+  // valid cell tiles of this utterance inside the chunk form a rectangle;
+  // this workgroup takes the kpart-th of ksplit equal runs of their stages
   const int tv = min(a.CT, Tl - a.ct0), uv = min(a.CU, Ul + 1 - a.cu0);
   if (tv <= 0 || uv <= 0) return;
   const int ntt = (tv + kTileT - 1) / kTileT, ntu = (uv + kTileU - 1) / kTileU;
-  const int nstage = ntt * ntu * C::SPT;
+  const int nall = ntt * ntu * C::SPT;
+  const int s_begin = (int)(((long long)nall * kpart) / a.ksplit);
+  const int s_end = (int)(((long long)nall * (kpart + 1)) / a.ksplit);
+  const int nstage = s_end - s_begin;
+  if (nstage <= 0) return;
   const int n_tu = a.CU / kTileU;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int kh = lane >> 5;
@@ -310,7 +316,8 @@ __global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
   for (int i = 0; i < C::CE; ++i) dbacc[i] = 0.0;
 
   u32x4 ra[C::CH], rb[C::CH];
-  auto load_stage = [&](int s) {
+  auto load_stage = [&](int sl) {
+    const int s = s_begin + sl;
     const int tile = s / C::SPT, part = s % C::SPT;
     const int t0 = a.ct0 + (tile / ntu) * kTileT + part * (C::KB / kTileU);
     const int u0 = a.cu0 + (tile % ntu) * kTileU;
@@ -493,7 +500,7 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, hipStream_t st) {
 }
 
 hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st) {
-  dim3 grid((a.d.V + 127) / 128, (a.d.H + 127) / 128, a.d.B), block(256);
+  dim3 grid((a.d.V + 127) / 128, (a.d.H + 127) / 128, a.d.B * a.ksplit), block(256);
   if (bf16)
     hipLaunchKernelGGL(dw_kernel<uint16_t>, grid, block, 0, st, a);
   else

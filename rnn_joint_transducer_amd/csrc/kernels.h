@@ -107,6 +107,7 @@ struct DwArgs {
   const int32_t* Ueff;
   Dims d;
   int ct0, cu0, CT, CU;
+  int ksplit;  // workgroups sharing one utterance's cells (split-K)
   float* d_W;
   double* d_b64;
 };
