@@ -32,7 +32,7 @@ struct Plan {
   size_t elem;
   // saved layout (byte offsets)
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
-      o_z;
+      o_cs, o_z;
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
   size_t o_ws_db, o_ws_g, o_ws_h;  // backward workspace layout
@@ -79,6 +79,7 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_beta = o;   o = align_up(o + 8 * cells);
   q.o_E = o;      o = align_up(o + 4 * (size_t)B * T * H);
   q.o_P = o;      o = align_up(o + 4 * (size_t)B * (U + 1) * H);
+  q.o_cs = o;     o = align_up(o + 4 * (size_t)V);
   q.o_z = o;
   if (q.untiled) o = align_up(o + q.elem * (size_t)B * q.d.Tpad * q.d.U1pad * V);
   q.saved_bytes = o;
@@ -224,7 +225,8 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
   float* Eexp = at<float>(saved, p.o_E);
   float* Pexp = at<float>(saved, p.o_P);
   if ((e = timed("prep", st, [&] {
-         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Eexp, Pexp, status, st);
+         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Eexp, Pexp,
+                            at<float>(saved, p.o_cs), status, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   if ((e = timed("transpose", st, [&] { return launch_transpose(W_out, Wt, H, V, p.bf16, st); })) !=

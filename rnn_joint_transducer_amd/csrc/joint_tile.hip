@@ -23,7 +23,9 @@
 // row r <-> (t0 + 4w + r/8, u0 + r%8).  The wave keeps its 32 rows of h for
 // the whole H in registers as MFMA A-fragments, and streams W_out^T through
 // LDS in [128 vocab x BK hidden] slices (double buffered); each slice feeds
-// four 32x32 output blocks per wave.
+// four 32x32 output blocks per wave.  The slices are copied global -> LDS
+// directly (no staging registers), which leaves the registers for h, the
+// accumulators and B fragments read one k-step ahead of the MFMAs.
 //
 // h uses tanh(x) = 1 - 2 / (1 + e^{2 enc} e^{2 pred}) from the per-row
 // exponentials the forward precomputes, unless some finite |enc| or |pred|
@@ -45,36 +47,42 @@ struct StageCfg {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int BK = kBf16 ? 128 : 64;             // hidden elements per W^T slice
   static constexpr int CE = 16 / (int)sizeof(T);          // elements per 16-byte chunk
-  static constexpr int LDK = BK + CE;                     // LDS row: 272 B, conflict-free b128
-  static constexpr int CPR = BK / CE;                     // 16 chunks per slice row
-  static constexpr int CHUNKS = kVocabTile * CPR / 256;   // 8 loads of 16 B per thread
+  static constexpr int ROWB = 256;                        // bytes per slice row (16 chunks)
   static constexpr int KK = BK / 16;                      // k-steps per slice
+  static constexpr int SLICE = kVocabTile * ROWB;         // 32 KB per slice
 };
 
-// Per-thread part of one W^T slice [vt .. vt+127] x [kc .. kc+BK): chunk q
-// covers slice row tid/16 + 16q, hidden columns (tid%16)*CE .. +CE.
+// One W^T slice [vt .. vt+127] x [kc .. kc+BK) goes straight from global
+// memory into LDS (global_load_lds, 16 bytes per lane, 1 KB per wave
+// instruction, no staging registers): wave w writes LDS chunks
+// (8w + q)*64 + lane, q = 0..7, i.e. slice row r = 32w + 4q + lane/16, chunk
+// slot lane%16.  Slot s of row r holds hidden chunk s ^ (r & 15): rows are
+// unpadded (the copy writes 1 KB contiguously) and the XOR keeps the
+// fragment reads of 8 or 16 consecutive rows on distinct banks.  Outside an
+// exact shape the source row / column is clamped to valid memory; those
+// columns are masked and those k-steps skipped by the caller.
 template <typename T, bool EXACT>
-__device__ __forceinline__ void load_slice(const T* __restrict__ Wt, int H, int V, int vt,
-                                           int kc, u32x4 (&regs)[StageCfg<T>::CHUNKS]) {
+__device__ __forceinline__ void dma_slice(const T* __restrict__ Wt, int H, int V, int vt, int kc,
+                                          char* lds_slice) {
   using C = StageCfg<T>;
-  const int row = threadIdx.x / C::CPR, col = (threadIdx.x % C::CPR) * C::CE;
-  const T* p = Wt + (size_t)(vt + row) * H + kc + col;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int q = 0; q < C::CHUNKS; ++q) {
-    if (EXACT || (vt + row + 16 * q < V && kc + col < H))
-      regs[q] = *reinterpret_cast<const u32x4*>(p + (size_t)16 * q * H);
-    else
-      regs[q] = u32x4{0u, 0u, 0u, 0u};
+  for (int q = 0; q < 8; ++q) {
+    const int r = 32 * w + 4 * q + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    int n = vt + r, k = kc + c * C::CE;
+    if (!EXACT) {
+      n = n < V ? n : V - 1;
+      k = k < H ? k : H - C::CE;
+    }
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(Wt + (size_t)n * H + k),
+        (__attribute__((address_space(3))) void*)(lds_slice + (8 * w + q) * 1024), 16, 0, 0);
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void store_slice(T* ws, const u32x4 (&regs)[StageCfg<T>::CHUNKS]) {
-  using C = StageCfg<T>;
-  T* p = ws + (threadIdx.x / C::CPR) * C::LDK + (threadIdx.x % C::CPR) * C::CE;
-#pragma unroll
-  for (int q = 0; q < C::CHUNKS; ++q) *reinterpret_cast<u32x4*>(p + 16 * q * C::LDK) = regs[q];
-}
+// all of this wave's direct-to-LDS copies (and any other loads) have landed
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float sel4(const f32x16 (&acc)[4], int blk, int r) {
   float v = acc[0][r];
@@ -103,7 +111,10 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   constexpr bool kBf16 = C::kBf16;
   constexpr int KC_MAX = (KS * 16 + C::BK - 1) / C::BK;
   constexpr bool kStores = (MODE == kStoreZ || MODE == kGrad) && kBf16;
-  __shared__ __align__(16) T Ws[2][kVocabTile * C::LDK];
+  // two separately named slice buffers: the compiler then knows that the
+  // copy into one does not alias the fragment reads of the other
+  __shared__ __align__(16) char Ws0[C::SLICE];
+  __shared__ __align__(16) char Ws1[C::SLICE];
   __shared__ __align__(16) uint16_t Ts[kStores ? 4 : 1][kStores ? 128 * 32 : 8];
   __shared__ float cap_blank[kTileCells];
   __shared__ float cap_label[kTileCells];
@@ -141,8 +152,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   if (nstage <= 0) return;
 
   // ---- prologue: start the first W^T slice, build h in registers
-  u32x4 regs[C::CHUNKS];
-  load_slice<T, EXACT>(Wt, H, V, vt_begin * kVocabTile, 0, regs);
+  dma_slice<T, EXACT>(Wt, H, V, vt_begin * kVocabTile, 0, Ws0);
 
   Frag8<T> hA[KS];
   {
@@ -193,8 +203,6 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       }
     }
   }
-  store_slice<T>(Ws[0], regs);
-
   // labels of this lane's accumulator rows: u = u0 + 4*kh + j
   int lab[4];
 #pragma unroll
@@ -226,6 +234,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
     }
     gc = a.gcost ? a.gcost[b] : 1.0f;
   }
+  wait_vmem();
   __syncthreads();
   if constexpr (MODE == kGrad) {
 #pragma unroll
@@ -254,29 +263,62 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       for (int r = 0; r < 16; ++r) acc[blk][r] = bc;
     }
 
+    // B-fragment reads: row lc of each 32-row block; hidden chunk c of that
+    // row is stored at slot c ^ (lc & 15)
+    const int xm = lc & 15;
 #pragma unroll
     for (int kc = 0; kc < KC_MAX; ++kc) {
       if (EXACT || kc < nkc) {
-        const int cur = s & 1;
         const bool has_next = (s + 1) < nstage;
-        if (has_next) {
-          const int ns = s + 1;
-          load_slice<T, EXACT>(Wt, H, V, (vt_begin + ns / nkc) * kVocabTile,
-                               (ns % nkc) * C::BK, regs);
-        }
-        const T* ws = Ws[cur] + lc * C::LDK + 8 * kh;
-#pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
-          const int ks = kc * C::KK + kk;
-          if (ks < KS && (EXACT || ks < nks)) {
-#pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
-              const Frag8<T> bf = load_frag(ws + blk * 32 * C::LDK + kk * 16);
-              mma_step(acc[blk], hA[ks < KS ? ks : 0], bf);
+        const int ns = s + 1;
+        const int nvt = (vt_begin + ns / nkc) * kVocabTile, nkc0 = (ns % nkc) * C::BK;
+        // one stage: start the copy of the next slice into `nxt`, run the
+        // MFMAs of this slice from `src` (B fragments one k-step ahead)
+        auto stage = [&](const char* src, char* nxt) {
+          if (has_next) dma_slice<T, EXACT>(Wt, H, V, nvt, nkc0, nxt);
+          const char* wrow = src + lc * C::ROWB;
+          // bf16: a fragment is one 16-byte chunk (2*kk + kh); fp32: two
+          // chunks (4*kk + 2*kh, +1), each at its own swizzled slot
+          auto bfrag = [&](int blk, int kk) {
+            const char* rb = wrow + blk * 32 * C::ROWB;
+            Frag8<T> f;
+            if constexpr (kBf16) {
+              f.v = *reinterpret_cast<const u32x4*>(rb + (((2 * kk + kh) ^ xm) << 4));
+            } else {
+              f.lo = *reinterpret_cast<const f32x4*>(rb + (((4 * kk + 2 * kh) ^ xm) << 4));
+              f.hi = *reinterpret_cast<const f32x4*>(rb + (((4 * kk + 2 * kh + 1) ^ xm) << 4));
             }
+            return f;
+          };
+          Frag8<T> bcur[4], bnxt[4];
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) bcur[blk] = bfrag(blk, 0);
+#pragma unroll
+          for (int kk = 0; kk < C::KK; ++kk) {
+            const int ks = kc * C::KK + kk;
+            const bool live = ks < KS && (EXACT || ks < nks);
+            const bool nlive = kk + 1 < C::KK && ks + 1 < KS && (EXACT || ks + 1 < nks);
+            if (nlive) {
+#pragma unroll
+              for (int blk = 0; blk < 4; ++blk) bnxt[blk] = bfrag(blk, kk + 1);
+            }
+            // keep the reads for k-step kk+1 issued ahead of this k-step's MFMAs
+            __builtin_amdgcn_sched_barrier(0);
+            if (live) {
+#pragma unroll
+              for (int blk = 0; blk < 4; ++blk)
+                mma_step(acc[blk], hA[ks < KS ? ks : 0], bcur[blk]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) bcur[blk] = bnxt[blk];
           }
-        }
-        if (has_next) store_slice<T>(Ws[cur ^ 1], regs);
+        };
+        if ((s & 1) == 0)
+          stage(Ws0, Ws1);
+        else
+          stage(Ws1, Ws0);
+        wait_vmem();
         __syncthreads();
         ++s;
       }

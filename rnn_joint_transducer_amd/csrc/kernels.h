@@ -57,9 +57,10 @@ hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
 
 // Eexp = e^{2 enc}, Pexp = e^{2 pred} (float32), hdr[1] |= kFlagEpBad if some
 // finite |enc| or |pred| exceeds 40; hdr[2] = max_v sum_k |W[k,v]| + |b[v]|.
+// colsum [V] is float scratch (zeroed here).
 hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
-                       bool bf16, const Dims& d, float* Eexp, float* Pexp, int32_t* hdr,
-                       hipStream_t st);
+                       bool bf16, const Dims& d, float* Eexp, float* Pexp, float* colsum,
+                       int32_t* hdr, hipStream_t st);
 
 // dst[V, H] = transpose(src[H, V])
 hipError_t launch_transpose(const void* src, void* dst, int H, int V, bool bf16,

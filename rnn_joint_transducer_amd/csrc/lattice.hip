@@ -11,13 +11,10 @@
 //   beta(t,u) = logaddexp(beta(t+1,u) + LB(t,u), beta(t,u+1) + LE(t,u))
 //
 // One wave64 per (utterance, direction): cells of one anti-diagonal t+u are
-// independent, so the wave sweeps the T'+U' anti-diagonals with label
-// position u = 64*j + lane held in register slot j.  The u-1 / u+1
-// neighbour on the previous diagonal comes from the adjacent lane by a
-// cross-lane shuffle.  State is float64 (the posteriors later take
-// exp(alpha + beta - logP) of numbers of size ~1e4); the logaddexp
+// independent, so the wave sweeps the T'+U' anti-diagonals with the label
+// positions spread over the lanes.  State is float64 (the posteriors later
+// take exp(alpha + beta - logP) of numbers of size ~1e4); the logaddexp
 // correction log(1 + e^-|x-y|) lies in [0, ln 2] and is evaluated in float32.
-// LB / LE of upcoming diagonals are loaded kPrefetch steps ahead.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,20 +23,43 @@ namespace rnntj {
 namespace {
 
 constexpr double kNegInfD = -__builtin_inf();
-constexpr int kPrefetch = 4;
 
+// log(e^x + e^y) without branches: the max plus a float32 correction
+// log(1 + e^-|x-y|) in [0, ln 2].  (-inf, -inf) gives -inf; a NaN operand
+// gives NaN (comparisons, not fmax, pick hi / lo).
 __device__ __forceinline__ double log_add_exp(double x, double y) {
-  // comparisons (not fmax) so that a NaN operand propagates
   const bool xg = x > y;
   const double hi = xg ? x : y;
   const double lo = xg ? y : x;
-  if (hi == kNegInfD) return kNegInfD;
   const float dl = (float)(lo - hi);
   const float c = __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(dl * kLog2e)) * kLn2;
-  return hi + (double)c;
+  const double r = hi + (double)c;
+  return (hi == kNegInfD && lo == kNegInfD) ? kNegInfD : r;
 }
 
-template <int NU>
+// Cross-lane shift of a float64 by one lane (DPP wave shifts): shr moves
+// lane l-1's value to lane l (lane 0 receives `fill`), shl moves lane l+1's
+// value to lane l (lane 63 receives `fill`).
+__device__ __forceinline__ double wave_shr1(double v, double fill) {
+  const long long x = __double_as_longlong(v), f = __double_as_longlong(fill);
+  const int lo = __builtin_amdgcn_update_dpp((int)f, (int)x, 0x138, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(f >> 32), (int)(x >> 32), 0x138, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+__device__ __forceinline__ double wave_shl1(double v, double fill) {
+  const long long x = __double_as_longlong(v), f = __double_as_longlong(fill);
+  const int lo = __builtin_amdgcn_update_dpp((int)f, (int)x, 0x130, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp((int)(f >> 32), (int)(x >> 32), 0x130, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Lane l owns the NU consecutive label positions u = NU*l .. NU*l + NU-1, so
+// on each anti-diagonal the u-1 (alpha) or u+1 (beta) neighbour is in the
+// same lane except at the block edge, which one DPP lane shift supplies.
+// LB / LE of diagonal dg+PD are loaded while diagonal dg is computed; every
+// load is issued unconditionally (clamped address) so that the hardware
+// load counter can wait for exactly the oldest ones.
+template <int NU, int PD>
 __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ LB,
                                                      const float* __restrict__ LE,
                                                      const int32_t* __restrict__ Teff,
@@ -62,45 +82,34 @@ __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ L
   const float* lb = LB + base;
   const float* le = LE + base;
   double* out = (dir == 0 ? alpha : beta) + base;
+  const int last = d.DG * d.U1 - 1;  // clamp for the unconditional loads
 
   double prev[NU];
 #pragma unroll
   for (int j = 0; j < NU; ++j) prev[j] = kNegInfD;
 
-  // operands of step s (anti-diagonal dg(s)) for slot j:
-  //   alpha: LB(t-1,u), LE(t,u-1) (both on diagonal dg-1)
-  //   beta : LB(t,u),   LE(t,u)   (on diagonal dg)
-  auto diag_of = [&](int s) { return dir == 0 ? s : nd - 1 - s; };
+  // operands of step s for slot j (diagonal dg = s for alpha, nd-1-s for beta):
+  //   alpha: LB(t-1,u), LE(t,u-1) on diagonal dg-1;  beta: LB(t,u), LE(t,u) on dg
   auto fetch = [&](int s, float (&fb)[NU], float (&fe)[NU]) {
+    const int dg = dir == 0 ? s - 1 : nd - 1 - s;
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
-      fb[j] = 0.f;
-      fe[j] = 0.f;
-    }
-    if (s >= nd) return;
-    const int dg = diag_of(s);
-#pragma unroll
-    for (int j = 0; j < NU; ++j) {
-      const int u = 64 * j + l;
-      const int t = dg - u;
-      if (u > Ul || t < 0 || t >= Tl) continue;
-      if (dir == 0) {
-        if (t >= 1) fb[j] = lb[(size_t)(dg - 1) * d.U1 + u];
-        if (u >= 1) fe[j] = le[(size_t)(dg - 1) * d.U1 + u - 1];
-      } else {
-        fb[j] = lb[(size_t)dg * d.U1 + u];
-        if (u < Ul) fe[j] = le[(size_t)dg * d.U1 + u];
-      }
+      const int u = NU * l + j;
+      int ib = dg * d.U1 + u, ie = dir == 0 ? ib - 1 : ib;
+      ib = ib < 0 ? 0 : (ib > last ? last : ib);
+      ie = ie < 0 ? 0 : (ie > last ? last : ie);
+      fb[j] = lb[ib];
+      fe[j] = le[ie];
     }
   };
 
-  float rb[kPrefetch][NU], re[kPrefetch][NU];
+  float rb[PD][NU], re[PD][NU];
 #pragma unroll
-  for (int p = 0; p < kPrefetch; ++p) fetch(p, rb[p], re[p]);
+  for (int p = 0; p < PD; ++p) fetch(p, rb[p], re[p]);
 
-  for (int s0 = 0; s0 < nd; s0 += kPrefetch) {
+  for (int s0 = 0; s0 < nd; s0 += PD) {
 #pragma unroll
-    for (int p = 0; p < kPrefetch; ++p) {
+    for (int p = 0; p < PD; ++p) {
       const int s = s0 + p;
       if (s < nd) {  // uniform across the wave
         float cb[NU], ce[NU];
@@ -109,56 +118,43 @@ __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ L
           cb[j] = rb[p][j];
           ce[j] = re[p][j];
         }
-        fetch(s + kPrefetch, rb[p], re[p]);
-        const int dg = diag_of(s);
-        double nb[NU];
+        fetch(s + PD, rb[p], re[p]);
+        const int dg = dir == 0 ? s : nd - 1 - s;
+        double cur[NU];
         if (dir == 0) {
-          // alpha(t, u-1) on the previous diagonal: lane l-1 (slot j), or
-          // lane 63 of slot j-1 for lane 0
+          // alpha(t, u-1) on the previous diagonal
+          const double edge = wave_shr1(prev[NU - 1], kNegInfD);
 #pragma unroll
           for (int j = 0; j < NU; ++j) {
-            const double up = __shfl_up(prev[j], 1);
-            const double wrap = __shfl(j > 0 ? prev[j > 0 ? j - 1 : 0] : kNegInfD, 63);
-            nb[j] = (l == 0) ? (j > 0 ? wrap : kNegInfD) : up;
+            const int u = NU * l + j;
+            const int t = dg - u;
+            const bool valid = (u <= Ul) & (t >= 0) & (t < Tl);
+            const double nb = j > 0 ? prev[j > 0 ? j - 1 : 0] : edge;
+            const double ft = (t >= 1) ? prev[j] + (double)cb[j] : kNegInfD;
+            const double fu = (u >= 1) ? nb + (double)ce[j] : kNegInfD;
+            double v = log_add_exp(ft, fu);
+            v = (dg == 0) ? 0.0 : v;
+            v = valid ? v : kNegInfD;
+            if (valid) out[(size_t)dg * d.U1 + u] = v;
+            cur[j] = v;
           }
         } else {
-          // beta(t, u+1) on the previous (later) diagonal: lane l+1 (slot j),
-          // or lane 0 of slot j+1 for lane 63
+          // beta(t, u+1) on the previous (later) diagonal
+          const double edge = wave_shl1(prev[0], kNegInfD);
 #pragma unroll
           for (int j = 0; j < NU; ++j) {
-            const double dn = __shfl_down(prev[j], 1);
-            const double wrap = __shfl(j + 1 < NU ? prev[j + 1 < NU ? j + 1 : 0] : kNegInfD, 0);
-            nb[j] = (l == 63) ? (j + 1 < NU ? wrap : kNegInfD) : dn;
+            const int u = NU * l + j;
+            const int t = dg - u;
+            const bool valid = (u <= Ul) & (t >= 0) & (t < Tl);
+            const double nb = j + 1 < NU ? prev[j + 1 < NU ? j + 1 : 0] : edge;
+            const double ft = (t + 1 < Tl) ? prev[j] + (double)cb[j] : kNegInfD;
+            const double fu = (u < Ul) ? nb + (double)ce[j] : kNegInfD;
+            double v = log_add_exp(ft, fu);
+            v = (t == Tl - 1 && u == Ul) ? (double)cb[j] : v;
+            v = valid ? v : kNegInfD;
+            if (valid) out[(size_t)dg * d.U1 + u] = v;
+            cur[j] = v;
           }
-        }
-        double cur[NU];
-#pragma unroll
-        for (int j = 0; j < NU; ++j) {
-          const int u = 64 * j + l;
-          const int t = dg - u;
-          const bool valid = (u <= Ul) && (t >= 0) && (t < Tl);
-          double v = kNegInfD;
-          if (valid) {
-            if (dir == 0) {
-              if (dg == 0) {
-                v = 0.0;
-              } else {
-                const double ft = (t >= 1) ? prev[j] + (double)cb[j] : kNegInfD;
-                const double fu = (u >= 1) ? nb[j] + (double)ce[j] : kNegInfD;
-                v = log_add_exp(ft, fu);
-              }
-            } else {
-              if (t == Tl - 1 && u == Ul) {
-                v = (double)cb[j];
-              } else {
-                const double ft = (t + 1 < Tl) ? prev[j] + (double)cb[j] : kNegInfD;
-                const double fu = (u < Ul) ? nb[j] + (double)ce[j] : kNegInfD;
-                v = log_add_exp(ft, fu);
-              }
-            }
-            out[(size_t)dg * d.U1 + u] = v;
-          }
-          cur[j] = v;
         }
 #pragma unroll
         for (int j = 0; j < NU; ++j) prev[j] = cur[j];
@@ -166,7 +162,7 @@ __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ L
           // final cell (T'-1, U') lies on the last diagonal
 #pragma unroll
           for (int j = 0; j < NU; ++j) {
-            if (64 * j + l == Ul) {
+            if (NU * l + j == Ul) {
               const double lp = cur[j] + (double)lb[(size_t)dg * d.U1 + Ul];
               logP[b] = lp;
               costs[b] = (float)(-lp);
@@ -245,16 +241,45 @@ __global__ void ep_kernel(const E* __restrict__ enc, const E* __restrict__ pred,
   if (bad) atomicOr(&hdr[1], kFlagEpBad);
 }
 
-// hdr[2] = max_v (|b[v]| + sum_k |W[k,v]|) as float bits (non-negative, so
-// integer max orders them; a NaN column bound wins and disables the bound).
+// colsum[v] += sum over 64 hidden rows of |W[k,v]| (one 64 x 64 block per
+// workgroup: 4 row groups of 16, coalesced 64-column rows)
 template <typename E>
-__global__ void colbound_kernel(const E* __restrict__ W, const E* __restrict__ bias, Dims d,
-                                int32_t* __restrict__ hdr) {
-  const int v = blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= d.V) return;
-  float s = fabsf(ElemTraits<E>::to_f32(bias[v]));
-  for (int k = 0; k < d.H; ++k) s += fabsf(ElemTraits<E>::to_f32(W[(size_t)k * d.V + v]));
-  atomicMax(&hdr[2], __float_as_int(s));
+__global__ void colsum_kernel(const E* __restrict__ W, Dims d, float* __restrict__ colsum) {
+  __shared__ float part[4][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int v = blockIdx.x * 64 + c, k0 = blockIdx.y * 64 + 16 * g;
+  float s = 0.f;
+  if (v < d.V) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int k = k0 + i;
+      if (k < d.H) s += fabsf(ElemTraits<E>::to_f32(W[(size_t)k * d.V + v]));
+    }
+  }
+  part[g][c] = s;
+  __syncthreads();
+  if (g == 0 && v < d.V) atomicAdd(&colsum[v], part[0][c] + part[1][c] + part[2][c] + part[3][c]);
+}
+
+// hdr[2] = max_v (|b[v]| + colsum[v]) as float bits: non-negative floats
+// order like their bit patterns, and a NaN column sum wins the integer max
+// and disables the bound.
+template <typename E>
+__global__ void colbound_kernel(const float* __restrict__ colsum, const E* __restrict__ bias,
+                                Dims d, int32_t* __restrict__ hdr) {
+  __shared__ int red[256];
+  int m = 0;
+  for (int v = threadIdx.x; v < d.V; v += 256) {
+    const float s = colsum[v] + fabsf(ElemTraits<E>::to_f32(bias[v]));
+    m = max(m, __float_as_int(s));
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + o]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) hdr[2] = red[0];
 }
 
 __global__ void zero_kernel(uint32_t* __restrict__ p, size_t n) {
@@ -269,10 +294,10 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
                           double* logP, float* costs, hipStream_t st) {
   const int nu = (d.U1 + 63) / 64;
   dim3 grid(d.B, 2), block(64);
-#define RNNTJ_LAT(N)                                                                        \
-  case N:                                                                                   \
-    hipLaunchKernelGGL(lattice_kernel<N>, grid, block, 0, st, LB, LE, Teff, Ueff, d, alpha, \
-                       beta, logP, costs);                                                  \
+#define RNNTJ_LAT(N)                                                                       \
+  case N:                                                                                  \
+    hipLaunchKernelGGL((lattice_kernel<N, (N <= 4 ? 6 : 3)>), grid, block, 0, st, LB, LE, \
+                       Teff, Ueff, d, alpha, beta, logP, costs);                           \
     break;
   switch (nu) {
     RNNTJ_LAT(1)
@@ -311,24 +336,30 @@ hipError_t launch_transpose(const void* src, void* dst, int H, int V, bool bf16,
 }
 
 hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
-                       bool bf16, const Dims& d, float* Eexp, float* Pexp, int32_t* hdr,
-                       hipStream_t st) {
+                       bool bf16, const Dims& d, float* Eexp, float* Pexp, float* colsum,
+                       int32_t* hdr, hipStream_t st) {
   const size_t n = (size_t)d.B * (d.T + d.U1) * d.H;
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  const dim3 gb((d.V + 255) / 256);
+  const dim3 gs((d.V + 63) / 64, (d.H + 63) / 64);
+  hipError_t e = launch_zero(colsum, (size_t)d.V, st);
+  if (e != hipSuccess) return e;
   if (bf16) {
     hipLaunchKernelGGL(ep_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
                        static_cast<const uint16_t*>(enc), static_cast<const uint16_t*>(pred), d,
                        Eexp, Pexp, hdr);
-    hipLaunchKernelGGL(colbound_kernel<uint16_t>, gb, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(W), static_cast<const uint16_t*>(bias), d, hdr);
+    hipLaunchKernelGGL(colsum_kernel<uint16_t>, gs, dim3(256), 0, st,
+                       static_cast<const uint16_t*>(W), d, colsum);
+    hipLaunchKernelGGL(colbound_kernel<uint16_t>, dim3(1), dim3(256), 0, st, colsum,
+                       static_cast<const uint16_t*>(bias), d, hdr);
   } else {
     hipLaunchKernelGGL(ep_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
                        static_cast<const float*>(enc), static_cast<const float*>(pred), d, Eexp,
                        Pexp, hdr);
-    hipLaunchKernelGGL(colbound_kernel<float>, gb, dim3(256), 0, st,
-                       static_cast<const float*>(W), static_cast<const float*>(bias), d, hdr);
+    hipLaunchKernelGGL(colsum_kernel<float>, gs, dim3(256), 0, st, static_cast<const float*>(W),
+                       d, colsum);
+    hipLaunchKernelGGL(colbound_kernel<float>, dim3(1), dim3(256), 0, st, colsum,
+                       static_cast<const float*>(bias), d, hdr);
   }
   return hipGetLastError();
 }
