@@ -43,7 +43,7 @@
  *     carried: 0 selects the default (128); 128 is supported.
  *   - Limits (else RNNTJ_ERR_UNSUPPORTED): H a multiple of 16 with
  *     16 <= H <= 768 for bf16 and H <= 256 for fp32; V a multiple of 8,
- *     8 <= V; U + 1 <= 512.
+ *     8 <= V; U + 1 <= 512; B <= 8191; T <= 65520.
  *   - Host-side argument errors (null pointers, bad shapes, blank outside
  *     [0,V), unsupported tiles, workspace too small) return a nonzero code
  *     before anything is enqueued; outputs are untouched.
@@ -92,7 +92,8 @@ const char* rnnt_joint_loss_last_error(void);
  * saved holds the per-utterance validated lengths, log P and status, a
  * transposed copy of W_out, e^{2 enc} and e^{2 pred} (float32), and per cell
  * (diagonal-skewed [B, T+U, U+1]): lse, LB, LE (float32) and alpha, beta
- * (float64).  In the untiled mode it also holds the logits
+ * (float64), and the list of active 16 x 8 cell tiles (int32, one word per
+ * tile of the padded lattice).  In the untiled mode it also holds the logits
  * [B, ceil16(T), ceil8(U+1), V] in dtype.
  * Writes *out; returns a status code.
  */
@@ -105,7 +106,8 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
  * accumulator for d_b_out [V], the joint activations h of one lattice chunk
  * [B, tile_t, tile_u, H] in dtype (the whole padded lattice when untiled)
  * and, in the tiled mode, that chunk's logit gradients [B, tile_t, tile_u, V]
- * in dtype.  Writes *out; returns a status code.
+ * in dtype plus the active-tile list of every chunk (int32, one word per
+ * 16 x 8 tile).  Writes *out; returns a status code.
  */
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
                                     int tile_t, int tile_u, int tile_v, int pass,

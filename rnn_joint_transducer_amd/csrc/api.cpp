@@ -32,10 +32,13 @@ struct Plan {
   size_t elem;
   // saved layout (byte offsets)
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
-      o_cs, o_z;
+      o_cs, o_tiles, o_tcount, o_z;
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
-  size_t o_ws_db, o_ws_g, o_ws_h;  // backward workspace layout
+  size_t o_ws_db, o_ws_g, o_ws_h, o_ws_tiles, o_ws_tcount;  // backward workspace layout
+  int cap_all;                // active-tile list capacity of the whole lattice
+  int n_cu_chunks, n_chunks;  // backward chunk grid (tiled mode)
+  int cap_chunk;              // active-tile list capacity of one chunk
 };
 
 int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile_u, int tile_v,
@@ -47,6 +50,7 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   if (H % 16 != 0 || H > (bf16 ? 768 : 256)) return RNNTJ_ERR_UNSUPPORTED;
   if (V % 8 != 0 || V < 8) return RNNTJ_ERR_UNSUPPORTED;
   if (U + 1 > 512) return RNNTJ_ERR_UNSUPPORTED;
+  if (B > 8191 || T > 65520) return RNNTJ_ERR_UNSUPPORTED;  // packed tile coordinates
   if (tile_t % kTileT != 0 || tile_u % kTileU != 0) return RNNTJ_ERR_UNSUPPORTED;
   if (tile_v != 0 && tile_v != kVocabTile) return RNNTJ_ERR_UNSUPPORTED;
   Plan& q = *p;
@@ -80,6 +84,9 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_E = o;      o = align_up(o + 4 * (size_t)B * T * H);
   q.o_P = o;      o = align_up(o + 4 * (size_t)B * (U + 1) * H);
   q.o_cs = o;     o = align_up(o + 4 * (size_t)V);
+  q.cap_all = B * (q.d.Tpad / kTileT) * (q.d.U1pad / kTileU);
+  q.o_tiles = o;  o = align_up(o + 4 * (size_t)q.cap_all);
+  q.o_tcount = o; o = align_up(o + 16);
   q.o_z = o;
   if (q.untiled) o = align_up(o + q.elem * (size_t)B * q.d.Tpad * q.d.U1pad * V);
   q.saved_bytes = o;
@@ -88,10 +95,15 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   // chunk of logit gradients [B, CT, CU, V]
   // joint activations h of the chunk [B, CT, CU, H] (the whole lattice when
   // untiled)
+  q.n_cu_chunks = (q.d.U1pad + q.CU - 1) / q.CU;
+  q.n_chunks = ((q.d.Tpad + q.CT - 1) / q.CT) * q.n_cu_chunks;
+  q.cap_chunk = B * (q.CT / kTileT) * (q.CU / kTileU);
   q.o_ws_db = 0;
   q.o_ws_g = align_up(8 * (size_t)V);
   q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
-  q.ws_bwd = q.o_ws_h + align_up(q.elem * (size_t)B * q.CT * q.CU * H);
+  q.o_ws_tiles = q.o_ws_h + align_up(q.elem * (size_t)B * q.CT * q.CU * H);
+  q.o_ws_tcount = q.o_ws_tiles + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks * q.cap_chunk));
+  q.ws_bwd = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
   return RNNTJ_OK;
 }
 
@@ -233,6 +245,14 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
       hipSuccess)
     return RNNTJ_ERR_HIP;
 
+  int32_t* tiles = at<int32_t>(saved, p.o_tiles);
+  int32_t* tcount = at<int32_t>(saved, p.o_tcount);
+  if ((e = timed("tile_list", st, [&] {
+         return launch_tile_list(Teff, Ueff, p.d, p.d.Tpad, p.d.U1pad, 1, 1, p.cap_all, tiles,
+                                 tcount, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+
   JointArgs a = {};
   a.enc = enc;
   a.pred = pred;
@@ -244,6 +264,8 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
   a.hdr = status;
   a.Eexp = Eexp;
   a.Pexp = Pexp;
+  a.tiles = tiles;
+  a.tile_count = tcount;
   a.vsplit = 1;
   a.d = p.d;
   a.ct0 = 0;
@@ -255,9 +277,8 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
   a.LB = LB;
   a.LE = LE;
   a.zout = p.untiled ? at<char>(saved, p.o_z) : nullptr;
-  const int n_tiles = (p.d.Tpad / kTileT) * a.n_tu;
   if ((e = timed(p.untiled ? "joint_fwd_store" : "joint_fwd", st, [&] {
-         return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, n_tiles, st);
+         return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, p.cap_all, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   if ((e = timed("lattice", st, [&] {
@@ -381,13 +402,21 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   // The logit-gradient kernel splits the vocabulary tiles of each cell tile
   // over several workgroups when a chunk alone has too few cell tiles to
   // give every compute unit (256 on gfx950) about four of them.
-  const int chunk_tiles = B * (p.CT / kTileT) * (p.CU / kTileU);
+  const int chunk_tiles = p.cap_chunk;
   const int nvt = (V + kVocabTile - 1) / kVocabTile;
   int vsplit = 1;
   while (vsplit < nvt && chunk_tiles * vsplit < 1024) vsplit *= 2;
   if (vsplit > nvt) vsplit = nvt;
+  int32_t* ctiles = at<int32_t>(workspace, p.o_ws_tiles);
+  int32_t* ccount = at<int32_t>(workspace, p.o_ws_tcount);
+  if ((e = timed("tile_list", st, [&] {
+         return launch_tile_list(Teff, Ueff, p.d, p.CT, p.CU, p.n_cu_chunks, p.n_chunks,
+                                 p.cap_chunk, ctiles, ccount, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  int chunk = 0;
   for (int ct0 = 0; ct0 < p.d.Tpad; ct0 += p.CT) {
-    for (int cu0 = 0; cu0 < p.d.U1pad; cu0 += p.CU) {
+    for (int cu0 = 0; cu0 < p.d.U1pad; cu0 += p.CU, ++chunk) {
       a.ct0 = ct0;
       a.cu0 = cu0;
       a.CT = p.CT;
@@ -396,8 +425,10 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
       a.vsplit = vsplit;
       a.gout = gchunk;
       a.hout = hchunk;
+      a.tiles = ctiles + (size_t)chunk * p.cap_chunk;
+      a.tile_count = ccount + chunk;
       if ((e = timed("joint_grad", st, [&] {
-             return launch_joint_tile(a, kGrad, p.bf16, (p.CT / kTileT) * a.n_tu, st);
+             return launch_joint_tile(a, kGrad, p.bf16, p.cap_chunk * vsplit, st);
            })) != hipSuccess)
         return RNNTJ_ERR_HIP;
       h.g = gchunk;

@@ -151,8 +151,9 @@ __device__ __forceinline__ void mma_step(f32x16& acc, const Frag8<float>& a,
 // bf16 uses two ds_read_tr16_b64: within each 16-lane group, lane i receives
 // element i%4 of the 8-byte words addressed by lanes 4j + i/4 (j = 0..3), so a
 // lane that points at tile[kb + i/4][cb + 4*(i%4)] hands every lane i of the
-// group four consecutive rows kb..kb+3 of column cb + i.  fp32 uses eight
-// scalar reads.
+// group four consecutive rows kb..kb+3 of column cb + i.  A lane's result
+// depends on addresses held by other lanes, so the call must be made with
+// every lane of the wave active.  fp32 uses eight scalar reads.
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 __device__ __forceinline__ Frag8<uint16_t> load_frag_T(const uint16_t* tile, int ld, int row0,

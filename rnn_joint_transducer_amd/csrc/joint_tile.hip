@@ -17,8 +17,12 @@
 //             dz[v] = gc * (occ * exp(z[v] - lse) - gB [v=blank] - gE [v=y_u]),
 //             occ = gB + gE, written to a chunk buffer, plus the h rows.
 //
-// Work decomposition (gfx950, wave64): a workgroup = 4 waves = one tile of
-// 16 frames x 8 label positions of one utterance.  Wave w owns frames
+// Work decomposition (gfx950, wave64): the kernel is persistent -- one
+// workgroup per compute unit walks the list of active tiles (tiles holding at
+// least one lattice cell; the list is built on the device), so every compute
+// unit gets the same number of tiles whatever the length mix.  A tile is
+// 16 frames x 8 label positions of one utterance, processed by 4 waves.
+// Wave w owns frames
 // t0+4w..t0+4w+3 x label positions u0..u0+7 = 32 rows of a 32x32 MFMA block,
 // row r <-> (t0 + 4w + r/8, u0 + r%8).  The wave keeps its 32 rows of h for
 // the whole H in registers as MFMA A-fragments, and streams W_out^T through
@@ -30,7 +34,10 @@
 // h uses tanh(x) = 1 - 2 / (1 + e^{2 enc} e^{2 pred}) from the per-row
 // exponentials the forward precomputes, unless some finite |enc| or |pred|
 // exceeds 40 (then e^{2x} could overflow before the product), in which case
-// it is evaluated directly.  Both give tanh to a few 1e-7.
+// it is evaluated directly.  Both give tanh to a few 1e-7.  The 16 + 8
+// exponential rows of a tile are copied into LDS in one batch of direct
+// loads (issued for the next tile while the current one runs), so building
+// h costs LDS reads instead of a chain of dependent global loads.
 #include <type_traits>
 
 #include "common.h"
@@ -105,9 +112,21 @@ __device__ __forceinline__ int ts_idx(int col, int row) {
 
 }  // namespace
 
+// Largest hidden size whose 24 exponential rows are staged in LDS (the
+// budget left next to the W^T slices and the store staging).
+template <typename T, int KS>
+struct EpCfg {
+  static constexpr int kMaxH = sizeof(T) == 2 ? 640 : 256;
+  static constexpr bool kStage = KS * 16 <= kMaxH;
+  // 16 e^{2 enc} rows then 8 e^{2 pred} rows (float32), plus one 1 KB copy
+  // of slack for a partial last copy
+  static constexpr int kBytes = kStage ? 96 * KS * 16 + 1024 : 16;
+};
+
 template <typename T, int KS, int MODE, bool EXACT>
 __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   using C = StageCfg<T>;
+  using EP = EpCfg<T, KS>;
   constexpr bool kBf16 = C::kBf16;
   constexpr int KC_MAX = (KS * 16 + C::BK - 1) / C::BK;
   constexpr bool kStores = (MODE == kStoreZ || MODE == kGrad) && kBf16;
@@ -121,16 +140,11 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   __shared__ float row_c[kTileCells];  // kGrad: (lse - ln occ) * log2(e)
   __shared__ float row_b[kTileCells];  // kGrad: gc * gB
   __shared__ float row_e[kTileCells];  // kGrad: gc * gE
+  __shared__ __align__(16) char Ep[EP::kBytes];
 
   const Dims d = a.d;
-  const int b = blockIdx.y;
-  const int tile = blockIdx.x;
-  const int t0 = a.ct0 + (tile / a.n_tu) * kTileT;
-  const int u0 = a.cu0 + (tile % a.n_tu) * kTileU;
-  const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  if (t0 >= Tl || u0 > Ul) return;  // whole tile outside the lattice (uniform)
-
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = lane >> 5, lc = lane & 31;
   const int H = d.H, V = d.V;
   const int nks = EXACT ? KS : H / 16;
@@ -140,19 +154,93 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   const T* __restrict__ bias = static_cast<const T*>(a.bias);
   const int hflags = a.hdr[1];
   const bool use_ep = (hflags & kFlagEpBad) == 0;
+  const bool stage_ep = EP::kStage && use_ep;
   const bool bounded = __int_as_float(a.hdr[2]) < 64.0f;  // NaN bound -> false
 
-  // vocabulary tiles of this workgroup (the tiled backward splits them)
   const int nvt_all = (V + kVocabTile - 1) / kVocabTile;
   const int vsplit = (MODE == kGrad) ? a.vsplit : 1;
-  const int vr = (MODE == kGrad) ? (int)blockIdx.z : 0;
-  const int vt_begin = (nvt_all * vr) / vsplit, vt_end = (nvt_all * (vr + 1)) / vsplit;
   const int nkc = EXACT ? KC_MAX : (H + C::BK - 1) / C::BK;
+  const int n_items = a.tile_count[0] * vsplit;
+
+  // item -> tile origin, utterance, vocabulary range (the tiled backward
+  // splits a tile's vocabulary tiles over `vsplit` items)
+  auto item_tile = [&](int item, int& b, int& t0, int& u0) {
+    int tt, tu;
+    tile_unpack(a.tiles[item / vsplit], b, tt, tu);
+    t0 = a.ct0 + tt * kTileT;
+    u0 = a.cu0 + tu * kTileU;
+  };
+  // the 16 e^{2 enc} rows t0.. and 8 e^{2 pred} rows u0.. of a tile -> Ep,
+  // 1 KB direct copies spread over the waves (sources clamped to the tables)
+  auto issue_ep = [&](int b, int t0, int u0) {
+    if constexpr (EP::kStage) {
+      const char* esrc = reinterpret_cast<const char*>(a.Eexp + ((size_t)b * d.T + t0) * H);
+      const char* psrc = reinterpret_cast<const char*>(a.Pexp + ((size_t)b * d.U1 + u0) * H);
+      const char* elim = reinterpret_cast<const char*>(a.Eexp + (size_t)d.B * d.T * H) - 16;
+      const char* plim = reinterpret_cast<const char*>(a.Pexp + (size_t)d.B * d.U1 * H) - 16;
+      const int ne = (64 * H + 1023) >> 10, np = (32 * H + 1023) >> 10;
+      for (int q = w; q < ne + np; q += 4) {
+        const bool isE = q < ne;
+        const int j = isE ? q : q - ne;
+        const char* src = (isE ? esrc : psrc) + j * 1024 + lane * 16;
+        const char* lim = isE ? elim : plim;
+        src = src < lim ? src : lim;
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)src,
+            (__attribute__((address_space(3))) void*)(Ep + (isE ? 0 : 64 * H) + j * 1024), 16, 0,
+            0);
+      }
+    }
+  };
+  // h = tanh(enc + pred) evaluated directly from the inputs (rows whose
+  // e^{2x} could overflow)
+  auto build_h_direct = [&](Frag8<T>(&hA)[KS], int b, int tv, int uv, bool valid) {
+    const T* er = enc + ((size_t)b * d.T + tv) * H + 8 * kh;
+    const T* pr = pred + ((size_t)b * d.U1 + uv) * H + 8 * kh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if ((EXACT || ks < nks) && valid) {
+        const Frag8<T> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fast_tanh(e.get(i) + p.get(i));
+        pack_frag(hA[ks], x);
+      } else {
+        zero_frag(hA[ks]);
+      }
+    }
+  };
+  if (stage_ep && (int)blockIdx.x < n_items) {
+    int b, t0, u0;
+    item_tile(blockIdx.x, b, t0, u0);
+    issue_ep(b, t0, u0);
+  }
+
+  for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+  int b, t0, u0;
+  item_tile(item, b, t0, u0);
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  // vocabulary tiles of this item
+  const int vr = (MODE == kGrad) ? item % vsplit : 0;
+  const int vt_begin = (nvt_all * vr) / vsplit, vt_end = (nvt_all * (vr + 1)) / vsplit;
   const int nstage = (vt_end - vt_begin) * nkc;
-  if (nstage <= 0) return;
+  if (nstage <= 0) {  // uniform; no work, but keep the row prefetch going
+    if (stage_ep && item + (int)gridDim.x < n_items) {
+      wait_vmem();
+      __syncthreads();
+      int nb, nt0, nu0;
+      item_tile(item + gridDim.x, nb, nt0, nu0);
+      issue_ep(nb, nt0, nu0);
+    }
+    continue;
+  }
 
   // ---- prologue: start the first W^T slice, build h in registers
   dma_slice<T, EXACT>(Wt, H, V, vt_begin * kVocabTile, 0, Ws0);
+  if (stage_ep) {
+    wait_vmem();  // this wave's exponential rows (and slice part) have landed
+    __syncthreads();
+  }
 
   Frag8<T> hA[KS];
   {
@@ -160,7 +248,29 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
     const int t = t0 + 4 * w + tt, u = u0 + uu;
     const bool valid = (t < Tl) && (u <= Ul);
     const int tv = valid ? t : 0, uv = valid ? u : 0;
-    if (use_ep) {
+    if constexpr (EP::kStage) {
+      // exponential rows from LDS
+      if (use_ep) {
+        const float* er = reinterpret_cast<const float*>(Ep) + (4 * w + tt) * H + 8 * kh;
+        const float* pr = reinterpret_cast<const float*>(Ep + 64 * H) + uu * H + 8 * kh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if ((EXACT || ks < nks) && valid) {
+            const Frag8<float> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+              x[i] = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e.get(i) * p.get(i));
+            pack_frag(hA[ks], x);
+          } else {
+            zero_frag(hA[ks]);
+          }
+        }
+      } else {
+        build_h_direct(hA, b, tv, uv, valid);
+      }
+    } else if (use_ep) {
+      // exponential rows straight from global memory
       const float* er = a.Eexp + ((size_t)b * d.T + tv) * H + 8 * kh;
       const float* pr = a.Pexp + ((size_t)b * d.U1 + uv) * H + 8 * kh;
 #pragma unroll
@@ -177,20 +287,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         }
       }
     } else {
-      const T* er = enc + ((size_t)b * d.T + tv) * H + 8 * kh;
-      const T* pr = pred + ((size_t)b * d.U1 + uv) * H + 8 * kh;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if ((EXACT || ks < nks) && valid) {
-          const Frag8<T> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
-          float x[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) x[i] = fast_tanh(e.get(i) + p.get(i));
-          pack_frag(hA[ks], x);
-        } else {
-          zero_frag(hA[ks]);
-        }
-      }
+      build_h_direct(hA, b, tv, uv, valid);
     }
     if constexpr (MODE == kGrad) {
       // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H])
@@ -236,6 +333,12 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   }
   wait_vmem();
   __syncthreads();
+  // every wave has built its h: the next item's exponential rows may load
+  if (stage_ep && item + (int)gridDim.x < n_items) {
+    int nb, nt0, nu0;
+    item_tile(item + gridDim.x, nb, nt0, nu0);
+    issue_ep(nb, nt0, nu0);
+  }
   if constexpr (MODE == kGrad) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) cst[r] = row_c[w * 32 + acc_row(r, kh)];
@@ -423,28 +526,30 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
           }
           __syncthreads();
         }
-        // ... then rows: each lane gets 8 consecutive columns of row l%32
+        // ... then rows: each lane gets 8 consecutive columns of row l%32.
+        // A transposing read hands a lane data addressed by the other lanes
+        // of its 16-lane group, so every lane takes part in the reads; only
+        // the stores are limited to lattice cells.
         const int row = lc;
         const int t = t0 + 4 * w + (row >> 3), u = u0 + (row & 7);
-        if (t < Tl && u <= Ul) {
-          T* orow = out + (((size_t)b * RT + (t - rt0)) * RU + (u - ru0)) * V + vt;
-          const int g = lane >> 4, i = lane & 15;
+        const bool row_ok = t < Tl && u <= Ul;
+        T* orow = out + (((size_t)b * RT + (row_ok ? t - rt0 : 0)) * RU + (row_ok ? u - ru0 : 0)) * V + vt;
+        const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-          for (int f = 0; f < 8; ++f) {
-            const int k0 = 16 * f + 8 * (g >> 1) + (i >> 2);
-            const int cb = 16 * (g & 1) + 4 * (i & 3);
-            const i16x4 lo =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0, cb)]));
-            const i16x4 hi =
-                __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0 + 4, cb)]));
-            u32x4 pk;
-            pk[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-            pk[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-            pk[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-            pk[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
-            const int colo = 16 * f + 8 * kh;
-            if (EXACT || vt + colo < V) *reinterpret_cast<u32x4*>(orow + colo) = pk;
-          }
+        for (int f = 0; f < 8; ++f) {
+          const int k0 = 16 * f + 8 * (g >> 1) + (i >> 2);
+          const int cb = 16 * (g & 1) + 4 * (i & 3);
+          const i16x4 lo =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0, cb)]));
+          const i16x4 hi =
+              __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0 + 4, cb)]));
+          u32x4 pk;
+          pk[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
+          pk[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
+          pk[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
+          pk[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+          const int colo = 16 * f + 8 * kh;
+          if (row_ok && (EXACT || vt + colo < V)) *reinterpret_cast<u32x4*>(orow + colo) = pk;
         }
         // Ts is rewritten only after the next tile's slice barriers
       } else {
@@ -518,9 +623,26 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       }
     }
   }
+  // the next item rewrites the captures, row constants and store staging
+  __syncthreads();
+  }  // item loop
 }
 
 // ------------------------------------------------------------------ dispatch
+
+// compute units of the current device (one resident workgroup each)
+static int cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 template <typename T, int KS, int MODE>
 static void launch_ks(const JointArgs& a, bool exact, dim3 grid, hipStream_t st) {
@@ -531,10 +653,11 @@ static void launch_ks(const JointArgs& a, bool exact, dim3 grid, hipStream_t st)
 }
 
 template <typename T, int MODE>
-static hipError_t launch_mode(const JointArgs& a, int n_tiles, hipStream_t st) {
+static hipError_t launch_mode(const JointArgs& a, int n_items, hipStream_t st) {
   using C = StageCfg<T>;
   const int nks = a.d.H / 16;
-  dim3 grid(n_tiles, a.d.B, MODE == kGrad ? (a.vsplit > 0 ? a.vsplit : 1) : 1);
+  const int ncu = cu_count();
+  dim3 grid(n_items < ncu ? n_items : ncu);
   auto exact = [&](int KS) {
     return nks == KS && a.d.H % C::BK == 0 && a.d.V % kVocabTile == 0;
   };
@@ -554,17 +677,17 @@ static hipError_t launch_mode(const JointArgs& a, int n_tiles, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_tiles,
+hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_items,
                              hipStream_t st) {
-  if (n_tiles <= 0 || a.d.B <= 0) return hipSuccess;
+  if (n_items <= 0 || a.d.B <= 0) return hipSuccess;
   if (bf16) {
-    if (mode == kLse) return launch_mode<uint16_t, kLse>(a, n_tiles, st);
-    if (mode == kStoreZ) return launch_mode<uint16_t, kStoreZ>(a, n_tiles, st);
-    return launch_mode<uint16_t, kGrad>(a, n_tiles, st);
+    if (mode == kLse) return launch_mode<uint16_t, kLse>(a, n_items, st);
+    if (mode == kStoreZ) return launch_mode<uint16_t, kStoreZ>(a, n_items, st);
+    return launch_mode<uint16_t, kGrad>(a, n_items, st);
   }
-  if (mode == kLse) return launch_mode<float, kLse>(a, n_tiles, st);
-  if (mode == kStoreZ) return launch_mode<float, kStoreZ>(a, n_tiles, st);
-  return launch_mode<float, kGrad>(a, n_tiles, st);
+  if (mode == kLse) return launch_mode<float, kLse>(a, n_items, st);
+  if (mode == kStoreZ) return launch_mode<float, kStoreZ>(a, n_items, st);
+  return launch_mode<float, kGrad>(a, n_items, st);
 }
 
 }  // namespace rnntj

@@ -16,6 +16,22 @@ enum JointMode { kLse = 0, kStoreZ = 1, kGrad = 2 };
 // upper bound on every |z| since |h| <= 1.
 constexpr int kFlagEpBad = 1;  // some finite |enc| or |pred| > 40
 
+// Active-tile lists.  A lattice chunk (frames ct0 .. ct0+CT-1, label
+// positions cu0 .. cu0+CU-1) is covered by 16 x 8 cell tiles; a tile is
+// active when it holds at least one cell t < T'_b, u <= U'_b.  The active
+// tiles of chunk c are list[c * cap + i], i < count[c], utterance by
+// utterance, each packed as b << 18 | tt << 6 | tu (tile row / column inside
+// the chunk).
+__host__ __device__ inline int tile_pack(int b, int tt, int tu) { return (b << 18) | (tt << 6) | tu; }
+__device__ inline void tile_unpack(int v, int& b, int& tt, int& tu) {
+  b = v >> 18;
+  tt = (v >> 6) & 0xfff;
+  tu = v & 63;
+}
+hipError_t launch_tile_list(const int32_t* Teff, const int32_t* Ueff, const Dims& d, int CT, int CU,
+                            int n_chunks_u, int n_chunks, int cap, int32_t* list, int32_t* count,
+                            hipStream_t st);
+
 struct JointArgs {
   const void* enc;
   const void* pred;
@@ -28,6 +44,8 @@ struct JointArgs {
   const float* Eexp;    // e^{2 enc} [B, T, H]
   const float* Pexp;    // e^{2 pred} [B, U+1, H]
   Dims d;
+  const int32_t* tiles;       // active tiles of this chunk
+  const int32_t* tile_count;  // number of entries in `tiles`
   int vsplit;    // kGrad: vocabulary tiles split over this many workgroups
   int ct0, cu0;  // chunk origin (frame, label position)
   int CT, CU;    // chunk extents, multiples of kTileT / kTileU
@@ -46,7 +64,9 @@ struct JointArgs {
   void* hout;          // kGrad: joint activations h [B, CT, CU, H]
 };
 
-hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_tiles,
+// Persistent launch: `n_items` = (maximum number of active tiles) * vsplit
+// bounds the work; the workgroups loop over the items the tile list holds.
+hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_items,
                              hipStream_t st);
 
 // Length / label validation: writes Teff/Ueff (0 / 0 for an invalid

@@ -282,6 +282,33 @@ __global__ void colbound_kernel(const float* __restrict__ colsum, const E* __res
   if (threadIdx.x == 0) hdr[2] = red[0];
 }
 
+// One workgroup per lattice chunk: per-utterance active-tile counts, their
+// running offsets, then the packed tile coordinates.
+__global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restrict__ Teff,
+                                                        const int32_t* __restrict__ Ueff, Dims d,
+                                                        int CT, int CU, int n_chunks_u, int cap,
+                                                        int32_t* __restrict__ list,
+                                                        int32_t* __restrict__ count) {
+  __shared__ int s_base;
+  const int c = blockIdx.x;
+  const int ct0 = (c / n_chunks_u) * CT, cu0 = (c % n_chunks_u) * CU;
+  int32_t* out = list + (size_t)c * cap;
+  if (threadIdx.x == 0) s_base = 0;
+  __syncthreads();
+  for (int b = 0; b < d.B; ++b) {
+    const int tv = min(CT, Teff[b] - ct0), uv = min(CU, Ueff[b] + 1 - cu0);
+    const int nt = tv > 0 && Teff[b] > 0 ? (tv + kTileT - 1) / kTileT : 0;
+    const int nu = uv > 0 ? (uv + kTileU - 1) / kTileU : 0;
+    const int base = s_base;
+    for (int i = threadIdx.x; i < nt * nu; i += blockDim.x)
+      out[base + i] = tile_pack(b, i / nu, i % nu);
+    __syncthreads();
+    if (threadIdx.x == 0) s_base = base + nt * nu;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) count[c] = s_base;
+}
+
 __global__ void zero_kernel(uint32_t* __restrict__ p, size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
@@ -312,6 +339,14 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
       return hipErrorInvalidValue;
   }
 #undef RNNTJ_LAT
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_list(const int32_t* Teff, const int32_t* Ueff, const Dims& d, int CT, int CU,
+                            int n_chunks_u, int n_chunks, int cap, int32_t* list, int32_t* count,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(tile_list_kernel, dim3(n_chunks), dim3(256), 0, st, Teff, Ueff, d, CT, CU,
+                     n_chunks_u, cap, list, count);
   return hipGetLastError();
 }
 

@@ -48,13 +48,16 @@ def test_buffer_sizes():
     rc, tiled = _saved(16, 500, 100, 640, 1024, 1, 64, 64, 0)
     assert rc == 0
     cells = 16 * 600 * 101
-    fixed = cells * 28 + 640 * 1024 * 2 + 4 * 16 * (500 + 101) * 640
+    tiles = 16 * 32 * 13  # 16 x 8 tiles of the padded lattice, one int32 each
+    fixed = cells * 28 + 640 * 1024 * 2 + 4 * 16 * (500 + 101) * 640 + 4 * tiles
     assert fixed <= tiled <= fixed + 64 * 1024
     rc, untiled = _saved(16, 500, 100, 640, 1024, 1)
     assert rc == 0
     assert untiled - tiled >= 16 * 512 * 104 * 1024 * 2
     chunk = 16 * 64 * 64
-    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + chunk * (1024 + 640) * 2)
+    # 8 x 2 chunks, each with a list of 16 * 4 * 8 tiles, and 16 tile counts
+    lists = 16 * (16 * 4 * 8) * 4 + 256
+    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + chunk * (1024 + 640) * 2 + lists)
     assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024 + 16 * 512 * 104 * 640 * 2)
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, 0, 0) == (0, 0)
 
@@ -68,6 +71,8 @@ def test_buffer_sizes():
     ((2, 10, 2, 512, 32, 0), 2),       # fp32 H > 256
     ((2, 10, 2, 64, 30, 0), 2),        # V not a multiple of 8
     ((2, 10, 600, 64, 32, 0), 2),      # U + 1 > 512
+    ((8192, 10, 2, 64, 32, 0), 2),     # B > 8191
+    ((2, 65521, 2, 64, 32, 0), 2),     # T > 65520
 ])
 def test_shape_errors(args, code):
     assert _saved(*args)[0] == code

@@ -76,6 +76,21 @@ def test_ragged_edges(dtype):
             assert np.all(g["dPred"][b, inp.U_lens[b] + 1:] == 0)
 
 
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
+def test_bf16_wide_hidden_partial_tiles(tiles):
+    """H = 640 (the widest hidden size whose h rows are staged in LDS) with
+    label counts that leave the last 8-wide label tile of every utterance
+    partly outside the lattice: the logit / gradient store path of partly
+    valid tiles, element by element."""
+    inp = make_inputs(3, 40, 13, 640, 256, dtype="bf16", sigma=0.05, seed=11, t_range=(17, 40),
+                      u_range=(3, 13))
+    inp.U_lens[:] = [13, 9, 4]
+    print(f"[bf16 H=640 tiles={tiles}]", flush=True)
+    g = run_gpu(inp, *tiles)
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp))
+
+
 def test_data_errors_flagged():
     inp = make_inputs(4, 12, 5, 32, 24, sigma=0.4, seed=5, t_range=(4, 12), u_range=(1, 5))
     good = make_inputs(4, 12, 5, 32, 24, sigma=0.4, seed=5, t_range=(4, 12), u_range=(1, 5))
