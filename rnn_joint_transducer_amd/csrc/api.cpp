@@ -385,8 +385,10 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
         hipSuccess)
       return RNNTJ_ERR_HIP;
     h.g = z;
-    h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad; h.n_tu = p.d.U1pad / kTileU;
-    if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, st); })) != hipSuccess)
+    h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad;
+    h.tiles = at<int32_t>(saved, p.o_tiles);
+    h.tile_count = at<int32_t>(saved, p.o_tcount);
+    if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
     w.g = z;
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
@@ -432,8 +434,11 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
            })) != hipSuccess)
         return RNNTJ_ERR_HIP;
       h.g = gchunk;
-      h.ct0 = ct0; h.cu0 = cu0; h.CT = p.CT; h.CU = p.CU; h.n_tu = p.CU / kTileU;
-      if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, st); })) != hipSuccess)
+      h.ct0 = ct0; h.cu0 = cu0; h.CT = p.CT; h.CU = p.CU;
+      h.tiles = a.tiles;
+      h.tile_count = a.tile_count;
+      if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_chunk, st); })) !=
+          hipSuccess)
         return RNNTJ_ERR_HIP;
       w.g = gchunk;
       w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;

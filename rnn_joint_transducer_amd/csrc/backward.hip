@@ -93,174 +93,323 @@ __global__ __launch_bounds__(256) void grad_inplace_kernel(T* __restrict__ z, Jo
   }
 }
 
-// ------------------------------------------------------------ staging config
-
+// ------------------------------------------------------------ dh GEMM
+//
+// d_enc / d_pred contributions of the 128 cells of one active 16 x 8 tile and
+// 256 hidden columns:
+//   dh[cell, n] = sum_v dz[cell, v] W_out[n, v]                    (MFMA)
+//   dpre = (1 - h^2) dh,  d_enc[t] += sum_u dpre,  d_pred[u] += sum_t dpre
+// The kernel is persistent over (tile, hidden block) items.  dz rows and W_out
+// rows stream through LDS in K-slices of KB vocabulary entries (128-byte rows,
+// three slices resident, direct global -> LDS copies); the slice stream runs
+// on across items, so the next item's first slices load while this item's
+// epilogue runs.  4 waves (2 x 2), each 64 cells x 128 hidden columns = 2 x 4
+// blocks of 32 x 32.  Tile row r is cell (t0 + r/8, u0 + r%8).
 template <typename T>
-struct Cfg {
-  static constexpr int BK = std::is_same<T, float>::value ? 32 : 64;  // dh: k (vocab) per stage
-  static constexpr int CE = 16 / (int)sizeof(T);
-  static constexpr int LDK = BK + CE;
-  static constexpr int CH = 128 * BK / CE / 256;  // 16 B chunks per thread per operand
+struct DhCfg {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int CE = 16 / (int)sizeof(T);  // elements per 16-byte chunk
+  static constexpr int KB = 8 * CE;               // vocabulary entries per slice (128-byte rows)
+  static constexpr int KSTEPS = KB / 16;          // 16-wide k-steps per slice: bf16 4, fp32 2
+  static constexpr int NB = 256;                  // hidden columns per item
+  static constexpr int ROWS = kTileCells + NB;    // slice rows: 128 dz rows, then 256 W_out rows
+  static constexpr int SLICE = ROWS * 128;        // 48 KB
+  static constexpr int NST = 3;                   // slices resident
+  static constexpr int CPW = SLICE / 1024 / 4;    // 1 KB copies per wave per slice (12)
 };
 
-// ------------------------------------------------------------ dh GEMM
+// slot of 16-byte chunk c (0..7) of 128-byte row r: 16-byte fragment reads of
+// 16 consecutive rows at one chunk hit 16 distinct bank groups
+__device__ __forceinline__ int slot128(int r, int c) { return c ^ ((r >> 1) & 7); }
 
 template <typename T>
-__device__ __forceinline__ void dh_load(const DhArgs& a, int b, int t0, int u0, int Tl, int Ul,
-                                        int n0, int k0, u32x4 (&ra)[Cfg<T>::CH],
-                                        u32x4 (&rb)[Cfg<T>::CH]) {
-  using C = Cfg<T>;
-  const T* g = static_cast<const T*>(a.g);
-  const T* W = static_cast<const T*>(a.W);
-  const Dims& d = a.d;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < C::CH; ++q) {
-    const int c = tid + 256 * q;
-    const int row = c / (C::BK / C::CE);
-    const int col = (c % (C::BK / C::CE)) * C::CE;
-    const int k = k0 + col;
-    // A: dz rows of the cell tile, row = 8*tt + uu
-    const int t = t0 + (row >> 3), u = u0 + (row & 7);
-    if (t < Tl && u <= Ul && k < d.V)
-      ra[q] = *reinterpret_cast<const u32x4*>(
-          g + (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * d.V + k);
-    else
-      ra[q] = u32x4{0u, 0u, 0u, 0u};
-    // B: W_out rows n0 + row (hidden index), contiguous in the vocabulary
-    const int n = n0 + row;
-    if (n < d.H && k < d.V)
-      rb[q] = *reinterpret_cast<const u32x4*>(W + (size_t)n * d.V + k);
-    else
-      rb[q] = u32x4{0u, 0u, 0u, 0u};
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void stage_store(T* lds, const u32x4 (&r)[Cfg<T>::CH]) {
-  using C = Cfg<T>;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int q = 0; q < C::CH; ++q) {
-    const int c = tid + 256 * q;
-    const int row = c / (C::BK / C::CE);
-    const int col = (c % (C::BK / C::CE)) * C::CE;
-    *reinterpret_cast<u32x4*>(lds + row * C::LDK + col) = r[q];
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void dh_kernel(DhArgs a) {
-  using C = Cfg<T>;
-  __shared__ __align__(16) T As[2][128 * C::LDK];
-  __shared__ __align__(16) T Bs[2][128 * C::LDK];
+__global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
+  using C = DhCfg<T>;
+  __shared__ __align__(16) char lds[C::NST * C::SLICE];
   const Dims d = a.d;
-  const int b = blockIdx.z;
-  const int t0 = a.ct0 + (blockIdx.x / a.n_tu) * kTileT;
-  const int u0 = a.cu0 + (blockIdx.x % a.n_tu) * kTileU;
-  const int n0 = blockIdx.y * 128;
-  const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  if (t0 >= Tl || u0 > Ul) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = lane >> 5, lc = lane & 31;
-  const int wm = w >> 1, wn = w & 1;  // 64 rows x 64 cols per wave
+  const int wm = w >> 1, wn = w & 1;
+  const int H = d.H, V = d.V;
+  const T* __restrict__ G = static_cast<const T*>(a.g);
+  const T* __restrict__ W = static_cast<const T*>(a.W);
+  const int nnb = (H + C::NB - 1) / C::NB;
+  const int n_items = ld_const(a.tile_count) * nnb;
+  const int nk = (V + C::KB - 1) / C::KB;
+  const int bid = blockIdx.x, gsz = gridDim.x;
+  const int my_items = bid < n_items ? (n_items - 1 - bid) / gsz + 1 : 0;
+  const int total = my_items * nk;  // slices in this workgroup's stream
+  if (total == 0) return;
+  const uint32_t lbase = lds_addr(lds);
+  const bool use_ep = (ld_const(a.hdr + 1) & kFlagEpBad) == 0;
 
-  f32x16 acc[2][2];
+  // An item is carried as its packed tile word and hidden block (two
+  // uniform words); decode() expands it where needed (scalar loads).
+  struct Item {
+    int b, t0, u0, n0, Tl, Ul;
+  };
+  struct ItemRef {
+    int tile, nb;
+  };
+  auto item_ref = [&](int i) {  // i-th item of this workgroup
+    const int item = bid + i * gsz;
+    ItemRef r;
+    r.tile = ld_const(a.tiles + item / nnb);
+    r.nb = item % nnb;
+    return r;
+  };
+  auto decode = [&](ItemRef r) {
+    Item it;
+    int tt, tu;
+    tile_unpack(r.tile, it.b, tt, tu);
+    it.t0 = a.ct0 + tt * kTileT;
+    it.u0 = a.cu0 + tu * kTileU;
+    it.n0 = r.nb * C::NB;
+    it.Tl = ld_const(a.Teff + it.b);
+    it.Ul = ld_const(a.Ueff + it.b);
+    return it;
+  };
+
+  // Direct copies of one slice: copy q of wave w fills slice rows
+  // 8 (CPW w + q) .. +7; lane l takes row 8 (CPW w + q) + l/8 and LDS slot
+  // l%8, holding 16-byte chunk slot128(row, l%8).  Rows below 128 are dz
+  // rows of the tile (cells outside the lattice read the tile's first cell,
+  // which is always inside; their results are never used), the rest W_out
+  // rows n0 + r - 128 (clamped to H - 1).  The row + chunk source of every
+  // copy is set once per item; a slice only adds its vocabulary offset.
+  // Chunks past V (last slice, V not a multiple of KB) are clamped to the
+  // row's last chunk; their fragments are zeroed before the MFMAs.
+  // dz rows: offsets (elements) from the item's first cell row; W_out rows:
+  // offsets from W_out.  Both fit 32 bits (a tile spans 16 frames of one
+  // chunk; W_out is at most 768 rows).
+  const T* gbase = G;
+  uint32_t coff[C::CPW];
+  auto set_sources = [&](ItemRef ref) {
+    const Item it = decode(ref);
+    gbase = G + (((size_t)it.b * a.CT + (it.t0 - a.ct0)) * a.CU + (it.u0 - a.cu0)) * V;
+#pragma unroll
+    for (int q = 0; q < C::CPW; ++q) {
+      const int ins = C::CPW * w + q;
+      const int r = 8 * ins + (lane >> 3);
+      const int c = slot128(r, lane & 7);
+      if (ins < kTileCells / 8) {  // uniform: the first 16 copies hold dz rows
+        int dt = r >> 3, du = r & 7;
+        const bool ok = it.t0 + dt < it.Tl && it.u0 + du <= it.Ul;
+        dt = ok ? dt : 0;
+        du = ok ? du : 0;
+        coff[q] = (uint32_t)((dt * a.CU + du) * V + c * C::CE);
+      } else {
+        const int n = min(it.n0 + r - kTileCells, H - 1);
+        coff[q] = (uint32_t)(n * V + c * C::CE);
+      }
+    }
+  };
+  auto issue = [&](int s, int buf) {
+    const int k0 = s * C::KB;
+    const uint32_t st = lbase + buf * C::SLICE + C::CPW * w * 1024;
+    const bool tail = k0 + C::KB > V;
+#pragma unroll
+    for (int q = 0; q < C::CPW; ++q) {
+      const T* base = (C::CPW * w + q < kTileCells / 8) ? gbase : W;
+      uint32_t off = coff[q] + k0;
+      if (tail) {  // chunks past V re-read the row's last chunk
+        const int r = 8 * (C::CPW * w + q) + (lane >> 3);
+        const int c = slot128(r, lane & 7);
+        if (k0 + c * C::CE + C::CE > V) off = coff[q] - c * C::CE + (V - C::CE);
+      }
+      dma16(base + off, st + q * 1024);
+    }
+  };
+
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  u32x4 ra[C::CH], rb[C::CH];
-  const int nk = (d.V + C::BK - 1) / C::BK;
-  dh_load<T>(a, b, t0, u0, Tl, Ul, n0, 0, ra, rb);
-  stage_store<T>(As[0], ra);
-  stage_store<T>(Bs[0], rb);
-  __syncthreads();
-  for (int kb = 0; kb < nk; ++kb) {
-    const int cur = kb & 1;
-    const bool has_next = kb + 1 < nk;
-    if (has_next) dh_load<T>(a, b, t0, u0, Tl, Ul, n0, (kb + 1) * C::BK, ra, rb);
-#pragma unroll
-    for (int kk = 0; kk < C::BK / 16; ++kk) {
-      Frag8<T> fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = load_frag(&As[cur][(64 * wm + 32 * i + lc) * C::LDK + kk * 16 + 8 * kh]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = load_frag(&Bs[cur][(64 * wn + 32 * j + lc) * C::LDK + kk * 16 + 8 * kh]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) mma_step(acc[i][j], fa[i], fb[j]);
-    }
-    if (has_next) {
-      stage_store<T>(As[cur ^ 1], ra);
-      stage_store<T>(Bs[cur ^ 1], rb);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: dpre = (1 - h^2) * dh, h rebuilt from enc / pred
-  const T* enc = static_cast<const T*>(a.enc);
-  const T* pred = static_cast<const T*>(a.pred);
-  const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
-  // wave rows: 64*wm + 32*i + acc_row(r, kh)  <->  tt = 8*wm + 4*i + r/4, uu = 4*kh + r%4
-  float pred_sum[2][4];  // [j][r%4]: sum over this wave's frames, per label position
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) pred_sum[j][q] = 0.f;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + 64 * wn + 32 * j + lc;
-    const bool nvalid = n < d.H;
+  Frag8<T> fa[2][2], fb[2][4];
+  // fragments of k-step kk of stream slice g (buffer g % NST)
+  auto rd = [&](int g, int kk, int fbuf) {
+    const char* sl = lds + (g % C::NST) * C::SLICE;
+    const int kbase = (g % nk) * C::KB + 16 * kk + 8 * kh;  // this lane's first k
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const int r = 64 * wm + 32 * i + lc;
+      const char* row = sl + r * 128;
+      if constexpr (C::kBf16) {
+        fa[fbuf][i].v = *reinterpret_cast<const u32x4*>(row + (slot128(r, 2 * kk + kh) << 4));
+      } else {
+        fa[fbuf][i].lo = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh) << 4));
+        fa[fbuf][i].hi = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh + 1) << 4));
+      }
+      if (kbase >= V) zero_frag(fa[fbuf][i]);  // vocabulary tail
+    }
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {  // frame within the 32-row block
-        const int t = t0 + 8 * wm + 4 * i + q4;
-        float enc_sum = 0.f;
-        const bool tn = nvalid && t < Tl;
-        const size_t ie = ((size_t)b * d.T + t) * d.H + n;
-        const float ev = tn ? (use_ep ? a.Eexp[ie] : ElemTraits<T>::to_f32(enc[ie])) : 0.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {  // label position within the half
-          const int r = 4 * q4 + q;
-          const int u = u0 + 4 * kh + q;
-          float v = 0.f;
-          if (tn && u <= Ul) {
-            const size_t ip = ((size_t)b * d.U1 + u) * d.H + n;
-            const float h = use_ep
-                                ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + ev * a.Pexp[ip])
-                                : fast_tanh(ev + ElemTraits<T>::to_f32(pred[ip]));
-            v = (1.0f - h * h) * acc[i][j][r];
-          }
-          enc_sum += v;
-          pred_sum[j][q] += v;
-        }
-        // the other 4 label positions of this frame live in lane l ^ 32
-        enc_sum += __shfl_xor(enc_sum, 32);
-        if (kh == 0 && nvalid && t < Tl)
-          atomicAdd(&a.d_enc[((size_t)b * d.T + t) * d.H + n], enc_sum);
+    for (int j = 0; j < 4; ++j) {
+      const int r = kTileCells + 128 * wn + 32 * j + lc;
+      const char* row = sl + r * 128;
+      if constexpr (C::kBf16) {
+        fb[fbuf][j].v = *reinterpret_cast<const u32x4*>(row + (slot128(r, 2 * kk + kh) << 4));
+      } else {
+        fb[fbuf][j].lo = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh) << 4));
+        fb[fbuf][j].hi = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh + 1) << 4));
       }
     }
-  }
+  };
+  auto mm = [&](int fbuf) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + 64 * wn + 32 * j + lc;
-    if (n < d.H) {
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma_step(acc[i][j], fa[fbuf][i], fb[fbuf][j]);
+  };
+
+  // epilogue inputs, loaded during an item's last slice: for this lane's
+  // columns j and frames (i, q4) / label positions q, e^{2 enc}, e^{2 pred}
+  // (or enc, pred when those exponentials could overflow)
+  float ex[2][4][4], px[4][4];  // [i][q4][j], [q][j]
+  auto load_ep_from = [&](const Item& it, auto src_e, auto src_p) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = min(it.n0 + 128 * wn + 32 * j + lc, H - 1);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int t = min(it.t0 + 8 * wm + 4 * i + q4, d.T - 1);
+          ex[i][q4][j] = src_e(((size_t)it.b * d.T + t) * H + n);
+        }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int u = u0 + 4 * kh + q;
-        if (u <= Ul) atomicAdd(&a.d_pred[((size_t)b * d.U1 + u) * d.H + n], pred_sum[j][q]);
+        const int u = min(it.u0 + 4 * kh + q, d.U1 - 1);
+        px[q][j] = src_p(((size_t)it.b * d.U1 + u) * H + n);
       }
+    }
+  };
+  auto load_ep = [&](const Item& it) {
+    if (use_ep) {
+      load_ep_from(it, [&](size_t i) { return a.Eexp[i]; }, [&](size_t i) { return a.Pexp[i]; });
+    } else {
+      const T* enc = static_cast<const T*>(a.enc);
+      const T* pred = static_cast<const T*>(a.pred);
+      load_ep_from(it, [&](size_t i) { return ElemTraits<T>::to_f32(enc[i]); },
+                   [&](size_t i) { return ElemTraits<T>::to_f32(pred[i]); });
+    }
+  };
+  // dpre = (1 - h^2) dh, reduced over label positions (d_enc) and frames
+  // (d_pred) in registers, then added with float32 atomics
+  auto epilogue = [&](const Item& it) {
+    float psum[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) psum[j][q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = it.n0 + 128 * wn + 32 * j + lc;
+      const bool nvalid = n < H;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int t = it.t0 + 8 * wm + 4 * i + q4;
+          const bool tv = nvalid && t < it.Tl;
+          float esum = 0.f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int u = it.u0 + 4 * kh + q;
+            const float hval = use_ep
+                                   ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + ex[i][q4][j] * px[q][j])
+                                   : fast_tanh(ex[i][q4][j] + px[q][j]);
+            const float v = (tv && u <= it.Ul) ? (1.0f - hval * hval) * acc[i][j][4 * q4 + q] : 0.f;
+            esum += v;
+            psum[j][q] += v;
+            acc[i][j][4 * q4 + q] = 0.f;
+          }
+          // the other 4 label positions of this frame live in lane l ^ 32
+          esum += __shfl_xor(esum, 32);
+          if (kh == 0 && tv) atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], esum);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int n = it.n0 + 128 * wn + 32 * j + lc;
+      if (n < H) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = it.u0 + 4 * kh + q;
+          if (u <= it.Ul) atomicAdd(&a.d_pred[((size_t)it.b * d.U1 + u) * H + n], psum[j][q]);
+        }
+      }
+    }
+  };
+
+  // ---- the slice stream: slice g is slice g % nk of item g / nk.  Two
+  // cursors walk it: the copy cursor (slices are issued two ahead) and the
+  // compute cursor; each holds its item and loads the following one early
+  // (scalar loads, waited for only at first use).
+  ItemRef cur = item_ref(0);
+  ItemRef cur_next = my_items > 1 ? item_ref(1) : cur;
+  ItemRef iss_next = cur_next;
+  int iss_i = 0, iss_s = 0, iss_g = 0;
+  set_sources(cur);
+  auto issue_next = [&]() {  // copy slice iss_g into buffer iss_g % NST
+    issue(iss_s, iss_g % C::NST);
+    ++iss_g;
+    if (++iss_s == nk) {
+      iss_s = 0;
+      if (++iss_i < my_items) {
+        set_sources(iss_next);
+        if (iss_i + 1 < my_items) iss_next = item_ref(iss_i + 1);
+      }
+    }
+  };
+  issue_next();
+  if (total > 1) {
+    issue_next();
+    wait_vm<C::CPW>();  // slice 0 landed, slice 1 may be in flight
+  } else {
+    wait_vm<0>();
+  }
+  __builtin_amdgcn_s_barrier();
+  rd(0, 0, 0);
+  // MFMAs of stream slice g, with the fragment reads one k-step ahead
+  auto slice = [&](int g) {
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      const int fcur = kk & 1;
+      if (kk + 1 < C::KSTEPS) {
+        rd(g, kk + 1, fcur ^ 1);
+      } else if (g + 1 < total) {
+        // slice g+1 has landed (nothing newer is in flight) and every wave
+        // is past slice g-1: refill that buffer with slice g+2
+        wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        if (iss_g < total) issue_next();
+        rd(g + 1, 0, fcur ^ 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fcur);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  for (int g = 0; g < total; ++g) {
+    const int s = g % nk;
+    // during an item's last slice its epilogue inputs load
+    if (s == nk - 1) load_ep(decode(cur));
+    slice(g);
+    if (s == nk - 1) {
+      epilogue(decode(cur));
+      const int li = g / nk;
+      cur = cur_next;
+      if (li + 2 < my_items) cur_next = item_ref(li + 2);
     }
   }
 }
+
 
 // ------------------------------------------------------------ dW GEMM
 
@@ -490,8 +639,12 @@ hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_dh(const DhArgs& a, bool bf16, hipStream_t st) {
-  dim3 grid((a.CT / kTileT) * a.n_tu, (a.d.H + 127) / 128, a.d.B), block(256);
+hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) {
+  const int nnb = (a.d.H + DhCfg<float>::NB - 1) / DhCfg<float>::NB;
+  const long long items = (long long)max_tiles * nnb;
+  if (items <= 0) return hipSuccess;
+  const int ncu = device_cu_count();
+  dim3 grid((unsigned)(items < ncu ? items : ncu)), block(256);
   if (bf16)
     hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, a);
   else

@@ -183,6 +183,35 @@ __device__ __forceinline__ Frag8<float> load_frag_T(const float* tile, int ld, i
   return f;
 }
 
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's bytes land at LDS address lds_base + 16 l.  lds_base must be the
+// same in every lane of the wave.  Issued as inline assembly, so the
+// compiler does not track it: the caller waits for it with wait_vm<N>()
+// (vmcnt counts these copies like any other vector memory access) and makes
+// it visible to the other waves with a barrier.
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc),
+               "s"(lds_base)
+               : "memory");
+}
+// wait until at most N vector memory accesses of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Load of a value the kernel never writes, through the constant address
+// space: with a wave-uniform address it becomes a scalar load, which neither
+// waits for nor is waited on by the vector-memory counter.
+template <typename P>
+__device__ __forceinline__ P ld_const(const P* p) {
+  return *(const __attribute__((address_space(4))) P*)p;
+}
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
+}
+
 // Row of accumulator register r of a 32x32 block for lane-half kh = l/32
 // (column is l % 32): rows 8*(r/4) + 4*kh + (r%4).
 __device__ __forceinline__ int acc_row(int r, int kh) { return 8 * (r >> 2) + 4 * kh + (r & 3); }

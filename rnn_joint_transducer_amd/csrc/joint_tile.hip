@@ -630,8 +630,8 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
 
 // ------------------------------------------------------------------ dispatch
 
-// compute units of the current device (one resident workgroup each)
-static int cu_count() {
+// compute units of the current device
+int device_cu_count() {
   static int cache[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -656,7 +656,7 @@ template <typename T, int MODE>
 static hipError_t launch_mode(const JointArgs& a, int n_items, hipStream_t st) {
   using C = StageCfg<T>;
   const int nks = a.d.H / 16;
-  const int ncu = cu_count();
+  const int ncu = device_cu_count();
   dim3 grid(n_items < ncu ? n_items : ncu);
   auto exact = [&](int KS) {
     return nks == KS && a.d.H % C::BK == 0 && a.d.V % kVocabTile == 0;

@@ -101,8 +101,12 @@ hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st);
 // in place.
 hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, hipStream_t st);
 
-// dh = dz @ W_out^T for one chunk; dpre = (1 - h^2) dh summed into d_enc over
-// u and into d_pred over t.
+// dh = dz @ W_out^T for the active tiles of one chunk; dpre = (1 - h^2) dh
+// summed into d_enc over u and into d_pred over t.
+// Compute units of the current device (persistent launches use one or two
+// workgroups per unit).
+int device_cu_count();
+
 struct DhArgs {
   const void* g;      // [B, CT, CU, V] logit gradients of the chunk
   const void* W;      // [H, V]
@@ -114,11 +118,14 @@ struct DhArgs {
   const float* Eexp;
   const float* Pexp;
   Dims d;
-  int ct0, cu0, CT, CU, n_tu;
+  const int32_t* tiles;       // active tiles of the chunk
+  const int32_t* tile_count;
+  int ct0, cu0, CT, CU;
   float* d_enc;
   float* d_pred;
 };
-hipError_t launch_dh(const DhArgs& a, bool bf16, hipStream_t st);
+// Persistent launch; max_tiles bounds the entries of the tile list.
+hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st);
 
 // d_W_out += h^T dz and d_b64 += column sums of dz (float64) over one chunk.
 struct DwArgs {
