@@ -79,8 +79,10 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_lse = o;    o = align_up(o + 4 * cells);
   q.o_lb = o;     o = align_up(o + 4 * cells);
   q.o_le = o;     o = align_up(o + 4 * cells);
-  q.o_alpha = o;  o = align_up(o + 8 * cells);
-  q.o_beta = o;   o = align_up(o + 8 * cells);
+  // alpha / beta carry a trash area of 512 float64 past the cells (slots of
+  // the lattice sweep that fall outside the lattice are stored there)
+  q.o_alpha = o;  o = align_up(o + 8 * (cells + 512));
+  q.o_beta = o;   o = align_up(o + 8 * (cells + 512));
   q.o_E = o;      o = align_up(o + 4 * (size_t)B * T * H);
   q.o_P = o;      o = align_up(o + 4 * (size_t)B * (U + 1) * H);
   q.o_cs = o;     o = align_up(o + 4 * (size_t)V);

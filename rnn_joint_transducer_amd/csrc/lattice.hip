@@ -56,22 +56,27 @@ __device__ __forceinline__ double wave_shl1(double v, double fill) {
 // Lane l owns the NU consecutive label positions u = NU*l .. NU*l + NU-1, so
 // on each anti-diagonal the u-1 (alpha) or u+1 (beta) neighbour is in the
 // same lane except at the block edge, which one DPP lane shift supplies.
-// LB / LE of diagonal dg+PD are loaded while diagonal dg is computed; every
-// load is issued unconditionally (clamped address) so that the hardware
-// load counter can wait for exactly the oldest ones.
-template <int NU, int PD>
-__global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ LB,
-                                                     const float* __restrict__ LE,
-                                                     const int32_t* __restrict__ Teff,
-                                                     const int32_t* __restrict__ Ueff, Dims d,
-                                                     double* __restrict__ alpha,
-                                                     double* __restrict__ beta,
-                                                     double* __restrict__ logP,
-                                                     float* __restrict__ costs) {
-  const int b = blockIdx.x, dir = blockIdx.y, l = threadIdx.x;
+// One wave per (utterance, direction); DIR = 0 sweeps alpha forward over the
+// diagonals, DIR = 1 beta backward.  The diagonals are taken in chunks of CH:
+// the LB / LE operands of the next chunk are loaded into registers while this
+// chunk is computed, and the chunk's results are stored at its end.  Every
+// load and store is issued unconditionally (clamped loads; results of slots
+// outside the lattice go to a per-lane trash slot past the array), so the
+// number of memory operations in flight is the same on every path and the
+// compiler's waits only cover what each step really needs.
+template <int DIR, int NU, int CH>
+__device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
+                                              const float* __restrict__ LE,
+                                              const int32_t* __restrict__ Teff,
+                                              const int32_t* __restrict__ Ueff, const Dims& d,
+                                              double* __restrict__ alpha,
+                                              double* __restrict__ beta,
+                                              double* __restrict__ logP,
+                                              float* __restrict__ costs) {
+  const int b = blockIdx.x, l = threadIdx.x;
   const int Tl = Teff[b], Ul = Ueff[b];
   if (Tl == 0) {  // invalid utterance
-    if (dir == 0 && l == 0) {
+    if (DIR == 0 && l == 0) {
       costs[b] = __builtin_nanf("");
       logP[b] = __builtin_nan("");
     }
@@ -81,8 +86,10 @@ __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ L
   const size_t base = (size_t)b * d.DG * d.U1;
   const float* lb = LB + base;
   const float* le = LE + base;
-  double* out = (dir == 0 ? alpha : beta) + base;
-  const int last = d.DG * d.U1 - 1;  // clamp for the unconditional loads
+  double* arr = DIR == 0 ? alpha : beta;
+  double* out = arr + base;
+  double* trash = arr + (size_t)d.B * d.DG * d.U1 + NU * l;
+  const int last = d.DG * d.U1 - 1;  // clamp for the loads
 
   double prev[NU];
 #pragma unroll
@@ -90,88 +97,115 @@ __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ L
 
   // operands of step s for slot j (diagonal dg = s for alpha, nd-1-s for beta):
   //   alpha: LB(t-1,u), LE(t,u-1) on diagonal dg-1;  beta: LB(t,u), LE(t,u) on dg
-  auto fetch = [&](int s, float (&fb)[NU], float (&fe)[NU]) {
-    const int dg = dir == 0 ? s - 1 : nd - 1 - s;
+  float cb[CH][NU], ce[CH][NU], nb[CH][NU], ne[CH][NU];
+  auto fetch = [&](int s0, float (&fb)[CH][NU], float (&fe)[CH][NU]) {
 #pragma unroll
-    for (int j = 0; j < NU; ++j) {
-      const int u = NU * l + j;
-      int ib = dg * d.U1 + u, ie = dir == 0 ? ib - 1 : ib;
-      ib = ib < 0 ? 0 : (ib > last ? last : ib);
-      ie = ie < 0 ? 0 : (ie > last ? last : ie);
-      fb[j] = lb[ib];
-      fe[j] = le[ie];
+    for (int c = 0; c < CH; ++c) {
+      const int dg = DIR == 0 ? s0 + c - 1 : nd - 1 - s0 - c;
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        const int u = NU * l + j;
+        int ib = dg * d.U1 + u, ie = DIR == 0 ? ib - 1 : ib;
+        ib = ib < 0 ? 0 : (ib > last ? last : ib);
+        ie = ie < 0 ? 0 : (ie > last ? last : ie);
+        fb[c][j] = lb[ib];
+        fe[c][j] = le[ie];
+      }
     }
   };
 
-  float rb[PD][NU], re[PD][NU];
+  // one chunk: steps s0 .. s0+CH-1 from (ub, ue) while the next chunk's
+  // operands load into (fb, fe)
+  auto chunk = [&](int s0, const float (&ub)[CH][NU], const float (&ue)[CH][NU],
+                   float (&fb)[CH][NU], float (&fe)[CH][NU]) {
+    // next chunk's operands (loads past the lattice are clamped and unused),
+    // kept issued here, ahead of this chunk's steps
+    fetch(s0 + CH, fb, fe);
+    __builtin_amdgcn_sched_barrier(0);
+    double res[CH][NU];
 #pragma unroll
-  for (int p = 0; p < PD; ++p) fetch(p, rb[p], re[p]);
-
-  for (int s0 = 0; s0 < nd; s0 += PD) {
+    for (int c = 0; c < CH; ++c) {
+      const int s = s0 + c;
+      const int dg = DIR == 0 ? s : nd - 1 - s;
+      // neighbour on the previous diagonal across the lane edge
+      const double edge =
+          DIR == 0 ? wave_shr1(prev[NU - 1], kNegInfD) : wave_shl1(prev[0], kNegInfD);
 #pragma unroll
-    for (int p = 0; p < PD; ++p) {
-      const int s = s0 + p;
-      if (s < nd) {  // uniform across the wave
-        float cb[NU], ce[NU];
+      for (int j = 0; j < NU; ++j) {
+        const int u = NU * l + j;
+        const int t = dg - u;
+        const bool valid = (s < nd) & (u <= Ul) & (t >= 0) & (t < Tl);
+        double v;
+        if (DIR == 0) {
+          // alpha(t-1,u) + LB(t-1,u),  alpha(t,u-1) + LE(t,u-1)
+          const double nbv = j > 0 ? prev[j > 0 ? j - 1 : 0] : edge;
+          const double ft = (t >= 1) ? prev[j] + (double)ub[c][j] : kNegInfD;
+          const double fu = (u >= 1) ? nbv + (double)ue[c][j] : kNegInfD;
+          v = log_add_exp(ft, fu);
+          v = (dg == 0) ? 0.0 : v;
+        } else {
+          // beta(t+1,u) + LB(t,u),  beta(t,u+1) + LE(t,u)
+          const double nbv = j + 1 < NU ? prev[j + 1 < NU ? j + 1 : 0] : edge;
+          const double ft = (t + 1 < Tl) ? prev[j] + (double)ub[c][j] : kNegInfD;
+          const double fu = (u < Ul) ? nbv + (double)ue[c][j] : kNegInfD;
+          v = log_add_exp(ft, fu);
+          v = (t == Tl - 1 && u == Ul) ? (double)ub[c][j] : v;
+        }
+        res[c][j] = valid ? v : kNegInfD;
+      }
+      // the diagonal is complete: it becomes the previous one
+#pragma unroll
+      for (int j = 0; j < NU; ++j) prev[j] = res[c][j];
+      if (DIR == 0 && s == nd - 1) {
+        // final cell (T'-1, U') lies on the last diagonal
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
-          cb[j] = rb[p][j];
-          ce[j] = re[p][j];
-        }
-        fetch(s + PD, rb[p], re[p]);
-        const int dg = dir == 0 ? s : nd - 1 - s;
-        double cur[NU];
-        if (dir == 0) {
-          // alpha(t, u-1) on the previous diagonal
-          const double edge = wave_shr1(prev[NU - 1], kNegInfD);
-#pragma unroll
-          for (int j = 0; j < NU; ++j) {
-            const int u = NU * l + j;
-            const int t = dg - u;
-            const bool valid = (u <= Ul) & (t >= 0) & (t < Tl);
-            const double nb = j > 0 ? prev[j > 0 ? j - 1 : 0] : edge;
-            const double ft = (t >= 1) ? prev[j] + (double)cb[j] : kNegInfD;
-            const double fu = (u >= 1) ? nb + (double)ce[j] : kNegInfD;
-            double v = log_add_exp(ft, fu);
-            v = (dg == 0) ? 0.0 : v;
-            v = valid ? v : kNegInfD;
-            if (valid) out[(size_t)dg * d.U1 + u] = v;
-            cur[j] = v;
-          }
-        } else {
-          // beta(t, u+1) on the previous (later) diagonal
-          const double edge = wave_shl1(prev[0], kNegInfD);
-#pragma unroll
-          for (int j = 0; j < NU; ++j) {
-            const int u = NU * l + j;
-            const int t = dg - u;
-            const bool valid = (u <= Ul) & (t >= 0) & (t < Tl);
-            const double nb = j + 1 < NU ? prev[j + 1 < NU ? j + 1 : 0] : edge;
-            const double ft = (t + 1 < Tl) ? prev[j] + (double)cb[j] : kNegInfD;
-            const double fu = (u < Ul) ? nb + (double)ce[j] : kNegInfD;
-            double v = log_add_exp(ft, fu);
-            v = (t == Tl - 1 && u == Ul) ? (double)cb[j] : v;
-            v = valid ? v : kNegInfD;
-            if (valid) out[(size_t)dg * d.U1 + u] = v;
-            cur[j] = v;
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < NU; ++j) prev[j] = cur[j];
-        if (dir == 0 && s == nd - 1) {
-          // final cell (T'-1, U') lies on the last diagonal
-#pragma unroll
-          for (int j = 0; j < NU; ++j) {
-            if (NU * l + j == Ul) {
-              const double lp = cur[j] + (double)lb[(size_t)dg * d.U1 + Ul];
-              logP[b] = lp;
-              costs[b] = (float)(-lp);
-            }
+          if (NU * l + j == Ul) {
+            const double lp = prev[j] + (double)lb[(size_t)dg * d.U1 + Ul];
+            logP[b] = lp;
+            costs[b] = (float)(-lp);
           }
         }
       }
     }
+    // store the chunk (slots outside the lattice go to the trash slot)
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int s = s0 + c;
+      const int dg = DIR == 0 ? s : nd - 1 - s;
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        const int u = NU * l + j;
+        const int t = dg - u;
+        const bool valid = (s < nd) & (u <= Ul) & (t >= 0) & (t < Tl);
+        double* dst = valid ? out + (size_t)dg * d.U1 + u : trash + j;
+        *dst = res[c][j];
+      }
+    }
+  };
+
+  // chunks alternate between the two operand buffers (no register copies)
+  fetch(0, cb, ce);
+  for (int s0 = 0; s0 < nd; s0 += 2 * CH) {
+    chunk(s0, cb, ce, nb, ne);
+    if (s0 + CH < nd) chunk(s0 + CH, nb, ne, cb, ce);  // uniform
   }
+}
+
+// both directions of every utterance in one launch: blockIdx.y = direction
+template <int NU, int CH>
+__global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ LB,
+                                                     const float* __restrict__ LE,
+                                                     const int32_t* __restrict__ Teff,
+                                                     const int32_t* __restrict__ Ueff, Dims d,
+                                                     double* __restrict__ alpha,
+                                                     double* __restrict__ beta,
+                                                     double* __restrict__ logP,
+                                                     float* __restrict__ costs) {
+  if (blockIdx.y == 0)
+    lattice_sweep<0, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
+  else
+    lattice_sweep<1, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
 }
 
 __global__ void validate_kernel(const int32_t* __restrict__ T_lens,
@@ -321,20 +355,22 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
                           double* logP, float* costs, hipStream_t st) {
   const int nu = (d.U1 + 63) / 64;
   dim3 grid(d.B, 2), block(64);
-#define RNNTJ_LAT(N)                                                                       \
-  case N:                                                                                  \
-    hipLaunchKernelGGL((lattice_kernel<N, (N <= 4 ? 6 : 3)>), grid, block, 0, st, LB, LE, \
-                       Teff, Ueff, d, alpha, beta, logP, costs);                           \
+  // chunk length: 2 loads + 1 store per slot and step stay within the
+  // 63 memory operations the wave can track
+#define RNNTJ_LAT(N, CH)                                                                 \
+  case N:                                                                                \
+    hipLaunchKernelGGL((lattice_kernel<N, CH>), grid, block, 0, st, LB, LE, Teff, Ueff, d, \
+                       alpha, beta, logP, costs);                                        \
     break;
   switch (nu) {
-    RNNTJ_LAT(1)
-    RNNTJ_LAT(2)
-    RNNTJ_LAT(3)
-    RNNTJ_LAT(4)
-    RNNTJ_LAT(5)
-    RNNTJ_LAT(6)
-    RNNTJ_LAT(7)
-    RNNTJ_LAT(8)
+    RNNTJ_LAT(1, 16)
+    RNNTJ_LAT(2, 8)
+    RNNTJ_LAT(3, 6)
+    RNNTJ_LAT(4, 4)
+    RNNTJ_LAT(5, 4)
+    RNNTJ_LAT(6, 3)
+    RNNTJ_LAT(7, 3)
+    RNNTJ_LAT(8, 2)
     default:
       return hipErrorInvalidValue;
   }
