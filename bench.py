@@ -36,7 +36,7 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 MFMA_KERNELS = ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
 DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (64, 64, 128),
-                 "medium_lv": (64, 64, 128), "long": (64, 64, 128)}
+                 "medium_lv": (64, 64, 256), "long": (64, 64, 256)}
 
 
 def parse():

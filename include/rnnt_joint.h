@@ -33,17 +33,20 @@
  *     enc, pred, W_out and b_out all have type `dtype`; costs and every
  *     gradient are float32 whatever `dtype` is.
  *   - Modes: tile_t == 0 and tile_u == 0 selects the UNTILED mode: the forward
- *     stores the logits (dtype) in `saved` and the backward turns them into
- *     logit gradients in place, so one forward feeds exactly one backward.
+ *     stores the logits (dtype) in `saved` and the backward forms the logit
+ *     gradients from them as it goes (`saved` is read, not modified).
  *     Otherwise the TILED mode stores only per-cell scalars and recomputes the
  *     joint and logits in the backward, one lattice chunk of tile_t frames x
  *     tile_u label positions (all utterances) at a time; 0 on one axis means
  *     the whole axis.  tile_t must be a multiple of 16 and tile_u of 8.
- *     tile_v is the vocabulary tile over which the online max / log-sum-exp is
- *     carried: 0 selects the default (128); 128 is supported.
+ *     tile_v bounds the vocabulary columns of one step of the online max /
+ *     log-sum-exp (which never materialises more than one step of logits per
+ *     cell): 0 or any multiple of 128.  The kernels step by 128 columns, which
+ *     is within every accepted bound, so tile_v changes neither memory nor
+ *     results (the order of the floating-point sums is the same).
  *   - Limits (else RNNTJ_ERR_UNSUPPORTED): H a multiple of 16 with
  *     16 <= H <= 768 for bf16 and H <= 256 for fp32; V a multiple of 8,
- *     8 <= V; U + 1 <= 512; B <= 8191; T <= 65520.
+ *     8 <= V <= 262144; U + 1 <= 512; B <= 8191; T <= 65520.
  *   - Host-side argument errors (null pointers, bad shapes, blank outside
  *     [0,V), unsupported tiles, workspace too small) return a nonzero code
  *     before anything is enqueued; outputs are untouched.
@@ -107,7 +110,8 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
  * [B, tile_t, tile_u, H] in dtype (the whole padded lattice when untiled)
  * and, in the tiled mode, that chunk's logit gradients [B, tile_t, tile_u, V]
  * in dtype plus the active-tile list of every chunk (int32, one word per
- * 16 x 8 tile).  Writes *out; returns a status code.
+ * 16 x 8 tile); in the untiled mode, 16 bytes of logit-gradient constants per
+ * cell of the padded lattice.  Writes *out; returns a status code.
  */
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
                                     int tile_t, int tile_u, int tile_v, int pass,
@@ -134,8 +138,8 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out,
  * d_b_out [V] (float32) with the gradients of sum_b grad_costs[b] * costs[b]
  * (grad_costs float32 [B] on the device, or NULL for all ones).  Takes the
  * same inputs, sizes and tiles as the forward that filled `saved`; the whole
- * batch is handled in one call.  In the untiled mode it consumes the logits
- * stored in `saved`.  Entries of d_enc / d_pred past each utterance's lengths
+ * batch is handled in one call; `saved` is only read, so one forward may
+ * feed several backward calls.  Entries of d_enc / d_pred past each utterance's lengths
  * are zero.  Returns a status code (host-side checks and launch errors only).
  */
 int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,

@@ -175,7 +175,9 @@ _FN = None
 
 def rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, tile_t=0,
                     tile_u=0, tile_v=0):
-    """Per-utterance costs [B] with autograd support (one backward per forward)."""
+    """Per-utterance costs [B] with autograd support.  The saved forward state is
+    only read by the backward, so a graph kept with retain_graph=True may be
+    differentiated more than once."""
     global _FN
     if _FN is None:
         _FN = _make_function()

@@ -35,7 +35,7 @@ struct Plan {
       o_cs, o_tiles, o_tcount, o_z;
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
-  size_t o_ws_db, o_ws_g, o_ws_h, o_ws_tiles, o_ws_tcount;  // backward workspace layout
+  size_t o_ws_db, o_ws_g, o_ws_h, o_ws_tiles, o_ws_tcount, o_ws_cc;  // backward workspace layout
   int cap_all;                // active-tile list capacity of the whole lattice
   int n_cu_chunks, n_chunks;  // backward chunk grid (tiled mode)
   int cap_chunk;              // active-tile list capacity of one chunk
@@ -48,11 +48,13 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   if (tile_t < 0 || tile_u < 0 || tile_v < 0) return RNNTJ_ERR_ARG;
   const bool bf16 = dtype == RNNTJ_BF16;
   if (H % 16 != 0 || H > (bf16 ? 768 : 256)) return RNNTJ_ERR_UNSUPPORTED;
-  if (V % 8 != 0 || V < 8) return RNNTJ_ERR_UNSUPPORTED;
+  if (V % 8 != 0 || V < 8 || V > kMaxV) return RNNTJ_ERR_UNSUPPORTED;
   if (U + 1 > 512) return RNNTJ_ERR_UNSUPPORTED;
   if (B > 8191 || T > 65520) return RNNTJ_ERR_UNSUPPORTED;  // packed tile coordinates
   if (tile_t % kTileT != 0 || tile_u % kTileU != 0) return RNNTJ_ERR_UNSUPPORTED;
-  if (tile_v != 0 && tile_v != kVocabTile) return RNNTJ_ERR_UNSUPPORTED;
+  // tile_v bounds the vocabulary columns of one online log-sum-exp step; the
+  // kernels step by kVocabTile, which is within any accepted tile_v
+  if (tile_v % kVocabTile != 0) return RNNTJ_ERR_UNSUPPORTED;
   Plan& q = *p;
   q.bf16 = bf16;
   q.elem = bf16 ? 2 : 4;
@@ -105,7 +107,9 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
   q.o_ws_tiles = q.o_ws_h + align_up(q.elem * (size_t)B * q.CT * q.CU * H);
   q.o_ws_tcount = q.o_ws_tiles + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks * q.cap_chunk));
-  q.ws_bwd = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
+  q.o_ws_cc = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
+  // untiled: logit-gradient constants of every row of the active tiles
+  q.ws_bwd = q.o_ws_cc + (q.untiled ? align_up(16 * (size_t)q.cap_all * kTileCells) : 0);
   return RNNTJ_OK;
 }
 
@@ -365,38 +369,50 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   h.d_pred = d_pred;
   DwArgs w = {};
   w.h = hchunk;
-  w.Teff = Teff;
-  w.Ueff = Ueff;
+  w.gcost = grad_costs;
   w.d = p.d;
   w.d_W = d_W_out;
   w.d_b64 = db64;
-  // split-K so that the weight-gradient GEMM has >= 1024 workgroups
-  auto set_ksplit = [&](int CT, int CU) {
-    const int tiles = B * ((H + 127) / 128) * ((V + 127) / 128);
-    const int max_stages = (CT / kTileT) * (CU / kTileU) * 2;
-    int k = (1024 + tiles - 1) / tiles;
-    w.ksplit = k < 1 ? 1 : (k > max_stages ? max_stages : k);
+  h.gcost = grad_costs;
+  // split-K of the weight-gradient GEMM: about two workgroups per compute
+  // unit, at most one run of the tile list per tile
+  // split-K runs of the dW GEMM: one workgroup per compute unit (one round),
+  // fewest float32 partial sums per output element
+  auto kparts_for = [&](int max_tiles) {
+    const int per = ((H + 127) / 128) * ((V + 255) / 256);
+    int k = device_cu_count() / per;
+    return k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
   };
   auto finalize = [&] {
     return timed("db_finalize", st, [&] { return launch_db_finalize(db64, d_b_out, V, st); });
   };
 
   if (p.untiled) {
+    // the stored logits are turned into logit gradients on the fly by the
+    // dh and dW GEMMs, from per-cell constants
     void* z = at<char>(saved, p.o_z);
-    if ((e = timed("grad_inplace", st, [&] { return launch_grad_inplace(z, p.bf16, a, st); })) !=
+    float4* cc = at<float4>(workspace, p.o_ws_cc);
+    a.tiles = at<int32_t>(saved, p.o_tiles);
+    a.tile_count = at<int32_t>(saved, p.o_tcount);
+    a.ct0 = 0; a.cu0 = 0; a.CT = p.d.Tpad; a.CU = p.d.U1pad;
+    if ((e = timed("cell_consts", st, [&] { return launch_cell_consts(a, p.cap_all, cc, st); })) !=
         hipSuccess)
       return RNNTJ_ERR_HIP;
     h.g = z;
+    h.cc = cc;
     h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad;
-    h.tiles = at<int32_t>(saved, p.o_tiles);
-    h.tile_count = at<int32_t>(saved, p.o_tcount);
+    h.tiles = a.tiles;
+    h.tile_count = a.tile_count;
     if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    w.g = z;
-    w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
-    set_ksplit(w.CT, w.CU);
     if ((e = timed("hrow", st, [&] { return launch_hrow(hchunk, p.bf16, a, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
+    w.g = z;
+    w.cc = cc;
+    w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
+    w.tiles = a.tiles;
+    w.tile_count = a.tile_count;
+    w.kparts = kparts_for(p.cap_all);
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
     return finalize() == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
@@ -444,7 +460,9 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
         return RNNTJ_ERR_HIP;
       w.g = gchunk;
       w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;
-      set_ksplit(w.CT, w.CU);
+      w.tiles = a.tiles;
+      w.tile_count = a.tile_count;
+      w.kparts = kparts_for(p.cap_chunk);
       if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
         return RNNTJ_ERR_HIP;
     }

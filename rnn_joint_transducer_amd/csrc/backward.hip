@@ -9,17 +9,19 @@
 //   d_enc[t] = sum_u dpre(t,u),  d_pred[u] = sum_t dpre(t,u)
 //
 // Kernels here:
-//   grad_inplace_kernel : untiled mode, stored logits -> dz in place.
-//   dh_kernel           : MFMA GEMM dz[cells, V] x W_out^T -> [cells, H] for
-//                         one 16x8 cell tile and 128 hidden columns, with the
-//                         (1 - h^2) epilogue and the two lattice reductions
-//                         done in registers before float32 atomics.
-//   dw_kernel           : MFMA GEMM h^T[H, cells] x dz[cells, V] split over
-//                         utterances (split-K); h and dz rows are staged
-//                         row-major and read with transposing LDS loads; the
-//                         hidden-row-0 workgroups also sum dz columns into
-//                         db_out (float64).
-//   hrow_kernel         : untiled mode, h = tanh(enc + pred) rows for dw.
+//   cell_consts_kernel : untiled mode, per-cell constants of dz (from the
+//                        float64 posteriors) for the GEMMs below, which form
+//                        dz from the stored logits on the fly.
+//   dh_kernel          : MFMA GEMM dz[cells, V] x W_out^T -> [cells, H] per
+//                        active 16x8 tile and 256 hidden columns, with the
+//                        (1 - h^2) epilogue and the two lattice reductions
+//                        done in registers before float32 atomics.
+//   dw_kernel          : MFMA GEMM h^T[H, cells] x dz[cells, V] split over
+//                        runs of the tile list (split-K); h and dz cell rows
+//                        are read as MFMA operands with transposing LDS
+//                        loads; the hidden-block-0 workgroups also sum dz
+//                        columns into db_out (float64).
+//   hrow_kernel        : untiled mode, h = tanh(enc + pred) rows for dw.
 #include <type_traits>
 
 #include "common.h"
@@ -30,67 +32,53 @@ namespace rnntj {
 namespace {
 
 constexpr float kInf = __builtin_inff();
+// bits of the fourth word of a cell's logit-gradient constants
+constexpr uint32_t kCellLabel = 0x3FFFFFFFu, kCellNeg = 0x40000000u, kCellOut = 0x80000000u;
 
 // ------------------------------------------------------------ untiled dz
 
-template <typename T>
-__global__ __launch_bounds__(256) void grad_inplace_kernel(T* __restrict__ z, JointArgs a) {
-  __shared__ float row_c[kTileCells], row_b[kTileCells], row_e[kTileCells];
-  __shared__ int row_y[kTileCells];
+// Constants of the logit gradient of every row of the active tiles, from the
+// float64 transition posteriors (see launch_cell_consts).  With
+// dz[v] = gc (occ p[v] - gB [v=blank] - gE [v=label]) and p = softmax(z):
+//   x = (lse - ln(occ |gc|)) log2(e), so that gc occ p[v] = sgn(gc) 2^(z log2(e) - x)
+//       (+inf when occ gc = 0: the term vanishes),
+//   y = gc gB,  z = gc gE,
+//   w (bits) = label + 1 in bits 0..29 (0: no label at this u), bit 30 set when
+//       gc < 0, bit 31 set for a cell outside the lattice (dz = 0).
+__global__ __launch_bounds__(128) void cell_consts_kernel(JointArgs a, float4* __restrict__ out) {
+  const int tix = blockIdx.x;
+  if (tix >= a.tile_count[0]) return;
+  int b, tt, tu;
+  tile_unpack(a.tiles[tix], b, tt, tu);
   const Dims d = a.d;
-  const int b = blockIdx.y;
-  const int n_tu = d.U1pad / kTileU;
-  const int t0 = (blockIdx.x / n_tu) * kTileT;
-  const int u0 = (blockIdx.x % n_tu) * kTileU;
+  const int r = threadIdx.x;
+  const int t = a.ct0 + tt * kTileT + (r >> 3), u = a.cu0 + tu * kTileU + (r & 7);
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  if (t0 >= Tl || u0 > Ul) return;
-  const int tid = threadIdx.x;
-  if (tid < kTileCells) {
-    const int t = t0 + (tid >> 3), u = u0 + (tid & 7);
-    float c = kInf, gb = 0.f, ge = 0.f;
-    int y = -1;
-    if (t < Tl && u <= Ul) {
-      const double g = a.gcost ? (double)a.gcost[b] : 1.0;
-      double gB, gE;
-      cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE);
-      const double occ = gB + gE;
-      const double lse = (double)a.lse[skew_idx(d, b, t, u)];
-      c = occ > 0.0 ? (float)(lse - log(occ)) : kInf;
-      gb = (float)(g * gB);
-      ge = (float)(g * gE);
-      if (u < Ul) y = a.labels[(size_t)b * d.U + u];
-    }
-    row_c[tid] = c;
-    row_b[tid] = gb;
-    row_e[tid] = ge;
-    row_y[tid] = y;
+  float4 o = make_float4(kInf, 0.f, 0.f, __uint_as_float(kCellOut));
+  if (t < Tl && u <= Ul) {
+    const double g = a.gcost ? (double)a.gcost[b] : 1.0;
+    double gB, gE;
+    cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE);
+    const double m = (gB + gE) * fabs(g);
+    const double lse = (double)a.lse[skew_idx(d, b, t, u)];
+    o.x = m > 0.0 ? (float)((lse - log(m)) * 1.4426950408889634) : kInf;
+    o.y = (float)(g * gB);
+    o.z = (float)(g * gE);
+    const uint32_t lab = u < Ul ? (uint32_t)a.labels[(size_t)b * d.U + u] + 1u : 0u;
+    o.w = __uint_as_float(lab | (g < 0.0 ? kCellNeg : 0u));
   }
-  __syncthreads();
-  const float gc = a.gcost ? a.gcost[b] : 1.0f;
-  const int V = d.V;
-  const int cpr = V / 8;  // 8-element chunks per row
-  for (int c = tid; c < kTileCells * cpr; c += 256) {
-    const int row = c / cpr, v0 = (c % cpr) * 8;
-    const int t = t0 + (row >> 3), u = u0 + (row & 7);
-    T* zp = z + (((size_t)b * d.Tpad + t) * d.U1pad + u) * V + v0;
-    Frag8<T> f;
-    if (t < Tl && u <= Ul) {
-      f = load_frag(zp);
-      float x[8];
-      const float cr = row_c[row];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float g = gc * __expf(f.get(i) - cr);
-        if (v0 + i == d.blank) g -= row_b[row];
-        if (v0 + i == row_y[row]) g -= row_e[row];
-        x[i] = g;
-      }
-      pack_frag(f, x);
-    } else {
-      zero_frag(f);
-    }
-    store_frag(zp, f);
-  }
+  out[(size_t)tix * kTileCells + r] = o;
+}
+
+// dz of logit v of a cell from the stored logit z and the cell's constants;
+// v1 = v + 1 (compared with the stored label + 1)
+__device__ __forceinline__ float dz_from_z(float z, int v, int v1, const float4& c, int blank) {
+  const uint32_t w = __float_as_uint(c.w);
+  const float e = exp2_fast(z * kLog2e - c.x);
+  float g = __uint_as_float(__float_as_uint(e) ^ ((w << 1) & 0x80000000u));
+  g -= (v == blank) ? c.y : 0.f;
+  g -= ((int)(w & kCellLabel) == v1) ? c.z : 0.f;
+  return (int)w < 0 ? 0.f : g;
 }
 
 // ------------------------------------------------------------ dh GEMM
@@ -113,16 +101,23 @@ struct DhCfg {
   static constexpr int KSTEPS = KB / 16;          // 16-wide k-steps per slice: bf16 4, fp32 2
   static constexpr int NB = 256;                  // hidden columns per item
   static constexpr int ROWS = kTileCells + NB;    // slice rows: 128 dz rows, then 256 W_out rows
-  static constexpr int SLICE = ROWS * 128;        // 48 KB
+  static constexpr int ROWB = ROWS * 128;         // 48 KB of rows
+  static constexpr int SLICE = ROWB + kTileCells * 16;  // + the dz rows' constants (logit input)
   static constexpr int NST = 3;                   // slices resident
-  static constexpr int CPW = SLICE / 1024 / 4;    // 1 KB copies per wave per slice (12)
+  static constexpr int CPW = ROWB / 1024 / 4;     // 1 KB row copies per wave per slice (12)
 };
 
 // slot of 16-byte chunk c (0..7) of 128-byte row r: 16-byte fragment reads of
 // 16 consecutive rows at one chunk hit 16 distinct bank groups
 __device__ __forceinline__ int slot128(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <typename T>
+// Registers that a compiler-visible load filled are "used" here, right after
+// an explicit vmcnt(0) and before the next direct copies are issued, so that
+// the wait the compiler places before their first use falls where nothing
+// else is in flight.
+__device__ __forceinline__ void touch(float x) { asm volatile("" ::"v"(x)); }
+
+template <typename T, bool FROMZ>
 __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   using C = DhCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
@@ -150,12 +145,13 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
     int b, t0, u0, n0, Tl, Ul;
   };
   struct ItemRef {
-    int tile, nb;
+    int tile, nb, tix;
   };
   auto item_ref = [&](int i) {  // i-th item of this workgroup
     const int item = bid + i * gsz;
     ItemRef r;
-    r.tile = ld_const(a.tiles + item / nnb);
+    r.tix = item / nnb;
+    r.tile = ld_const(a.tiles + r.tix);
     r.nb = item % nnb;
     return r;
   };
@@ -171,7 +167,9 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
     return it;
   };
 
-  // Direct copies of one slice: copy q of wave w fills slice rows
+  // Direct copies of one slice (the 128 rows' logit-gradient constants
+  // travel with every slice: one more half-wave copy per wave).
+  // Copy q of wave w fills slice rows
   // 8 (CPW w + q) .. +7; lane l takes row 8 (CPW w + q) + l/8 and LDS slot
   // l%8, holding 16-byte chunk slot128(row, l%8).  Rows below 128 are dz
   // rows of the tile (cells outside the lattice read the tile's first cell,
@@ -184,9 +182,11 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   // offsets from W_out.  Both fit 32 bits (a tile spans 16 frames of one
   // chunk; W_out is at most 768 rows).
   const T* gbase = G;
+  const float4* ccsrc = a.cc;
   uint32_t coff[C::CPW];
   auto set_sources = [&](ItemRef ref) {
     const Item it = decode(ref);
+    if constexpr (FROMZ) ccsrc = a.cc + (size_t)ref.tix * kTileCells + 32 * w + (lane & 31);
     gbase = G + (((size_t)it.b * a.CT + (it.t0 - a.ct0)) * a.CU + (it.u0 - a.cu0)) * V;
 #pragma unroll
     for (int q = 0; q < C::CPW; ++q) {
@@ -220,7 +220,11 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
       }
       dma16(base + off, st + q * 1024);
     }
+    if constexpr (FROMZ) {
+      if (lane < 32) dma16(ccsrc, lbase + buf * C::SLICE + C::ROWB + 512 * w);
+    }
   };
+  constexpr int kCopies = C::CPW + (FROMZ ? 1 : 0);  // per wave per slice
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -232,9 +236,12 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
 
   Frag8<T> fa[2][2], fb[2][4];
   // fragments of k-step kk of stream slice g (buffer g % NST)
+  const bool has_vtail = V % C::KB != 0;
   auto rd = [&](int g, int kk, int fbuf) {
     const char* sl = lds + (g % C::NST) * C::SLICE;
-    const int kbase = (g % nk) * C::KB + 16 * kk + 8 * kh;  // this lane's first k
+    const int s = g % nk;
+    const bool vtail = has_vtail && s == nk - 1;  // uniform
+    const int kbase = s * C::KB + 16 * kk + 8 * kh;  // this lane's first k
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 64 * wm + 32 * i + lc;
@@ -245,7 +252,16 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
         fa[fbuf][i].lo = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh) << 4));
         fa[fbuf][i].hi = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh + 1) << 4));
       }
-      if (kbase >= V) zero_frag(fa[fbuf][i]);  // vocabulary tail
+      if constexpr (FROMZ) {
+        // logits -> logit gradients of this row (rounded as the stored dz would be)
+        const float4 c = *reinterpret_cast<const float4*>(sl + C::ROWB + 16 * r);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          x[e] = dz_from_z(fa[fbuf][i].get(e), kbase + e, kbase + e + 1, c, d.blank);
+        pack_frag(fa[fbuf][i], x);
+      }
+      if (vtail && kbase >= V) zero_frag(fa[fbuf][i]);  // vocabulary tail
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -348,7 +364,7 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   };
 
   // ---- the slice stream: slice g is slice g % nk of item g / nk.  Two
-  // cursors walk it: the copy cursor (slices are issued two ahead) and the
+  // cursors walk it: the copy cursor (slices are issued three ahead) and the
   // compute cursor; each holds its item and loads the following one early
   // (scalar loads, waited for only at first use).
   ItemRef cur = item_ref(0);
@@ -368,25 +384,45 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
     }
   };
   issue_next();
-  if (total > 1) {
-    issue_next();
-    wait_vm<C::CPW>();  // slice 0 landed, slice 1 may be in flight
-  } else {
-    wait_vm<0>();
-  }
+  if (total > 1) issue_next();
+  if (total > 2) issue_next();
+  // slice 0 landed; slices 1 and 2 may be in flight
+  if (total > 2) wait_vm<2 * kCopies>();
+  else if (total > 1) wait_vm<kCopies>();
+  else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
   rd(0, 0, 0);
-  // MFMAs of stream slice g, with the fragment reads one k-step ahead
-  auto slice = [&](int g) {
+  // MFMAs of stream slice g, with the fragment reads one k-step ahead; `last`
+  // marks an item's last slice, whose epilogue loads (issued after the copies
+  // of slice g+2) are waited for and touched at its end
+  auto slice = [&](int g, bool last) {
 #pragma unroll
     for (int kk = 0; kk < C::KSTEPS; ++kk) {
-      const int fcur = kk & 1;
+      const int fcur = kk & 1;  // KSTEPS is even: parity of the k-step in the stream
       if (kk + 1 < C::KSTEPS) {
         rd(g, kk + 1, fcur ^ 1);
       } else if (g + 1 < total) {
-        // slice g+1 has landed (nothing newer is in flight) and every wave
-        // is past slice g-1: refill that buffer with slice g+2
-        wait_vm<0>();
+        // slice g+1 has landed (g+2 may still be in flight), this wave's
+        // reads of slice g are done, and after the barrier every wave's
+        // are: refill that buffer with slice g+3
+        if (last) {
+          wait_vm<0>();
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) touch(ex[i][q4][j]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) touch(px[q][j]);
+        } else if (g + 2 < total) {
+          wait_vm<kCopies>();
+        } else {
+          wait_vm<0>();
+        }
+        wait_lgkm0();
         __builtin_amdgcn_s_barrier();
         if (iss_g < total) issue_next();
         rd(g + 1, 0, fcur ^ 1);
@@ -396,173 +432,293 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int g = 0; g < total; ++g) {
-    const int s = g % nk;
-    // during an item's last slice its epilogue inputs load
-    if (s == nk - 1) load_ep(decode(cur));
-    slice(g);
-    if (s == nk - 1) {
-      epilogue(decode(cur));
-      const int li = g / nk;
-      cur = cur_next;
-      if (li + 2 < my_items) cur_next = item_ref(li + 2);
+  // items outside, their slices inside: the accumulators stay in the MFMA
+  // registers through the slice loop and are only read by the epilogue
+  for (int li = 0; li < my_items; ++li) {
+    for (int s = 0; s < nk; ++s) {
+      const bool last = s == nk - 1;
+      // during an item's last slice its epilogue inputs load
+      if (last) load_ep(decode(cur));
+      slice(li * nk + s, last);
     }
+    epilogue(decode(cur));
+    cur = cur_next;
+    if (li + 2 < my_items) cur_next = item_ref(li + 2);
   }
 }
 
 
 // ------------------------------------------------------------ dW GEMM
-
-// d_W_out[m0:m0+128, n0:n0+128] += h^T dz over the valid cells of one
-// utterance in the chunk.  h rows [cell][H] and dz rows [cell][V] are staged
-// row-major (16-byte copies) and read as MFMA operands with load_frag_T, so
-// neither operand is transposed in memory.  K block = 8 frames x 8 label
-// positions (bf16) or 4 x 8 (fp32) of one 16x8 cell tile.
+//
+// d_W_out[m, n] += sum over cells h[cell, m] dz[cell, n] and d_b64[n] +=
+// sum over cells dz[cell, n], over the active tiles of one chunk.  Items:
+// 128 hidden rows x 256 vocabulary columns x one of `kparts` runs of the tile
+// list (split-K); one workgroup per item.  Workgroups are dealt to the 8 XCDs
+// round-robin; consecutive items (the column blocks of one run) are placed on
+// one XCD so that the h and dz rows they share come from that XCD's L2.  Cell
+// rows of h and dz stream through LDS in slices of KB cells (direct copies,
+// three slices resident, issued three ahead) and are read as MFMA operands
+// with transposing (bf16) or scalar (fp32) LDS reads, so neither operand is
+// transposed in memory.  With logit input, dz is formed from the logits and
+// per-cell constants, which travel with each slice.  4 waves (2 x 2), each 64
+// hidden rows x 128 vocabulary columns.
 template <typename T>
 struct DwCfg {
   static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int KB = kBf16 ? 64 : 32;           // cells per stage
-  static constexpr int LD = 128 + (kBf16 ? 16 : 4);    // LDS row (elements): 288 B / 528 B
-  static constexpr int CE = 16 / (int)sizeof(T);       // elements per 16-byte chunk
-  static constexpr int CPR = 128 / CE;                 // chunks per staged row
-  static constexpr int CH = KB * CPR / 256;            // chunks per thread per operand
-  static constexpr int SPT = kTileCells / KB;          // stages per cell tile
+  static constexpr int E = sizeof(T);
+  static constexpr int CE = 16 / E;                    // elements per 16-byte granule
+  static constexpr int BM = 128, BN = 256;
+  static constexpr int KB = kBf16 ? 64 : 32;           // cells per slice
+  static constexpr int KSTEPS = KB / 16;               // 4 / 2
+  static constexpr int SPT = kTileCells / KB;          // slices per tile
+  static constexpr int ROWA = BM * E, ROWB = BN * E;   // bytes per cell row
+  static constexpr int GA = ROWA / 16, GB = ROWB / 16; // granules per row
+  static constexpr int SA = KB * ROWA, SB = KB * ROWB; // 16 KB, 32 KB
+  static constexpr int CA = SA / 1024, CB = SB / 1024; // 1 KB copies per part
+  static constexpr int QPW = (CA + CB) / 4;            // row copies per wave per slice (12)
+  static constexpr int SLICE = SA + SB + KB * 16;      // + the slice's cell constants
+  static constexpr int NST = 3;
+  static_assert(KSTEPS % 2 == 0 && (CA + CB) % 4 == 0, "slice shape");
 };
 
-template <typename T>
-__global__ __launch_bounds__(256) void dw_kernel(DwArgs a) {
+// 16-byte granule swizzle of cell row r: the transposing reads of 4
+// consecutive rows and the scalar reads of rows r, r+8 hit distinct banks
+__device__ __forceinline__ int swz_dw(int r) { return (4 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
+
+template <typename T, bool FROMZ>
+__global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
   using C = DwCfg<T>;
-  __shared__ __align__(16) T As[2][C::KB * C::LD];  // h  [cell][hidden]
-  __shared__ __align__(16) T Bs[2][C::KB * C::LD];  // dz [cell][vocab]
-  __shared__ double dbw[4][128];
+  __shared__ __align__(16) char lds[C::NST * C::SLICE];
   const Dims d = a.d;
-  const int n0 = blockIdx.x * 128, m0 = blockIdx.y * 128;
-  const int b = blockIdx.z / a.ksplit, kpart = blockIdx.z % a.ksplit;
-  const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  // valid cell tiles of this utterance inside the chunk form a rectangle;
-  // this workgroup takes the kpart-th of ksplit equal runs of their stages
-  const int tv = min(a.CT, Tl - a.ct0), uv = min(a.CU, Ul + 1 - a.cu0);
-  if (tv <= 0 || uv <= 0) return;
-  const int ntt = (tv + kTileT - 1) / kTileT, ntu = (uv + kTileU - 1) / kTileU;
-  const int nall = ntt * ntu * C::SPT;
-  const int s_begin = (int)(((long long)nall * kpart) / a.ksplit);
-  const int s_end = (int)(((long long)nall * (kpart + 1)) / a.ksplit);
-  const int nstage = s_end - s_begin;
-  if (nstage <= 0) return;
-  const int n_tu = a.CU / kTileU;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kh = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = lane >> 5, lc = lane & 31;
   const int wm = w >> 1, wn = w & 1;
-  const bool do_db = (blockIdx.y == 0);
-  const T* hsrc = static_cast<const T*>(a.h);
-  const T* gsrc = static_cast<const T*>(a.g);
-  // this thread's staging chunks: row = c / CPR, column chunk = c % CPR
-  // (c = tid + 256 q, so the column chunk is the same for every q)
-  const int ccol = (tid % C::CPR) * C::CE;
-  const bool mok = m0 + ccol < d.H, nok = n0 + ccol < d.V;
-  double dbacc[C::CE];
-#pragma unroll
-  for (int i = 0; i < C::CE; ++i) dbacc[i] = 0.0;
+  const int H = d.H, V = d.V;
+  const int nmb = (H + C::BM - 1) / C::BM, nnb = (V + C::BN - 1) / C::BN;
+  const int nmn = nmb * nnb;
+  // item of this workgroup: XCD x = blockIdx % 8 takes items x * per .. +per-1
+  const int per = gridDim.x >> 3;
+  const int item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int kp = item / nmn, nb = (item % nmn) / nmb, mb = item % nmb;
+  if (kp >= a.kparts) return;
+  const int count = ld_const(a.tile_count);
+  const int tb = (int)((long long)count * kp / a.kparts);
+  const int te = (int)((long long)count * (kp + 1) / a.kparts);
+  const int total = (te - tb) * C::SPT;  // slices of this item
+  if (total <= 0) return;
+  const int m0 = mb * C::BM, n0 = nb * C::BN;
+  const T* __restrict__ Hs = static_cast<const T*>(a.h);
+  const T* __restrict__ Gs = static_cast<const T*>(a.g);
+  const uint32_t lbase = lds_addr(lds);
+  // column sums of dz for db_out: wave row 0 of the hidden-block-0 workgroups
+  const bool do_db = mb == 0 && wm == 0;
 
-  u32x4 ra[C::CH], rb[C::CH];
-  auto load_stage = [&](int sl) {
-    const int s = s_begin + sl;
-    const int tile = s / C::SPT, part = s % C::SPT;
-    const int t0 = a.ct0 + (tile / ntu) * kTileT + part * (C::KB / kTileU);
-    const int u0 = a.cu0 + (tile % ntu) * kTileU;
+  // Copies of one slice: copy q (0 .. CA-1: the h part, cell rows of BM
+  // hidden values; CA .. CA+CB-1: the dz part, BN vocabulary values) is
+  // issued by wave q % 4; lane l fills 16 bytes of the part at offset
+  // 1024 q' + 16 l.  The element offset of each copy inside a tile is fixed
+  // per item; a slice adds its tile base and (slice in tile) * KB/8 frames.
+  // With logit input, wave w also copies the constants of cells
+  // KB/4 w .. KB/4 (w+1) - 1 of the slice (lanes below KB/4).
+  constexpr int NQ = C::QPW + (FROMZ ? 1 : 0);  // copies per wave per slice
+  uint32_t coff[C::QPW];
 #pragma unroll
-    for (int q = 0; q < C::CH; ++q) {
-      const int row = (tid + 256 * q) / C::CPR;
-      const int t = t0 + row / kTileU, u = u0 + row % kTileU;
-      const bool ok = t < Tl && u <= Ul;
-      const size_t crow = ((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0);
-      ra[q] = (ok && mok) ? *reinterpret_cast<const u32x4*>(hsrc + crow * d.H + m0 + ccol)
-                          : u32x4{0u, 0u, 0u, 0u};
-      rb[q] = (ok && nok) ? *reinterpret_cast<const u32x4*>(gsrc + crow * d.V + n0 + ccol)
-                          : u32x4{0u, 0u, 0u, 0u};
+  for (int k = 0; k < C::QPW; ++k) {
+    const int q = w + 4 * k;
+    uint32_t off;
+    if (q < C::CA) {
+      const int row = q * (1024 / C::ROWA) + lane / C::GA;
+      const int lg = (lane % C::GA) ^ swz_dw(row);
+      const int col = min(m0 + lg * C::CE, H - C::CE);
+      off = (uint32_t)((((row >> 3) * a.CU) + (row & 7)) * H + col);
+    } else {
+      const int qb = q - C::CA;
+      const int row = qb * (1024 / C::ROWB) + lane / C::GB;
+      const int lg = (lane % C::GB) ^ swz_dw(row);
+      const int col = min(n0 + lg * C::CE, V - C::CE);
+      off = (uint32_t)((((row >> 3) * a.CU) + (row & 7)) * V + col);
     }
-    (void)n_tu;
+    coff[k] = off;
+  }
+  auto issue = [&](int g) {
+    const int tix = tb + g / C::SPT, ss = g % C::SPT;
+    int b, tt, tu;
+    tile_unpack(ld_const(a.tiles + tix), b, tt, tu);
+    // the slice's first cell row: frame tt*16 + ss*KB/8, label position tu*8
+    const size_t crow = ((size_t)b * a.CT + tt * kTileT + ss * (C::KB / 8)) * a.CU + tu * kTileU;
+    const T* hb = Hs + crow * H;
+    const T* gb = Gs + crow * V;
+    const uint32_t st = lbase + (g % C::NST) * C::SLICE;
+#pragma unroll
+    for (int k = 0; k < C::QPW; ++k) {
+      const int q = w + 4 * k;
+      if (q < C::CA) dma16(hb + coff[k], st + q * 1024);
+      else dma16(gb + coff[k], st + C::SA + (q - C::CA) * 1024);
+    }
+    if constexpr (FROMZ) {
+      if (lane < C::KB / 4)
+        dma16(a.cc + (size_t)tix * kTileCells + ss * C::KB + (C::KB / 4) * w + lane,
+              st + C::SA + C::SB + 4 * C::KB * w);
+    }
   };
-  auto store_stage = [&](int buf) {
+
+  // Fragment of 8 consecutive cell rows (k) of one column: rows 16 kk + 8
+  // (l/32) + e, column col0 + l%32, of a slice part with rowb-byte rows.
+  // bf16: two transposing reads, of rows 16 kk + r and 16 kk + r + 4, where
+  // lane l supplies r = 8 (l/32) + (l%16)/4 and 4 columns from
+  // col0 + 16 ((l/16) & 1) + 4 (l%4).  The granule swizzle of those rows
+  // does not depend on kk, so a lane's byte offset inside the part is fixed
+  // (lane_off) and a k-step adds 16 kk rows.
+  auto lane_off = [&](int rowb, int col0) -> uint32_t {
+    const int g16 = lane >> 4, i16 = lane & 15;
+    const int r = 8 * (g16 >> 1) + (i16 >> 2);
+    const int col = col0 + 16 * (g16 & 1) + 4 * (i16 & 3);
+    return (uint32_t)(r * rowb + ((((col * 2) >> 4) ^ swz_dw(r)) << 4) + ((col * 2) & 15));
+  };
+  uint32_t offA[2], offB[4];
 #pragma unroll
-    for (int q = 0; q < C::CH; ++q) {
-      const int row = (tid + 256 * q) / C::CPR;
-      *reinterpret_cast<u32x4*>(&As[buf][row * C::LD + ccol]) = ra[q];
-      *reinterpret_cast<u32x4*>(&Bs[buf][row * C::LD + ccol]) = rb[q];
-      if (do_db) {
-        Frag8<T> f;
-        if constexpr (C::kBf16) {
-          f.v = rb[q];
-        } else {
-          f.lo = __builtin_bit_cast(f32x4, rb[q]);
-        }
+  for (int i = 0; i < 2; ++i) offA[i] = lane_off(C::ROWA, 64 * wm + 32 * i);
 #pragma unroll
-        for (int i = 0; i < C::CE; ++i) dbacc[i] += (double)f.get(i);
+  for (int j = 0; j < 4; ++j) offB[j] = C::SA + lane_off(C::ROWB, 128 * wn + 32 * j);
+  auto frag_T = [&](const char* sl, uint32_t off, const char* part, int rowb, int kk, int col0) {
+    Frag8<T> f;
+    if constexpr (C::kBf16) {
+      const char* p = sl + off + 16 * kk * rowb;
+      const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+      const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * rowb));
+      f.v[0] = (uint32_t)(uint16_t)x[0] | ((uint32_t)(uint16_t)x[1] << 16);
+      f.v[1] = (uint32_t)(uint16_t)x[2] | ((uint32_t)(uint16_t)x[3] << 16);
+      f.v[2] = (uint32_t)(uint16_t)y[0] | ((uint32_t)(uint16_t)y[1] << 16);
+      f.v[3] = (uint32_t)(uint16_t)y[2] | ((uint32_t)(uint16_t)y[3] << 16);
+    } else {
+      const int col = col0 + lc;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 16 * kk + 8 * kh + e;
+        x[e] = *reinterpret_cast<const float*>(part + r * rowb + ((((col * 4) >> 4) ^ swz_dw(r)) << 4) +
+                                               ((col * 4) & 15));
       }
+      pack_frag(f, x);
     }
+    return f;
+  };
+  // sum of a fragment's 8 values (the column's 8 cells of a k-step)
+  auto fsum = [&](const Frag8<T>& f) {
+    float sdb = 0.f;
+    if constexpr (C::kBf16) {
+      // two bf16 values per dot product with (1, 1); the builtin takes the
+      // bf16 pairs as 2 x 16-bit integer vectors (bit patterns)
+      typedef short s16x2 __attribute__((ext_vector_type(2)));
+      const s16x2 one = __builtin_bit_cast(s16x2, 0x3f803f80u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t w = f.v[q];
+        sdb = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(s16x2, w), one, sdb, false);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sdb += f.get(e);
+    }
+    return sdb;
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  double dbacc[4] = {0.0, 0.0, 0.0, 0.0};
 
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  for (int s = 0; s < nstage; ++s) {
-    const int cur = s & 1;
-    const bool has_next = s + 1 < nstage;
-    if (has_next) load_stage(s + 1);
+  Frag8<T> fa[2][2], fb[2][4];
+  auto rd = [&](int g, int kk, int fbuf) {
+    const char* sl = lds + (g % C::NST) * C::SLICE;
 #pragma unroll
-    for (int kk = 0; kk < C::KB / 16; ++kk) {
-      Frag8<T> fa[2], fb[2];
+    for (int i = 0; i < 2; ++i) fa[fbuf][i] = frag_T(sl, offA[i], sl, C::ROWA, kk, 64 * wm + 32 * i);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = load_frag_T(As[cur], C::LD, kk * 16, 64 * wm + 32 * i);
+    for (int j = 0; j < 4; ++j) fb[fbuf][j] = frag_T(sl, offB[j], sl + C::SA, C::ROWB, kk, 128 * wn + 32 * j);
+    if constexpr (FROMZ) {
+      // logits -> logit gradients, with the cells' constants
+      const float4* cs = reinterpret_cast<const float4*>(sl + C::SA + C::SB);
+      float4 c[8];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = load_frag_T(Bs[cur], C::LD, kk * 16, 64 * wn + 32 * j);
+      for (int e = 0; e < 8; ++e) c[e] = cs[16 * kk + 8 * kh + e];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int j = 0; j < 4; ++j) {
+        const int v = n0 + 128 * wn + 32 * j + lc;
+        float x[8];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) mma_step(acc[i][j], fa[i], fb[j]);
+        for (int e = 0; e < 8; ++e) x[e] = dz_from_z(fb[fbuf][j].get(e), v, v + 1, c[e], d.blank);
+        pack_frag(fb[fbuf][j], x);
+      }
     }
-    if (has_next) store_stage(cur ^ 1);
-    __syncthreads();
+    if (do_db) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dbacc[j] += (double)fsum(fb[fbuf][j]);
+    }
+  };
+  auto mm = [&](int fbuf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) mma_step(acc[i][j], fa[fbuf][i], fb[fbuf][j]);
+  };
+
+  // ---- slices 0, 1, 2 in flight; slice g+3 is issued into slice g's buffer
+  // once every wave is done reading slice g
+  issue(0);
+  if (total > 1) issue(1);
+  if (total > 2) issue(2);
+  if (total > 2) wait_vm<2 * NQ>();
+  else if (total > 1) wait_vm<NQ>();
+  else wait_vm<0>();
+  __builtin_amdgcn_s_barrier();
+  rd(0, 0, 0);
+  for (int g = 0; g < total; ++g) {
+#pragma unroll
+    for (int kk = 0; kk < C::KSTEPS; ++kk) {
+      const int fcur = kk & 1;  // KSTEPS is even: parity of the k-step in the stream
+      if (kk + 1 < C::KSTEPS) {
+        rd(g, kk + 1, fcur ^ 1);
+      } else if (g + 1 < total) {
+        if (g + 2 < total) wait_vm<NQ>();  // slice g+1 landed, g+2 may be in flight
+        else wait_vm<0>();
+        wait_lgkm0();  // this wave's reads of slice g are done
+        __builtin_amdgcn_s_barrier();
+        if (g + 3 < total) issue(g + 3);
+        rd(g + 1, 0, fcur ^ 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fcur);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
+  // ---- float32 atomics into d_W_out; float64 column sums into d_b64
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = n0 + 64 * wn + 32 * j + (lane & 31);
-      if (n < d.V) {
+    for (int j = 0; j < 4; ++j) {
+      const int n = n0 + 128 * wn + 32 * j + lc;
+      if (n < V) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 64 * wm + 32 * i + acc_row(r, kh);
-          if (m < d.H) atomicAdd(&a.d_W[(size_t)m * d.V + n], acc[i][j][r]);
+          if (m < H) atomicAdd(&a.d_W[(size_t)m * V + n], acc[i][j][r]);
         }
       }
     }
-
   if (do_db) {
-    // threads with equal tid % CPR share columns: 4 per wave for bf16
-    // (CPR = 16), 2 per wave for fp32 (CPR = 32); then across the 4 waves
 #pragma unroll
-    for (int i = 0; i < C::CE; ++i) {
-      double v = dbacc[i];
-      for (int off = C::CPR; off < 64; off <<= 1) v += __shfl_xor(v, off);
-      dbacc[i] = v;
+    for (int j = 0; j < 4; ++j) {
+      // the other 8 cells of each k-step sit in lane l ^ 32
+      const double v = dbacc[j] + __shfl_xor(dbacc[j], 32);
+      const int n = n0 + 128 * wn + 32 * j + lc;
+      if (kh == 0 && n < V) atomicAdd(&a.d_b64[n], v);
     }
-    if (lane < C::CPR) {
-#pragma unroll
-      for (int i = 0; i < C::CE; ++i) dbw[w][ccol + i] = dbacc[i];
-    }
-    __syncthreads();
-    if (tid < 128 && n0 + tid < d.V)
-      atomicAdd(&a.d_b64[n0 + tid], dbw[0][tid] + dbw[1][tid] + dbw[2][tid] + dbw[3][tid]);
   }
 }
 
@@ -628,14 +784,9 @@ hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, hipStream_t st) {
-  dim3 grid((a.d.Tpad / kTileT) * (a.d.U1pad / kTileU), a.d.B), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(grad_inplace_kernel<uint16_t>, grid, block, 0, st,
-                       static_cast<uint16_t*>(z), a);
-  else
-    hipLaunchKernelGGL(grad_inplace_kernel<float>, grid, block, 0, st, static_cast<float*>(z),
-                       a);
+hipError_t launch_cell_consts(const JointArgs& a, int max_tiles, float4* out, hipStream_t st) {
+  if (max_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(cell_consts_kernel, dim3(max_tiles), dim3(kTileCells), 0, st, a, out);
   return hipGetLastError();
 }
 
@@ -645,19 +796,31 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
   if (items <= 0) return hipSuccess;
   const int ncu = device_cu_count();
   dim3 grid((unsigned)(items < ncu ? items : ncu)), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL(dh_kernel<float>, grid, block, 0, st, a);
+  const bool fromz = a.cc != nullptr;
+  if (bf16) {
+    if (fromz) hipLaunchKernelGGL((dh_kernel<uint16_t, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((dh_kernel<uint16_t, false>), grid, block, 0, st, a);
+  } else {
+    if (fromz) hipLaunchKernelGGL((dh_kernel<float, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((dh_kernel<float, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st) {
-  dim3 grid((a.d.V + 127) / 128, (a.d.H + 127) / 128, a.d.B * a.ksplit), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(dw_kernel<uint16_t>, grid, block, 0, st, a);
-  else
-    hipLaunchKernelGGL(dw_kernel<float>, grid, block, 0, st, a);
+  const int nmb = (a.d.H + DwCfg<float>::BM - 1) / DwCfg<float>::BM;
+  const int nnb = (a.d.V + DwCfg<float>::BN - 1) / DwCfg<float>::BN;
+  const long long items = (long long)nmb * nnb * a.kparts;
+  if (items <= 0) return hipSuccess;
+  dim3 grid((unsigned)((items + 7) / 8 * 8)), block(256);  // 8 XCDs, items grouped per XCD
+  const bool fromz = a.cc != nullptr;
+  if (bf16) {
+    if (fromz) hipLaunchKernelGGL((dw_kernel<uint16_t, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((dw_kernel<uint16_t, false>), grid, block, 0, st, a);
+  } else {
+    if (fromz) hipLaunchKernelGGL((dw_kernel<float, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((dw_kernel<float, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 

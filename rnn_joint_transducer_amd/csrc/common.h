@@ -27,6 +27,9 @@ constexpr int kTileT = 16;
 constexpr int kTileU = 8;
 constexpr int kTileCells = kTileT * kTileU;
 constexpr int kVocabTile = 128;  // vocabulary columns per pass of one wave
+// Largest vocabulary: keeps 32-bit element offsets inside a 16-frame tile of
+// logit rows (16 x 512 rows x V) and a label + 1 inside 30 bits.
+constexpr int kMaxV = 262144;
 
 // Shapes shared by every kernel.
 struct Dims {
@@ -191,7 +194,7 @@ __device__ __forceinline__ Frag8<float> load_frag_T(const float* tile, int ld, i
 // it visible to the other waves with a barrier.
 __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc),
-               "s"(lds_base)
+               "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
 // wait until at most N vector memory accesses of this wave are outstanding
@@ -199,6 +202,8 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// wait until this wave's LDS reads (and scalar loads) have completed
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Load of a value the kernel never writes, through the constant address
 // space: with a wave-uniform address it becomes a scalar load, which neither
 // waits for nor is waited on by the vector-memory counter.

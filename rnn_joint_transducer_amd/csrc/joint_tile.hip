@@ -290,8 +290,9 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       build_h_direct(hA, b, tv, uv, valid);
     }
     if constexpr (MODE == kGrad) {
-      // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H])
-      if (valid && vr == 0) {
+      // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H]);
+      // every row of the tile is written (zero outside the lattice)
+      if (vr == 0) {
         T* hrow = static_cast<T*>(a.hout) +
                   (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
 #pragma unroll
@@ -533,7 +534,11 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         const int row = lc;
         const int t = t0 + 4 * w + (row >> 3), u = u0 + (row & 7);
         const bool row_ok = t < Tl && u <= Ul;
-        T* orow = out + (((size_t)b * RT + (row_ok ? t - rt0 : 0)) * RU + (row_ok ? u - ru0 : 0)) * V + vt;
+        // logits: cells of the lattice only; logit gradients: every row of
+        // the tile (zero outside the lattice), as the weight gradient reads
+        // whole tiles
+        const bool row_st = MODE == kGrad || row_ok;
+        T* orow = out + (((size_t)b * RT + (row_st ? t - rt0 : 0)) * RU + (row_st ? u - ru0 : 0)) * V + vt;
         const int g = lane >> 4, i = lane & 15;
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
@@ -549,7 +554,8 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
           pk[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
           pk[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
           const int colo = 16 * f + 8 * kh;
-          if (row_ok && (EXACT || vt + colo < V)) *reinterpret_cast<u32x4*>(orow + colo) = pk;
+          if (!row_ok) pk = u32x4{0u, 0u, 0u, 0u};
+          if (row_st && (EXACT || vt + colo < V)) *reinterpret_cast<u32x4*>(orow + colo) = pk;
         }
         // Ts is rewritten only after the next tile's slice barriers
       } else {
@@ -558,7 +564,8 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int rowi = w * 32 + acc_row(r, kh);
           const int t = t0 + 4 * w + (r >> 2), u = u0 + 4 * kh + (r & 3);
-          if (t < Tl && u <= Ul) {
+          const bool ok = t < Tl && u <= Ul;
+          if (MODE == kGrad || ok) {
             T* orow = out + (((size_t)b * RT + (t - rt0)) * RU + (u - ru0)) * V;
 #pragma unroll
             for (int blk = 0; blk < 4; ++blk) {
@@ -568,6 +575,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
                 if constexpr (MODE == kGrad) {
                   if (col == d.blank) g -= row_b[rowi];
                   if (col == lab[r & 3]) g -= row_e[rowi];
+                  g = ok ? g : 0.f;
                 }
                 orow[col] = g;
               }

@@ -97,9 +97,6 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
 // Untiled backward: h rows of every cell into h [B, Tpad, U1pad, H].
 hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st);
 
-// Untiled backward: logits [B, Tpad, U1pad, V] turned into logit gradients
-// in place.
-hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, hipStream_t st);
 
 // dh = dz @ W_out^T for the active tiles of one chunk; dpre = (1 - h^2) dh
 // summed into d_enc over u and into d_pred over t.
@@ -120,6 +117,8 @@ struct DhArgs {
   Dims d;
   const int32_t* tiles;       // active tiles of the chunk
   const int32_t* tile_count;
+  const float4* cc;           // per-cell constants (g holds logits) or null (g holds dz)
+  const float* gcost;         // [B] or null
   int ct0, cu0, CT, CU;
   float* d_enc;
   float* d_pred;
@@ -127,15 +126,26 @@ struct DhArgs {
 // Persistent launch; max_tiles bounds the entries of the tile list.
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st);
 
-// d_W_out += h^T dz and d_b64 += column sums of dz (float64) over one chunk.
+// Per-cell constants of the logit gradient (untiled backward), one float4
+// per row of every active tile (list order x 128 rows):
+//   dz[v] = gc * exp2(z[v] log2(e) - x) - y [v = blank] - z [v = label]
+// x = (lse - ln occ) log2(e) (+inf when occ = 0), y = gc gB, z = gc gE, and w
+// the bits of the label (-1: none, -2: the cell is outside the lattice, dz = 0).
+hipError_t launch_cell_consts(const JointArgs& a, int max_tiles, float4* out, hipStream_t st);
+
+// d_W_out += h^T dz and d_b64 += column sums of dz (float64) over the active
+// tiles of one chunk (split-K over the tile list).  With `cc` set, g holds
+// the logits and dz is formed from them on the fly (untiled backward).
 struct DwArgs {
-  const void* g;  // dz rows [B, CT, CU, V]
-  const void* h;  // h rows  [B, CT, CU, H]
-  const int32_t* Teff;
-  const int32_t* Ueff;
+  const void* g;              // dz (or logit) rows [B, CT, CU, V]
+  const void* h;              // h rows [B, CT, CU, H]; rows of cells outside the lattice are 0
+  const int32_t* tiles;       // active tiles of the chunk
+  const int32_t* tile_count;
+  const float4* cc;           // per-cell constants (logit input) or null (dz input)
+  const float* gcost;         // [B] or null
   Dims d;
   int ct0, cu0, CT, CU;
-  int ksplit;  // workgroups sharing one utterance's cells (split-K)
+  int kparts;                 // split-K: parts of the tile list
   float* d_W;
   double* d_b64;
 };

@@ -58,7 +58,10 @@ def test_buffer_sizes():
     # 8 x 2 chunks, each with a list of 16 * 4 * 8 tiles, and 16 tile counts
     lists = 16 * (16 * 4 * 8) * 4 + 256
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + chunk * (1024 + 640) * 2 + lists)
-    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024 + 16 * 512 * 104 * 640 * 2)
+    # untiled: h rows of the padded lattice and one float4 of logit-gradient
+    # constants per row of every 16 x 8 tile
+    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024 + 16 * 512 * 104 * 640 * 2
+                                                 + 16 * 32 * 13 * 128 * 16)
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, 0, 0) == (0, 0)
 
 
@@ -73,6 +76,7 @@ def test_buffer_sizes():
     ((2, 10, 600, 64, 32, 0), 2),      # U + 1 > 512
     ((8192, 10, 2, 64, 32, 0), 2),     # B > 8191
     ((2, 65521, 2, 64, 32, 0), 2),     # T > 65520
+    ((2, 10, 2, 64, 262152, 0), 2),    # V > 262144
 ])
 def test_shape_errors(args, code):
     assert _saved(*args)[0] == code
@@ -83,6 +87,8 @@ def test_tile_errors():
     assert _saved(2, 10, 2, 64, 32, 0, 16, 4)[0] == 2   # tile_u not a multiple of 8
     assert _saved(2, 10, 2, 64, 32, 0, 16, 8, 64)[0] == 2
     assert _saved(2, 10, 2, 64, 32, 0, 16, 8, 128)[0] == 0
+    assert _saved(2, 10, 2, 64, 32, 0, 16, 8, 256)[0] == 0
+    assert _saved(2, 10, 2, 64, 32, 0, 16, 8, 320)[0] == 2
     assert _saved(2, 10, 2, 64, 32, 0, -16, 8)[0] == 1
 
 

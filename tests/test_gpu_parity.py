@@ -135,6 +135,33 @@ def test_autograd_wrapper():
     check_grad("d_W_out", dev["W_out"].grad.double().cpu().numpy(), ref["dW"], "fp32")
 
 
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
+def test_saved_state_reused(tiles):
+    """The backward only reads the forward's saved state: a second backward
+    from the same forward gives the same gradients (retain_graph)."""
+    import torch
+    import rnn_joint_transducer_amd as rj
+    inp = make_config("tiny")
+    dev = to_device(inp)
+    for k in ("enc", "pred", "W_out", "b_out"):
+        dev[k].requires_grad_(True)
+    costs = rj.rnnt_joint_loss(**dev, tile_t=tiles[0], tile_u=tiles[1], tile_v=tiles[2])
+    loss = (costs * torch.tensor([2.0, -0.5], device=costs.device)).sum()
+    loss.backward(retain_graph=True)
+    first = [dev[k].grad.clone() for k in ("enc", "pred", "W_out", "b_out")]
+    for k in ("enc", "pred", "W_out", "b_out"):
+        dev[k].grad = None
+    loss.backward()
+    second = [dev[k].grad for k in ("enc", "pred", "W_out", "b_out")]
+    ref = _oracle_full(inp, grad_costs=[2.0, -0.5])
+    check_grad("d_enc", first[0].double().cpu().numpy(), ref["dEnc"], "fp32")
+    check_grad("d_W_out", first[2].double().cpu().numpy(), ref["dW"], "fp32")
+    check_grad("d_b_out", first[3].double().cpu().numpy(), ref["db"], "fp32")
+    for a, b in zip(first, second):
+        # float32 atomics may add in another order
+        np.testing.assert_allclose(b.cpu().numpy(), a.cpu().numpy(), atol=1e-6, rtol=1e-5)
+
+
 # ------------------------------------------------------------------ full-size workloads
 
 def _sampled(inp, tiles, cost_utts, grad_utts):
@@ -182,14 +209,14 @@ def test_medium(tiles):
 def test_medium_large_vocab():
     inp = make_config("medium_lv")
     print("[medium_lv]", flush=True)
-    _sampled(inp, (64, 64, 128), cost_utts=[2, 9], grad_utts=[9])
+    _sampled(inp, (64, 64, 256), cost_utts=[2, 9], grad_utts=[9])
 
 
 def test_long_tiled():
     inp = make_config("long")
     b = int(np.argmin(inp.T_lens.astype(np.int64) * (inp.U_lens + 1)))
     print(f"[long sampled utt {b}]", flush=True)
-    _sampled(inp, (64, 64, 128), cost_utts=[b], grad_utts=[])
+    _sampled(inp, (64, 64, 256), cost_utts=[b], grad_utts=[])
 
 
 @pytest.mark.parametrize("name", ["medium", "long"])
