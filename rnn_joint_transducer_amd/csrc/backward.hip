@@ -105,6 +105,8 @@ struct DhCfg {
   static constexpr int SLICE = ROWB + kTileCells * 16;  // + the dz rows' constants (logit input)
   static constexpr int NST = 3;                   // slices resident
   static constexpr int CPW = ROWB / 1024 / 4;     // 1 KB row copies per wave per slice (12)
+  static constexpr int NMFMA = kBf16 ? 8 : 64;      // MFMA instructions per k-step and wave
+  static constexpr int NVALU = kBf16 ? 2 : 1;       // other VALU per MFMA (dz input)
 };
 
 // slot of 16-byte chunk c (0..7) of 128-byte row r: 16-byte fragment reads of
@@ -132,8 +134,16 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   const int nnb = (H + C::NB - 1) / C::NB;
   const int n_items = ld_const(a.tile_count) * nnb;
   const int nk = (V + C::KB - 1) / C::KB;
-  const int bid = blockIdx.x, gsz = gridDim.x;
-  const int my_items = bid < n_items ? (n_items - 1 - bid) / gsz + 1 : 0;
+  // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  XCD x
+  // takes the x-th of 8 contiguous runs of items, its workgroups striding
+  // through the run together, so that the hidden blocks of one tile (which
+  // read the same dz rows) and the tiles sharing W_out rows run at the same
+  // time on one L2.
+  const int wpx = gridDim.x >> 3, lx = blockIdx.x >> 3, xcd = blockIdx.x & 7;
+  const int per = (n_items + 7) >> 3;
+  const int xbase = xcd * per;
+  const int xcount = min(per, n_items - xbase);
+  const int my_items = xcount > lx ? (xcount - 1 - lx) / wpx + 1 : 0;
   const int total = my_items * nk;  // slices in this workgroup's stream
   if (total == 0) return;
   const uint32_t lbase = lds_addr(lds);
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
     int tile, nb, tix;
   };
   auto item_ref = [&](int i) {  // i-th item of this workgroup
-    const int item = bid + i * gsz;
+    const int item = xbase + lx + i * wpx;
     ItemRef r;
     r.tix = item / nnb;
     r.tile = ld_const(a.tiles + r.tix);
@@ -399,12 +409,16 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
 #pragma unroll
     for (int kk = 0; kk < C::KSTEPS; ++kk) {
       const int fcur = kk & 1;  // KSTEPS is even: parity of the k-step in the stream
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fcur);
       if (kk + 1 < C::KSTEPS) {
         rd(g, kk + 1, fcur ^ 1);
+        interleave_mfma<C::NMFMA, 1, FROMZ ? (C::kBf16 ? 20 : 3) : C::NVALU>();
       } else if (g + 1 < total) {
-        // slice g+1 has landed (g+2 may still be in flight), this wave's
-        // reads of slice g are done, and after the barrier every wave's
-        // are: refill that buffer with slice g+3
+        // (the MFMAs above run on while this wave waits) slice g+1 has
+        // landed (g+2 may still be in flight), this wave's reads of slice g
+        // are done, and after the barrier every wave's are: refill that
+        // buffer with slice g+3
         if (last) {
           wait_vm<0>();
 #pragma unroll
@@ -427,8 +441,6 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
         if (iss_g < total) issue_next();
         rd(g + 1, 0, fcur ^ 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mm(fcur);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -478,6 +490,7 @@ struct DwCfg {
   static constexpr int QPW = (CA + CB) / 4;            // row copies per wave per slice (12)
   static constexpr int SLICE = SA + SB + KB * 16;      // + the slice's cell constants
   static constexpr int NST = 3;
+  static constexpr int NMFMA = kBf16 ? 8 : 64;         // MFMA instructions per k-step and wave
   static_assert(KSTEPS % 2 == 0 && (CA + CB) % 4 == 0, "slice shape");
 };
 
@@ -681,9 +694,13 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
 #pragma unroll
     for (int kk = 0; kk < C::KSTEPS; ++kk) {
       const int fcur = kk & 1;  // KSTEPS is even: parity of the k-step in the stream
+      __builtin_amdgcn_sched_barrier(0);
+      mm(fcur);
       if (kk + 1 < C::KSTEPS) {
         rd(g, kk + 1, fcur ^ 1);
+        interleave_mfma<C::NMFMA, C::kBf16 ? 3 : 1, C::kBf16 ? (FROMZ ? 40 : 4) : (FROMZ ? 6 : 1)>();
       } else if (g + 1 < total) {
+        // (the MFMAs above run on while this wave waits)
         if (g + 2 < total) wait_vm<NQ>();  // slice g+1 landed, g+2 may be in flight
         else wait_vm<0>();
         wait_lgkm0();  // this wave's reads of slice g are done
@@ -691,8 +708,6 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
         if (g + 3 < total) issue(g + 3);
         rd(g + 1, 0, fcur ^ 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      mm(fcur);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -794,8 +809,10 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
   const int nnb = (a.d.H + DhCfg<float>::NB - 1) / DhCfg<float>::NB;
   const long long items = (long long)max_tiles * nnb;
   if (items <= 0) return hipSuccess;
-  const int ncu = device_cu_count();
-  dim3 grid((unsigned)(items < ncu ? items : ncu)), block(256);
+  // a multiple of 8 workgroups (one per XCD in turn), at most one per CU
+  const int ncu = max(8, device_cu_count() & ~7);
+  const long long g8 = (items + 7) / 8 * 8;
+  dim3 grid((unsigned)(g8 < ncu ? g8 : ncu)), block(256);
   const bool fromz = a.cc != nullptr;
   if (bf16) {
     if (fromz) hipLaunchKernelGGL((dh_kernel<uint16_t, true>), grid, block, 0, st, a);

@@ -202,6 +202,19 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
+// Orders the current scheduling region as NM repetitions of (one MFMA, up to
+// NDS LDS reads, up to NV other vector ALU instructions), so that with one
+// wave per SIMD the operand reads and arithmetic of the next k-step issue in
+// the shadow of this k-step's MFMAs instead of after them.
+template <int NM, int NDS, int NV>
+__device__ __forceinline__ void interleave_mfma() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (NDS > 0) __builtin_amdgcn_sched_group_barrier(0x100, NDS, 0);
+    if (NV > 0) __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
 // wait until this wave's LDS reads (and scalar loads) have completed
 __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 // Load of a value the kernel never writes, through the constant address
