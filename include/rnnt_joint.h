@@ -33,8 +33,8 @@
  *     enc, pred, W_out and b_out all have type `dtype`; costs and every
  *     gradient are float32 whatever `dtype` is.
  *   - Modes: tile_t == 0 and tile_u == 0 selects the UNTILED mode: the forward
- *     stores the logits (dtype) in `saved` and the backward forms the logit
- *     gradients from them as it goes (`saved` is read, not modified).
+ *     stores the logits (dtype) in `saved` and the backward turns them into
+ *     the logit gradients in place, so one forward feeds one backward.
  *     Otherwise the TILED mode stores only per-cell scalars and recomputes the
  *     joint and logits in the backward, one lattice chunk of tile_t frames x
  *     tile_u label positions (all utterances) at a time; 0 on one axis means
@@ -110,8 +110,7 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
  * [B, tile_t, tile_u, H] in dtype (the whole padded lattice when untiled)
  * and, in the tiled mode, that chunk's logit gradients [B, tile_t, tile_u, V]
  * in dtype plus the active-tile list of every chunk (int32, one word per
- * 16 x 8 tile); in the untiled mode, 16 bytes of logit-gradient constants per
- * cell of the padded lattice.  Writes *out; returns a status code.
+ * 16 x 8 tile).  Writes *out; returns a status code.
  */
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
                                     int tile_t, int tile_u, int tile_v, int pass,
@@ -138,9 +137,13 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out,
  * d_b_out [V] (float32) with the gradients of sum_b grad_costs[b] * costs[b]
  * (grad_costs float32 [B] on the device, or NULL for all ones).  Takes the
  * same inputs, sizes and tiles as the forward that filled `saved`; the whole
- * batch is handled in one call; `saved` is only read, so one forward may
- * feed several backward calls.  Entries of d_enc / d_pred past each utterance's lengths
- * are zero.  Returns a status code (host-side checks and launch errors only).
+ * batch is handled in one call.  Tiled mode: `saved` is only read, so one
+ * forward may feed several backward calls.  Untiled mode: the stored logits
+ * become the logit gradients in place and `saved` is marked consumed; a
+ * second backward from it gives invalid gradients and sets data-error bit 4
+ * (rnnt_joint_loss_status).  Entries of d_enc / d_pred past each utterance's
+ * lengths are zero.  Returns a status code (host-side checks and launch
+ * errors only).
  */
 int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,
                         const void* b_out, int dtype, const int32_t* labels,
@@ -153,7 +156,9 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,
 /*
  * Synchronises `stream`, then copies the data-error word of `saved` to
  * *data_error: 0 = every utterance valid, else a bit mask (1 = a length out of
- * range, 2 = a label out of range or equal to blank).  Returns a status code.
+ * range, 2 = a label out of range or equal to blank, 4 = an untiled backward
+ * ran on a state whose logits an earlier backward had already consumed).
+ * Returns a status code.
  */
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error);
 

@@ -155,12 +155,20 @@ def _make_function():
                                                blank, tile_t, tile_u, tile_v)
             ctx.save_for_backward(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved)
             ctx.cfg = (blank, tile_t, tile_u, tile_v)
+            ctx.consumed = False
             return costs
 
         @staticmethod
         def backward(ctx, grad_costs):
             enc, pred, W_out, b_out, labels, T_lens, U_lens, saved = ctx.saved_tensors
             blank, tile_t, tile_u, tile_v = ctx.cfg
+            if tile_t == 0 and tile_u == 0:
+                if ctx.consumed:
+                    raise RuntimeError(
+                        "rnnt_joint_loss: the untiled backward turns the forward's stored logits "
+                        "into gradients in place, so it runs once per forward; use a tiled mode "
+                        "(tile_t or tile_u > 0) to differentiate the same graph again")
+                ctx.consumed = True
             d_enc, d_pred, d_W, d_b = rnnt_joint_loss_bwd(
                 enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, blank, tile_t, tile_u,
                 tile_v, grad_costs=grad_costs.float().contiguous())
@@ -175,9 +183,10 @@ _FN = None
 
 def rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, tile_t=0,
                     tile_u=0, tile_v=0):
-    """Per-utterance costs [B] with autograd support.  The saved forward state is
-    only read by the backward, so a graph kept with retain_graph=True may be
-    differentiated more than once."""
+    """Per-utterance costs [B] with autograd support.  In the untiled mode the
+    backward consumes the forward's stored logits (one backward per forward);
+    in a tiled mode the saved state is only read, so a graph kept with
+    retain_graph=True may be differentiated again."""
     global _FN
     if _FN is None:
         _FN = _make_function()

@@ -35,7 +35,7 @@ struct Plan {
       o_cs, o_tiles, o_tcount, o_z;
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
-  size_t o_ws_db, o_ws_g, o_ws_h, o_ws_tiles, o_ws_tcount, o_ws_cc;  // backward workspace layout
+  size_t o_ws_db, o_ws_g, o_ws_h, o_ws_tiles, o_ws_tcount;  // backward workspace layout
   int cap_all;                // active-tile list capacity of the whole lattice
   int n_cu_chunks, n_chunks;  // backward chunk grid (tiled mode)
   int cap_chunk;              // active-tile list capacity of one chunk
@@ -107,9 +107,7 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
   q.o_ws_tiles = q.o_ws_h + align_up(q.elem * (size_t)B * q.CT * q.CU * H);
   q.o_ws_tcount = q.o_ws_tiles + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks * q.cap_chunk));
-  q.o_ws_cc = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
-  // untiled: logit-gradient constants of every row of the active tiles
-  q.ws_bwd = q.o_ws_cc + (q.untiled ? align_up(16 * (size_t)q.cap_all * kTileCells) : 0);
+  q.ws_bwd = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
   return RNNTJ_OK;
 }
 
@@ -369,13 +367,10 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   h.d_pred = d_pred;
   DwArgs w = {};
   w.h = hchunk;
-  w.gcost = grad_costs;
   w.d = p.d;
   w.d_W = d_W_out;
   w.d_b64 = db64;
   h.gcost = grad_costs;
-  // split-K of the weight-gradient GEMM: about two workgroups per compute
-  // unit, at most one run of the tile list per tile
   // split-K runs of the dW GEMM: one workgroup per compute unit (one round),
   // fewest float32 partial sums per output element
   auto kparts_for = [&](int max_tiles) {
@@ -383,23 +378,22 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
     int k = device_cu_count() / per;
     return k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
   };
-  auto finalize = [&] {
-    return timed("db_finalize", st, [&] { return launch_db_finalize(db64, d_b_out, V, st); });
+  auto finalize = [&](int32_t* mark) {
+    return timed("db_finalize", st,
+                 [&] { return launch_db_finalize(db64, d_b_out, V, mark, st); });
   };
 
   if (p.untiled) {
-    // the stored logits are turned into logit gradients on the fly by the
-    // dh and dW GEMMs, from per-cell constants
+    // the stored logits become the logit gradients in place; dh and dW then
+    // read them as plain GEMM operands
     void* z = at<char>(saved, p.o_z);
-    float4* cc = at<float4>(workspace, p.o_ws_cc);
     a.tiles = at<int32_t>(saved, p.o_tiles);
     a.tile_count = at<int32_t>(saved, p.o_tcount);
     a.ct0 = 0; a.cu0 = 0; a.CT = p.d.Tpad; a.CU = p.d.U1pad;
-    if ((e = timed("cell_consts", st, [&] { return launch_cell_consts(a, p.cap_all, cc, st); })) !=
-        hipSuccess)
+    if ((e = timed("grad_inplace", st,
+                   [&] { return launch_grad_inplace(z, p.bf16, a, p.cap_all, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
     h.g = z;
-    h.cc = cc;
     h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad;
     h.tiles = a.tiles;
     h.tile_count = a.tile_count;
@@ -408,14 +402,13 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
     if ((e = timed("hrow", st, [&] { return launch_hrow(hchunk, p.bf16, a, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
     w.g = z;
-    w.cc = cc;
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
     w.tiles = a.tiles;
     w.tile_count = a.tile_count;
     w.kparts = kparts_for(p.cap_all);
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    return finalize() == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
+    return finalize(a.hdr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
   }
 
   // tiled: one lattice chunk of CT frames x CU label positions at a time.
@@ -467,7 +460,7 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
         return RNNTJ_ERR_HIP;
     }
   }
-  return finalize() == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
+  return finalize(nullptr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
 }
 
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error) {

@@ -9,9 +9,10 @@
 //   d_enc[t] = sum_u dpre(t,u),  d_pred[u] = sum_t dpre(t,u)
 //
 // Kernels here:
-//   cell_consts_kernel : untiled mode, per-cell constants of dz (from the
-//                        float64 posteriors) for the GEMMs below, which form
-//                        dz from the stored logits on the fly.
+//   grad_inplace_kernel: untiled mode, the stored logits -> dz in place, one
+//                        active tile per workgroup (constants of its rows
+//                        from the float64 posteriors, then a 16-byte stream
+//                        per lane).
 //   dh_kernel          : MFMA GEMM dz[cells, V] x W_out^T -> [cells, H] per
 //                        active 16x8 tile and 256 hidden columns, with the
 //                        (1 - h^2) epilogue and the two lattice reductions
@@ -37,22 +38,15 @@ constexpr uint32_t kCellLabel = 0x3FFFFFFFu, kCellNeg = 0x40000000u, kCellOut = 
 
 // ------------------------------------------------------------ untiled dz
 
-// Constants of the logit gradient of every row of the active tiles, from the
-// float64 transition posteriors (see launch_cell_consts).  With
-// dz[v] = gc (occ p[v] - gB [v=blank] - gE [v=label]) and p = softmax(z):
+// Constants of the logit gradient of lattice row (t, u) of utterance b.
+// With dz[v] = gc (occ p[v] - gB [v=blank] - gE [v=label]) and p = softmax(z):
 //   x = (lse - ln(occ |gc|)) log2(e), so that gc occ p[v] = sgn(gc) 2^(z log2(e) - x)
 //       (+inf when occ gc = 0: the term vanishes),
 //   y = gc gB,  z = gc gE,
 //   w (bits) = label + 1 in bits 0..29 (0: no label at this u), bit 30 set when
 //       gc < 0, bit 31 set for a cell outside the lattice (dz = 0).
-__global__ __launch_bounds__(128) void cell_consts_kernel(JointArgs a, float4* __restrict__ out) {
-  const int tix = blockIdx.x;
-  if (tix >= a.tile_count[0]) return;
-  int b, tt, tu;
-  tile_unpack(a.tiles[tix], b, tt, tu);
+__device__ float4 cell_consts(const JointArgs& a, int b, int t, int u) {
   const Dims d = a.d;
-  const int r = threadIdx.x;
-  const int t = a.ct0 + tt * kTileT + (r >> 3), u = a.cu0 + tu * kTileU + (r & 7);
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   float4 o = make_float4(kInf, 0.f, 0.f, __uint_as_float(kCellOut));
   if (t < Tl && u <= Ul) {
@@ -67,7 +61,7 @@ __global__ __launch_bounds__(128) void cell_consts_kernel(JointArgs a, float4* _
     const uint32_t lab = u < Ul ? (uint32_t)a.labels[(size_t)b * d.U + u] + 1u : 0u;
     o.w = __uint_as_float(lab | (g < 0.0 ? kCellNeg : 0u));
   }
-  out[(size_t)tix * kTileCells + r] = o;
+  return o;
 }
 
 // dz of logit v of a cell from the stored logit z and the cell's constants;
@@ -79,6 +73,71 @@ __device__ __forceinline__ float dz_from_z(float z, int v, int v1, const float4&
   g -= (v == blank) ? c.y : 0.f;
   g -= ((int)(w & kCellLabel) == v1) ? c.z : 0.f;
   return (int)w < 0 ? 0.f : g;
+}
+
+// Untiled backward: the stored logits of active tile blockIdx.x become its
+// logit gradients (in place, same type).  Wave w walks rows 32w .. 32w+31 of
+// the tile (4 frames x 8 label positions, contiguous per frame); each lane
+// takes 16-byte chunks of a row, eight loads in flight.  Rows outside the
+// lattice are written as zeros.  A forward's logits serve one backward: the
+// backward marks the state (kFlagConsumed, set by its last kernel), and a
+// later backward from the same state reports kErrConsumed.
+template <typename T>
+__global__ __launch_bounds__(256) void grad_inplace_kernel(JointArgs a, T* __restrict__ z) {
+  constexpr int CE = 16 / (int)sizeof(T);
+  __shared__ float4 cs[kTileCells];
+  const int tix = blockIdx.x, tid = threadIdx.x;
+  if (tix == 0 && tid == 0 && (a.hdr[1] & kFlagConsumed)) atomicOr(&a.hdr[0], kErrConsumed);
+  if (tix >= a.tile_count[0]) return;
+  int b, tt, tu;
+  tile_unpack(a.tiles[tix], b, tt, tu);
+  const Dims d = a.d;
+  const int t0 = tt * kTileT, u0 = tu * kTileU;
+  if (tid < kTileCells) cs[tid] = cell_consts(a, b, t0 + (tid >> 3), u0 + (tid & 7));
+  __syncthreads();
+  const int w = tid >> 6, lane = tid & 63, V = d.V;
+  const int nch = (V + 64 * CE - 1) / (64 * CE);  // chunk columns per row per lane
+  const int n = 32 * nch;                         // (row, chunk) pairs of this wave
+  T* const zt = z + (((size_t)b * d.Tpad + t0) * d.U1pad + u0) * V;
+  for (int i0 = 0; i0 < n; i0 += 8) {
+    u32x4 x[8];
+    T* ptr[8];
+    bool ok[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = i0 + k, rr = i / nch, v0 = ((i % nch) * 64 + lane) * CE;
+      const int r = 32 * w + rr;
+      ok[k] = i < n && v0 < V;
+      ptr[k] = zt + ((size_t)(r >> 3) * d.U1pad + (r & 7)) * V + v0;
+      if (ok[k]) x[k] = *reinterpret_cast<const u32x4*>(ptr[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (!ok[k]) continue;
+      const int i = i0 + k, v0 = ((i % nch) * 64 + lane) * CE;
+      const float4 c = cs[32 * w + i / nch];
+      float g[CE];
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < CE; ++e) {
+          const uint32_t bits = (x[k][e >> 1] >> (16 * (e & 1))) << 16;
+          g[e] = dz_from_z(__uint_as_float(bits & 0xffff0000u), v0 + e, v0 + e + 1, c, d.blank);
+        }
+        u32x4 y;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          y[q] = (uint32_t)ElemTraits<uint16_t>::from_f32(g[2 * q]) |
+                 ((uint32_t)ElemTraits<uint16_t>::from_f32(g[2 * q + 1]) << 16);
+        *reinterpret_cast<u32x4*>(ptr[k]) = y;
+      } else {
+#pragma unroll
+        for (int e = 0; e < CE; ++e)
+          g[e] = dz_from_z(__uint_as_float(x[k][e]), v0 + e, v0 + e + 1, c, d.blank);
+        *reinterpret_cast<u32x4*>(ptr[k]) =
+            u32x4{__float_as_uint(g[0]), __float_as_uint(g[1]), __float_as_uint(g[2]), __float_as_uint(g[3])};
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------ dh GEMM
@@ -101,12 +160,11 @@ struct DhCfg {
   static constexpr int KSTEPS = KB / 16;          // 16-wide k-steps per slice: bf16 4, fp32 2
   static constexpr int NB = 256;                  // hidden columns per item
   static constexpr int ROWS = kTileCells + NB;    // slice rows: 128 dz rows, then 256 W_out rows
-  static constexpr int ROWB = ROWS * 128;         // 48 KB of rows
-  static constexpr int SLICE = ROWB + kTileCells * 16;  // + the dz rows' constants (logit input)
+  static constexpr int SLICE = ROWS * 128;        // 48 KB
   static constexpr int NST = 3;                   // slices resident
-  static constexpr int CPW = ROWB / 1024 / 4;     // 1 KB row copies per wave per slice (12)
+  static constexpr int CPW = SLICE / 1024 / 4;    // 1 KB copies per wave per slice (12)
   static constexpr int NMFMA = kBf16 ? 8 : 64;      // MFMA instructions per k-step and wave
-  static constexpr int NVALU = kBf16 ? 2 : 1;       // other VALU per MFMA (dz input)
+  static constexpr int NVALU = kBf16 ? 2 : 1;       // other VALU per MFMA
 };
 
 // slot of 16-byte chunk c (0..7) of 128-byte row r: 16-byte fragment reads of
@@ -119,7 +177,7 @@ __device__ __forceinline__ int slot128(int r, int c) { return c ^ ((r >> 1) & 7)
 // else is in flight.
 __device__ __forceinline__ void touch(float x) { asm volatile("" ::"v"(x)); }
 
-template <typename T, bool FROMZ>
+template <typename T>
 __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   using C = DhCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
@@ -177,9 +235,7 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
     return it;
   };
 
-  // Direct copies of one slice (the 128 rows' logit-gradient constants
-  // travel with every slice: one more half-wave copy per wave).
-  // Copy q of wave w fills slice rows
+  // Direct copies of one slice: copy q of wave w fills slice rows
   // 8 (CPW w + q) .. +7; lane l takes row 8 (CPW w + q) + l/8 and LDS slot
   // l%8, holding 16-byte chunk slot128(row, l%8).  Rows below 128 are dz
   // rows of the tile (cells outside the lattice read the tile's first cell,
@@ -192,11 +248,9 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   // offsets from W_out.  Both fit 32 bits (a tile spans 16 frames of one
   // chunk; W_out is at most 768 rows).
   const T* gbase = G;
-  const float4* ccsrc = a.cc;
   uint32_t coff[C::CPW];
   auto set_sources = [&](ItemRef ref) {
     const Item it = decode(ref);
-    if constexpr (FROMZ) ccsrc = a.cc + (size_t)ref.tix * kTileCells + 32 * w + (lane & 31);
     gbase = G + (((size_t)it.b * a.CT + (it.t0 - a.ct0)) * a.CU + (it.u0 - a.cu0)) * V;
 #pragma unroll
     for (int q = 0; q < C::CPW; ++q) {
@@ -230,11 +284,8 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
       }
       dma16(base + off, st + q * 1024);
     }
-    if constexpr (FROMZ) {
-      if (lane < 32) dma16(ccsrc, lbase + buf * C::SLICE + C::ROWB + 512 * w);
-    }
   };
-  constexpr int kCopies = C::CPW + (FROMZ ? 1 : 0);  // per wave per slice
+  constexpr int kCopies = C::CPW;  // per wave per slice
 
   f32x16 acc[2][4];
 #pragma unroll
@@ -261,15 +312,6 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
       } else {
         fa[fbuf][i].lo = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh) << 4));
         fa[fbuf][i].hi = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh + 1) << 4));
-      }
-      if constexpr (FROMZ) {
-        // logits -> logit gradients of this row (rounded as the stored dz would be)
-        const float4 c = *reinterpret_cast<const float4*>(sl + C::ROWB + 16 * r);
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          x[e] = dz_from_z(fa[fbuf][i].get(e), kbase + e, kbase + e + 1, c, d.blank);
-        pack_frag(fa[fbuf][i], x);
       }
       if (vtail && kbase >= V) zero_frag(fa[fbuf][i]);  // vocabulary tail
     }
@@ -413,7 +455,7 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
       mm(fcur);
       if (kk + 1 < C::KSTEPS) {
         rd(g, kk + 1, fcur ^ 1);
-        interleave_mfma<C::NMFMA, 1, FROMZ ? (C::kBf16 ? 20 : 3) : C::NVALU>();
+        interleave_mfma<C::NMFMA, 1, C::NVALU>();
       } else if (g + 1 < total) {
         // (the MFMAs above run on while this wave waits) slice g+1 has
         // landed (g+2 may still be in flight), this wave's reads of slice g
@@ -471,9 +513,8 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
 // rows of h and dz stream through LDS in slices of KB cells (direct copies,
 // three slices resident, issued three ahead) and are read as MFMA operands
 // with transposing (bf16) or scalar (fp32) LDS reads, so neither operand is
-// transposed in memory.  With logit input, dz is formed from the logits and
-// per-cell constants, which travel with each slice.  4 waves (2 x 2), each 64
-// hidden rows x 128 vocabulary columns.
+// transposed in memory.  4 waves (2 x 2), each 64 hidden rows x 128
+// vocabulary columns.
 template <typename T>
 struct DwCfg {
   static constexpr bool kBf16 = sizeof(T) == 2;
@@ -488,7 +529,7 @@ struct DwCfg {
   static constexpr int SA = KB * ROWA, SB = KB * ROWB; // 16 KB, 32 KB
   static constexpr int CA = SA / 1024, CB = SB / 1024; // 1 KB copies per part
   static constexpr int QPW = (CA + CB) / 4;            // row copies per wave per slice (12)
-  static constexpr int SLICE = SA + SB + KB * 16;      // + the slice's cell constants
+  static constexpr int SLICE = SA + SB;
   static constexpr int NST = 3;
   static constexpr int NMFMA = kBf16 ? 8 : 64;         // MFMA instructions per k-step and wave
   static_assert(KSTEPS % 2 == 0 && (CA + CB) % 4 == 0, "slice shape");
@@ -498,7 +539,7 @@ struct DwCfg {
 // consecutive rows and the scalar reads of rows r, r+8 hit distinct banks
 __device__ __forceinline__ int swz_dw(int r) { return (4 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
 
-template <typename T, bool FROMZ>
+template <typename T>
 __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
   using C = DwCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
@@ -532,9 +573,7 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
   // issued by wave q % 4; lane l fills 16 bytes of the part at offset
   // 1024 q' + 16 l.  The element offset of each copy inside a tile is fixed
   // per item; a slice adds its tile base and (slice in tile) * KB/8 frames.
-  // With logit input, wave w also copies the constants of cells
-  // KB/4 w .. KB/4 (w+1) - 1 of the slice (lanes below KB/4).
-  constexpr int NQ = C::QPW + (FROMZ ? 1 : 0);  // copies per wave per slice
+  constexpr int NQ = C::QPW;  // copies per wave per slice
   uint32_t coff[C::QPW];
 #pragma unroll
   for (int k = 0; k < C::QPW; ++k) {
@@ -568,11 +607,6 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
       const int q = w + 4 * k;
       if (q < C::CA) dma16(hb + coff[k], st + q * 1024);
       else dma16(gb + coff[k], st + C::SA + (q - C::CA) * 1024);
-    }
-    if constexpr (FROMZ) {
-      if (lane < C::KB / 4)
-        dma16(a.cc + (size_t)tix * kTileCells + ss * C::KB + (C::KB / 4) * w + lane,
-              st + C::SA + C::SB + 4 * C::KB * w);
     }
   };
 
@@ -653,21 +687,6 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
     for (int i = 0; i < 2; ++i) fa[fbuf][i] = frag_T(sl, offA[i], sl, C::ROWA, kk, 64 * wm + 32 * i);
 #pragma unroll
     for (int j = 0; j < 4; ++j) fb[fbuf][j] = frag_T(sl, offB[j], sl + C::SA, C::ROWB, kk, 128 * wn + 32 * j);
-    if constexpr (FROMZ) {
-      // logits -> logit gradients, with the cells' constants
-      const float4* cs = reinterpret_cast<const float4*>(sl + C::SA + C::SB);
-      float4 c[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = cs[16 * kk + 8 * kh + e];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int v = n0 + 128 * wn + 32 * j + lc;
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = dz_from_z(fb[fbuf][j].get(e), v, v + 1, c[e], d.blank);
-        pack_frag(fb[fbuf][j], x);
-      }
-    }
     if (do_db) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) dbacc[j] += (double)fsum(fb[fbuf][j]);
@@ -698,7 +717,7 @@ __global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
       mm(fcur);
       if (kk + 1 < C::KSTEPS) {
         rd(g, kk + 1, fcur ^ 1);
-        interleave_mfma<C::NMFMA, C::kBf16 ? 3 : 1, C::kBf16 ? (FROMZ ? 40 : 4) : (FROMZ ? 6 : 1)>();
+        interleave_mfma<C::NMFMA, C::kBf16 ? 3 : 1, C::kBf16 ? 4 : 1>();
       } else if (g + 1 < total) {
         // (the MFMAs above run on while this wave waits)
         if (g + 2 < total) wait_vm<NQ>();  // slice g+1 landed, g+2 may be in flight
@@ -778,15 +797,18 @@ __global__ __launch_bounds__(256) void hrow_kernel(JointArgs a, T* __restrict__ 
   }
 }
 
-__global__ void db_finalize_kernel(const double* __restrict__ src, float* __restrict__ dst, int V) {
+__global__ void db_finalize_kernel(const double* __restrict__ src, float* __restrict__ dst, int V,
+                                   int32_t* mark) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
   if (v < V) dst[v] = (float)src[v];
+  if (mark && v == 0) atomicOr(&mark[1], kFlagConsumed);  // the stored logits are now dz
 }
 
 }  // namespace
 
-hipError_t launch_db_finalize(const double* db64, float* d_b, int V, hipStream_t st) {
-  hipLaunchKernelGGL(db_finalize_kernel, dim3((V + 255) / 256), dim3(256), 0, st, db64, d_b, V);
+hipError_t launch_db_finalize(const double* db64, float* d_b, int V, int32_t* mark, hipStream_t st) {
+  hipLaunchKernelGGL(db_finalize_kernel, dim3((V + 255) / 256), dim3(256), 0, st, db64, d_b, V,
+                     mark);
   return hipGetLastError();
 }
 
@@ -799,9 +821,15 @@ hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_cell_consts(const JointArgs& a, int max_tiles, float4* out, hipStream_t st) {
+hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, int max_tiles,
+                               hipStream_t st) {
   if (max_tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL(cell_consts_kernel, dim3(max_tiles), dim3(kTileCells), 0, st, a, out);
+  if (bf16)
+    hipLaunchKernelGGL(grad_inplace_kernel<uint16_t>, dim3(max_tiles), dim3(256), 0, st, a,
+                       static_cast<uint16_t*>(z));
+  else
+    hipLaunchKernelGGL(grad_inplace_kernel<float>, dim3(max_tiles), dim3(256), 0, st, a,
+                       static_cast<float*>(z));
   return hipGetLastError();
 }
 
@@ -813,14 +841,8 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
   const int ncu = max(8, device_cu_count() & ~7);
   const long long g8 = (items + 7) / 8 * 8;
   dim3 grid((unsigned)(g8 < ncu ? g8 : ncu)), block(256);
-  const bool fromz = a.cc != nullptr;
-  if (bf16) {
-    if (fromz) hipLaunchKernelGGL((dh_kernel<uint16_t, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((dh_kernel<uint16_t, false>), grid, block, 0, st, a);
-  } else {
-    if (fromz) hipLaunchKernelGGL((dh_kernel<float, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((dh_kernel<float, false>), grid, block, 0, st, a);
-  }
+  if (bf16) hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(dh_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 
@@ -830,14 +852,8 @@ hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st) {
   const long long items = (long long)nmb * nnb * a.kparts;
   if (items <= 0) return hipSuccess;
   dim3 grid((unsigned)((items + 7) / 8 * 8)), block(256);  // 8 XCDs, items grouped per XCD
-  const bool fromz = a.cc != nullptr;
-  if (bf16) {
-    if (fromz) hipLaunchKernelGGL((dw_kernel<uint16_t, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((dw_kernel<uint16_t, false>), grid, block, 0, st, a);
-  } else {
-    if (fromz) hipLaunchKernelGGL((dw_kernel<float, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((dw_kernel<float, false>), grid, block, 0, st, a);
-  }
+  if (bf16) hipLaunchKernelGGL(dw_kernel<uint16_t>, grid, block, 0, st, a);
+  else hipLaunchKernelGGL(dw_kernel<float>, grid, block, 0, st, a);
   return hipGetLastError();
 }
 

@@ -14,7 +14,10 @@ enum JointMode { kLse = 0, kStoreZ = 1, kGrad = 2 };
 // Header of the forward -> backward state (int32 words): [0] data-error mask,
 // [1] flags, [2] float bits of max_v (sum_k |W_out[k,v]| + |b_out[v]|), an
 // upper bound on every |z| since |h| <= 1.
-constexpr int kFlagEpBad = 1;  // some finite |enc| or |pred| > 40
+constexpr int kFlagEpBad = 1;     // some finite |enc| or |pred| > 40
+constexpr int kFlagConsumed = 2;  // an untiled backward turned the stored logits into dz
+// data-error bit: a backward found its logits already consumed by another
+constexpr int kErrConsumed = 4;
 
 // Active-tile lists.  A lattice chunk (frames ct0 .. ct0+CT-1, label
 // positions cu0 .. cu0+CU-1) is covered by 16 x 8 cell tiles; a tile is
@@ -40,7 +43,7 @@ struct JointArgs {
   const int32_t* labels;
   const int32_t* Teff;  // validated lengths (0 frames = invalid utterance)
   const int32_t* Ueff;
-  const int32_t* hdr;   // state header (flags, logit bound)
+  int32_t* hdr;         // state header (data-error mask, flags, logit bound)
   const float* Eexp;    // e^{2 enc} [B, T, H]
   const float* Pexp;    // e^{2 pred} [B, U+1, H]
   Dims d;
@@ -117,7 +120,6 @@ struct DhArgs {
   Dims d;
   const int32_t* tiles;       // active tiles of the chunk
   const int32_t* tile_count;
-  const float4* cc;           // per-cell constants (g holds logits) or null (g holds dz)
   const float* gcost;         // [B] or null
   int ct0, cu0, CT, CU;
   float* d_enc;
@@ -126,23 +128,19 @@ struct DhArgs {
 // Persistent launch; max_tiles bounds the entries of the tile list.
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st);
 
-// Per-cell constants of the logit gradient (untiled backward), one float4
-// per row of every active tile (list order x 128 rows):
-//   dz[v] = gc * exp2(z[v] log2(e) - x) - y [v = blank] - z [v = label]
-// x = (lse - ln occ) log2(e) (+inf when occ = 0), y = gc gB, z = gc gE, and w
-// the bits of the label (-1: none, -2: the cell is outside the lattice, dz = 0).
-hipError_t launch_cell_consts(const JointArgs& a, int max_tiles, float4* out, hipStream_t st);
+// Untiled backward: the stored logits [B, Tpad, U1pad, V] of the active tiles
+// become the logit gradients (same type), rows outside the lattice zero; a.hdr
+// must point at the (writable) state header.  One workgroup per list entry.
+hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, int max_tiles,
+                               hipStream_t st);
 
 // d_W_out += h^T dz and d_b64 += column sums of dz (float64) over the active
-// tiles of one chunk (split-K over the tile list).  With `cc` set, g holds
-// the logits and dz is formed from them on the fly (untiled backward).
+// tiles of one chunk (split-K over the tile list).
 struct DwArgs {
-  const void* g;              // dz (or logit) rows [B, CT, CU, V]
+  const void* g;              // dz rows [B, CT, CU, V]
   const void* h;              // h rows [B, CT, CU, H]; rows of cells outside the lattice are 0
   const int32_t* tiles;       // active tiles of the chunk
   const int32_t* tile_count;
-  const float4* cc;           // per-cell constants (logit input) or null (dz input)
-  const float* gcost;         // [B] or null
   Dims d;
   int ct0, cu0, CT, CU;
   int kparts;                 // split-K: parts of the tile list
@@ -151,7 +149,9 @@ struct DwArgs {
 };
 hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st);
 
-// d_b[v] = (float) db64[v]
-hipError_t launch_db_finalize(const double* db64, float* d_b, int V, hipStream_t st);
+// d_b[v] = (float) db64[v]; with `mark` (the state header of an untiled
+// backward) also sets kFlagConsumed in mark[1].
+hipError_t launch_db_finalize(const double* db64, float* d_b, int V, int32_t* mark,
+                              hipStream_t st);
 
 }  // namespace rnntj

@@ -58,10 +58,9 @@ def test_buffer_sizes():
     # 8 x 2 chunks, each with a list of 16 * 4 * 8 tiles, and 16 tile counts
     lists = 16 * (16 * 4 * 8) * 4 + 256
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + chunk * (1024 + 640) * 2 + lists)
-    # untiled: h rows of the padded lattice and one float4 of logit-gradient
-    # constants per row of every 16 x 8 tile
-    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024 + 16 * 512 * 104 * 640 * 2
-                                                 + 16 * 32 * 13 * 128 * 16)
+    # untiled: h rows of the padded lattice (the logit gradients replace the
+    # stored logits in place)
+    assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024 + 16 * 512 * 104 * 640 * 2)
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, 0, 0) == (0, 0)
 
 

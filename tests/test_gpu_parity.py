@@ -135,10 +135,7 @@ def test_autograd_wrapper():
     check_grad("d_W_out", dev["W_out"].grad.double().cpu().numpy(), ref["dW"], "fp32")
 
 
-@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
-def test_saved_state_reused(tiles):
-    """The backward only reads the forward's saved state: a second backward
-    from the same forward gives the same gradients (retain_graph)."""
+def _grad_leaves(tiles, grad_costs):
     import torch
     import rnn_joint_transducer_amd as rj
     inp = make_config("tiny")
@@ -146,20 +143,56 @@ def test_saved_state_reused(tiles):
     for k in ("enc", "pred", "W_out", "b_out"):
         dev[k].requires_grad_(True)
     costs = rj.rnnt_joint_loss(**dev, tile_t=tiles[0], tile_u=tiles[1], tile_v=tiles[2])
-    loss = (costs * torch.tensor([2.0, -0.5], device=costs.device)).sum()
+    loss = (costs * torch.tensor(grad_costs, device=costs.device)).sum()
+    return inp, dev, loss
+
+
+def test_saved_state_reused_tiled():
+    """Tiled mode: the backward only reads the forward's saved state, so a
+    second backward from the same forward (retain_graph) gives the same
+    gradients; a negative cost gradient exercises the sign handling."""
+    inp, dev, loss = _grad_leaves((16, 8, 0), [2.0, -0.5])
+    keys = ("enc", "pred", "W_out", "b_out")
     loss.backward(retain_graph=True)
-    first = [dev[k].grad.clone() for k in ("enc", "pred", "W_out", "b_out")]
-    for k in ("enc", "pred", "W_out", "b_out"):
+    first = [dev[k].grad.clone() for k in keys]
+    for k in keys:
         dev[k].grad = None
     loss.backward()
-    second = [dev[k].grad for k in ("enc", "pred", "W_out", "b_out")]
     ref = _oracle_full(inp, grad_costs=[2.0, -0.5])
     check_grad("d_enc", first[0].double().cpu().numpy(), ref["dEnc"], "fp32")
     check_grad("d_W_out", first[2].double().cpu().numpy(), ref["dW"], "fp32")
     check_grad("d_b_out", first[3].double().cpu().numpy(), ref["db"], "fp32")
-    for a, b in zip(first, second):
+    for k, a in zip(keys, first):
         # float32 atomics may add in another order
-        np.testing.assert_allclose(b.cpu().numpy(), a.cpu().numpy(), atol=1e-6, rtol=1e-5)
+        np.testing.assert_allclose(dev[k].grad.cpu().numpy(), a.cpu().numpy(), atol=1e-6, rtol=1e-5)
+
+
+def test_untiled_state_consumed_once():
+    """Untiled mode: the backward turns the stored logits into gradients in
+    place.  Its gradients are right (negative cost gradient included); the
+    autograd wrapper refuses a second backward, and a second call through the
+    C ABI is reported by the status word (bit 4)."""
+    import rnn_joint_transducer_amd as rj
+    inp, dev, loss = _grad_leaves((0, 0, 0), [2.0, -0.5])
+    loss.backward(retain_graph=True)
+    ref = _oracle_full(inp, grad_costs=[2.0, -0.5])
+    check_grad("d_enc", dev["enc"].grad.double().cpu().numpy(), ref["dEnc"], "fp32")
+    check_grad("d_pred", dev["pred"].grad.double().cpu().numpy(), ref["dPred"], "fp32")
+    check_grad("d_W_out", dev["W_out"].grad.double().cpu().numpy(), ref["dW"], "fp32")
+    check_grad("d_b_out", dev["b_out"].grad.double().cpu().numpy(), ref["db"], "fp32")
+    with pytest.raises(RuntimeError, match="once per forward"):
+        loss.backward()
+    d = to_device(inp)
+    costs, saved = rj.rnnt_joint_loss_fwd(**d)
+    rj.rnnt_joint_loss_bwd(**d, saved=saved)
+    assert rj.rnnt_joint_loss_status(saved) == 0
+    rj.rnnt_joint_loss_bwd(**d, saved=saved)
+    assert rj.rnnt_joint_loss_status(saved) == 4
+    # a new forward into the same buffer starts clean
+    rj.rnnt_joint_loss_fwd(**d, costs=costs, saved=saved)
+    g = rj.rnnt_joint_loss_bwd(**d, saved=saved)
+    assert rj.rnnt_joint_loss_status(saved) == 0
+    check_grad("d_W_out", g[2].double().cpu().numpy(), _oracle_full(inp)["dW"], "fp32")
 
 
 # ------------------------------------------------------------------ full-size workloads
