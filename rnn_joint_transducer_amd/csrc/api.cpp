@@ -365,17 +365,19 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   h.d = p.d;
   h.d_enc = d_enc;
   h.d_pred = d_pred;
+  h.ksplit = 1;
   DwArgs w = {};
   w.h = hchunk;
   w.d = p.d;
   w.d_W = d_W_out;
   w.d_b64 = db64;
   h.gcost = grad_costs;
-  // split-K runs of the dW GEMM: one workgroup per compute unit (one round),
-  // fewest float32 partial sums per output element
+  // split-K runs of the dW GEMM: one round of resident workgroups (two per
+  // compute unit for bf16, one for fp32), fewest float32 partial sums per
+  // output element
   auto kparts_for = [&](int max_tiles) {
     const int per = ((H + 127) / 128) * ((V + 255) / 256);
-    int k = device_cu_count() / per;
+    int k = device_cu_count() * (p.bf16 ? 2 : 1) / per;
     return k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
   };
   auto finalize = [&](int32_t* mark) {

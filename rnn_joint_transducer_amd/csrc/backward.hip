@@ -156,20 +156,30 @@ template <typename T>
 struct DhCfg {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int CE = 16 / (int)sizeof(T);  // elements per 16-byte chunk
-  static constexpr int KB = 8 * CE;               // vocabulary entries per slice (128-byte rows)
-  static constexpr int KSTEPS = KB / 16;          // 16-wide k-steps per slice: bf16 4, fp32 2
+  // bf16: 64-byte slice rows and two workgroups per CU (two waves per SIMD);
+  // fp32: 128-byte rows, one workgroup per CU
+  static constexpr int RB = kBf16 ? 64 : 128;     // bytes per slice row
+  static constexpr int CPR = RB / 16;             // chunks per row
+  static constexpr int RPC = 1024 / RB;           // rows per 1 KB copy
+  static constexpr int KB = RB / (int)sizeof(T);  // vocabulary entries per slice (32)
+  static constexpr int KSTEPS = KB / 16;          // 16-wide k-steps per slice (2)
   static constexpr int NB = 256;                  // hidden columns per item
   static constexpr int ROWS = kTileCells + NB;    // slice rows: 128 dz rows, then 256 W_out rows
-  static constexpr int SLICE = ROWS * 128;        // 48 KB
+  static constexpr int SLICE = ROWS * RB;         // bf16 24 KB, fp32 48 KB
   static constexpr int NST = 3;                   // slices resident
-  static constexpr int CPW = SLICE / 1024 / 4;    // 1 KB copies per wave per slice (12)
-  static constexpr int NMFMA = kBf16 ? 8 : 64;      // MFMA instructions per k-step and wave
-  static constexpr int NVALU = kBf16 ? 2 : 1;       // other VALU per MFMA
+  static constexpr int CPW = SLICE / 1024 / 4;    // 1 KB copies per wave per slice (6 / 12)
+  static constexpr int OCC = kBf16 ? 2 : 1;       // workgroups per CU
+  static constexpr int NMFMA = kBf16 ? 8 : 64;    // MFMA instructions per k-step and wave
+  static constexpr int NVALU = kBf16 ? 2 : 1;     // other VALU per MFMA
+  static_assert(KSTEPS % 2 == 0, "slice shape");
 };
 
-// slot of 16-byte chunk c (0..7) of 128-byte row r: 16-byte fragment reads of
-// 16 consecutive rows at one chunk hit 16 distinct bank groups
-__device__ __forceinline__ int slot128(int r, int c) { return c ^ ((r >> 1) & 7); }
+// slot of 16-byte chunk c of row r of a slice with RB-byte rows: the 16-byte
+// fragment reads of 16 consecutive rows at one chunk hit distinct bank groups
+template <int RB>
+__device__ __forceinline__ int slot_of(int r, int c) {
+  return c ^ ((r / (256 / RB)) & (RB / 16 - 1));
+}
 
 // Registers that a compiler-visible load filled are "used" here, right after
 // an explicit vmcnt(0) and before the next direct copies are issued, so that
@@ -178,7 +188,7 @@ __device__ __forceinline__ int slot128(int r, int c) { return c ^ ((r >> 1) & 7)
 __device__ __forceinline__ void touch(float x) { asm volatile("" ::"v"(x)); }
 
 template <typename T>
-__global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
+__global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   using C = DhCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
   const Dims d = a.d;
@@ -190,8 +200,14 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   const T* __restrict__ G = static_cast<const T*>(a.g);
   const T* __restrict__ W = static_cast<const T*>(a.W);
   const int nnb = (H + C::NB - 1) / C::NB;
-  const int n_items = ld_const(a.tile_count) * nnb;
-  const int nk = (V + C::KB - 1) / C::KB;
+  const int n_tiles = ld_const(a.tile_count);
+  // an item is (tile, hidden block, vocabulary part): with few tiles the
+  // vocabulary is split so that the workgroups get equal shares (dh is
+  // linear in dz, so the parts' d_enc / d_pred contributions simply add)
+  const int ks = a.ksplit;
+  const int n_items = n_tiles * nnb * ks;
+  const int nk = (V + C::KB - 1) / C::KB;  // slices of the whole vocabulary
+  const int nks = nk / ks;                  // slices of one item (ks divides nk)
   // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  XCD x
   // takes the x-th of 8 contiguous runs of items, its workgroups striding
   // through the run together, so that the hidden blocks of one tile (which
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   const int xbase = xcd * per;
   const int xcount = min(per, n_items - xbase);
   const int my_items = xcount > lx ? (xcount - 1 - lx) / wpx + 1 : 0;
-  const int total = my_items * nk;  // slices in this workgroup's stream
+  const int total = my_items * nks;  // slices in this workgroup's stream
   if (total == 0) return;
   const uint32_t lbase = lds_addr(lds);
   const bool use_ep = (ld_const(a.hdr + 1) & kFlagEpBad) == 0;
@@ -213,14 +229,16 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
     int b, t0, u0, n0, Tl, Ul;
   };
   struct ItemRef {
-    int tile, nb, tix;
+    int tile, nb, tix, kp;
   };
   auto item_ref = [&](int i) {  // i-th item of this workgroup
     const int item = xbase + lx + i * wpx;
     ItemRef r;
-    r.tix = item / nnb;
+    r.kp = item % ks;  // vocabulary part, then hidden block, then tile
+    const int tn = item / ks;
+    r.tix = tn / nnb;
+    r.nb = tn % nnb;
     r.tile = ld_const(a.tiles + r.tix);
-    r.nb = item % nnb;
     return r;
   };
   auto decode = [&](ItemRef r) {
@@ -236,52 +254,57 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   };
 
   // Direct copies of one slice: copy q of wave w fills slice rows
-  // 8 (CPW w + q) .. +7; lane l takes row 8 (CPW w + q) + l/8 and LDS slot
-  // l%8, holding 16-byte chunk slot128(row, l%8).  Rows below 128 are dz
+  // RPC (CPW w + q) .. +RPC-1; lane l takes row RPC (CPW w + q) + l/CPR and LDS
+  // slot l%CPR, holding 16-byte chunk slot_of(row, l%CPR).  Rows below 128 are dz
   // rows of the tile (cells outside the lattice read the tile's first cell,
   // which is always inside; their results are never used), the rest W_out
-  // rows n0 + r - 128 (clamped to H - 1).  The row + chunk source of every
-  // copy is set once per item; a slice only adds its vocabulary offset.
-  // Chunks past V (last slice, V not a multiple of KB) are clamped to the
-  // row's last chunk; their fragments are zeroed before the MFMAs.
-  // dz rows: offsets (elements) from the item's first cell row; W_out rows:
-  // offsets from W_out.  Both fit 32 bits (a tile spans 16 frames of one
-  // chunk; W_out is at most 768 rows).
+  // rows n0 + r - 128 (clamped to H - 1).  Each copy's source is formed from
+  // the item's (uniform) coordinates as it is issued, so no per-copy offsets
+  // occupy registers between slices.  Chunks past V (last slice, V not a
+  // multiple of KB) are clamped to the row's last chunk; their fragments are
+  // zeroed before the MFMAs.  Element offsets fit 32 bits (a tile spans 16
+  // frames of one chunk; W_out is at most 768 rows).
+  // (Two workgroups per CU leave no registers for per-copy offsets: there
+  // they are formed at issue time from the item's uniform coordinates; with
+  // one per CU they are set once per item.)
+  const int lr = lane / C::CPR, lcc = lane % C::CPR;
   const T* gbase = G;
-  uint32_t coff[C::CPW];
+  Item src_it = {};
+  int src_k0 = 0;  // first vocabulary entry of the issuing item's part
+  uint32_t coff[C::OCC == 1 ? C::CPW : 1];
+  auto copy_off = [&](int q, int k0) -> uint32_t {  // element offset of copy q
+    const int ins = C::CPW * w + q;  // uniform
+    const int r = C::RPC * ins + lr;
+    const int col = min(k0 + slot_of<C::RB>(r, lcc) * C::CE, V - C::CE);
+    if (ins < kTileCells / C::RPC) {  // dz rows of the tile
+      int dt = r >> 3, du = r & 7;
+      const bool ok = src_it.t0 + dt < src_it.Tl && src_it.u0 + du <= src_it.Ul;
+      dt = ok ? dt : 0;
+      du = ok ? du : 0;
+      return (uint32_t)((dt * a.CU + du) * V + col);
+    }
+    const int n = min(src_it.n0 + r - kTileCells, H - 1);
+    return (uint32_t)(n * V + col);
+  };
   auto set_sources = [&](ItemRef ref) {
-    const Item it = decode(ref);
-    gbase = G + (((size_t)it.b * a.CT + (it.t0 - a.ct0)) * a.CU + (it.u0 - a.cu0)) * V;
+    src_it = decode(ref);
+    src_k0 = ref.kp * nks * C::KB;
+    gbase = G + (((size_t)src_it.b * a.CT + (src_it.t0 - a.ct0)) * a.CU + (src_it.u0 - a.cu0)) * V;
+    if constexpr (C::OCC == 1) {
 #pragma unroll
-    for (int q = 0; q < C::CPW; ++q) {
-      const int ins = C::CPW * w + q;
-      const int r = 8 * ins + (lane >> 3);
-      const int c = slot128(r, lane & 7);
-      if (ins < kTileCells / 8) {  // uniform: the first 16 copies hold dz rows
-        int dt = r >> 3, du = r & 7;
-        const bool ok = it.t0 + dt < it.Tl && it.u0 + du <= it.Ul;
-        dt = ok ? dt : 0;
-        du = ok ? du : 0;
-        coff[q] = (uint32_t)((dt * a.CU + du) * V + c * C::CE);
-      } else {
-        const int n = min(it.n0 + r - kTileCells, H - 1);
-        coff[q] = (uint32_t)(n * V + c * C::CE);
-      }
+      for (int q = 0; q < C::CPW; ++q) coff[q] = copy_off(q, 0);
     }
   };
   auto issue = [&](int s, int buf) {
-    const int k0 = s * C::KB;
+    const int k0 = src_k0 + s * C::KB;
     const uint32_t st = lbase + buf * C::SLICE + C::CPW * w * 1024;
     const bool tail = k0 + C::KB > V;
 #pragma unroll
     for (int q = 0; q < C::CPW; ++q) {
-      const T* base = (C::CPW * w + q < kTileCells / 8) ? gbase : W;
-      uint32_t off = coff[q] + k0;
-      if (tail) {  // chunks past V re-read the row's last chunk
-        const int r = 8 * (C::CPW * w + q) + (lane >> 3);
-        const int c = slot128(r, lane & 7);
-        if (k0 + c * C::CE + C::CE > V) off = coff[q] - c * C::CE + (V - C::CE);
-      }
+      const T* base = (C::CPW * w + q < kTileCells / C::RPC) ? gbase : W;
+      uint32_t off;
+      if constexpr (C::OCC == 1) off = tail ? copy_off(q, k0) : coff[q] + (uint32_t)k0;
+      else off = copy_off(q, k0);
       dma16(base + off, st + q * 1024);
     }
   };
@@ -300,30 +323,30 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   const bool has_vtail = V % C::KB != 0;
   auto rd = [&](int g, int kk, int fbuf) {
     const char* sl = lds + (g % C::NST) * C::SLICE;
-    const int s = g % nk;
-    const bool vtail = has_vtail && s == nk - 1;  // uniform
+    const int s = g % nks;  // slice of the item (ks == 1 whenever V has a tail)
+    const bool vtail = has_vtail && s == nks - 1;  // uniform
     const int kbase = s * C::KB + 16 * kk + 8 * kh;  // this lane's first k
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 64 * wm + 32 * i + lc;
-      const char* row = sl + r * 128;
+      const char* row = sl + r * C::RB;
       if constexpr (C::kBf16) {
-        fa[fbuf][i].v = *reinterpret_cast<const u32x4*>(row + (slot128(r, 2 * kk + kh) << 4));
+        fa[fbuf][i].v = *reinterpret_cast<const u32x4*>(row + (slot_of<C::RB>(r, 2 * kk + kh) << 4));
       } else {
-        fa[fbuf][i].lo = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh) << 4));
-        fa[fbuf][i].hi = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh + 1) << 4));
+        fa[fbuf][i].lo = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh) << 4));
+        fa[fbuf][i].hi = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh + 1) << 4));
       }
       if (vtail && kbase >= V) zero_frag(fa[fbuf][i]);  // vocabulary tail
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = kTileCells + 128 * wn + 32 * j + lc;
-      const char* row = sl + r * 128;
+      const char* row = sl + r * C::RB;
       if constexpr (C::kBf16) {
-        fb[fbuf][j].v = *reinterpret_cast<const u32x4*>(row + (slot128(r, 2 * kk + kh) << 4));
+        fb[fbuf][j].v = *reinterpret_cast<const u32x4*>(row + (slot_of<C::RB>(r, 2 * kk + kh) << 4));
       } else {
-        fb[fbuf][j].lo = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh) << 4));
-        fb[fbuf][j].hi = *reinterpret_cast<const f32x4*>(row + (slot128(r, 4 * kk + 2 * kh + 1) << 4));
+        fb[fbuf][j].lo = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh) << 4));
+        fb[fbuf][j].hi = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh + 1) << 4));
       }
     }
   };
@@ -427,7 +450,7 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   auto issue_next = [&]() {  // copy slice iss_g into buffer iss_g % NST
     issue(iss_s, iss_g % C::NST);
     ++iss_g;
-    if (++iss_s == nk) {
+    if (++iss_s == nks) {
       iss_s = 0;
       if (++iss_i < my_items) {
         set_sources(iss_next);
@@ -461,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
         // landed (g+2 may still be in flight), this wave's reads of slice g
         // are done, and after the barrier every wave's are: refill that
         // buffer with slice g+3
-        if (last) {
+        if (C::OCC == 1 && last) {
           wait_vm<0>();
 #pragma unroll
           for (int i = 0; i < 2; ++i)
@@ -489,12 +512,15 @@ __global__ __launch_bounds__(256, 1) void dh_kernel(DhArgs a) {
   // items outside, their slices inside: the accumulators stay in the MFMA
   // registers through the slice loop and are only read by the epilogue
   for (int li = 0; li < my_items; ++li) {
-    for (int s = 0; s < nk; ++s) {
-      const bool last = s == nk - 1;
-      // during an item's last slice its epilogue inputs load
-      if (last) load_ep(decode(cur));
-      slice(li * nk + s, last);
+    for (int s = 0; s < nks; ++s) {
+      const bool last = s == nks - 1;
+      // one workgroup per CU: the epilogue inputs load during an item's last
+      // slice; two per CU: they load after it (the other workgroup's MFMAs
+      // cover the wait, and the registers stay free during the slices)
+      if (C::OCC == 1 && last) load_ep(decode(cur));
+      slice(li * nks + s, last);
     }
+    if constexpr (C::OCC > 1) load_ep(decode(cur));
     epilogue(decode(cur));
     cur = cur_next;
     if (li + 2 < my_items) cur_next = item_ref(li + 2);
@@ -521,17 +547,20 @@ struct DwCfg {
   static constexpr int E = sizeof(T);
   static constexpr int CE = 16 / E;                    // elements per 16-byte granule
   static constexpr int BM = 128, BN = 256;
-  static constexpr int KB = kBf16 ? 64 : 32;           // cells per slice
-  static constexpr int KSTEPS = KB / 16;               // 4 / 2
+  static constexpr int KB = 32;                        // cells per slice
+  static constexpr int KSTEPS = KB / 16;               // 2
   static constexpr int SPT = kTileCells / KB;          // slices per tile
   static constexpr int ROWA = BM * E, ROWB = BN * E;   // bytes per cell row
   static constexpr int GA = ROWA / 16, GB = ROWB / 16; // granules per row
-  static constexpr int SA = KB * ROWA, SB = KB * ROWB; // 16 KB, 32 KB
+  static constexpr int SA = KB * ROWA, SB = KB * ROWB; // bf16 8 + 16 KB, fp32 16 + 32 KB
   static constexpr int CA = SA / 1024, CB = SB / 1024; // 1 KB copies per part
-  static constexpr int QPW = (CA + CB) / 4;            // row copies per wave per slice (12)
+  static constexpr int QPW = (CA + CB) / 4;            // row copies per wave per slice (6 / 12)
   static constexpr int SLICE = SA + SB;
   static constexpr int NST = 3;
   static constexpr int NMFMA = kBf16 ? 8 : 64;         // MFMA instructions per k-step and wave
+  // bf16: two workgroups per CU (72 KB of LDS each, two waves per SIMD) so
+  // that one workgroup's fragment reads and copies overlap the other's MFMAs
+  static constexpr int OCC = kBf16 ? 2 : 1;
   static_assert(KSTEPS % 2 == 0 && (CA + CB) % 4 == 0, "slice shape");
 };
 
@@ -540,7 +569,7 @@ struct DwCfg {
 __device__ __forceinline__ int swz_dw(int r) { return (4 * (r & 3)) ^ (8 * ((r >> 3) & 1)); }
 
 template <typename T>
-__global__ __launch_bounds__(256, 1) void dw_kernel(DwArgs a) {
+__global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
   using C = DwCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
   const Dims d = a.d;
@@ -835,14 +864,25 @@ hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, int max_t
 
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) {
   const int nnb = (a.d.H + DhCfg<float>::NB - 1) / DhCfg<float>::NB;
-  const long long items = (long long)max_tiles * nnb;
+  const int kb = bf16 ? DhCfg<uint16_t>::KB : DhCfg<float>::KB;
+  const int nk = (a.d.V + kb - 1) / kb;
+  // resident workgroups (a multiple of 8: one per XCD in turn)
+  const int gmax = max(8, (device_cu_count() * (bf16 ? DhCfg<uint16_t>::OCC : DhCfg<float>::OCC)) & ~7);
+  // split the vocabulary of each (tile, hidden block) until every resident
+  // workgroup gets at least three items (judged from the list capacity),
+  // keeping at least 32 slices per part (the per-item overhead)
+  DhArgs b = a;
+  b.ksplit = 1;
+  if (a.d.V % kb == 0)
+    while (b.ksplit < 4 && nk % (2 * b.ksplit) == 0 && nk / (2 * b.ksplit) >= 32 &&
+           (long long)max_tiles * nnb * b.ksplit < 3LL * gmax)
+      b.ksplit *= 2;
+  const long long items = (long long)max_tiles * nnb * b.ksplit;
   if (items <= 0) return hipSuccess;
-  // a multiple of 8 workgroups (one per XCD in turn), at most one per CU
-  const int ncu = max(8, device_cu_count() & ~7);
   const long long g8 = (items + 7) / 8 * 8;
-  dim3 grid((unsigned)(g8 < ncu ? g8 : ncu)), block(256);
-  if (bf16) hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, a);
-  else hipLaunchKernelGGL(dh_kernel<float>, grid, block, 0, st, a);
+  dim3 grid((unsigned)(g8 < gmax ? g8 : gmax)), block(256);
+  if (bf16) hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, b);
+  else hipLaunchKernelGGL(dh_kernel<float>, grid, block, 0, st, b);
   return hipGetLastError();
 }
 

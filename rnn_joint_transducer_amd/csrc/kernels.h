@@ -122,6 +122,7 @@ struct DhArgs {
   const int32_t* tile_count;
   const float* gcost;         // [B] or null
   int ct0, cu0, CT, CU;
+  int ksplit;                 // vocabulary parts per (tile, hidden block); divides the slice count
   float* d_enc;
   float* d_pred;
 };
