@@ -32,7 +32,7 @@ struct Plan {
   size_t elem;
   // saved layout (byte offsets)
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
-      o_cs, o_tiles, o_tcount, o_z;
+      o_tiles, o_tcount, o_z;
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
   size_t o_ws_db, o_ws_g, o_ws_h, o_ws_tiles, o_ws_tcount;  // backward workspace layout
@@ -87,7 +87,6 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_beta = o;   o = align_up(o + 8 * (cells + 512));
   q.o_E = o;      o = align_up(o + 4 * (size_t)B * T * H);
   q.o_P = o;      o = align_up(o + 4 * (size_t)B * (U + 1) * H);
-  q.o_cs = o;     o = align_up(o + 4 * (size_t)V);
   q.cap_all = B * (q.d.Tpad / kTileT) * (q.d.U1pad / kTileU);
   q.o_tiles = o;  o = align_up(o + 4 * (size_t)q.cap_all);
   q.o_tcount = o; o = align_up(o + 16);
@@ -241,12 +240,8 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
   float* Eexp = at<float>(saved, p.o_E);
   float* Pexp = at<float>(saved, p.o_P);
   if ((e = timed("prep", st, [&] {
-         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Eexp, Pexp,
-                            at<float>(saved, p.o_cs), status, st);
+         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Wt, Eexp, Pexp, status, st);
        })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-  if ((e = timed("transpose", st, [&] { return launch_transpose(W_out, Wt, H, V, p.bf16, st); })) !=
-      hipSuccess)
     return RNNTJ_ERR_HIP;
 
   int32_t* tiles = at<int32_t>(saved, p.o_tiles);
@@ -325,11 +320,8 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
 
   hipError_t e;
   if ((e = timed("zero", st, [&] {
-         hipError_t r = launch_zero(d_enc, (size_t)B * T * H, st);
-         if (r == hipSuccess) r = launch_zero(d_pred, (size_t)B * (U + 1) * H, st);
-         if (r == hipSuccess) r = launch_zero(d_W_out, (size_t)H * V, st);
-         if (r == hipSuccess) r = launch_zero(db64, 2 * (size_t)V, st);
-         return r;
+         return launch_zero4(d_enc, (size_t)B * T * H, d_pred, (size_t)B * (U + 1) * H, d_W_out,
+                             (size_t)H * V, db64, 2 * (size_t)V, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
 

@@ -78,19 +78,18 @@ hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
                            int32_t* Ueff, int32_t* status, hipStream_t st);
 
-// Eexp = e^{2 enc}, Pexp = e^{2 pred} (float32), hdr[1] |= kFlagEpBad if some
-// finite |enc| or |pred| exceeds 40; hdr[2] = max_v sum_k |W[k,v]| + |b[v]|.
-// colsum [V] is float scratch (zeroed here).
+// One launch: Wt[V, H] = W_out transposed; Eexp = e^{2 enc}, Pexp = e^{2 pred}
+// (float32), hdr[1] |= kFlagEpBad if some finite |enc| or |pred| exceeds 40;
+// hdr[2] = max(hdr[2], bits of max_v sum_k |W[k,v]| + |b[v]|), hdr[2] zero on entry.
 hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
-                       bool bf16, const Dims& d, float* Eexp, float* Pexp, float* colsum,
+                       bool bf16, const Dims& d, void* Wt, float* Eexp, float* Pexp,
                        int32_t* hdr, hipStream_t st);
 
-// dst[V, H] = transpose(src[H, V])
-hipError_t launch_transpose(const void* src, void* dst, int H, int V, bool bf16,
-                            hipStream_t st);
-
-// Fill n floats / int32s with zero (a kernel, never a memset node).
+// Fill n floats / int32s with zero (a kernel, never a memset node); the
+// four-buffer form zeroes up to four (null pointers skipped) in one launch.
 hipError_t launch_zero(void* p, size_t n_words, hipStream_t st);
+hipError_t launch_zero4(void* p0, size_t n0, void* p1, size_t n1, void* p2, size_t n2, void* p3,
+                        size_t n3, hipStream_t st);
 
 // Alpha / beta recursion over the anti-diagonals; costs[b] = -logP.
 hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,

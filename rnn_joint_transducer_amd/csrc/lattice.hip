@@ -236,33 +236,77 @@ __global__ void validate_kernel(const int32_t* __restrict__ T_lens,
   }
 }
 
+// Forward preparation in one launch, three independent jobs by block range:
+//   [0, n_tr)            W_out^T, 32 x 32 tiles through LDS;
+//   [n_tr, n_tr + n_cb)  the logit bound: for 64 columns v, |b[v]| + sum_k |W[k,v]|,
+//                        whose maximum goes to hdr[2] as float bits (non-negative
+//                        floats order like their bit patterns; a NaN sum, its sign
+//                        bit cleared by fabsf, wins the integer max and disables
+//                        the bound); hdr[2] starts at 0;
+//   [n_tr + n_cb, ...)   e^{2x} of every enc and pred element (accurate expf) and
+//                        the flag that some finite |x| exceeds 40, where e^{2x}
+//                        alone could overflow although enc + pred is moderate.
 template <typename E>
-__global__ void transpose_kernel(const E* __restrict__ src, E* __restrict__ dst, int H, int V) {
-  __shared__ E tile[32][33];
-  const int v0 = blockIdx.x * 32, h0 = blockIdx.y * 32;
-  const int tx = threadIdx.x, ty = threadIdx.y;  // 32 x 8
-  for (int i = ty; i < 32; i += 8) {
-    const int h = h0 + i, v = v0 + tx;
-    if (h < H && v < V) tile[i][tx] = src[(size_t)h * V + v];
+__global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ enc,
+                                                   const E* __restrict__ pred,
+                                                   const E* __restrict__ W,
+                                                   const E* __restrict__ bias, Dims d,
+                                                   E* __restrict__ Wt, float* __restrict__ Eexp,
+                                                   float* __restrict__ Pexp,
+                                                   int32_t* __restrict__ hdr, int n_tr, int n_cb) {
+  __shared__ float sh[32 * 33];
+  const int tid = threadIdx.x;
+  const int H = d.H, V = d.V;
+  int blk = blockIdx.x;
+  if (blk < n_tr) {
+    E* tile = reinterpret_cast<E*>(sh);  // [32][33]
+    const int gx = (V + 31) / 32;
+    const int v0 = (blk % gx) * 32, h0 = (blk / gx) * 32;
+    const int tx = tid & 31, ty = tid >> 5;  // 32 x 8
+    for (int i = ty; i < 32; i += 8) {
+      const int h = h0 + i, v = v0 + tx;
+      if (h < H && v < V) tile[i * 33 + tx] = W[(size_t)h * V + v];
+    }
+    __syncthreads();
+    for (int i = ty; i < 32; i += 8) {
+      const int v = v0 + i, h = h0 + tx;
+      if (v < V && h < H) Wt[(size_t)v * H + h] = tile[tx * 33 + i];
+    }
+    return;
   }
-  __syncthreads();
-  for (int i = ty; i < 32; i += 8) {
-    const int v = v0 + i, h = h0 + tx;
-    if (v < V && h < H) dst[(size_t)v * H + h] = tile[tx][i];
+  blk -= n_tr;
+  if (blk < n_cb) {
+    const int c = tid & 63, g = tid >> 6;
+    const int v = blk * 64 + c;
+    float s = 0.f;
+    if (v < V) {
+      // rows g, g+4, ...: eight independent loads in flight per step
+      float p[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int k = g;
+      for (; k + 28 < H; k += 32) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) p[i] += fabsf(ElemTraits<E>::to_f32(W[(size_t)(k + 4 * i) * V + v]));
+      }
+      for (; k < H; k += 4) p[0] += fabsf(ElemTraits<E>::to_f32(W[(size_t)k * V + v]));
+      s = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+    }
+    sh[g * 64 + c] = s;
+    __syncthreads();
+    if (g == 0) {
+      int m = 0;
+      if (v < V)
+        m = __float_as_int(sh[c] + sh[64 + c] + sh[128 + c] + sh[192 + c] +
+                           fabsf(ElemTraits<E>::to_f32(bias[v])));
+      for (int off = 32; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off));
+      if (c == 0) atomicMax(&hdr[2], m);
+    }
+    return;
   }
-}
-
-// e^{2x} of every enc and pred element (accurate expf), and the flag that
-// some finite |x| exceeds 40, where e^{2x} alone could overflow although the
-// joint's sum enc + pred is moderate.
-template <typename E>
-__global__ void ep_kernel(const E* __restrict__ enc, const E* __restrict__ pred, Dims d,
-                          float* __restrict__ Eexp, float* __restrict__ Pexp,
-                          int32_t* __restrict__ hdr) {
-  const size_t ne = (size_t)d.B * d.T * d.H, np = (size_t)d.B * d.U1 * d.H;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  blk -= n_cb;
+  const size_t ne = (size_t)d.B * d.T * H, np = (size_t)d.B * d.U1 * H;
+  const size_t stride = (size_t)(gridDim.x - n_tr - n_cb) * blockDim.x;
   bool bad = false;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < ne + np; i += stride) {
+  for (size_t i = (size_t)blk * blockDim.x + tid; i < ne + np; i += stride) {
     const float x = i < ne ? ElemTraits<E>::to_f32(enc[i]) : ElemTraits<E>::to_f32(pred[i - ne]);
     const float ax = fabsf(x);
     if (ax > 40.0f && ax != __builtin_inff()) bad = true;
@@ -273,47 +317,6 @@ __global__ void ep_kernel(const E* __restrict__ enc, const E* __restrict__ pred,
       Pexp[i - ne] = e;
   }
   if (bad) atomicOr(&hdr[1], kFlagEpBad);
-}
-
-// colsum[v] += sum over 64 hidden rows of |W[k,v]| (one 64 x 64 block per
-// workgroup: 4 row groups of 16, coalesced 64-column rows)
-template <typename E>
-__global__ void colsum_kernel(const E* __restrict__ W, Dims d, float* __restrict__ colsum) {
-  __shared__ float part[4][64];
-  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
-  const int v = blockIdx.x * 64 + c, k0 = blockIdx.y * 64 + 16 * g;
-  float s = 0.f;
-  if (v < d.V) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int k = k0 + i;
-      if (k < d.H) s += fabsf(ElemTraits<E>::to_f32(W[(size_t)k * d.V + v]));
-    }
-  }
-  part[g][c] = s;
-  __syncthreads();
-  if (g == 0 && v < d.V) atomicAdd(&colsum[v], part[0][c] + part[1][c] + part[2][c] + part[3][c]);
-}
-
-// hdr[2] = max_v (|b[v]| + colsum[v]) as float bits: non-negative floats
-// order like their bit patterns, and a NaN column sum wins the integer max
-// and disables the bound.
-template <typename E>
-__global__ void colbound_kernel(const float* __restrict__ colsum, const E* __restrict__ bias,
-                                Dims d, int32_t* __restrict__ hdr) {
-  __shared__ int red[256];
-  int m = 0;
-  for (int v = threadIdx.x; v < d.V; v += 256) {
-    const float s = colsum[v] + fabsf(ElemTraits<E>::to_f32(bias[v]));
-    m = max(m, __float_as_int(s));
-  }
-  red[threadIdx.x] = m;
-  __syncthreads();
-  for (int o = 128; o > 0; o >>= 1) {
-    if (threadIdx.x < o) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + o]);
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) hdr[2] = red[0];
 }
 
 // One workgroup per lattice chunk: per-utterance active-tile counts, their
@@ -343,9 +346,17 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
   if (threadIdx.x == 0) count[c] = s_base;
 }
 
-__global__ void zero_kernel(uint32_t* __restrict__ p, size_t n) {
+// Zeroes up to four buffers (32-bit words) in one launch.
+struct ZeroList {
+  uint32_t* p[4];
+  size_t n[4];
+};
+__global__ void zero_kernel(ZeroList z) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0u;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < z.n[k]; i += stride)
+      z.p[k][i] = 0u;
 }
 
 }  // namespace
@@ -394,53 +405,42 @@ hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
   return hipGetLastError();
 }
 
-hipError_t launch_transpose(const void* src, void* dst, int H, int V, bool bf16,
-                            hipStream_t st) {
-  dim3 grid((V + 31) / 32, (H + 31) / 32), block(32, 8);
-  if (bf16)
-    hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, block, 0, st,
-                       static_cast<const uint16_t*>(src), static_cast<uint16_t*>(dst), H, V);
-  else
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, block, 0, st,
-                       static_cast<const float*>(src), static_cast<float*>(dst), H, V);
-  return hipGetLastError();
-}
-
 hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
-                       bool bf16, const Dims& d, float* Eexp, float* Pexp, float* colsum,
+                       bool bf16, const Dims& d, void* Wt, float* Eexp, float* Pexp,
                        int32_t* hdr, hipStream_t st) {
   const size_t n = (size_t)d.B * (d.T + d.U1) * d.H;
-  size_t blocks = (n + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  const dim3 gs((d.V + 63) / 64, (d.H + 63) / 64);
-  hipError_t e = launch_zero(colsum, (size_t)d.V, st);
-  if (e != hipSuccess) return e;
-  if (bf16) {
-    hipLaunchKernelGGL(ep_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const uint16_t*>(enc), static_cast<const uint16_t*>(pred), d,
-                       Eexp, Pexp, hdr);
-    hipLaunchKernelGGL(colsum_kernel<uint16_t>, gs, dim3(256), 0, st,
-                       static_cast<const uint16_t*>(W), d, colsum);
-    hipLaunchKernelGGL(colbound_kernel<uint16_t>, dim3(1), dim3(256), 0, st, colsum,
-                       static_cast<const uint16_t*>(bias), d, hdr);
-  } else {
-    hipLaunchKernelGGL(ep_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, st,
-                       static_cast<const float*>(enc), static_cast<const float*>(pred), d, Eexp,
-                       Pexp, hdr);
-    hipLaunchKernelGGL(colsum_kernel<float>, gs, dim3(256), 0, st, static_cast<const float*>(W),
-                       d, colsum);
-    hipLaunchKernelGGL(colbound_kernel<float>, dim3(1), dim3(256), 0, st, colsum,
-                       static_cast<const float*>(bias), d, hdr);
-  }
+  size_t n_ep = (n + 255) / 256;
+  if (n_ep > 8192) n_ep = 8192;
+  const int n_tr = ((d.V + 31) / 32) * ((d.H + 31) / 32), n_cb = (d.V + 63) / 64;
+  const dim3 grid((unsigned)(n_tr + n_cb + n_ep)), block(256);
+  if (bf16)
+    hipLaunchKernelGGL(prep_kernel<uint16_t>, grid, block, 0, st, static_cast<const uint16_t*>(enc),
+                       static_cast<const uint16_t*>(pred), static_cast<const uint16_t*>(W),
+                       static_cast<const uint16_t*>(bias), d, static_cast<uint16_t*>(Wt), Eexp, Pexp,
+                       hdr, n_tr, n_cb);
+  else
+    hipLaunchKernelGGL(prep_kernel<float>, grid, block, 0, st, static_cast<const float*>(enc),
+                       static_cast<const float*>(pred), static_cast<const float*>(W),
+                       static_cast<const float*>(bias), d, static_cast<float*>(Wt), Eexp, Pexp, hdr,
+                       n_tr, n_cb);
   return hipGetLastError();
 }
 
 hipError_t launch_zero(void* p, size_t n_words, hipStream_t st) {
-  if (n_words == 0) return hipSuccess;
-  size_t blocks = (n_words + 255) / 256;
+  return launch_zero4(p, n_words, nullptr, 0, nullptr, 0, nullptr, 0, st);
+}
+
+hipError_t launch_zero4(void* p0, size_t n0, void* p1, size_t n1, void* p2, size_t n2, void* p3,
+                        size_t n3, hipStream_t st) {
+  ZeroList z = {{static_cast<uint32_t*>(p0), static_cast<uint32_t*>(p1), static_cast<uint32_t*>(p2),
+                 static_cast<uint32_t*>(p3)},
+                {p0 ? n0 : 0, p1 ? n1 : 0, p2 ? n2 : 0, p3 ? n3 : 0}};
+  size_t most = 0;
+  for (int k = 0; k < 4; ++k) most = z.n[k] > most ? z.n[k] : most;
+  if (most == 0) return hipSuccess;
+  size_t blocks = (most + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
-                     static_cast<uint32_t*>(p), n_words);
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, z);
   return hipGetLastError();
 }
 
