@@ -408,12 +408,13 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   // tiled: one lattice chunk of CT frames x CU label positions at a time.
   // The logit-gradient kernel splits the vocabulary tiles of each cell tile
   // over several workgroups when a chunk alone has too few cell tiles to
-  // give every compute unit (256 on gfx950) about four of them.
+  // give every compute unit (256 on gfx950) about four of them, as long as
+  // each part keeps at least 8 vocabulary tiles: every part rebuilds the
+  // tile's h rows and posteriors, which shorter parts do not amortise.
   const int chunk_tiles = p.cap_chunk;
   const int nvt = (V + kVocabTile - 1) / kVocabTile;
   int vsplit = 1;
-  while (vsplit < nvt && chunk_tiles * vsplit < 1024) vsplit *= 2;
-  if (vsplit > nvt) vsplit = nvt;
+  while (chunk_tiles * vsplit < 1024 && nvt / (2 * vsplit) >= 8) vsplit *= 2;
   int32_t* ctiles = at<int32_t>(workspace, p.o_ws_tiles);
   int32_t* ccount = at<int32_t>(workspace, p.o_ws_tcount);
   if ((e = timed("tile_list", st, [&] {

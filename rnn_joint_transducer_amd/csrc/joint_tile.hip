@@ -308,6 +308,12 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
     const int u = u0 + 4 * kh + j;
     lab[j] = (u < Ul) ? a.labels[(size_t)b * d.U + u] : -1;
   }
+  // kGrad: label of tile row lc (u = u0 + lc % 8), for the one-hot terms
+  int lab_row = -1;
+  if constexpr (MODE == kGrad) {
+    const int u = u0 + (lc & 7);
+    lab_row = (u < Ul) ? a.labels[(size_t)b * d.U + u] : -1;
+  }
 
   float gc = 1.0f;
   float cst[16];  // kGrad: per-row exponent offsets
@@ -514,12 +520,11 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
           // one-hot terms: lane lc of the first half fixes row lc
           if (kh == 0) {
             const int rowi = w * 32 + lc;
-            const int u = u0 + (lc & 7);
             if (d.blank >= vt && d.blank < vt + kVocabTile) {
               uint16_t* p = &ts[ts_idx(d.blank - vt, lc)];
               *p = f32_to_bf16_hw(bf16_to_f32(*p) - row_b[rowi]);
             }
-            const int y = (u < Ul) ? a.labels[(size_t)b * d.U + u] : -1;
+            const int y = lab_row;
             if (y >= vt && y < vt + kVocabTile) {
               uint16_t* p = &ts[ts_idx(y - vt, lc)];
               *p = f32_to_bf16_hw(bf16_to_f32(*p) - row_e[rowi]);
