@@ -18,7 +18,8 @@ Sources, all on the pages that describe the method:
   encodings are combined by a feed-forward layer into one distribution over
   the label space per (frame, label-history) pair.
 * "Daily Papers" page, abstract comparing the full-sum RNN-T criterion with the
-  maximum approximation: the criterion computed here is the full sum.
+  maximum approximation: both are computed here (``criterion="sum"``, the
+  default, or ``"max"``: the single best alignment).
 
 Every function is pinned by the tests in ``tests/test_oracle_pins.py``
 (brute-force enumeration, alpha/beta agreement, closed forms, invariants,
@@ -28,10 +29,12 @@ from .rnnt import (  # noqa: F401
     cell_scores,
     alpha_lattice,
     beta_lattice,
+    viterbi_lattice,
     posteriors,
     utterance_loss_and_grads,
     loss_and_grads,
     loss_only,
     brute_force_utterance,
     closed_form_zero_weights,
+    closed_form_zero_weights_max,
 )

@@ -1,4 +1,5 @@
-"""Float64 oracle: RNN-T joint network + full-sum transducer loss, fwd + bwd.
+"""Float64 oracle: RNN-T joint network + transducer loss (full sum over
+alignments, or its maximum approximation), fwd + bwd.
 
 TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).
 
@@ -37,6 +38,21 @@ Transition posteriors and gradient of sum_b gc_b * cost_b:
     dL/dz(t,u)[v] = gc * ((gB+gE) * softmax(z)[v] - gB*[v=blank] - gE*[v=y_u])
     dW_out += h^T dz,  db_out += dz,  dh = dz @ W_out^T,  dpre = (1 - h^2) * dh
     dEnc[t] += dpre(t,u) over u,  dPred[u] += dpre(t,u) over t
+
+Maximum approximation ("Daily Papers" page, abstract comparing the full-sum
+criterion with the maximum approximation; read here as the single best
+alignment): the sum over alignments becomes a maximum,
+
+    alpha*(t,u) = max(alpha*(t-1,u) + LB(t-1,u), alpha*(t,u-1) + LE(t,u-1))
+    logP* = alpha*(T'-1,U') + LB(T'-1,U'),   cost = -logP*
+
+the best alignment is read back from the predecessor decisions (on equal
+scores the blank predecessor (t-1,u) is taken), and the posteriors become
+that alignment's transition indicators: gB(t,u) = 1 where it takes the blank
+step out of (t,u) (including the final blank), gE(t,u) = 1 where it takes the
+label step.  The gradient is the formula above with these 0/1 posteriors
+(the cost is -sum of the path's log-probabilities; the path is constant where
+the maximum is unique).
 
 Cells outside (t < T', u <= U') do not exist: the gradients of enc rows t >= T',
 pred rows u > U' are exactly zero and labels past U' are never read.
@@ -126,6 +142,40 @@ def beta_lattice(LB, LE):
     return beta
 
 
+def viterbi_lattice(LB, LE):
+    """Maximum approximation: alpha* [T', U'+1], logP* and the best
+    alignment's transition indicators gB, gE [T', U'+1] (0/1)."""
+    T_len, Up1 = LB.shape
+    alpha = np.full((T_len, Up1), NEG_INF)
+    from_blank = np.zeros((T_len, Up1), dtype=bool)  # predecessor is (t-1, u)
+    alpha[0, 0] = 0.0
+    for d in range(1, T_len + Up1 - 1):
+        u = np.arange(max(0, d - T_len + 1), min(d, Up1 - 1) + 1)
+        t = d - u
+        from_t = np.full(u.shape, NEG_INF)
+        ok = t >= 1
+        from_t[ok] = alpha[t[ok] - 1, u[ok]] + LB[t[ok] - 1, u[ok]]
+        from_u = np.full(u.shape, NEG_INF)
+        ok = u >= 1
+        from_u[ok] = alpha[t[ok], u[ok] - 1] + LE[t[ok], u[ok] - 1]
+        pick_t = from_t >= from_u
+        alpha[t, u] = np.where(pick_t, from_t, from_u)
+        from_blank[t, u] = pick_t
+    logP = alpha[T_len - 1, Up1 - 1] + LB[T_len - 1, Up1 - 1]
+    gB = np.zeros((T_len, Up1))
+    gE = np.zeros((T_len, Up1))
+    t, u = T_len - 1, Up1 - 1
+    gB[t, u] = 1.0  # the final blank
+    while (t, u) != (0, 0):
+        if from_blank[t, u]:
+            t -= 1
+            gB[t, u] = 1.0
+        else:
+            u -= 1
+            gE[t, u] = 1.0
+    return alpha, logP, gB, gE
+
+
 def posteriors(alpha, beta, LB, LE, logP):
     """Blank and label transition posteriors gB, gE [T', U'+1]."""
     T_len, Up1 = LB.shape
@@ -140,12 +190,14 @@ def posteriors(alpha, beta, LB, LE, logP):
 
 
 def utterance_loss_and_grads(enc_b, pred_b, W, b_out, y, T_len, U_len, blank,
-                             grad_cost=1.0, want_cell_grads=False):
+                             grad_cost=1.0, want_cell_grads=False, criterion="sum"):
     """Cost and gradients of grad_cost * cost for one utterance.
 
-    Returns a dict: cost, logP, dEnc [T', H], dPred [U'+1, H], dW [H, V],
-    db [V], lse, LB, LE, alpha, beta, gB, gE and, if want_cell_grads, the
-    per-cell logit gradients dz [T', U'+1, V] (small shapes only)."""
+    criterion "sum" (full sum over alignments) or "max" (maximum
+    approximation).  Returns a dict: cost, logP, dEnc [T', H], dPred [U'+1, H],
+    dW [H, V], db [V], lse, LB, LE, alpha, beta (None for "max"), gB, gE and,
+    if want_cell_grads, the per-cell logit gradients dz [T', U'+1, V] (small
+    shapes only)."""
     enc_b = np.asarray(enc_b, np.float64)
     pred_b = np.asarray(pred_b, np.float64)
     W = np.asarray(W, np.float64)
@@ -154,9 +206,14 @@ def utterance_loss_and_grads(enc_b, pred_b, W, b_out, y, T_len, U_len, blank,
     H, V = W.shape
     Up1 = U_len + 1
     lse, LB, LE = cell_scores(enc_b, pred_b, W, b_out, y, T_len, U_len, blank)
-    alpha, logP = alpha_lattice(LB, LE)
-    beta = beta_lattice(LB, LE)
-    gB, gE = posteriors(alpha, beta, LB, LE, logP)
+    if criterion == "max":
+        alpha, logP, gB, gE = viterbi_lattice(LB, LE)
+        beta = None
+    else:
+        assert criterion == "sum", criterion
+        alpha, logP = alpha_lattice(LB, LE)
+        beta = beta_lattice(LB, LE)
+        gB, gE = posteriors(alpha, beta, LB, LE, logP)
     dEnc = np.zeros((T_len, H))
     dPred = np.zeros((Up1, H))
     dW = np.zeros((H, V))
@@ -183,19 +240,19 @@ def utterance_loss_and_grads(enc_b, pred_b, W, b_out, y, T_len, U_len, blank,
 
 
 def _utt_job(args):
-    (enc_b, pred_b, W, b_out, y, T_len, U_len, blank, gc, threads) = args
+    (enc_b, pred_b, W, b_out, y, T_len, U_len, blank, gc, threads, criterion) = args
     try:
         from threadpoolctl import threadpool_limits
         with threadpool_limits(limits=threads):
             return utterance_loss_and_grads(enc_b, pred_b, W, b_out, y, T_len,
-                                            U_len, blank, gc)
+                                            U_len, blank, gc, criterion=criterion)
     except ImportError:  # pragma: no cover
         return utterance_loss_and_grads(enc_b, pred_b, W, b_out, y, T_len, U_len,
-                                        blank, gc)
+                                        blank, gc, criterion=criterion)
 
 
 def loss_and_grads(enc, pred, W, b_out, labels, T_lens, U_lens, blank,
-                   grad_costs=None, workers=1, keep_cells=False):
+                   grad_costs=None, workers=1, keep_cells=False, criterion="sum"):
     """Batched costs [B] and gradients (dEnc [B,T,H], dPred [B,U+1,H],
     dW [H,V], db [V]), float64.  ``workers`` > 1 runs utterances in a
     process pool.  With keep_cells the per-utterance dicts are returned too."""
@@ -210,14 +267,14 @@ def loss_and_grads(enc, pred, W, b_out, labels, T_lens, U_lens, blank,
     threads = max(1, (os.cpu_count() or 1) // max(1, workers))
     for b in range(B):
         jobs.append((enc[b], pred[b], W, b_out, np.asarray(labels[b]),
-                     int(T_lens[b]), int(U_lens[b]), blank, gcs[b], threads))
+                     int(T_lens[b]), int(U_lens[b]), blank, gcs[b], threads, criterion))
     if workers > 1 and B > 1:
         # spawn, never fork: the caller may have initialised a GPU runtime
         ctx = multiprocessing.get_context("spawn")
         with ProcessPoolExecutor(max_workers=min(workers, B), mp_context=ctx) as ex:
             outs = list(ex.map(_utt_job, jobs))
     else:
-        outs = [utterance_loss_and_grads(*j[:9]) for j in jobs]
+        outs = [utterance_loss_and_grads(*j[:9], criterion=criterion) for j in jobs]
     costs = np.array([o["cost"] for o in outs])
     dEnc = np.zeros((B, T, H))
     dPred = np.zeros((B, pred.shape[1], H))
@@ -234,23 +291,27 @@ def loss_and_grads(enc, pred, W, b_out, labels, T_lens, U_lens, blank,
     return res
 
 
-def loss_only(enc, pred, W, b_out, labels, T_lens, U_lens, blank):
+def loss_only(enc, pred, W, b_out, labels, T_lens, U_lens, blank, criterion="sum"):
     """Costs [B] only (forward scores + alpha recursion)."""
     out = []
     for b in range(len(T_lens)):
         _, LB, LE = cell_scores(enc[b], pred[b], W, b_out, np.asarray(labels[b]),
                                 int(T_lens[b]), int(U_lens[b]), blank)
-        _, logP = alpha_lattice(LB, LE)
+        if criterion == "max":
+            _, logP, _, _ = viterbi_lattice(LB, LE)
+        else:
+            _, logP = alpha_lattice(LB, LE)
         out.append(-logP)
     return np.array(out)
 
 
-def brute_force_utterance(LB, LE):
+def brute_force_utterance(LB, LE, criterion="sum"):
     """Enumerate every alignment of one utterance (small T', U' only).
 
-    Returns logP = log of the summed path probabilities and the posteriors
+    "sum": logP = log of the summed path probabilities and the posteriors
     gB, gE obtained by adding up the probability of every path that takes each
-    transition."""
+    transition.  "max": logP = the largest path log-probability and gB, gE the
+    transitions of that path (the first one enumerated on a tie)."""
     T_len, Up1 = LB.shape
     U_len = Up1 - 1
     n_moves = T_len - 1 + U_len          # moves before the final blank
@@ -277,9 +338,13 @@ def brute_force_utterance(LB, LE):
         paths.append(steps)
     logws = np.array(logws)
     m = logws.max()
-    logP = m + math.log(np.sum(np.exp(logws - m)))
     gB = np.zeros((T_len, Up1))
     gE = np.zeros((T_len, Up1))
+    if criterion == "max":
+        for kind, t, u in paths[int(np.argmax(logws))]:
+            (gB if kind == "B" else gE)[t, u] = 1.0
+        return m, gB, gE, len(paths)
+    logP = m + math.log(np.sum(np.exp(logws - m)))
     for lw, steps in zip(logws, paths):
         w = math.exp(lw - logP)
         for kind, t, u in steps:
@@ -299,3 +364,11 @@ def closed_form_zero_weights(T_len, U_len, y, b_out, blank):
     n_paths = math.comb(T_len + U_len - 1, U_len)
     return -(T_len * logp[blank] + sum(logp[int(k)] for k in y[:U_len])
              + math.log(n_paths))
+
+
+def closed_form_zero_weights_max(T_len, U_len, y, b_out, blank):
+    """Maximum-approximation cost when W_out = 0: all alignments have the same
+    probability, so the best one is any of them."""
+    b_out = np.asarray(b_out, np.float64)
+    logp = b_out - (b_out.max() + math.log(np.sum(np.exp(b_out - b_out.max()))))
+    return -(T_len * logp[blank] + sum(logp[int(k)] for k in y[:U_len]))

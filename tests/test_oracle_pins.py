@@ -329,3 +329,143 @@ def test_pool_matches_serial():
                               inp.T_lens, inp.U_lens, 0, workers=3)
     for k in ("costs", "dEnc", "dPred", "dW", "db"):
         np.testing.assert_allclose(a[k], b[k], rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------- maximum approximation
+#
+# The maximum approximation ("Daily Papers" page, abstract comparing the
+# full-sum criterion with it) keeps only the best alignment.  Its pins do not
+# use the oracle's recursion: brute-force maximum over every alignment, the
+# bounds that relate it to the full sum, a lattice whose alignments all tie
+# exactly (pins the tie rule and the read-back of the path), the closed form
+# for W_out = 0, and finite differences.
+
+def _max_margin(LB, LE):
+    """Gap between the best and second-best alignment scores (brute force)."""
+    T_len, Up1 = LB.shape
+    n_moves = T_len - 1 + Up1 - 1
+    scores = []
+    import itertools
+    for slots in itertools.combinations(range(n_moves), Up1 - 1):
+        s = set(slots)
+        t = u = 0
+        lw = 0.0
+        for k in range(n_moves):
+            if k in s:
+                lw += LE[t, u]
+                u += 1
+            else:
+                lw += LB[t, u]
+                t += 1
+        scores.append(lw + LB[t, u])
+    scores = np.sort(np.array(scores))
+    return scores[-1] - scores[-2] if len(scores) > 1 else np.inf
+
+
+def test_max_brute_force_tiny_config():
+    inp = make_config("tiny")
+    for b in range(inp.B):
+        o = _utt(inp, b, criterion="max")
+        logP, gB, gE, n = rnnt.brute_force_utterance(o["LB"], o["LE"], criterion="max")
+        assert n == 42504
+        assert _max_margin(o["LB"], o["LE"]) > 1e-9  # the best alignment is unique
+        assert abs(o["logP"] - logP) <= 1e-12 * abs(logP)
+        np.testing.assert_array_equal(o["gB"], gB)
+        np.testing.assert_array_equal(o["gE"], gE)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_max_brute_force_random_small(seed):
+    rng = np.random.default_rng(200 + seed)
+    T = int(rng.integers(1, 7))
+    U = int(rng.integers(0, 6))
+    inp = make_inputs(1, T, U, 5, 7, sigma=0.8, seed=50 + seed)
+    o = _utt(inp, 0, criterion="max")
+    logP, gB, gE, _ = rnnt.brute_force_utterance(o["LB"], o["LE"], criterion="max")
+    assert _max_margin(o["LB"], o["LE"]) > 1e-9
+    assert abs(o["logP"] - logP) <= 1e-12 * max(1.0, abs(logP))
+    np.testing.assert_array_equal(o["gB"], gB)
+    np.testing.assert_array_equal(o["gE"], gE)
+
+
+@pytest.mark.parametrize("name", ["tiny", "short"])
+def test_max_bounds_and_path_counts(name):
+    """cost_sum <= cost_max <= cost_sum + log(#alignments); the best alignment
+    takes T' blanks and U' labels, one outgoing step per visited cell."""
+    inp = make_config(name)
+    for b in range(min(inp.B, 3)):
+        T_len, U_len = int(inp.T_lens[b]), int(inp.U_lens[b])
+        s = _utt(inp, b)
+        m = _utt(inp, b, criterion="max")
+        n_paths = math.comb(T_len + U_len - 1, U_len)
+        assert s["cost"] <= m["cost"] + 1e-9
+        assert m["cost"] <= s["cost"] + math.log(n_paths) + 1e-9
+        assert m["gB"].sum() == T_len and m["gE"].sum() == U_len
+        assert np.all(m["gB"] + m["gE"] <= 1.0)
+        # the steps chain from (0,0) to the final blank at (T'-1, U')
+        t = u = 0
+        for _ in range(T_len + U_len):
+            if m["gB"][t, u]:
+                if (t, u) == (T_len - 1, U_len):
+                    break
+                t += 1
+            else:
+                assert m["gE"][t, u]
+                u += 1
+        assert (t, u) == (T_len - 1, U_len)
+
+
+def test_max_exact_ties_take_blank_predecessor():
+    """LB = -1, LE = -2 everywhere: every alignment scores exactly
+    -(T' + 2 U'), and taking the blank predecessor on each tie reads back the
+    alignment that emits all labels in frame 0."""
+    T_len, U_len = 5, 3
+    LB = np.full((T_len, U_len + 1), -1.0)
+    LE = np.full((T_len, U_len), -2.0)
+    _, logP, gB, gE = rnnt.viterbi_lattice(LB, LE)
+    assert logP == -(T_len + 2 * U_len)
+    want_gB = np.zeros((T_len, U_len + 1))
+    want_gB[:, U_len] = 1.0
+    want_gE = np.zeros((T_len, U_len + 1))
+    want_gE[0, :U_len] = 1.0
+    np.testing.assert_array_equal(gB, want_gB)
+    np.testing.assert_array_equal(gE, want_gE)
+
+
+@pytest.mark.parametrize("name", ["tiny", "short"])
+def test_max_zero_weights_closed_form(name):
+    inp = make_config(name)
+    inp.W_f64 = np.zeros_like(inp.W_f64)
+    c = rnnt.loss_only(inp.enc_f64, inp.pred_f64, inp.W_f64, inp.b_f64, inp.labels,
+                       inp.T_lens, inp.U_lens, inp.blank, criterion="max")
+    for b in range(inp.B):
+        want = oracle.closed_form_zero_weights_max(int(inp.T_lens[b]), int(inp.U_lens[b]),
+                                                   inp.labels[b], inp.b_f64, inp.blank)
+        assert abs(c[b] - want) <= 1e-10 * abs(want)
+
+
+def test_max_finite_differences_tiny():
+    inp = make_inputs(2, 5, 3, 6, 7, sigma=0.5, seed=9, t_range=(3, 5), u_range=(1, 3))
+    gc = np.array([1.0, -0.6])
+
+    def total(enc, pred, W, bo):
+        c = rnnt.loss_only(enc, pred, W, bo, inp.labels, inp.T_lens, inp.U_lens, 0,
+                           criterion="max")
+        return float(np.dot(gc, c))
+
+    res = oracle.loss_and_grads(inp.enc_f64, inp.pred_f64, inp.W_f64, inp.b_f64,
+                                inp.labels, inp.T_lens, inp.U_lens, 0, grad_costs=gc,
+                                criterion="max")
+    base = [inp.enc_f64.copy(), inp.pred_f64.copy(), inp.W_f64.copy(), inp.b_f64.copy()]
+    grads = [res["dEnc"], res["dPred"], res["dW"], res["db"]]
+    eps = 1e-6
+    for k in range(4):
+        it = np.nditer(base[k], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            args_p = [a.copy() for a in base]
+            args_m = [a.copy() for a in base]
+            args_p[k][idx] += eps
+            args_m[k][idx] -= eps
+            fd = (total(*args_p) - total(*args_m)) / (2 * eps)
+            assert abs(fd - grads[k][idx]) <= 1e-7 + 1e-6 * abs(fd), (k, idx, fd, grads[k][idx])
