@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="short",
                     choices=["tiny", "short", "medium", "medium_lv", "long"])
+    ap.add_argument("--criterion", default="sum", choices=["sum", "max"],
+                    help="full sum over alignments, or the best alignment only")
     ap.add_argument("--tile-t", type=int, default=None)
     ap.add_argument("--tile-u", type=int, default=None)
     ap.add_argument("--tile-v", type=int, default=None)
@@ -69,7 +71,7 @@ def kernel_source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(workload, kernel, mode):
+def measured_traffic(workload, kernel, mode, criterion="sum"):
     """HBM bytes per launch recorded in profiles/traffic.json by rocprofv3
     FETCH_SIZE / WRITE_SIZE passes (scaled by the copy calibration), or None
     when no entry exists or the kernel sources changed since it was taken."""
@@ -81,7 +83,8 @@ def measured_traffic(workload, kernel, mode):
     digest = kernel_source_digest()
     for e in entries:
         if (e.get("workload") == workload and e.get("kernel") == kernel
-                and e.get("mode") == mode and e.get("source_sha256") == digest):
+                and e.get("mode") == mode and e.get("criterion", "sum") == criterion
+                and e.get("source_sha256") == digest):
             return e.get("bytes_per_launch")
     return None
 
@@ -96,7 +99,7 @@ def calibrate_copy(nbytes):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 5}))
 
 
-def cpu_baseline(inp, target_s):
+def cpu_baseline(inp, target_s, criterion="sum"):
     """Float64 oracle (fwd+bwd, one utterance at a time, NumPy BLAS on all host
     threads) on a bounded sample of the workload: whole utterances in order
     until about target_s seconds are spent, or the first utterance cut to its
@@ -115,7 +118,7 @@ def cpu_baseline(inp, target_s):
         t0 = time.perf_counter()
         rnnt.utterance_loss_and_grads(inp.enc_f64[b, :t_s], inp.pred_f64[b], inp.W_f64,
                                       inp.b_f64, inp.labels[b], t_s, int(inp.U_lens[b]),
-                                      inp.blank)
+                                      inp.blank, criterion=criterion)
         return time.perf_counter() - t0
 
     Tl0, Ul0 = int(inp.T_lens[0]), int(inp.U_lens[0])
@@ -194,7 +197,7 @@ def main():
 
     def step():
         rj.rnnt_joint_loss_fwd(**tensors, tile_t=tt, tile_u=tu, tile_v=tv, costs=costs,
-                               saved=saved)
+                               saved=saved, criterion=args.criterion)
         rj.rnnt_joint_loss_bwd(**tensors, saved=saved, tile_t=tt, tile_u=tu, tile_v=tv,
                                workspace=ws, out=grads)
 
@@ -259,10 +262,10 @@ def main():
                 "algorithmic_per_launch": per_launch}
 
     mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
-    roof["traffic"] = measured_traffic(args.workload, dom, mode)
+    roof["traffic"] = measured_traffic(args.workload, dom, mode, args.criterion)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds)
+        cpu = cpu_baseline(inp, args.cpu_seconds, args.criterion)
 
     line = {
         "metric": METRIC, "value": value, "unit": "cells/s", "n_gpus": 1,
@@ -270,7 +273,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "T": T, "U": U, "H": H, "V": V,
-                   "mode": mode, "tile_t": tt, "tile_u": tu, "tile_v": tv,
+                   "mode": mode, "criterion": args.criterion, "tile_t": tt, "tile_u": tu, "tile_v": tv,
                    "valid_cells": valid, "valid_cells_per_s": valid / (ms / 1e3),
                    "peak_gb": round(peak_gb, 3), "peak_gb_above_inputs": round(extra_gb, 3)},
         "roofline": roof,

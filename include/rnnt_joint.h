@@ -71,6 +71,16 @@ extern "C" {
 
 enum rnntj_dtype { RNNTJ_F32 = 0, RNNTJ_BF16 = 1 };
 
+/* Training criterion ("Daily Papers" page, abstract comparing the full-sum
+ * RNN-T criterion with the maximum approximation):
+ *   RNNTJ_CRIT_SUM  cost = -log of the probability summed over all alignments;
+ *   RNNTJ_CRIT_MAX  cost = -log of the probability of the best alignment
+ *                   (ties between a cell's two predecessors go to the blank
+ *                   step (t-1,u) -> (t,u)); gradients flow through that
+ *                   alignment only (its transitions' posteriors are 1, all
+ *                   others 0). */
+enum rnntj_criterion { RNNTJ_CRIT_SUM = 0, RNNTJ_CRIT_MAX = 1 };
+
 enum rnntj_status {
   RNNTJ_OK = 0,
   RNNTJ_ERR_ARG = 1,          /* null pointer, non-positive size, blank out of range */
@@ -131,6 +141,21 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out,
                         int U, int H, int V, int blank, int tile_t, int tile_u,
                         int tile_v, float* costs, void* saved, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/*
+ * Forward with a choice of criterion (rnntj_criterion; rnnt_joint_loss_fwd is
+ * this with RNNTJ_CRIT_SUM).  The criterion is recorded in `saved`, and the
+ * backward from that state follows it: with RNNTJ_CRIT_MAX the alpha pass is
+ * the max-plus recursion and the best alignment is read back into `saved`.
+ * Buffer sizes are the same for both criteria.  An unknown criterion returns
+ * RNNTJ_ERR_ARG before anything is enqueued.
+ */
+int rnnt_joint_loss_fwd_ex(const void* enc, const void* pred, const void* W_out,
+                           const void* b_out, int dtype, const int32_t* labels,
+                           const int32_t* T_lens, const int32_t* U_lens, int B, int T,
+                           int U, int H, int V, int blank, int tile_t, int tile_u,
+                           int tile_v, int criterion, float* costs, void* saved,
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Backward: overwrites d_enc [B,T,H], d_pred [B,U+1,H], d_W_out [H,V] and

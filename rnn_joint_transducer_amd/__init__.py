@@ -82,9 +82,16 @@ def _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens):
     return B, T, U, H, V
 
 
+CRITERIA = {"sum": 0, "max": 1}  # rnntj_criterion
+
+
 def rnnt_joint_loss_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, tile_t=0,
-                        tile_u=0, tile_v=0, costs=None, saved=None):
-    """Costs [B] (float32) and the uint8 `saved` state for the backward."""
+                        tile_u=0, tile_v=0, costs=None, saved=None, criterion="sum"):
+    """Costs [B] (float32) and the uint8 `saved` state for the backward.
+    criterion: "sum" (full sum over alignments) or "max" (best alignment);
+    the backward follows the criterion recorded in `saved`."""
+    if criterion not in CRITERIA:
+        raise ValueError(f"criterion must be one of {sorted(CRITERIA)}, not {criterion!r}")
     import torch
     B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
     dc = _dtype_code(enc)
@@ -95,11 +102,11 @@ def rnnt_joint_loss_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0
         raise ValueError(f"saved buffer too small ({saved.numel()} < {nbytes})")
     if costs is None:
         costs = torch.empty(B, dtype=torch.float32, device=enc.device)
-    rc = load().rnnt_joint_loss_fwd(_ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out), dc,
-                                    _ptr(labels), _ptr(T_lens), _ptr(U_lens), B, T, U, H, V,
-                                    blank, tile_t, tile_u, tile_v, _ptr(costs), _ptr(saved),
-                                    None, 0, _stream(enc.device))
-    check(rc, "rnnt_joint_loss_fwd")
+    rc = load().rnnt_joint_loss_fwd_ex(_ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out), dc,
+                                       _ptr(labels), _ptr(T_lens), _ptr(U_lens), B, T, U, H, V,
+                                       blank, tile_t, tile_u, tile_v, CRITERIA[criterion],
+                                       _ptr(costs), _ptr(saved), None, 0, _stream(enc.device))
+    check(rc, "rnnt_joint_loss_fwd_ex")
     return costs, saved
 
 
@@ -150,9 +157,9 @@ def _make_function():
     class _RNNTJointLoss(torch.autograd.Function):
         @staticmethod
         def forward(ctx, enc, pred, W_out, b_out, labels, T_lens, U_lens, blank, tile_t, tile_u,
-                    tile_v):
+                    tile_v, criterion):
             costs, saved = rnnt_joint_loss_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens,
-                                               blank, tile_t, tile_u, tile_v)
+                                               blank, tile_t, tile_u, tile_v, criterion=criterion)
             ctx.save_for_backward(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved)
             ctx.cfg = (blank, tile_t, tile_u, tile_v)
             ctx.consumed = False
@@ -173,7 +180,7 @@ def _make_function():
                 enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, blank, tile_t, tile_u,
                 tile_v, grad_costs=grad_costs.float().contiguous())
             return (d_enc.to(enc.dtype), d_pred.to(pred.dtype), d_W.to(W_out.dtype),
-                    d_b.to(b_out.dtype), None, None, None, None, None, None, None)
+                    d_b.to(b_out.dtype), None, None, None, None, None, None, None, None)
 
     return _RNNTJointLoss
 
@@ -182,7 +189,7 @@ _FN = None
 
 
 def rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, tile_t=0,
-                    tile_u=0, tile_v=0):
+                    tile_u=0, tile_v=0, criterion="sum"):
     """Per-utterance costs [B] with autograd support.  In the untiled mode the
     backward consumes the forward's stored logits (one backward per forward);
     in a tiled mode the saved state is only read, so a graph kept with
@@ -191,4 +198,4 @@ def rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, ti
     if _FN is None:
         _FN = _make_function()
     return _FN.apply(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank, tile_t, tile_u,
-                     tile_v)
+                     tile_v, criterion)

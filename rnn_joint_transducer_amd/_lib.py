@@ -28,6 +28,8 @@ _SIG = {
     "rnnt_joint_loss_workspace_bytes": (_c_int, [_c_int] * 10 + [ctypes.POINTER(_c_size)]),
     "rnnt_joint_loss_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 9
                             + [_vp, _vp, _vp, _c_size, _vp]),
+    "rnnt_joint_loss_fwd_ex": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 10
+                               + [_vp, _vp, _vp, _c_size, _vp]),
     "rnnt_joint_loss_bwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp] + [_c_int] * 9
                             + [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "rnnt_joint_loss_status": (_c_int, [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]),

@@ -205,10 +205,23 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
                         const int32_t* U_lens, int B, int T, int U, int H, int V, int blank,
                         int tile_t, int tile_u, int tile_v, float* costs, void* saved,
                         void* workspace, size_t workspace_bytes, void* stream) {
+  return rnnt_joint_loss_fwd_ex(enc, pred, W_out, b_out, dtype, labels, T_lens, U_lens, B, T, U,
+                                H, V, blank, tile_t, tile_u, tile_v, RNNTJ_CRIT_SUM, costs, saved,
+                                workspace, workspace_bytes, stream);
+}
+
+int rnnt_joint_loss_fwd_ex(const void* enc, const void* pred, const void* W_out,
+                           const void* b_out, int dtype, const int32_t* labels,
+                           const int32_t* T_lens, const int32_t* U_lens, int B, int T, int U,
+                           int H, int V, int blank, int tile_t, int tile_u, int tile_v,
+                           int criterion, float* costs, void* saved, void* workspace,
+                           size_t workspace_bytes, void* stream) {
   (void)workspace;
   Plan p;
   int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
+  if (criterion != RNNTJ_CRIT_SUM && criterion != RNNTJ_CRIT_MAX) return RNNTJ_ERR_ARG;
+  const int crit = criterion == RNNTJ_CRIT_MAX ? kCritMax : kCritSum;
   if (!enc || !pred || !W_out || !b_out || !T_lens || !U_lens || !costs || !saved)
     return RNNTJ_ERR_ARG;
   if (U > 0 && !labels) return RNNTJ_ERR_ARG;
@@ -234,7 +247,7 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
   if ((e = timed("zero", st, [&] { return launch_zero(status, 4, st); })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   if ((e = timed("validate", st, [&] {
-         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, st);
+         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, crit, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   float* Eexp = at<float>(saved, p.o_E);
@@ -281,8 +294,12 @@ int rnnt_joint_loss_fwd(const void* enc, const void* pred, const void* W_out, co
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   if ((e = timed("lattice", st, [&] {
-         return launch_lattice(LB, LE, Teff, Ueff, p.d, alpha, beta, logP, costs, st);
+         return launch_lattice(LB, LE, Teff, Ueff, p.d, alpha, beta, logP, costs, crit, st);
        })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  if (crit == kCritMax &&
+      (e = timed("backtrace", st, [&] { return launch_backtrace(Teff, Ueff, p.d, beta, st); })) !=
+          hipSuccess)
     return RNNTJ_ERR_HIP;
   return RNNTJ_OK;
 }

@@ -52,7 +52,7 @@ __device__ float4 cell_consts(const JointArgs& a, int b, int t, int u) {
   if (t < Tl && u <= Ul) {
     const double g = a.gcost ? (double)a.gcost[b] : 1.0;
     double gB, gE;
-    cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE);
+    cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE, a.hdr[3]);
     const double m = (gB + gE) * fabs(g);
     const double lse = (double)a.lse[skew_idx(d, b, t, u)];
     o.x = m > 0.0 ? (float)((lse - log(m)) * 1.4426950408889634) : kInf;

@@ -23,6 +23,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // Cell tile of the joint kernels: 16 frames x 8 label positions = 128 cells,
 // processed by 4 waves that own 4 frames x 8 label positions (32 rows) each.
+// Training criterion of a forward (word 3 of the state header): the full sum
+// over alignments, or its maximum approximation (the best alignment).
+constexpr int kCritSum = 0, kCritMax = 1;
+
 constexpr int kTileT = 16;
 constexpr int kTileU = 8;
 constexpr int kTileCells = kTileT * kTileU;
@@ -250,13 +254,24 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 //   gB(t,u) = exp(alpha(t,u) + LB(t,u) + beta(t+1,u) - logP)  (t < T'-1)
 //   gB(T'-1,U') = exp(alpha + LB - logP),  gB(T'-1,u<U') = 0
 //   gE(t,u) = exp(alpha(t,u) + LE(t,u) + beta(t,u+1) - logP)  (u < U'), else 0
+// Maximum approximation: the lattice pass leaves in `beta` the marks of the
+// best alignment's steps (kPathBlank / kPathLabel on the cell a step leaves;
+// other cells hold their predecessor decision, a positive value).
+constexpr double kPathBlank = -1.0, kPathLabel = -2.0;
+
 __device__ __forceinline__ void cell_posteriors(const Dims& d, const double* __restrict__ alpha,
                                                 const double* __restrict__ beta,
                                                 const float* __restrict__ LB,
                                                 const float* __restrict__ LE, double logP,
                                                 int b, int t, int u, int Tl, int Ul,
-                                                double& gB, double& gE) {
+                                                double& gB, double& gE, int crit) {
   const size_t ix = skew_idx(d, b, t, u);
+  if (crit == kCritMax) {  // 0/1 indicators of the best alignment's steps
+    const double m = beta[ix];
+    gB = m == kPathBlank ? 1.0 : 0.0;
+    gE = m == kPathLabel ? 1.0 : 0.0;
+    return;
+  }
   const double a = alpha[ix];
   if (t < Tl - 1)
     gB = exp(a + (double)LB[ix] + beta[skew_idx(d, b, t + 1, u)] - logP);

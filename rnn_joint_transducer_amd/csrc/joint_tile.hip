@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       if (t < Tl && u <= Ul) {
         const double g = a.gcost ? (double)a.gcost[b] : 1.0;
         double gB, gE;
-        cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE);
+        cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE, a.hdr[3]);
         const double occ = gB + gE;
         const double lse = (double)a.lse[skew_idx(d, b, t, u)];
         c = occ > 0.0 ? (float)((lse - log(occ)) * 1.4426950408889634) : kInf;

@@ -73,10 +73,11 @@ hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_item
                              hipStream_t st);
 
 // Length / label validation: writes Teff/Ueff (0 / 0 for an invalid
-// utterance) and ORs a bit mask into *status.
+// utterance), ORs a bit mask into status[0] and stores the criterion
+// (kCritSum / kCritMax) in status[3].
 hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
-                           int32_t* Ueff, int32_t* status, hipStream_t st);
+                           int32_t* Ueff, int32_t* status, int crit, hipStream_t st);
 
 // One launch: Wt[V, H] = W_out transposed; Eexp = e^{2 enc}, Pexp = e^{2 pred}
 // (float32), hdr[1] |= kFlagEpBad if some finite |enc| or |pred| exceeds 40;
@@ -91,10 +92,15 @@ hipError_t launch_zero(void* p, size_t n_words, hipStream_t st);
 hipError_t launch_zero4(void* p0, size_t n0, void* p1, size_t n1, void* p2, size_t n2, void* p3,
                         size_t n3, hipStream_t st);
 
-// Alpha / beta recursion over the anti-diagonals; costs[b] = -logP.
+// Alpha / beta recursion over the anti-diagonals; costs[b] = -logP.  With
+// kCritMax: the max-plus alpha and, in beta, each cell's predecessor decision,
+// which launch_backtrace turns into the best alignment's step marks (read by
+// cell_posteriors).
 hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
                           const int32_t* Ueff, const Dims& d, double* alpha, double* beta,
-                          double* logP, float* costs, hipStream_t st);
+                          double* logP, float* costs, int crit, hipStream_t st);
+hipError_t launch_backtrace(const int32_t* Teff, const int32_t* Ueff, const Dims& d, double* beta,
+                            hipStream_t st);
 
 // Untiled backward: h rows of every cell into h [B, Tpad, U1pad, H].
 hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st);

@@ -9,6 +9,11 @@
 //   logP = alpha(T'-1,U') + LB(T'-1,U')
 //   beta(T'-1,U') = LB(T'-1,U')
 //   beta(t,u) = logaddexp(beta(t+1,u) + LB(t,u), beta(t,u+1) + LE(t,u))
+// Maximum approximation (best alignment; same abstract): alpha with max in
+// place of logaddexp, the blank predecessor taken on equal scores; the
+// predecessor decision of every cell goes to the beta array (1: blank from
+// (t-1,u), 2: label from (t,u-1)), and a read-back from (T'-1,U') then marks
+// the best alignment's steps there (kPathBlank / kPathLabel).
 //
 // One wave64 per (utterance, direction): cells of one anti-diagonal t+u are
 // independent, so the wave sweeps the T'+U' anti-diagonals with the label
@@ -57,7 +62,8 @@ __device__ __forceinline__ double wave_shl1(double v, double fill) {
 // on each anti-diagonal the u-1 (alpha) or u+1 (beta) neighbour is in the
 // same lane except at the block edge, which one DPP lane shift supplies.
 // One wave per (utterance, direction); DIR = 0 sweeps alpha forward over the
-// diagonals, DIR = 1 beta backward.  The diagonals are taken in chunks of CH:
+// diagonals, DIR = 1 beta backward, DIR = 2 the max-plus alpha (maximum
+// approximation) with its predecessor decisions.  The diagonals are taken in chunks of CH:
 // the LB / LE operands of the next chunk are loaded into registers while this
 // chunk is computed, and the chunk's results are stored at its end.  Every
 // load and store is issued unconditionally (clamped loads; results of slots
@@ -86,9 +92,11 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
   const size_t base = (size_t)b * d.DG * d.U1;
   const float* lb = LB + base;
   const float* le = LE + base;
-  double* arr = DIR == 0 ? alpha : beta;
+  double* arr = DIR == 1 ? beta : alpha;
   double* out = arr + base;
   double* trash = arr + (size_t)d.B * d.DG * d.U1 + NU * l;
+  double* dec_out = beta + base;  // DIR == 2: predecessor decisions
+  double* dec_trash = beta + (size_t)d.B * d.DG * d.U1 + NU * l;
   const int last = d.DG * d.U1 - 1;  // clamp for the loads
 
   double prev[NU];
@@ -97,15 +105,16 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
 
   // operands of step s for slot j (diagonal dg = s for alpha, nd-1-s for beta):
   //   alpha: LB(t-1,u), LE(t,u-1) on diagonal dg-1;  beta: LB(t,u), LE(t,u) on dg
+  constexpr bool kFwd = DIR != 1;
   float cb[CH][NU], ce[CH][NU], nb[CH][NU], ne[CH][NU];
   auto fetch = [&](int s0, float (&fb)[CH][NU], float (&fe)[CH][NU]) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int dg = DIR == 0 ? s0 + c - 1 : nd - 1 - s0 - c;
+      const int dg = kFwd ? s0 + c - 1 : nd - 1 - s0 - c;
 #pragma unroll
       for (int j = 0; j < NU; ++j) {
         const int u = NU * l + j;
-        int ib = dg * d.U1 + u, ie = DIR == 0 ? ib - 1 : ib;
+        int ib = dg * d.U1 + u, ie = kFwd ? ib - 1 : ib;
         ib = ib < 0 ? 0 : (ib > last ? last : ib);
         ie = ie < 0 ? 0 : (ie > last ? last : ie);
         fb[c][j] = lb[ib];
@@ -123,25 +132,34 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
     fetch(s0 + CH, fb, fe);
     __builtin_amdgcn_sched_barrier(0);
     double res[CH][NU];
+    double dec[CH][NU];  // DIR == 2 only
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int s = s0 + c;
-      const int dg = DIR == 0 ? s : nd - 1 - s;
+      const int dg = kFwd ? s : nd - 1 - s;
       // neighbour on the previous diagonal across the lane edge
       const double edge =
-          DIR == 0 ? wave_shr1(prev[NU - 1], kNegInfD) : wave_shl1(prev[0], kNegInfD);
+          kFwd ? wave_shr1(prev[NU - 1], kNegInfD) : wave_shl1(prev[0], kNegInfD);
 #pragma unroll
       for (int j = 0; j < NU; ++j) {
         const int u = NU * l + j;
         const int t = dg - u;
         const bool valid = (s < nd) & (u <= Ul) & (t >= 0) & (t < Tl);
         double v;
-        if (DIR == 0) {
+        if (DIR == 0 || DIR == 2) {
           // alpha(t-1,u) + LB(t-1,u),  alpha(t,u-1) + LE(t,u-1)
           const double nbv = j > 0 ? prev[j > 0 ? j - 1 : 0] : edge;
           const double ft = (t >= 1) ? prev[j] + (double)ub[c][j] : kNegInfD;
           const double fu = (u >= 1) ? nbv + (double)ue[c][j] : kNegInfD;
-          v = log_add_exp(ft, fu);
+          if constexpr (DIR == 0) {
+            v = log_add_exp(ft, fu);
+          } else {
+            // best predecessor, blank on equal scores; a NaN operand stays NaN
+            const bool pick_t = ft >= fu;
+            v = pick_t ? ft : fu;
+            v = (ft != ft || fu != fu) ? ft + fu : v;
+            dec[c][j] = pick_t ? 1.0 : 2.0;
+          }
           v = (dg == 0) ? 0.0 : v;
         } else {
           // beta(t+1,u) + LB(t,u),  beta(t,u+1) + LE(t,u)
@@ -156,7 +174,7 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
       // the diagonal is complete: it becomes the previous one
 #pragma unroll
       for (int j = 0; j < NU; ++j) prev[j] = res[c][j];
-      if (DIR == 0 && s == nd - 1) {
+      if (kFwd && s == nd - 1) {
         // final cell (T'-1, U') lies on the last diagonal
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
@@ -172,7 +190,7 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
       const int s = s0 + c;
-      const int dg = DIR == 0 ? s : nd - 1 - s;
+      const int dg = kFwd ? s : nd - 1 - s;
 #pragma unroll
       for (int j = 0; j < NU; ++j) {
         const int u = NU * l + j;
@@ -180,6 +198,10 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
         const bool valid = (s < nd) & (u <= Ul) & (t >= 0) & (t < Tl);
         double* dst = valid ? out + (size_t)dg * d.U1 + u : trash + j;
         *dst = res[c][j];
+        if constexpr (DIR == 2) {
+          double* dd = valid ? dec_out + (size_t)dg * d.U1 + u : dec_trash + j;
+          *dd = dec[c][j];
+        }
       }
     }
   };
@@ -193,7 +215,8 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
 }
 
 // both directions of every utterance in one launch: blockIdx.y = direction
-template <int NU, int CH>
+// (full sum); the maximum approximation runs its one forward sweep
+template <int NU, int CH, bool MAXA>
 __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ LB,
                                                      const float* __restrict__ LE,
                                                      const int32_t* __restrict__ Teff,
@@ -202,19 +225,48 @@ __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ L
                                                      double* __restrict__ beta,
                                                      double* __restrict__ logP,
                                                      float* __restrict__ costs) {
-  if (blockIdx.y == 0)
+  if constexpr (MAXA)
+    lattice_sweep<2, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
+  else if (blockIdx.y == 0)
     lattice_sweep<0, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
   else
     lattice_sweep<1, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
+}
+
+// Maximum approximation: read the best alignment back from (T'-1, U') over
+// the predecessor decisions in `beta` (one lane per utterance; the path has
+// T'+U' steps, each depending on the last) and mark each step on the cell it
+// leaves: the final blank at (T'-1, U'), then kPathBlank on (t-1,u) or
+// kPathLabel on (t,u-1).
+__global__ __launch_bounds__(64) void backtrace_kernel(const int32_t* __restrict__ Teff,
+                                                       const int32_t* __restrict__ Ueff, Dims d,
+                                                       double* __restrict__ beta) {
+  const int b = blockIdx.x * 64 + threadIdx.x;
+  if (b >= d.B) return;
+  const int Tl = Teff[b], Ul = Ueff[b];
+  if (Tl == 0) return;  // invalid utterance
+  int t = Tl - 1, u = Ul;
+  size_t ix = skew_idx(d, b, t, u);
+  double dc = beta[ix];
+  beta[ix] = kPathBlank;
+  while (t > 0 || u > 0) {
+    const bool from_blank = u == 0 || (t > 0 && dc == 1.0);
+    if (from_blank) --t;
+    else --u;
+    ix = skew_idx(d, b, t, u);
+    dc = beta[ix];
+    beta[ix] = from_blank ? kPathBlank : kPathLabel;
+  }
 }
 
 __global__ void validate_kernel(const int32_t* __restrict__ T_lens,
                                 const int32_t* __restrict__ U_lens,
                                 const int32_t* __restrict__ labels, Dims d,
                                 int32_t* __restrict__ Teff, int32_t* __restrict__ Ueff,
-                                int32_t* __restrict__ status) {
+                                int32_t* __restrict__ status, int crit) {
   __shared__ int sbad;
   const int b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) status[3] = crit;  // header word 3: the criterion
   if (threadIdx.x == 0) sbad = 0;
   __syncthreads();
   const int Tl = T_lens[b], Ul = U_lens[b];
@@ -363,15 +415,20 @@ __global__ void zero_kernel(ZeroList z) {
 
 hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
                           const int32_t* Ueff, const Dims& d, double* alpha, double* beta,
-                          double* logP, float* costs, hipStream_t st) {
+                          double* logP, float* costs, int crit, hipStream_t st) {
   const int nu = (d.U1 + 63) / 64;
-  dim3 grid(d.B, 2), block(64);
-  // chunk length: 2 loads + 1 store per slot and step stay within the
-  // 63 memory operations the wave can track
-#define RNNTJ_LAT(N, CH)                                                                 \
-  case N:                                                                                \
-    hipLaunchKernelGGL((lattice_kernel<N, CH>), grid, block, 0, st, LB, LE, Teff, Ueff, d, \
-                       alpha, beta, logP, costs);                                        \
+  const bool maxa = crit == kCritMax;
+  dim3 grid(d.B, maxa ? 1 : 2), block(64);
+  // chunk length: 2 loads + 1 store per slot and step (max: 2 stores) stay
+  // within the 63 memory operations the wave can track
+#define RNNTJ_LAT(N, CH)                                                                   \
+  case N:                                                                                  \
+    if (maxa)                                                                              \
+      hipLaunchKernelGGL((lattice_kernel<N, CH, true>), grid, block, 0, st, LB, LE, Teff,  \
+                         Ueff, d, alpha, beta, logP, costs);                               \
+    else                                                                                   \
+      hipLaunchKernelGGL((lattice_kernel<N, CH, false>), grid, block, 0, st, LB, LE, Teff, \
+                         Ueff, d, alpha, beta, logP, costs);                               \
     break;
   switch (nu) {
     RNNTJ_LAT(1, 16)
@@ -389,6 +446,13 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
   return hipGetLastError();
 }
 
+hipError_t launch_backtrace(const int32_t* Teff, const int32_t* Ueff, const Dims& d, double* beta,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(backtrace_kernel, dim3((d.B + 63) / 64), dim3(64), 0, st, Teff, Ueff, d,
+                     beta);
+  return hipGetLastError();
+}
+
 hipError_t launch_tile_list(const int32_t* Teff, const int32_t* Ueff, const Dims& d, int CT, int CU,
                             int n_chunks_u, int n_chunks, int cap, int32_t* list, int32_t* count,
                             hipStream_t st) {
@@ -399,9 +463,9 @@ hipError_t launch_tile_list(const int32_t* Teff, const int32_t* Ueff, const Dims
 
 hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
-                           int32_t* Ueff, int32_t* status, hipStream_t st) {
+                           int32_t* Ueff, int32_t* status, int crit, hipStream_t st) {
   hipLaunchKernelGGL(validate_kernel, dim3(d.B), dim3(256), 0, st, T_lens, U_lens, labels, d,
-                     Teff, Ueff, status);
+                     Teff, Ueff, status, crit);
   return hipGetLastError();
 }
 

@@ -24,12 +24,13 @@ def to_device(inp, device="cuda"):
                 labels=i32(inp.labels), T_lens=i32(inp.T_lens), U_lens=i32(inp.U_lens))
 
 
-def run_gpu(inp, tile_t=0, tile_u=0, tile_v=0, grad_costs=None, dev=None, bwd=True):
+def run_gpu(inp, tile_t=0, tile_u=0, tile_v=0, grad_costs=None, dev=None, bwd=True,
+            criterion="sum"):
     import torch
     import rnn_joint_transducer_amd as rj
     dev = dev or to_device(inp)
     costs, saved = rj.rnnt_joint_loss_fwd(**dev, blank=inp.blank, tile_t=tile_t,
-                                          tile_u=tile_u, tile_v=tile_v)
+                                          tile_u=tile_u, tile_v=tile_v, criterion=criterion)
     out = dict(costs=costs)
     if bwd:
         gc = None if grad_costs is None else torch.tensor(grad_costs, dtype=torch.float32,

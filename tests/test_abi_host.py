@@ -14,7 +14,8 @@ def test_exports_every_declared_symbol():
     names = _lib.declared_functions()
     assert set(names) == {"rnnt_joint_loss_abi_version", "rnnt_joint_loss_strerror",
                           "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
-                          "rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd", "rnnt_joint_loss_last_error",
+                          "rnnt_joint_loss_fwd", "rnnt_joint_loss_fwd_ex", "rnnt_joint_loss_bwd",
+                          "rnnt_joint_loss_last_error",
                           "rnnt_joint_loss_status", "rnnt_joint_loss_timing",
                           "rnnt_joint_loss_timing_report"}
     for n in names:
@@ -141,3 +142,13 @@ def test_timing_report_empty():
     assert _lib.timing_report() == {}
     assert lib.rnnt_joint_loss_timing(0) == 0
     assert lib.rnnt_joint_loss_timing_report(None, 0) == 1
+
+
+def test_fwd_ex_rejects_unknown_criterion():
+    """rnnt_joint_loss_fwd_ex checks the criterion on the host (nothing is
+    enqueued, so fake aligned pointers suffice)."""
+    v = lambda: ctypes.c_void_p(16 * 4096)
+    args = [v(), v(), v(), v(), 0, v(), v(), v(), 2, 10, 2, 64, 32, 0, 0, 0, 0]
+    for crit in (-1, 2, 7):
+        rc = lib.rnnt_joint_loss_fwd_ex(*args, crit, v(), v(), None, 0, None)
+        assert rc == 1, (crit, rc)

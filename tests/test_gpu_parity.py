@@ -23,10 +23,10 @@ pytestmark = pytest.mark.gpu
 WORKERS = min(16, os.cpu_count() or 1)
 
 
-def _oracle_full(inp, grad_costs=None):
+def _oracle_full(inp, grad_costs=None, criterion="sum"):
     return oracle.loss_and_grads(inp.enc_f64, inp.pred_f64, inp.W_f64, inp.b_f64, inp.labels,
                                  inp.T_lens, inp.U_lens, inp.blank, grad_costs=grad_costs,
-                                 workers=min(WORKERS, inp.B))
+                                 workers=min(WORKERS, inp.B), criterion=criterion)
 
 
 def _compare_all(inp, g, ref):
@@ -272,3 +272,68 @@ def test_zero_weights_closed_form_full_size(name):
         np.add.at(want_db, inp.labels[b, :Ul], -1.0)
     np.testing.assert_allclose(g["db"], want_db, atol=2e-2 * np.abs(want_db).max())
     assert abs(g["db"].sum()) <= 1e-3 * np.abs(want_db).max()
+
+
+# ------------------------------------------------------------------ maximum approximation
+#
+# The best-alignment criterion against the oracle's maximum-approximation
+# mode.  The inputs are continuous random draws, so the best alignment is
+# unique and both sides read back the same one.
+
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
+def test_max_tiny(tiles):
+    inp = make_config("tiny")
+    print(f"[max tiny tiles={tiles}]", flush=True)
+    g = run_gpu(inp, *tiles, grad_costs=[1.0, -0.5], criterion="max")
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp, grad_costs=[1.0, -0.5], criterion="max"))
+
+
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (64, 64, 128)])
+def test_max_short(tiles):
+    inp = make_config("short")
+    print(f"[max short tiles={tiles}]", flush=True)
+    g = run_gpu(inp, *tiles, criterion="max")
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp, criterion="max"))
+
+
+def test_max_ragged_bf16():
+    inp = make_inputs(5, 37, 11, 64, 96, sigma=0.2, seed=31, dtype="bf16",
+                      t_range=(1, 37), u_range=(0, 11))
+    print("[max ragged bf16]", flush=True)
+    g = run_gpu(inp, 16, 8, 0, criterion="max")
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp, criterion="max"))
+
+
+def test_max_medium_sampled():
+    inp = make_config("medium")
+    print("[max medium sampled]", flush=True)
+    g = run_gpu(inp, 64, 64, 0, criterion="max")
+    assert g["status"] == 0
+    utts = [4, 12]
+    refc = rnnt.loss_only(inp.enc_f64[utts], inp.pred_f64[utts], inp.W_f64, inp.b_f64,
+                          inp.labels[utts], inp.T_lens[utts], inp.U_lens[utts], 0,
+                          criterion="max")
+    check_costs(g["costs"], refc, inp.dtype, idx=utts)
+    b = 12
+    o = rnnt.utterance_loss_and_grads(inp.enc_f64[b], inp.pred_f64[b], inp.W_f64, inp.b_f64,
+                                      inp.labels[b], int(inp.T_lens[b]), int(inp.U_lens[b]),
+                                      0, criterion="max")
+    Tl, Ul = int(inp.T_lens[b]), int(inp.U_lens[b])
+    check_grad(f"d_enc[{b}]", g["dEnc"][b, :Tl], o["dEnc"], inp.dtype)
+    check_grad(f"d_pred[{b}]", g["dPred"][b, :Ul + 1], o["dPred"], inp.dtype)
+
+
+def test_max_zero_weights_closed_form_medium():
+    """W_out = 0: every alignment has the same probability, so the best one's
+    cost is -(T' log p_blank + sum_u log p_{y_u}) whatever the tie order."""
+    inp = make_config("medium")
+    inp.W = np.zeros_like(inp.W)
+    g = run_gpu(inp, 64, 64, 0, bwd=False, criterion="max")
+    assert g["status"] == 0
+    want = [oracle.closed_form_zero_weights_max(int(inp.T_lens[b]), int(inp.U_lens[b]),
+                                                inp.labels[b], inp.b_f64, inp.blank)
+            for b in range(inp.B)]
+    check_costs(g["costs"], want, inp.dtype)
