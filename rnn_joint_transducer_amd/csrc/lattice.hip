@@ -234,28 +234,132 @@ __global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ L
 }
 
 // Maximum approximation: read the best alignment back from (T'-1, U') over
-// the predecessor decisions in `beta` (one lane per utterance; the path has
-// T'+U' steps, each depending on the last) and mark each step on the cell it
-// leaves: the final blank at (T'-1, U'), then kPathBlank on (t-1,u) or
-// kPathLabel on (t,u-1).
-__global__ __launch_bounds__(64) void backtrace_kernel(const int32_t* __restrict__ Teff,
-                                                       const int32_t* __restrict__ Ueff, Dims d,
-                                                       double* __restrict__ beta) {
-  const int b = blockIdx.x * 64 + threadIdx.x;
-  if (b >= d.B) return;
+// the predecessor decisions the max-plus pass left in `beta` (1.0: the blank
+// step from (t-1,u); anything else: the label step from (t,u-1)), and mark
+// each step on the cell it leaves (kPathBlank / kPathLabel).  One workgroup
+// per utterance.  Walking back, the path enters row u at some t_hi(u) and
+// leaves it at t_lo(u), the highest t <= t_hi(u) whose decision is "label"
+// (t = 0 at the latest, where only the label step exists); row 0 runs down to
+// t = 0, and t_hi(u-1) = t_lo(u).  So the decisions are packed one bit per
+// cell into LDS, row-major in u with t as the bit index (rows S words apart,
+// S odd, so that lanes on consecutive u hit distinct banks), and a row's exit
+// is a find-last-set over its words (one wave, 64 words a probe).  Utterances
+// with more frames than fit are packed in chunks of t from the top, which
+// the walk crosses downwards once.  Each anti-diagonal n = t + u holds one
+// path cell, in the row u whose [t_lo(u) + u, t_hi(u) + u] contains n, so all
+// threads then write the marks at once.
+constexpr int kBtThreads = 512, kBtWords = 8192, kBtBatch = 16;
+
+__global__ __launch_bounds__(kBtThreads) void backtrace_kernel(const int32_t* __restrict__ Teff,
+                                                               const int32_t* __restrict__ Ueff,
+                                                               Dims d, double* __restrict__ beta) {
+  __shared__ uint32_t bits[kBtWords];
+  __shared__ int tlo[512], thi[512];
+  __shared__ int s_t, s_u, s_more;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int Tl = Teff[b], Ul = Ueff[b];
-  if (Tl == 0) return;  // invalid utterance
-  int t = Tl - 1, u = Ul;
-  size_t ix = skew_idx(d, b, t, u);
-  double dc = beta[ix];
-  beta[ix] = kPathBlank;
-  while (t > 0 || u > 0) {
-    const bool from_blank = u == 0 || (t > 0 && dc == 1.0);
-    if (from_blank) --t;
-    else --u;
-    ix = skew_idx(d, b, t, u);
-    dc = beta[ix];
-    beta[ix] = from_blank ? kPathBlank : kPathLabel;
+  if (Tl == 0) return;  // invalid utterance (uniform over the block)
+  const int R = Ul + 1;  // rows u = 0..U'
+  // W words (32 W frames) of a row per chunk, rows S = W | 1 words apart;
+  // R <= 512 gives W >= 15
+  const int W = min((Tl + 31) >> 5, kBtWords / R - 1), S = W | 1;
+  const int CT = W * 32;
+  if (tid == 0) {
+    s_t = Tl - 1;
+    s_u = Ul;
+    thi[Ul] = Tl - 1;
+  }
+  const double* ub = beta + (size_t)b * d.DG * d.U1;
+  const int q = kBtThreads / R, r = kBtThreads - q * R;
+  for (int t1 = Tl;;) {  // chunk: t in [t0, t1)
+    const int t0 = max(0, t1 - CT);
+    for (int i = tid; i < R * S; i += kBtThreads) bits[i] = 0u;
+    __syncthreads();
+    // cells of diagonals n in [t0, t1 + U'), u fastest (contiguous in the
+    // skewed layout); (no, u) = divmod(i, R) stepped by kBtThreads.  The
+    // loads of a batch are unconditional (cells outside the chunk read the
+    // utterance's first cell and are dropped), so that they are all in flight
+    // together.
+    const int nd = t1 - t0 + Ul;
+    int no = tid / R, u = tid - (tid / R) * R;
+    while (no < nd) {
+      double v[kBtBatch];
+      int word[kBtBatch];
+      uint32_t bit[kBtBatch];
+#pragma unroll
+      for (int k = 0; k < kBtBatch; ++k) {
+        const int t = t0 + no - u;
+        const bool ok = no < nd && t >= t0 && t < t1;
+        v[k] = ub[ok ? (size_t)(t + u) * d.U1 + u : 0];
+        word[k] = u * S + ((t - t0) >> 5);
+        bit[k] = ok ? 1u << ((t - t0) & 31) : 0u;
+        no += q;
+        u += r;
+        if (u >= R) {
+          u -= R;
+          ++no;
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kBtBatch; ++k)
+        if (bit[k] != 0u && v[k] != 1.0) atomicOr(&bits[word[k]], bit[k]);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      int t = s_t, uu = s_u, more = 0;
+      while (uu > 0) {
+        const uint32_t* row = bits + uu * S;
+        const int w = (t - t0) >> 5, sh = (t - t0) & 31;
+        int found = -1;
+        for (int wb = w; wb >= 0 && found < 0; wb -= 64) {
+          const int wl = wb - lane;
+          uint32_t m = 0u;
+          if (wl >= 0) {
+            m = row[wl];
+            if (wl == w && sh < 31) m &= (2u << sh) - 1u;
+          }
+          const unsigned long long bal = __ballot(m != 0u);
+          if (bal) {
+            const int L = __builtin_ctzll(bal);  // lowest lane: the highest word
+            const uint32_t mw = __shfl(m, L);
+            found = t0 + (wb - L) * 32 + (31 - __clz(mw));
+          }
+        }
+        if (found < 0) {
+          if (t0 > 0) {  // no label decision in this chunk: continue below it
+            t = t0 - 1;
+            more = 1;
+            break;
+          }
+          found = 0;
+        }
+        if (lane == 0) {
+          tlo[uu] = found;
+          thi[uu - 1] = found;
+        }
+        t = found;
+        --uu;
+      }
+      if (lane == 0) {
+        if (!more) tlo[0] = 0;
+        s_t = t;
+        s_u = uu;
+        s_more = more;
+      }
+    }
+    __syncthreads();
+    if (!s_more) break;
+    t1 = t0;
+  }
+  for (int n = tid; n < Tl + Ul; n += kBtThreads) {
+    int lo = 0, hi = Ul;  // the largest u with t_lo(u) + u <= n
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (tlo[mid] + mid <= n) lo = mid;
+      else hi = mid - 1;
+    }
+    const int t = n - lo;
+    beta[skew_idx(d, b, t, lo)] = (lo < Ul && t == thi[lo]) ? kPathLabel : kPathBlank;
   }
 }
 
@@ -448,8 +552,7 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
 
 hipError_t launch_backtrace(const int32_t* Teff, const int32_t* Ueff, const Dims& d, double* beta,
                             hipStream_t st) {
-  hipLaunchKernelGGL(backtrace_kernel, dim3((d.B + 63) / 64), dim3(64), 0, st, Teff, Ueff, d,
-                     beta);
+  hipLaunchKernelGGL(backtrace_kernel, dim3(d.B), dim3(kBtThreads), 0, st, Teff, Ueff, d, beta);
   return hipGetLastError();
 }
 

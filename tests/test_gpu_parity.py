@@ -307,6 +307,40 @@ def test_max_ragged_bf16():
     _compare_all(inp, g, _oracle_full(inp, criterion="max"))
 
 
+def test_max_long_paths_chunked():
+    """Best-alignment read-back over more frames than its packed decision bits
+    hold at once: with U'+1 = 401 rows the bits cover 640 frames, so T' = 1500
+    is read in three chunks of t; U' = 300 in two, U' = 137 in one, U' = 0 is
+    a single row.  Every output is compared.  With unit upstream gradients
+    these 1500-frame paths give |d_pred| up to ~380 and |d_b_out| ~4300, where
+    an fp32 value cannot hold a 1e-4 absolute error (half an ulp at 4300 is
+    2.4e-4); upstream gradients of at most 0.3 keep every entry below ~1300,
+    while a single wrong step on a path would still move d_enc by ~1e-2."""
+    inp = make_inputs(4, 1500, 400, 64, 32, sigma=0.1, seed=47, dtype="fp32")
+    inp.T_lens = np.array([1500, 1500, 1201, 300], dtype=np.int32)
+    inp.U_lens = np.array([400, 300, 137, 0], dtype=np.int32)
+    gcs = [0.25, -0.2, 0.25, 0.3]
+    print("[max long paths chunked]", flush=True)
+    g = run_gpu(inp, 0, 0, 0, grad_costs=gcs, criterion="max")
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp, grad_costs=gcs, criterion="max"))
+
+
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
+def test_max_exact_ties_follow_blank_first(tiles):
+    """W_out = 0 and b_out = 0: every alignment has exactly the same score, so
+    the best one is decided by the tie rule alone (the blank predecessor wins).
+    d_enc and d_pred vanish, but d_W_out = sum over the path of h (x) dz does
+    depend on which cells the path visits."""
+    inp = make_config("short")
+    inp.W = np.zeros_like(inp.W)
+    inp.W_f64 = np.zeros_like(inp.W_f64)
+    print(f"[max exact ties tiles={tiles}]", flush=True)
+    g = run_gpu(inp, *tiles, criterion="max")
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp, criterion="max"))
+
+
 def test_max_medium_sampled():
     inp = make_config("medium")
     print("[max medium sampled]", flush=True)
