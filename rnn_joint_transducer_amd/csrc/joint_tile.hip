@@ -61,7 +61,9 @@ struct StageCfg {
 
 // One W^T slice [vt .. vt+127] x [kc .. kc+BK) goes straight from global
 // memory into LDS (global_load_lds, 16 bytes per lane, 1 KB per wave
-// instruction, no staging registers): wave w writes LDS chunks
+// instruction, no staging registers; issued as `dma16`, which the compiler's
+// wait insertion does not track, so that it never holds the current slice's
+// reads back for the next slice's copy): wave w writes LDS chunks
 // (8w + q)*64 + lane, q = 0..7, i.e. slice row r = 32w + 4q + lane/16, chunk
 // slot lane%16.  Slot s of row r holds hidden chunk s ^ (r & 15): rows are
 // unpadded (the copy writes 1 KB contiguously) and the XOR keeps the
@@ -82,9 +84,7 @@ __device__ __forceinline__ void dma_slice(const T* __restrict__ Wt, int H, int V
       n = n < V ? n : V - 1;
       k = k < H ? k : H - C::CE;
     }
-    __builtin_amdgcn_global_load_lds(
-        (const __attribute__((address_space(1))) void*)(Wt + (size_t)n * H + k),
-        (__attribute__((address_space(3))) void*)(lds_slice + (8 * w + q) * 1024), 16, 0, 0);
+    dma16(Wt + (size_t)n * H + k, lds_addr(lds_slice) + (8 * w + q) * 1024);
   }
 }
 
@@ -185,10 +185,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         const char* src = (isE ? esrc : psrc) + j * 1024 + lane * 16;
         const char* lim = isE ? elim : plim;
         src = src < lim ? src : lim;
-        __builtin_amdgcn_global_load_lds(
-            (const __attribute__((address_space(1))) void*)src,
-            (__attribute__((address_space(3))) void*)(Ep + (isE ? 0 : 64 * H) + j * 1024), 16, 0,
-            0);
+        dma16(src, lds_addr(Ep) + (isE ? 0 : 64 * H) + j * 1024);
       }
     }
   };
