@@ -201,6 +201,17 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
                "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
+// As dma16, addressed as a wave-uniform base plus a per-lane 32-bit byte
+// offset (the scalar-base form of the global load): a copy pattern repeated
+// from many bases keeps its per-lane part in one register.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  const uint64_t p = reinterpret_cast<uint64_t>(sbase);
+  const uint64_t up = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff),
+               "s"(up), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
 // wait until at most N vector memory accesses of this wave are outstanding
 template <int N>
 __device__ __forceinline__ void wait_vm() {

@@ -67,24 +67,42 @@ struct StageCfg {
 // (8w + q)*64 + lane, q = 0..7, i.e. slice row r = 32w + 4q + lane/16, chunk
 // slot lane%16.  Slot s of row r holds hidden chunk s ^ (r & 15): rows are
 // unpadded (the copy writes 1 KB contiguously) and the XOR keeps the
-// fragment reads of 8 or 16 consecutive rows on distinct banks.  Outside an
-// exact shape the source row / column is clamped to valid memory; those
-// columns are masked and those k-steps skipped by the caller.
-template <typename T, bool EXACT>
-__device__ __forceinline__ void dma_slice(const T* __restrict__ Wt, int H, int V, int vt, int kc,
-                                          char* lds_slice) {
+// fragment reads of 8 or 16 consecutive rows on distinct banks.  In an exact
+// shape a copy's source is the slice origin Wt[vt][kc] (wave-uniform) plus
+// the per-lane byte offset voff[q] of row r, chunk c, the same for every
+// slice.  Otherwise the source row / column is clamped to valid memory;
+// those columns are masked and those k-steps skipped by the caller.
+template <typename T>
+__device__ __forceinline__ void slice_offsets(int H, uint32_t (&voff)[8]) {
   using C = StageCfg<T>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int r = 32 * w + 4 * q + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);
-    int n = vt + r, k = kc + c * C::CE;
-    if (!EXACT) {
+    voff[q] = (uint32_t)((r * H + c * C::CE) * (int)sizeof(T));
+  }
+}
+template <typename T, bool EXACT>
+__device__ __forceinline__ void dma_slice(const T* __restrict__ Wt, int H, int V, int vt, int kc,
+                                          const uint32_t (&voff)[8], char* lds_slice) {
+  using C = StageCfg<T>;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t lds = lds_addr(lds_slice) + 8 * w * 1024;
+  if constexpr (EXACT) {
+    const T* base = Wt + (size_t)vt * H + kc;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) dma16s(base, voff[q], lds + q * 1024);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = 32 * w + 4 * q + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);
+      int n = vt + r, k = kc + c * C::CE;
       n = n < V ? n : V - 1;
       k = k < H ? k : H - C::CE;
+      dma16(Wt + (size_t)n * H + k, lds + q * 1024);
     }
-    dma16(Wt + (size_t)n * H + k, lds_addr(lds_slice) + (8 * w + q) * 1024);
   }
 }
 
@@ -207,6 +225,18 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       }
     }
   };
+  uint32_t voff[8];
+  slice_offsets<T>(H, voff);
+  // first vocabulary tile and slice count of an item
+  auto item_range = [&](int it, int& vb, int& ns) {
+    const int r = (MODE == kGrad) ? it % vsplit : 0;
+    vb = (nvt_all * r) / vsplit;
+    ns = ((nvt_all * (r + 1)) / vsplit - vb) * nkc;
+  };
+  // the slice being computed sits in Ws1 when `par` is set; the last slice
+  // of an item starts the copy of the next item's first slice (`pre`)
+  int par = 0;
+  bool pre = false;
   if (stage_ep && (int)blockIdx.x < n_items) {
     int b, t0, u0;
     item_tile(blockIdx.x, b, t0, u0);
@@ -219,8 +249,11 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   // vocabulary tiles of this item
   const int vr = (MODE == kGrad) ? item % vsplit : 0;
-  const int vt_begin = (nvt_all * vr) / vsplit, vt_end = (nvt_all * (vr + 1)) / vsplit;
-  const int nstage = (vt_end - vt_begin) * nkc;
+  int vt_begin, nstage;
+  item_range(item, vt_begin, nstage);
+  const int vt_end = vt_begin + nstage / nkc;
+  int next_vb = 0, next_ns = 0;
+  if (item + (int)gridDim.x < n_items) item_range(item + gridDim.x, next_vb, next_ns);
   if (nstage <= 0) {  // uniform; no work, but keep the row prefetch going
     if (stage_ep && item + (int)gridDim.x < n_items) {
       wait_vmem();
@@ -232,8 +265,9 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
     continue;
   }
 
-  // ---- prologue: start the first W^T slice, build h in registers
-  dma_slice<T, EXACT>(Wt, H, V, vt_begin * kVocabTile, 0, Ws0);
+  // ---- prologue: start the first W^T slice (unless the previous item
+  // did), build h in registers
+  if (!pre) dma_slice<T, EXACT>(Wt, H, V, vt_begin * kVocabTile, 0, voff, par ? Ws1 : Ws0);
   if (stage_ep) {
     wait_vmem();  // this wave's exponential rows (and slice part) have landed
     __syncthreads();
@@ -377,12 +411,14 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
     for (int kc = 0; kc < KC_MAX; ++kc) {
       if (EXACT || kc < nkc) {
         const bool has_next = (s + 1) < nstage;
+        const bool cross = !has_next && next_ns > 0;  // the next item's first slice
         const int ns = s + 1;
-        const int nvt = (vt_begin + ns / nkc) * kVocabTile, nkc0 = (ns % nkc) * C::BK;
+        const int nvt = has_next ? (vt_begin + ns / nkc) * kVocabTile : next_vb * kVocabTile;
+        const int nkc0 = has_next ? (ns % nkc) * C::BK : 0;
         // one stage: start the copy of the next slice into `nxt`, run the
         // MFMAs of this slice from `src` (B fragments one k-step ahead)
         auto stage = [&](const char* src, char* nxt) {
-          if (has_next) dma_slice<T, EXACT>(Wt, H, V, nvt, nkc0, nxt);
+          if (has_next || cross) dma_slice<T, EXACT>(Wt, H, V, nvt, nkc0, voff, nxt);
           const char* wrow = src + lc * C::ROWB;
           // bf16: a fragment is one 16-byte chunk (2*kk + kh); fp32: two
           // chunks (4*kk + 2*kh, +1), each at its own swizzled slot
@@ -421,13 +457,14 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
             for (int blk = 0; blk < 4; ++blk) bcur[blk] = bnxt[blk];
           }
         };
-        if ((s & 1) == 0)
+        if (par == 0)
           stage(Ws0, Ws1);
         else
           stage(Ws1, Ws0);
         wait_vmem();
         __syncthreads();
         ++s;
+        par ^= 1;
       }
     }
 
@@ -587,6 +624,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       }
     }
   }
+  pre = next_ns > 0;  // the last slice started the next item's first copy
 
   if constexpr (MODE == kLse || MODE == kStoreZ) {
     // combine the per-lane partial sums of the 32 lanes that share each row
