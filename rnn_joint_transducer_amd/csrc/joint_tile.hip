@@ -49,54 +49,61 @@ namespace {
 
 constexpr float kInf = __builtin_inff();
 
-template <typename T>
+// NBLK: 32-column output blocks per wave, i.e. a vocabulary step of
+// VT = 32 NBLK columns (128 with one workgroup per compute unit; 64 with two,
+// which halves the accumulators and the slices so that two workgroups fit)
+template <typename T, int NBLK = 4>
 struct StageCfg {
   static constexpr bool kBf16 = sizeof(T) == 2;
   static constexpr int BK = kBf16 ? 128 : 64;             // hidden elements per W^T slice
   static constexpr int CE = 16 / (int)sizeof(T);          // elements per 16-byte chunk
   static constexpr int ROWB = 256;                        // bytes per slice row (16 chunks)
   static constexpr int KK = BK / 16;                      // k-steps per slice
-  static constexpr int SLICE = kVocabTile * ROWB;         // 32 KB per slice
+  static constexpr int VT = 32 * NBLK;                    // vocabulary columns per step
+  static constexpr int SLICE = VT * ROWB;                 // 32 / 16 KB per slice
+  static constexpr int CPW = VT / 16;                     // 1 KB copies per wave per slice
+  static constexpr int OCC = NBLK == 2 ? 2 : 1;           // workgroups per compute unit
 };
 
-// One W^T slice [vt .. vt+127] x [kc .. kc+BK) goes straight from global
+// One W^T slice [vt .. vt+VT) x [kc .. kc+BK) goes straight from global
 // memory into LDS (global_load_lds, 16 bytes per lane, 1 KB per wave
 // instruction, no staging registers; issued as `dma16`, which the compiler's
 // wait insertion does not track, so that it never holds the current slice's
 // reads back for the next slice's copy): wave w writes LDS chunks
-// (8w + q)*64 + lane, q = 0..7, i.e. slice row r = 32w + 4q + lane/16, chunk
-// slot lane%16.  Slot s of row r holds hidden chunk s ^ (r & 15): rows are
+// (CPW w + q)*64 + lane, q < CPW, i.e. slice row r = 4 (CPW w + q) + lane/16,
+// chunk slot lane%16.  Slot s of row r holds hidden chunk s ^ (r & 15): rows are
 // unpadded (the copy writes 1 KB contiguously) and the XOR keeps the
 // fragment reads of 8 or 16 consecutive rows on distinct banks.  In an exact
 // shape a copy's source is the slice origin Wt[vt][kc] (wave-uniform) plus
 // the per-lane byte offset voff[q] of row r, chunk c, the same for every
 // slice.  Otherwise the source row / column is clamped to valid memory;
 // those columns are masked and those k-steps skipped by the caller.
-template <typename T>
-__device__ __forceinline__ void slice_offsets(int H, uint32_t (&voff)[8]) {
-  using C = StageCfg<T>;
+template <typename T, int NBLK>
+__device__ __forceinline__ void slice_offsets(int H, uint32_t (&voff)[StageCfg<T, NBLK>::CPW]) {
+  using C = StageCfg<T, NBLK>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = 32 * w + 4 * q + (lane >> 4);
+  for (int q = 0; q < C::CPW; ++q) {
+    const int r = 4 * (C::CPW * w + q) + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);
     voff[q] = (uint32_t)((r * H + c * C::CE) * (int)sizeof(T));
   }
 }
-template <typename T, bool EXACT>
+template <typename T, int NBLK, bool EXACT>
 __device__ __forceinline__ void dma_slice(const T* __restrict__ Wt, int H, int V, int vt, int kc,
-                                          const uint32_t (&voff)[8], char* lds_slice) {
-  using C = StageCfg<T>;
+                                          const uint32_t (&voff)[StageCfg<T, NBLK>::CPW],
+                                          char* lds_slice) {
+  using C = StageCfg<T, NBLK>;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const uint32_t lds = lds_addr(lds_slice) + 8 * w * 1024;
+  const uint32_t lds = lds_addr(lds_slice) + C::CPW * w * 1024;
   if constexpr (EXACT) {
     const T* base = Wt + (size_t)vt * H + kc;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) dma16s(base, voff[q], lds + q * 1024);
+    for (int q = 0; q < C::CPW; ++q) dma16s(base, voff[q], lds + q * 1024);
   } else {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int r = 32 * w + 4 * q + (lane >> 4);
+    for (int q = 0; q < C::CPW; ++q) {
+      const int r = 4 * (C::CPW * w + q) + (lane >> 4);
       const int c = (lane & 15) ^ (r & 15);
       int n = vt + r, k = kc + c * C::CE;
       n = n < V ? n : V - 1;
@@ -109,11 +116,69 @@ __device__ __forceinline__ void dma_slice(const T* __restrict__ Wt, int H, int V
 // all of this wave's direct-to-LDS copies (and any other loads) have landed
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ float sel4(const f32x16 (&acc)[4], int blk, int r) {
+// Butterfly reduce-scatter over the 32 lanes of a row group (lanes with the
+// same lane / 32): v[r] is this lane's partial sum for accumulator row r; the
+// result is the sum over the 32 lanes for row rs_row(lane).  Each of the four
+// halving steps keeps half of the rows (by one lane bit) and adds the
+// partner's copy of them; the last step adds the two 16-lane halves.
+__device__ __forceinline__ int rs_row(int lane) {
+  return ((lane & 1) << 3) | ((lane & 2) << 1) | ((lane & 4) >> 1) | ((lane & 8) >> 3);
+}
+__device__ __forceinline__ float rs_sum16(const float (&v)[16], int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
+  float a[8], c[4], e[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (b0 ? v[i + 8] : v[i]) + __shfl_xor(b0 ? v[i] : v[i + 8], 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) c[i] = (b1 ? a[i + 4] : a[i]) + __shfl_xor(b1 ? a[i] : a[i + 4], 2);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) e[i] = (b2 ? c[i + 2] : c[i]) + __shfl_xor(b2 ? c[i] : c[i + 2], 4);
+  const float f = (b3 ? e[1] : e[0]) + __shfl_xor(b3 ? e[0] : e[1], 8);
+  return f + __shfl_xor(f, 16);
+}
+// (m, s) <- (m, s) + (m2, s2) for sums s of 2^(x - m)
+__device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s2) {
+  const float mn = fmaxf(m, m2);
+  if (mn > -kInf) {
+    s = s * exp2_fast(m - mn) + s2 * exp2_fast(m2 - mn);
+    m = mn;
+  }
+}
+// the same reduce-scatter over (max, sum) pairs
+__device__ __forceinline__ void rs_lse16(const float (&m)[16], const float (&s)[16], int lane,
+                                         float& mo, float& so) {
+  float am[8], as[8], cm[4], cs[4], em[2], es[2];
+  auto step = [&](bool hi, float km, float ks, float sm, float ss, int off, float& rm, float& rs) {
+    (void)hi;
+    const float pm = __shfl_xor(sm, off), ps = __shfl_xor(ss, off);
+    rm = km;
+    rs = ks;
+    lse2_merge(rm, rs, pm, ps);
+  };
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    step(b0, b0 ? m[i + 8] : m[i], b0 ? s[i + 8] : s[i], b0 ? m[i] : m[i + 8], b0 ? s[i] : s[i + 8],
+         1, am[i], as[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    step(b1, b1 ? am[i + 4] : am[i], b1 ? as[i + 4] : as[i], b1 ? am[i] : am[i + 4],
+         b1 ? as[i] : as[i + 4], 2, cm[i], cs[i]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    step(b2, b2 ? cm[i + 2] : cm[i], b2 ? cs[i + 2] : cs[i], b2 ? cm[i] : cm[i + 2],
+         b2 ? cs[i] : cs[i + 2], 4, em[i], es[i]);
+  float fm, fs;
+  step(b3, b3 ? em[1] : em[0], b3 ? es[1] : es[0], b3 ? em[0] : em[1], b3 ? es[0] : es[1], 8, fm, fs);
+  step(false, fm, fs, fm, fs, 16, mo, so);
+}
+
+// acc[blk][r] without dynamic register indexing
+template <int N>
+__device__ __forceinline__ float sel_blk(const f32x16 (&acc)[N], int blk, int r) {
   float v = acc[0][r];
-  v = blk == 1 ? acc[1][r] : v;
-  v = blk == 2 ? acc[2][r] : v;
-  v = blk == 3 ? acc[3][r] : v;
+#pragma unroll
+  for (int i = 1; i < N; ++i) v = blk == i ? acc[i][r] : v;
   return v;
 }
 
@@ -131,20 +196,22 @@ __device__ __forceinline__ int ts_idx(int col, int row) {
 }  // namespace
 
 // Largest hidden size whose 24 exponential rows are staged in LDS (the
-// budget left next to the W^T slices and the store staging).
-template <typename T, int KS>
+// budget left next to the W^T slices and the store staging); with two
+// workgroups per compute unit the rows are read from global memory instead.
+template <typename T, int KS, int NBLK>
 struct EpCfg {
   static constexpr int kMaxH = sizeof(T) == 2 ? 640 : 256;
-  static constexpr bool kStage = KS * 16 <= kMaxH;
+  static constexpr bool kStage = NBLK == 4 && KS * 16 <= kMaxH;
   // 16 e^{2 enc} rows then 8 e^{2 pred} rows (float32), plus one 1 KB copy
   // of slack for a partial last copy
   static constexpr int kBytes = kStage ? 96 * KS * 16 + 1024 : 16;
 };
 
-template <typename T, int KS, int MODE, bool EXACT>
-__global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
-  using C = StageCfg<T>;
-  using EP = EpCfg<T, KS>;
+template <typename T, int KS, int MODE, bool EXACT, int NBLK>
+__global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(JointArgs a) {
+  using C = StageCfg<T, NBLK>;
+  using EP = EpCfg<T, KS, NBLK>;
+  constexpr int VT = C::VT;
   constexpr bool kBf16 = C::kBf16;
   constexpr int KC_MAX = (KS * 16 + C::BK - 1) / C::BK;
   constexpr bool kStores = (MODE == kStoreZ || MODE == kGrad) && kBf16;
@@ -152,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   // copy into one does not alias the fragment reads of the other
   __shared__ __align__(16) char Ws0[C::SLICE];
   __shared__ __align__(16) char Ws1[C::SLICE];
-  __shared__ __align__(16) uint16_t Ts[kStores ? 4 : 1][kStores ? 128 * 32 : 8];
+  __shared__ __align__(16) uint16_t Ts[kStores ? 4 : 1][kStores ? VT * 32 : 8];
   __shared__ float cap_blank[kTileCells];
   __shared__ float cap_label[kTileCells];
   __shared__ float row_c[kTileCells];  // kGrad: (lse - ln occ) * log2(e)
@@ -175,7 +242,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   const bool stage_ep = EP::kStage && use_ep;
   const bool bounded = __int_as_float(a.hdr[2]) < 64.0f;  // NaN bound -> false
 
-  const int nvt_all = (V + kVocabTile - 1) / kVocabTile;
+  const int nvt_all = (V + VT - 1) / VT;
   const int vsplit = (MODE == kGrad) ? a.vsplit : 1;
   const int nkc = EXACT ? KC_MAX : (H + C::BK - 1) / C::BK;
   const int n_items = a.tile_count[0] * vsplit;
@@ -225,8 +292,8 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       }
     }
   };
-  uint32_t voff[8];
-  slice_offsets<T>(H, voff);
+  uint32_t voff[C::CPW];
+  slice_offsets<T, NBLK>(H, voff);
   // first vocabulary tile and slice count of an item
   auto item_range = [&](int it, int& vb, int& ns) {
     const int r = (MODE == kGrad) ? it % vsplit : 0;
@@ -267,7 +334,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
 
   // ---- prologue: start the first W^T slice (unless the previous item
   // did), build h in registers
-  if (!pre) dma_slice<T, EXACT>(Wt, H, V, vt_begin * kVocabTile, 0, voff, par ? Ws1 : Ws0);
+  if (!pre) dma_slice<T, NBLK, EXACT>(Wt, H, V, vt_begin * VT, 0, voff, par ? Ws1 : Ws0);
   if (stage_ep) {
     wait_vmem();  // this wave's exponential rows (and slice part) have landed
     __syncthreads();
@@ -316,6 +383,9 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         } else {
           zero_frag(hA[ks]);
         }
+        // at most four k-steps of loads in flight: h itself fills most of
+        // the registers of a two-workgroup-per-CU launch
+        if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     } else {
       build_h_direct(hA, b, tv, uv, valid);
@@ -347,7 +417,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   }
 
   float gc = 1.0f;
-  float cst[16];  // kGrad: per-row exponent offsets
+  float cst[16];  // kGrad, NBLK == 4: per-row exponent offsets (NBLK == 2 reads row_c)
   if constexpr (MODE == kGrad) {
     if (tid < kTileCells) {
       const int rw = tid >> 5, rr = tid & 31;
@@ -379,24 +449,28 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   }
   if constexpr (MODE == kGrad) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cst[r] = row_c[w * 32 + acc_row(r, kh)];
+    for (int r = 0; r < 16; ++r) cst[r] = NBLK == 4 ? row_c[w * 32 + acc_row(r, kh)] : 0.f;
   }
 
+  // running max (base 2) and sum of each row: NBLK == 4 keeps this lane's
+  // columns of its 16 rows and combines the lanes at the end; NBLK == 2 adds
+  // every vocabulary step's reduce-scatter into one row per lane (rs_row)
   float mrun[16], srun[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     mrun[r] = -kInf;
     srun[r] = 0.f;
   }
+  float mrow = -kInf, srow = 0.f;
 
   int s = 0;
   for (int vti = vt_begin; vti < vt_end; ++vti) {
-    const int vt = vti * kVocabTile;
+    const int vt = vti * VT;
     // accumulators start at the bias of their column
-    f32x16 acc[4];
-    bool cvalid[4];
+    f32x16 acc[NBLK];
+    bool cvalid[NBLK];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
+    for (int blk = 0; blk < NBLK; ++blk) {
       const int col = vt + blk * 32 + lc;
       cvalid[blk] = EXACT || col < V;
       const float bc = cvalid[blk] ? ElemTraits<T>::to_f32(bias[col]) : 0.f;
@@ -413,12 +487,12 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         const bool has_next = (s + 1) < nstage;
         const bool cross = !has_next && next_ns > 0;  // the next item's first slice
         const int ns = s + 1;
-        const int nvt = has_next ? (vt_begin + ns / nkc) * kVocabTile : next_vb * kVocabTile;
+        const int nvt = has_next ? (vt_begin + ns / nkc) * VT : next_vb * VT;
         const int nkc0 = has_next ? (ns % nkc) * C::BK : 0;
         // one stage: start the copy of the next slice into `nxt`, run the
         // MFMAs of this slice from `src` (B fragments one k-step ahead)
         auto stage = [&](const char* src, char* nxt) {
-          if (has_next || cross) dma_slice<T, EXACT>(Wt, H, V, nvt, nkc0, voff, nxt);
+          if (has_next || cross) dma_slice<T, NBLK, EXACT>(Wt, H, V, nvt, nkc0, voff, nxt);
           const char* wrow = src + lc * C::ROWB;
           // bf16: a fragment is one 16-byte chunk (2*kk + kh); fp32: two
           // chunks (4*kk + 2*kh, +1), each at its own swizzled slot
@@ -433,9 +507,9 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
             }
             return f;
           };
-          Frag8<T> bcur[4], bnxt[4];
+          Frag8<T> bcur[NBLK], bnxt[NBLK];
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk) bcur[blk] = bfrag(blk, 0);
+          for (int blk = 0; blk < NBLK; ++blk) bcur[blk] = bfrag(blk, 0);
 #pragma unroll
           for (int kk = 0; kk < C::KK; ++kk) {
             const int ks = kc * C::KK + kk;
@@ -443,18 +517,18 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
             const bool nlive = kk + 1 < C::KK && ks + 1 < KS && (EXACT || ks + 1 < nks);
             if (nlive) {
 #pragma unroll
-              for (int blk = 0; blk < 4; ++blk) bnxt[blk] = bfrag(blk, kk + 1);
+              for (int blk = 0; blk < NBLK; ++blk) bnxt[blk] = bfrag(blk, kk + 1);
             }
             // keep the reads for k-step kk+1 issued ahead of this k-step's MFMAs
             __builtin_amdgcn_sched_barrier(0);
             if (live) {
 #pragma unroll
-              for (int blk = 0; blk < 4; ++blk)
+              for (int blk = 0; blk < NBLK; ++blk)
                 mma_step(acc[blk], hA[ks < KS ? ks : 0], bcur[blk]);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) bcur[blk] = bnxt[blk];
+            for (int blk = 0; blk < NBLK; ++blk) bcur[blk] = bnxt[blk];
           }
         };
         if (par == 0)
@@ -468,25 +542,61 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
       }
     }
 
-    // ---- epilogue for vocabulary columns vt .. vt+127
-    if constexpr (MODE == kLse || MODE == kStoreZ) {
+    // ---- epilogue for vocabulary columns vt .. vt+VT-1
+    if constexpr ((MODE == kLse || MODE == kStoreZ) && NBLK == 2) {
+      if (bounded) {
+        float tsum[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float sum = 0.f;
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk)
+            sum += cvalid[blk] ? exp2_fast(acc[blk][r] * kLog2e) : 0.f;
+          tsum[r] = sum;
+        }
+        srow += rs_sum16(tsum, lane);
+      } else {
+        float tm[16], tsum[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x[NBLK];
+          float mx = -kInf;
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk) {
+            x[blk] = cvalid[blk] ? acc[blk][r] * kLog2e : -kInf;
+            mx = fmaxf(mx, x[blk]);
+          }
+          float sum = 0.f;
+          if (mx > -kInf) {
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk) sum += exp2_fast(x[blk] - mx);
+          }
+          tm[r] = mx;
+          tsum[r] = sum;
+        }
+        float m2, s2;
+        rs_lse16(tm, tsum, lane, m2, s2);
+        lse2_merge(mrow, srow, m2, s2);
+      }
+    }
+    if constexpr ((MODE == kLse || MODE == kStoreZ) && NBLK == 4) {
       if (bounded) {
         // every |z| < 64: sum e^z directly, no running max needed
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float sum = srun[r];
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk)
+          for (int blk = 0; blk < NBLK; ++blk)
             sum += cvalid[blk] ? exp2_fast(acc[blk][r] * kLog2e) : 0.f;
           srun[r] = sum;
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x[4];
+          float x[NBLK];
           float mx = -kInf;
 #pragma unroll
-          for (int blk = 0; blk < 4; ++blk) {
+          for (int blk = 0; blk < NBLK; ++blk) {
             x[blk] = cvalid[blk] ? acc[blk][r] * kLog2e : -kInf;
             mx = fmaxf(mx, x[blk]);
           }
@@ -494,39 +604,43 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
           if (mn > -kInf) {
             float sum = srun[r] * exp2_fast(mrun[r] - mn);
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) sum += exp2_fast(x[blk] - mn);
+            for (int blk = 0; blk < NBLK; ++blk) sum += exp2_fast(x[blk] - mn);
             srun[r] = sum;
             mrun[r] = mn;
           }
         }
       }
+    }
+    if constexpr (MODE == kLse || MODE == kStoreZ) {
       // blank logit
-      if (d.blank >= vt && d.blank < vt + kVocabTile) {
+      if (d.blank >= vt && d.blank < vt + VT) {
         const int bb = d.blank - vt;
         if (lc == (bb & 31)) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            cap_blank[w * 32 + acc_row(r, kh)] = sel4(acc, bb >> 5, r);
+            cap_blank[w * 32 + acc_row(r, kh)] = sel_blk<NBLK>(acc, bb >> 5, r);
         }
       }
       // label logits
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int dl = lab[j] - vt;
-        if (dl >= 0 && dl < kVocabTile && (dl & 31) == lc) {
+        if (dl >= 0 && dl < VT && (dl & 31) == lc) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int r = 4 * i + j;
-            cap_label[w * 32 + acc_row(r, kh)] = sel4(acc, dl >> 5, r);
+            cap_label[w * 32 + acc_row(r, kh)] = sel_blk<NBLK>(acc, dl >> 5, r);
           }
         }
       }
     } else {  // kGrad: acc <- dz without the one-hot terms
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
+      for (int r = 0; r < 16; ++r) {
+        const float c = NBLK == 4 ? cst[r] : row_c[w * 32 + acc_row(r, kh)];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk)
-          acc[blk][r] = gc * exp2_fast(acc[blk][r] * kLog2e - cst[r]);
+        for (int blk = 0; blk < NBLK; ++blk)
+          acc[blk][r] = gc * exp2_fast(acc[blk][r] * kLog2e - c);
+      }
     }
 
     if constexpr (MODE == kStoreZ || MODE == kGrad) {
@@ -537,7 +651,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         // accumulator columns -> Ts[col][row] (8-byte writes of 4 rows) ...
         uint16_t* ts = Ts[w];
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
+        for (int blk = 0; blk < NBLK; ++blk) {
           const int col = blk * 32 + lc;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -554,12 +668,12 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
           // one-hot terms: lane lc of the first half fixes row lc
           if (kh == 0) {
             const int rowi = w * 32 + lc;
-            if (d.blank >= vt && d.blank < vt + kVocabTile) {
+            if (d.blank >= vt && d.blank < vt + VT) {
               uint16_t* p = &ts[ts_idx(d.blank - vt, lc)];
               *p = f32_to_bf16_hw(bf16_to_f32(*p) - row_b[rowi]);
             }
             const int y = lab_row;
-            if (y >= vt && y < vt + kVocabTile) {
+            if (y >= vt && y < vt + VT) {
               uint16_t* p = &ts[ts_idx(y - vt, lc)];
               *p = f32_to_bf16_hw(bf16_to_f32(*p) - row_e[rowi]);
             }
@@ -580,7 +694,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
         T* orow = out + (((size_t)b * RT + (row_st ? t - rt0 : 0)) * RU + (row_st ? u - ru0 : 0)) * V + vt;
         const int g = lane >> 4, i = lane & 15;
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
+        for (int f = 0; f < VT / 16; ++f) {
           const int k0 = 16 * f + 8 * (g >> 1) + (i >> 2);
           const int cb = 16 * (g & 1) + 4 * (i & 3);
           const i16x4 lo =
@@ -607,7 +721,7 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
           if (MODE == kGrad || ok) {
             T* orow = out + (((size_t)b * RT + (t - rt0)) * RU + (u - ru0)) * V;
 #pragma unroll
-            for (int blk = 0; blk < 4; ++blk) {
+            for (int blk = 0; blk < NBLK; ++blk) {
               const int col = vt + blk * 32 + lc;
               if (cvalid[blk]) {
                 float g = acc[blk][r];
@@ -626,7 +740,22 @@ __global__ __launch_bounds__(256, 1) void joint_tile_kernel(JointArgs a) {
   }
   pre = next_ns > 0;  // the last slice started the next item's first copy
 
-  if constexpr (MODE == kLse || MODE == kStoreZ) {
+  if constexpr ((MODE == kLse || MODE == kStoreZ) && NBLK == 2) {
+    __syncthreads();  // captures visible
+    if (lc < 16) {
+      const int r = rs_row(lc);
+      const int rowi = w * 32 + acc_row(r, kh);
+      const int t = t0 + 4 * w + (r >> 2), u = u0 + 4 * kh + (r & 3);
+      if (t < Tl && u <= Ul) {
+        const float lse = ((bounded ? 0.f : mrow) + __builtin_amdgcn_logf(srow)) * kLn2;
+        const size_t ix = skew_idx(d, b, t, u);
+        a.lse[ix] = lse;
+        a.LB[ix] = cap_blank[rowi] - lse;
+        a.LE[ix] = (u < Ul) ? cap_label[rowi] - lse : 0.f;
+      }
+    }
+  }
+  if constexpr ((MODE == kLse || MODE == kStoreZ) && NBLK == 4) {
     // combine the per-lane partial sums of the 32 lanes that share each row
     if (bounded) {
 #pragma unroll
@@ -692,34 +821,41 @@ int device_cu_count() {
   return cache[dev];
 }
 
+// bf16 with H <= 256: 64-column vocabulary steps and two workgroups per
+// compute unit (the MFMA work of one overlaps the other's h build,
+// exponentials, stores and slice barriers), which fits the registers of a
+// two-wave-per-SIMD launch only while the h fragments of a wave take at most
+// 64 of them; otherwise 128-column steps, one workgroup per compute unit
+template <typename T, int KS>
+constexpr int kJointBlocks = (sizeof(T) == 2 && KS <= 16) ? 2 : 4;
+
 template <typename T, int KS, int MODE>
-static void launch_ks(const JointArgs& a, bool exact, dim3 grid, hipStream_t st) {
+static void launch_ks(const JointArgs& a, int n_items, hipStream_t st) {
+  constexpr int NB = kJointBlocks<T, KS>;
+  using C = StageCfg<T, NB>;
+  const bool exact = a.d.H / 16 == KS && a.d.H % C::BK == 0 && a.d.V % C::VT == 0;
+  const int slots = device_cu_count() * C::OCC;
+  const dim3 grid(n_items < slots ? n_items : slots);
   if (exact)
-    hipLaunchKernelGGL((joint_tile_kernel<T, KS, MODE, true>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((joint_tile_kernel<T, KS, MODE, true, NB>), grid, dim3(256), 0, st, a);
   else
-    hipLaunchKernelGGL((joint_tile_kernel<T, KS, MODE, false>), grid, dim3(256), 0, st, a);
+    hipLaunchKernelGGL((joint_tile_kernel<T, KS, MODE, false, NB>), grid, dim3(256), 0, st, a);
 }
 
 template <typename T, int MODE>
 static hipError_t launch_mode(const JointArgs& a, int n_items, hipStream_t st) {
-  using C = StageCfg<T>;
   const int nks = a.d.H / 16;
-  const int ncu = device_cu_count();
-  dim3 grid(n_items < ncu ? n_items : ncu);
-  auto exact = [&](int KS) {
-    return nks == KS && a.d.H % C::BK == 0 && a.d.V % kVocabTile == 0;
-  };
   if constexpr (std::is_same<T, float>::value) {
-    if (nks <= 4) launch_ks<T, 4, MODE>(a, exact(4), grid, st);
-    else if (nks <= 8) launch_ks<T, 8, MODE>(a, exact(8), grid, st);
-    else if (nks <= 16) launch_ks<T, 16, MODE>(a, exact(16), grid, st);
+    if (nks <= 4) launch_ks<T, 4, MODE>(a, n_items, st);
+    else if (nks <= 8) launch_ks<T, 8, MODE>(a, n_items, st);
+    else if (nks <= 16) launch_ks<T, 16, MODE>(a, n_items, st);
     else return hipErrorInvalidValue;
   } else {
-    if (nks <= 8) launch_ks<T, 8, MODE>(a, exact(8), grid, st);
-    else if (nks <= 16) launch_ks<T, 16, MODE>(a, exact(16), grid, st);
-    else if (nks <= 32) launch_ks<T, 32, MODE>(a, exact(32), grid, st);
-    else if (nks <= 40) launch_ks<T, 40, MODE>(a, exact(40), grid, st);
-    else if (nks <= 48) launch_ks<T, 48, MODE>(a, exact(48), grid, st);
+    if (nks <= 8) launch_ks<T, 8, MODE>(a, n_items, st);
+    else if (nks <= 16) launch_ks<T, 16, MODE>(a, n_items, st);
+    else if (nks <= 32) launch_ks<T, 32, MODE>(a, n_items, st);
+    else if (nks <= 40) launch_ks<T, 40, MODE>(a, n_items, st);
+    else if (nks <= 48) launch_ks<T, 48, MODE>(a, n_items, st);
     else return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -76,6 +76,30 @@ def test_ragged_edges(dtype):
             assert np.all(g["dPred"][b, inp.U_lens[b] + 1:] == 0)
 
 
+@pytest.mark.parametrize("dtype,H,V,sigma", [
+    ("bf16", 128, 256, 0.05),  # exact shape, every |z| provably below 64
+    ("bf16", 128, 256, 1.5),   # exact shape, bound above 64: running maxima
+    ("bf16", 64, 200, 2.0),    # partial vocabulary step, running maxima
+    ("fp32", 64, 200, 2.0),
+])
+def test_small_hidden_and_logit_bound(dtype, H, V, sigma):
+    """Hidden sizes up to 256 in bf16 (the 64-column vocabulary step with
+    two workgroups per compute unit), with the max-free log-sum-exp and, when
+    sum_k |W_kv| + |b_v| reaches 64, the one with running maxima.  Untiled
+    bf16 keeps the logits in bf16, whose rounding (|z| 2^-9, ~0.06 at the
+    |z| ~ 30 these weights give) enters exp(z - lse) directly, so the large-
+    logit bf16 cases run the tiled modes, which recompute the logits in fp32."""
+    inp = make_inputs(3, 29, 9, H, V, dtype=dtype, sigma=sigma, seed=53, t_range=(5, 29),
+                      u_range=(0, 9))
+    ref = _oracle_full(inp, grad_costs=[1.0, -0.5, 0.25])
+    large_bf16 = dtype == "bf16" and sigma > 1.0
+    for tiles in ([(16, 8, 0), (0, 8, 128)] if large_bf16 else [(0, 0, 0), (16, 8, 0)]):
+        print(f"[small hidden {dtype} H={H} V={V} sigma={sigma} tiles={tiles}]", flush=True)
+        g = run_gpu(inp, *tiles, grad_costs=[1.0, -0.5, 0.25])
+        assert g["status"] == 0
+        _compare_all(inp, g, ref)
+
+
 @pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
 def test_bf16_wide_hidden_partial_tiles(tiles):
     """H = 640 (the widest hidden size whose h rows are staged in LDS) with
