@@ -20,6 +20,8 @@ Sources, all on the pages that describe the method:
 * "Daily Papers" page, abstract comparing the full-sum RNN-T criterion with the
   maximum approximation: both are computed here (``criterion="sum"``, the
   default, or ``"max"``: the single best alignment).
+* The Transformer-Transducer abstract's feed-forward combination, read as an
+  affine projection of each encoding ahead of the joint (``proj.py``).
 
 Every function is pinned by the tests in ``tests/test_oracle_pins.py``
 (brute-force enumeration, alpha/beta agreement, closed forms, invariants,
@@ -38,3 +40,4 @@ from .rnnt import (  # noqa: F401
     closed_form_zero_weights,
     closed_form_zero_weights_max,
 )
+from .proj import linear, linear_grads, projected_loss_and_grads  # noqa: F401
