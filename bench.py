@@ -35,6 +35,7 @@ METRIC = "lattice cells/sec (B·T·U) fused joint+loss fwd+bwd"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 MFMA_KERNELS = ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
+PROJ_KERNELS = ("proj_fwd", "proj_dx", "proj_dw")
 DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (64, 64, 128),
                  "medium_lv": (64, 64, 256), "long": (64, 64, 256)}
 
@@ -48,6 +49,9 @@ def parse():
                     choices=["tiny", "short", "medium", "medium_lv", "long"])
     ap.add_argument("--criterion", default="sum", choices=["sum", "max"],
                     help="full sum over alignments, or the best alignment only")
+    ap.add_argument("--proj", default=None, metavar="E,P",
+                    help="put joint input projections (enc: E -> H, pred: P -> H) in front of the "
+                         "joint, their gradients after it, inside the timed step")
     ap.add_argument("--tile-t", type=int, default=None)
     ap.add_argument("--tile-u", type=int, default=None)
     ap.add_argument("--tile-v", type=int, default=None)
@@ -99,7 +103,7 @@ def calibrate_copy(nbytes):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 5}))
 
 
-def cpu_baseline(inp, target_s, criterion="sum"):
+def cpu_baseline(inp, target_s, criterion="sum", pj=None):
     """Float64 oracle (fwd+bwd, one utterance at a time, NumPy BLAS on all host
     threads) on a bounded sample of the workload: whole utterances in order
     until about target_s seconds are spent, or the first utterance cut to its
@@ -116,9 +120,18 @@ def cpu_baseline(inp, target_s, criterion="sum"):
 
     def run(b, t_s):
         t0 = time.perf_counter()
-        rnnt.utterance_loss_and_grads(inp.enc_f64[b, :t_s], inp.pred_f64[b], inp.W_f64,
-                                      inp.b_f64, inp.labels[b], t_s, int(inp.U_lens[b]),
-                                      inp.blank, criterion=criterion)
+        if pj is None:
+            rnnt.utterance_loss_and_grads(inp.enc_f64[b, :t_s], inp.pred_f64[b], inp.W_f64,
+                                          inp.b_f64, inp.labels[b], t_s, int(inp.U_lens[b]),
+                                          inp.blank, criterion=criterion)
+        else:
+            from oracle import proj
+            ep = proj.linear(pj.enc_in_f64[b, :t_s], pj.W_enc_f64, pj.b_enc_f64)
+            pp = proj.linear(pj.pred_in_f64[b], pj.W_pred_f64, pj.b_pred_f64)
+            o = rnnt.utterance_loss_and_grads(ep, pp, inp.W_f64, inp.b_f64, inp.labels[b], t_s,
+                                              int(inp.U_lens[b]), inp.blank, criterion=criterion)
+            proj.linear_grads(pj.enc_in_f64[b, :t_s], pj.W_enc_f64, o["dEnc"])
+            proj.linear_grads(pj.pred_in_f64[b, :o["dPred"].shape[0]], pj.W_pred_f64, o["dPred"])
         return time.perf_counter() - t0
 
     Tl0, Ul0 = int(inp.T_lens[0]), int(inp.U_lens[0])
@@ -143,7 +156,8 @@ def cpu_baseline(inp, target_s, criterion="sum"):
     value = inp.B * inp.T * inp.U / full_time
     return {"value": value, "unit": "cells/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{desc}: {sample_cells} valid cells in {el:.2f} s, float64 NumPy "
-                      f"fwd+bwd, scaled by valid cells ({total_valid}) to the B*T*U metric"}
+                      f"fwd+bwd{'' if pj is None else ' with the input projections'}, scaled by "
+                      f"valid cells ({total_valid}) to the B*T*U metric"}
 
 
 def main():
@@ -161,7 +175,7 @@ def main():
 
     import rnn_joint_transducer_amd as rj
     from rnn_joint_transducer_amd import _lib
-    from synth import make_config
+    from synth import make_config, make_proj_inputs
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -183,6 +197,12 @@ def main():
     tensors = dict(enc=conv(inp.enc), pred=conv(inp.pred), W_out=conv(inp.W), b_out=conv(inp.b),
                    labels=i32(inp.labels), T_lens=i32(inp.T_lens), U_lens=i32(inp.U_lens))
     B, T, U, H, V = inp.B, inp.T, inp.U, inp.H, inp.V
+    pj = None
+    if args.proj:
+        E, P = (int(x) for x in args.proj.split(","))
+        pj = make_proj_inputs(inp, E, P, seed=1)
+        ptens = dict(enc_in=conv(pj.enc_in), pred_in=conv(pj.pred_in), W_enc=conv(pj.W_enc),
+                     b_enc=conv(pj.b_enc), W_pred=conv(pj.W_pred), b_pred=conv(pj.b_pred))
     dc = rj.RNNTJ_BF16 if bf16 else rj.RNNTJ_F32
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
@@ -196,10 +216,17 @@ def main():
              torch.empty(H, V, device=dev), torch.empty(V, device=dev))
 
     def step():
+        if pj is not None:
+            tensors["enc"] = rj.rnnt_joint_proj_fwd(ptens["enc_in"], ptens["W_enc"], ptens["b_enc"])
+            tensors["pred"] = rj.rnnt_joint_proj_fwd(ptens["pred_in"], ptens["W_pred"],
+                                                     ptens["b_pred"])
         rj.rnnt_joint_loss_fwd(**tensors, tile_t=tt, tile_u=tu, tile_v=tv, costs=costs,
                                saved=saved, criterion=args.criterion)
         rj.rnnt_joint_loss_bwd(**tensors, saved=saved, tile_t=tt, tile_u=tu, tile_v=tv,
                                workspace=ws, out=grads)
+        if pj is not None:
+            rj.rnnt_joint_proj_bwd(ptens["enc_in"], ptens["W_enc"], grads[0])
+            rj.rnnt_joint_proj_bwd(ptens["pred_in"], ptens["W_pred"], grads[1])
 
     for _ in range(args.warmup):
         step()
@@ -239,6 +266,10 @@ def main():
         if name in MFMA_KERNELS:
             flops_step = 2.0 * H * V * valid
             k["tflops"] = flops_step / (tot / kin / 1e3) / 1e12
+        elif name in PROJ_KERNELS and pj is not None:
+            # each of the three products: 2 * rows * in_width * H per projection
+            flops_step = 2.0 * H * (B * T * pj.E + B * (U + 1) * pj.P)
+            k["tflops"] = flops_step / (tot / kin / 1e3) / 1e12
         kernels[name] = k
         print(f"#   {name:16s} {n / kin:5.1f} launches/step {tot / kin:9.4f} ms/step", file=sys.stderr)
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
@@ -265,7 +296,7 @@ def main():
     roof["traffic"] = measured_traffic(args.workload, dom, mode, args.criterion)
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds, args.criterion)
+        cpu = cpu_baseline(inp, args.cpu_seconds, args.criterion, pj)
 
     line = {
         "metric": METRIC, "value": value, "unit": "cells/s", "n_gpus": 1,
@@ -273,7 +304,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "T": T, "U": U, "H": H, "V": V,
-                   "mode": mode, "criterion": args.criterion, "tile_t": tt, "tile_u": tu, "tile_v": tv,
+                   "mode": mode, "criterion": args.criterion,
+                   "proj": None if pj is None else {"E": pj.E, "P": pj.P}, "tile_t": tt, "tile_u": tu, "tile_v": tv,
                    "valid_cells": valid, "valid_cells_per_s": valid / (ms / 1e3),
                    "peak_gb": round(peak_gb, 3), "peak_gb_above_inputs": round(extra_gb, 3)},
         "roofline": roof,

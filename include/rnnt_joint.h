@@ -188,6 +188,35 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error);
 
 /*
+ * Joint input projections ("Daily Papers" page, Transformer-Transducer
+ * abstract: the two encodings are combined by a feed-forward layer; read as
+ * one affine map per encoding ahead of the joint's add):
+ *     enc_p = enc @ W_enc + b_enc,   pred_p = pred @ W_pred + b_pred,
+ * each computed by rnnt_joint_proj_fwd and fed to rnnt_joint_loss_fwd/bwd as
+ * `enc` / `pred`; the d_enc / d_pred that the loss backward returns are the
+ * `dy` of rnnt_joint_proj_bwd.
+ *
+ * rnnt_joint_proj_fwd: y[M,N] = x[M,K] @ W[K,N] + b[N].  x, W, b, y device
+ * pointers of `dtype` (row-major, contiguous); products accumulate in fp32
+ * and y is rounded once to dtype.  For enc: M = B*T, K = E (input width),
+ * N = H; for pred: M = B*(U+1), K = P, N = H.
+ *
+ * rnnt_joint_proj_bwd: from dy[M,N] (float32) writes dx[M,K] = dy @ W^T,
+ * dW[K,N] = x^T @ dy and db[N] = sum of the rows of dy, all float32 and
+ * overwritten (dx may be NULL to skip it).  x and W as in the forward.
+ *
+ * Both: x, W, y / dy, dx, dW 16-byte aligned; K and N multiples of 16 and at
+ * most 65536, M >= 1 (else RNNTJ_ERR_UNSUPPORTED / RNNTJ_ERR_ARG, returned
+ * before anything is enqueued).  Kernels run on `stream` (hipStream_t, NULL =
+ * default stream) and allocate nothing; results are ready when the stream
+ * reaches them.  Returns a status code.
+ */
+int rnnt_joint_proj_fwd(const void* x, const void* W, const void* b, int dtype, int M, int K,
+                        int N, void* y, void* stream);
+int rnnt_joint_proj_bwd(const void* x, const void* W, int dtype, int M, int K, int N,
+                        const float* dy, float* dx, float* dW, float* db, void* stream);
+
+/*
  * Kernel timing (measurement aid; no counterpart on the pages).
  * rnnt_joint_loss_timing(1) makes every later call bracket each kernel it
  * enqueues with a pair of HIP events recorded on that call's `stream`;

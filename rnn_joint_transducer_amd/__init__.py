@@ -199,3 +199,79 @@ def rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, ti
         _FN = _make_function()
     return _FN.apply(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank, tile_t, tile_u,
                      tile_v, criterion)
+
+
+# ---------------------------------------------------------------- joint input projections
+
+def _check_linear(x, W, b=None):
+    import torch
+    if not (x.is_cuda and W.is_cuda) or x.dtype != W.dtype or (b is not None and b.dtype != x.dtype):
+        raise TypeError("x, W (and b) must be device tensors of one dtype")
+    if W.dim() != 2 or x.shape[-1] != W.shape[0] or (b is not None and b.shape != (W.shape[1],)):
+        raise ValueError(f"shapes x {tuple(x.shape)}, W {tuple(W.shape)} do not form x @ W + b")
+    for t in (x, W) + (() if b is None else (b,)):
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    M = x.numel() // x.shape[-1] if x.numel() else 0
+    return M, W.shape[0], W.shape[1]
+
+
+def rnnt_joint_proj_fwd(x, W, b):
+    """Joint input projection y = x @ W + b (x [..., K], W [K, N], b [N], one
+    dtype; fp32 accumulation, y rounded once to that dtype)."""
+    import torch
+    M, K, N = _check_linear(x, W, b)
+    y = torch.empty(*x.shape[:-1], N, dtype=x.dtype, device=x.device)
+    check(load().rnnt_joint_proj_fwd(_ptr(x), _ptr(W), _ptr(b), _dtype_code(x), M, K, N, _ptr(y),
+                                     _stream(x.device)), "rnnt_joint_proj_fwd")
+    return y
+
+
+def rnnt_joint_proj_bwd(x, W, dy, need_dx=True):
+    """Gradients of y = x @ W + b from dy [..., N] (float32): (dx or None,
+    dW, db), all float32."""
+    import torch
+    M, K, N = _check_linear(x, W)
+    if dy.dtype != torch.float32 or not dy.is_contiguous() or dy.shape != (*x.shape[:-1], N):
+        raise ValueError("dy must be a contiguous float32 tensor shaped like y")
+    dev = x.device
+    dx = torch.empty(x.shape, dtype=torch.float32, device=dev) if need_dx else None
+    dW = torch.empty(K, N, dtype=torch.float32, device=dev)
+    db = torch.empty(N, dtype=torch.float32, device=dev)
+    check(load().rnnt_joint_proj_bwd(_ptr(x), _ptr(W), _dtype_code(x), M, K, N, _ptr(dy), _ptr(dx),
+                                     _ptr(dW), _ptr(db), _stream(dev)), "rnnt_joint_proj_bwd")
+    return dx, dW, db
+
+
+def _make_proj_function():
+    import torch
+
+    class _JointProj(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, x, W, b):
+            ctx.save_for_backward(x, W)
+            return rnnt_joint_proj_fwd(x, W, b)
+
+        @staticmethod
+        def backward(ctx, dy):
+            x, W = ctx.saved_tensors
+            dx, dW, db = rnnt_joint_proj_bwd(x, W, dy.float().contiguous(),
+                                             need_dx=ctx.needs_input_grad[0])
+            return (None if dx is None else dx.to(x.dtype)), dW.to(W.dtype), db.to(W.dtype)
+
+    return _JointProj
+
+
+_PROJ = None
+
+
+def rnnt_joint_proj(x, W, b):
+    """y = x @ W + b with autograd support (feed y to rnnt_joint_loss as enc
+    or pred)."""
+    global _PROJ
+    if _PROJ is None:
+        _PROJ = _make_proj_function()
+    return _PROJ.apply(x, W, b)
+
+
+__all__ += ["rnnt_joint_proj_fwd", "rnnt_joint_proj_bwd", "rnnt_joint_proj"]

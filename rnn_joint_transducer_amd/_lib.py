@@ -35,6 +35,9 @@ _SIG = {
     "rnnt_joint_loss_status": (_c_int, [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]),
     "rnnt_joint_loss_timing": (_c_int, [_c_int]),
     "rnnt_joint_loss_timing_report": (_c_int, [ctypes.c_char_p, _c_size]),
+    "rnnt_joint_proj_fwd": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp]),
+    "rnnt_joint_proj_bwd": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                                     _vp]),
 }
 
 _lib = None
@@ -82,7 +85,7 @@ def declared_functions(header: str = HEADER):
     """Names of the functions include/rnnt_joint.h declares."""
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rnnt_joint_loss_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rnnt_joint_(?:loss|proj)_\w+)\s*\(", text)))
 
 
 def check(code: int, where: str):

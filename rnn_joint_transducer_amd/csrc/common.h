@@ -34,6 +34,7 @@ constexpr int kVocabTile = 128;  // vocabulary columns per pass of one wave
 // Largest vocabulary: keeps 32-bit element offsets inside a 16-frame tile of
 // logit rows (16 x 512 rows x V) and a label + 1 inside 30 bits.
 constexpr int kMaxV = 262144;
+constexpr int kMaxProj = 65536;  // largest input / output width of a joint input projection
 
 // Shapes shared by every kernel.
 struct Dims {

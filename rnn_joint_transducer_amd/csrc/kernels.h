@@ -160,4 +160,17 @@ hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st);
 hipError_t launch_db_finalize(const double* db64, float* d_b, int V, int32_t* mark,
                               hipStream_t st);
 
+// Joint input projections (proj.hip), row-major operands, fp32 accumulation:
+//   y[M,N] = x[M,K] W[K,N] + b[N] in the operand type;
+//   dx[M,K] = dy[M,N] W^T (fp32, stored);
+//   dW[K,N] += x^T dy and db[N] += column sums of dy (fp32 atomics: dW and
+//   db must be zeroed first).
+// K and N multiples of 16.
+hipError_t launch_proj_fwd(const void* x, const void* W, const void* b, bool bf16, int M, int K,
+                           int N, void* y, hipStream_t st);
+hipError_t launch_proj_dx(const float* dy, const void* W, bool bf16, int M, int K, int N,
+                          float* dx, hipStream_t st);
+hipError_t launch_proj_dw(const void* x, const float* dy, bool bf16, int M, int K, int N,
+                          float* dW, float* db, int cus, hipStream_t st);
+
 }  // namespace rnntj

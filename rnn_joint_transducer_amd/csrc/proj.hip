@@ -1,0 +1,217 @@
+// Joint input projections: the affine maps that take each encoding into the
+// joint's hidden size ahead of the add.
+//
+// "Daily Papers" page, Transformer-Transducer abstract: the audio and label
+// encodings are combined by a feed-forward layer into one label distribution
+// per (frame, label history); read as one affine map per encoding,
+//     enc_p = enc @ W_enc + b_enc,   pred_p = pred @ W_pred + b_pred,
+// whose gradients chain from the joint's gradients of enc_p and pred_p:
+//     dx = dy @ W^T,   dW = x^T @ dy,   db = sum over rows of dy.
+//
+// All three products run on one kernel: a 64 x 64 output tile per workgroup
+// (four waves, each a 32 x 32 fp32 MFMA block), 32-deep k-steps staged in LDS
+// as fp32 (bf16 operands are widened on the way in, so every product is
+// exact and accumulates in fp32), the next k-step's global loads issued
+// before the current one's MFMAs.  An operand is read either with its k
+// index contiguous (x, dy, W in dx = dy W^T) or with its other index
+// contiguous (W in y = x W, x^T in dW = x^T dy); either way a thread loads
+// 8 consecutive elements.  dW splits its k range (the rows of x) over
+// workgroups and adds the partial sums with fp32 atomics into a zeroed
+// output; the workgroups of its first row tile also sum the dy rows they
+// stage (db), so dy is read once for both.
+#include "common.h"
+#include "kernels.h"
+
+namespace rnntj {
+
+namespace {
+
+constexpr int kPT = 64;   // output tile edge
+constexpr int kPK = 32;   // k-step
+constexpr int kLdA = 36;  // LDS row strides (floats): 16-byte aligned rows,
+constexpr int kLdB = 68;  // conflict-free fragment reads
+
+template <typename X>
+__device__ __forceinline__ void load8(const X* p, bool ok, float (&v)[8]) {
+  if constexpr (sizeof(X) == 2) {
+    u32x4 w = u32x4{0u, 0u, 0u, 0u};
+    if (ok) w = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    f32x4 a = f32x4{0.f, 0.f, 0.f, 0.f}, b = a;
+    if (ok) {
+      a = *reinterpret_cast<const f32x4*>(p);
+      b = *reinterpret_cast<const f32x4*>(p + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
+  }
+}
+
+// C[i][j] = sum_k A(i,k) B(k,j) over k in [k0, k1) of this workgroup's
+// split: A(i,k) = a[i*sai + k] (AK) or a[k*sak + i] (!AK); B(k,j) =
+// b[k*sbk + j] (BJ) or b[j*sbj + k] (!BJ).  OUT: 0 store fp32, 1 atomic add
+// fp32, 2 add bias[j] and store as the operand type TO.  With OUT == 1 and
+// colsum set, workgroups with blockIdx.x == 0 also add the column sums of
+// their B rows (k range) into colsum[j].
+struct GemmArgs {
+  const void* a;
+  long long sa;  // row stride of a
+  const void* b;
+  long long sb;  // row stride of b
+  const void* bias;
+  void* c;
+  long long ldc;
+  int M, N, K, kchunk;
+  float* colsum;
+};
+
+template <typename TA, typename TB, bool AK, bool BJ, int OUT, typename TO>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  __shared__ __align__(16) float As[kPT * kLdA];  // [i][k]
+  __shared__ __align__(16) float Bs[kPK * kLdB];  // [k][j]; also the column-sum reduction
+  const TA* __restrict__ A = static_cast<const TA*>(g.a);
+  const TB* __restrict__ Bm = static_cast<const TB*>(g.b);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i0 = blockIdx.x * kPT, j0 = blockIdx.y * kPT;
+  const int kb = blockIdx.z * g.kchunk;
+  const int ke = min(g.K, kb + g.kchunk);
+  // this thread's 8-element piece of the A and B tiles
+  const int ai = AK ? tid >> 2 : (tid & 7) * 8, ak = AK ? (tid & 3) * 8 : tid >> 3;
+  const int bk = BJ ? tid >> 3 : (tid & 3) * 8, bj = BJ ? (tid & 7) * 8 : tid >> 2;
+  float av[8], bv[8];
+  auto fetch = [&](int k0) {
+    const int gi = i0 + ai, gk = k0 + ak;
+    if constexpr (AK)
+      load8(A + (size_t)gi * g.sa + gk, gi < g.M && gk < ke, av);
+    else
+      load8(A + (size_t)gk * g.sa + gi, gi < g.M && gk < ke, av);
+    const int hk = k0 + bk, hj = j0 + bj;
+    if constexpr (BJ)
+      load8(Bm + (size_t)hk * g.sb + hj, hk < ke && hj < g.N, bv);
+    else
+      load8(Bm + (size_t)hj * g.sb + hk, hk < ke && hj < g.N, bv);
+  };
+  auto stash = [&]() {
+    if constexpr (AK) {
+      *reinterpret_cast<f32x4*>(&As[ai * kLdA + ak]) = f32x4{av[0], av[1], av[2], av[3]};
+      *reinterpret_cast<f32x4*>(&As[ai * kLdA + ak + 4]) = f32x4{av[4], av[5], av[6], av[7]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) As[(ai + e) * kLdA + ak] = av[e];
+    }
+    if constexpr (BJ) {
+      *reinterpret_cast<f32x4*>(&Bs[bk * kLdB + bj]) = f32x4{bv[0], bv[1], bv[2], bv[3]};
+      *reinterpret_cast<f32x4*>(&Bs[bk * kLdB + bj + 4]) = f32x4{bv[4], bv[5], bv[6], bv[7]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Bs[(bk + e) * kLdB + bj] = bv[e];
+    }
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  constexpr bool kColsum = OUT == 1 && BJ;
+  const bool do_cs = kColsum && g.colsum != nullptr && blockIdx.x == 0;
+  float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int wi = (w >> 1) * 32, wj = (w & 1) * 32;
+  if (kb < ke) fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += kPK) {
+    __syncthreads();  // the previous k-step's fragment reads are done
+    stash();
+    if (do_cs) {  // bv: 8 columns of one staged row (zero outside the k range)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cs[e] += bv[e];
+    }
+    __syncthreads();
+    if (k0 + kPK < ke) fetch(k0 + kPK);
+#pragma unroll
+    for (int ks = 0; ks < kPK; ks += 16) {
+      const float* ap = &As[(wi + (lane & 31)) * kLdA + ks + 8 * (lane >> 5)];
+      Frag8<float> fa, fb;
+      fa.lo = *reinterpret_cast<const f32x4*>(ap);
+      fa.hi = *reinterpret_cast<const f32x4*>(ap + 4);
+      fb = load_frag_T(Bs, kLdB, ks, wj);
+      mma_step(acc, fa, fb);
+    }
+  }
+  if (do_cs) {  // uniform: reduce the 32 threads of each column group
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) Bs[bk * kLdB + bj + e] = cs[e];
+    __syncthreads();
+    if (tid < kPT && j0 + tid < g.N) {
+      float s = 0.f;
+      for (int r = 0; r < kPK; ++r) s += Bs[r * kLdB + tid];
+      atomicAdd(&g.colsum[j0 + tid], s);
+    }
+  }
+  const int kh = lane >> 5, col = j0 + wj + (lane & 31);
+  if (col >= g.N) return;
+  float bias = 0.f;
+  if constexpr (OUT == 2) bias = ElemTraits<TO>::to_f32(static_cast<const TO*>(g.bias)[col]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = i0 + wi + acc_row(r, kh);
+    if (row >= g.M) continue;
+    const size_t o = (size_t)row * g.ldc + col;
+    if constexpr (OUT == 0) {
+      static_cast<float*>(g.c)[o] = acc[r];
+    } else if constexpr (OUT == 1) {
+      atomicAdd(static_cast<float*>(g.c) + o, acc[r]);
+    } else {
+      static_cast<TO*>(g.c)[o] = ElemTraits<TO>::from_f32(acc[r] + bias);
+    }
+  }
+}
+
+template <typename TA, typename TB, bool AK, bool BJ, int OUT, typename TO>
+hipError_t gemm(const GemmArgs& g, int splits, hipStream_t st) {
+  const dim3 grid((g.M + kPT - 1) / kPT, (g.N + kPT - 1) / kPT, splits);
+  hipLaunchKernelGGL((gemm_kernel<TA, TB, AK, BJ, OUT, TO>), grid, dim3(256), 0, st, g);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_proj_fwd(const void* x, const void* W, const void* b, bool bf16, int M, int K,
+                           int N, void* y, hipStream_t st) {
+  GemmArgs g{x, K, W, N, b, y, N, M, N, K, K, nullptr};
+  if (bf16) return gemm<uint16_t, uint16_t, true, true, 2, uint16_t>(g, 1, st);
+  return gemm<float, float, true, true, 2, float>(g, 1, st);
+}
+
+hipError_t launch_proj_dx(const float* dy, const void* W, bool bf16, int M, int K, int N,
+                          float* dx, hipStream_t st) {
+  // dx[M,K] = dy[M,N] W[K,N]^T: k runs over N
+  GemmArgs g{dy, N, W, N, nullptr, dx, K, M, K, N, N, nullptr};
+  if (bf16) return gemm<float, uint16_t, true, false, 0, float>(g, 1, st);
+  return gemm<float, float, true, false, 0, float>(g, 1, st);
+}
+
+hipError_t launch_proj_dw(const void* x, const float* dy, bool bf16, int M, int K, int N,
+                          float* dW, float* db, int cus, hipStream_t st) {
+  // dW[K,N] += x[M,K]^T dy[M,N] and db[N] += column sums of dy: k runs over
+  // the M rows, split so that the grid holds about four workgroups per
+  // compute unit
+  const int tiles = ((K + kPT - 1) / kPT) * ((N + kPT - 1) / kPT);
+  int splits = (4 * cus + tiles - 1) / tiles;
+  const int max_splits = (M + kPK - 1) / kPK;
+  splits = splits < 1 ? 1 : (splits > max_splits ? max_splits : splits);
+  int kchunk = (M + splits - 1) / splits;
+  kchunk = (kchunk + kPK - 1) / kPK * kPK;
+  splits = (M + kchunk - 1) / kchunk;
+  GemmArgs g{x, K, dy, N, nullptr, dW, N, K, N, M, kchunk, db};
+  if (bf16) return gemm<uint16_t, float, false, true, 1, float>(g, splits, st);
+  return gemm<float, float, false, true, 1, float>(g, splits, st);
+}
+
+
+}  // namespace rnntj

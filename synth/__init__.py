@@ -168,3 +168,46 @@ def make_config(name: str, seed: int = 0, **overrides) -> Inputs:
     kw = dict(CONFIGS[name])
     kw.update(overrides)
     return make_inputs(seed=seed, name=name, **kw)
+
+
+@dataclasses.dataclass
+class ProjInputs:
+    """Joint input projections for one batch: raw encodings enc_in [B,T,E],
+    pred_in [B,U+1,P] and the affine maps W_enc [E,H], b_enc [H], W_pred [P,H],
+    b_pred [H], as storage arrays (float32 or uint16 bf16 bits) with float64
+    twins holding the same values."""
+    E: int
+    P: int
+    enc_in: np.ndarray
+    pred_in: np.ndarray
+    W_enc: np.ndarray
+    b_enc: np.ndarray
+    W_pred: np.ndarray
+    b_pred: np.ndarray
+    enc_in_f64: np.ndarray
+    pred_in_f64: np.ndarray
+    W_enc_f64: np.ndarray
+    b_enc_f64: np.ndarray
+    W_pred_f64: np.ndarray
+    b_pred_f64: np.ndarray
+
+
+def make_proj_inputs(inp: Inputs, E: int, P: int, *, seed: int = 0, sigma: float = 0.05,
+                     w_scale: Optional[float] = None) -> ProjInputs:
+    """Projection inputs matching batch ``inp`` (its B, T, U, H and dtype):
+    enc_in, pred_in ~ N(0, sigma); W_enc, W_pred ~ N(0, w_scale) with w_scale
+    = 1/sqrt(fan-in) by default (so the projected encodings keep about the
+    spread of the inputs); biases ~ N(0, sigma).  Drawn in that order from
+    numpy.random.default_rng(seed) in float64, then cast like the batch."""
+    rng = np.random.default_rng(seed)
+    B, T, U, H = inp.B, inp.T, inp.U, inp.H
+    enc_in = rng.normal(0.0, sigma, size=(B, T, E))
+    pred_in = rng.normal(0.0, sigma, size=(B, U + 1, P))
+    W_enc = rng.normal(0.0, w_scale or 1.0 / np.sqrt(E), size=(E, H))
+    b_enc = rng.normal(0.0, sigma, size=H)
+    W_pred = rng.normal(0.0, w_scale or 1.0 / np.sqrt(P), size=(P, H))
+    b_pred = rng.normal(0.0, sigma, size=H)
+    parts = [_cast(x, inp.dtype) for x in (enc_in, pred_in, W_enc, b_enc, W_pred, b_pred)]
+    s = [p[0] for p in parts]
+    f = [p[1] for p in parts]
+    return ProjInputs(E, P, *s, *f)

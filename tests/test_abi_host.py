@@ -17,7 +17,8 @@ def test_exports_every_declared_symbol():
                           "rnnt_joint_loss_fwd", "rnnt_joint_loss_fwd_ex", "rnnt_joint_loss_bwd",
                           "rnnt_joint_loss_last_error",
                           "rnnt_joint_loss_status", "rnnt_joint_loss_timing",
-                          "rnnt_joint_loss_timing_report"}
+                          "rnnt_joint_loss_timing_report", "rnnt_joint_proj_fwd",
+                          "rnnt_joint_proj_bwd"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -152,3 +153,22 @@ def test_fwd_ex_rejects_unknown_criterion():
     for crit in (-1, 2, 7):
         rc = lib.rnnt_joint_loss_fwd_ex(*args, crit, v(), v(), None, 0, None)
         assert rc == 1, (crit, rc)
+
+
+def test_proj_rejects_before_launch():
+    """The projection entry points check pointers, dtype, sizes and alignment
+    on the host (nothing is enqueued, so fake aligned pointers suffice)."""
+    v = lambda k=1: ctypes.c_void_p(16 * 4096 * k)
+    fwd = lambda *a: lib.rnnt_joint_proj_fwd(*a)
+    assert fwd(v(), v(), v(), 0, 10, 64, 64, None, None) == 1          # y missing
+    assert fwd(v(), v(), v(), 2, 10, 64, 64, v(), None) == 1           # dtype
+    assert fwd(v(), v(), v(), 0, 0, 64, 64, v(), None) == 1            # M < 1
+    assert fwd(v(), v(), v(), 0, 10, 60, 64, v(), None) == 2           # K not a multiple of 16
+    assert fwd(v(), v(), v(), 1, 10, 64, 72, v(), None) == 2           # N not a multiple of 16
+    assert fwd(v(), v(), v(), 0, 10, 65552, 64, v(), None) == 2        # K > 65536
+    assert fwd(ctypes.c_void_p(16 * 4096 + 8), v(), v(), 0, 10, 64, 64, v(), None) == 1  # align
+    bwd = lambda *a: lib.rnnt_joint_proj_bwd(*a)
+    assert bwd(v(), v(), 0, 10, 64, 64, None, v(), v(), v(), None) == 1   # dy missing
+    assert bwd(v(), v(), 0, 10, 64, 64, v(), v(), None, v(), None) == 1   # dW missing
+    assert bwd(v(), v(), 0, 10, 64, 64, v(), v(), v(), None, None) == 1   # db missing
+    assert bwd(v(), v(), 0, 10, 48, 40, v(), v(), v(), v(), None) == 2    # N not a multiple of 16
