@@ -271,25 +271,53 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // other cells hold their predecessor decision, a positive value).
 constexpr double kPathBlank = -1.0, kPathLabel = -2.0;
 
+// The per-cell inputs of the posteriors, loaded in one go so that a caller
+// can issue the loads well before it needs the result.
+struct CellPostIn {
+  double a, bt, bu, m;  // alpha(t,u), beta(t+1,u), beta(t,u+1); max: the mark
+  float lb, le;
+};
+__device__ __forceinline__ CellPostIn cell_post_load(const Dims& d,
+                                                    const double* __restrict__ alpha,
+                                                    const double* __restrict__ beta,
+                                                    const float* __restrict__ LB,
+                                                    const float* __restrict__ LE, int b, int t,
+                                                    int u, int Tl, int Ul, int crit) {
+  const size_t ix = skew_idx(d, b, t, u);
+  CellPostIn c{0.0, 0.0, 0.0, 0.0, 0.f, 0.f};
+  if (crit == kCritMax) {
+    c.m = beta[ix];
+    return c;
+  }
+  c.a = alpha[ix];
+  c.lb = LB[ix];
+  c.le = LE[ix];
+  if (t < Tl - 1) c.bt = beta[skew_idx(d, b, t + 1, u)];
+  if (u < Ul) c.bu = beta[skew_idx(d, b, t, u + 1)];
+  return c;
+}
+__device__ __forceinline__ void cell_post_eval(const CellPostIn& c, double logP, int t, int u,
+                                               int Tl, int Ul, double& gB, double& gE,
+                                               int crit) {
+  if (crit == kCritMax) {  // 0/1 indicators of the best alignment's steps
+    gB = c.m == kPathBlank ? 1.0 : 0.0;
+    gE = c.m == kPathLabel ? 1.0 : 0.0;
+    return;
+  }
+  if (t < Tl - 1)
+    gB = exp(c.a + (double)c.lb + c.bt - logP);
+  else
+    gB = (u == Ul) ? exp(c.a + (double)c.lb - logP) : 0.0;
+  gE = (u < Ul) ? exp(c.a + (double)c.le + c.bu - logP) : 0.0;
+}
 __device__ __forceinline__ void cell_posteriors(const Dims& d, const double* __restrict__ alpha,
                                                 const double* __restrict__ beta,
                                                 const float* __restrict__ LB,
                                                 const float* __restrict__ LE, double logP,
                                                 int b, int t, int u, int Tl, int Ul,
                                                 double& gB, double& gE, int crit) {
-  const size_t ix = skew_idx(d, b, t, u);
-  if (crit == kCritMax) {  // 0/1 indicators of the best alignment's steps
-    const double m = beta[ix];
-    gB = m == kPathBlank ? 1.0 : 0.0;
-    gE = m == kPathLabel ? 1.0 : 0.0;
-    return;
-  }
-  const double a = alpha[ix];
-  if (t < Tl - 1)
-    gB = exp(a + (double)LB[ix] + beta[skew_idx(d, b, t + 1, u)] - logP);
-  else
-    gB = (u == Ul) ? exp(a + (double)LB[ix] - logP) : 0.0;
-  gE = (u < Ul) ? exp(a + (double)LE[ix] + beta[skew_idx(d, b, t, u + 1)] - logP) : 0.0;
+  cell_post_eval(cell_post_load(d, alpha, beta, LB, LE, b, t, u, Tl, Ul, crit), logP, t, u, Tl,
+                 Ul, gB, gE, crit);
 }
 
 }  // namespace rnntj

@@ -339,6 +339,20 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     wait_vmem();  // this wave's exponential rows (and slice part) have landed
     __syncthreads();
   }
+  // kGrad: the inputs of row tid's posteriors, loaded now and used after
+  // the h build (which hides their latency)
+  const int prw = tid >> 5, prr = tid & 31;
+  const int pt = t0 + 4 * prw + (prr >> 3), pu = u0 + (prr & 7);
+  const bool prow = MODE == kGrad && tid < kTileCells && pt < Tl && pu <= Ul;
+  CellPostIn pin{0.0, 0.0, 0.0, 0.0, 0.f, 0.f};
+  float plse = 0.f;
+  double plogP = 0.0, pg = 1.0;
+  if (prow) {
+    pin = cell_post_load(d, a.alpha, a.beta, a.LB, a.LE, b, pt, pu, Tl, Ul, a.hdr[3]);
+    plse = a.lse[skew_idx(d, b, pt, pu)];
+    plogP = a.logP[b];
+    pg = a.gcost ? (double)a.gcost[b] : 1.0;
+  }
 
   Frag8<T> hA[KS];
   {
@@ -390,17 +404,6 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     } else {
       build_h_direct(hA, b, tv, uv, valid);
     }
-    if constexpr (MODE == kGrad) {
-      // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H]);
-      // every row of the tile is written (zero outside the lattice)
-      if (vr == 0) {
-        T* hrow = static_cast<T*>(a.hout) +
-                  (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          if (EXACT || ks < nks) store_frag(hrow + ks * 16, hA[ks]);
-      }
-    }
   }
   // labels of this lane's accumulator rows: u = u0 + 4*kh + j
   int lab[4];
@@ -420,18 +423,14 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   float cst[16];  // kGrad, NBLK == 4: per-row exponent offsets (NBLK == 2 reads row_c)
   if constexpr (MODE == kGrad) {
     if (tid < kTileCells) {
-      const int rw = tid >> 5, rr = tid & 31;
-      const int t = t0 + 4 * rw + (rr >> 3), u = u0 + (rr & 7);
       float c = kInf, gb = 0.f, ge = 0.f;
-      if (t < Tl && u <= Ul) {
-        const double g = a.gcost ? (double)a.gcost[b] : 1.0;
+      if (prow) {
         double gB, gE;
-        cell_posteriors(d, a.alpha, a.beta, a.LB, a.LE, a.logP[b], b, t, u, Tl, Ul, gB, gE, a.hdr[3]);
+        cell_post_eval(pin, plogP, pt, pu, Tl, Ul, gB, gE, a.hdr[3]);
         const double occ = gB + gE;
-        const double lse = (double)a.lse[skew_idx(d, b, t, u)];
-        c = occ > 0.0 ? (float)((lse - log(occ)) * 1.4426950408889634) : kInf;
-        gb = (float)(g * gB);
-        ge = (float)(g * gE);
+        c = occ > 0.0 ? (float)(((double)plse - log(occ)) * 1.4426950408889634) : kInf;
+        gb = (float)(pg * gB);
+        ge = (float)(pg * gE);
       }
       row_c[tid] = c;
       row_b[tid] = gb;
@@ -446,6 +445,20 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     int nb, nt0, nu0;
     item_tile(item + gridDim.x, nb, nt0, nu0);
     issue_ep(nb, nt0, nu0);
+  }
+  if constexpr (MODE == kGrad) {
+    // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H]);
+    // every row of the tile is written (zero outside the lattice).  Issued
+    // after the barrier, so the first slice's MFMAs cover their completion
+    // instead of the barrier waiting for it.
+    if (vr == 0) {
+      const int t = t0 + 4 * w + (lc >> 3), u = u0 + (lc & 7);
+      T* hrow = static_cast<T*>(a.hout) +
+                (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        if (EXACT || ks < nks) store_frag(hrow + ks * 16, hA[ks]);
+    }
   }
   if constexpr (MODE == kGrad) {
 #pragma unroll
