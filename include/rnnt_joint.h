@@ -197,13 +197,15 @@ int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error)
  * `dy` of rnnt_joint_proj_bwd.
  *
  * rnnt_joint_proj_fwd: y[M,N] = x[M,K] @ W[K,N] + b[N].  x, W, b, y device
- * pointers of `dtype` (row-major, contiguous); products accumulate in fp32
- * and y is rounded once to dtype.  For enc: M = B*T, K = E (input width),
+ * pointers of `dtype` (row-major, contiguous; b may be NULL for no bias);
+ * products accumulate in fp32 and y is rounded once to dtype.  y must not
+ * overlap x, W or b.  For enc: M = B*T, K = E (input width),
  * N = H; for pred: M = B*(U+1), K = P, N = H.
  *
  * rnnt_joint_proj_bwd: from dy[M,N] (float32) writes dx[M,K] = dy @ W^T,
  * dW[K,N] = x^T @ dy and db[N] = sum of the rows of dy, all float32 and
- * overwritten (dx may be NULL to skip it).  x and W as in the forward.
+ * overwritten (dx and db may be NULL to skip them).  x and W as in the
+ * forward; the outputs must not overlap each other or the inputs.
  *
  * Both: x, W, y / dy, dx, dW 16-byte aligned; K and N multiples of 16 and at
  * most 65536, M >= 1 (else RNNTJ_ERR_UNSUPPORTED / RNNTJ_ERR_ARG, returned

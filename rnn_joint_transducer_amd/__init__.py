@@ -204,6 +204,7 @@ def rnnt_joint_loss(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0, ti
 # ---------------------------------------------------------------- joint input projections
 
 def _check_linear(x, W, b=None):
+    """Shapes (M, K, N) of y = x @ W + b; b may be None."""
     import torch
     if not (x.is_cuda and W.is_cuda) or x.dtype != W.dtype or (b is not None and b.dtype != x.dtype):
         raise TypeError("x, W (and b) must be device tensors of one dtype")
@@ -216,9 +217,9 @@ def _check_linear(x, W, b=None):
     return M, W.shape[0], W.shape[1]
 
 
-def rnnt_joint_proj_fwd(x, W, b):
-    """Joint input projection y = x @ W + b (x [..., K], W [K, N], b [N], one
-    dtype; fp32 accumulation, y rounded once to that dtype)."""
+def rnnt_joint_proj_fwd(x, W, b=None):
+    """Joint input projection y = x @ W + b (x [..., K], W [K, N], b [N] or
+    None, one dtype; fp32 accumulation, y rounded once to that dtype)."""
     import torch
     M, K, N = _check_linear(x, W, b)
     y = torch.empty(*x.shape[:-1], N, dtype=x.dtype, device=x.device)
@@ -227,9 +228,9 @@ def rnnt_joint_proj_fwd(x, W, b):
     return y
 
 
-def rnnt_joint_proj_bwd(x, W, dy, need_dx=True):
+def rnnt_joint_proj_bwd(x, W, dy, need_dx=True, need_db=True):
     """Gradients of y = x @ W + b from dy [..., N] (float32): (dx or None,
-    dW, db), all float32."""
+    dW, db or None), all float32."""
     import torch
     M, K, N = _check_linear(x, W)
     if dy.dtype != torch.float32 or not dy.is_contiguous() or dy.shape != (*x.shape[:-1], N):
@@ -237,7 +238,7 @@ def rnnt_joint_proj_bwd(x, W, dy, need_dx=True):
     dev = x.device
     dx = torch.empty(x.shape, dtype=torch.float32, device=dev) if need_dx else None
     dW = torch.empty(K, N, dtype=torch.float32, device=dev)
-    db = torch.empty(N, dtype=torch.float32, device=dev)
+    db = torch.empty(N, dtype=torch.float32, device=dev) if need_db else None
     check(load().rnnt_joint_proj_bwd(_ptr(x), _ptr(W), _dtype_code(x), M, K, N, _ptr(dy), _ptr(dx),
                                      _ptr(dW), _ptr(db), _stream(dev)), "rnnt_joint_proj_bwd")
     return dx, dW, db

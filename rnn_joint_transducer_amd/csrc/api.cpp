@@ -489,7 +489,7 @@ const char* rnnt_joint_loss_last_error(void) { return g_last_error; }
 
 int rnnt_joint_proj_fwd(const void* x, const void* W, const void* b, int dtype, int M, int K,
                         int N, void* y, void* stream) {
-  if (!x || !W || !b || !y || M < 1 || K < 1 || N < 1) return RNNTJ_ERR_ARG;
+  if (!x || !W || !y || M < 1 || K < 1 || N < 1) return RNNTJ_ERR_ARG;
   if (dtype != RNNTJ_F32 && dtype != RNNTJ_BF16) return RNNTJ_ERR_ARG;
   if (misaligned(x) || misaligned(W) || misaligned(y)) return RNNTJ_ERR_ARG;
   if (K % 16 != 0 || N % 16 != 0 || K > kMaxProj || N > kMaxProj) return RNNTJ_ERR_UNSUPPORTED;
@@ -503,15 +503,15 @@ int rnnt_joint_proj_fwd(const void* x, const void* W, const void* b, int dtype, 
 
 int rnnt_joint_proj_bwd(const void* x, const void* W, int dtype, int M, int K, int N,
                         const float* dy, float* dx, float* dW, float* db, void* stream) {
-  if (!x || !W || !dy || !dW || !db || M < 1 || K < 1 || N < 1) return RNNTJ_ERR_ARG;
+  if (!x || !W || !dy || !dW || M < 1 || K < 1 || N < 1) return RNNTJ_ERR_ARG;
   if (dtype != RNNTJ_F32 && dtype != RNNTJ_BF16) return RNNTJ_ERR_ARG;
   if (misaligned(x) || misaligned(W) || misaligned(dy) || misaligned(dx) || misaligned(dW))
     return RNNTJ_ERR_ARG;
   if (K % 16 != 0 || N % 16 != 0 || K > kMaxProj || N > kMaxProj) return RNNTJ_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = dtype == RNNTJ_BF16;
-  if (timed("zero", st, [&] { return launch_zero4(dW, (size_t)K * N, db, N, nullptr, 0, nullptr,
-                                                  0, st); }) != hipSuccess)
+  if (timed("zero", st, [&] { return launch_zero4(dW, (size_t)K * N, db, db ? N : 0, nullptr, 0,
+                                                  nullptr, 0, st); }) != hipSuccess)
     return RNNTJ_ERR_HIP;
   if (dx && timed("proj_dx", st, [&] { return launch_proj_dx(dy, W, bf16, M, K, N, dx, st); }) !=
                 hipSuccess)

@@ -156,7 +156,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int kh = lane >> 5, col = j0 + wj + (lane & 31);
   if (col >= g.N) return;
   float bias = 0.f;
-  if constexpr (OUT == 2) bias = ElemTraits<TO>::to_f32(static_cast<const TO*>(g.bias)[col]);
+  if constexpr (OUT == 2)
+    if (g.bias) bias = ElemTraits<TO>::to_f32(static_cast<const TO*>(g.bias)[col]);
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = i0 + wi + acc_row(r, kh);

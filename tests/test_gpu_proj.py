@@ -104,7 +104,7 @@ def test_projected_chain_small(dtype, tiles):
 
 def test_projected_chain_medium_subbatch():
     """Two utterances of the medium workload at its full sizes (bf16, H = E =
-    P = 640, V = 1024, tiled 64 x 64 x 256 as benchmarked)."""
+    P = 640, V = 1024, tiled 64 x 64 x 256)."""
     full = make_config("medium")
     idx = [3, 11]
     inp = make_inputs(2, full.T, full.U, full.H, full.V, dtype=full.dtype, sigma=0.05, seed=0)
@@ -165,3 +165,22 @@ def test_projection_autograd_matches_explicit_calls():
                     ("pred_in", "dPred"), ("W_pred", "dW_pred"), ("b_pred", "db_pred")):
         np.testing.assert_allclose(_np(t[k].grad), g[name], rtol=1e-6, atol=1e-7, err_msg=k)
     np.testing.assert_allclose(_np(W_out.grad), g["dW"], rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_projection_without_bias_and_skipped_outputs(dtype):
+    """b = NULL is a projection without bias; dx and db may be skipped."""
+    import rnn_joint_transducer_amd as rj
+    from synth import _cast
+    rng = np.random.default_rng(91)
+    M, K, N = 300, 32, 48
+    x_s, x64 = _cast(rng.normal(0, 0.5, (M, K)), dtype)
+    W_s, W64 = _cast(rng.normal(0, 0.2, (K, N)), dtype)
+    dy = rng.normal(0, 1.0, (M, N)).astype(np.float32)
+    y = _np(rj.rnnt_joint_proj_fwd(_dev(x_s, dtype), _dev(W_s, dtype), None))
+    _check_act("y", y, proj.linear(x64, W64, np.zeros(N)), dtype)
+    dx, dW, db = rj.rnnt_joint_proj_bwd(_dev(x_s, dtype), _dev(W_s, dtype), _dev(dy, "fp32"),
+                                        need_dx=False, need_db=False)
+    assert dx is None and db is None
+    _, rdW, _ = proj.linear_grads(x64, W64, dy.astype(np.float64))
+    assert float(np.max(np.abs(_np(dW) - rdW))) <= FP32_GRAD_ABS
