@@ -408,9 +408,11 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
     h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad;
     h.tiles = a.tiles;
     h.tile_count = a.tile_count;
+    h.hout = p.bf16 ? nullptr : hchunk;  // fp32: dh also writes the h rows dW reads
     if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    if ((e = timed("hrow", st, [&] { return launch_hrow(hchunk, p.bf16, a, st); })) != hipSuccess)
+    if (p.bf16 &&
+        (e = timed("hrow", st, [&] { return launch_hrow(hchunk, p.bf16, a, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
     w.g = z;
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;

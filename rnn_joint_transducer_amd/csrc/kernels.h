@@ -102,9 +102,6 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
 hipError_t launch_backtrace(const int32_t* Teff, const int32_t* Ueff, const Dims& d, double* beta,
                             hipStream_t st);
 
-// Untiled backward: h rows of every cell into h [B, Tpad, U1pad, H].
-hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st);
-
 
 // dh = dz @ W_out^T for the active tiles of one chunk; dpre = (1 - h^2) dh
 // summed into d_enc over u and into d_pred over t.
@@ -130,9 +127,16 @@ struct DhArgs {
   int ksplit;                 // vocabulary parts per (tile, hidden block); divides the slice count
   float* d_enc;
   float* d_pred;
+  void* hout;                 // untiled fp32: h rows [B, Tpad, U1pad, H] of the active tiles
+                              // for the weight gradient (zero outside the lattice), or null
 };
 // Persistent launch; max_tiles bounds the entries of the tile list.
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st);
+
+// Untiled bf16 backward: h rows of every cell into h [B, Tpad, U1pad, H] (the
+// fp32 dh writes them itself; in bf16 the extra stores do not fit beside two
+// workgroups per compute unit).
+hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st);
 
 // Untiled backward: the stored logits [B, Tpad, U1pad, V] of the active tiles
 // become the logit gradients (same type), rows outside the lattice zero; a.hdr
