@@ -395,3 +395,40 @@ def test_max_zero_weights_closed_form_medium():
                                                 inp.labels[b], inp.b_f64, inp.blank)
             for b in range(inp.B)]
     check_costs(g["costs"], want, inp.dtype)
+
+
+# ------------------------------------------------------------------ maximum sizes
+
+@pytest.mark.parametrize("case", ["U_max", "V_max", "H_max_bf16", "B_max", "T_max"])
+def test_maximum_sizes(case):
+    """Each size limit the library accepts, with the other sizes small enough
+    for the oracle: U + 1 = 512 (both criteria), V = 262144, H = 768 in bf16,
+    B = 8191, T = 65520.  Every output is compared.  The largest-B and
+    longest-T cases weight their costs by 1e-3 and 1e-4: unweighted, d_b_out
+    sums to ~1.1e4 over 8191 utterances (half an fp32 ulp there is 4.9e-4)
+    and d_W_out to ~40 over 65520 frames, beyond what an fp32 value can hold
+    to the 1e-4 absolute bound; a wrong gradient still misses it by far."""
+    gcs = None
+    runs = [((0, 0, 0), "sum"), ((16, 8, 0), "sum")]
+    if case == "U_max":
+        inp = make_inputs(2, 24, 511, 64, 40, sigma=0.2, seed=101)
+        inp.U_lens = np.array([511, 300], dtype=np.int32)
+        runs += [((0, 0, 0), "max"), ((64, 64, 128), "max")]
+    elif case == "V_max":
+        inp = make_inputs(2, 5, 2, 32, 262144, sigma=0.2, seed=102)
+    elif case == "H_max_bf16":
+        inp = make_inputs(2, 20, 6, 768, 96, dtype="bf16", sigma=0.05, seed=103)
+    elif case == "B_max":
+        inp = make_inputs(8191, 2, 1, 16, 16, sigma=0.3, seed=104, t_range=(1, 2), u_range=(0, 1))
+        gcs = [1e-3] * inp.B
+    else:
+        inp = make_inputs(1, 65520, 0, 16, 8, sigma=0.3, seed=105)
+        gcs = [1e-4]
+    refs = {}
+    for tiles, crit in runs:
+        print(f"[maximum size {case} tiles={tiles} criterion={crit}]", flush=True)
+        g = run_gpu(inp, *tiles, grad_costs=gcs, criterion=crit)
+        assert g["status"] == 0
+        if crit not in refs:
+            refs[crit] = _oracle_full(inp, grad_costs=gcs, criterion=crit)
+        _compare_all(inp, g, refs[crit])
