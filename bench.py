@@ -106,7 +106,8 @@ def calibrate_copy(nbytes):
 def cpu_baseline(inp, target_s, criterion="sum", pj=None):
     """Float64 oracle (fwd+bwd, one utterance at a time, NumPy BLAS on all host
     threads) on a bounded sample of the workload: whole utterances in order
-    until about target_s seconds are spent, or the first utterance cut to its
+    until about target_s seconds are spent (whole passes over the batch
+    repeated while a pass takes less), or the first utterance cut to its
     first t_s frames when even one utterance would take longer (t_s from a
     4-frame pilot).  Scaled to B*T*U cells/s of the whole workload by the
     ratio of valid lattice cells."""
@@ -143,14 +144,25 @@ def cpu_baseline(inp, target_s, criterion="sum", pj=None):
         sample_cells = t_s * (Ul0 + 1)
         desc = f"utterance 0 (T'={Tl0}, U'={Ul0}) cut to its first {t_s} frames"
     else:
-        el, sample_cells, nb = 0.0, 0, 0
-        for b in range(inp.B):
-            el += run(b, int(inp.T_lens[b]))
-            sample_cells += int(inp.T_lens[b]) * (int(inp.U_lens[b]) + 1)
-            nb += 1
-            if el >= target_s:
-                break
-        desc = f"utterances 0..{nb - 1} of {inp.B} in full"
+        el, sample_cells, nb, full, extra = 0.0, 0, 0, 0, 0
+        while el < target_s:
+            done = 0
+            for b in range(inp.B):
+                el += run(b, int(inp.T_lens[b]))
+                sample_cells += int(inp.T_lens[b]) * (int(inp.U_lens[b]) + 1)
+                nb = max(nb, b + 1)
+                done += 1
+                if el >= target_s:
+                    break
+            if done == inp.B:
+                full += 1
+            else:
+                extra = done
+        if full == 0:
+            desc = f"utterances 0..{nb - 1} of {inp.B} in full"
+        else:
+            desc = f"{full} full pass{'es' if full > 1 else ''} over all {inp.B} utterances" + (
+                f" and utterances 0..{extra - 1} once more" if extra else "")
     total_valid = int(np.sum(inp.T_lens.astype(np.int64) * (inp.U_lens.astype(np.int64) + 1)))
     full_time = el * total_valid / sample_cells
     value = inp.B * inp.T * inp.U / full_time
