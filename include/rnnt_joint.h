@@ -41,9 +41,10 @@
  *     the whole axis.  tile_t must be a multiple of 16 and tile_u of 8.
  *     tile_v bounds the vocabulary columns of one step of the online max /
  *     log-sum-exp (which never materialises more than one step of logits per
- *     cell): 0 or any multiple of 128.  The kernels step by 128 columns, which
- *     is within every accepted bound, so tile_v changes neither memory nor
- *     results (the order of the floating-point sums is the same).
+ *     cell): 0 or any multiple of 128.  The kernels step by 128 columns (64
+ *     for bf16 with H <= 256), which is within every accepted bound, so tile_v
+ *     changes neither memory nor results (the order of the floating-point sums
+ *     is the same).
  *   - Limits (else RNNTJ_ERR_UNSUPPORTED): H a multiple of 16 with
  *     16 <= H <= 768 for bf16 and H <= 256 for fp32; V a multiple of 8,
  *     8 <= V <= 262144; U + 1 <= 512; B <= 8191; T <= 65520.
