@@ -15,11 +15,15 @@
 // (t-1,u), 2: label from (t,u-1)), and a read-back from (T'-1,U') then marks
 // the best alignment's steps there (kPathBlank / kPathLabel).
 //
-// One wave64 per (utterance, direction): cells of one anti-diagonal t+u are
-// independent, so the wave sweeps the T'+U' anti-diagonals with the label
-// positions spread over the lanes.  State is float64 (the posteriors later
-// take exp(alpha + beta - logP) of numbers of size ~1e4); the logaddexp
-// correction log(1 + e^-|x-y|) lies in [0, ln 2] and is evaluated in float32.
+// Cells of one anti-diagonal t+u are independent, so one wave sweeps the
+// T'+U' anti-diagonals of an (utterance, direction) with the label positions
+// spread over its lanes, while three more waves of its workgroup feed it the
+// step weights and store its results.  State is float64, kept in base-2
+// units inside the sweep (the posteriors later take exp(alpha + beta - logP)
+// of numbers of size ~1e4); the log-add-exp correction log2(1 + 2^-|x-y|)
+// lies in [0, 1] and is evaluated in float32.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -29,49 +33,65 @@ namespace {
 
 constexpr double kNegInfD = -__builtin_inf();
 
-// log(e^x + e^y) without branches: the max plus a float32 correction
-// log(1 + e^-|x-y|) in [0, ln 2].  (-inf, -inf) gives -inf; a NaN operand
-// gives NaN (comparisons, not fmax, pick hi / lo).
-__device__ __forceinline__ double log_add_exp(double x, double y) {
-  const bool xg = x > y;
-  const double hi = xg ? x : y;
-  const double lo = xg ? y : x;
-  const float dl = (float)(lo - hi);
-  const float c = __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(dl * kLog2e)) * kLn2;
-  const double r = hi + (double)c;
-  return (hi == kNegInfD && lo == kNegInfD) ? kNegInfD : r;
-}
+constexpr double kLog2eD = 1.4426950408889634, kLn2D = 0.6931471805599453;
 
 // Cross-lane shift of a float64 by one lane (DPP wave shifts): shr moves
-// lane l-1's value to lane l (lane 0 receives `fill`), shl moves lane l+1's
-// value to lane l (lane 63 receives `fill`).
-__device__ __forceinline__ double wave_shr1(double v, double fill) {
-  const long long x = __double_as_longlong(v), f = __double_as_longlong(fill);
-  const int lo = __builtin_amdgcn_update_dpp((int)f, (int)x, 0x138, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp((int)(f >> 32), (int)(x >> 32), 0x138, 0xf, 0xf, false);
+// lane l-1's value to lane l, shl lane l+1's to lane l; the lane without a
+// source (0, resp. 63) receives 0.0.
+__device__ __forceinline__ double wave_shr1z(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)x, 0x138, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(x >> 32), 0x138, 0xf, 0xf, true);
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
-__device__ __forceinline__ double wave_shl1(double v, double fill) {
-  const long long x = __double_as_longlong(v), f = __double_as_longlong(fill);
-  const int lo = __builtin_amdgcn_update_dpp((int)f, (int)x, 0x130, 0xf, 0xf, false);
-  const int hi = __builtin_amdgcn_update_dpp((int)(f >> 32), (int)(x >> 32), 0x130, 0xf, 0xf, false);
+__device__ __forceinline__ double wave_shl1z(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)x, 0x130, 0xf, 0xf, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(x >> 32), 0x130, 0xf, 0xf, true);
   return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
 }
 
-// Lane l owns the NU consecutive label positions u = NU*l .. NU*l + NU-1, so
-// on each anti-diagonal the u-1 (alpha) or u+1 (beta) neighbour is in the
-// same lane except at the block edge, which one DPP lane shift supplies.
-// One wave per (utterance, direction); DIR = 0 sweeps alpha forward over the
-// diagonals, DIR = 1 beta backward, DIR = 2 the max-plus alpha (maximum
-// approximation) with its predecessor decisions.  The diagonals are taken in chunks of CH:
-// the LB / LE operands of the next chunk are loaded into registers while this
-// chunk is computed, and the chunk's results are stored at its end.  Every
-// load and store is issued unconditionally (clamped loads; results of slots
-// outside the lattice go to a per-lane trash slot past the array), so the
-// number of memory operations in flight is the same on every path and the
-// compiler's waits only cover what each step really needs.
+// One workgroup of four waves per (utterance, direction); lane l owns the NU
+// consecutive label positions u = NU*l .. NU*l + NU-1, so on each
+// anti-diagonal the u-1 (alpha) or u+1 (beta) neighbour is in the same lane
+// except at the lane edge, which one DPP lane shift supplies.  The
+// anti-diagonals go in chunks of CH, and the waves split the work of a chunk
+// so that the recursion wave runs nothing but the recursion itself:
+//   wave 0   the recursion (two LDS reads, two adds, one log-add-exp and one
+//            LDS write per cell),
+//   wave 1/2 the step weights of the next chunk: the blank / label
+//            log-probabilities loaded, scaled to base 2 and replaced by the
+//            finite sentinel kSent wherever the step does not exist,
+//   wave 3   the previous chunk's results, scaled back to natural logs and
+//            stored (cells outside the lattice are not written).
+// With finite sentinels every value the recursion meets is finite unless an
+// input is NaN or infinite, so the log-add-exp needs no guard against
+// -inf - -inf: an impossible step adds kSent = -1e300, whose correction
+// term rounds to exactly 0, and values near kSent (at most about 7e4 of them
+// summed) mark unreachable cells, which are stored as -inf.  The maximum
+// approximation (DIR = 2) runs the same scheme with max in place of
+// log-add-exp and also hands the predecessor decisions to wave 3.
+constexpr double kSent = -1e300;
+constexpr double kSentCut = -1e299;  // below: unreachable (-inf)
+
+template <int NU, int CH>
+struct LatLds {
+  double w[2][2][CH][NU][64];  // [buffer][blank, label][step][slot][lane]
+  double r[2][CH][NU][64];     // results (base 2)
+  unsigned char dec[2][CH][NU][64];
+};
+
+// log2(2^x + 2^y) = max + log2(1 + 2^-|x-y|), the correction in float32.
+// A NaN operand makes x - y, and so the result, NaN.
+__device__ __forceinline__ double lse2_step(double x, double y) {
+  const double m = __builtin_fmax(x, y);
+  const float e = (float)(-__builtin_fabs(x - y));
+  const float c = __builtin_amdgcn_logf(1.0f + __builtin_amdgcn_exp2f(e));
+  return m + (double)c;
+}
+
 template <int DIR, int NU, int CH>
-__device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
+__device__ __forceinline__ void lattice_sweep(LatLds<NU, CH>& sm, const float* __restrict__ LB,
                                               const float* __restrict__ LE,
                                               const int32_t* __restrict__ Teff,
                                               const int32_t* __restrict__ Ueff, const Dims& d,
@@ -79,158 +99,196 @@ __device__ __forceinline__ void lattice_sweep(const float* __restrict__ LB,
                                               double* __restrict__ beta,
                                               double* __restrict__ logP,
                                               float* __restrict__ costs) {
-  const int b = blockIdx.x, l = threadIdx.x;
+  const int b = blockIdx.x, tid = threadIdx.x, l = tid & 63, w = tid >> 6;
   const int Tl = Teff[b], Ul = Ueff[b];
-  if (Tl == 0) {  // invalid utterance
-    if (DIR == 0 && l == 0) {
+  if (Tl == 0) {  // invalid utterance (uniform over the workgroup)
+    if (DIR != 1 && tid == 0) {
       costs[b] = __builtin_nanf("");
       logP[b] = __builtin_nan("");
     }
     return;
   }
+  constexpr bool kFwd = DIR != 1;
   const int nd = Tl + Ul;  // number of anti-diagonals of this lattice
+  const int nch = (nd + CH - 1) / CH;
   const size_t base = (size_t)b * d.DG * d.U1;
   const float* lb = LB + base;
   const float* le = LE + base;
+  const int last = d.DG * d.U1 - 1;  // clamp for the loads
+  // diagonal of step s
+  auto diag = [&](int s) { return kFwd ? s : nd - 1 - s; };
+
+  // waves 1 (K = 0, blank) and 2 (K = 1, label): raw operands of chunk k
+  // (clamped, so always in bounds):
+  //   alpha: LB(t-1,u), LE(t,u-1) on diagonal dg-1;  beta: LB(t,u), LE(t,u) on dg
+  auto load_raw = [&](auto kind, int k, float (&r)[CH][NU]) {
+    constexpr int K = decltype(kind)::value;
+    const float* src = K ? le : lb;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int dg = diag(k * CH + c);
+      const int i0 = (kFwd ? dg - 1 : dg) * d.U1 - ((kFwd && K) ? 1 : 0);
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        const int i = min(max(i0 + NU * l + j, 0), last);
+        r[c][j] = src[(unsigned)i];
+      }
+    }
+  };
+  // ... and the weights they give, into LDS buffer k & 1
+  auto convert = [&](auto kind, int k, const float (&r)[CH][NU]) {
+    constexpr int K = decltype(kind)::value;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int dg = diag(k * CH + c);
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        const int u = NU * l + j;
+        const int t = dg - u;
+        bool ex;
+        if (kFwd)
+          ex = K ? ((unsigned)t < (unsigned)Tl && u >= 1 && u <= Ul)  // (t,u-1) -> (t,u)
+                 : ((unsigned)(t - 1) < (unsigned)(Tl - 1) && u <= Ul);  // (t-1,u) -> (t,u)
+        else
+          ex = K ? ((unsigned)t < (unsigned)Tl && u < Ul)  // (t,u) -> (t,u+1)
+                 : (u <= Ul && ((unsigned)t < (unsigned)(Tl - 1) || (t == Tl - 1 && u == Ul)));
+        double v = (double)r[c][j] * kLog2eD;
+        v = (ex && !(v < kSent)) ? v : kSent;
+        // alpha(0,0) = 0: a zero blank weight from the virtual alpha(-1,0) = 0
+        if (kFwd && !K && c == 0)
+          if (k == 0) v = u == 0 ? 0.0 : v;
+        sm.w[k & 1][K][c][j][l] = v;
+      }
+    }
+  };
+
+  // wave 0: the previous diagonal, in base 2.  It starts as a virtual
+  // diagonal with one zero: alpha(-1, 0) (alpha), beta(T', U') behind the
+  // final blank (beta).
+  double prev[NU];
+#pragma unroll
+  for (int j = 0; j < NU; ++j) {
+    const int u = NU * l + j;
+    prev[j] = (DIR == 1 ? u == Ul : u == 0) ? 0.0 : kSent;
+  }
+  auto recurse = [&](int k) {
+    const int q = k & 1;
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      // the lane edge gets 0.0: the step from there never exists, so its
+      // weight is kSent
+      const double edge = kFwd ? wave_shr1z(prev[NU - 1]) : wave_shl1z(prev[0]);
+      double res[NU];
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        const double nbv = kFwd ? (j > 0 ? prev[j > 0 ? j - 1 : 0] : edge)
+                                : (j + 1 < NU ? prev[j + 1 < NU ? j + 1 : 0] : edge);
+        const double ft = prev[j] + sm.w[q][0][c][j][l];
+        const double fu = nbv + sm.w[q][1][c][j][l];
+        if constexpr (DIR == 2) {
+          // best predecessor, blank on equal scores; a NaN operand stays NaN
+          const bool pick_t = ft >= fu;
+          double v = pick_t ? ft : fu;
+          res[j] = (ft != ft || fu != fu) ? ft + fu : v;
+          sm.dec[q][c][j][l] = pick_t ? 1 : 2;
+        } else {
+          res[j] = lse2_step(ft, fu);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NU; ++j) {
+        prev[j] = res[j];
+        sm.r[q][c][j][l] = res[j];
+      }
+    }
+  };
+
+  // wave 3: store chunk k (natural logs; unreachable cells -inf; slots
+  // outside the lattice go to a per-lane trash slot past the array) and, on
+  // the last alpha diagonal, logP = alpha(T'-1,U') + LB(T'-1,U')
   double* arr = DIR == 1 ? beta : alpha;
   double* out = arr + base;
   double* trash = arr + (size_t)d.B * d.DG * d.U1 + NU * l;
-  double* dec_out = beta + base;  // DIR == 2: predecessor decisions
+  double* dec_out = beta + base;
   double* dec_trash = beta + (size_t)d.B * d.DG * d.U1 + NU * l;
-  const int last = d.DG * d.U1 - 1;  // clamp for the loads
-
-  double prev[NU];
-#pragma unroll
-  for (int j = 0; j < NU; ++j) prev[j] = kNegInfD;
-
-  // operands of step s for slot j (diagonal dg = s for alpha, nd-1-s for beta):
-  //   alpha: LB(t-1,u), LE(t,u-1) on diagonal dg-1;  beta: LB(t,u), LE(t,u) on dg
-  constexpr bool kFwd = DIR != 1;
-  float cb[CH][NU], ce[CH][NU], nb[CH][NU], ne[CH][NU];
-  auto fetch = [&](int s0, float (&fb)[CH][NU], float (&fe)[CH][NU]) {
+  auto fin = [](double v) { return v < kSentCut ? kNegInfD : v; };
+  auto store = [&](int k) {
+    const int q = k & 1;
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int dg = kFwd ? s0 + c - 1 : nd - 1 - s0 - c;
+      const int dg = diag(k * CH + c);
 #pragma unroll
       for (int j = 0; j < NU; ++j) {
         const int u = NU * l + j;
-        int ib = dg * d.U1 + u, ie = kFwd ? ib - 1 : ib;
-        ib = ib < 0 ? 0 : (ib > last ? last : ib);
-        ie = ie < 0 ? 0 : (ie > last ? last : ie);
-        fb[c][j] = lb[ib];
-        fe[c][j] = le[ie];
+        const bool valid = (unsigned)(dg - u) < (unsigned)Tl && u <= Ul;
+        const size_t o = (size_t)dg * d.U1 + u;
+        *(valid ? out + o : trash + j) = fin(sm.r[q][c][j][l]) * kLn2D;
+        if constexpr (DIR == 2) *(valid ? dec_out + o : dec_trash + j) = (double)sm.dec[q][c][j][l];
       }
+    }
+    if (kFwd && (nd - 1) / CH == k && l == Ul / NU) {
+      const double lp =
+          (fin(sm.r[q][nd - 1 - k * CH][Ul % NU][l]) +
+           (double)lb[(size_t)(nd - 1) * d.U1 + Ul] * kLog2eD) * kLn2D;
+      logP[b] = lp;
+      costs[b] = (float)(-lp);
     }
   };
 
-  // one chunk: steps s0 .. s0+CH-1 from (ub, ue) while the next chunk's
-  // operands load into (fb, fe)
-  auto chunk = [&](int s0, const float (&ub)[CH][NU], const float (&ue)[CH][NU],
-                   float (&fb)[CH][NU], float (&fe)[CH][NU]) {
-    // next chunk's operands (loads past the lattice are clamped and unused),
-    // kept issued here, ahead of this chunk's steps
-    fetch(s0 + CH, fb, fe);
-    __builtin_amdgcn_sched_barrier(0);
-    double res[CH][NU];
-    double dec[CH][NU];  // DIR == 2 only
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int s = s0 + c;
-      const int dg = kFwd ? s : nd - 1 - s;
-      // neighbour on the previous diagonal across the lane edge
-      const double edge =
-          kFwd ? wave_shr1(prev[NU - 1], kNegInfD) : wave_shl1(prev[0], kNegInfD);
-#pragma unroll
-      for (int j = 0; j < NU; ++j) {
-        const int u = NU * l + j;
-        const int t = dg - u;
-        const bool valid = (s < nd) & (u <= Ul) & (t >= 0) & (t < Tl);
-        double v;
-        if (DIR == 0 || DIR == 2) {
-          // alpha(t-1,u) + LB(t-1,u),  alpha(t,u-1) + LE(t,u-1)
-          const double nbv = j > 0 ? prev[j > 0 ? j - 1 : 0] : edge;
-          const double ft = (t >= 1) ? prev[j] + (double)ub[c][j] : kNegInfD;
-          const double fu = (u >= 1) ? nbv + (double)ue[c][j] : kNegInfD;
-          if constexpr (DIR == 0) {
-            v = log_add_exp(ft, fu);
-          } else {
-            // best predecessor, blank on equal scores; a NaN operand stays NaN
-            const bool pick_t = ft >= fu;
-            v = pick_t ? ft : fu;
-            v = (ft != ft || fu != fu) ? ft + fu : v;
-            dec[c][j] = pick_t ? 1.0 : 2.0;
-          }
-          v = (dg == 0) ? 0.0 : v;
-        } else {
-          // beta(t+1,u) + LB(t,u),  beta(t,u+1) + LE(t,u)
-          const double nbv = j + 1 < NU ? prev[j + 1 < NU ? j + 1 : 0] : edge;
-          const double ft = (t + 1 < Tl) ? prev[j] + (double)ub[c][j] : kNegInfD;
-          const double fu = (u < Ul) ? nbv + (double)ue[c][j] : kNegInfD;
-          v = log_add_exp(ft, fu);
-          v = (t == Tl - 1 && u == Ul) ? (double)ub[c][j] : v;
-        }
-        res[c][j] = valid ? v : kNegInfD;
-      }
-      // the diagonal is complete: it becomes the previous one
-#pragma unroll
-      for (int j = 0; j < NU; ++j) prev[j] = res[c][j];
-      if (kFwd && s == nd - 1) {
-        // final cell (T'-1, U') lies on the last diagonal
-#pragma unroll
-        for (int j = 0; j < NU; ++j) {
-          if (NU * l + j == Ul) {
-            const double lp = prev[j] + (double)lb[(size_t)dg * d.U1 + Ul];
-            logP[b] = lp;
-            costs[b] = (float)(-lp);
-          }
-        }
-      }
-    }
-    // store the chunk (slots outside the lattice go to the trash slot)
-#pragma unroll
-    for (int c = 0; c < CH; ++c) {
-      const int s = s0 + c;
-      const int dg = kFwd ? s : nd - 1 - s;
-#pragma unroll
-      for (int j = 0; j < NU; ++j) {
-        const int u = NU * l + j;
-        const int t = dg - u;
-        const bool valid = (s < nd) & (u <= Ul) & (t >= 0) & (t < Tl);
-        double* dst = valid ? out + (size_t)dg * d.U1 + u : trash + j;
-        *dst = res[c][j];
-        if constexpr (DIR == 2) {
-          double* dd = valid ? dec_out + (size_t)dg * d.U1 + u : dec_trash + j;
-          *dd = dec[c][j];
-        }
-      }
-    }
+  // pipeline: in iteration i wave 0 runs chunk i, waves 1/2 prepare chunk
+  // i+1 (loaded in iteration i-1) and load chunk i+2, wave 3 stores chunk
+  // i-1; the raw operand registers alternate (no copies)
+  using Blank = std::integral_constant<int, 0>;
+  using Label = std::integral_constant<int, 1>;
+  float ra[CH][NU], rb[CH][NU];
+  auto prologue = [&](auto kind) {
+    load_raw(kind, 0, ra);
+    if (nch > 1) load_raw(kind, 1, rb);
+    convert(kind, 0, ra);
   };
-
-  // chunks alternate between the two operand buffers (no register copies)
-  fetch(0, cb, ce);
-  for (int s0 = 0; s0 < nd; s0 += 2 * CH) {
-    chunk(s0, cb, ce, nb, ne);
-    if (s0 + CH < nd) chunk(s0 + CH, nb, ne, cb, ce);  // uniform
+  auto produce = [&](auto kind, int i, const float (&cur)[CH][NU], float (&nxt)[CH][NU]) {
+    if (i + 2 < nch) load_raw(kind, i + 2, nxt);
+    if (i + 1 < nch) convert(kind, i + 1, cur);
+  };
+  if (w == 1) prologue(Blank{});
+  if (w == 2) prologue(Label{});
+  __syncthreads();
+  auto iter = [&](int i, const float (&cur)[CH][NU], float (&nxt)[CH][NU]) {
+    if (w == 0) {
+      if (i < nch) recurse(i);
+    } else if (w == 1) {
+      produce(Blank{}, i, cur, nxt);
+    } else if (w == 2) {
+      produce(Label{}, i, cur, nxt);
+    } else if (i >= 1) {
+      store(i - 1);
+    }
+    __syncthreads();
+  };
+  for (int i = 0; i <= nch; i += 2) {
+    iter(i, rb, ra);
+    if (i + 1 <= nch) iter(i + 1, ra, rb);  // uniform
   }
 }
 
 // both directions of every utterance in one launch: blockIdx.y = direction
 // (full sum); the maximum approximation runs its one forward sweep
 template <int NU, int CH, bool MAXA>
-__global__ __launch_bounds__(64) void lattice_kernel(const float* __restrict__ LB,
-                                                     const float* __restrict__ LE,
-                                                     const int32_t* __restrict__ Teff,
-                                                     const int32_t* __restrict__ Ueff, Dims d,
-                                                     double* __restrict__ alpha,
-                                                     double* __restrict__ beta,
-                                                     double* __restrict__ logP,
-                                                     float* __restrict__ costs) {
+__global__ __launch_bounds__(256) void lattice_kernel(const float* __restrict__ LB,
+                                                      const float* __restrict__ LE,
+                                                      const int32_t* __restrict__ Teff,
+                                                      const int32_t* __restrict__ Ueff, Dims d,
+                                                      double* __restrict__ alpha,
+                                                      double* __restrict__ beta,
+                                                      double* __restrict__ logP,
+                                                      float* __restrict__ costs) {
+  __shared__ LatLds<NU, CH> sm;
   if constexpr (MAXA)
-    lattice_sweep<2, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
+    lattice_sweep<2, NU, CH>(sm, LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
   else if (blockIdx.y == 0)
-    lattice_sweep<0, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
+    lattice_sweep<0, NU, CH>(sm, LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
   else
-    lattice_sweep<1, NU, CH>(LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
+    lattice_sweep<1, NU, CH>(sm, LB, LE, Teff, Ueff, d, alpha, beta, logP, costs);
 }
 
 // Maximum approximation: read the best alignment back from (T'-1, U') over
@@ -522,9 +580,8 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
                           double* logP, float* costs, int crit, hipStream_t st) {
   const int nu = (d.U1 + 63) / 64;
   const bool maxa = crit == kCritMax;
-  dim3 grid(d.B, maxa ? 1 : 2), block(64);
-  // chunk length: 2 loads + 1 store per slot and step (max: 2 stores) stay
-  // within the 63 memory operations the wave can track
+  dim3 grid(d.B, maxa ? 1 : 2), block(256);
+  // chunk length: about 16 cells per lane and chunk (48 KiB of LDS)
 #define RNNTJ_LAT(N, CH)                                                                   \
   case N:                                                                                  \
     if (maxa)                                                                              \
@@ -537,11 +594,11 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
   switch (nu) {
     RNNTJ_LAT(1, 16)
     RNNTJ_LAT(2, 8)
-    RNNTJ_LAT(3, 6)
+    RNNTJ_LAT(3, 5)
     RNNTJ_LAT(4, 4)
-    RNNTJ_LAT(5, 4)
+    RNNTJ_LAT(5, 3)
     RNNTJ_LAT(6, 3)
-    RNNTJ_LAT(7, 3)
+    RNNTJ_LAT(7, 2)
     RNNTJ_LAT(8, 2)
     default:
       return hipErrorInvalidValue;
