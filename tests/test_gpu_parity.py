@@ -134,6 +134,30 @@ def test_data_errors_flagged():
     check_grad("d_W_out", g["dW"], ref["dW"], "fp32")
 
 
+@pytest.mark.parametrize("criterion", ["sum", "max"])
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
+def test_nan_input_stays_in_its_utterance(criterion, tiles):
+    """A NaN in one utterance's encodings makes that utterance's cost NaN and
+    leaves every other cost and encoder / prediction gradient as the oracle
+    computes it without that utterance: the lattice carries NaN through its
+    log-add-exp (or max) steps but never into another utterance, and no
+    finite cell of the NaN utterance turns a neighbour's result into a
+    sentinel or -inf."""
+    inp = make_inputs(4, 24, 6, 32, 40, sigma=0.4, seed=23, t_range=(10, 24), u_range=(2, 6))
+    inp.enc[1, 3, 5] = np.nan
+    print(f"[nan input {criterion} tiles={tiles}]", flush=True)
+    g = run_gpu(inp, *tiles, criterion=criterion)
+    assert g["status"] == 0
+    assert math.isnan(g["costs"][1])
+    sub = [0, 2, 3]
+    ref = oracle.loss_and_grads(inp.enc_f64[sub], inp.pred_f64[sub], inp.W_f64, inp.b_f64,
+                                inp.labels[sub], inp.T_lens[sub], inp.U_lens[sub], 0,
+                                criterion=criterion)
+    check_costs(g["costs"], ref["costs"], "fp32", idx=sub)
+    check_grad("d_enc", g["dEnc"][sub], ref["dEnc"], "fp32")
+    check_grad("d_pred", g["dPred"][sub], ref["dPred"], "fp32")
+
+
 def test_tile_invariance_short():
     inp = make_config("short")
     base = run_gpu(inp, 0, 0, 0)
