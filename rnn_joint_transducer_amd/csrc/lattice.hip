@@ -64,9 +64,10 @@ __device__ __forceinline__ double wave_shl1z(double v) {
 //            finite sentinel kSent wherever the step does not exist,
 //   wave 3   the previous chunk's results, scaled back to natural logs and
 //            stored (cells outside the lattice are not written).
-// With finite sentinels every value the recursion meets is finite unless an
-// input is NaN or infinite, so the log-add-exp needs no guard against
-// -inf - -inf: an impossible step adds kSent = -1e300, whose correction
+// With finite sentinels (a weight of -inf is raised to kSent as well) every
+// value the recursion meets is finite unless an input is NaN, so the
+// log-add-exp needs no guard against -inf - -inf: an impossible step adds
+// kSent = -1e300, whose correction
 // term rounds to exactly 0, and values near kSent (at most about 7e4 of them
 // summed) mark unreachable cells, which are stored as -inf.  The maximum
 // approximation (DIR = 2) runs the same scheme with max in place of
