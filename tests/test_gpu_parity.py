@@ -158,6 +158,23 @@ def test_nan_input_stays_in_its_utterance(criterion, tiles):
     check_grad("d_pred", g["dPred"][sub], ref["dPred"], "fp32")
 
 
+@pytest.mark.parametrize("criterion", ["sum", "max"])
+@pytest.mark.parametrize("U1", [64, 65, 129, 192, 193, 256, 320, 321, 385, 448, 449, 512])
+def test_lattice_label_blocking(U1, criterion):
+    """Every label-position blocking of the lattice sweep (1 to 8 positions
+    per lane, each with its own chunk length), at and just past each block
+    boundary, with label counts up to the padded maximum: every output
+    against the oracle."""
+    U = U1 - 1
+    inp = make_inputs(2, 12, U, 32, 64, sigma=0.3, seed=U1, t_range=(5, 12),
+                      u_range=(max(0, U - 70), U))
+    inp.U_lens[0] = U
+    print(f"[lattice blocking U+1={U1} {criterion} U'={list(inp.U_lens)}]", flush=True)
+    g = run_gpu(inp, criterion=criterion)
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp, criterion=criterion))
+
+
 def test_tile_invariance_short():
     inp = make_config("short")
     base = run_gpu(inp, 0, 0, 0)
