@@ -16,15 +16,15 @@
 //   dh_kernel          : MFMA GEMM dz[cells, V] x W_out^T -> [cells, H] per
 //                        active 16x8 tile and 256 hidden columns, with the
 //                        (1 - h^2) epilogue and the two lattice reductions
-//                        done in registers before float32 atomics; in the
-//                        untiled fp32 mode the h values of that epilogue are
-//                        also written out as the h rows dw reads.
+//                        done in registers before float32 atomics.
 //   dw_kernel          : MFMA GEMM h^T[H, cells] x dz[cells, V] split over
 //                        runs of the tile list (split-K); h and dz cell rows
 //                        are read as MFMA operands with transposing LDS
 //                        loads; the hidden-block-0 workgroups also sum dz
 //                        columns into db_out (float64).
-//   hrow_kernel        : untiled bf16 mode, h = tanh(enc + pred) rows for dw.
+//   hrow_kernel        : untiled bf16 mode, h = tanh(enc + pred) rows for dw
+//                        (in the untiled fp32 mode the forward joint kernel
+//                        keeps them).
 #include <type_traits>
 
 #include "common.h"
@@ -189,7 +189,7 @@ __device__ __forceinline__ int slot_of(int r, int c) {
 // else is in flight.
 __device__ __forceinline__ void touch(float x) { asm volatile("" ::"v"(x)); }
 
-template <typename T, bool WH>
+template <typename T>
 __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   using C = DhCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
@@ -395,8 +395,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   // (d_pred) in registers, then added with float32 atomics.  With `wh` (the
   // item's vocabulary part 0 in the untiled mode) the h values it evaluates
   // are also the weight gradient's h rows, stored as they are formed.
-  auto epilogue = [&](const Item& it, bool wh) {  // wh only in WH launches
-    T* hrow = static_cast<T*>(a.hout);
+  auto epilogue = [&](const Item& it) {
     float psum[4][4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -420,9 +419,6 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
                                    ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + ex[i][q4][j] * px[q][j])
                                    : fast_tanh(ex[i][q4][j] + px[q][j]);
             const float v = (tv && u <= it.Ul) ? (1.0f - hval * hval) * acc[i][j][4 * q4 + q] : 0.f;
-            if (WH && wh && nvalid)
-              hrow[(((size_t)it.b * d.Tpad + t) * d.U1pad + u) * H + n] =
-                  ElemTraits<T>::from_f32((tv && u <= it.Ul) ? hval : 0.f);
             esum += v;
             psum[j][q] += v;
             acc[i][j][4 * q4 + q] = 0.f;
@@ -529,7 +525,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
       slice(li * nks + s, last);
     }
     if constexpr (C::OCC > 1) load_ep(decode(cur));
-    epilogue(decode(cur), WH && cur.kp == 0);
+    epilogue(decode(cur));
     cur = cur_next;
     if (li + 2 < my_items) cur_next = item_ref(li + 2);
   }
@@ -890,14 +886,8 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
   if (items <= 0) return hipSuccess;
   const long long g8 = (items + 7) / 8 * 8;
   dim3 grid((unsigned)(g8 < gmax ? g8 : gmax)), block(256);
-  // WH: the untiled mode, where dh also writes the h rows
-  if (bf16) {
-    if (b.hout) return hipErrorInvalidValue;  // no room for the h-row stores (see launch_hrow)
-    hipLaunchKernelGGL((dh_kernel<uint16_t, false>), grid, block, 0, st, b);
-  } else {
-    if (b.hout) hipLaunchKernelGGL((dh_kernel<float, true>), grid, block, 0, st, b);
-    else hipLaunchKernelGGL((dh_kernel<float, false>), grid, block, 0, st, b);
-  }
+  if (bf16) hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, b);
+  else hipLaunchKernelGGL(dh_kernel<float>, grid, block, 0, st, b);
   return hipGetLastError();
 }
 

@@ -446,12 +446,13 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     item_tile(item + gridDim.x, nb, nt0, nu0);
     issue_ep(nb, nt0, nu0);
   }
-  if constexpr (MODE == kGrad) {
+  if constexpr (MODE == kGrad || (MODE == kStoreZ && !kBf16)) {
     // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H]);
     // every row of the tile is written (zero outside the lattice).  Issued
     // after the barrier, so the first slice's MFMAs cover their completion
-    // instead of the barrier waiting for it.
-    if (vr == 0) {
+    // instead of the barrier waiting for it.  (Untiled fp32 forward: the h
+    // rows of the whole padded lattice, kept for the backward.)
+    if (vr == 0 && (MODE == kGrad || a.hout != nullptr)) {
       const int t = t0 + 4 * w + (lc >> 3), u = u0 + (lc & 7);
       T* hrow = static_cast<T*>(a.hout) +
                 (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;

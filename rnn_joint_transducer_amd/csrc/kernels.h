@@ -64,7 +64,8 @@ struct JointArgs {
   const double* logP;
   const float* gcost;  // [B] or null
   void* gout;          // kGrad: logit gradients [B, CT, CU, V]
-  void* hout;          // kGrad: joint activations h [B, CT, CU, H]
+  void* hout;          // kGrad: joint activations h [B, CT, CU, H]; kStoreZ (fp32): the
+                       // h rows [B, Tpad, U1pad, H] of the active tiles, or null
 };
 
 // Persistent launch: `n_items` = (maximum number of active tiles) * vsplit
@@ -127,8 +128,6 @@ struct DhArgs {
   int ksplit;                 // vocabulary parts per (tile, hidden block); divides the slice count
   float* d_enc;
   float* d_pred;
-  void* hout;                 // untiled fp32: h rows [B, Tpad, U1pad, H] of the active tiles
-                              // for the weight gradient (zero outside the lattice), or null
 };
 // Persistent launch; max_tiles bounds the entries of the tile list.
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st);
