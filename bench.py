@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload short]
                     [--tile-t T --tile-u U --tile-v V] [--no-cpu-baseline]
+    python bench.py --sweep --workload medium --steps 3 --warmup 1
 
 One step = one forward + one backward over a whole synthetic batch (every
 kernel of the path: validation, W_out transpose, fused joint + projection +
@@ -36,8 +37,11 @@ PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
 MFMA_KERNELS = ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
 PROJ_KERNELS = ("proj_fwd", "proj_dx", "proj_dw")
-DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (64, 64, 128),
-                 "medium_lv": (64, 64, 256), "long": (64, 64, 256)}
+# Tiled defaults: medium and medium_lv take the lowest-memory tiling within
+# 95 % of the best tiled throughput of a full tile sweep (`--sweep`;
+# medium_lv at its tile_v = 256); long keeps its configured 64 x 64 chunks.
+DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (128, 0, 256),
+                 "medium_lv": (32, 0, 256), "long": (64, 64, 256)}
 
 
 def parse():
@@ -58,6 +62,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the tile grid (tile_t, tile_u in 16, 32, 64, 128, 0; tile_v in "
+                         "128, 256, 512, 0) instead of one configuration and print the "
+                         "throughput-memory frontier")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device-to-device copies of BYTES bytes (the "
                          "reference kernel for scaling FETCH_SIZE / WRITE_SIZE counters)")
@@ -172,6 +180,79 @@ def cpu_baseline(inp, target_s, criterion="sum", pj=None):
                       f"valid cells ({total_valid}) to the B*T*U metric"}
 
 
+def tile_sweep(args, rj, torch, tensors, inp, dev, dc):
+    """Throughput and memory over the tile grid: tile_t, tile_u in {16, 32, 64,
+    128, 0} (0: the whole axis; both 0: the untiled mode) and tile_v in {128,
+    256, 512, 0}.  Memory is the peak allocated above the inputs in one
+    fwd+bwd (saved state, workspace, costs and gradients).  Prints one JSON
+    line: every configuration, the throughput-memory frontier (no other
+    configuration is both faster and smaller), and per mode the
+    lowest-memory configuration within 95 % of that mode's best throughput."""
+    B, T, U, H, V = inp.B, inp.T, inp.U, inp.H, inp.V
+    costs = torch.empty(B, dtype=torch.float32, device=dev)
+    grads = (torch.empty(B, T, H, device=dev), torch.empty(B, U + 1, H, device=dev),
+             torch.empty(H, V, device=dev), torch.empty(V, device=dev))
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated(dev) - sum(
+        t.numel() * t.element_size() for t in (costs, *grads))
+    rows = []
+    for tt in (16, 32, 64, 128, 0):
+        for tu in (16, 32, 64, 128, 0):
+            for tv in (128, 256, 512, 0):
+                torch.cuda.synchronize()
+                torch.cuda.reset_peak_memory_stats(dev)
+                saved = torch.empty(rj.rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tt, tu, tv),
+                                    dtype=torch.uint8, device=dev)
+                ws = torch.empty(rj.rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tt, tu,
+                                                                     tv, 1),
+                                 dtype=torch.uint8, device=dev)
+
+                def step():
+                    rj.rnnt_joint_loss_fwd(**tensors, tile_t=tt, tile_u=tu, tile_v=tv,
+                                           costs=costs, saved=saved)
+                    rj.rnnt_joint_loss_bwd(**tensors, saved=saved, tile_t=tt, tile_u=tu,
+                                           tile_v=tv, workspace=ws, out=grads)
+
+                for _ in range(max(1, args.warmup)):
+                    step()
+                torch.cuda.synchronize()
+                gb = (torch.cuda.max_memory_allocated(dev) - base) / 1e9
+                status = rj.rnnt_joint_loss_status(saved)
+                ev0 = torch.cuda.Event(enable_timing=True)
+                ev1 = torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                for _ in range(args.steps):
+                    step()
+                ev1.record()
+                torch.cuda.synchronize()
+                ms = ev0.elapsed_time(ev1) / args.steps
+                mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
+                rows.append({"mode": mode, "tile_t": tt, "tile_u": tu, "tile_v": tv,
+                             "ms_per_step": round(ms, 4),
+                             "cells_per_s": B * T * U / (ms / 1e3), "gb_above_inputs": round(gb, 4),
+                             "status": status})
+                print(f"# sweep {mode:7s} tile_t={tt:3d} tile_u={tu:3d} tile_v={tv:3d}: "
+                      f"{ms:9.3f} ms/step, {gb:7.3f} GB above inputs, status {status}",
+                      file=sys.stderr, flush=True)
+                del saved, ws
+
+    def dominated(r):
+        return any(o["ms_per_step"] <= r["ms_per_step"] and o["gb_above_inputs"] <= r["gb_above_inputs"]
+                   and (o["ms_per_step"] < r["ms_per_step"] or o["gb_above_inputs"] < r["gb_above_inputs"])
+                   for o in rows)
+
+    frontier = sorted((r for r in rows if not dominated(r)), key=lambda r: r["gb_above_inputs"])
+    pick = {}
+    for mode in ("untiled", "tiled"):
+        rs = [r for r in rows if r["mode"] == mode and r["status"] == 0]
+        best = min(r["ms_per_step"] for r in rs)
+        pick[mode] = min((r for r in rs if best / r["ms_per_step"] >= 0.95),
+                         key=lambda r: (r["gb_above_inputs"], r["ms_per_step"]))
+    print(json.dumps({"metric": METRIC, "workload": args.workload, "steps": args.steps,
+                      "warmup": max(1, args.warmup), "data": "synthetic", "sweep": rows,
+                      "frontier": frontier, "lowest_memory_within_95pct": pick}), flush=True)
+
+
 def main():
     args = parse()
     if args.calibrate_copy:
@@ -216,6 +297,9 @@ def main():
         ptens = dict(enc_in=conv(pj.enc_in), pred_in=conv(pj.pred_in), W_enc=conv(pj.W_enc),
                      b_enc=conv(pj.b_enc), W_pred=conv(pj.W_pred), b_pred=conv(pj.b_pred))
     dc = rj.RNNTJ_BF16 if bf16 else rj.RNNTJ_F32
+    if args.sweep:
+        tile_sweep(args, rj, torch, tensors, inp, dev, dc)
+        return
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     base_mem = torch.cuda.memory_allocated(dev)

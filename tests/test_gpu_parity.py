@@ -296,7 +296,7 @@ def _sub_batch_weights(inp, tiles, utts):
     check_grad("d_b_out(sub)", g["db"], ref["db"], inp.dtype)
 
 
-@pytest.mark.parametrize("tiles", [(64, 64, 0), (0, 0, 0)])
+@pytest.mark.parametrize("tiles", [(64, 64, 0), (0, 0, 0), (128, 0, 256)])
 def test_medium(tiles):
     inp = make_config("medium")
     print(f"[medium tiles={tiles}]", flush=True)
@@ -304,10 +304,11 @@ def test_medium(tiles):
     _sub_batch_weights(inp, tiles, [3, 11])
 
 
-def test_medium_large_vocab():
+@pytest.mark.parametrize("tiles", [(64, 64, 256), (32, 0, 256)])
+def test_medium_large_vocab(tiles):
     inp = make_config("medium_lv")
-    print("[medium_lv]", flush=True)
-    _sampled(inp, (64, 64, 256), cost_utts=[2, 9], grad_utts=[9])
+    print(f"[medium_lv tiles={tiles}]", flush=True)
+    _sampled(inp, tiles, cost_utts=[2, 9], grad_utts=[9])
 
 
 def test_long_tiled():
