@@ -392,9 +392,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
     }
   };
   // dpre = (1 - h^2) dh, reduced over label positions (d_enc) and frames
-  // (d_pred) in registers, then added with float32 atomics.  With `wh` (the
-  // item's vocabulary part 0 in the untiled mode) the h values it evaluates
-  // are also the weight gradient's h rows, stored as they are formed.
+  // (d_pred) in registers, then added with float32 atomics.
   auto epilogue = [&](const Item& it) {
     float psum[4][4];
 #pragma unroll

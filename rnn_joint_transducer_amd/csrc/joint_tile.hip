@@ -11,7 +11,8 @@
 //   kLse    : running sum of exp(z) carried across vocabulary tiles (with a
 //             running max unless every |z| is provably below 64); at the end
 //             lse, LB = z[blank] - lse, LE = z[label] - lse.
-//   kStoreZ : kLse plus the logits written to HBM (untiled mode).
+//   kStoreZ : kLse plus the logits written to HBM (untiled mode); in float32
+//             also the h rows the weight gradient reads.
 //   kGrad   : logit gradient of the loss (tiled backward), from the per-cell
 //             transition posteriors gB, gE and the stored lse:
 //             dz[v] = gc * (occ * exp(z[v] - lse) - gB [v=blank] - gE [v=y_u]),
