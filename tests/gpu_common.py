@@ -4,7 +4,7 @@ from __future__ import annotations
 
 import numpy as np
 
-# the benchmark spec tolerances: fp32 |dloss|/loss <= 1e-5 and grad abs err <= 1e-4;
+# Parity bar: fp32 |dloss|/loss <= 1e-5 and grad abs err <= 1e-4;
 # bf16 2e-2 relative (loss per utterance, gradients as max-abs error over the
 # tensor's max-abs value).
 FP32_LOSS_REL = 1e-5
