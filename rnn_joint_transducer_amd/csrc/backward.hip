@@ -193,6 +193,7 @@ template <typename T>
 __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   using C = DhCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
+  __shared__ __align__(16) float xch[2 * 64 * 16];  // d_pred partial sums of wave row 1
   const Dims d = a.d;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -427,14 +428,35 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
         }
       }
     }
+    // the two wave rows hold the d_pred sums of the tile's two frame halves
+    // for the same (u, n): row 1 hands its sums over through LDS and row 0
+    // adds both to memory, half the atomics.  The second barrier keeps the
+    // next item's hand-over from overwriting sums row 0 has not read yet.
+    f32x4* xw = reinterpret_cast<f32x4*>(xch + (wn * 64 + lane) * 16);
+    if (wm == 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = it.n0 + 128 * wn + 32 * j + lc;
-      if (n < H) {
+      for (int j = 0; j < 4; ++j) xw[j] = f32x4{psum[j][0], psum[j][1], psum[j][2], psum[j][3]};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wm == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int u = it.u0 + 4 * kh + q;
-          if (u <= it.Ul) atomicAdd(&a.d_pred[((size_t)it.b * d.U1 + u) * H + n], psum[j][q]);
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 o = xw[j];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) psum[j][q] += o[q];
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (wm == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = it.n0 + 128 * wn + 32 * j + lc;
+        if (n < H) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int u = it.u0 + 4 * kh + q;
+            if (u <= it.Ul) atomicAdd(&a.d_pred[((size_t)it.b * d.U1 + u) * H + n], psum[j][q]);
+          }
         }
       }
     }
