@@ -406,6 +406,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
       const bool nvalid = n < H;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
+        float es[4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int t = it.t0 + 8 * wm + 4 * i + q4;
@@ -423,8 +424,20 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
             acc[i][j][4 * q4 + q] = 0.f;
           }
           // the other 4 label positions of this frame live in lane l ^ 32
-          esum += __shfl_xor(esum, 32);
-          if (kh == 0 && tv) atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], esum);
+          es[q4] = esum + __shfl_xor(esum, 32);
+          if (C::kBf16 && kh == 0 && tv)
+            atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], es[q4]);
+        }
+        // fp32: both lane halves hold every frame's sum, so each half adds
+        // one of two frames and one full-wave atomic covers two frames (in
+        // bf16 the extra registers this holds cost more than it saves)
+        if constexpr (!C::kBf16) {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const int t = it.t0 + 8 * wm + 4 * i + 2 * m + kh;
+            if (nvalid && t < it.Tl)
+              atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], kh ? es[2 * m + 1] : es[2 * m]);
+          }
         }
       }
     }
