@@ -108,8 +108,8 @@ const char* rnnt_joint_loss_last_error(void);
  * (diagonal-skewed [B, T+U, U+1]): lse, LB, LE (float32) and alpha, beta
  * (float64), and the list of active 16 x 8 cell tiles (int32, one word per
  * tile of the padded lattice).  In the untiled mode it also holds the logits
- * [B, ceil16(T), ceil8(U+1), V] in dtype and, for float32, the joint
- * activations h [B, ceil16(T), ceil8(U+1), H] of the active tiles.
+ * [B, ceil16(T), ceil8(U+1), V] in dtype and the joint activations h
+ * [B, ceil16(T), ceil8(U+1), H] of the active tiles in dtype.
  * Writes *out; returns a status code.
  */
 int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
@@ -118,10 +118,9 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
 /*
  * Bytes of scratch `workspace` needed by the forward (pass = 0) or the
  * backward (pass = 1).  The forward needs none.  The backward needs a float64
- * accumulator for d_b_out [V], the joint activations h of one lattice chunk
- * [B, tile_t, tile_u, H] in dtype (untiled bfloat16: the whole padded
- * lattice; untiled float32: none, they are in `saved`) and, in the tiled
- * mode, that chunk's logit gradients [B, tile_t, tile_u, V]
+ * accumulator for d_b_out [V] and, in the tiled mode, the joint activations
+ * h of one lattice chunk [B, tile_t, tile_u, H] in dtype (untiled: none,
+ * they are in `saved`), that chunk's logit gradients [B, tile_t, tile_u, V]
  * in dtype plus the active-tile list of every chunk (int32, one word per
  * 16 x 8 tile).  Writes *out; returns a status code.
  */
@@ -134,8 +133,8 @@ int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype
  * backward needs, written into `saved` (rnnt_joint_loss_saved_bytes bytes,
  * caller-owned, contents overwritten).  enc/pred/W_out/b_out are read only.
  * Launch order on `stream`: length/label validation, W_out transpose, fused
- * joint + projection + online log-sum-exp (+ logit store when untiled, and
- * the h rows too for float32),
+ * joint + projection + online log-sum-exp (+ logit and h-row store when
+ * untiled),
  * alpha/beta lattice recursion.  Returns a status code (host-side checks and
  * launch errors only).
  */

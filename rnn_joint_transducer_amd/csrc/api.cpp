@@ -31,7 +31,7 @@ struct Plan {
   int CT, CU;  // backward chunk extents
   size_t elem;
   // saved layout (byte offsets)
-  size_t o_h;  // untiled fp32: h rows [B, Tpad, U1pad, H]
+  size_t o_h;  // untiled: h rows [B, Tpad, U1pad, H]
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
       o_tiles, o_tcount, o_z;
   size_t saved_bytes;
@@ -93,23 +93,22 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_tcount = o; o = align_up(o + 16);
   q.o_z = o;
   if (q.untiled) o = align_up(o + q.elem * (size_t)B * q.d.Tpad * q.d.U1pad * V);
-  // untiled fp32: the forward keeps the h rows of the padded lattice for dW
+  // untiled: the forward keeps the h rows of the padded lattice for dW
   q.o_h = o;
-  if (q.untiled && !bf16) o = align_up(o + 4 * (size_t)B * q.d.Tpad * q.d.U1pad * H);
+  if (q.untiled) o = align_up(o + q.elem * (size_t)B * q.d.Tpad * q.d.U1pad * H);
   q.saved_bytes = o;
   q.ws_fwd = 0;
   // backward workspace: float64 d_b_out accumulator [V], then (tiled) one
   // chunk of logit gradients [B, CT, CU, V] and its joint activations h
-  // [B, CT, CU, H] (untiled bf16: h of the whole padded lattice; untiled
-  // fp32: none, the forward keeps them)
+  // [B, CT, CU, H] (untiled: none, the forward keeps h)
   q.n_cu_chunks = (q.d.U1pad + q.CU - 1) / q.CU;
   q.n_chunks = ((q.d.Tpad + q.CT - 1) / q.CT) * q.n_cu_chunks;
   q.cap_chunk = B * (q.CT / kTileT) * (q.CU / kTileU);
   q.o_ws_db = 0;
   q.o_ws_g = align_up(8 * (size_t)V);
   q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
-  // (untiled fp32: the h rows are part of the saved state instead)
-  q.o_ws_tiles = q.o_ws_h + ((q.untiled && !bf16) ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * H));
+  // (untiled: the h rows are part of the saved state instead)
+  q.o_ws_tiles = q.o_ws_h + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * H));
   q.o_ws_tcount = q.o_ws_tiles + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks * q.cap_chunk));
   q.ws_bwd = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
   return RNNTJ_OK;
@@ -294,7 +293,7 @@ int rnnt_joint_loss_fwd_ex(const void* enc, const void* pred, const void* W_out,
   a.LB = LB;
   a.LE = LE;
   a.zout = p.untiled ? at<char>(saved, p.o_z) : nullptr;
-  a.hout = (p.untiled && !p.bf16) ? at<char>(saved, p.o_h) : nullptr;
+  a.hout = p.untiled ? at<char>(saved, p.o_h) : nullptr;
   if ((e = timed(p.untiled ? "joint_fwd_store" : "joint_fwd", st, [&] {
          return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, p.cap_all, st);
        })) != hipSuccess)
@@ -416,11 +415,8 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
     h.tile_count = a.tile_count;
     if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    if (p.bf16 &&
-        (e = timed("hrow", st, [&] { return launch_hrow(hchunk, p.bf16, a, st); })) != hipSuccess)
-      return RNNTJ_ERR_HIP;
     w.g = z;
-    if (!p.bf16) w.h = at<char>(saved, p.o_h);  // written by the forward
+    w.h = at<char>(saved, p.o_h);  // written by the forward
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
     w.tiles = a.tiles;
     w.tile_count = a.tile_count;

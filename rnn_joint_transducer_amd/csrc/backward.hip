@@ -22,9 +22,6 @@
 //                        are read as MFMA operands with transposing LDS
 //                        loads; the hidden-block-0 workgroups also sum dz
 //                        columns into db_out (float64).
-//   hrow_kernel        : untiled bf16 mode, h = tanh(enc + pred) rows for dw
-//                        (in the untiled fp32 mode the forward joint kernel
-//                        keeps them).
 #include <type_traits>
 
 #include "common.h"
@@ -822,47 +819,6 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
   }
 }
 
-// h rows of every valid cell of the lattice ([B, Tpad, U1pad, H], untiled
-// backward): h = tanh(enc[b,t] + pred[b,u]); rows of invalid cells are zero.
-template <typename T>
-__global__ __launch_bounds__(256) void hrow_kernel(JointArgs a, T* __restrict__ hout) {
-  const Dims d = a.d;
-  const int b = blockIdx.y;
-  const int n_tu = d.U1pad / kTileU;
-  const int t0 = (blockIdx.x / n_tu) * kTileT;
-  const int u0 = (blockIdx.x % n_tu) * kTileU;
-  const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  if (t0 >= Tl || u0 > Ul) return;
-  const T* enc = static_cast<const T*>(a.enc);
-  const T* pred = static_cast<const T*>(a.pred);
-  const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
-  const int cpr = d.H / 8;
-  for (int c = threadIdx.x; c < kTileCells * cpr; c += 256) {
-    const int row = c / cpr, k0 = (c % cpr) * 8;
-    const int t = t0 + (row >> 3), u = u0 + (row & 7);
-    T* hp = hout + (((size_t)b * d.Tpad + t) * d.U1pad + u) * d.H + k0;
-    Frag8<T> f;
-    if (t < Tl && u <= Ul) {
-      const size_t ie = ((size_t)b * d.T + t) * d.H + k0, ip = ((size_t)b * d.U1 + u) * d.H + k0;
-      float x[8];
-      if (use_ep) {
-        const Frag8<float> e = load_frag(a.Eexp + ie), p = load_frag(a.Pexp + ip);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          x[i] = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e.get(i) * p.get(i));
-      } else {
-        const Frag8<T> e = load_frag(enc + ie), p = load_frag(pred + ip);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = fast_tanh(e.get(i) + p.get(i));
-      }
-      pack_frag(f, x);
-    } else {
-      zero_frag(f);
-    }
-    store_frag(hp, f);
-  }
-}
-
 __global__ void db_finalize_kernel(const double* __restrict__ src, float* __restrict__ dst, int V,
                                    int32_t* mark) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
@@ -871,15 +827,6 @@ __global__ void db_finalize_kernel(const double* __restrict__ src, float* __rest
 }
 
 }  // namespace
-
-hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st) {
-  dim3 grid((a.d.Tpad / kTileT) * (a.d.U1pad / kTileU), a.d.B), block(256);
-  if (bf16)
-    hipLaunchKernelGGL(hrow_kernel<uint16_t>, grid, block, 0, st, a, static_cast<uint16_t*>(h));
-  else
-    hipLaunchKernelGGL(hrow_kernel<float>, grid, block, 0, st, a, static_cast<float*>(h));
-  return hipGetLastError();
-}
 
 hipError_t launch_db_finalize(const double* db64, float* d_b, int V, int32_t* mark, hipStream_t st) {
   hipLaunchKernelGGL(db_finalize_kernel, dim3((V + 255) / 256), dim3(256), 0, st, db64, d_b, V,

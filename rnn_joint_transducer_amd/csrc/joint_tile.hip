@@ -11,8 +11,8 @@
 //   kLse    : running sum of exp(z) carried across vocabulary tiles (with a
 //             running max unless every |z| is provably below 64); at the end
 //             lse, LB = z[blank] - lse, LE = z[label] - lse.
-//   kStoreZ : kLse plus the logits written to HBM (untiled mode); in float32
-//             also the h rows the weight gradient reads.
+//   kStoreZ : kLse plus the logits written to HBM (untiled mode), and the h
+//             rows the weight gradient reads.
 //   kGrad   : logit gradient of the loss (tiled backward), from the per-cell
 //             transition posteriors gB, gE and the stored lse:
 //             dz[v] = gc * (occ * exp(z[v] - lse) - gB [v=blank] - gE [v=y_u]),
@@ -447,12 +447,12 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     item_tile(item + gridDim.x, nb, nt0, nu0);
     issue_ep(nb, nt0, nu0);
   }
-  if constexpr (MODE == kGrad || (MODE == kStoreZ && !kBf16)) {
+  if constexpr (MODE == kGrad || MODE == kStoreZ) {
     // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H]);
     // every row of the tile is written (zero outside the lattice).  Issued
     // after the barrier, so the first slice's MFMAs cover their completion
-    // instead of the barrier waiting for it.  (Untiled fp32 forward: the h
-    // rows of the whole padded lattice, kept for the backward.)
+    // instead of the barrier waiting for it.  (Untiled forward: the h rows
+    // of the whole padded lattice, kept for the backward.)
     if (vr == 0 && (MODE == kGrad || a.hout != nullptr)) {
       const int t = t0 + 4 * w + (lc >> 3), u = u0 + (lc & 7);
       T* hrow = static_cast<T*>(a.hout) +

@@ -64,8 +64,8 @@ struct JointArgs {
   const double* logP;
   const float* gcost;  // [B] or null
   void* gout;          // kGrad: logit gradients [B, CT, CU, V]
-  void* hout;          // kGrad: joint activations h [B, CT, CU, H]; kStoreZ (fp32): the
-                       // h rows [B, Tpad, U1pad, H] of the active tiles, or null
+  void* hout;          // kGrad: joint activations h [B, CT, CU, H]; kStoreZ: the h rows
+                       // [B, Tpad, U1pad, H] of the active tiles, or null
 };
 
 // Persistent launch: `n_items` = (maximum number of active tiles) * vsplit
@@ -132,10 +132,6 @@ struct DhArgs {
 // Persistent launch; max_tiles bounds the entries of the tile list.
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st);
 
-// Untiled bf16 backward: h rows of every cell into h [B, Tpad, U1pad, H] (the
-// fp32 dh writes them itself; in bf16 the extra stores do not fit beside two
-// workgroups per compute unit).
-hipError_t launch_hrow(void* h, bool bf16, const JointArgs& a, hipStream_t st);
 
 // Untiled backward: the stored logits [B, Tpad, U1pad, V] of the active tiles
 // become the logit gradients (same type), rows outside the lattice zero; a.hdr
