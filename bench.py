@@ -1,6 +1,6 @@
 """Benchmark of the fused RNN-T joint + transducer loss (forward + backward).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload short]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long]
                     [--tile-t T --tile-u U --tile-v V] [--no-cpu-baseline]
     python bench.py --sweep --workload medium --steps 3 --warmup 1
 
@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="short",
+    ap.add_argument("--workload", default="long",
                     choices=["tiny", "short", "medium", "medium_lv", "long"])
     ap.add_argument("--criterion", default="sum", choices=["sum", "max"],
                     help="full sum over alignments, or the best alignment only")
@@ -126,6 +126,15 @@ def cpu_baseline(inp, target_s, criterion="sum", pj=None):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    cpu_model = "unknown"
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                cpu_model = ln.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
 
     def run(b, t_s):
         t0 = time.perf_counter()
@@ -175,6 +184,8 @@ def cpu_baseline(inp, target_s, criterion="sum", pj=None):
     full_time = el * total_valid / sample_cells
     value = inp.B * inp.T * inp.U / full_time
     return {"value": value, "unit": "cells/s", "cores": int(threads), "kind": "oracle",
+            "nproc": int(nproc or 1), "cpu_model": cpu_model,
+            "numpy": np.__version__,
             "sample": f"{desc}: {sample_cells} valid cells in {el:.2f} s, float64 NumPy "
                       f"fwd+bwd{'' if pj is None else ' with the input projections'}, scaled by "
                       f"valid cells ({total_valid}) to the B*T*U metric"}
@@ -331,20 +342,24 @@ def main():
     extra_gb = (torch.cuda.max_memory_allocated(dev) - base_mem) / 1e9
     status = rj.rnnt_joint_loss_status(saved)
 
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # one event between consecutive steps: the mean over the K steps gives
+    # ms_per_step and value, the per-step spans give the median and p10 / p90
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = ev0.elapsed_time(ev1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    spans = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    pct = lambda q: float(np.percentile(spans, q))
     value = B * T * U / (ms / 1e3)
-    print(f"# {args.workload}: {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}), "
-          f"{value:.4g} cells/s, peak {peak_gb:.2f} GB, status {status}", file=sys.stderr,
-          flush=True)
+    print(f"# {args.workload}: {ms:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}; median "
+          f"{pct(50):.3f}, p10 {pct(10):.3f}, p90 {pct(90):.3f}), {value:.4g} cells/s, "
+          f"peak {peak_gb:.2f} GB, status {status}", file=sys.stderr, flush=True)
 
     # per-kernel durations from HIP events recorded by the library on its stream
     _lib.timing(True)
@@ -390,6 +405,16 @@ def main():
 
     mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
     roof["traffic"] = measured_traffic(args.workload, dom, mode, args.criterion)
+    # the lattice pass against HBM peak (32 B per valid cell: the alpha and beta
+    # chains each read LB, LE and write one float64) and per anti-diagonal step
+    lat = None
+    if "lattice" in kernels:
+        kl = kernels["lattice"]
+        diags = int(np.max(inp.T_lens.astype(np.int64) + inp.U_lens))
+        gbs = 32.0 * valid / kl["launches_per_step"] / (kl["ms_per_launch"] / 1e3) / 1e9
+        lat = {"ms_per_launch": kl["ms_per_launch"], "gb_s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS,
+               "bytes_per_valid_cell": 32, "diagonals": diags,
+               "us_per_diagonal": kl["ms_per_launch"] * 1e3 / diags}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, args.cpu_seconds, args.criterion, pj)
@@ -399,12 +424,14 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dt,
         "data": "synthetic",
+        "ms_median": pct(50), "ms_p10": pct(10), "ms_p90": pct(90),
         "config": {"workload": args.workload, "B": B, "T": T, "U": U, "H": H, "V": V,
                    "mode": mode, "criterion": args.criterion,
                    "proj": None if pj is None else {"E": pj.E, "P": pj.P}, "tile_t": tt, "tile_u": tu, "tile_v": tv,
                    "valid_cells": valid, "valid_cells_per_s": valid / (ms / 1e3),
                    "peak_gb": round(peak_gb, 3), "peak_gb_above_inputs": round(extra_gb, 3)},
         "roofline": roof,
+        "lattice": lat,
         "kernels": {k: {kk: round(vv, 6) for kk, vv in v.items()} for k, v in kernels.items()},
         "cpu_baseline": cpu,
     }

@@ -34,7 +34,12 @@
  *     gradient are float32 whatever `dtype` is.
  *   - Modes: tile_t == 0 and tile_u == 0 selects the UNTILED mode: the forward
  *     stores the logits (dtype) in `saved` and the backward turns them into
- *     the logit gradients in place, so one forward feeds one backward.
+ *     the logit gradients in place, so one forward feeds one backward.  In
+ *     bf16 each row's logits are stored relative to the row's largest logit
+ *     within each vocabulary step of the forward kernel (64 or 128 columns),
+ *     with those offsets kept in float32: the rounding error of a stored
+ *     logit then moves its softmax entry by at most 2^-8 / e, whatever the
+ *     size of the logits.
  *     Otherwise the TILED mode stores only per-cell scalars and recomputes the
  *     joint and logits in the backward, one lattice chunk of tile_t frames x
  *     tile_u label positions (all utterances) at a time; 0 on one axis means
@@ -109,7 +114,11 @@ const char* rnnt_joint_loss_last_error(void);
  * (float64), and the list of active 16 x 8 cell tiles (int32, one word per
  * tile of the padded lattice).  In the untiled mode it also holds the logits
  * [B, ceil16(T), ceil8(U+1), V] in dtype and the joint activations h
- * [B, ceil16(T), ceil8(U+1), H] of the active tiles in dtype.
+ * [B, ceil16(T), ceil8(U+1), H] of the active tiles in dtype, and for bf16
+ * the float32 offsets of the stored logits (one per row and vocabulary step
+ * of 64 columns when H <= 256, else 128).  A 32-byte header records the
+ * status, the criterion and what a backward must match (sizes, dtype, blank,
+ * whether the logits are stored).
  * Writes *out; returns a status code.
  */
 int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
@@ -169,7 +178,12 @@ int rnnt_joint_loss_fwd_ex(const void* enc, const void* pred, const void* W_out,
  * forward may feed several backward calls.  Untiled mode: the stored logits
  * become the logit gradients in place and `saved` is marked consumed; a
  * second backward from it gives invalid gradients and sets data-error bit 4
- * (rnnt_joint_loss_status).  Entries of d_enc / d_pred past each utterance's
+ * (rnnt_joint_loss_status).  The backward checks on the device, before it
+ * reads anything but the header of `saved`, that the state comes from a
+ * forward with the same B, T, U, H, V, dtype and blank (and, for the untiled
+ * backward, one that stored the logits; a tiled backward accepts an untiled
+ * forward's state): otherwise it computes nothing, leaves the gradients zero
+ * and sets data-error bit 8.  Entries of d_enc / d_pred past each utterance's
  * lengths are zero.  Returns a status code (host-side checks and launch
  * errors only).
  */
@@ -185,7 +199,9 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,
  * Synchronises `stream`, then copies the data-error word of `saved` to
  * *data_error: 0 = every utterance valid, else a bit mask (1 = a length out of
  * range, 2 = a label out of range or equal to blank, 4 = an untiled backward
- * ran on a state whose logits an earlier backward had already consumed).
+ * ran on a state whose logits an earlier backward had already consumed, 8 = a
+ * backward was given a state whose sizes, dtype, blank or mode do not match
+ * its own arguments and computed nothing).
  * Returns a status code.
  */
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error);

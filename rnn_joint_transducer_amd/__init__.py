@@ -118,6 +118,11 @@ def rnnt_joint_loss_bwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, 
     B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
     dc = _dtype_code(enc)
     dev = enc.device
+    need = rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v)
+    if saved.dtype != torch.uint8 or saved.device != dev or saved.numel() < need:
+        raise ValueError(f"saved: expected a uint8 buffer of at least {need} bytes on {dev} "
+                         f"(the forward's state for these sizes and tiles), got "
+                         f"{saved.numel()} {saved.dtype} on {saved.device}")
     ws = rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, 1)
     if workspace is None:
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)

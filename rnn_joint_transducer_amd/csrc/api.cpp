@@ -34,6 +34,8 @@ struct Plan {
   size_t o_h;  // untiled: h rows [B, Tpad, U1pad, H]
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
       o_tiles, o_tcount, o_z;
+  size_t o_zm;  // untiled bf16: the per-(row, vocabulary step) logit offsets
+  int zstep;    // vocabulary columns per forward step (the offsets' granularity)
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
   size_t o_ws_db, o_ws_g, o_ws_h, o_ws_tiles, o_ws_tcount;  // backward workspace layout
@@ -74,7 +76,7 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.CU = q.untiled ? q.d.U1pad : (tile_u ? (tile_u < q.d.U1pad ? tile_u : q.d.U1pad) : q.d.U1pad);
   const size_t cells = (size_t)B * q.d.DG * q.d.U1;
   size_t o = 0;
-  q.o_status = o; o = align_up(o + 16);
+  q.o_status = o; o = align_up(o + 4 * kHdrWords);
   q.o_teff = o;   o = align_up(o + 4 * (size_t)B);
   q.o_ueff = o;   o = align_up(o + 4 * (size_t)B);
   q.o_logp = o;   o = align_up(o + 8 * (size_t)B);
@@ -96,6 +98,11 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   // untiled: the forward keeps the h rows of the padded lattice for dW
   q.o_h = o;
   if (q.untiled) o = align_up(o + q.elem * (size_t)B * q.d.Tpad * q.d.U1pad * H);
+  // untiled bf16: float32 offset of every row's stored logits per vocabulary step
+  q.zstep = joint_vocab_step(bf16, H);
+  q.o_zm = o;
+  if (q.untiled && bf16)
+    o = align_up(o + 4 * (size_t)B * q.d.Tpad * q.d.U1pad * ((V + q.zstep - 1) / q.zstep));
   q.saved_bytes = o;
   q.ws_fwd = 0;
   // backward workspace: float64 d_b_out accumulator [V], then (tiled) one
@@ -120,6 +127,20 @@ inline P* at(void* base, size_t off) {
 }
 
 inline bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Tag of what a backward must share with the forward that filled `saved`:
+// sizes, dtype and blank (FNV-1a over them, kept positive and nonzero).
+int32_t plan_tag(const Plan& p, int blank) {
+  const int v[7] = {p.d.B, p.d.T, p.d.U, p.d.H, p.d.V, p.bf16 ? 1 : 0, blank};
+  uint32_t h = 2166136261u;
+  for (int x : v)
+    for (int k = 0; k < 4; ++k) {
+      h ^= (uint32_t)(x >> (8 * k)) & 0xffu;
+      h *= 16777619u;
+    }
+  h &= 0x7fffffffu;
+  return (int32_t)(h ? h : 1);
+}
 
 // ---- optional per-kernel event timing (rnnt_joint_loss_timing)
 struct TimedLaunch {
@@ -248,10 +269,12 @@ int rnnt_joint_loss_fwd_ex(const void* enc, const void* pred, const void* W_out,
   double* beta = at<double>(saved, p.o_beta);
 
   hipError_t e;
-  if ((e = timed("zero", st, [&] { return launch_zero(status, 4, st); })) != hipSuccess)
+  if ((e = timed("zero", st, [&] { return launch_zero(status, kHdrWords, st); })) != hipSuccess)
     return RNNTJ_ERR_HIP;
+  const int32_t tag = plan_tag(p, blank);
   if ((e = timed("validate", st, [&] {
-         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, crit, st);
+         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, crit, tag,
+                                p.untiled ? 1 : 0, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   float* Eexp = at<float>(saved, p.o_E);
@@ -294,6 +317,8 @@ int rnnt_joint_loss_fwd_ex(const void* enc, const void* pred, const void* W_out,
   a.LE = LE;
   a.zout = p.untiled ? at<char>(saved, p.o_z) : nullptr;
   a.hout = p.untiled ? at<char>(saved, p.o_h) : nullptr;
+  a.zmax = (p.untiled && p.bf16) ? at<float>(saved, p.o_zm) : nullptr;
+  a.zstep = p.zstep;
   if ((e = timed(p.untiled ? "joint_fwd_store" : "joint_fwd", st, [&] {
          return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, p.cap_all, st);
        })) != hipSuccess)
@@ -325,7 +350,9 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
     return RNNTJ_ERR_ARG;
   if (U > 0 && !labels) return RNNTJ_ERR_ARG;
   if (blank < 0 || blank >= V) return RNNTJ_ERR_ARG;
-  if (misaligned(enc) || misaligned(pred) || misaligned(W_out) || misaligned(saved))
+  if (misaligned(enc) || misaligned(pred) || misaligned(W_out) || misaligned(saved) ||
+      misaligned(d_enc) || misaligned(d_pred) || misaligned(d_W_out) || misaligned(d_b_out) ||
+      misaligned(grad_costs))
     return RNNTJ_ERR_ARG;
   if (workspace_bytes < p.ws_bwd || !workspace) return RNNTJ_ERR_WORKSPACE;
   if (misaligned(workspace)) return RNNTJ_ERR_ARG;
@@ -346,6 +373,13 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
                              (size_t)H * V, db64, 2 * (size_t)V, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
+  // the state must come from a forward with these sizes, dtype and blank
+  // (and, for the untiled backward, one that stored the logits)
+  int32_t* hdr = at<int32_t>(saved, p.o_status);
+  if ((e = timed("guard", st, [&] {
+         return launch_guard(hdr, plan_tag(p, blank), p.untiled ? 1 : 0, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
 
   JointArgs a = {};
   a.enc = enc;
@@ -355,7 +389,7 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   a.labels = labels;
   a.Teff = Teff;
   a.Ueff = Ueff;
-  a.hdr = at<int32_t>(saved, p.o_status);
+  a.hdr = hdr;
   a.Eexp = at<float>(saved, p.o_E);
   a.Pexp = at<float>(saved, p.o_P);
   a.d = p.d;
@@ -366,6 +400,8 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   a.beta = at<double>(saved, p.o_beta);
   a.logP = logP;
   a.gcost = grad_costs;
+  a.zmax = (p.untiled && p.bf16) ? at<float>(saved, p.o_zm) : nullptr;
+  a.zstep = p.zstep;
 
   DhArgs h = {};
   h.W = W_out;
@@ -385,6 +421,7 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   w.d = p.d;
   w.d_W = d_W_out;
   w.d_b64 = db64;
+  w.hdr = hdr;
   h.gcost = grad_costs;
   // split-K runs of the dW GEMM: one round of resident workgroups (two per
   // compute unit for bf16, one for fp32), fewest float32 partial sums per
@@ -509,7 +546,8 @@ int rnnt_joint_proj_bwd(const void* x, const void* W, int dtype, int M, int K, i
                         const float* dy, float* dx, float* dW, float* db, void* stream) {
   if (!x || !W || !dy || !dW || M < 1 || K < 1 || N < 1) return RNNTJ_ERR_ARG;
   if (dtype != RNNTJ_F32 && dtype != RNNTJ_BF16) return RNNTJ_ERR_ARG;
-  if (misaligned(x) || misaligned(W) || misaligned(dy) || misaligned(dx) || misaligned(dW))
+  if (misaligned(x) || misaligned(W) || misaligned(dy) || misaligned(dx) || misaligned(dW) ||
+      misaligned(db))
     return RNNTJ_ERR_ARG;
   if (K % 16 != 0 || N % 16 != 0 || K > kMaxProj || N > kMaxProj) return RNNTJ_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -86,6 +86,7 @@ __global__ __launch_bounds__(256) void grad_inplace_kernel(JointArgs a, T* __res
   constexpr int CE = 16 / (int)sizeof(T);
   __shared__ float4 cs[kTileCells];
   const int tix = blockIdx.x, tid = threadIdx.x;
+  if (ld_const(a.hdr + kHdrRefuse)) return;  // the state does not belong to this backward
   if (tix == 0 && tid == 0 && (a.hdr[1] & kFlagConsumed)) atomicOr(&a.hdr[0], kErrConsumed);
   if (tix >= a.tile_count[0]) return;
   int b, tt, tu;
@@ -98,8 +99,13 @@ __global__ __launch_bounds__(256) void grad_inplace_kernel(JointArgs a, T* __res
   const int nch = (V + 64 * CE - 1) / (64 * CE);  // chunk columns per row per lane
   const int n = 32 * nch;                         // (row, chunk) pairs of this wave
   T* const zt = z + (((size_t)b * d.Tpad + t0) * d.U1pad + u0) * V;
+  // bf16: the stored values are z - M, M per row and vocabulary step
+  constexpr bool kShift = sizeof(T) == 2;
+  const int nvs = kShift ? (V + a.zstep - 1) / a.zstep : 0;
+  const float* zm = kShift ? a.zmax + (((size_t)b * d.Tpad + t0) * d.U1pad + u0) * nvs : nullptr;
   for (int i0 = 0; i0 < n; i0 += 8) {
     u32x4 x[8];
+    float zoff[8];
     T* ptr[8];
     bool ok[8];
 #pragma unroll
@@ -107,8 +113,13 @@ __global__ __launch_bounds__(256) void grad_inplace_kernel(JointArgs a, T* __res
       const int i = i0 + k, rr = i / nch, v0 = ((i % nch) * 64 + lane) * CE;
       const int r = 32 * w + rr;
       ok[k] = i < n && v0 < V;
-      ptr[k] = zt + ((size_t)(r >> 3) * d.U1pad + (r & 7)) * V + v0;
-      if (ok[k]) x[k] = *reinterpret_cast<const u32x4*>(ptr[k]);
+      const size_t row = (size_t)(r >> 3) * d.U1pad + (r & 7);
+      ptr[k] = zt + row * V + v0;
+      zoff[k] = 0.f;
+      if (ok[k]) {
+        x[k] = *reinterpret_cast<const u32x4*>(ptr[k]);
+        if constexpr (kShift) zoff[k] = zm[row * nvs + v0 / a.zstep];
+      }
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
@@ -120,7 +131,8 @@ __global__ __launch_bounds__(256) void grad_inplace_kernel(JointArgs a, T* __res
 #pragma unroll
         for (int e = 0; e < CE; ++e) {
           const uint32_t bits = (x[k][e >> 1] >> (16 * (e & 1))) << 16;
-          g[e] = dz_from_z(__uint_as_float(bits & 0xffff0000u), v0 + e, v0 + e + 1, c, d.blank);
+          g[e] = dz_from_z(__uint_as_float(bits & 0xffff0000u) + zoff[k], v0 + e, v0 + e + 1, c,
+                           d.blank);
         }
         u32x4 y;
 #pragma unroll
@@ -200,6 +212,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   const T* __restrict__ G = static_cast<const T*>(a.g);
   const T* __restrict__ W = static_cast<const T*>(a.W);
   const int nnb = (H + C::NB - 1) / C::NB;
+  if (ld_const(a.hdr + kHdrRefuse)) return;  // the state does not belong to this backward
   const int n_tiles = ld_const(a.tile_count);
   // an item is (tile, hidden block, vocabulary part): with few tiles the
   // vocabulary is split so that the workgroups get equal shares (dh is
@@ -619,6 +632,7 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
   const int item = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
   const int kp = item / nmn, nb = (item % nmn) / nmb, mb = item % nmb;
   if (kp >= a.kparts) return;
+  if (ld_const(a.hdr + kHdrRefuse)) return;  // the state does not belong to this backward
   const int count = ld_const(a.tile_count);
   const int tb = (int)((long long)count * kp / a.kparts);
   const int te = (int)((long long)count * (kp + 1) / a.kparts);
@@ -823,7 +837,8 @@ __global__ void db_finalize_kernel(const double* __restrict__ src, float* __rest
                                    int32_t* mark) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
   if (v < V) dst[v] = (float)src[v];
-  if (mark && v == 0) atomicOr(&mark[1], kFlagConsumed);  // the stored logits are now dz
+  // the stored logits are now dz (unless this backward refused the state)
+  if (mark && v == 0 && mark[kHdrRefuse] == 0) atomicOr(&mark[1], kFlagConsumed);
 }
 
 }  // namespace

@@ -137,6 +137,22 @@ __device__ __forceinline__ float rs_sum16(const float (&v)[16], int lane) {
   const float f = (b3 ? e[1] : e[0]) + __shfl_xor(b3 ? e[0] : e[1], 8);
   return f + __shfl_xor(f, 16);
 }
+// the same reduce-scatter with max in place of the sum
+__device__ __forceinline__ float rs_max16(const float (&v)[16], int lane) {
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
+  float a[8], c[4], e[2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    a[i] = fmaxf(b0 ? v[i + 8] : v[i], __shfl_xor(b0 ? v[i] : v[i + 8], 1));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c[i] = fmaxf(b1 ? a[i + 4] : a[i], __shfl_xor(b1 ? a[i] : a[i + 4], 2));
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    e[i] = fmaxf(b2 ? c[i + 2] : c[i], __shfl_xor(b2 ? c[i] : c[i + 2], 4));
+  const float f = fmaxf(b3 ? e[1] : e[0], __shfl_xor(b3 ? e[0] : e[1], 8));
+  return fmaxf(f, __shfl_xor(f, 16));
+}
 // (m, s) <- (m, s) + (m2, s2) for sums s of 2^(x - m)
 __device__ __forceinline__ void lse2_merge(float& m, float& s, float m2, float s2) {
   const float mn = fmaxf(m, m2);
@@ -227,6 +243,8 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   __shared__ float row_b[kTileCells];  // kGrad: gc * gB
   __shared__ float row_e[kTileCells];  // kGrad: gc * gE
   __shared__ __align__(16) char Ep[EP::kBytes];
+  // kStoreZ, bf16: each row's largest logit of the vocabulary step
+  __shared__ __align__(16) float zm_row[(MODE == kStoreZ && kBf16) ? 4 : 1][32];
 
   const Dims d = a.d;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -238,6 +256,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   const T* __restrict__ pred = static_cast<const T*>(a.pred);
   const T* __restrict__ Wt = static_cast<const T*>(a.Wt);
   const T* __restrict__ bias = static_cast<const T*>(a.bias);
+  if (MODE == kGrad && ld_const(a.hdr + kHdrRefuse)) return;  // state refused by this backward
   const int hflags = a.hdr[1];
   const bool use_ep = (hflags & kFlagEpBad) == 0;
   const bool stage_ep = EP::kStage && use_ep;
@@ -662,6 +681,42 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
       const int RT = MODE == kGrad ? a.CT : d.Tpad, RU = MODE == kGrad ? a.CU : d.U1pad;
       const int rt0 = MODE == kGrad ? a.ct0 : 0, ru0 = MODE == kGrad ? a.cu0 : 0;
       T* out = static_cast<T*>(MODE == kGrad ? a.gout : a.zout);
+      if constexpr (MODE == kStoreZ && kBf16) {
+        // Stored as bf16(z - M), M = the row's largest logit of this step
+        // (kept in float32 beside them).  A logit of size |z| would carry a
+        // bf16 rounding error of up to |z| 2^-8 into exp(z - lse); relative
+        // to M the error is at most |z - M| 2^-8, and since
+        // exp(z - lse) <= exp(z - M), its effect on a softmax entry stays
+        // below 2^-8 / e whatever the size of the logits.
+        float tm[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float mx = -kInf;
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk)
+            if (cvalid[blk]) mx = fmaxf(mx, acc[blk][r]);
+          tm[r] = mx;
+        }
+        const float mr = rs_max16(tm, lane);  // accumulator row rs_row(lane) of this half
+        if (lc < 16) {
+          const int r = rs_row(lc);
+          const int row = acc_row(r, kh);
+          zm_row[w][row] = mr;
+          const int t = t0 + 4 * w + (row >> 3), u = u0 + (row & 7);
+          const int nvs = (V + VT - 1) / VT;
+          a.zmax[(((size_t)b * d.Tpad + t) * d.U1pad + u) * nvs + vt / VT] = mr;
+        }
+        wait_lgkm0();  // this wave's rows are in LDS (read back by the same wave)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // rows acc_row(4i + j, kh) = 8i + 4kh + j
+          const f32x4 m4 = *reinterpret_cast<const f32x4*>(&zm_row[w][8 * i + 4 * kh]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk) acc[blk][4 * i + j] -= m4[j];
+        }
+      }
       if constexpr (kBf16) {
         // accumulator columns -> Ts[col][row] (8-byte writes of 4 rows) ...
         uint16_t* ts = Ts[w];
@@ -843,6 +898,11 @@ int device_cu_count() {
 // 64 of them; otherwise 128-column steps, one workgroup per compute unit
 template <typename T, int KS>
 constexpr int kJointBlocks = (sizeof(T) == 2 && KS <= 16) ? 2 : 4;
+
+int joint_vocab_step(bool bf16, int H) {
+  const int nks = (H + 15) / 16;
+  return (bf16 && nks <= 16) ? 32 * 2 : 32 * 4;  // kJointBlocks<T, KS> 32-column blocks
+}
 
 template <typename T, int KS, int MODE>
 static void launch_ks(const JointArgs& a, int n_items, hipStream_t st) {

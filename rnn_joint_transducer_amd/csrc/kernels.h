@@ -18,6 +18,14 @@ constexpr int kFlagEpBad = 1;     // some finite |enc| or |pred| > 40
 constexpr int kFlagConsumed = 2;  // an untiled backward turned the stored logits into dz
 // data-error bit: a backward found its logits already consumed by another
 constexpr int kErrConsumed = 4;
+// data-error bit: a backward's sizes, dtype, blank or mode do not match the
+// forward that wrote the state; that backward then computes nothing
+constexpr int kErrPlan = 8;
+// Header words 4 and 5 hold the forward's plan tag and whether the state
+// carries logits (untiled); word 6 is set by a backward that refuses the
+// state (every later kernel of that backward returns at once).
+constexpr int kHdrWords = 8;
+constexpr int kHdrRefuse = 6;
 
 // Active-tile lists.  A lattice chunk (frames ct0 .. ct0+CT-1, label
 // positions cu0 .. cu0+CU-1) is covered by 16 x 8 cell tiles; a tile is
@@ -58,6 +66,11 @@ struct JointArgs {
   float* LB;
   float* LE;
   void* zout;  // kStoreZ: logits [B, Tpad, U1pad, V]
+  // kStoreZ, bf16: the logits are stored as bf16(z - M), M the row's largest
+  // logit within each vocabulary step of `zstep` columns, and M (float32) in
+  // zmax [B, Tpad, U1pad, ceil(V / zstep)]; read back as stored + M
+  float* zmax;
+  int zstep;
   // backward inputs / output
   const double* alpha;
   const double* beta;
@@ -67,6 +80,10 @@ struct JointArgs {
   void* hout;          // kGrad: joint activations h [B, CT, CU, H]; kStoreZ: the h rows
                        // [B, Tpad, U1pad, H] of the active tiles, or null
 };
+
+// Vocabulary columns of one step of the forward joint kernel for this dtype
+// and hidden size (the granularity of JointArgs::zmax).
+int joint_vocab_step(bool bf16, int H);
 
 // Persistent launch: `n_items` = (maximum number of active tiles) * vsplit
 // bounds the work; the workgroups loop over the items the tile list holds.
@@ -78,7 +95,10 @@ hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_item
 // (kCritSum / kCritMax) in status[3].
 hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
-                           int32_t* Ueff, int32_t* status, int crit, hipStream_t st);
+                           int32_t* Ueff, int32_t* status, int crit, int32_t tag,
+                           int has_logits, hipStream_t st);
+// Backward's first check of the state header (see kErrPlan).
+hipError_t launch_guard(int32_t* hdr, int32_t tag, int need_logits, hipStream_t st);
 
 // One launch: Wt[V, H] = W_out transposed; Eexp = e^{2 enc}, Pexp = e^{2 pred}
 // (float32), hdr[1] |= kFlagEpBad if some finite |enc| or |pred| exceeds 40;
@@ -149,6 +169,7 @@ struct DwArgs {
   Dims d;
   int ct0, cu0, CT, CU;
   int kparts;                 // split-K: parts of the tile list
+  const int32_t* hdr;         // state header (refusal word)
   float* d_W;
   double* d_b64;
 };

@@ -426,10 +426,15 @@ __global__ void validate_kernel(const int32_t* __restrict__ T_lens,
                                 const int32_t* __restrict__ U_lens,
                                 const int32_t* __restrict__ labels, Dims d,
                                 int32_t* __restrict__ Teff, int32_t* __restrict__ Ueff,
-                                int32_t* __restrict__ status, int crit) {
+                                int32_t* __restrict__ status, int crit, int32_t tag,
+                                int has_logits) {
   __shared__ int sbad;
   const int b = blockIdx.x;
-  if (b == 0 && threadIdx.x == 0) status[3] = crit;  // header word 3: the criterion
+  if (b == 0 && threadIdx.x == 0) {
+    status[3] = crit;  // header word 3: the criterion
+    status[4] = tag;   // words 4, 5: what a backward from this state must match
+    status[5] = has_logits;
+  }
   if (threadIdx.x == 0) sbad = 0;
   __syncthreads();
   const int Tl = T_lens[b], Ul = U_lens[b];
@@ -624,9 +629,25 @@ hipError_t launch_tile_list(const int32_t* Teff, const int32_t* Ueff, const Dims
 
 hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
-                           int32_t* Ueff, int32_t* status, int crit, hipStream_t st) {
+                           int32_t* Ueff, int32_t* status, int crit, int32_t tag,
+                           int has_logits, hipStream_t st) {
   hipLaunchKernelGGL(validate_kernel, dim3(d.B), dim3(256), 0, st, T_lens, U_lens, labels, d,
-                     Teff, Ueff, status, crit);
+                     Teff, Ueff, status, crit, tag, has_logits);
+  return hipGetLastError();
+}
+
+// A backward checks the state it is given against its own arguments before
+// any kernel reads more than the header: on a mismatch it sets kErrPlan and
+// the refusal word, which every later kernel of that backward reads first.
+__global__ void guard_kernel(int32_t* hdr, int32_t tag, int need_logits) {
+  if (threadIdx.x != 0) return;
+  const bool ok = hdr[4] == tag && (!need_logits || hdr[5] == 1);
+  hdr[kHdrRefuse] = ok ? 0 : 1;
+  if (!ok) atomicOr(&hdr[0], kErrPlan);
+}
+
+hipError_t launch_guard(int32_t* hdr, int32_t tag, int need_logits, hipStream_t st) {
+  hipLaunchKernelGGL(guard_kernel, dim3(1), dim3(64), 0, st, hdr, tag, need_logits);
   return hipGetLastError();
 }
 

@@ -63,3 +63,33 @@ def check_grad(name, gpu, ref, dtype):
     rel = err / scale if scale > 0 else err
     assert rel <= BF16_REL, f"{name}: rel err {rel:.3e} > {BF16_REL} (abs {err:.3e})"
     return rel
+
+
+def _loss_only_job(args):
+    """One utterance's cost from the oracle (process-pool worker)."""
+    enc_b, pred_b, W, b_out, y, Tl, Ul, blank, threads, criterion = args
+    from oracle import rnnt
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=threads):
+        return float(rnnt.loss_only(enc_b[None], pred_b[None], W, b_out, y[None],
+                                    np.array([Tl]), np.array([Ul]), blank,
+                                    criterion=criterion)[0])
+
+
+def oracle_costs(inp, utts, workers, criterion="sum"):
+    """Oracle costs of the given utterances, one process per utterance (spawned:
+    the calling process may hold a GPU runtime)."""
+    import multiprocessing
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+    utts = list(utts)
+    workers = max(1, min(workers, len(utts)))
+    threads = max(1, (os.cpu_count() or 1) // workers)
+    jobs = [(inp.enc_f64[b], inp.pred_f64[b], inp.W_f64, inp.b_f64, inp.labels[b],
+             int(inp.T_lens[b]), int(inp.U_lens[b]), inp.blank, threads, criterion)
+            for b in utts]
+    if workers == 1:
+        return [_loss_only_job(j) for j in jobs]
+    ctx = multiprocessing.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        return list(ex.map(_loss_only_job, jobs))

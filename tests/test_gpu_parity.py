@@ -16,7 +16,7 @@ import oracle
 from oracle import rnnt
 from synth import make_config, make_inputs
 
-from gpu_common import BF16_REL, check_costs, check_grad, run_gpu, to_device
+from gpu_common import BF16_REL, check_costs, check_grad, oracle_costs, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -85,15 +85,15 @@ def test_ragged_edges(dtype):
 def test_small_hidden_and_logit_bound(dtype, H, V, sigma):
     """Hidden sizes up to 256 in bf16 (the 64-column vocabulary step with
     two workgroups per compute unit), with the max-free log-sum-exp and, when
-    sum_k |W_kv| + |b_v| reaches 64, the one with running maxima.  Untiled
-    bf16 keeps the logits in bf16, whose rounding (|z| 2^-9, ~0.06 at the
-    |z| ~ 30 these weights give) enters exp(z - lse) directly, so the large-
-    logit bf16 cases run the tiled modes, which recompute the logits in fp32."""
+    sum_k |W_kv| + |b_v| reaches 64, the one with running maxima.  The large
+    weights give logits |z| ~ 30: untiled bf16 stores them relative to each
+    row's largest logit of the vocabulary step, which keeps the storage error
+    of every softmax entry below 2^-8 / e whatever |z| is (stored as plain
+    bf16 they would carry |z| 2^-8 ~ 0.1 into exp(z - lse))."""
     inp = make_inputs(3, 29, 9, H, V, dtype=dtype, sigma=sigma, seed=53, t_range=(5, 29),
                       u_range=(0, 9))
     ref = _oracle_full(inp, grad_costs=[1.0, -0.5, 0.25])
-    large_bf16 = dtype == "bf16" and sigma > 1.0
-    for tiles in ([(16, 8, 0), (0, 8, 128)] if large_bf16 else [(0, 0, 0), (16, 8, 0)]):
+    for tiles in [(0, 0, 0), (16, 8, 0), (0, 8, 128)]:
         print(f"[small hidden {dtype} H={H} V={V} sigma={sigma} tiles={tiles}]", flush=True)
         g = run_gpu(inp, *tiles, grad_costs=[1.0, -0.5, 0.25])
         assert g["status"] == 0
@@ -265,12 +265,9 @@ def test_untiled_state_consumed_once():
 def _sampled(inp, tiles, cost_utts, grad_utts):
     g = run_gpu(inp, *tiles)
     assert g["status"] == 0
-    refc = []
-    for b in cost_utts:
-        refc.append(rnnt.loss_only(inp.enc_f64[b:b + 1], inp.pred_f64[b:b + 1], inp.W_f64,
-                                   inp.b_f64, inp.labels[b:b + 1], inp.T_lens[b:b + 1],
-                                   inp.U_lens[b:b + 1], 0)[0])
-    check_costs(g["costs"], refc, inp.dtype, idx=cost_utts)
+    refc = oracle_costs(inp, cost_utts, WORKERS)
+    worst = check_costs(g["costs"], refc, inp.dtype, idx=cost_utts)
+    print(f"  costs of {len(cost_utts)} utterances: worst rel err {worst:.2e}", flush=True)
     for b in grad_utts:
         o = rnnt.utterance_loss_and_grads(inp.enc_f64[b], inp.pred_f64[b], inp.W_f64, inp.b_f64,
                                           inp.labels[b], int(inp.T_lens[b]),
@@ -298,9 +295,11 @@ def _sub_batch_weights(inp, tiles, utts):
 
 @pytest.mark.parametrize("tiles", [(64, 64, 0), (0, 0, 0), (128, 0, 256)])
 def test_medium(tiles):
+    """Every cost of the batch, the gradients of one utterance, and the weight
+    gradients of a two-utterance sub-batch at the full sizes."""
     inp = make_config("medium")
     print(f"[medium tiles={tiles}]", flush=True)
-    _sampled(inp, tiles, cost_utts=[0, 7, 15], grad_utts=[7])
+    _sampled(inp, tiles, cost_utts=list(range(inp.B)), grad_utts=[7])
     _sub_batch_weights(inp, tiles, [3, 11])
 
 
@@ -308,14 +307,41 @@ def test_medium(tiles):
 def test_medium_large_vocab(tiles):
     inp = make_config("medium_lv")
     print(f"[medium_lv tiles={tiles}]", flush=True)
-    _sampled(inp, tiles, cost_utts=[2, 9], grad_utts=[9])
+    _sampled(inp, tiles, cost_utts=list(range(inp.B)), grad_utts=[9])
+    _sub_batch_weights(inp, tiles, [5, 13])
 
 
-def test_long_tiled():
+# The long workload in the tiling the benchmark times (64 x 64 chunks, tile_v
+# 256), split into three tests so that each one's oracle work stays around a
+# minute on the host cores.
+LONG_TILES = (64, 64, 256)
+
+
+def test_long_tiled_costs():
+    """Every utterance's cost."""
     inp = make_config("long")
-    b = int(np.argmin(inp.T_lens.astype(np.int64) * (inp.U_lens + 1)))
-    print(f"[long sampled utt {b}]", flush=True)
-    _sampled(inp, (64, 64, 256), cost_utts=[b], grad_utts=[])
+    print(f"[long costs tiles={LONG_TILES}]", flush=True)
+    _sampled(inp, LONG_TILES, cost_utts=list(range(inp.B)), grad_utts=[])
+
+
+def test_long_tiled_largest_utterance_grads():
+    """d_enc and d_pred of the utterance with the most lattice cells (its
+    lattice reaches into the last frame and label chunks), from the whole
+    batch's backward."""
+    inp = make_config("long")
+    b = int(np.argmax(inp.T_lens.astype(np.int64) * (inp.U_lens + 1)))
+    print(f"[long grads utt {b}: T'={inp.T_lens[b]} U'={inp.U_lens[b]} tiles={LONG_TILES}]",
+          flush=True)
+    _sampled(inp, LONG_TILES, cost_utts=[b], grad_utts=[b])
+
+
+def test_long_tiled_sub_batch_weights():
+    """d_W_out and d_b_out of a two-utterance sub-batch at the full H, V, T, U."""
+    inp = make_config("long")
+    cells = inp.T_lens.astype(np.int64) * (inp.U_lens + 1)
+    utts = [int(i) for i in np.argsort(cells)[:2]]
+    print(f"[long sub-batch {utts} tiles={LONG_TILES}]", flush=True)
+    _sub_batch_weights(inp, LONG_TILES, utts)
 
 
 @pytest.mark.parametrize("name", ["medium", "long"])
@@ -449,7 +475,10 @@ def test_maximum_sizes(case):
     longest-T cases weight their costs by 1e-3 and 1e-4: unweighted, d_b_out
     sums to ~1.1e4 over 8191 utterances (half an fp32 ulp there is 4.9e-4)
     and d_W_out to ~40 over 65520 frames, beyond what an fp32 value can hold
-    to the 1e-4 absolute bound; a wrong gradient still misses it by far."""
+    to the 1e-4 absolute bound.  Weighted, the gradients are small enough
+    that the absolute bound alone would also accept zeros, so those cases
+    also compare every gradient relative to its largest oracle entry: fp32
+    sums of up to 65520 terms keep that within 1e-4."""
     gcs = None
     runs = [((0, 0, 0), "sum"), ((16, 8, 0), "sum")]
     if case == "U_max":
@@ -474,3 +503,50 @@ def test_maximum_sizes(case):
         if crit not in refs:
             refs[crit] = _oracle_full(inp, grad_costs=gcs, criterion=crit)
         _compare_all(inp, g, refs[crit])
+        if gcs is not None:
+            for k in ("dEnc", "dPred", "dW", "db"):
+                scale = float(np.max(np.abs(refs[crit][k])))
+                rel = float(np.max(np.abs(g[k] - refs[crit][k]))) / scale
+                print(f"  {k}: max|ref| {scale:.3e}, rel err {rel:.2e}", flush=True)
+                assert scale > 0 and rel <= 1e-4, (k, scale, rel)
+
+
+# ------------------------------------------------------------------ state / backward mismatch
+
+def test_backward_checks_the_state_it_is_given():
+    """A backward checks that `saved` comes from a forward with its sizes,
+    dtype and blank, and (untiled) one that stored the logits.  On a mismatch
+    it computes nothing: gradients zero, data-error bit 8.  The buffers here
+    are sized for the larger (untiled) layout, so nothing could be read out of
+    bounds even without the check.  An untiled forward's state carries all a
+    tiled backward needs, which is accepted and exact."""
+    import torch
+    import rnn_joint_transducer_amd as rj
+    inp = make_config("tiny")
+    d = to_device(inp)
+    B, T, U, H, V = inp.B, inp.T, inp.U, inp.H, inp.V
+    nbytes = rj.rnnt_joint_loss_saved_bytes(B, T, U, H, V, rj.RNNTJ_F32, 0, 0, 0)
+    ref = _oracle_full(inp)
+    # untiled backward from a tiled forward's state
+    saved = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rj.rnnt_joint_loss_fwd(**d, tile_t=16, tile_u=8, saved=saved)
+    g = rj.rnnt_joint_loss_bwd(**d, saved=saved)
+    assert rj.rnnt_joint_loss_status(saved) == 8
+    assert all(float(x.abs().max()) == 0.0 for x in g)
+    # a backward with another blank than its forward
+    saved = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rj.rnnt_joint_loss_fwd(**d, tile_t=16, tile_u=8, saved=saved)
+    g = rj.rnnt_joint_loss_bwd(**d, saved=saved, blank=1, tile_t=16, tile_u=8)
+    assert rj.rnnt_joint_loss_status(saved) == 8
+    assert all(float(x.abs().max()) == 0.0 for x in g)
+    # a tiled backward from the untiled forward's state: accepted and exact
+    costs, saved = rj.rnnt_joint_loss_fwd(**d)
+    g = rj.rnnt_joint_loss_bwd(**d, saved=saved, tile_t=16, tile_u=8)
+    assert rj.rnnt_joint_loss_status(saved) == 0
+    for name, x, k in zip(("d_enc", "d_pred", "d_W_out", "d_b_out"), g,
+                          ("dEnc", "dPred", "dW", "db")):
+        check_grad(name, x.double().cpu().numpy(), ref[k], "fp32")
+    # the binding refuses a state buffer smaller than the backward's layout
+    _, small = rj.rnnt_joint_loss_fwd(**d, tile_t=16, tile_u=8)
+    with pytest.raises(ValueError, match="saved"):
+        rj.rnnt_joint_loss_bwd(**d, saved=small)

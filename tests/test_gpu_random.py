@@ -3,7 +3,8 @@
 Each case draws, from its own seed, the batch size, the padded and actual
 lengths (single frames and utterances without labels included), hidden and
 vocabulary sizes, the blank index (first, last or inside the vocabulary), a
-nonzero output bias, the tiling (untiled, or tiled with or without a
+nonzero output bias, the weight scale (every fourth case, odd seeds: bf16,
+large logits in the untiled mode), the tiling (untiled, or tiled with or without a
 vocabulary bound), the dtype, the criterion and signed cost weights.  Every
 output is compared with the float64 oracle, element by element.  Each case
 prints its parameters before it runs.
@@ -33,13 +34,15 @@ def _case(seed):
     H = 16 * int(rng.integers(1, (256 if dtype == "fp32" else 384) // 16 + 1))
     V = 8 * int(rng.integers(1, 65))
     blank = [0, V - 1, int(rng.integers(0, V))][seed % 3]
-    inp = make_inputs(B, T, U, H, V, dtype=dtype, sigma=0.3, seed=2000 + seed, blank=blank,
+    # every fourth case draws large weights (logits of size ~10-40)
+    sigma = 1.5 if seed % 4 == 1 else 0.3
+    inp = make_inputs(B, T, U, H, V, dtype=dtype, sigma=sigma, seed=2000 + seed, blank=blank,
                       t_range=(1, T), u_range=(0, U))
     # labels anywhere in the vocabulary except the blank
     lab = rng.integers(0, V - 1, size=(B, U))
     inp.labels = (lab + (lab >= blank)).astype(np.int32)
     inp.b, inp.b_f64 = _cast(rng.normal(0.0, 0.3, V), dtype)
-    if rng.random() < 0.4:
+    if rng.random() < 0.4 or sigma > 1.0:
         tiles = (0, 0, 0)
     else:
         tiles = (16 * int(rng.integers(0, 4)), 8 * int(rng.integers(0, 3)),
