@@ -22,6 +22,10 @@ Sources, all on the pages that describe the method:
   default, or ``"max"``: the single best alignment).
 * The Transformer-Transducer abstract's feed-forward combination, read as an
   affine projection of each encoding ahead of the joint (``proj.py``).
+* "Pruned RNN-T for fast, memory-efficient ASR training", Abstract: pruning
+  bounds from a simple joiner linear in the two embeddings, then the full
+  joiner evaluated inside them (``pruned.py``, pinned by
+  ``tests/test_oracle_pruned_pins.py``).
 
 Every function is pinned by the tests in ``tests/test_oracle_pins.py``
 (brute-force enumeration, alpha/beta agreement, closed forms, invariants,
@@ -41,3 +45,4 @@ from .rnnt import (  # noqa: F401
     closed_form_zero_weights_max,
 )
 from .proj import linear, linear_grads, projected_loss_and_grads  # noqa: F401
+from . import pruned  # noqa: F401,E402
