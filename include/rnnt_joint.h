@@ -23,7 +23,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller: contiguous,
  *     row-major, 16-byte aligned.  The library never allocates, frees or keeps
  *     device memory between calls and is reentrant; its only global state is
- *     the optional kernel-timing record (rnnt_joint_loss_timing, below).
+ *     the optional kernel-timing record (rnnt_joint_loss_timing, below) and
+ *     the static scratch array of rnnt_joint_loss_bwd_noalloc (one per GPU).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *     on it and the call returns without synchronising, except
  *     rnnt_joint_loss_status, which synchronises `stream`.
@@ -194,6 +195,33 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,
                         int tile_v, const float* grad_costs, void* saved,
                         float* d_enc, float* d_pred, float* d_W_out, float* d_b_out,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors as rnnt_joint_loss_bwd without `workspace` / `workspace_bytes`: the
+ * backward's scratch is instead a static device array of
+ * RNNTJ_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends.  Sizes whose backward workspace
+ * (rnnt_joint_loss_workspace_bytes, pass 1) exceeds it return
+ * RNNTJ_ERR_WORKSPACE before anything is enqueued: this covers the untiled
+ * mode at every accepted size and the tiled mode while one chunk's logit
+ * gradients and activations fit.  `stream` must belong to the calling
+ * thread's current device (else RNNTJ_ERR_ARG).  No hipMalloc / hipFree or
+ * allocating library call is made.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents (the backward clears what it
+ * needs zeroed itself): calls that overlap on one GPU race, so serialise
+ * them (for example, issue them on one stream).
+ */
+#define RNNTJ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int rnnt_joint_loss_bwd_noalloc(const void* enc, const void* pred, const void* W_out,
+                                const void* b_out, int dtype, const int32_t* labels,
+                                const int32_t* T_lens, const int32_t* U_lens, int B, int T,
+                                int U, int H, int V, int blank, int tile_t, int tile_u,
+                                int tile_v, const float* grad_costs, void* saved,
+                                float* d_enc, float* d_pred, float* d_W_out, float* d_b_out,
+                                void* stream);
 
 /*
  * Synchronises `stream`, then copies the data-error word of `saved` to

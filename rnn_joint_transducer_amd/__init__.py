@@ -19,7 +19,8 @@ import ctypes
 from ._lib import (RNNTJ_BF16, RNNTJ_F32, RNNTJointError, check, declared_functions,  # noqa: F401
                    load)
 
-__all__ = ["rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd", "rnnt_joint_loss_status",
+__all__ = ["rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd", "rnnt_joint_loss_bwd_noalloc",
+           "rnnt_joint_loss_status",
            "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
            "rnnt_joint_loss", "RNNTJointError", "load"]
 
@@ -145,6 +146,36 @@ def rnnt_joint_loss_bwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, 
                                     _ptr(d_b), _ptr(workspace), workspace.numel(),
                                     _stream(dev))
     check(rc, "rnnt_joint_loss_bwd")
+    return out
+
+
+def rnnt_joint_loss_bwd_noalloc(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, blank=0,
+                                tile_t=0, tile_u=0, tile_v=0, grad_costs=None, out=None):
+    """As rnnt_joint_loss_bwd, with the library's static per-GPU scratch in
+    place of a workspace (for callers that cannot allocate device memory;
+    `out` must then be given).  Calls that overlap on one GPU race."""
+    import torch
+    B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
+    dc = _dtype_code(enc)
+    dev = enc.device
+    need = rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v)
+    if saved.dtype != torch.uint8 or saved.device != dev or saved.numel() < need:
+        raise ValueError(f"saved: expected a uint8 buffer of at least {need} bytes on {dev}")
+    if out is None:
+        out = (torch.empty(B, T, H, dtype=torch.float32, device=dev),
+               torch.empty(B, U + 1, H, dtype=torch.float32, device=dev),
+               torch.empty(H, V, dtype=torch.float32, device=dev),
+               torch.empty(V, dtype=torch.float32, device=dev))
+    if grad_costs is not None and (grad_costs.dtype != torch.float32
+                                   or tuple(grad_costs.shape) != (B,)
+                                   or not grad_costs.is_contiguous()):
+        raise ValueError("grad_costs must be a contiguous float32 [B] tensor")
+    d_enc, d_pred, d_W, d_b = out
+    rc = load().rnnt_joint_loss_bwd_noalloc(
+        _ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out), dc, _ptr(labels), _ptr(T_lens),
+        _ptr(U_lens), B, T, U, H, V, blank, tile_t, tile_u, tile_v, _ptr(grad_costs),
+        _ptr(saved), _ptr(d_enc), _ptr(d_pred), _ptr(d_W), _ptr(d_b), _stream(dev))
+    check(rc, "rnnt_joint_loss_bwd_noalloc")
     return out
 
 

@@ -187,6 +187,41 @@ void drop_timed() {
   g_timed.clear();
 }
 
+// ---- scratch of rnnt_joint_loss_bwd_noalloc: a static device array (each
+// GPU the library runs on holds its own copy until the process ends).  In
+// host code `scratch` names a host-side stand-in, not device memory; its
+// device address is taken once per device with hipGetSymbolAddress (with that
+// device current) and only that address is ever passed to kernels.
+constexpr size_t kScratchBytes = RNNTJ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the scratch on the device of `st` (NULL: the current
+// device), which must be the calling thread's current device.
+int scratch_for(hipStream_t st, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RNNTJ_ERR_HIP;
+  if (st) {
+    hipDevice_t sd = -1;
+    if (hipStreamGetDevice(st, &sd) != hipSuccess) return RNNTJ_ERR_HIP;
+    if (sd != dev) return RNNTJ_ERR_ARG;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      note_error("scratch address", e != hipSuccess ? e : hipErrorInvalidSymbol);
+      return RNNTJ_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return RNNTJ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -514,6 +549,24 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
     }
   }
   return finalize(nullptr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
+}
+
+int rnnt_joint_loss_bwd_noalloc(const void* enc, const void* pred, const void* W_out,
+                                const void* b_out, int dtype, const int32_t* labels,
+                                const int32_t* T_lens, const int32_t* U_lens, int B, int T,
+                                int U, int H, int V, int blank, int tile_t, int tile_u,
+                                int tile_v, const float* grad_costs, void* saved, float* d_enc,
+                                float* d_pred, float* d_W_out, float* d_b_out, void* stream) {
+  Plan p;
+  const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
+  if (rc) return rc;
+  if (p.ws_bwd > kScratchBytes) return RNNTJ_ERR_WORKSPACE;  // before anything is enqueued
+  void* ws = nullptr;
+  const int src = scratch_for(static_cast<hipStream_t>(stream), &ws);
+  if (src) return src;
+  return rnnt_joint_loss_bwd(enc, pred, W_out, b_out, dtype, labels, T_lens, U_lens, B, T, U, H,
+                             V, blank, tile_t, tile_u, tile_v, grad_costs, saved, d_enc, d_pred,
+                             d_W_out, d_b_out, ws, kScratchBytes, stream);
 }
 
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error) {

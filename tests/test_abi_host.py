@@ -15,6 +15,7 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"rnnt_joint_loss_abi_version", "rnnt_joint_loss_strerror",
                           "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
                           "rnnt_joint_loss_fwd", "rnnt_joint_loss_fwd_ex", "rnnt_joint_loss_bwd",
+                          "rnnt_joint_loss_bwd_noalloc",
                           "rnnt_joint_loss_last_error",
                           "rnnt_joint_loss_status", "rnnt_joint_loss_timing",
                           "rnnt_joint_loss_timing_report", "rnnt_joint_proj_fwd",
@@ -171,3 +172,24 @@ def test_proj_rejects_before_launch():
     assert bwd(v(), v(), 0, 10, 64, 64, None, v(), v(), v(), None) == 1   # dy missing
     assert bwd(v(), v(), 0, 10, 64, 64, v(), v(), None, v(), None) == 1   # dW missing
     assert bwd(v(), v(), 0, 10, 48, 40, v(), v(), v(), v(), None) == 2    # N not a multiple of 16
+
+
+def test_noalloc_backward_rejects_sizes_beyond_its_scratch():
+    """The no-allocation backward refuses, before anything is enqueued, sizes
+    whose backward workspace exceeds its static scratch (64 MiB): the long
+    workload in 64 x 64 chunks needs ~0.3 GB of logit gradients per chunk."""
+    ws = _ws(8, 1500, 300, 640, 4096, 1, 64, 64, 256)[1]
+    assert ws > (64 << 20)
+    rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 8, 1500,
+                                         300, 640, 4096, 0, 64, 64, 256, None, None, None, None,
+                                         None, None, None)
+    assert rc == 3
+    rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 8, 1500,
+                                         300, 640, 4096, 0, 64, 64, 0, None, None, None, None,
+                                         None, None, None)
+    assert rc == 3
+    # bad sizes are reported as for the other entry points
+    rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 0, 10,
+                                         3, 64, 64, 0, 0, 0, 0, None, None, None, None,
+                                         None, None, None)
+    assert rc == 1
