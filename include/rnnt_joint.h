@@ -224,12 +224,61 @@ int rnnt_joint_loss_bwd_noalloc(const void* enc, const void* pred, const void* W
                                 void* stream);
 
 /*
+ * Pruned transducer loss ("Pruned RNN-T for fast, memory-efficient ASR
+ * training", Abstract: pruning bounds from a simple joiner linear in the two
+ * embeddings, then the full joiner evaluated inside them).
+ *
+ * rnnt_joint_loss_pruned_fwd: as rnnt_joint_loss_fwd (full sum, TILED mode
+ * only: tile_t or tile_u > 0), except that
+ *   1. the simple joiner zs(t,u) = (enc[t] + pred[u]) @ W_out + b_out (the
+ *      joiner without its tanh, same weights) is evaluated over the whole
+ *      lattice in float64 without a [T, U+1, V] tensor; its cost goes to
+ *      simple_costs[b] (float32 [B], or NULL to skip);
+ *   2. each frame t gets a window of S label positions starting at s_t: the
+ *      window centred on the frame's occupancy-weighted mean label position
+ *      under the simple joiner's alignment posterior (rounded half up,
+ *      clamped to [0, max(0, U'+1-S)]), then made to hold an alignment (first
+ *      window at 0, starts non-decreasing and at most S-1 apart, last window
+ *      at max(0, U'+1-S));
+ *   3. costs[b] is minus the log of the full joiner's probability summed over
+ *      the alignments that stay inside the windows.  With S >= U'+1 that is
+ *      the full-sum cost.
+ * The window starts are kept in `saved`; rnnt_joint_loss_bwd (tiled, same
+ * arguments) then returns the gradients of sum_b grad_costs[b] costs[b] with
+ * the windows held fixed, evaluating the full joiner only on cell tiles
+ * that meet the band.  An utterance with U' > T' (S - 1) fits in no band: its
+ * cost is NaN, its gradients zero, and data-error bit 16 is set.  S >= 1,
+ * T <= 32000 (else RNNTJ_ERR_ARG / RNNTJ_ERR_UNSUPPORTED); the untiled mode
+ * and the maximum approximation are not offered (RNNTJ_ERR_UNSUPPORTED).
+ * `workspace` (device, 16-byte aligned) holds the float64 simple-joiner
+ * lattice: rnnt_joint_loss_pruned_workspace_bytes bytes (about
+ * 8 B (T + U + 1) V + 40 B (T+U)(U+1) per utterance).  `saved` is sized by
+ * rnnt_joint_loss_saved_bytes with the same tiles.
+ */
+int rnnt_joint_loss_pruned_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
+                                           size_t* out);
+/* Copies the window starts s_t of a pruned forward's `saved` (int32 [B, T],
+ * entries past T'_b repeat the last window) to the device buffer `bounds`,
+ * enqueued on `stream`.  Sizes and tiles as given to that forward. */
+int rnnt_joint_loss_pruned_bounds(const void* saved, int B, int T, int U, int H, int V,
+                                  int dtype, int tile_t, int tile_u, int tile_v,
+                                  int32_t* bounds, void* stream);
+int rnnt_joint_loss_pruned_fwd(const void* enc, const void* pred, const void* W_out,
+                               const void* b_out, int dtype, const int32_t* labels,
+                               const int32_t* T_lens, const int32_t* U_lens, int B, int T,
+                               int U, int H, int V, int blank, int tile_t, int tile_u,
+                               int tile_v, int S, float* costs, float* simple_costs,
+                               void* saved, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Synchronises `stream`, then copies the data-error word of `saved` to
  * *data_error: 0 = every utterance valid, else a bit mask (1 = a length out of
  * range, 2 = a label out of range or equal to blank, 4 = an untiled backward
  * ran on a state whose logits an earlier backward had already consumed, 8 = a
  * backward was given a state whose sizes, dtype, blank or mode do not match
- * its own arguments and computed nothing).
+ * its own arguments and computed nothing, 16 = no pruning band of the pruned
+ * forward holds an alignment of some utterance).
  * Returns a status code.
  */
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error);

@@ -20,7 +20,8 @@ from ._lib import (RNNTJ_BF16, RNNTJ_F32, RNNTJointError, check, declared_functi
                    load)
 
 __all__ = ["rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd", "rnnt_joint_loss_bwd_noalloc",
-           "rnnt_joint_loss_status",
+           "rnnt_joint_loss_status", "rnnt_joint_loss_pruned_fwd",
+           "rnnt_joint_loss_pruned_workspace_bytes", "rnnt_joint_loss_pruned_bounds",
            "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
            "rnnt_joint_loss", "RNNTJointError", "load"]
 
@@ -109,6 +110,58 @@ def rnnt_joint_loss_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, blank=0
                                        _ptr(costs), _ptr(saved), None, 0, _stream(enc.device))
     check(rc, "rnnt_joint_loss_fwd_ex")
     return costs, saved
+
+
+def rnnt_joint_loss_pruned_workspace_bytes(B, T, U, H, V, dtype_code) -> int:
+    out = ctypes.c_size_t(0)
+    check(load().rnnt_joint_loss_pruned_workspace_bytes(B, T, U, H, V, dtype_code,
+                                                        ctypes.byref(out)),
+          "rnnt_joint_loss_pruned_workspace_bytes")
+    return out.value
+
+
+def rnnt_joint_loss_pruned_fwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, S, blank=0,
+                               tile_t=64, tile_u=0, tile_v=0, costs=None, simple_costs=None,
+                               saved=None, workspace=None):
+    """Pruned transducer loss (tiled mode): costs [B], simple_costs [B] (the
+    simple joiner's cost) and `saved`, from which rnnt_joint_loss_bwd with the
+    same tiles returns the gradients with the windows held fixed."""
+    import torch
+    B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
+    dc = _dtype_code(enc)
+    dev = enc.device
+    nbytes = rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v)
+    if saved is None:
+        saved = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    elif saved.numel() < nbytes:
+        raise ValueError(f"saved buffer too small ({saved.numel()} < {nbytes})")
+    ws = rnnt_joint_loss_pruned_workspace_bytes(B, T, U, H, V, dc)
+    if workspace is None:
+        workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws:
+        raise ValueError(f"workspace too small ({workspace.numel()} < {ws})")
+    if costs is None:
+        costs = torch.empty(B, dtype=torch.float32, device=dev)
+    if simple_costs is None:
+        simple_costs = torch.empty(B, dtype=torch.float32, device=dev)
+    rc = load().rnnt_joint_loss_pruned_fwd(_ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out), dc,
+                                           _ptr(labels), _ptr(T_lens), _ptr(U_lens), B, T, U, H,
+                                           V, blank, tile_t, tile_u, tile_v, S, _ptr(costs),
+                                           _ptr(simple_costs), _ptr(saved), _ptr(workspace),
+                                           workspace.numel(), _stream(dev))
+    check(rc, "rnnt_joint_loss_pruned_fwd")
+    return costs, simple_costs, saved
+
+
+def rnnt_joint_loss_pruned_bounds(saved, B, T, U, H, V, dtype_code, tile_t=64, tile_u=0,
+                                  tile_v=0):
+    """Window starts int32 [B, T] of a pruned forward's state."""
+    import torch
+    out = torch.empty(B, T, dtype=torch.int32, device=saved.device)
+    check(load().rnnt_joint_loss_pruned_bounds(_ptr(saved), B, T, U, H, V, dtype_code, tile_t,
+                                               tile_u, tile_v, _ptr(out), _stream(saved.device)),
+          "rnnt_joint_loss_pruned_bounds")
+    return out
 
 
 def rnnt_joint_loss_bwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, blank=0,

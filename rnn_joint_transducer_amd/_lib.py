@@ -34,6 +34,10 @@ _SIG = {
                             + [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "rnnt_joint_loss_bwd_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]
                                     + [_c_int] * 9 + [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "rnnt_joint_loss_pruned_workspace_bytes": (_c_int, [_c_int] * 6 + [ctypes.POINTER(_c_size)]),
+    "rnnt_joint_loss_pruned_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]
+                                   + [_c_int] * 10 + [_vp, _vp, _vp, _vp, _c_size, _vp]),
+    "rnnt_joint_loss_pruned_bounds": (_c_int, [_vp] + [_c_int] * 9 + [_vp, _vp]),
     "rnnt_joint_loss_status": (_c_int, [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]),
     "rnnt_joint_loss_timing": (_c_int, [_c_int]),
     "rnnt_joint_loss_timing_report": (_c_int, [ctypes.c_char_p, _c_size]),

@@ -22,6 +22,9 @@ using namespace rnntj;
 namespace {
 
 constexpr size_t kAlign = 256;
+// Longest padded time axis of the pruned forward (its window starts of one
+// utterance are kept in 64 KB of LDS as 16-bit values)
+constexpr int kMaxPrunedT = 32000;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
@@ -35,6 +38,10 @@ struct Plan {
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
       o_tiles, o_tcount, o_z;
   size_t o_zm;  // untiled bf16: the per-(row, vocabulary step) logit offsets
+  size_t o_bounds;  // pruning window starts [B, T] int32 (written by a pruned forward)
+  // pruned forward workspace (float64 simple-joiner lattice; byte offsets)
+  size_t o_pw_am, o_pw_lm, o_pw_ma, o_pw_ml, o_pw_amB, o_pw_amY, o_pw_lmB, o_pw_lmY, o_pw_LB,
+      o_pw_LE, o_pw_alpha, o_pw_beta, o_pw_logP, o_pw_centres, ws_pruned;
   int zstep;    // vocabulary columns per forward step (the offsets' granularity)
   size_t saved_bytes;
   size_t ws_fwd, ws_bwd;
@@ -103,8 +110,33 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_zm = o;
   if (q.untiled && bf16)
     o = align_up(o + 4 * (size_t)B * q.d.Tpad * q.d.U1pad * ((V + q.zstep - 1) / q.zstep));
+  q.o_bounds = o;
+  o = align_up(o + 4 * (size_t)B * T);
   q.saved_bytes = o;
   q.ws_fwd = 0;
+  {
+    size_t w = 0;
+    auto put = [&](size_t& off, size_t n) {
+      off = w;
+      w = align_up(w + 8 * n);
+    };
+    const size_t rt = (size_t)B * T, ru = (size_t)B * (U + 1);
+    put(q.o_pw_am, rt * V);
+    put(q.o_pw_lm, ru * V);
+    put(q.o_pw_ma, rt);
+    put(q.o_pw_ml, ru);
+    put(q.o_pw_amB, rt);
+    put(q.o_pw_amY, rt * (U > 0 ? U : 1));
+    put(q.o_pw_lmB, ru);
+    put(q.o_pw_lmY, ru);
+    put(q.o_pw_LB, cells);
+    put(q.o_pw_LE, cells);
+    put(q.o_pw_alpha, cells);
+    put(q.o_pw_beta, cells);
+    put(q.o_pw_logP, B);
+    put(q.o_pw_centres, rt);
+    q.ws_pruned = w;
+  }
   // backward workspace: float64 d_b_out accumulator [V], then (tiled) one
   // chunk of logit gradients [B, CT, CU, V] and its joint activations h
   // [B, CT, CU, H] (untiled: none, the forward keeps h)
@@ -222,6 +254,159 @@ int scratch_for(hipStream_t st, void** out) {
   return RNNTJ_OK;
 }
 
+// The forward of both entry points: S = 0 the full lattice (criterion sum or
+// max); S > 0 the pruned loss (full sum inside the band of S label positions
+// per frame that the simple joiner's lattice selects; tiled mode only).
+int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b_out, int dtype,
+             const int32_t* labels, const int32_t* T_lens, const int32_t* U_lens, int B, int T,
+             int U, int H, int V, int blank, int tile_t, int tile_u, int tile_v, int criterion,
+             int S, float* costs, float* simple_costs, void* saved, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
+  if (rc) return rc;
+  if (criterion != RNNTJ_CRIT_SUM && criterion != RNNTJ_CRIT_MAX) return RNNTJ_ERR_ARG;
+  const bool pruned = S > 0;
+  if (S < 0) return RNNTJ_ERR_ARG;
+  if (pruned) {
+    if (criterion != RNNTJ_CRIT_SUM || p.untiled || T > kMaxPrunedT) return RNNTJ_ERR_UNSUPPORTED;
+    if (workspace_bytes < p.ws_pruned || !workspace) return RNNTJ_ERR_WORKSPACE;
+    if (misaligned(workspace) || misaligned(simple_costs)) return RNNTJ_ERR_ARG;
+  }
+  const int crit = criterion == RNNTJ_CRIT_MAX ? kCritMax : kCritSum;
+  if (!enc || !pred || !W_out || !b_out || !T_lens || !U_lens || !costs || !saved)
+    return RNNTJ_ERR_ARG;
+  if (U > 0 && !labels) return RNNTJ_ERR_ARG;
+  if (blank < 0 || blank >= V) return RNNTJ_ERR_ARG;
+  if (misaligned(enc) || misaligned(pred) || misaligned(W_out) || misaligned(saved))
+    return RNNTJ_ERR_ARG;
+  if (workspace_bytes < p.ws_fwd) return RNNTJ_ERR_WORKSPACE;
+  p.d.blank = blank;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  int32_t* status = at<int32_t>(saved, p.o_status);
+  int32_t* Teff = at<int32_t>(saved, p.o_teff);
+  int32_t* Ueff = at<int32_t>(saved, p.o_ueff);
+  double* logP = at<double>(saved, p.o_logp);
+  void* Wt = at<char>(saved, p.o_wt);
+  float* lse = at<float>(saved, p.o_lse);
+  float* LB = at<float>(saved, p.o_lb);
+  float* LE = at<float>(saved, p.o_le);
+  double* alpha = at<double>(saved, p.o_alpha);
+  double* beta = at<double>(saved, p.o_beta);
+
+  hipError_t e;
+  if ((e = timed("zero", st, [&] { return launch_zero(status, kHdrWords, st); })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  const int32_t tag = plan_tag(p, blank);
+  if ((e = timed("validate", st, [&] {
+         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, crit, tag,
+                                p.untiled ? 1 : 0, S, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  float* Eexp = at<float>(saved, p.o_E);
+  float* Pexp = at<float>(saved, p.o_P);
+  if ((e = timed("prep", st, [&] {
+         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Wt, Eexp, Pexp, status, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+
+  int32_t* bounds = at<int32_t>(saved, p.o_bounds);
+  if (pruned) {
+    // the simple joiner's lattice and the window of every frame; then every
+    // step weight starts at -inf, so that cells of tiles outside the band
+    // carry no alignment
+    PruneArgs g = {};
+    g.enc = enc;
+    g.pred = pred;
+    g.W = W_out;
+    g.bias = b_out;
+    g.bf16 = p.bf16;
+    g.labels = labels;
+    g.Teff = Teff;
+    g.Ueff = Ueff;
+    g.status = status;
+    g.d = p.d;
+    g.S = S;
+    g.am = at<double>(workspace, p.o_pw_am);
+    g.lm = at<double>(workspace, p.o_pw_lm);
+    g.ma = at<double>(workspace, p.o_pw_ma);
+    g.ml = at<double>(workspace, p.o_pw_ml);
+    g.amB = at<double>(workspace, p.o_pw_amB);
+    g.amY = at<double>(workspace, p.o_pw_amY);
+    g.lmB = at<double>(workspace, p.o_pw_lmB);
+    g.lmY = at<double>(workspace, p.o_pw_lmY);
+    g.LBs = at<double>(workspace, p.o_pw_LB);
+    g.LEs = at<double>(workspace, p.o_pw_LE);
+    g.alpha = at<double>(workspace, p.o_pw_alpha);
+    g.beta = at<double>(workspace, p.o_pw_beta);
+    g.logPs = at<double>(workspace, p.o_pw_logP);
+    g.centres = at<double>(workspace, p.o_pw_centres);
+    g.simple_costs = simple_costs;
+    g.bounds = bounds;
+    if ((e = timed("pruning_bounds", st, [&] { return launch_pruning_bounds(g, st); })) !=
+        hipSuccess)
+      return RNNTJ_ERR_HIP;
+    const size_t cells = (size_t)B * p.d.DG * p.d.U1;
+    if ((e = timed("fill", st, [&] {
+           hipError_t r = launch_fill(LB, cells, -__builtin_inff(), st);
+           return r != hipSuccess ? r : launch_fill(LE, cells, -__builtin_inff(), st);
+         })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
+  }
+
+  int32_t* tiles = at<int32_t>(saved, p.o_tiles);
+  int32_t* tcount = at<int32_t>(saved, p.o_tcount);
+  if ((e = timed("tile_list", st, [&] {
+         return launch_tile_list(Teff, Ueff, p.d, p.d.Tpad, p.d.U1pad, 1, 1, p.cap_all, tiles,
+                                 tcount, status, bounds, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+
+  JointArgs a = {};
+  a.enc = enc;
+  a.pred = pred;
+  a.Wt = Wt;
+  a.bias = b_out;
+  a.labels = labels;
+  a.Teff = Teff;
+  a.Ueff = Ueff;
+  a.hdr = status;
+  a.Eexp = Eexp;
+  a.Pexp = Pexp;
+  a.tiles = tiles;
+  a.tile_count = tcount;
+  a.vsplit = 1;
+  a.d = p.d;
+  a.ct0 = 0;
+  a.cu0 = 0;
+  a.CT = p.d.Tpad;
+  a.CU = p.d.U1pad;
+  a.n_tu = p.d.U1pad / kTileU;
+  a.lse = lse;
+  a.LB = LB;
+  a.LE = LE;
+  a.zout = p.untiled ? at<char>(saved, p.o_z) : nullptr;
+  a.hout = p.untiled ? at<char>(saved, p.o_h) : nullptr;
+  a.zmax = (p.untiled && p.bf16) ? at<float>(saved, p.o_zm) : nullptr;
+  a.zstep = p.zstep;
+  a.bounds = bounds;
+  a.band = S;
+  if ((e = timed(p.untiled ? "joint_fwd_store" : "joint_fwd", st, [&] {
+         return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, p.cap_all, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  if ((e = timed("lattice", st, [&] {
+         return launch_lattice(LB, LE, Teff, Ueff, p.d, alpha, beta, logP, costs, crit, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  if (crit == kCritMax &&
+      (e = timed("backtrace", st, [&] { return launch_backtrace(Teff, Ueff, p.d, beta, st); })) !=
+          hipSuccess)
+    return RNNTJ_ERR_HIP;
+  return RNNTJ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -276,97 +461,47 @@ int rnnt_joint_loss_fwd_ex(const void* enc, const void* pred, const void* W_out,
                            int H, int V, int blank, int tile_t, int tile_u, int tile_v,
                            int criterion, float* costs, void* saved, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  (void)workspace;
+  return fwd_impl(enc, pred, W_out, b_out, dtype, labels, T_lens, U_lens, B, T, U, H, V, blank,
+                  tile_t, tile_u, tile_v, criterion, 0, costs, nullptr, saved, workspace,
+                  workspace_bytes, stream);
+}
+
+int rnnt_joint_loss_pruned_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
+                                           size_t* out) {
+  if (!out) return RNNTJ_ERR_ARG;
   Plan p;
-  int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
+  const int rc = make_plan(B, T, U, H, V, dtype, kTileT, kTileU, 0, &p);
   if (rc) return rc;
-  if (criterion != RNNTJ_CRIT_SUM && criterion != RNNTJ_CRIT_MAX) return RNNTJ_ERR_ARG;
-  const int crit = criterion == RNNTJ_CRIT_MAX ? kCritMax : kCritSum;
-  if (!enc || !pred || !W_out || !b_out || !T_lens || !U_lens || !costs || !saved)
-    return RNNTJ_ERR_ARG;
-  if (U > 0 && !labels) return RNNTJ_ERR_ARG;
-  if (blank < 0 || blank >= V) return RNNTJ_ERR_ARG;
-  if (misaligned(enc) || misaligned(pred) || misaligned(W_out) || misaligned(saved))
-    return RNNTJ_ERR_ARG;
-  if (workspace_bytes < p.ws_fwd) return RNNTJ_ERR_WORKSPACE;
-  p.d.blank = blank;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-
-  int32_t* status = at<int32_t>(saved, p.o_status);
-  int32_t* Teff = at<int32_t>(saved, p.o_teff);
-  int32_t* Ueff = at<int32_t>(saved, p.o_ueff);
-  double* logP = at<double>(saved, p.o_logp);
-  void* Wt = at<char>(saved, p.o_wt);
-  float* lse = at<float>(saved, p.o_lse);
-  float* LB = at<float>(saved, p.o_lb);
-  float* LE = at<float>(saved, p.o_le);
-  double* alpha = at<double>(saved, p.o_alpha);
-  double* beta = at<double>(saved, p.o_beta);
-
-  hipError_t e;
-  if ((e = timed("zero", st, [&] { return launch_zero(status, kHdrWords, st); })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-  const int32_t tag = plan_tag(p, blank);
-  if ((e = timed("validate", st, [&] {
-         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, crit, tag,
-                                p.untiled ? 1 : 0, st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-  float* Eexp = at<float>(saved, p.o_E);
-  float* Pexp = at<float>(saved, p.o_P);
-  if ((e = timed("prep", st, [&] {
-         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Wt, Eexp, Pexp, status, st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-
-  int32_t* tiles = at<int32_t>(saved, p.o_tiles);
-  int32_t* tcount = at<int32_t>(saved, p.o_tcount);
-  if ((e = timed("tile_list", st, [&] {
-         return launch_tile_list(Teff, Ueff, p.d, p.d.Tpad, p.d.U1pad, 1, 1, p.cap_all, tiles,
-                                 tcount, st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-
-  JointArgs a = {};
-  a.enc = enc;
-  a.pred = pred;
-  a.Wt = Wt;
-  a.bias = b_out;
-  a.labels = labels;
-  a.Teff = Teff;
-  a.Ueff = Ueff;
-  a.hdr = status;
-  a.Eexp = Eexp;
-  a.Pexp = Pexp;
-  a.tiles = tiles;
-  a.tile_count = tcount;
-  a.vsplit = 1;
-  a.d = p.d;
-  a.ct0 = 0;
-  a.cu0 = 0;
-  a.CT = p.d.Tpad;
-  a.CU = p.d.U1pad;
-  a.n_tu = p.d.U1pad / kTileU;
-  a.lse = lse;
-  a.LB = LB;
-  a.LE = LE;
-  a.zout = p.untiled ? at<char>(saved, p.o_z) : nullptr;
-  a.hout = p.untiled ? at<char>(saved, p.o_h) : nullptr;
-  a.zmax = (p.untiled && p.bf16) ? at<float>(saved, p.o_zm) : nullptr;
-  a.zstep = p.zstep;
-  if ((e = timed(p.untiled ? "joint_fwd_store" : "joint_fwd", st, [&] {
-         return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, p.cap_all, st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-  if ((e = timed("lattice", st, [&] {
-         return launch_lattice(LB, LE, Teff, Ueff, p.d, alpha, beta, logP, costs, crit, st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-  if (crit == kCritMax &&
-      (e = timed("backtrace", st, [&] { return launch_backtrace(Teff, Ueff, p.d, beta, st); })) !=
-          hipSuccess)
-    return RNNTJ_ERR_HIP;
+  if (T > kMaxPrunedT) return RNNTJ_ERR_UNSUPPORTED;
+  *out = p.ws_pruned;
   return RNNTJ_OK;
+}
+
+int rnnt_joint_loss_pruned_fwd(const void* enc, const void* pred, const void* W_out,
+                               const void* b_out, int dtype, const int32_t* labels,
+                               const int32_t* T_lens, const int32_t* U_lens, int B, int T, int U,
+                               int H, int V, int blank, int tile_t, int tile_u, int tile_v, int S,
+                               float* costs, float* simple_costs, void* saved, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (S < 1) return RNNTJ_ERR_ARG;
+  return fwd_impl(enc, pred, W_out, b_out, dtype, labels, T_lens, U_lens, B, T, U, H, V, blank,
+                  tile_t, tile_u, tile_v, RNNTJ_CRIT_SUM, S, costs, simple_costs, saved,
+                  workspace, workspace_bytes, stream);
+}
+
+int rnnt_joint_loss_pruned_bounds(const void* saved, int B, int T, int U, int H, int V, int dtype,
+                                  int tile_t, int tile_u, int tile_v, int32_t* bounds,
+                                  void* stream) {
+  Plan p;
+  const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
+  if (rc) return rc;
+  if (!saved || !bounds) return RNNTJ_ERR_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const void* src = static_cast<const char*>(saved) + p.o_bounds;
+  return note_error("bounds copy", hipMemcpyAsync(bounds, src, 4 * (size_t)B * T,
+                                                  hipMemcpyDeviceToDevice, st)) == hipSuccess
+             ? RNNTJ_OK
+             : RNNTJ_ERR_HIP;
 }
 
 int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, const void* b_out,
@@ -512,7 +647,8 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
   int32_t* ccount = at<int32_t>(workspace, p.o_ws_tcount);
   if ((e = timed("tile_list", st, [&] {
          return launch_tile_list(Teff, Ueff, p.d, p.CT, p.CU, p.n_cu_chunks, p.n_chunks,
-                                 p.cap_chunk, ctiles, ccount, st);
+                                 p.cap_chunk, ctiles, ccount, hdr, at<int32_t>(saved, p.o_bounds),
+                                 st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   int chunk = 0;

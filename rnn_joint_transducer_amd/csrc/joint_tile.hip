@@ -212,6 +212,25 @@ __device__ __forceinline__ int ts_idx(int col, int row) {
 
 }  // namespace
 
+// Pruned forward: the blank and label steps out of cell (t,u) of utterance b
+// are kept only when both ends lie in the band s_t <= u <= s_t + S - 1
+// (the final blank at (T'-1, U') always does); others get -inf.
+__device__ __forceinline__ void band_mask(const JointArgs& a, int b, int t, int u, int Tl, int Ul,
+                                          float& lb, float& le) {
+  const int32_t* s = a.bounds + (size_t)b * a.d.T;
+  const int S = a.band, s0 = s[t];
+  const bool in = u >= s0 && u <= s0 + S - 1;
+  bool nb;
+  if (t + 1 < Tl) {
+    const int s1 = s[t + 1];
+    nb = u >= s1 && u <= s1 + S - 1;
+  } else {
+    nb = u == Ul;
+  }
+  if (!(in && nb)) lb = -kInf;
+  if (!(in && u + 1 <= s0 + S - 1)) le = -kInf;
+}
+
 // Largest hidden size whose 24 exponential rows are staged in LDS (the
 // budget left next to the W^T slices and the store staging); with two
 // workgroups per compute unit the rows are read from global memory instead.
@@ -819,9 +838,11 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
       if (t < Tl && u <= Ul) {
         const float lse = ((bounded ? 0.f : mrow) + __builtin_amdgcn_logf(srow)) * kLn2;
         const size_t ix = skew_idx(d, b, t, u);
+        float lb = cap_blank[rowi] - lse, le = (u < Ul) ? cap_label[rowi] - lse : 0.f;
+        if (MODE == kLse && a.band > 0) band_mask(a, b, t, u, Tl, Ul, lb, le);
         a.lse[ix] = lse;
-        a.LB[ix] = cap_blank[rowi] - lse;
-        a.LE[ix] = (u < Ul) ? cap_label[rowi] - lse : 0.f;
+        a.LB[ix] = lb;
+        a.LE[ix] = le;
       }
     }
   }
@@ -864,9 +885,11 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
       if (t < Tl && u <= Ul) {
         const float lse = (m + __builtin_amdgcn_logf(sm)) * kLn2;
         const size_t ix = skew_idx(d, b, t, u);
+        float lb = cap_blank[rowi] - lse, le = (u < Ul) ? cap_label[rowi] - lse : 0.f;
+        if (MODE == kLse && a.band > 0) band_mask(a, b, t, u, Tl, Ul, lb, le);
         a.lse[ix] = lse;
-        a.LB[ix] = cap_blank[rowi] - lse;
-        a.LE[ix] = (u < Ul) ? cap_label[rowi] - lse : 0.f;
+        a.LB[ix] = lb;
+        a.LE[ix] = le;
       }
     }
   }

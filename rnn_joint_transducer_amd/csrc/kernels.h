@@ -26,6 +26,11 @@ constexpr int kErrPlan = 8;
 // state (every later kernel of that backward returns at once).
 constexpr int kHdrWords = 8;
 constexpr int kHdrRefuse = 6;
+// Header word 7: the pruning window S of a pruned forward (0: the full lattice).
+constexpr int kHdrBand = 7;
+// data-error bit: no band of pruning windows holds an alignment of the
+// utterance (U' > T' (S - 1)); it is then treated as invalid
+constexpr int kErrPruneInfeasible = 16;
 
 // Active-tile lists.  A lattice chunk (frames ct0 .. ct0+CT-1, label
 // positions cu0 .. cu0+CU-1) is covered by 16 x 8 cell tiles; a tile is
@@ -39,9 +44,11 @@ __device__ inline void tile_unpack(int v, int& b, int& tt, int& tu) {
   tt = (v >> 6) & 0xfff;
   tu = v & 63;
 }
+// With a pruned forward's state (hdr[kHdrBand] = S > 0) only tiles holding a
+// cell of the band s_t <= u <= s_t + S - 1 (bounds [B, T]) are listed.
 hipError_t launch_tile_list(const int32_t* Teff, const int32_t* Ueff, const Dims& d, int CT, int CU,
                             int n_chunks_u, int n_chunks, int cap, int32_t* list, int32_t* count,
-                            hipStream_t st);
+                            const int32_t* hdr, const int32_t* bounds, hipStream_t st);
 
 struct JointArgs {
   const void* enc;
@@ -71,6 +78,10 @@ struct JointArgs {
   // zmax [B, Tpad, U1pad, ceil(V / zstep)]; read back as stored + M
   float* zmax;
   int zstep;
+  // kLse of a pruned forward: window starts [B, T] and width band (0: none);
+  // steps that leave the band get log-probability -inf
+  const int32_t* bounds;
+  int band;
   // backward inputs / output
   const double* alpha;
   const double* beta;
@@ -96,7 +107,7 @@ hipError_t launch_joint_tile(const JointArgs& a, int mode, bool bf16, int n_item
 hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
                            int32_t* Ueff, int32_t* status, int crit, int32_t tag,
-                           int has_logits, hipStream_t st);
+                           int has_logits, int band, hipStream_t st);
 // Backward's first check of the state header (see kErrPlan).
 hipError_t launch_guard(int32_t* hdr, int32_t tag, int need_logits, hipStream_t st);
 
@@ -106,6 +117,43 @@ hipError_t launch_guard(int32_t* hdr, int32_t tag, int need_logits, hipStream_t 
 hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
                        bool bf16, const Dims& d, void* Wt, float* Eexp, float* Pexp,
                        int32_t* hdr, hipStream_t st);
+
+// Pruning bounds of the pruned transducer loss (pruned.hip): the simple
+// joiner's lattice in float64 and the window start of every frame.
+struct PruneArgs {
+  const void* enc;
+  const void* pred;
+  const void* W;     // W_out [H, V]
+  const void* bias;  // b_out [V]
+  bool bf16;
+  const int32_t* labels;
+  int32_t* Teff;     // zeroed for an utterance no band can hold
+  int32_t* Ueff;
+  int32_t* status;   // kErrPruneInfeasible
+  Dims d;
+  int S;
+  // float64 workspace
+  double* am;        // [B, T, V]
+  double* lm;        // [B, U+1, V]
+  double* ma;        // [B, T]
+  double* ml;        // [B, U+1]
+  double* amB;       // [B, T]
+  double* amY;       // [B, T, U]
+  double* lmB;       // [B, U+1]
+  double* lmY;       // [B, U+1]
+  double* LBs;       // diagonal-skewed [B, T+U, U+1]
+  double* LEs;
+  double* alpha;
+  double* beta;
+  double* logPs;     // [B]
+  double* centres;   // [B, T]
+  // outputs
+  float* simple_costs;  // [B] or null
+  int32_t* bounds;      // [B, T]
+};
+hipError_t launch_pruning_bounds(const PruneArgs& p, hipStream_t st);
+// p[i] = v for i < n
+hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
 
 // Fill n floats / int32s with zero (a kernel, never a memset node); the
 // four-buffer form zeroes up to four (null pointers skipped) in one launch.

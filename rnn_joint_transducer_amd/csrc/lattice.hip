@@ -427,13 +427,14 @@ __global__ void validate_kernel(const int32_t* __restrict__ T_lens,
                                 const int32_t* __restrict__ labels, Dims d,
                                 int32_t* __restrict__ Teff, int32_t* __restrict__ Ueff,
                                 int32_t* __restrict__ status, int crit, int32_t tag,
-                                int has_logits) {
+                                int has_logits, int band) {
   __shared__ int sbad;
   const int b = blockIdx.x;
   if (b == 0 && threadIdx.x == 0) {
     status[3] = crit;  // header word 3: the criterion
     status[4] = tag;   // words 4, 5: what a backward from this state must match
     status[5] = has_logits;
+    status[kHdrBand] = band;
   }
   if (threadIdx.x == 0) sbad = 0;
   __syncthreads();
@@ -545,25 +546,47 @@ __global__ __launch_bounds__(256) void tile_list_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ Ueff, Dims d,
                                                         int CT, int CU, int n_chunks_u, int cap,
                                                         int32_t* __restrict__ list,
-                                                        int32_t* __restrict__ count) {
+                                                        int32_t* __restrict__ count,
+                                                        const int32_t* __restrict__ hdr,
+                                                        const int32_t* __restrict__ bounds) {
   __shared__ int s_base;
-  const int c = blockIdx.x;
+  __shared__ int s_wave[4];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int ct0 = (c / n_chunks_u) * CT, cu0 = (c % n_chunks_u) * CU;
+  const int S = hdr ? hdr[kHdrBand] : 0;  // pruning window (0: every tile)
   int32_t* out = list + (size_t)c * cap;
-  if (threadIdx.x == 0) s_base = 0;
+  if (tid == 0) s_base = 0;
   __syncthreads();
   for (int b = 0; b < d.B; ++b) {
-    const int tv = min(CT, Teff[b] - ct0), uv = min(CU, Ueff[b] + 1 - cu0);
-    const int nt = tv > 0 && Teff[b] > 0 ? (tv + kTileT - 1) / kTileT : 0;
+    const int Tl = Teff[b], Ul = Ueff[b];
+    const int tv = min(CT, Tl - ct0), uv = min(CU, Ul + 1 - cu0);
+    const int nt = tv > 0 && Tl > 0 ? (tv + kTileT - 1) / kTileT : 0;
     const int nu = uv > 0 ? (uv + kTileU - 1) / kTileU : 0;
-    const int base = s_base;
-    for (int i = threadIdx.x; i < nt * nu; i += blockDim.x)
-      out[base + i] = tile_pack(b, i / nu, i % nu);
-    __syncthreads();
-    if (threadIdx.x == 0) s_base = base + nt * nu;
-    __syncthreads();
+    // tiles in order; with a band, a tile is kept when the band's label
+    // positions over its frames, [s_first, s_last + S - 1] (s is
+    // non-decreasing), meet its own
+    for (int i0 = 0; i0 < nt * nu; i0 += 256) {
+      const int i = i0 + tid;
+      bool keep = i < nt * nu;
+      if (keep && S > 0) {
+        const int t0 = ct0 + (i / nu) * kTileT, u0 = cu0 + (i % nu) * kTileU;
+        const int t1 = min(t0 + kTileT, Tl) - 1, u1 = min(u0 + kTileU - 1, Ul);
+        const int32_t* s = bounds + (size_t)b * d.T;
+        keep = s[t0] <= u1 && s[t1] + S - 1 >= u0;
+      }
+      const unsigned long long m = __ballot(keep);
+      if (lane == 0) s_wave[w] = __popcll(m);
+      __syncthreads();
+      int off = s_base;
+      for (int k = 0; k < w; ++k) off += s_wave[k];
+      const int tot = s_wave[0] + s_wave[1] + s_wave[2] + s_wave[3];
+      if (keep) out[off + __popcll(m & ((1ull << lane) - 1ull))] = tile_pack(b, i / nu, i % nu);
+      __syncthreads();
+      if (tid == 0) s_base += tot;
+      __syncthreads();
+    }
   }
-  if (threadIdx.x == 0) count[c] = s_base;
+  if (tid == 0) count[c] = s_base;
 }
 
 // Zeroes up to four buffers (32-bit words) in one launch.
@@ -621,18 +644,18 @@ hipError_t launch_backtrace(const int32_t* Teff, const int32_t* Ueff, const Dims
 
 hipError_t launch_tile_list(const int32_t* Teff, const int32_t* Ueff, const Dims& d, int CT, int CU,
                             int n_chunks_u, int n_chunks, int cap, int32_t* list, int32_t* count,
-                            hipStream_t st) {
+                            const int32_t* hdr, const int32_t* bounds, hipStream_t st) {
   hipLaunchKernelGGL(tile_list_kernel, dim3(n_chunks), dim3(256), 0, st, Teff, Ueff, d, CT, CU,
-                     n_chunks_u, cap, list, count);
+                     n_chunks_u, cap, list, count, hdr, bounds);
   return hipGetLastError();
 }
 
 hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
                            const int32_t* labels, const Dims& d, int32_t* Teff,
                            int32_t* Ueff, int32_t* status, int crit, int32_t tag,
-                           int has_logits, hipStream_t st) {
+                           int has_logits, int band, hipStream_t st) {
   hipLaunchKernelGGL(validate_kernel, dim3(d.B), dim3(256), 0, st, T_lens, U_lens, labels, d,
-                     Teff, Ueff, status, crit, tag, has_logits);
+                     Teff, Ueff, status, crit, tag, has_logits, band);
   return hipGetLastError();
 }
 

@@ -15,7 +15,8 @@ def test_exports_every_declared_symbol():
     assert set(names) == {"rnnt_joint_loss_abi_version", "rnnt_joint_loss_strerror",
                           "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
                           "rnnt_joint_loss_fwd", "rnnt_joint_loss_fwd_ex", "rnnt_joint_loss_bwd",
-                          "rnnt_joint_loss_bwd_noalloc",
+                          "rnnt_joint_loss_bwd_noalloc", "rnnt_joint_loss_pruned_fwd",
+                          "rnnt_joint_loss_pruned_workspace_bytes", "rnnt_joint_loss_pruned_bounds",
                           "rnnt_joint_loss_last_error",
                           "rnnt_joint_loss_status", "rnnt_joint_loss_timing",
                           "rnnt_joint_loss_timing_report", "rnnt_joint_proj_fwd",
@@ -193,3 +194,22 @@ def test_noalloc_backward_rejects_sizes_beyond_its_scratch():
                                          3, 64, 64, 0, 0, 0, 0, None, None, None, None,
                                          None, None, None)
     assert rc == 1
+
+
+def test_pruned_forward_host_checks():
+    """The pruned forward refuses, before anything is enqueued: the untiled
+    mode, a window below one position, too long a time axis, and a
+    workspace smaller than rnnt_joint_loss_pruned_workspace_bytes."""
+    out = ctypes.c_size_t(0)
+    assert lib.rnnt_joint_loss_pruned_workspace_bytes(2, 20, 5, 64, 32, 0, ctypes.byref(out)) == 0
+    ws = out.value
+    # float64 simple-joiner rows (am, lm), per-cell lattice arrays and row scalars
+    assert ws >= 8 * 2 * (20 + 6) * 32 + 4 * 8 * 2 * 25 * 6
+    assert lib.rnnt_joint_loss_pruned_workspace_bytes(1, 32001, 5, 64, 32, 0,
+                                                      ctypes.byref(out)) == 2
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its host checks
+    args = lambda tt, tu, S, wsb: (p, p, p, p, 0, p, p, p, 2, 20, 5, 64, 32, 0, tt, tu, 0, S, p,
+                                   None, p, p, wsb, None)
+    assert lib.rnnt_joint_loss_pruned_fwd(*args(0, 0, 3, ws)) == 2   # untiled
+    assert lib.rnnt_joint_loss_pruned_fwd(*args(16, 8, 0, ws)) == 1  # S < 1
+    assert lib.rnnt_joint_loss_pruned_fwd(*args(16, 8, 3, ws - 8)) == 3
