@@ -26,6 +26,10 @@ Sources, all on the pages that describe the method:
   bounds from a simple joiner linear in the two embeddings, then the full
   joiner evaluated inside them (``pruned.py``, pinned by
   ``tests/test_oracle_pruned_pins.py``).
+* "Daily Papers" page, Token-and-Duration Transducer abstract: a joint with
+  two independently normalised outputs, tokens and durations (frames a token
+  covers), whose lattice skips frames (``tdt.py``, pinned by
+  ``tests/test_oracle_tdt_pins.py``).
 
 Every function is pinned by the tests in ``tests/test_oracle_pins.py``
 (brute-force enumeration, alpha/beta agreement, closed forms, invariants,
@@ -46,3 +50,4 @@ from .rnnt import (  # noqa: F401
 )
 from .proj import linear, linear_grads, projected_loss_and_grads  # noqa: F401
 from . import pruned  # noqa: F401,E402
+from . import tdt  # noqa: F401,E402
