@@ -56,6 +56,12 @@ def parse():
     ap.add_argument("--proj", default=None, metavar="E,P",
                     help="put joint input projections (enc: E -> H, pred: P -> H) in front of the "
                          "joint, their gradients after it, inside the timed step")
+    ap.add_argument("--pruned", type=int, default=0, metavar="S",
+                    help="time the pruned transducer loss with windows of S label positions "
+                         "(tiled mode) instead of the full lattice")
+    ap.add_argument("--tdt", default=None, metavar="D0,D1,...",
+                    help="time the token-and-duration transducer loss with these durations "
+                         "(duration head from synth.make_duration_head, seed 1)")
     ap.add_argument("--tile-t", type=int, default=None)
     ap.add_argument("--tile-u", type=int, default=None)
     ap.add_argument("--tile-v", type=int, default=None)
@@ -111,7 +117,7 @@ def calibrate_copy(nbytes):
     print(json.dumps({"calibrate_copy_bytes": nbytes, "copies": 5}))
 
 
-def cpu_baseline(inp, target_s, criterion="sum", pj=None):
+def cpu_baseline(inp, target_s, criterion="sum", pj=None, pruned_S=0, head=None):
     """Float64 oracle (fwd+bwd, one utterance at a time, NumPy BLAS on all host
     threads) on a bounded sample of the workload: whole utterances in order
     until about target_s seconds are spent (whole passes over the batch
@@ -138,7 +144,16 @@ def cpu_baseline(inp, target_s, criterion="sum", pj=None):
 
     def run(b, t_s):
         t0 = time.perf_counter()
-        if pj is None:
+        if head is not None:
+            from oracle import tdt
+            tdt.utterance(inp.enc_f64[b, :t_s], inp.pred_f64[b], inp.W_f64, inp.b_f64,
+                          head.W_dur_f64, head.b_dur_f64, inp.labels[b], t_s, int(inp.U_lens[b]),
+                          inp.blank, head.durations)
+        elif pruned_S:
+            from oracle import pruned
+            pruned.utterance(inp.enc_f64[b, :t_s], inp.pred_f64[b], inp.W_f64, inp.b_f64,
+                             inp.labels[b], t_s, int(inp.U_lens[b]), inp.blank, pruned_S)
+        elif pj is None:
             rnnt.utterance_loss_and_grads(inp.enc_f64[b, :t_s], inp.pred_f64[b], inp.W_f64,
                                           inp.b_f64, inp.labels[b], t_s, int(inp.U_lens[b]),
                                           inp.blank, criterion=criterion)
@@ -187,7 +202,9 @@ def cpu_baseline(inp, target_s, criterion="sum", pj=None):
             "nproc": int(nproc or 1), "cpu_model": cpu_model,
             "numpy": np.__version__,
             "sample": f"{desc}: {sample_cells} valid cells in {el:.2f} s, float64 NumPy "
-                      f"fwd+bwd{'' if pj is None else ' with the input projections'}, scaled by "
+                      f"fwd+bwd{'' if pj is None else ' with the input projections'}"
+                      f"{'' if not pruned_S else f' (pruned loss, S={pruned_S})'}"
+                      f"{'' if head is None else f' (token-and-duration loss, durations {head.durations})'}, scaled by "
                       f"valid cells ({total_valid}) to the B*T*U metric"}
 
 
@@ -322,13 +339,46 @@ def main():
     grads = (torch.empty(B, T, H, device=dev), torch.empty(B, U + 1, H, device=dev),
              torch.empty(H, V, device=dev), torch.empty(V, device=dev))
 
+    head = None
+    if args.tdt:
+        from synth import make_duration_head
+        head = make_duration_head(inp, tuple(int(x) for x in args.tdt.split(",")), seed=1)
+        Wd, bd = conv(head.W_dur), conv(head.b_dur)
+        K = len(head.durations)
+        import ctypes
+        sz = ctypes.c_size_t(0)
+        _lib.check(_lib.load().rnnt_joint_loss_tdt_saved_bytes(B, T, U, H, V, dc, tt, tu, tv, K,
+                                                               ctypes.byref(sz)), "tdt_saved")
+        saved = torch.empty(sz.value, dtype=torch.uint8, device=dev)
+        _lib.check(_lib.load().rnnt_joint_loss_tdt_workspace_bytes(B, T, U, H, V, dc, tt, tu, tv,
+                                                                   K, 1, ctypes.byref(sz)),
+                   "tdt_ws")
+        ws = torch.empty(sz.value, dtype=torch.uint8, device=dev)
+    if args.pruned:
+        if tt == 0 and tu == 0:
+            sys.exit("bench.py: the pruned loss runs in the tiled mode (give --tile-t/--tile-u)")
+        pws = torch.empty(rj.rnnt_joint_loss_pruned_workspace_bytes(B, T, U, H, V, dc),
+                          dtype=torch.uint8, device=dev)
+        simple = torch.empty(B, dtype=torch.float32, device=dev)
+
     def step():
         if pj is not None:
             tensors["enc"] = rj.rnnt_joint_proj_fwd(ptens["enc_in"], ptens["W_enc"], ptens["b_enc"])
             tensors["pred"] = rj.rnnt_joint_proj_fwd(ptens["pred_in"], ptens["W_pred"],
                                                      ptens["b_pred"])
-        rj.rnnt_joint_loss_fwd(**tensors, tile_t=tt, tile_u=tu, tile_v=tv, costs=costs,
-                               saved=saved, criterion=args.criterion)
+        if head is not None:
+            rj.rnnt_joint_loss_tdt_fwd(**tensors, W_dur=Wd, b_dur=bd, durations=head.durations,
+                                       tile_t=tt, tile_u=tu, tile_v=tv, costs=costs, saved=saved)
+            rj.rnnt_joint_loss_tdt_bwd(**tensors, W_dur=Wd, b_dur=bd, durations=head.durations,
+                                       saved=saved, tile_t=tt, tile_u=tu, tile_v=tv, workspace=ws)
+            return
+        if args.pruned:
+            rj.rnnt_joint_loss_pruned_fwd(**tensors, S=args.pruned, tile_t=tt, tile_u=tu,
+                                          tile_v=tv, costs=costs, simple_costs=simple,
+                                          saved=saved, workspace=pws)
+        else:
+            rj.rnnt_joint_loss_fwd(**tensors, tile_t=tt, tile_u=tu, tile_v=tv, costs=costs,
+                                   saved=saved, criterion=args.criterion)
         rj.rnnt_joint_loss_bwd(**tensors, saved=saved, tile_t=tt, tile_u=tu, tile_v=tv,
                                workspace=ws, out=grads)
         if pj is not None:
@@ -370,12 +420,22 @@ def main():
     rep = _lib.timing_report()
     _lib.timing(False)
     valid = int(np.sum(inp.T_lens.astype(np.int64) * (inp.U_lens.astype(np.int64) + 1)))
+    band_cells = None
+    if args.pruned:
+        # cells of the band: the joint's algorithmic work in the pruned loss
+        bd = rj.rnnt_joint_loss_pruned_bounds(saved, B, T, U, H, V, dc, tt, tu, tv).cpu().numpy()
+        band_cells = 0
+        for b in range(B):
+            Tl, Ul = int(inp.T_lens[b]), int(inp.U_lens[b])
+            s0 = bd[b, :Tl].astype(np.int64)
+            band_cells += int(np.sum(np.minimum(s0 + args.pruned - 1, Ul) - s0 + 1))
+    work_cells = band_cells if band_cells is not None else valid
     kernels = {}
     for name, (n, tot) in rep.items():
         per_launch_ms = tot / n
         k = {"launches_per_step": n / kin, "ms_per_step": tot / kin, "ms_per_launch": per_launch_ms}
         if name in MFMA_KERNELS:
-            flops_step = 2.0 * H * V * valid
+            flops_step = 2.0 * H * V * work_cells
             k["tflops"] = flops_step / (tot / kin / 1e3) / 1e12
         elif name in PROJ_KERNELS and pj is not None:
             # each of the three products: 2 * rows * in_width * H per projection
@@ -387,7 +447,7 @@ def main():
     kd = kernels[dom]
     launches = kd["launches_per_step"]
     if dom in MFMA_KERNELS:
-        per_launch = 2.0 * H * V * valid / launches
+        per_launch = 2.0 * H * V * work_cells / launches
         achieved = per_launch / (kd["ms_per_launch"] / 1e3) / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[dt],
                 "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[dt], "traffic": None,
@@ -417,7 +477,7 @@ def main():
                "us_per_diagonal": kl["ms_per_launch"] * 1e3 / diags}
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(inp, args.cpu_seconds, args.criterion, pj)
+        cpu = cpu_baseline(inp, args.cpu_seconds, args.criterion, pj, args.pruned, head)
 
     line = {
         "metric": METRIC, "value": value, "unit": "cells/s", "n_gpus": 1,
@@ -427,7 +487,10 @@ def main():
         "ms_median": pct(50), "ms_p10": pct(10), "ms_p90": pct(90),
         "config": {"workload": args.workload, "B": B, "T": T, "U": U, "H": H, "V": V,
                    "mode": mode, "criterion": args.criterion,
-                   "proj": None if pj is None else {"E": pj.E, "P": pj.P}, "tile_t": tt, "tile_u": tu, "tile_v": tv,
+                   "proj": None if pj is None else {"E": pj.E, "P": pj.P},
+                   "pruned_S": args.pruned or None, "band_cells": band_cells,
+                   "tdt_durations": None if head is None else list(head.durations),
+                   "tile_t": tt, "tile_u": tu, "tile_v": tv,
                    "valid_cells": valid, "valid_cells_per_s": valid / (ms / 1e3),
                    "peak_gb": round(peak_gb, 3), "peak_gb_above_inputs": round(extra_gb, 3)},
         "roofline": roof,

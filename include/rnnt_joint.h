@@ -272,6 +272,56 @@ int rnnt_joint_loss_pruned_fwd(const void* enc, const void* pred, const void* W_
                                void* stream);
 
 /*
+ * Token-and-duration transducer ("Daily Papers" page, Token-and-Duration
+ * Transducer abstract: the joint has two outputs, normalised independently,
+ * over tokens and over durations -- the number of frames a token covers).
+ *
+ * A duration head W_dur [H, K], b_dur [K] (dtype) reads the same joint
+ * hidden h = tanh(enc[t] + pred[u]) as the token head; durations[K] (HOST
+ * int32 array, K <= 8 distinct values in [0, 15], at least one >= 1) lists
+ * the frames each duration class covers.  P(v, d_k | t, u) =
+ * softmax(h W_out + b_out)[v] * softmax(h W_dur + b_dur)[k].  Steps out of
+ * cell (t,u): a blank of duration d_k >= 1 to (t + d_k, u) (a blank of
+ * duration 0 would not move and is no step), label labels[b,u] (u < U') of
+ * duration d_k to (t + d_k, u + 1); an alignment starts at (0,0), visits
+ * cells t < T', u <= U' only and ends with a blank from (t, U') landing
+ * exactly on t + d_k = T'.  costs[b] = -log of the sum over alignments.  An
+ * utterance no alignment reaches (for example durations {1} with U' >= T')
+ * gets cost +inf and zero gradients.
+ *
+ * Buffers: `saved` of rnnt_joint_loss_tdt_saved_bytes bytes (the plain state
+ * plus the duration log-probabilities, float32 [cells, K]); the backward's
+ * workspace of rnnt_joint_loss_tdt_workspace_bytes (pass 1) bytes (the plain
+ * one plus the summed step posteriors, float64, and the duration-logit
+ * gradients, float32); the forward needs none (pass 0).  Untiled and tiled
+ * modes as in rnnt_joint_loss_fwd / _bwd; full sum over alignments.  The
+ * backward overwrites d_enc, d_pred, d_W_out, d_b_out, d_W_dur [H, K] and
+ * d_b_dur [K] (float32) and checks, like rnnt_joint_loss_bwd, that `saved`
+ * comes from a forward with the same sizes, dtype, blank and durations
+ * (else data-error bit 8, nothing computed).
+ */
+int rnnt_joint_loss_tdt_saved_bytes(int B, int T, int U, int H, int V, int dtype, int tile_t,
+                                    int tile_u, int tile_v, int K, size_t* out);
+int rnnt_joint_loss_tdt_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
+                                        int tile_t, int tile_u, int tile_v, int K, int pass,
+                                        size_t* out);
+int rnnt_joint_loss_tdt_fwd(const void* enc, const void* pred, const void* W_out,
+                            const void* b_out, const void* W_dur, const void* b_dur, int dtype,
+                            const int32_t* labels, const int32_t* T_lens, const int32_t* U_lens,
+                            int B, int T, int U, int H, int V, int blank,
+                            const int32_t* durations, int K, int tile_t, int tile_u, int tile_v,
+                            float* costs, void* saved, void* workspace, size_t workspace_bytes,
+                            void* stream);
+int rnnt_joint_loss_tdt_bwd(const void* enc, const void* pred, const void* W_out,
+                            const void* b_out, const void* W_dur, const void* b_dur, int dtype,
+                            const int32_t* labels, const int32_t* T_lens, const int32_t* U_lens,
+                            int B, int T, int U, int H, int V, int blank,
+                            const int32_t* durations, int K, int tile_t, int tile_u, int tile_v,
+                            const float* grad_costs, void* saved, float* d_enc, float* d_pred,
+                            float* d_W_out, float* d_b_out, float* d_W_dur, float* d_b_dur,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Synchronises `stream`, then copies the data-error word of `saved` to
  * *data_error: 0 = every utterance valid, else a bit mask (1 = a length out of
  * range, 2 = a label out of range or equal to blank, 4 = an untiled backward

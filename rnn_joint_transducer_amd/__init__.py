@@ -22,6 +22,7 @@ from ._lib import (RNNTJ_BF16, RNNTJ_F32, RNNTJointError, check, declared_functi
 __all__ = ["rnnt_joint_loss_fwd", "rnnt_joint_loss_bwd", "rnnt_joint_loss_bwd_noalloc",
            "rnnt_joint_loss_status", "rnnt_joint_loss_pruned_fwd",
            "rnnt_joint_loss_pruned_workspace_bytes", "rnnt_joint_loss_pruned_bounds",
+           "rnnt_joint_loss_tdt_fwd", "rnnt_joint_loss_tdt_bwd",
            "rnnt_joint_loss_saved_bytes", "rnnt_joint_loss_workspace_bytes",
            "rnnt_joint_loss", "RNNTJointError", "load"]
 
@@ -161,6 +162,86 @@ def rnnt_joint_loss_pruned_bounds(saved, B, T, U, H, V, dtype_code, tile_t=64, t
     check(load().rnnt_joint_loss_pruned_bounds(_ptr(saved), B, T, U, H, V, dtype_code, tile_t,
                                                tile_u, tile_v, _ptr(out), _stream(saved.device)),
           "rnnt_joint_loss_pruned_bounds")
+    return out
+
+
+def _durations(durations):
+    arr = (ctypes.c_int32 * len(durations))(*[int(d) for d in durations])
+    return arr, len(durations)
+
+
+def rnnt_joint_loss_tdt_fwd(enc, pred, W_out, b_out, W_dur, b_dur, labels, T_lens, U_lens,
+                            durations, blank=0, tile_t=0, tile_u=0, tile_v=0, costs=None,
+                            saved=None):
+    """Token-and-duration transducer loss: costs [B] (float32) and `saved`.
+    W_dur [H, K], b_dur [K] in the dtype of enc; durations: K ints (host)."""
+    import torch
+    B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
+    K = len(durations)
+    if (tuple(W_dur.shape) != (H, K) or tuple(b_dur.shape) != (K,) or W_dur.dtype != enc.dtype
+            or b_dur.dtype != enc.dtype or not W_dur.is_contiguous() or not b_dur.is_contiguous()
+            or W_dur.device != enc.device or b_dur.device != enc.device):
+        raise ValueError(f"W_dur / b_dur: expected contiguous [{H}, {K}] / [{K}] {enc.dtype}")
+    dc = _dtype_code(enc)
+    dev = enc.device
+    out = ctypes.c_size_t(0)
+    check(load().rnnt_joint_loss_tdt_saved_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, K,
+                                                 ctypes.byref(out)), "rnnt_joint_loss_tdt_saved_bytes")
+    if saved is None:
+        saved = torch.empty(out.value, dtype=torch.uint8, device=dev)
+    elif saved.numel() < out.value:
+        raise ValueError(f"saved buffer too small ({saved.numel()} < {out.value})")
+    if costs is None:
+        costs = torch.empty(B, dtype=torch.float32, device=dev)
+    dur, K = _durations(durations)
+    rc = load().rnnt_joint_loss_tdt_fwd(_ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out),
+                                        _ptr(W_dur), _ptr(b_dur), dc, _ptr(labels), _ptr(T_lens),
+                                        _ptr(U_lens), B, T, U, H, V, blank, dur, K, tile_t, tile_u,
+                                        tile_v, _ptr(costs), _ptr(saved), None, 0, _stream(dev))
+    check(rc, "rnnt_joint_loss_tdt_fwd")
+    return costs, saved
+
+
+def rnnt_joint_loss_tdt_bwd(enc, pred, W_out, b_out, W_dur, b_dur, labels, T_lens, U_lens,
+                            durations, saved, blank=0, tile_t=0, tile_u=0, tile_v=0,
+                            grad_costs=None, workspace=None):
+    """(d_enc, d_pred, d_W_out, d_b_out, d_W_dur, d_b_dur), float32."""
+    import torch
+    B, T, U, H, V = _check_inputs(enc, pred, W_out, b_out, labels, T_lens, U_lens)
+    K = len(durations)
+    dc = _dtype_code(enc)
+    dev = enc.device
+    need = ctypes.c_size_t(0)
+    check(load().rnnt_joint_loss_tdt_saved_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, K,
+                                                 ctypes.byref(need)), "rnnt_joint_loss_tdt_saved_bytes")
+    if saved.dtype != torch.uint8 or saved.device != dev or saved.numel() < need.value:
+        raise ValueError(f"saved: expected a uint8 buffer of at least {need.value} bytes on {dev}")
+    ws = ctypes.c_size_t(0)
+    check(load().rnnt_joint_loss_tdt_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v,
+                                                     K, 1, ctypes.byref(ws)),
+          "rnnt_joint_loss_tdt_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(ws.value, dtype=torch.uint8, device=dev)
+    elif workspace.numel() < ws.value:
+        raise ValueError(f"workspace too small ({workspace.numel()} < {ws.value})")
+    if grad_costs is not None:
+        if grad_costs.dtype != torch.float32 or tuple(grad_costs.shape) != (B,):
+            raise ValueError("grad_costs must be float32 [B]")
+        grad_costs = grad_costs.contiguous()
+    out = (torch.empty(B, T, H, dtype=torch.float32, device=dev),
+           torch.empty(B, U + 1, H, dtype=torch.float32, device=dev),
+           torch.empty(H, V, dtype=torch.float32, device=dev),
+           torch.empty(V, dtype=torch.float32, device=dev),
+           torch.empty(H, K, dtype=torch.float32, device=dev),
+           torch.empty(K, dtype=torch.float32, device=dev))
+    dur, K = _durations(durations)
+    rc = load().rnnt_joint_loss_tdt_bwd(_ptr(enc), _ptr(pred), _ptr(W_out), _ptr(b_out),
+                                        _ptr(W_dur), _ptr(b_dur), dc, _ptr(labels), _ptr(T_lens),
+                                        _ptr(U_lens), B, T, U, H, V, blank, dur, K, tile_t, tile_u,
+                                        tile_v, _ptr(grad_costs), _ptr(saved),
+                                        *(_ptr(x) for x in out), _ptr(workspace),
+                                        workspace.numel(), _stream(dev))
+    check(rc, "rnnt_joint_loss_tdt_bwd")
     return out
 
 

@@ -38,6 +38,12 @@ _SIG = {
     "rnnt_joint_loss_pruned_fwd": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _vp, _vp]
                                    + [_c_int] * 10 + [_vp, _vp, _vp, _vp, _c_size, _vp]),
     "rnnt_joint_loss_pruned_bounds": (_c_int, [_vp] + [_c_int] * 9 + [_vp, _vp]),
+    "rnnt_joint_loss_tdt_saved_bytes": (_c_int, [_c_int] * 10 + [ctypes.POINTER(_c_size)]),
+    "rnnt_joint_loss_tdt_workspace_bytes": (_c_int, [_c_int] * 11 + [ctypes.POINTER(_c_size)]),
+    "rnnt_joint_loss_tdt_fwd": (_c_int, [_vp] * 6 + [_c_int, _vp, _vp, _vp] + [_c_int] * 6
+                                + [_vp] + [_c_int] * 4 + [_vp, _vp, _vp, _c_size, _vp]),
+    "rnnt_joint_loss_tdt_bwd": (_c_int, [_vp] * 6 + [_c_int, _vp, _vp, _vp] + [_c_int] * 6
+                                + [_vp] + [_c_int] * 4 + [_vp] * 8 + [_vp, _c_size, _vp]),
     "rnnt_joint_loss_status": (_c_int, [_vp, _vp, ctypes.POINTER(ctypes.c_int32)]),
     "rnnt_joint_loss_timing": (_c_int, [_c_int]),
     "rnnt_joint_loss_timing_report": (_c_int, [ctypes.c_char_p, _c_size]),

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librnntjoint.so")
-SOURCES = ["joint_tile.hip", "lattice.hip", "backward.hip", "proj.hip", "pruned.hip", "api.cpp"]
+SOURCES = ["joint_tile.hip", "lattice.hip", "backward.hip", "proj.hip", "pruned.hip", "tdt.hip", "api.cpp"]
 ARCH = os.environ.get("RNNTJ_ARCH", "gfx950")
 
 

@@ -174,6 +174,48 @@ int32_t plan_tag(const Plan& p, int blank) {
   return (int32_t)(h ? h : 1);
 }
 
+// The duration head of a token-and-duration transducer call (host side).
+struct TdtIn {
+  const void* Wd;
+  const void* bd;
+  const int32_t* durations;  // host array of K distinct values in [0, kTdtMaxDur]
+  int K;
+};
+int check_tdt(const TdtIn& t) {
+  if (!t.Wd || !t.bd || !t.durations || t.K < 1 || t.K > kTdtMaxK) return RNNTJ_ERR_ARG;
+  if (misaligned(t.Wd) || misaligned(t.bd)) return RNNTJ_ERR_ARG;
+  bool moves = false;
+  for (int j = 0; j < t.K; ++j) {
+    const int dj = t.durations[j];
+    if (dj < 0 || dj > kTdtMaxDur) return RNNTJ_ERR_UNSUPPORTED;
+    for (int i = 0; i < j; ++i)
+      if (t.durations[i] == dj) return RNNTJ_ERR_ARG;
+    moves = moves || dj >= 1;
+  }
+  return moves ? RNNTJ_OK : RNNTJ_ERR_ARG;  // a blank needs a duration >= 1
+}
+// tag of a token-and-duration state: the plan's, mixed with the durations
+int32_t tdt_tag(const Plan& p, int blank, const TdtIn& t) {
+  uint32_t h = (uint32_t)plan_tag(p, blank) ^ 0x5bd1e995u;
+  for (int j = 0; j < t.K; ++j) h = (h ^ (uint32_t)(t.durations[j] + 1)) * 16777619u;
+  h = (h ^ (uint32_t)t.K) * 16777619u;
+  h &= 0x7fffffffu;
+  return (int32_t)(h ? h : 1);
+}
+size_t tdt_ld_bytes(const Plan& p, int K) {
+  return align_up(4 * (size_t)p.d.B * p.d.DG * p.d.U1 * K);
+}
+// backward workspace of a token-and-duration call: the plain one, then the
+// summed step posteriors (float64, two arrays) and the duration-logit
+// gradients (float32 [cells, K])
+void tdt_ws(const Plan& p, int K, size_t& o_gB, size_t& o_gE, size_t& o_dzd, size_t& total) {
+  const size_t cells = (size_t)p.d.B * p.d.DG * p.d.U1;
+  o_gB = align_up(p.ws_bwd);
+  o_gE = o_gB + align_up(8 * cells);
+  o_dzd = o_gE + align_up(8 * cells);
+  total = o_dzd + align_up(4 * cells * K);
+}
+
 // ---- optional per-kernel event timing (rnnt_joint_loss_timing)
 struct TimedLaunch {
   const char* name;
@@ -261,10 +303,14 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
              const int32_t* labels, const int32_t* T_lens, const int32_t* U_lens, int B, int T,
              int U, int H, int V, int blank, int tile_t, int tile_u, int tile_v, int criterion,
              int S, float* costs, float* simple_costs, void* saved, void* workspace,
-             size_t workspace_bytes, void* stream) {
+             size_t workspace_bytes, void* stream, const TdtIn* tdt = nullptr) {
   Plan p;
   int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
+  if (tdt) {
+    if ((rc = check_tdt(*tdt))) return rc;
+    if (criterion != RNNTJ_CRIT_SUM || S != 0) return RNNTJ_ERR_ARG;
+  }
   if (criterion != RNNTJ_CRIT_SUM && criterion != RNNTJ_CRIT_MAX) return RNNTJ_ERR_ARG;
   const bool pruned = S > 0;
   if (S < 0) return RNNTJ_ERR_ARG;
@@ -298,10 +344,10 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   hipError_t e;
   if ((e = timed("zero", st, [&] { return launch_zero(status, kHdrWords, st); })) != hipSuccess)
     return RNNTJ_ERR_HIP;
-  const int32_t tag = plan_tag(p, blank);
+  const int32_t tag = tdt ? tdt_tag(p, blank, *tdt) : plan_tag(p, blank);
   if ((e = timed("validate", st, [&] {
-         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status, crit, tag,
-                                p.untiled ? 1 : 0, S, st);
+         return launch_validate(T_lens, U_lens, labels, p.d, Teff, Ueff, status,
+                                tdt ? kCritTdt : crit, tag, p.untiled ? 1 : 0, S, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
   float* Eexp = at<float>(saved, p.o_E);
@@ -396,6 +442,37 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
          return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, p.cap_all, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
+  if (tdt) {
+    // the duration head's log-probabilities, then the lattice whose steps
+    // jump by the durations
+    TdtArgs g = {};
+    g.d = p.d;
+    g.bf16 = p.bf16;
+    g.enc = enc;
+    g.pred = pred;
+    g.Wd = tdt->Wd;
+    g.bd = tdt->bd;
+    g.K = tdt->K;
+    for (int j = 0; j < tdt->K; ++j) g.dur[j] = tdt->durations[j];
+    g.Teff = Teff;
+    g.Ueff = Ueff;
+    g.hdr = status;
+    g.Eexp = Eexp;
+    g.Pexp = Pexp;
+    g.LB = LB;
+    g.LE = LE;
+    g.LD = at<float>(saved, p.saved_bytes);
+    g.alpha = alpha;
+    g.beta = beta;
+    g.logP = logP;
+    g.costs = costs;
+    if ((e = timed("tdt_dur_head", st, [&] { return launch_tdt_dur_head(g, st); })) !=
+        hipSuccess)
+      return RNNTJ_ERR_HIP;
+    if ((e = timed("tdt_lattice", st, [&] { return launch_tdt_lattice(g, st); })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
+    return RNNTJ_OK;
+  }
   if ((e = timed("lattice", st, [&] {
          return launch_lattice(LB, LE, Teff, Ueff, p.d, alpha, beta, logP, costs, crit, st);
        })) != hipSuccess)
@@ -405,6 +482,242 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
           hipSuccess)
     return RNNTJ_ERR_HIP;
   return RNNTJ_OK;
+}
+
+// The backward of every entry point (tdt: a token-and-duration state, with
+// the duration head's weights and gradients).
+int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b_out, int dtype,
+             const int32_t* labels, int B, int T, int U, int H, int V, int blank, int tile_t,
+             int tile_u, int tile_v, const float* grad_costs, void* saved, float* d_enc,
+             float* d_pred, float* d_W_out, float* d_b_out, void* workspace,
+             size_t workspace_bytes, void* stream, const TdtIn* tdt = nullptr,
+             float* d_Wd = nullptr, float* d_bd = nullptr) {
+  Plan p;
+  int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
+  if (rc) return rc;
+  size_t o_gB = 0, o_gE = 0, o_dzd = 0, ws_need = p.ws_bwd;
+  if (tdt) {
+    if ((rc = check_tdt(*tdt))) return rc;
+    if (!d_Wd || !d_bd || misaligned(d_Wd) || misaligned(d_bd)) return RNNTJ_ERR_ARG;
+    tdt_ws(p, tdt->K, o_gB, o_gE, o_dzd, ws_need);
+  }
+  if (!enc || !pred || !W_out || !b_out || !saved || !d_enc || !d_pred || !d_W_out || !d_b_out)
+    return RNNTJ_ERR_ARG;
+  if (U > 0 && !labels) return RNNTJ_ERR_ARG;
+  if (blank < 0 || blank >= V) return RNNTJ_ERR_ARG;
+  if (misaligned(enc) || misaligned(pred) || misaligned(W_out) || misaligned(saved) ||
+      misaligned(d_enc) || misaligned(d_pred) || misaligned(d_W_out) || misaligned(d_b_out) ||
+      misaligned(grad_costs))
+    return RNNTJ_ERR_ARG;
+  if (workspace_bytes < ws_need || !workspace) return RNNTJ_ERR_WORKSPACE;
+  if (misaligned(workspace)) return RNNTJ_ERR_ARG;
+  p.d.blank = blank;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  int32_t* Teff = at<int32_t>(saved, p.o_teff);
+  int32_t* Ueff = at<int32_t>(saved, p.o_ueff);
+  double* logP = at<double>(saved, p.o_logp);
+  void* Wt = at<char>(saved, p.o_wt);
+  double* db64 = at<double>(workspace, p.o_ws_db);
+  void* gchunk = at<char>(workspace, p.o_ws_g);
+  void* hchunk = at<char>(workspace, p.o_ws_h);
+
+  hipError_t e;
+  if ((e = timed("zero", st, [&] {
+         return launch_zero4(d_enc, (size_t)B * T * H, d_pred, (size_t)B * (U + 1) * H, d_W_out,
+                             (size_t)H * V, db64, 2 * (size_t)V, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  // the state must come from a forward with these sizes, dtype and blank
+  // (and, for the untiled backward, one that stored the logits)
+  int32_t* hdr = at<int32_t>(saved, p.o_status);
+  if ((e = timed("guard", st, [&] {
+         return launch_guard(hdr, tdt ? tdt_tag(p, blank, *tdt) : plan_tag(p, blank),
+                             p.untiled ? 1 : 0, st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+
+  JointArgs a = {};
+  a.enc = enc;
+  a.pred = pred;
+  a.Wt = Wt;
+  a.bias = b_out;
+  a.labels = labels;
+  a.Teff = Teff;
+  a.Ueff = Ueff;
+  a.hdr = hdr;
+  a.Eexp = at<float>(saved, p.o_E);
+  a.Pexp = at<float>(saved, p.o_P);
+  a.d = p.d;
+  a.lse = at<float>(saved, p.o_lse);
+  a.LB = at<float>(saved, p.o_lb);
+  a.LE = at<float>(saved, p.o_le);
+  a.alpha = at<double>(saved, p.o_alpha);
+  a.beta = at<double>(saved, p.o_beta);
+  a.logP = logP;
+  a.gcost = grad_costs;
+  a.zmax = (p.untiled && p.bf16) ? at<float>(saved, p.o_zm) : nullptr;
+  a.zstep = p.zstep;
+  TdtArgs g = {};
+  if (tdt) {
+    // per-cell step posteriors (summed over the durations) and the duration
+    // logits' gradients; the token head's kernels then read the posteriors
+    // in place of alpha / beta
+    g.d = p.d;
+    g.d.blank = blank;
+    g.bf16 = p.bf16;
+    g.enc = enc;
+    g.pred = pred;
+    g.Wd = tdt->Wd;
+    g.bd = tdt->bd;
+    g.K = tdt->K;
+    for (int j = 0; j < tdt->K; ++j) g.dur[j] = tdt->durations[j];
+    g.Teff = Teff;
+    g.Ueff = Ueff;
+    g.hdr = hdr;
+    g.Eexp = a.Eexp;
+    g.Pexp = a.Pexp;
+    g.LB = a.LB;
+    g.LE = a.LE;
+    g.LD = at<float>(saved, p.saved_bytes);
+    g.alpha = at<double>(saved, p.o_alpha);
+    g.beta = at<double>(saved, p.o_beta);
+    g.logP = logP;
+    g.gcost = grad_costs;
+    g.gB = at<double>(workspace, o_gB);
+    g.gE = at<double>(workspace, o_gE);
+    g.dzd = at<float>(workspace, o_dzd);
+    g.d_enc = d_enc;
+    g.d_pred = d_pred;
+    g.d_Wd = d_Wd;
+    g.d_bd = d_bd;
+    if ((e = timed("zero", st, [&] {
+           return launch_zero4(d_Wd, (size_t)H * tdt->K, d_bd, (size_t)tdt->K, nullptr, 0,
+                               nullptr, 0, st);
+         })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
+    if ((e = timed("tdt_post", st, [&] { return launch_tdt_post(g, st); })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
+    a.alpha = g.gB;
+    a.beta = g.gE;
+  }
+
+  DhArgs h = {};
+  h.W = W_out;
+  h.enc = enc;
+  h.pred = pred;
+  h.Teff = Teff;
+  h.Ueff = Ueff;
+  h.hdr = a.hdr;
+  h.Eexp = a.Eexp;
+  h.Pexp = a.Pexp;
+  h.d = p.d;
+  h.d_enc = d_enc;
+  h.d_pred = d_pred;
+  h.ksplit = 1;
+  DwArgs w = {};
+  w.h = hchunk;
+  w.d = p.d;
+  w.d_W = d_W_out;
+  w.d_b64 = db64;
+  w.hdr = hdr;
+  h.gcost = grad_costs;
+  // split-K runs of the dW GEMM: one round of resident workgroups (two per
+  // compute unit for bf16, one for fp32), fewest float32 partial sums per
+  // output element
+  auto kparts_for = [&](int max_tiles) {
+    const int per = ((H + 127) / 128) * ((V + 255) / 256);
+    int k = device_cu_count() * (p.bf16 ? 2 : 1) / per;
+    return k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
+  };
+  auto finalize = [&](int32_t* mark) {
+    if (tdt) {
+      const hipError_t r = timed("tdt_dur_bwd", st, [&] { return launch_tdt_dur_bwd(g, st); });
+      if (r != hipSuccess) return r;
+    }
+    return timed("db_finalize", st,
+                 [&] { return launch_db_finalize(db64, d_b_out, V, mark, st); });
+  };
+
+  if (p.untiled) {
+    // the stored logits become the logit gradients in place; dh and dW then
+    // read them as plain GEMM operands
+    void* z = at<char>(saved, p.o_z);
+    a.tiles = at<int32_t>(saved, p.o_tiles);
+    a.tile_count = at<int32_t>(saved, p.o_tcount);
+    a.ct0 = 0; a.cu0 = 0; a.CT = p.d.Tpad; a.CU = p.d.U1pad;
+    if ((e = timed("grad_inplace", st,
+                   [&] { return launch_grad_inplace(z, p.bf16, a, p.cap_all, st); })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
+    h.g = z;
+    h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad;
+    h.tiles = a.tiles;
+    h.tile_count = a.tile_count;
+    if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
+    w.g = z;
+    w.h = at<char>(saved, p.o_h);  // written by the forward
+    w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
+    w.tiles = a.tiles;
+    w.tile_count = a.tile_count;
+    w.kparts = kparts_for(p.cap_all);
+    if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
+    return finalize(a.hdr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
+  }
+
+  // tiled: one lattice chunk of CT frames x CU label positions at a time.
+  // The logit-gradient kernel splits the vocabulary tiles of each cell tile
+  // over several workgroups when a chunk alone has too few cell tiles to
+  // give every compute unit (256 on gfx950) about four of them, as long as
+  // each part keeps at least 8 vocabulary tiles: every part rebuilds the
+  // tile's h rows and posteriors, which shorter parts do not amortise.
+  const int chunk_tiles = p.cap_chunk;
+  const int nvt = (V + kVocabTile - 1) / kVocabTile;
+  int vsplit = 1;
+  while (chunk_tiles * vsplit < 1024 && nvt / (2 * vsplit) >= 8) vsplit *= 2;
+  int32_t* ctiles = at<int32_t>(workspace, p.o_ws_tiles);
+  int32_t* ccount = at<int32_t>(workspace, p.o_ws_tcount);
+  if ((e = timed("tile_list", st, [&] {
+         return launch_tile_list(Teff, Ueff, p.d, p.CT, p.CU, p.n_cu_chunks, p.n_chunks,
+                                 p.cap_chunk, ctiles, ccount, hdr, at<int32_t>(saved, p.o_bounds),
+                                 st);
+       })) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  int chunk = 0;
+  for (int ct0 = 0; ct0 < p.d.Tpad; ct0 += p.CT) {
+    for (int cu0 = 0; cu0 < p.d.U1pad; cu0 += p.CU, ++chunk) {
+      a.ct0 = ct0;
+      a.cu0 = cu0;
+      a.CT = p.CT;
+      a.CU = p.CU;
+      a.n_tu = p.CU / kTileU;
+      a.vsplit = vsplit;
+      a.gout = gchunk;
+      a.hout = hchunk;
+      a.tiles = ctiles + (size_t)chunk * p.cap_chunk;
+      a.tile_count = ccount + chunk;
+      if ((e = timed("joint_grad", st, [&] {
+             return launch_joint_tile(a, kGrad, p.bf16, p.cap_chunk * vsplit, st);
+           })) != hipSuccess)
+        return RNNTJ_ERR_HIP;
+      h.g = gchunk;
+      h.ct0 = ct0; h.cu0 = cu0; h.CT = p.CT; h.CU = p.CU;
+      h.tiles = a.tiles;
+      h.tile_count = a.tile_count;
+      if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_chunk, st); })) !=
+          hipSuccess)
+        return RNNTJ_ERR_HIP;
+      w.g = gchunk;
+      w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;
+      w.tiles = a.tiles;
+      w.tile_count = a.tile_count;
+      w.kparts = kparts_for(p.cap_chunk);
+      if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
+        return RNNTJ_ERR_HIP;
+    }
+  }
+  return finalize(nullptr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
 }
 
 }  // namespace
@@ -513,178 +826,60 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out, co
                         void* stream) {
   (void)T_lens;
   (void)U_lens;
+  return bwd_impl(enc, pred, W_out, b_out, dtype, labels, B, T, U, H, V, blank, tile_t, tile_u,
+                  tile_v, grad_costs, saved, d_enc, d_pred, d_W_out, d_b_out, workspace,
+                  workspace_bytes, stream);
+}
+
+int rnnt_joint_loss_tdt_saved_bytes(int B, int T, int U, int H, int V, int dtype, int tile_t,
+                                    int tile_u, int tile_v, int K, size_t* out) {
+  if (!out || K < 1 || K > kTdtMaxK) return RNNTJ_ERR_ARG;
   Plan p;
-  int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
+  const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
-  if (!enc || !pred || !W_out || !b_out || !saved || !d_enc || !d_pred || !d_W_out || !d_b_out)
-    return RNNTJ_ERR_ARG;
-  if (U > 0 && !labels) return RNNTJ_ERR_ARG;
-  if (blank < 0 || blank >= V) return RNNTJ_ERR_ARG;
-  if (misaligned(enc) || misaligned(pred) || misaligned(W_out) || misaligned(saved) ||
-      misaligned(d_enc) || misaligned(d_pred) || misaligned(d_W_out) || misaligned(d_b_out) ||
-      misaligned(grad_costs))
-    return RNNTJ_ERR_ARG;
-  if (workspace_bytes < p.ws_bwd || !workspace) return RNNTJ_ERR_WORKSPACE;
-  if (misaligned(workspace)) return RNNTJ_ERR_ARG;
-  p.d.blank = blank;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  *out = p.saved_bytes + tdt_ld_bytes(p, K);
+  return RNNTJ_OK;
+}
 
-  int32_t* Teff = at<int32_t>(saved, p.o_teff);
-  int32_t* Ueff = at<int32_t>(saved, p.o_ueff);
-  double* logP = at<double>(saved, p.o_logp);
-  void* Wt = at<char>(saved, p.o_wt);
-  double* db64 = at<double>(workspace, p.o_ws_db);
-  void* gchunk = at<char>(workspace, p.o_ws_g);
-  void* hchunk = at<char>(workspace, p.o_ws_h);
+int rnnt_joint_loss_tdt_workspace_bytes(int B, int T, int U, int H, int V, int dtype, int tile_t,
+                                        int tile_u, int tile_v, int K, int pass, size_t* out) {
+  if (!out || K < 1 || K > kTdtMaxK || (pass != 0 && pass != 1)) return RNNTJ_ERR_ARG;
+  Plan p;
+  const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
+  if (rc) return rc;
+  size_t a, b, c, total;
+  tdt_ws(p, K, a, b, c, total);
+  *out = pass == 0 ? p.ws_fwd : total;
+  return RNNTJ_OK;
+}
 
-  hipError_t e;
-  if ((e = timed("zero", st, [&] {
-         return launch_zero4(d_enc, (size_t)B * T * H, d_pred, (size_t)B * (U + 1) * H, d_W_out,
-                             (size_t)H * V, db64, 2 * (size_t)V, st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-  // the state must come from a forward with these sizes, dtype and blank
-  // (and, for the untiled backward, one that stored the logits)
-  int32_t* hdr = at<int32_t>(saved, p.o_status);
-  if ((e = timed("guard", st, [&] {
-         return launch_guard(hdr, plan_tag(p, blank), p.untiled ? 1 : 0, st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
+int rnnt_joint_loss_tdt_fwd(const void* enc, const void* pred, const void* W_out,
+                            const void* b_out, const void* W_dur, const void* b_dur, int dtype,
+                            const int32_t* labels, const int32_t* T_lens, const int32_t* U_lens,
+                            int B, int T, int U, int H, int V, int blank,
+                            const int32_t* durations, int K, int tile_t, int tile_u, int tile_v,
+                            float* costs, void* saved, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  const TdtIn t{W_dur, b_dur, durations, K};
+  return fwd_impl(enc, pred, W_out, b_out, dtype, labels, T_lens, U_lens, B, T, U, H, V, blank,
+                  tile_t, tile_u, tile_v, RNNTJ_CRIT_SUM, 0, costs, nullptr, saved, workspace,
+                  workspace_bytes, stream, &t);
+}
 
-  JointArgs a = {};
-  a.enc = enc;
-  a.pred = pred;
-  a.Wt = Wt;
-  a.bias = b_out;
-  a.labels = labels;
-  a.Teff = Teff;
-  a.Ueff = Ueff;
-  a.hdr = hdr;
-  a.Eexp = at<float>(saved, p.o_E);
-  a.Pexp = at<float>(saved, p.o_P);
-  a.d = p.d;
-  a.lse = at<float>(saved, p.o_lse);
-  a.LB = at<float>(saved, p.o_lb);
-  a.LE = at<float>(saved, p.o_le);
-  a.alpha = at<double>(saved, p.o_alpha);
-  a.beta = at<double>(saved, p.o_beta);
-  a.logP = logP;
-  a.gcost = grad_costs;
-  a.zmax = (p.untiled && p.bf16) ? at<float>(saved, p.o_zm) : nullptr;
-  a.zstep = p.zstep;
-
-  DhArgs h = {};
-  h.W = W_out;
-  h.enc = enc;
-  h.pred = pred;
-  h.Teff = Teff;
-  h.Ueff = Ueff;
-  h.hdr = a.hdr;
-  h.Eexp = a.Eexp;
-  h.Pexp = a.Pexp;
-  h.d = p.d;
-  h.d_enc = d_enc;
-  h.d_pred = d_pred;
-  h.ksplit = 1;
-  DwArgs w = {};
-  w.h = hchunk;
-  w.d = p.d;
-  w.d_W = d_W_out;
-  w.d_b64 = db64;
-  w.hdr = hdr;
-  h.gcost = grad_costs;
-  // split-K runs of the dW GEMM: one round of resident workgroups (two per
-  // compute unit for bf16, one for fp32), fewest float32 partial sums per
-  // output element
-  auto kparts_for = [&](int max_tiles) {
-    const int per = ((H + 127) / 128) * ((V + 255) / 256);
-    int k = device_cu_count() * (p.bf16 ? 2 : 1) / per;
-    return k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
-  };
-  auto finalize = [&](int32_t* mark) {
-    return timed("db_finalize", st,
-                 [&] { return launch_db_finalize(db64, d_b_out, V, mark, st); });
-  };
-
-  if (p.untiled) {
-    // the stored logits become the logit gradients in place; dh and dW then
-    // read them as plain GEMM operands
-    void* z = at<char>(saved, p.o_z);
-    a.tiles = at<int32_t>(saved, p.o_tiles);
-    a.tile_count = at<int32_t>(saved, p.o_tcount);
-    a.ct0 = 0; a.cu0 = 0; a.CT = p.d.Tpad; a.CU = p.d.U1pad;
-    if ((e = timed("grad_inplace", st,
-                   [&] { return launch_grad_inplace(z, p.bf16, a, p.cap_all, st); })) != hipSuccess)
-      return RNNTJ_ERR_HIP;
-    h.g = z;
-    h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad;
-    h.tiles = a.tiles;
-    h.tile_count = a.tile_count;
-    if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
-      return RNNTJ_ERR_HIP;
-    w.g = z;
-    w.h = at<char>(saved, p.o_h);  // written by the forward
-    w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
-    w.tiles = a.tiles;
-    w.tile_count = a.tile_count;
-    w.kparts = kparts_for(p.cap_all);
-    if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
-      return RNNTJ_ERR_HIP;
-    return finalize(a.hdr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
-  }
-
-  // tiled: one lattice chunk of CT frames x CU label positions at a time.
-  // The logit-gradient kernel splits the vocabulary tiles of each cell tile
-  // over several workgroups when a chunk alone has too few cell tiles to
-  // give every compute unit (256 on gfx950) about four of them, as long as
-  // each part keeps at least 8 vocabulary tiles: every part rebuilds the
-  // tile's h rows and posteriors, which shorter parts do not amortise.
-  const int chunk_tiles = p.cap_chunk;
-  const int nvt = (V + kVocabTile - 1) / kVocabTile;
-  int vsplit = 1;
-  while (chunk_tiles * vsplit < 1024 && nvt / (2 * vsplit) >= 8) vsplit *= 2;
-  int32_t* ctiles = at<int32_t>(workspace, p.o_ws_tiles);
-  int32_t* ccount = at<int32_t>(workspace, p.o_ws_tcount);
-  if ((e = timed("tile_list", st, [&] {
-         return launch_tile_list(Teff, Ueff, p.d, p.CT, p.CU, p.n_cu_chunks, p.n_chunks,
-                                 p.cap_chunk, ctiles, ccount, hdr, at<int32_t>(saved, p.o_bounds),
-                                 st);
-       })) != hipSuccess)
-    return RNNTJ_ERR_HIP;
-  int chunk = 0;
-  for (int ct0 = 0; ct0 < p.d.Tpad; ct0 += p.CT) {
-    for (int cu0 = 0; cu0 < p.d.U1pad; cu0 += p.CU, ++chunk) {
-      a.ct0 = ct0;
-      a.cu0 = cu0;
-      a.CT = p.CT;
-      a.CU = p.CU;
-      a.n_tu = p.CU / kTileU;
-      a.vsplit = vsplit;
-      a.gout = gchunk;
-      a.hout = hchunk;
-      a.tiles = ctiles + (size_t)chunk * p.cap_chunk;
-      a.tile_count = ccount + chunk;
-      if ((e = timed("joint_grad", st, [&] {
-             return launch_joint_tile(a, kGrad, p.bf16, p.cap_chunk * vsplit, st);
-           })) != hipSuccess)
-        return RNNTJ_ERR_HIP;
-      h.g = gchunk;
-      h.ct0 = ct0; h.cu0 = cu0; h.CT = p.CT; h.CU = p.CU;
-      h.tiles = a.tiles;
-      h.tile_count = a.tile_count;
-      if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_chunk, st); })) !=
-          hipSuccess)
-        return RNNTJ_ERR_HIP;
-      w.g = gchunk;
-      w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;
-      w.tiles = a.tiles;
-      w.tile_count = a.tile_count;
-      w.kparts = kparts_for(p.cap_chunk);
-      if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
-        return RNNTJ_ERR_HIP;
-    }
-  }
-  return finalize(nullptr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
+int rnnt_joint_loss_tdt_bwd(const void* enc, const void* pred, const void* W_out,
+                            const void* b_out, const void* W_dur, const void* b_dur, int dtype,
+                            const int32_t* labels, const int32_t* T_lens, const int32_t* U_lens,
+                            int B, int T, int U, int H, int V, int blank,
+                            const int32_t* durations, int K, int tile_t, int tile_u, int tile_v,
+                            const float* grad_costs, void* saved, float* d_enc, float* d_pred,
+                            float* d_W_out, float* d_b_out, float* d_W_dur, float* d_b_dur,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  (void)T_lens;
+  (void)U_lens;
+  const TdtIn t{W_dur, b_dur, durations, K};
+  return bwd_impl(enc, pred, W_out, b_out, dtype, labels, B, T, U, H, V, blank, tile_t, tile_u,
+                  tile_v, grad_costs, saved, d_enc, d_pred, d_W_out, d_b_out, workspace,
+                  workspace_bytes, stream, &t, d_W_dur, d_b_dur);
 }
 
 int rnnt_joint_loss_bwd_noalloc(const void* enc, const void* pred, const void* W_out,

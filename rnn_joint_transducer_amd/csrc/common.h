@@ -26,6 +26,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 // Training criterion of a forward (word 3 of the state header): the full sum
 // over alignments, or its maximum approximation (the best alignment).
 constexpr int kCritSum = 0, kCritMax = 1;
+// Token-and-duration transducer: the token head's transition posteriors are
+// precomputed per cell (summed over durations) and handed over in place of
+// alpha (blank) and beta (label).
+constexpr int kCritTdt = 2;
 
 constexpr int kTileT = 16;
 constexpr int kTileU = 8;
@@ -289,6 +293,11 @@ __device__ __forceinline__ CellPostIn cell_post_load(const Dims& d,
     c.m = beta[ix];
     return c;
   }
+  if (crit == kCritTdt) {
+    c.a = alpha[ix];
+    c.m = beta[ix];
+    return c;
+  }
   c.a = alpha[ix];
   c.lb = LB[ix];
   c.le = LE[ix];
@@ -302,6 +311,11 @@ __device__ __forceinline__ void cell_post_eval(const CellPostIn& c, double logP,
   if (crit == kCritMax) {  // 0/1 indicators of the best alignment's steps
     gB = c.m == kPathBlank ? 1.0 : 0.0;
     gE = c.m == kPathLabel ? 1.0 : 0.0;
+    return;
+  }
+  if (crit == kCritTdt) {  // precomputed, summed over the durations
+    gB = c.a;
+    gE = c.m;
     return;
   }
   if (t < Tl - 1)

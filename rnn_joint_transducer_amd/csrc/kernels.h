@@ -155,6 +155,45 @@ hipError_t launch_pruning_bounds(const PruneArgs& p, hipStream_t st);
 // p[i] = v for i < n
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
 
+// Token-and-duration transducer (tdt.hip).  Up to kTdtMaxK durations, each
+// in [0, kTdtMaxDur].
+constexpr int kTdtMaxK = 8;
+constexpr int kTdtMaxDur = 15;
+struct TdtArgs {
+  Dims d;
+  bool bf16;
+  const void* enc;
+  const void* pred;
+  const void* Wd;  // W_dur [H, K]
+  const void* bd;  // b_dur [K]
+  int K;
+  int dur[kTdtMaxK];
+  const int32_t* Teff;
+  const int32_t* Ueff;
+  const int32_t* hdr;
+  const float* Eexp;
+  const float* Pexp;
+  const float* LB;   // token head (diagonal-skewed)
+  const float* LE;
+  float* LD;         // duration log-probabilities [cells, K]
+  double* alpha;
+  double* beta;
+  double* logP;
+  float* costs;
+  const float* gcost;
+  double* gB;        // backward: summed step posteriors per cell
+  double* gE;
+  float* dzd;        // backward: duration-logit gradients [cells, K]
+  float* d_enc;
+  float* d_pred;
+  float* d_Wd;
+  float* d_bd;
+};
+hipError_t launch_tdt_dur_head(const TdtArgs& a, hipStream_t st);
+hipError_t launch_tdt_lattice(const TdtArgs& a, hipStream_t st);
+hipError_t launch_tdt_post(const TdtArgs& a, hipStream_t st);
+hipError_t launch_tdt_dur_bwd(const TdtArgs& a, hipStream_t st);
+
 // Fill n floats / int32s with zero (a kernel, never a memset node); the
 // four-buffer form zeroes up to four (null pointers skipped) in one launch.
 hipError_t launch_zero(void* p, size_t n_words, hipStream_t st);

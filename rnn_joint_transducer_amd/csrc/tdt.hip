@@ -1,0 +1,384 @@
+// Token-and-duration transducer ("Daily Papers" page, Token-and-Duration
+// Transducer abstract): the joint has two outputs, normalised independently,
+// over tokens and over durations (the frames a token covers).
+//
+// The token head is the fused path's joint + vocabulary projection + online
+// log-sum-exp, unchanged (LB, LE per cell).  This file holds what the
+// durations add:
+//   dur_head_kernel      LD(t,u,k) = log_softmax(h W_dur + b_dur)[k] per cell,
+//                        h = tanh(enc[t] + pred[u]) rebuilt from the e^{2x} rows
+//   tdt_lattice_kernel   alpha / beta over the lattice whose steps jump d_k
+//                        frames (blank d_k >= 1: (t,u) -> (t+d,u); label:
+//                        (t,u) -> (t+d,u+1)); float64, exact log-add-exp
+//   tdt_post_kernel      per cell the summed blank / label step posteriors
+//                        (the token head's backward reads them in place of
+//                        alpha / beta) and the duration-logit gradient
+//                        dzd(t,u,k) = gc ((gB + gE) q_k - (gB_k + gE_k))
+//   dur_bwd_kernel       the duration head's share of d_enc (over a block of
+//                        frames) or d_pred (over one label position):
+//                        (1 - h^2) (W_dur dzd) summed over the lattice, plus
+//                        d_W_dur = sum h dzd^T and d_b_dur = sum dzd.
+// The lattice runs in float64 with one anti-diagonal per step: every
+// predecessor of a cell lies on one of the dmax + 1 previous diagonals, which
+// a ring of diagonals in LDS holds.
+#include <type_traits>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace rnntj {
+
+namespace {
+
+constexpr double kNegInfD = -__builtin_inf();
+constexpr int kRing = kTdtMaxDur + 2;  // diagonals kept: dmax + 1 back, plus the current
+
+__device__ __forceinline__ double lae(double a, double b) {
+  const double m = a > b ? a : b;
+  if (m == kNegInfD) return kNegInfD;
+  return m + log1p(exp(-fabs(a - b)));
+}
+
+// h of cell (t,u) for hidden unit k from the e^{2x} rows (or directly)
+__device__ __forceinline__ float h_of(const TdtArgs& a, int b, int t, int u, int k, bool use_ep) {
+  const Dims& d = a.d;
+  if (use_ep) {
+    const float e = a.Eexp[((size_t)b * d.T + t) * d.H + k];
+    const float p = a.Pexp[((size_t)b * d.U1 + u) * d.H + k];
+    return 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e * p);
+  }
+  float x;
+  if (a.bf16) {
+    x = bf16_to_f32(static_cast<const uint16_t*>(a.enc)[((size_t)b * d.T + t) * d.H + k]) +
+        bf16_to_f32(static_cast<const uint16_t*>(a.pred)[((size_t)b * d.U1 + u) * d.H + k]);
+  } else {
+    x = static_cast<const float*>(a.enc)[((size_t)b * d.T + t) * d.H + k] +
+        static_cast<const float*>(a.pred)[((size_t)b * d.U1 + u) * d.H + k];
+  }
+  return fast_tanh(x);
+}
+
+// the h the MFMA path multiplies: rounded to the input type
+__device__ __forceinline__ float h_round(const TdtArgs& a, float h) {
+  return a.bf16 ? bf16_to_f32(f32_to_bf16_hw(h)) : h;
+}
+
+__device__ __forceinline__ float wdur(const TdtArgs& a, int k, int j) {
+  const size_t i = (size_t)k * a.K + j;
+  return a.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.Wd)[i])
+                : static_cast<const float*>(a.Wd)[i];
+}
+__device__ __forceinline__ float bdur(const TdtArgs& a, int j) {
+  return a.bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.bd)[j])
+                : static_cast<const float*>(a.bd)[j];
+}
+
+// ------------------------------------------------------------ duration head
+//
+// One workgroup per (b, t), one thread per cell u; W_dur (float32) and the
+// frame's e^{2 enc} row in LDS.
+__global__ __launch_bounds__(256) void dur_head_kernel(TdtArgs a) {
+  extern __shared__ float sm[];  // W_dur [H][K], then the e^{2 enc} row [H]
+  const Dims d = a.d;
+  const int b = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  if (t >= Tl) return;  // uniform
+  const int H = d.H, K = a.K;
+  float* w = sm;
+  float* er = sm + H * K;
+  const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
+  for (int i = tid; i < H * K; i += 256) w[i] = wdur(a, i / K, i % K);
+  for (int k = tid; k < H; k += 256) er[k] = a.Eexp[((size_t)b * d.T + t) * H + k];
+  __syncthreads();
+  for (int u = tid; u <= Ul; u += 256) {
+    float z[kTdtMaxK];
+#pragma unroll
+    for (int j = 0; j < kTdtMaxK; ++j) z[j] = j < K ? bdur(a, j) : 0.f;
+    const float* pr = a.Pexp + ((size_t)b * d.U1 + u) * H;
+    for (int k = 0; k < H; ++k) {
+      const float h = h_round(a, use_ep ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + er[k] * pr[k])
+                                        : h_of(a, b, t, u, k, false));
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j)
+        if (j < K) z[j] = fmaf(h, w[k * K + j], z[j]);
+    }
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < kTdtMaxK; ++j)
+      if (j < K) m = fmaxf(m, z[j]);
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kTdtMaxK; ++j)
+      if (j < K) s += __expf(z[j] - m);
+    const float lse = m + __logf(s);
+    float* ld = a.LD + skew_idx(d, b, t, u) * K;
+#pragma unroll
+    for (int j = 0; j < kTdtMaxK; ++j)
+      if (j < K) ld[j] = z[j] - lse;
+  }
+}
+
+// ------------------------------------------------------------ lattice
+//
+// blockIdx.y == 0: alpha, == 1: beta; thread u owns label position u.
+__global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
+  __shared__ double ring[kRing][513];
+  const Dims d = a.d;
+  const int b = blockIdx.x, u = threadIdx.x, K = a.K;
+  const bool fwd = blockIdx.y == 0;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  if (Tl == 0) {
+    if (fwd && u == 0) {
+      a.costs[b] = __builtin_nanf("");
+      a.logP[b] = __builtin_nan("");
+    }
+    return;
+  }
+  for (int r = 0; r < kRing; ++r) {
+    ring[r][u] = kNegInfD;
+    if (u == 0) ring[r][512] = kNegInfD;
+  }
+  __syncthreads();
+  const bool lane_on = u <= Ul;
+  const int nd = Tl + Ul;  // diagonals 0 .. Tl-1+Ul
+  auto LBv = [&](int t, int uu) { return (double)a.LB[skew_idx(d, b, t, uu)]; };
+  auto LEv = [&](int t, int uu) { return (double)a.LE[skew_idx(d, b, t, uu)]; };
+  auto LDv = [&](int t, int uu, int j) { return (double)a.LD[skew_idx(d, b, t, uu) * K + j]; };
+  if (fwd) {
+    for (int k = 0; k < nd; ++k) {
+      const int t = k - u;
+      const bool on = lane_on && t >= 0 && t < Tl;
+      double v = kNegInfD;
+      if (on) {
+        if (k == 0) {
+          v = 0.0;
+        } else {
+          for (int j = 0; j < K; ++j) {
+            const int dj = a.dur[j], s = t - dj;
+            if (s < 0) continue;
+            if (dj >= 1)  // blank (s,u) -> (t,u), on diagonal k - dj
+              v = lae(v, ring[(k - dj) % kRing][u] + LBv(s, u) + LDv(s, u, j));
+            if (u >= 1)   // label (s,u-1) -> (t,u), on diagonal k - dj - 1
+              v = lae(v, ring[(k - dj - 1) % kRing][u - 1] + LEv(s, u - 1) + LDv(s, u - 1, j));
+          }
+        }
+        a.alpha[skew_idx(d, b, t, u)] = v;
+      }
+      ring[k % kRing][u] = on ? v : kNegInfD;
+      __syncthreads();
+    }
+    if (u == Ul) {  // the final blank lands exactly on frame T'
+      double lp = kNegInfD;
+      for (int j = 0; j < K; ++j) {
+        const int dj = a.dur[j], s = Tl - dj;
+        if (dj >= 1 && s >= 0) lp = lae(lp, a.alpha[skew_idx(d, b, s, Ul)] + LBv(s, Ul) + LDv(s, Ul, j));
+      }
+      a.logP[b] = lp;
+      a.costs[b] = (float)(-lp);
+    }
+  } else {
+    for (int k = nd - 1; k >= 0; --k) {
+      const int t = k - u;
+      const bool on = lane_on && t >= 0 && t < Tl;
+      double v = kNegInfD;
+      if (on) {
+        const double lb = LBv(t, u), le = u < Ul ? LEv(t, u) : 0.0;
+        for (int j = 0; j < K; ++j) {
+          const int dj = a.dur[j];
+          const double ldj = LDv(t, u, j);
+          if (dj >= 1) {
+            if (t + dj == Tl && u == Ul) v = lae(v, lb + ldj);
+            else if (t + dj < Tl) v = lae(v, lb + ldj + ring[(k + dj) % kRing][u]);
+          }
+          if (u < Ul && t + dj < Tl) v = lae(v, le + ldj + ring[(k + dj + 1) % kRing][u + 1]);
+        }
+        a.beta[skew_idx(d, b, t, u)] = v;
+      }
+      ring[k % kRing][u] = on ? v : kNegInfD;
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------ posteriors
+//
+// One thread per cell: gbt = sum_k gB, get = sum_k gE (float64; the token
+// head's backward reads them as its transition posteriors), dzd (float32,
+// the grad_costs weight included).
+__global__ __launch_bounds__(256) void tdt_post_kernel(TdtArgs a) {
+  const Dims d = a.d;
+  const int b = blockIdx.y, t = blockIdx.x, K = a.K;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  if (t >= Tl) return;
+  const double lp = a.logP[b];
+  const double gc = a.gcost ? (double)a.gcost[b] : 1.0;
+  // no alignment reaches the end (logP = -inf): cost +inf, gradients zero
+  const bool dead = lp == kNegInfD;
+  for (int u = threadIdx.x; u <= Ul; u += blockDim.x) {
+    const size_t ix = skew_idx(d, b, t, u);
+    if (dead) {
+      a.gB[ix] = 0.0;
+      a.gE[ix] = 0.0;
+      for (int j = 0; j < K; ++j) a.dzd[ix * K + j] = 0.f;
+      continue;
+    }
+    const double al = a.alpha[ix];
+    const double lb = a.LB[ix], le = u < Ul ? (double)a.LE[ix] : 0.0;
+    double sB = 0.0, sE = 0.0, g[kTdtMaxK];
+#pragma unroll
+    for (int j = 0; j < kTdtMaxK; ++j) {
+      g[j] = 0.0;
+      if (j >= K) continue;
+      const int dj = a.dur[j];
+      const double ldj = a.LD[ix * K + j];
+      double gb = 0.0, ge = 0.0;
+      if (dj >= 1) {
+        if (t + dj == Tl && u == Ul) gb = exp(al + lb + ldj - lp);
+        else if (t + dj < Tl) gb = exp(al + lb + ldj + a.beta[skew_idx(d, b, t + dj, u)] - lp);
+      }
+      if (u < Ul && t + dj < Tl) ge = exp(al + le + ldj + a.beta[skew_idx(d, b, t + dj, u + 1)] - lp);
+      sB += gb;
+      sE += ge;
+      g[j] = gb + ge;
+    }
+    a.gB[ix] = sB;
+    a.gE[ix] = sE;
+    const double occ = sB + sE;
+#pragma unroll
+    for (int j = 0; j < kTdtMaxK; ++j)
+      if (j < K) a.dzd[ix * K + j] = (float)(gc * (occ * exp((double)a.LD[ix * K + j]) - g[j]));
+  }
+}
+
+// ------------------------------------------------------------ duration head backward
+//
+// mode 0: one workgroup per (b, block of kFrames frames): the frames' d_enc
+// rows and the block's share of d_W_dur, d_b_dur; mode 1: one workgroup per
+// (b, u): the d_pred row.  Threads over hidden units k.
+constexpr int kFrames = 16;
+constexpr int kHPer = 3;  // hidden units per thread (H <= 768)
+
+template <int MODE>
+__global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
+  const Dims d = a.d;
+  const int b = blockIdx.y, tid = threadIdx.x, K = a.K;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  const int H = d.H;
+  const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
+  int t_lo, t_hi, u_lo, u_hi;
+  if (MODE == 0) {
+    t_lo = blockIdx.x * kFrames;
+    t_hi = min(t_lo + kFrames, Tl);
+    u_lo = 0;
+    u_hi = Ul;
+    if (t_lo >= Tl) return;
+  } else {
+    u_lo = u_hi = blockIdx.x;
+    t_lo = 0;
+    t_hi = Tl;
+    if (u_lo > Ul || Tl == 0) return;
+  }
+  float w[kHPer][kTdtMaxK];
+#pragma unroll
+  for (int i = 0; i < kHPer; ++i)
+#pragma unroll
+    for (int j = 0; j < kTdtMaxK; ++j) {
+      const int k = tid + 256 * i;
+      w[i][j] = (k < H && j < K) ? wdur(a, k, j) : 0.f;
+    }
+  float dw[kHPer][kTdtMaxK];
+  float db[kTdtMaxK];
+#pragma unroll
+  for (int j = 0; j < kTdtMaxK; ++j) {
+    db[j] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kHPer; ++i) dw[i][j] = 0.f;
+  }
+  float acc[kHPer] = {0.f, 0.f, 0.f};  // mode 1: the d_pred row
+  for (int t = t_lo; t < t_hi; ++t) {
+    float ae[kHPer] = {0.f, 0.f, 0.f};  // mode 0: this frame's d_enc row
+    for (int u = u_lo; u <= u_hi; ++u) {
+      const size_t ix = skew_idx(d, b, t, u);
+      float z[kTdtMaxK];
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j) z[j] = j < K ? ld_const(a.dzd + ix * K + j) : 0.f;
+      if (MODE == 0) {
+#pragma unroll
+        for (int j = 0; j < kTdtMaxK; ++j) db[j] += z[j];
+      }
+#pragma unroll
+      for (int i = 0; i < kHPer; ++i) {
+        const int k = tid + 256 * i;
+        if (k >= H) continue;
+        const float h = h_of(a, b, t, u, k, use_ep);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < kTdtMaxK; ++j) s = fmaf(w[i][j], z[j], s);
+        const float dp = (1.0f - h * h) * s;
+        if (MODE == 0) {
+          ae[i] += dp;
+          const float hr = h_round(a, h);
+#pragma unroll
+          for (int j = 0; j < kTdtMaxK; ++j) dw[i][j] = fmaf(hr, z[j], dw[i][j]);
+        } else {
+          acc[i] += dp;
+        }
+      }
+    }
+    if (MODE == 0) {
+#pragma unroll
+      for (int i = 0; i < kHPer; ++i) {
+        const int k = tid + 256 * i;
+        if (k < H) atomicAdd(&a.d_enc[((size_t)b * d.T + t) * H + k], ae[i]);
+      }
+    }
+  }
+  if (MODE == 0) {
+#pragma unroll
+    for (int i = 0; i < kHPer; ++i) {
+      const int k = tid + 256 * i;
+      if (k >= H) continue;
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j)
+        if (j < K) atomicAdd(&a.d_Wd[(size_t)k * K + j], dw[i][j]);
+    }
+    if (tid == 0) {
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j)
+        if (j < K) atomicAdd(&a.d_bd[j], db[j]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kHPer; ++i) {
+      const int k = tid + 256 * i;
+      if (k < H) atomicAdd(&a.d_pred[((size_t)b * d.U1 + u_lo) * H + k], acc[i]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tdt_dur_head(const TdtArgs& a, hipStream_t st) {
+  const size_t lds = sizeof(float) * (size_t)a.d.H * (a.K + 1);
+  hipLaunchKernelGGL(dur_head_kernel, dim3(a.d.T, a.d.B), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tdt_lattice(const TdtArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(tdt_lattice_kernel, dim3(a.d.B, 2), dim3(512), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tdt_post(const TdtArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(tdt_post_kernel, dim3(a.d.T, a.d.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tdt_dur_bwd(const TdtArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(dur_bwd_kernel<0>, dim3((a.d.T + kFrames - 1) / kFrames, a.d.B), dim3(256),
+                     0, st, a);
+  hipLaunchKernelGGL(dur_bwd_kernel<1>, dim3(a.d.U1, a.d.B), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace rnntj

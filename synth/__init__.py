@@ -28,7 +28,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["CONFIGS", "Inputs", "make_inputs", "make_config", "to_bf16_bits",
-           "bf16_bits_to_f64"]
+           "bf16_bits_to_f64", "make_duration_head"]
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -211,3 +211,27 @@ def make_proj_inputs(inp: Inputs, E: int, P: int, *, seed: int = 0, sigma: float
     s = [p[0] for p in parts]
     f = [p[1] for p in parts]
     return ProjInputs(E, P, *s, *f)
+
+
+@dataclasses.dataclass
+class DurationHead:
+    """Duration head of a token-and-duration transducer for one batch:
+    durations (frames per duration class), W_dur [H, K], b_dur [K] as storage
+    arrays with float64 twins."""
+    durations: tuple
+    W_dur: np.ndarray
+    b_dur: np.ndarray
+    W_dur_f64: np.ndarray
+    b_dur_f64: np.ndarray
+
+
+def make_duration_head(inp: Inputs, durations=(0, 1, 2, 3, 4), *, seed: int = 0,
+                       sigma: float = 0.05, b_sigma: float = 0.5) -> DurationHead:
+    """W_dur ~ N(0, sigma) then b_dur ~ N(0, b_sigma), drawn in that order from
+    numpy.random.default_rng(seed) in float64 and cast like the batch."""
+    rng = np.random.default_rng(seed)
+    K = len(durations)
+    W = rng.normal(0.0, sigma, size=(inp.H, K))
+    b = rng.normal(0.0, b_sigma, size=K)
+    (Ws, Wf), (bs, bf) = _cast(W, inp.dtype), _cast(b, inp.dtype)
+    return DurationHead(tuple(int(d) for d in durations), Ws, bs, Wf, bf)

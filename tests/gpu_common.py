@@ -124,3 +124,34 @@ def pruned_oracle(inp, S, utts, workers, grad_costs=None, want_grads=True):
     ctx = multiprocessing.get_context("spawn")
     with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
         return list(ex.map(_pruned_job, jobs))
+
+
+def _tdt_job(args):
+    """One utterance of the token-and-duration oracle (process-pool worker)."""
+    enc_b, pred_b, W, b_out, Wd, bd, y, Tl, Ul, blank, durs, gc, want, threads = args
+    from oracle import tdt
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=threads):
+        o = tdt.utterance(enc_b[:Tl], pred_b[:Ul + 1], W, b_out, Wd, bd, y, Tl, Ul, blank, durs,
+                          grad_cost=gc, want_grads=want)
+    keep = ("cost", "dEnc", "dPred", "dW", "db", "dWd", "dbd")
+    return {k: o[k] for k in keep if k in o}
+
+
+def tdt_oracle(inp, head, utts, workers, grad_costs=None, want_grads=True):
+    """Per-utterance token-and-duration oracle results, one process each."""
+    import multiprocessing
+    import os
+    from concurrent.futures import ProcessPoolExecutor
+    utts = list(utts)
+    gcs = np.ones(inp.B) if grad_costs is None else np.asarray(grad_costs, np.float64)
+    workers = max(1, min(workers, len(utts)))
+    threads = max(1, (os.cpu_count() or 1) // workers)
+    jobs = [(inp.enc_f64[b], inp.pred_f64[b], inp.W_f64, inp.b_f64, head.W_dur_f64,
+             head.b_dur_f64, inp.labels[b], int(inp.T_lens[b]), int(inp.U_lens[b]), inp.blank,
+             head.durations, float(gcs[b]), want_grads, threads) for b in utts]
+    if workers == 1:
+        return [_tdt_job(j) for j in jobs]
+    ctx = multiprocessing.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
+        return list(ex.map(_tdt_job, jobs))

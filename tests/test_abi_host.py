@@ -17,6 +17,8 @@ def test_exports_every_declared_symbol():
                           "rnnt_joint_loss_fwd", "rnnt_joint_loss_fwd_ex", "rnnt_joint_loss_bwd",
                           "rnnt_joint_loss_bwd_noalloc", "rnnt_joint_loss_pruned_fwd",
                           "rnnt_joint_loss_pruned_workspace_bytes", "rnnt_joint_loss_pruned_bounds",
+                          "rnnt_joint_loss_tdt_saved_bytes", "rnnt_joint_loss_tdt_workspace_bytes",
+                          "rnnt_joint_loss_tdt_fwd", "rnnt_joint_loss_tdt_bwd",
                           "rnnt_joint_loss_last_error",
                           "rnnt_joint_loss_status", "rnnt_joint_loss_timing",
                           "rnnt_joint_loss_timing_report", "rnnt_joint_proj_fwd",
@@ -213,3 +215,28 @@ def test_pruned_forward_host_checks():
     assert lib.rnnt_joint_loss_pruned_fwd(*args(0, 0, 3, ws)) == 2   # untiled
     assert lib.rnnt_joint_loss_pruned_fwd(*args(16, 8, 0, ws)) == 1  # S < 1
     assert lib.rnnt_joint_loss_pruned_fwd(*args(16, 8, 3, ws - 8)) == 3
+
+
+def test_tdt_host_checks():
+    """Token-and-duration calls: buffer sizes grow by the duration
+    log-probabilities (saved) and the posteriors and duration gradients
+    (backward workspace); bad duration sets are refused before anything is
+    enqueued."""
+    base = _saved(2, 20, 5, 64, 32, 0, 16, 8)[1]
+    out = ctypes.c_size_t(0)
+    assert lib.rnnt_joint_loss_tdt_saved_bytes(2, 20, 5, 64, 32, 0, 16, 8, 0, 5,
+                                               ctypes.byref(out)) == 0
+    cells = 2 * 25 * 6
+    assert out.value >= base + 4 * cells * 5
+    wsb = _ws(2, 20, 5, 64, 32, 0, 16, 8)[1]
+    assert lib.rnnt_joint_loss_tdt_workspace_bytes(2, 20, 5, 64, 32, 0, 16, 8, 0, 5, 1,
+                                                   ctypes.byref(out)) == 0
+    assert out.value >= wsb + 16 * cells + 4 * cells * 5
+    assert lib.rnnt_joint_loss_tdt_saved_bytes(2, 20, 5, 64, 32, 0, 16, 8, 0, 9,
+                                               ctypes.byref(out)) == 1
+    p = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails its host checks
+    for durs, code in (((0,), 1), ((1, 1), 1), ((0, 16), 2), ((-1, 1), 2)):
+        arr = (ctypes.c_int32 * len(durs))(*durs)
+        rc = lib.rnnt_joint_loss_tdt_fwd(p, p, p, p, p, p, 0, p, p, p, 2, 20, 5, 64, 32, 0, arr,
+                                         len(durs), 16, 8, 0, p, p, None, 0, None)
+        assert rc == code, (durs, rc)
