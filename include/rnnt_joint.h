@@ -100,6 +100,28 @@ enum rnntj_status {
 /* Version of this ABI (RNNTJ_ABI_VERSION of the built library). */
 int rnnt_joint_loss_abi_version(void);
 
+/*
+ * Process-wide switches (robustness aids; no counterpart on the pages).
+ * Initialised when the library loads from the environment: RNNTJ_DEBUG=1 sets
+ * RNNTJ_FLAG_DEBUG, RNNTJ_DETERMINISTIC=1 sets RNNTJ_FLAG_DETERMINISTIC.
+ *   RNNTJ_FLAG_DEBUG: every call waits for each of its kernels and returns
+ *     RNNTJ_ERR_HIP naming the first one that fails (rnnt_joint_loss_last_error),
+ *     and the forward and backward return RNNTJ_ERR_DATA when the state's
+ *     data-error word is nonzero at their end (results are written as usual).
+ *   RNNTJ_FLAG_DETERMINISTIC: the backward reduces d_enc, d_pred, d_W_out and
+ *     d_b_out through partial-sum buffers added in a fixed order instead of
+ *     float atomics, so repeated calls give bitwise identical gradients.  The
+ *     backward workspace is larger in this mode (rnnt_joint_loss_workspace_bytes
+ *     reports the size for the current flags).  The token-and-duration head's
+ *     own reductions and the projection gradients keep their atomics.
+ * Changing the flags while calls are in flight on other threads is not
+ * supported.  set returns RNNTJ_ERR_ARG for unknown bits.
+ */
+#define RNNTJ_FLAG_DEBUG 1
+#define RNNTJ_FLAG_DETERMINISTIC 2
+int rnnt_joint_loss_get_flags(void);
+int rnnt_joint_loss_set_flags(int flags);
+
 /* Human-readable text for a status code; never NULL, static storage. */
 const char* rnnt_joint_loss_strerror(int code);
 

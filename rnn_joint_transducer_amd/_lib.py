@@ -22,6 +22,8 @@ STATUS = {0: "RNNTJ_OK", 1: "RNNTJ_ERR_ARG", 2: "RNNTJ_ERR_UNSUPPORTED",
 _c_int, _c_size, _vp = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
 _SIG = {
     "rnnt_joint_loss_abi_version": (_c_int, []),
+    "rnnt_joint_loss_get_flags": (_c_int, []),
+    "rnnt_joint_loss_set_flags": (_c_int, [_c_int]),
     "rnnt_joint_loss_strerror": (ctypes.c_char_p, [_c_int]),
     "rnnt_joint_loss_last_error": (ctypes.c_char_p, []),
     "rnnt_joint_loss_saved_bytes": (_c_int, [_c_int] * 9 + [ctypes.POINTER(_c_size)]),
@@ -120,3 +122,16 @@ def timing_report() -> dict:
         name, n, ms = line.split()
         out[name] = (int(n), float(ms))
     return out
+
+
+FLAG_DEBUG = 1
+FLAG_DETERMINISTIC = 2
+
+
+def get_flags() -> int:
+    """The library's process-wide switches (FLAG_DEBUG | FLAG_DETERMINISTIC)."""
+    return load().rnnt_joint_loss_get_flags()
+
+
+def set_flags(flags: int) -> None:
+    check(load().rnnt_joint_loss_set_flags(flags), "rnnt_joint_loss_set_flags")

@@ -7,8 +7,10 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <map>
 #include <mutex>
 #include <string>
@@ -26,6 +28,20 @@ constexpr size_t kAlign = 256;
 // utterance are kept in 64 KB of LDS as 16-bit values)
 constexpr int kMaxPrunedT = 32000;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// process-wide switches (rnnt_joint_loss_set_flags), first read from the
+// environment: RNNTJ_DEBUG=1, RNNTJ_DETERMINISTIC=1
+int env_flags() {
+  auto on = [](const char* n) {
+    const char* v = getenv(n);
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+  };
+  return (on("RNNTJ_DEBUG") ? RNNTJ_FLAG_DEBUG : 0) |
+         (on("RNNTJ_DETERMINISTIC") ? RNNTJ_FLAG_DETERMINISTIC : 0);
+}
+std::atomic<int> g_flags{env_flags()};
+inline bool debug_on() { return (g_flags.load() & RNNTJ_FLAG_DEBUG) != 0; }
+inline bool deterministic_on() { return (g_flags.load() & RNNTJ_FLAG_DETERMINISTIC) != 0; }
 
 struct Plan {
   Dims d;
@@ -49,6 +65,10 @@ struct Plan {
   int cap_all;                // active-tile list capacity of the whole lattice
   int n_cu_chunks, n_chunks;  // backward chunk grid (tiled mode)
   int cap_chunk;              // active-tile list capacity of one chunk
+  // deterministic mode: extra backward workspace and the fixed split-K count
+  size_t o_ws_encp, o_ws_predp, o_ws_wpart, o_ws_bpart, ws_bwd_det;
+  int kparts_det;
+  size_t bwd_ws() const { return deterministic_on() ? ws_bwd_det : ws_bwd; }
 };
 
 int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile_u, int tile_v,
@@ -150,6 +170,21 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_ws_tiles = q.o_ws_h + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * H));
   q.o_ws_tcount = q.o_ws_tiles + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks * q.cap_chunk));
   q.ws_bwd = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
+  // deterministic reductions: per-tile d_enc / d_pred rows of one chunk and
+  // the split-K parts of d_W_out / d_b_out
+  {
+    const int cap = q.untiled ? q.cap_all : q.cap_chunk;
+    const int per = ((H + 127) / 128) * ((V + 255) / 256);
+    int kp = 256 * (bf16 ? 2 : 1) / per;
+    kp = kp < 1 ? 1 : (kp > cap ? cap : kp);
+    q.kparts_det = kp;
+    size_t w = align_up(q.ws_bwd);
+    q.o_ws_encp = w;  w = align_up(w + 4 * (size_t)cap * kTileT * H);
+    q.o_ws_predp = w; w = align_up(w + 4 * (size_t)cap * kTileU * H);
+    q.o_ws_wpart = w; w = align_up(w + 4 * (size_t)kp * H * V);
+    q.o_ws_bpart = w; w = align_up(w + 8 * (size_t)kp * V);
+    q.ws_bwd_det = w;
+  }
   return RNNTJ_OK;
 }
 
@@ -210,7 +245,7 @@ size_t tdt_ld_bytes(const Plan& p, int K) {
 // gradients (float32 [cells, K])
 void tdt_ws(const Plan& p, int K, size_t& o_gB, size_t& o_gE, size_t& o_dzd, size_t& total) {
   const size_t cells = (size_t)p.d.B * p.d.DG * p.d.U1;
-  o_gB = align_up(p.ws_bwd);
+  o_gB = align_up(p.bwd_ws());
   o_gE = o_gB + align_up(8 * cells);
   o_dzd = o_gE + align_up(8 * cells);
   total = o_dzd + align_up(4 * cells * K);
@@ -241,6 +276,14 @@ hipError_t note_error(const char* name, hipError_t e) {
 template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   (void)hipGetLastError();
+  if (debug_on()) {
+    // synchronous checking: every kernel completes (and reports) before
+    // the call goes on
+    hipError_t e = launch();
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess) e = hipGetLastError();
+    return note_error(name, e);
+  }
   if (!g_timing) return note_error(name, launch());
   TimedLaunch t{name, nullptr, nullptr};
   if (hipEventCreate(&t.start) != hipSuccess || hipEventCreate(&t.stop) != hipSuccess)
@@ -294,6 +337,18 @@ int scratch_for(hipStream_t st, void** out) {
   }
   *out = g_scratch_ptr[dev];
   return RNNTJ_OK;
+}
+
+// Debug mode: wait for the call's kernels and report a nonzero data-error
+// word of the state as RNNTJ_ERR_DATA (otherwise only
+// rnnt_joint_loss_status reports it).
+int debug_data_check(const int32_t* hdr, hipStream_t st) {
+  if (!debug_on()) return RNNTJ_OK;
+  int32_t v = 0;
+  if (hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpy(&v, hdr, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
+    return RNNTJ_ERR_HIP;
+  return v ? RNNTJ_ERR_DATA : RNNTJ_OK;
 }
 
 // The forward of both entry points: S = 0 the full lattice (criterion sum or
@@ -471,7 +526,7 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
       return RNNTJ_ERR_HIP;
     if ((e = timed("tdt_lattice", st, [&] { return launch_tdt_lattice(g, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    return RNNTJ_OK;
+    return debug_data_check(status, st);
   }
   if ((e = timed("lattice", st, [&] {
          return launch_lattice(LB, LE, Teff, Ueff, p.d, alpha, beta, logP, costs, crit, st);
@@ -481,7 +536,7 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
       (e = timed("backtrace", st, [&] { return launch_backtrace(Teff, Ueff, p.d, beta, st); })) !=
           hipSuccess)
     return RNNTJ_ERR_HIP;
-  return RNNTJ_OK;
+  return debug_data_check(status, st);
 }
 
 // The backward of every entry point (tdt: a token-and-duration state, with
@@ -495,7 +550,7 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   Plan p;
   int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
-  size_t o_gB = 0, o_gE = 0, o_dzd = 0, ws_need = p.ws_bwd;
+  size_t o_gB = 0, o_gE = 0, o_dzd = 0, ws_need = p.bwd_ws();
   if (tdt) {
     if ((rc = check_tdt(*tdt))) return rc;
     if (!d_Wd || !d_bd || misaligned(d_Wd) || misaligned(d_bd)) return RNNTJ_ERR_ARG;
@@ -615,7 +670,16 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   h.d_enc = d_enc;
   h.d_pred = d_pred;
   h.ksplit = 1;
+  const bool det = deterministic_on();
+  if (det) {
+    h.enc_part = at<float>(workspace, p.o_ws_encp);
+    h.pred_part = at<float>(workspace, p.o_ws_predp);
+  }
   DwArgs w = {};
+  if (det) {
+    w.w_part = at<float>(workspace, p.o_ws_wpart);
+    w.b_part = at<double>(workspace, p.o_ws_bpart);
+  }
   w.h = hchunk;
   w.d = p.d;
   w.d_W = d_W_out;
@@ -628,7 +692,16 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   auto kparts_for = [&](int max_tiles) {
     const int per = ((H + 127) / 128) * ((V + 255) / 256);
     int k = device_cu_count() * (p.bf16 ? 2 : 1) / per;
-    return k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
+    k = k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
+    return det ? (k < p.kparts_det ? k : p.kparts_det) : k;
+  };
+  // deterministic mode: dh and dW store partial sums that two ordered
+  // reduction kernels add after each GEMM, in place of float atomics
+  auto reduce = [&]() -> hipError_t {
+    if (!det) return hipSuccess;
+    hipError_t r = timed("dh_reduce", st, [&] { return launch_dh_reduce(h, st); });
+    if (r != hipSuccess) return r;
+    return timed("dw_reduce", st, [&] { return launch_dw_reduce(w, st); });
   };
   auto finalize = [&](int32_t* mark) {
     if (tdt) {
@@ -663,7 +736,9 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
     w.kparts = kparts_for(p.cap_all);
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    return finalize(a.hdr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
+    if (reduce() != hipSuccess) return RNNTJ_ERR_HIP;
+    if (finalize(a.hdr) != hipSuccess) return RNNTJ_ERR_HIP;
+    return debug_data_check(hdr, st);
   }
 
   // tiled: one lattice chunk of CT frames x CU label positions at a time.
@@ -715,9 +790,11 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
       w.kparts = kparts_for(p.cap_chunk);
       if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
         return RNNTJ_ERR_HIP;
+      if (reduce() != hipSuccess) return RNNTJ_ERR_HIP;
     }
   }
-  return finalize(nullptr) == hipSuccess ? RNNTJ_OK : RNNTJ_ERR_HIP;
+  if (finalize(nullptr) != hipSuccess) return RNNTJ_ERR_HIP;
+  return debug_data_check(hdr, st);
 }
 
 }  // namespace
@@ -725,6 +802,14 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
 extern "C" {
 
 int rnnt_joint_loss_abi_version(void) { return RNNTJ_ABI_VERSION; }
+
+int rnnt_joint_loss_get_flags(void) { return g_flags.load(); }
+
+int rnnt_joint_loss_set_flags(int flags) {
+  if (flags & ~(RNNTJ_FLAG_DEBUG | RNNTJ_FLAG_DETERMINISTIC)) return RNNTJ_ERR_ARG;
+  g_flags.store(flags);
+  return RNNTJ_OK;
+}
 
 const char* rnnt_joint_loss_strerror(int code) {
   switch (code) {
@@ -754,7 +839,7 @@ int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype
   Plan p;
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
-  *out = pass == 0 ? p.ws_fwd : p.ws_bwd;
+  *out = pass == 0 ? p.ws_fwd : p.bwd_ws();
   return RNNTJ_OK;
 }
 
@@ -891,7 +976,7 @@ int rnnt_joint_loss_bwd_noalloc(const void* enc, const void* pred, const void* W
   Plan p;
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
-  if (p.ws_bwd > kScratchBytes) return RNNTJ_ERR_WORKSPACE;  // before anything is enqueued
+  if (p.bwd_ws() > kScratchBytes) return RNNTJ_ERR_WORKSPACE;  // before anything is enqueued
   void* ws = nullptr;
   const int src = scratch_for(static_cast<hipStream_t>(stream), &ws);
   if (src) return src;

@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   // An item is carried as its packed tile word and hidden block (two
   // uniform words); decode() expands it where needed (scalar loads).
   struct Item {
-    int b, t0, u0, n0, Tl, Ul;
+    int b, t0, u0, n0, Tl, Ul, tix;
   };
   struct ItemRef {
     int tile, nb, tix, kp;
@@ -263,6 +263,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
     it.n0 = r.nb * C::NB;
     it.Tl = ld_const(a.Teff + it.b);
     it.Ul = ld_const(a.Ueff + it.b);
+    it.tix = r.tix;
     return it;
   };
 
@@ -435,8 +436,12 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
           }
           // the other 4 label positions of this frame live in lane l ^ 32
           es[q4] = esum + __shfl_xor(esum, 32);
-          if (C::kBf16 && kh == 0 && tv)
-            atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], es[q4]);
+          if (C::kBf16 && kh == 0 && tv) {
+            if (a.enc_part)
+              a.enc_part[((size_t)it.tix * kTileT + (t - it.t0)) * H + n] = es[q4];
+            else
+              atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], es[q4]);
+          }
         }
         // fp32: both lane halves hold every frame's sum, so each half adds
         // one of two frames and one full-wave atomic covers two frames (in
@@ -445,8 +450,13 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             const int t = it.t0 + 8 * wm + 4 * i + 2 * m + kh;
-            if (nvalid && t < it.Tl)
-              atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], kh ? es[2 * m + 1] : es[2 * m]);
+            if (nvalid && t < it.Tl) {
+              const float v = kh ? es[2 * m + 1] : es[2 * m];
+              if (a.enc_part)
+                a.enc_part[((size_t)it.tix * kTileT + (t - it.t0)) * H + n] = v;
+              else
+                atomicAdd(&a.d_enc[((size_t)it.b * d.T + t) * H + n], v);
+            }
           }
         }
       }
@@ -478,7 +488,11 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int u = it.u0 + 4 * kh + q;
-            if (u <= it.Ul) atomicAdd(&a.d_pred[((size_t)it.b * d.U1 + u) * H + n], psum[j][q]);
+            if (u > it.Ul) continue;
+            if (a.pred_part)
+              a.pred_part[((size_t)it.tix * kTileU + (u - it.u0)) * H + n] = psum[j][q];
+            else
+              atomicAdd(&a.d_pred[((size_t)it.b * d.U1 + u) * H + n], psum[j][q]);
           }
         }
       }
@@ -637,7 +651,8 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
   const int tb = (int)((long long)count * kp / a.kparts);
   const int te = (int)((long long)count * (kp + 1) / a.kparts);
   const int total = (te - tb) * C::SPT;  // slices of this item
-  if (total <= 0) return;
+  // (with partial buffers an empty part still stores its zeros)
+  if (total <= 0 && !a.w_part) return;
   const int m0 = mb * C::BM, n0 = nb * C::BN;
   const T* __restrict__ Hs = static_cast<const T*>(a.h);
   const T* __restrict__ Gs = static_cast<const T*>(a.g);
@@ -778,6 +793,7 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
 
   // ---- slices 0, 1, 2 in flight; slice g+3 is issued into slice g's buffer
   // once every wave is done reading slice g
+  if (total > 0) {
   issue(0);
   if (total > 1) issue(1);
   if (total > 2) issue(2);
@@ -786,6 +802,7 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
   else wait_vm<0>();
   __builtin_amdgcn_s_barrier();
   rd(0, 0, 0);
+  }
   for (int g = 0; g < total; ++g) {
 #pragma unroll
     for (int kk = 0; kk < C::KSTEPS; ++kk) {
@@ -818,7 +835,11 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 64 * wm + 32 * i + acc_row(r, kh);
-          if (m < H) atomicAdd(&a.d_W[(size_t)m * V + n], acc[i][j][r]);
+          if (m >= H) continue;
+          if (a.w_part)
+            a.w_part[((size_t)kp * H + m) * V + n] = acc[i][j][r];
+          else
+            atomicAdd(&a.d_W[(size_t)m * V + n], acc[i][j][r]);
         }
       }
     }
@@ -828,8 +849,59 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
       // the other 8 cells of each k-step sit in lane l ^ 32
       const double v = dbacc[j] + __shfl_xor(dbacc[j], 32);
       const int n = n0 + 128 * wn + 32 * j + lc;
-      if (kh == 0 && n < V) atomicAdd(&a.d_b64[n], v);
+      if (kh == 0 && n < V) {
+        if (a.b_part)
+          a.b_part[(size_t)kp * V + n] = v;
+        else
+          atomicAdd(&a.d_b64[n], v);
+      }
     }
+  }
+}
+
+// Deterministic d_enc / d_pred of one chunk: thread n of workgroup
+// (b, n-block) walks the chunk's tile list in order and adds the stored
+// per-tile rows of utterance b (each output element has one writer).
+__global__ __launch_bounds__(256) void dh_reduce_kernel(DhArgs a) {
+  if (ld_const(a.hdr + kHdrRefuse)) return;
+  const Dims d = a.d;
+  const int b = blockIdx.x, n = blockIdx.y * 256 + threadIdx.x, H = d.H;
+  if (n >= H) return;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  const int count = a.tile_count[0];
+  for (int i = 0; i < count; ++i) {
+    int tb, tt, tu;
+    tile_unpack(a.tiles[i], tb, tt, tu);
+    if (tb != b) continue;
+    const int t0 = a.ct0 + tt * kTileT, u0 = a.cu0 + tu * kTileU;
+    for (int r = 0; r < kTileT; ++r) {
+      const int t = t0 + r;
+      if (t < Tl)
+        a.d_enc[((size_t)b * d.T + t) * H + n] += a.enc_part[((size_t)i * kTileT + r) * H + n];
+    }
+    for (int q = 0; q < kTileU; ++q) {
+      const int u = u0 + q;
+      if (u <= Ul)
+        a.d_pred[((size_t)b * d.U1 + u) * H + n] += a.pred_part[((size_t)i * kTileU + q) * H + n];
+    }
+  }
+}
+
+// Deterministic d_W_out / d_b_out of one chunk: the split-K parts added in
+// order, one thread per element.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(DwArgs a) {
+  if (ld_const(a.hdr + kHdrRefuse)) return;
+  const size_t HV = (size_t)a.d.H * a.d.V;
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < HV) {
+    float s = 0.f;
+    for (int kp = 0; kp < a.kparts; ++kp) s += a.w_part[kp * HV + i];
+    a.d_W[i] += s;
+  }
+  if (i < (size_t)a.d.V) {
+    double s = 0.0;
+    for (int kp = 0; kp < a.kparts; ++kp) s += a.b_part[(size_t)kp * a.d.V + i];
+    a.d_b64[i] += s;
   }
 }
 
@@ -862,6 +934,17 @@ hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, int max_t
   return hipGetLastError();
 }
 
+hipError_t launch_dh_reduce(const DhArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(dh_reduce_kernel, dim3(a.d.B, (a.d.H + 255) / 256), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw_reduce(const DwArgs& a, hipStream_t st) {
+  const size_t n = (size_t)a.d.H * a.d.V;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) {
   const int nnb = (a.d.H + DhCfg<float>::NB - 1) / DhCfg<float>::NB;
   const int kb = bf16 ? DhCfg<uint16_t>::KB : DhCfg<float>::KB;
@@ -873,7 +956,7 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
   // keeping at least 32 slices per part (the per-item overhead)
   DhArgs b = a;
   b.ksplit = 1;
-  if (a.d.V % kb == 0)
+  if (a.d.V % kb == 0 && !a.enc_part)  // per-tile partial rows: one vocabulary part
     while (b.ksplit < 4 && nk % (2 * b.ksplit) == 0 && nk / (2 * b.ksplit) >= 32 &&
            (long long)max_tiles * nnb * b.ksplit < 3LL * gmax)
       b.ksplit *= 2;

@@ -752,7 +752,9 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
             *reinterpret_cast<uint2*>(&ts[ts_idx(col, 8 * i + 4 * kh)]) = pk;
           }
         }
-        __syncthreads();
+        // Ts[w] is this wave's own: its writes are complete once the wave's
+        // LDS counter drains, no workgroup barrier needed
+        wait_lgkm0();
         if constexpr (MODE == kGrad) {
           // one-hot terms: lane lc of the first half fixes row lc
           if (kh == 0) {
@@ -767,7 +769,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
               *p = f32_to_bf16_hw(bf16_to_f32(*p) - row_e[rowi]);
             }
           }
-          __syncthreads();
+          wait_lgkm0();
         }
         // ... then rows: each lane gets 8 consecutive columns of row l%32.
         // A transposing read hands a lane data addressed by the other lanes

@@ -235,6 +235,11 @@ struct DhArgs {
   int ksplit;                 // vocabulary parts per (tile, hidden block); divides the slice count
   float* d_enc;
   float* d_pred;
+  // deterministic reductions (both set, ksplit 1): each tile's d_enc rows
+  // [tiles, 16, H] and d_pred rows [tiles, 8, H] are stored here instead of
+  // being added with atomics; launch_dh_reduce then adds them in list order
+  float* enc_part;
+  float* pred_part;
 };
 // Persistent launch; max_tiles bounds the entries of the tile list.
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st);
@@ -259,7 +264,14 @@ struct DwArgs {
   const int32_t* hdr;         // state header (refusal word)
   float* d_W;
   double* d_b64;
+  // deterministic reductions (both set): split-K part kp stores its sums in
+  // w_part [kparts, H, V] and b_part [kparts, V] instead of adding them with
+  // atomics; launch_dw_reduce then adds the parts in order
+  float* w_part;
+  double* b_part;
 };
+hipError_t launch_dh_reduce(const DhArgs& a, hipStream_t st);
+hipError_t launch_dw_reduce(const DwArgs& a, hipStream_t st);
 hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st);
 
 // d_b[v] = (float) db64[v]; with `mark` (the state header of an untiled

@@ -8,7 +8,8 @@
 // whose gradients chain from the joint's gradients of enc_p and pred_p:
 //     dx = dy @ W^T,   dW = x^T @ dy,   db = sum over rows of dy.
 //
-// All three products run on one kernel: a 64 x 64 output tile per workgroup
+// The products run on one kernel (plus a bf16 MFMA variant of y = x W + b
+// when x and W are bf16): a 64 x 64 output tile per workgroup
 // (four waves, each a 32 x 32 fp32 MFMA block), 32-deep k-steps staged in LDS
 // as fp32 (bf16 operands are widened on the way in, so every product is
 // exact and accumulates in fp32), the next k-step's global loads issued
@@ -173,6 +174,60 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   }
 }
 
+// y = x W + b with x, W (and y) bf16: the same 64 x 64 tiles and 32-deep
+// k-steps, staged in LDS as bf16 and multiplied by v_mfma_f32_32x32x16_bf16
+// (bf16 products are exact, the sums accumulate in fp32): 16 times the
+// widened fp32 MFMA rate.  x's fragments are 16-byte row reads; W's, with
+// the output column contiguous, come from transposing LDS reads.
+constexpr int kLdA16 = kPK + 8;  // bf16 row strides: 16-byte aligned rows
+constexpr int kLdB16 = kPT + 8;
+__global__ __launch_bounds__(256) void proj_fwd_bf16_kernel(GemmArgs g) {
+  __shared__ __align__(16) uint16_t As[kPT * kLdA16];  // [i][k]
+  __shared__ __align__(16) uint16_t Bs[kPK * kLdB16];  // [k][j]
+  const uint16_t* __restrict__ A = static_cast<const uint16_t*>(g.a);
+  const uint16_t* __restrict__ Bm = static_cast<const uint16_t*>(g.b);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i0 = blockIdx.x * kPT, j0 = blockIdx.y * kPT;
+  const int ai = tid >> 2, ak = (tid & 3) * 8;  // 8 consecutive k of row ai
+  const int bk = tid >> 3, bj = (tid & 7) * 8;  // 8 consecutive j of k-row bk
+  u32x4 av, bv;
+  auto fetch = [&](int k0) {
+    const int gi = i0 + ai, gk = k0 + ak, hk = k0 + bk, hj = j0 + bj;
+    av = u32x4{0u, 0u, 0u, 0u};
+    bv = av;
+    if (gi < g.M && gk < g.K) av = *reinterpret_cast<const u32x4*>(A + (size_t)gi * g.sa + gk);
+    if (hk < g.K && hj < g.N) bv = *reinterpret_cast<const u32x4*>(Bm + (size_t)hk * g.sb + hj);
+  };
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  const int wi = (w >> 1) * 32, wj = (w & 1) * 32;
+  fetch(0);
+  for (int k0 = 0; k0 < g.K; k0 += kPK) {
+    __syncthreads();  // the previous k-step's fragment reads are done
+    *reinterpret_cast<u32x4*>(&As[ai * kLdA16 + ak]) = av;
+    *reinterpret_cast<u32x4*>(&Bs[bk * kLdB16 + bj]) = bv;
+    __syncthreads();
+    if (k0 + kPK < g.K) fetch(k0 + kPK);
+#pragma unroll
+    for (int ks = 0; ks < kPK; ks += 16) {
+      Frag8<uint16_t> fa;
+      fa.v = *reinterpret_cast<const u32x4*>(&As[(wi + (lane & 31)) * kLdA16 + ks + 8 * (lane >> 5)]);
+      const Frag8<uint16_t> fb = load_frag_T(Bs, kLdB16, ks, wj);
+      mma_step(acc, fa, fb);
+    }
+  }
+  const int kh = lane >> 5, col = j0 + wj + (lane & 31);
+  if (col >= g.N) return;
+  const float bias = g.bias ? bf16_to_f32(static_cast<const uint16_t*>(g.bias)[col]) : 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = i0 + wi + acc_row(r, kh);
+    if (row < g.M)
+      static_cast<uint16_t*>(g.c)[(size_t)row * g.ldc + col] = f32_to_bf16_hw(acc[r] + bias);
+  }
+}
+
 template <typename TA, typename TB, bool AK, bool BJ, int OUT, typename TO>
 hipError_t gemm(const GemmArgs& g, int splits, hipStream_t st) {
   const dim3 grid((g.M + kPT - 1) / kPT, (g.N + kPT - 1) / kPT, splits);
@@ -185,7 +240,11 @@ hipError_t gemm(const GemmArgs& g, int splits, hipStream_t st) {
 hipError_t launch_proj_fwd(const void* x, const void* W, const void* b, bool bf16, int M, int K,
                            int N, void* y, hipStream_t st) {
   GemmArgs g{x, K, W, N, b, y, N, M, N, K, K, nullptr};
-  if (bf16) return gemm<uint16_t, uint16_t, true, true, 2, uint16_t>(g, 1, st);
+  if (bf16) {
+    const dim3 grid((M + kPT - 1) / kPT, (N + kPT - 1) / kPT, 1);
+    hipLaunchKernelGGL(proj_fwd_bf16_kernel, grid, dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
   return gemm<float, float, true, true, 2, float>(g, 1, st);
 }
 

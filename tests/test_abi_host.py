@@ -19,6 +19,7 @@ def test_exports_every_declared_symbol():
                           "rnnt_joint_loss_pruned_workspace_bytes", "rnnt_joint_loss_pruned_bounds",
                           "rnnt_joint_loss_tdt_saved_bytes", "rnnt_joint_loss_tdt_workspace_bytes",
                           "rnnt_joint_loss_tdt_fwd", "rnnt_joint_loss_tdt_bwd",
+                          "rnnt_joint_loss_get_flags", "rnnt_joint_loss_set_flags",
                           "rnnt_joint_loss_last_error",
                           "rnnt_joint_loss_status", "rnnt_joint_loss_timing",
                           "rnnt_joint_loss_timing_report", "rnnt_joint_proj_fwd",
@@ -240,3 +241,39 @@ def test_tdt_host_checks():
         rc = lib.rnnt_joint_loss_tdt_fwd(p, p, p, p, p, p, 0, p, p, p, 2, 20, 5, 64, 32, 0, arr,
                                          len(durs), 16, 8, 0, p, p, None, 0, None)
         assert rc == code, (durs, rc)
+
+
+def test_flags_roundtrip_and_environment():
+    """The debug / deterministic switches: set and read back, unknown bits
+    refused, the environment read when the library loads, and the backward
+    workspace growing by the partial-sum buffers in deterministic mode."""
+    import os
+    import subprocess
+    import sys
+    old = _lib.get_flags()
+    try:
+        _lib.set_flags(0)
+        assert _lib.get_flags() == 0
+        plain = _ws(8, 200, 50, 256, 512, 0, 64, 64, 128)[1]
+        _lib.set_flags(_lib.FLAG_DETERMINISTIC)
+        assert _lib.get_flags() == _lib.FLAG_DETERMINISTIC
+        det = _ws(8, 200, 50, 256, 512, 0, 64, 64, 128)[1]
+        # per-tile d_enc / d_pred rows of a 64 x 64 chunk (8 x 4 x 8 tiles) and
+        # at least one split-K part of d_W_out
+        assert det >= plain + 4 * 256 * 24 * 256 + 4 * 256 * 512
+        assert lib.rnnt_joint_loss_set_flags(4) == 1
+        assert _lib.get_flags() == _lib.FLAG_DETERMINISTIC
+    finally:
+        _lib.set_flags(old)
+    code = ("import sys; sys.path.insert(0, %r); from rnn_joint_transducer_amd import _lib; "
+            "print(_lib.get_flags())" % os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    env = dict(os.environ, RNNTJ_DEBUG="1", RNNTJ_DETERMINISTIC="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "3"
+    env = dict(os.environ, RNNTJ_DEBUG="0")
+    env.pop("RNNTJ_DETERMINISTIC", None)
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                       timeout=300)
+    assert r.stdout.strip().splitlines()[-1] == "0"
