@@ -45,12 +45,14 @@
  *     joint and logits in the backward, one lattice chunk of tile_t frames x
  *     tile_u label positions (all utterances) at a time; 0 on one axis means
  *     the whole axis.  tile_t must be a multiple of 16 and tile_u of 8.
- *     tile_v bounds the vocabulary columns of one step of the online max /
- *     log-sum-exp (which never materialises more than one step of logits per
- *     cell): 0 or any multiple of 128.  The kernels step by 128 columns (64
- *     for bf16 with H <= 256), which is within every accepted bound, so tile_v
- *     changes neither memory nor results (the order of the floating-point sums
- *     is the same).
+ *     tile_v (0 or a multiple of 128; 0 = the whole vocabulary) splits each
+ *     chunk of the tiled backward into vocabulary parts of tile_v columns:
+ *     the logit gradients of one part alone are held in the workspace (its
+ *     size falls with tile_v), and every part recomputes the joint for its
+ *     columns.  It is also an upper bound on the columns of one step of the
+ *     online max / log-sum-exp, which the kernels keep at 128 (64 for bf16
+ *     with H <= 256).  The untiled mode stores whole rows of logits and
+ *     ignores tile_v.
  *   - Limits (else RNNTJ_ERR_UNSUPPORTED): H a multiple of 16 with
  *     16 <= H <= 768 for bf16 and H <= 256 for fp32; V a multiple of 8,
  *     8 <= V <= 262144; U + 1 <= 512; B <= 8191; T <= 65520.
@@ -152,9 +154,11 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
  * backward (pass = 1).  The forward needs none.  The backward needs a float64
  * accumulator for d_b_out [V] and, in the tiled mode, the joint activations
  * h of one lattice chunk [B, tile_t, tile_u, H] in dtype (untiled: none,
- * they are in `saved`), that chunk's logit gradients [B, tile_t, tile_u, V]
- * in dtype plus the active-tile list of every chunk (int32, one word per
- * 16 x 8 tile).  Writes *out; returns a status code.
+ * they are in `saved`), that chunk's logit gradients of one vocabulary part
+ * [B, tile_t, tile_u, min(tile_v, V)] (tile_v = 0: V) in dtype plus the
+ * active-tile list of every chunk (int32, one word per 16 x 8 tile); in the
+ * deterministic mode (rnnt_joint_loss_set_flags) also its partial-sum
+ * buffers.  Writes *out; returns a status code.
  */
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
                                     int tile_t, int tile_u, int tile_v, int pass,

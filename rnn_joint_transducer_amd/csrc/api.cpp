@@ -48,6 +48,7 @@ struct Plan {
   bool bf16;
   bool untiled;
   int CT, CU;  // backward chunk extents
+  int Vp;      // vocabulary columns per part of the tiled backward
   size_t elem;
   // saved layout (byte offsets)
   size_t o_h;  // untiled: h rows [B, Tpad, U1pad, H]
@@ -82,8 +83,9 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   if (U + 1 > 512) return RNNTJ_ERR_UNSUPPORTED;
   if (B > 8191 || T > 65520) return RNNTJ_ERR_UNSUPPORTED;  // packed tile coordinates
   if (tile_t % kTileT != 0 || tile_u % kTileU != 0) return RNNTJ_ERR_UNSUPPORTED;
-  // tile_v bounds the vocabulary columns of one online log-sum-exp step; the
-  // kernels step by kVocabTile, which is within any accepted tile_v
+  // tile_v: vocabulary columns of one part of the tiled backward (and an
+  // upper bound on the columns of one online log-sum-exp step, which steps
+  // by at most kVocabTile); 0 = the whole vocabulary
   if (tile_v % kVocabTile != 0) return RNNTJ_ERR_UNSUPPORTED;
   Plan& q = *p;
   q.bf16 = bf16;
@@ -101,6 +103,9 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.untiled = (tile_t == 0 && tile_u == 0);
   q.CT = q.untiled ? q.d.Tpad : (tile_t ? (tile_t < q.d.Tpad ? tile_t : q.d.Tpad) : q.d.Tpad);
   q.CU = q.untiled ? q.d.U1pad : (tile_u ? (tile_u < q.d.U1pad ? tile_u : q.d.U1pad) : q.d.U1pad);
+  // tiled backward: each chunk's vocabulary in parts of Vp columns, whose
+  // logit gradients alone are held at once
+  q.Vp = (q.untiled || tile_v == 0 || tile_v >= V) ? V : tile_v;
   const size_t cells = (size_t)B * q.d.DG * q.d.U1;
   size_t o = 0;
   q.o_status = o; o = align_up(o + 4 * kHdrWords);
@@ -158,14 +163,14 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
     q.ws_pruned = w;
   }
   // backward workspace: float64 d_b_out accumulator [V], then (tiled) one
-  // chunk of logit gradients [B, CT, CU, V] and its joint activations h
+  // chunk's logit gradients of one vocabulary part [B, CT, CU, Vp] and its joint activations h
   // [B, CT, CU, H] (untiled: none, the forward keeps h)
   q.n_cu_chunks = (q.d.U1pad + q.CU - 1) / q.CU;
   q.n_chunks = ((q.d.Tpad + q.CT - 1) / q.CT) * q.n_cu_chunks;
   q.cap_chunk = B * (q.CT / kTileT) * (q.CU / kTileU);
   q.o_ws_db = 0;
   q.o_ws_g = align_up(8 * (size_t)V);
-  q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * V));
+  q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * q.Vp));
   // (untiled: the h rows are part of the saved state instead)
   q.o_ws_tiles = q.o_ws_h + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * H));
   q.o_ws_tcount = q.o_ws_tiles + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks * q.cap_chunk));
@@ -174,15 +179,15 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   // the split-K parts of d_W_out / d_b_out
   {
     const int cap = q.untiled ? q.cap_all : q.cap_chunk;
-    const int per = ((H + 127) / 128) * ((V + 255) / 256);
+    const int per = ((H + 127) / 128) * ((q.Vp + 255) / 256);
     int kp = 256 * (bf16 ? 2 : 1) / per;
     kp = kp < 1 ? 1 : (kp > cap ? cap : kp);
     q.kparts_det = kp;
     size_t w = align_up(q.ws_bwd);
     q.o_ws_encp = w;  w = align_up(w + 4 * (size_t)cap * kTileT * H);
     q.o_ws_predp = w; w = align_up(w + 4 * (size_t)cap * kTileU * H);
-    q.o_ws_wpart = w; w = align_up(w + 4 * (size_t)kp * H * V);
-    q.o_ws_bpart = w; w = align_up(w + 8 * (size_t)kp * V);
+    q.o_ws_wpart = w; w = align_up(w + 4 * (size_t)kp * H * q.Vp);
+    q.o_ws_bpart = w; w = align_up(w + 8 * (size_t)kp * q.Vp);
     q.ws_bwd_det = w;
   }
   return RNNTJ_OK;
@@ -493,6 +498,9 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   a.zstep = p.zstep;
   a.bounds = bounds;
   a.band = S;
+  a.gv0 = 0;
+  a.gvw = V;
+  a.gld = V;
   if ((e = timed(p.untiled ? "joint_fwd_store" : "joint_fwd", st, [&] {
          return launch_joint_tile(a, p.untiled ? kStoreZ : kLse, p.bf16, p.cap_all, st);
        })) != hipSuccess)
@@ -670,12 +678,18 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   h.d_enc = d_enc;
   h.d_pred = d_pred;
   h.ksplit = 1;
+  h.v0 = 0;
+  h.vw = V;
+  h.ldg = V;
   const bool det = deterministic_on();
   if (det) {
     h.enc_part = at<float>(workspace, p.o_ws_encp);
     h.pred_part = at<float>(workspace, p.o_ws_predp);
   }
   DwArgs w = {};
+  w.v0 = 0;
+  w.vw = V;
+  w.ldg = V;
   if (det) {
     w.w_part = at<float>(workspace, p.o_ws_wpart);
     w.b_part = at<double>(workspace, p.o_ws_bpart);
@@ -690,17 +704,22 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   // compute unit for bf16, one for fp32), fewest float32 partial sums per
   // output element
   auto kparts_for = [&](int max_tiles) {
-    const int per = ((H + 127) / 128) * ((V + 255) / 256);
+    const int per = ((H + 127) / 128) * ((p.Vp + 255) / 256);  // items of one part
     int k = device_cu_count() * (p.bf16 ? 2 : 1) / per;
-    k = k < 1 ? 1 : (k > max_tiles ? max_tiles : k);
+    // each run at least 4 tiles: shorter runs spend more on their atomics
+    // (an H x 256 block per item) than on their MFMAs
+    const int kmax = max_tiles / 4 > 1 ? max_tiles / 4 : 1;
+    k = k < 1 ? 1 : (k > kmax ? kmax : k);
     return det ? (k < p.kparts_det ? k : p.kparts_det) : k;
   };
   // deterministic mode: dh and dW store partial sums that two ordered
   // reduction kernels add after each GEMM, in place of float atomics
-  auto reduce = [&]() -> hipError_t {
+  auto reduce_dh = [&]() -> hipError_t {
     if (!det) return hipSuccess;
-    hipError_t r = timed("dh_reduce", st, [&] { return launch_dh_reduce(h, st); });
-    if (r != hipSuccess) return r;
+    return timed("dh_reduce", st, [&] { return launch_dh_reduce(h, st); });
+  };
+  auto reduce_dw = [&]() -> hipError_t {
+    if (!det) return hipSuccess;
     return timed("dw_reduce", st, [&] { return launch_dw_reduce(w, st); });
   };
   auto finalize = [&](int32_t* mark) {
@@ -736,7 +755,7 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
     w.kparts = kparts_for(p.cap_all);
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    if (reduce() != hipSuccess) return RNNTJ_ERR_HIP;
+    if (reduce_dh() != hipSuccess || reduce_dw() != hipSuccess) return RNNTJ_ERR_HIP;
     if (finalize(a.hdr) != hipSuccess) return RNNTJ_ERR_HIP;
     return debug_data_check(hdr, st);
   }
@@ -748,7 +767,7 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   // each part keeps at least 8 vocabulary tiles: every part rebuilds the
   // tile's h rows and posteriors, which shorter parts do not amortise.
   const int chunk_tiles = p.cap_chunk;
-  const int nvt = (V + kVocabTile - 1) / kVocabTile;
+  const int nvt = (p.Vp + kVocabTile - 1) / kVocabTile;
   int vsplit = 1;
   while (chunk_tiles * vsplit < 1024 && nvt / (2 * vsplit) >= 8) vsplit *= 2;
   int32_t* ctiles = at<int32_t>(workspace, p.o_ws_tiles);
@@ -772,25 +791,35 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
       a.hout = hchunk;
       a.tiles = ctiles + (size_t)chunk * p.cap_chunk;
       a.tile_count = ccount + chunk;
-      if ((e = timed("joint_grad", st, [&] {
-             return launch_joint_tile(a, kGrad, p.bf16, p.cap_chunk * vsplit, st);
-           })) != hipSuccess)
-        return RNNTJ_ERR_HIP;
       h.g = gchunk;
       h.ct0 = ct0; h.cu0 = cu0; h.CT = p.CT; h.CU = p.CU;
       h.tiles = a.tiles;
       h.tile_count = a.tile_count;
-      if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_chunk, st); })) !=
-          hipSuccess)
-        return RNNTJ_ERR_HIP;
       w.g = gchunk;
       w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;
       w.tiles = a.tiles;
       w.tile_count = a.tile_count;
       w.kparts = kparts_for(p.cap_chunk);
-      if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
-        return RNNTJ_ERR_HIP;
-      if (reduce() != hipSuccess) return RNNTJ_ERR_HIP;
+      // the chunk's vocabulary in parts of Vp columns: the logit gradients
+      // of one part, that part's share of dh (linear in dz, so the parts'
+      // d_enc / d_pred contributions add) and its columns of dW
+      for (int v0 = 0; v0 < V; v0 += p.Vp) {
+        const int vw = V - v0 < p.Vp ? V - v0 : p.Vp;
+        a.gv0 = v0; a.gvw = vw; a.gld = p.Vp;
+        h.v0 = v0; h.vw = vw; h.ldg = p.Vp;
+        w.v0 = v0; w.vw = vw; w.ldg = p.Vp;
+        if ((e = timed("joint_grad", st, [&] {
+               return launch_joint_tile(a, kGrad, p.bf16, p.cap_chunk * vsplit, st);
+             })) != hipSuccess)
+          return RNNTJ_ERR_HIP;
+        if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_chunk, st); })) !=
+            hipSuccess)
+          return RNNTJ_ERR_HIP;
+        if (reduce_dh() != hipSuccess) return RNNTJ_ERR_HIP;
+        if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
+          return RNNTJ_ERR_HIP;
+        if (reduce_dw() != hipSuccess) return RNNTJ_ERR_HIP;
+      }
     }
   }
   if (finalize(nullptr) != hipSuccess) return RNNTJ_ERR_HIP;
@@ -977,6 +1006,8 @@ int rnnt_joint_loss_bwd_noalloc(const void* enc, const void* pred, const void* W
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
   if (p.bwd_ws() > kScratchBytes) return RNNTJ_ERR_WORKSPACE;  // before anything is enqueued
+  if (!enc || !pred || !W_out || !b_out || !saved || !d_enc || !d_pred || !d_W_out || !d_b_out)
+    return RNNTJ_ERR_ARG;
   void* ws = nullptr;
   const int src = scratch_for(static_cast<hipStream_t>(stream), &ws);
   if (src) return src;

@@ -209,6 +209,9 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   const int kh = lane >> 5, lc = lane & 31;
   const int wm = w >> 1, wn = w & 1;
   const int H = d.H, V = d.V;
+  // vocabulary part [V0, V0 + VW) of this launch: dz rows have stride LG, W_out
+  // rows stride V
+  const int V0 = a.v0, VW = a.vw, LG = a.ldg;
   const T* __restrict__ G = static_cast<const T*>(a.g);
   const T* __restrict__ W = static_cast<const T*>(a.W);
   const int nnb = (H + C::NB - 1) / C::NB;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   // linear in dz, so the parts' d_enc / d_pred contributions simply add)
   const int ks = a.ksplit;
   const int n_items = n_tiles * nnb * ks;
-  const int nk = (V + C::KB - 1) / C::KB;  // slices of the whole vocabulary
+  const int nk = (VW + C::KB - 1) / C::KB;  // slices of the vocabulary part
   const int nks = nk / ks;                  // slices of one item (ks divides nk)
   // Workgroups are dealt to the 8 XCDs round-robin (blockIdx % 8).  XCD x
   // takes the x-th of 8 contiguous runs of items, its workgroups striding
@@ -289,21 +292,21 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   auto copy_off = [&](int q, int k0) -> uint32_t {  // element offset of copy q
     const int ins = C::CPW * w + q;  // uniform
     const int r = C::RPC * ins + lr;
-    const int col = min(k0 + slot_of<C::RB>(r, lcc) * C::CE, V - C::CE);
+    const int col = min(k0 + slot_of<C::RB>(r, lcc) * C::CE, VW - C::CE);
     if (ins < kTileCells / C::RPC) {  // dz rows of the tile
       int dt = r >> 3, du = r & 7;
       const bool ok = src_it.t0 + dt < src_it.Tl && src_it.u0 + du <= src_it.Ul;
       dt = ok ? dt : 0;
       du = ok ? du : 0;
-      return (uint32_t)((dt * a.CU + du) * V + col);
+      return (uint32_t)((dt * a.CU + du) * LG + col);
     }
     const int n = min(src_it.n0 + r - kTileCells, H - 1);
-    return (uint32_t)(n * V + col);
+    return (uint32_t)(n * V + V0 + col);
   };
   auto set_sources = [&](ItemRef ref) {
     src_it = decode(ref);
     src_k0 = ref.kp * nks * C::KB;
-    gbase = G + (((size_t)src_it.b * a.CT + (src_it.t0 - a.ct0)) * a.CU + (src_it.u0 - a.cu0)) * V;
+    gbase = G + (((size_t)src_it.b * a.CT + (src_it.t0 - a.ct0)) * a.CU + (src_it.u0 - a.cu0)) * LG;
     if constexpr (C::OCC == 1) {
 #pragma unroll
       for (int q = 0; q < C::CPW; ++q) coff[q] = copy_off(q, 0);
@@ -312,7 +315,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   auto issue = [&](int s, int buf) {
     const int k0 = src_k0 + s * C::KB;
     const uint32_t st = lbase + buf * C::SLICE + C::CPW * w * 1024;
-    const bool tail = k0 + C::KB > V;
+    const bool tail = k0 + C::KB > VW;
 #pragma unroll
     for (int q = 0; q < C::CPW; ++q) {
       const T* base = (C::CPW * w + q < kTileCells / C::RPC) ? gbase : W;
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
 
   Frag8<T> fa[2][2], fb[2][4];
   // fragments of k-step kk of stream slice g (buffer g % NST)
-  const bool has_vtail = V % C::KB != 0;
+  const bool has_vtail = VW % C::KB != 0;
   auto rd = [&](int g, int kk, int fbuf) {
     const char* sl = lds + (g % C::NST) * C::SLICE;
     const int s = g % nks;  // slice of the item (ks == 1 whenever V has a tail)
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
         fa[fbuf][i].lo = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh) << 4));
         fa[fbuf][i].hi = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh + 1) << 4));
       }
-      if (vtail && kbase >= V) zero_frag(fa[fbuf][i]);  // vocabulary tail
+      if (vtail && kbase >= VW) zero_frag(fa[fbuf][i]);  // vocabulary tail
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -639,7 +642,9 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
   const int kh = lane >> 5, lc = lane & 31;
   const int wm = w >> 1, wn = w & 1;
   const int H = d.H, V = d.V;
-  const int nmb = (H + C::BM - 1) / C::BM, nnb = (V + C::BN - 1) / C::BN;
+  // vocabulary part [V0, V0 + VW): dz columns (row stride LG), d_W_out columns
+  const int V0 = a.v0, VW = a.vw, LG = a.ldg;
+  const int nmb = (H + C::BM - 1) / C::BM, nnb = (VW + C::BN - 1) / C::BN;
   const int nmn = nmb * nnb;
   // item of this workgroup: XCD x = blockIdx % 8 takes items x * per .. +per-1
   const int per = gridDim.x >> 3;
@@ -680,8 +685,8 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
       const int qb = q - C::CA;
       const int row = qb * (1024 / C::ROWB) + lane / C::GB;
       const int lg = (lane % C::GB) ^ swz_dw(row);
-      const int col = min(n0 + lg * C::CE, V - C::CE);
-      off = (uint32_t)((((row >> 3) * a.CU) + (row & 7)) * V + col);
+      const int col = min(n0 + lg * C::CE, VW - C::CE);
+      off = (uint32_t)((((row >> 3) * a.CU) + (row & 7)) * LG + col);
     }
     coff[k] = off;
   }
@@ -692,7 +697,7 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
     // the slice's first cell row: frame tt*16 + ss*KB/8, label position tu*8
     const size_t crow = ((size_t)b * a.CT + tt * kTileT + ss * (C::KB / 8)) * a.CU + tu * kTileU;
     const T* hb = Hs + crow * H;
-    const T* gb = Gs + crow * V;
+    const T* gb = Gs + crow * LG;
     const uint32_t st = lbase + (g % C::NST) * C::SLICE;
 #pragma unroll
     for (int k = 0; k < C::QPW; ++k) {
@@ -831,15 +836,15 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int n = n0 + 128 * wn + 32 * j + lc;
-      if (n < V) {
+      if (n < VW) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 64 * wm + 32 * i + acc_row(r, kh);
           if (m >= H) continue;
           if (a.w_part)
-            a.w_part[((size_t)kp * H + m) * V + n] = acc[i][j][r];
+            a.w_part[((size_t)kp * H + m) * LG + n] = acc[i][j][r];
           else
-            atomicAdd(&a.d_W[(size_t)m * V + n], acc[i][j][r]);
+            atomicAdd(&a.d_W[(size_t)m * V + V0 + n], acc[i][j][r]);
         }
       }
     }
@@ -849,11 +854,11 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
       // the other 8 cells of each k-step sit in lane l ^ 32
       const double v = dbacc[j] + __shfl_xor(dbacc[j], 32);
       const int n = n0 + 128 * wn + 32 * j + lc;
-      if (kh == 0 && n < V) {
+      if (kh == 0 && n < VW) {
         if (a.b_part)
-          a.b_part[(size_t)kp * V + n] = v;
+          a.b_part[(size_t)kp * LG + n] = v;
         else
-          atomicAdd(&a.d_b64[n], v);
+          atomicAdd(&a.d_b64[V0 + n], v);
       }
     }
   }
@@ -887,21 +892,24 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(DhArgs a) {
   }
 }
 
-// Deterministic d_W_out / d_b_out of one chunk: the split-K parts added in
-// order, one thread per element.
+// Deterministic d_W_out / d_b_out of one vocabulary part of one chunk: the
+// split-K parts (stored [kparts, H, ldg] and [kparts, ldg]) added in order,
+// one thread per element of the part's columns.
 __global__ __launch_bounds__(256) void dw_reduce_kernel(DwArgs a) {
   if (ld_const(a.hdr + kHdrRefuse)) return;
-  const size_t HV = (size_t)a.d.H * a.d.V;
+  const int H = a.d.H, V = a.d.V, VW = a.vw, LG = a.ldg;
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < HV) {
+  const size_t HL = (size_t)H * LG;
+  if (i < (size_t)H * VW) {
+    const int m = (int)(i / VW), n = (int)(i % VW);
     float s = 0.f;
-    for (int kp = 0; kp < a.kparts; ++kp) s += a.w_part[kp * HV + i];
-    a.d_W[i] += s;
+    for (int kp = 0; kp < a.kparts; ++kp) s += a.w_part[kp * HL + (size_t)m * LG + n];
+    a.d_W[(size_t)m * V + a.v0 + n] += s;
   }
-  if (i < (size_t)a.d.V) {
+  if (i < (size_t)VW) {
     double s = 0.0;
-    for (int kp = 0; kp < a.kparts; ++kp) s += a.b_part[(size_t)kp * a.d.V + i];
-    a.d_b64[i] += s;
+    for (int kp = 0; kp < a.kparts; ++kp) s += a.b_part[(size_t)kp * LG + i];
+    a.d_b64[a.v0 + i] += s;
   }
 }
 
@@ -940,7 +948,7 @@ hipError_t launch_dh_reduce(const DhArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_dw_reduce(const DwArgs& a, hipStream_t st) {
-  const size_t n = (size_t)a.d.H * a.d.V;
+  const size_t n = (size_t)a.d.H * a.vw;
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -948,7 +956,7 @@ hipError_t launch_dw_reduce(const DwArgs& a, hipStream_t st) {
 hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) {
   const int nnb = (a.d.H + DhCfg<float>::NB - 1) / DhCfg<float>::NB;
   const int kb = bf16 ? DhCfg<uint16_t>::KB : DhCfg<float>::KB;
-  const int nk = (a.d.V + kb - 1) / kb;
+  const int nk = (a.vw + kb - 1) / kb;
   // resident workgroups (a multiple of 8: one per XCD in turn)
   const int gmax = max(8, (device_cu_count() * (bf16 ? DhCfg<uint16_t>::OCC : DhCfg<float>::OCC)) & ~7);
   // split the vocabulary of each (tile, hidden block) until every resident
@@ -956,7 +964,7 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
   // keeping at least 32 slices per part (the per-item overhead)
   DhArgs b = a;
   b.ksplit = 1;
-  if (a.d.V % kb == 0 && !a.enc_part)  // per-tile partial rows: one vocabulary part
+  if (a.vw % kb == 0 && !a.enc_part)  // per-tile partial rows: one vocabulary part
     while (b.ksplit < 4 && nk % (2 * b.ksplit) == 0 && nk / (2 * b.ksplit) >= 32 &&
            (long long)max_tiles * nnb * b.ksplit < 3LL * gmax)
       b.ksplit *= 2;
@@ -971,7 +979,7 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
 
 hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st) {
   const int nmb = (a.d.H + DwCfg<float>::BM - 1) / DwCfg<float>::BM;
-  const int nnb = (a.d.V + DwCfg<float>::BN - 1) / DwCfg<float>::BN;
+  const int nnb = (a.vw + DwCfg<float>::BN - 1) / DwCfg<float>::BN;
   const long long items = (long long)nmb * nnb * a.kparts;
   if (items <= 0) return hipSuccess;
   dim3 grid((unsigned)((items + 7) / 8 * 8)), block(256);  // 8 XCDs, items grouped per XCD

@@ -278,10 +278,16 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   if (MODE == kGrad && ld_const(a.hdr + kHdrRefuse)) return;  // state refused by this backward
   const int hflags = a.hdr[1];
   const bool use_ep = (hflags & kFlagEpBad) == 0;
-  const bool stage_ep = EP::kStage && use_ep;
+  // kGrad in a vocabulary part after the first: the tile's h rows were
+  // stored by the first part; they are read back instead of rebuilt
+  const bool h_from_mem = MODE == kGrad && a.gv0 > 0;
+  const bool stage_ep = EP::kStage && use_ep && !h_from_mem;
   const bool bounded = __int_as_float(a.hdr[2]) < 64.0f;  // NaN bound -> false
 
-  const int nvt_all = (V + VT - 1) / VT;
+  // vocabulary steps of this launch: [gv0, gv0 + gvw) (the whole vocabulary
+  // outside the tiled backward's vocabulary parts)
+  const int vt0 = (MODE == kGrad) ? a.gv0 / VT : 0;
+  const int nvt_all = (MODE == kGrad) ? (a.gvw + VT - 1) / VT : (V + VT - 1) / VT;
   const int vsplit = (MODE == kGrad) ? a.vsplit : 1;
   const int nkc = EXACT ? KC_MAX : (H + C::BK - 1) / C::BK;
   const int n_items = a.tile_count[0] * vsplit;
@@ -336,8 +342,9 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   // first vocabulary tile and slice count of an item
   auto item_range = [&](int it, int& vb, int& ns) {
     const int r = (MODE == kGrad) ? it % vsplit : 0;
-    vb = (nvt_all * r) / vsplit;
-    ns = ((nvt_all * (r + 1)) / vsplit - vb) * nkc;
+    const int base = (nvt_all * r) / vsplit;
+    vb = vt0 + base;
+    ns = ((nvt_all * (r + 1)) / vsplit - base) * nkc;
   };
   // the slice being computed sits in Ws1 when `par` is set; the last slice
   // of an item starts the copy of the next item's first slice (`pre`)
@@ -399,7 +406,17 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     const int t = t0 + 4 * w + tt, u = u0 + uu;
     const bool valid = (t < Tl) && (u <= Ul);
     const int tv = valid ? t : 0, uv = valid ? u : 0;
-    if constexpr (EP::kStage) {
+    if (h_from_mem) {
+      // the same fragments the first part built and stored (zero rows
+      // outside the lattice)
+      const T* hrow = static_cast<const T*>(a.hout) +
+                      (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (EXACT || ks < nks) hA[ks] = load_frag(hrow + ks * 16);
+        else zero_frag(hA[ks]);
+      }
+    } else if constexpr (EP::kStage) {
       // exponential rows from LDS
       if (use_ep) {
         const float* er = reinterpret_cast<const float*>(Ep) + (4 * w + tt) * H + 8 * kh;
@@ -491,7 +508,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     // after the barrier, so the first slice's MFMAs cover their completion
     // instead of the barrier waiting for it.  (Untiled forward: the h rows
     // of the whole padded lattice, kept for the backward.)
-    if (vr == 0 && (MODE == kGrad || a.hout != nullptr)) {
+    if (vr == 0 && (MODE == kGrad ? a.gv0 == 0 : a.hout != nullptr)) {
       const int t = t0 + 4 * w + (lc >> 3), u = u0 + (lc & 7);
       T* hrow = static_cast<T*>(a.hout) +
                 (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
@@ -700,6 +717,10 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
       const int RT = MODE == kGrad ? a.CT : d.Tpad, RU = MODE == kGrad ? a.CU : d.U1pad;
       const int rt0 = MODE == kGrad ? a.ct0 : 0, ru0 = MODE == kGrad ? a.cu0 : 0;
       T* out = static_cast<T*>(MODE == kGrad ? a.gout : a.zout);
+      // rows of the output: the whole vocabulary (logits), or the launch's
+      // vocabulary part (logit gradients)
+      const size_t ldz = MODE == kGrad ? (size_t)a.gld : (size_t)V;
+      const int zc0 = MODE == kGrad ? a.gv0 : 0;
       if constexpr (MODE == kStoreZ && kBf16) {
         // Stored as bf16(z - M), M = the row's largest logit of this step
         // (kept in float32 beside them).  A logit of size |z| would carry a
@@ -782,7 +803,8 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
         // the tile (zero outside the lattice), as the weight gradient reads
         // whole tiles
         const bool row_st = MODE == kGrad || row_ok;
-        T* orow = out + (((size_t)b * RT + (row_st ? t - rt0 : 0)) * RU + (row_st ? u - ru0 : 0)) * V + vt;
+        T* orow = out + (((size_t)b * RT + (row_st ? t - rt0 : 0)) * RU + (row_st ? u - ru0 : 0)) * ldz +
+                  (vt - zc0);
         const int g = lane >> 4, i = lane & 15;
 #pragma unroll
         for (int f = 0; f < VT / 16; ++f) {
@@ -810,7 +832,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
           const int t = t0 + 4 * w + (r >> 2), u = u0 + 4 * kh + (r & 3);
           const bool ok = t < Tl && u <= Ul;
           if (MODE == kGrad || ok) {
-            T* orow = out + (((size_t)b * RT + (t - rt0)) * RU + (u - ru0)) * V;
+            T* orow = out + (((size_t)b * RT + (t - rt0)) * RU + (u - ru0)) * ldz;
 #pragma unroll
             for (int blk = 0; blk < NBLK; ++blk) {
               const int col = vt + blk * 32 + lc;
@@ -821,7 +843,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
                   if (col == lab[r & 3]) g -= row_e[rowi];
                   g = ok ? g : 0.f;
                 }
-                orow[col] = g;
+                orow[col - zc0] = g;
               }
             }
           }

@@ -87,7 +87,10 @@ struct JointArgs {
   const double* beta;
   const double* logP;
   const float* gcost;  // [B] or null
-  void* gout;          // kGrad: logit gradients [B, CT, CU, V]
+  // kGrad: the vocabulary part [gv0, gv0 + gvw) of this launch (gv0 a
+  // multiple of the vocabulary step); gout rows have stride gld
+  int gv0, gvw, gld;
+  void* gout;          // kGrad: logit gradients [B, CT, CU, gld] of the part
   void* hout;          // kGrad: joint activations h [B, CT, CU, H]; kStoreZ: the h rows
                        // [B, Tpad, U1pad, H] of the active tiles, or null
 };
@@ -218,7 +221,7 @@ hipError_t launch_backtrace(const int32_t* Teff, const int32_t* Ueff, const Dims
 int device_cu_count();
 
 struct DhArgs {
-  const void* g;      // [B, CT, CU, V] logit gradients of the chunk
+  const void* g;      // [B, CT, CU, ldg] logit gradients of the chunk's vocabulary part
   const void* W;      // [H, V]
   const void* enc;
   const void* pred;
@@ -233,6 +236,7 @@ struct DhArgs {
   const float* gcost;         // [B] or null
   int ct0, cu0, CT, CU;
   int ksplit;                 // vocabulary parts per (tile, hidden block); divides the slice count
+  int v0, vw, ldg;            // vocabulary part [v0, v0 + vw) of g (row stride ldg) and W_out
   float* d_enc;
   float* d_pred;
   // deterministic reductions (both set, ksplit 1): each tile's d_enc rows
@@ -254,13 +258,14 @@ hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, int max_t
 // d_W_out += h^T dz and d_b64 += column sums of dz (float64) over the active
 // tiles of one chunk (split-K over the tile list).
 struct DwArgs {
-  const void* g;              // dz rows [B, CT, CU, V]
+  const void* g;              // dz rows [B, CT, CU, ldg] of the vocabulary part
   const void* h;              // h rows [B, CT, CU, H]; rows of cells outside the lattice are 0
   const int32_t* tiles;       // active tiles of the chunk
   const int32_t* tile_count;
   Dims d;
   int ct0, cu0, CT, CU;
   int kparts;                 // split-K: parts of the tile list
+  int v0, vw, ldg;            // vocabulary part [v0, v0 + vw): columns of g (row stride ldg)
   const int32_t* hdr;         // state header (refusal word)
   float* d_W;
   double* d_b64;

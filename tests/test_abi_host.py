@@ -181,17 +181,20 @@ def test_proj_rejects_before_launch():
 def test_noalloc_backward_rejects_sizes_beyond_its_scratch():
     """The no-allocation backward refuses, before anything is enqueued, sizes
     whose backward workspace exceeds its static scratch (64 MiB): the long
-    workload in 64 x 64 chunks needs ~0.3 GB of logit gradients per chunk."""
-    ws = _ws(8, 1500, 300, 640, 4096, 1, 64, 64, 256)[1]
+    workload in 64 x 64 chunks over the whole vocabulary needs ~0.3 GB of
+    logit gradients per chunk.  In vocabulary parts of 256 columns it needs
+    ~59 MB, which passes the size check (and then fails the null pointers)."""
+    ws = _ws(8, 1500, 300, 640, 4096, 1, 64, 64, 0)[1]
     assert ws > (64 << 20)
-    rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 8, 1500,
-                                         300, 640, 4096, 0, 64, 64, 256, None, None, None, None,
-                                         None, None, None)
-    assert rc == 3
     rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 8, 1500,
                                          300, 640, 4096, 0, 64, 64, 0, None, None, None, None,
                                          None, None, None)
     assert rc == 3
+    assert _ws(8, 1500, 300, 640, 4096, 1, 64, 64, 256)[1] <= (64 << 20)
+    rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 8, 1500,
+                                         300, 640, 4096, 0, 64, 64, 256, None, None, None, None,
+                                         None, None, None)
+    assert rc == 1
     # bad sizes are reported as for the other entry points
     rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 0, 10,
                                          3, 64, 64, 0, 0, 0, 0, None, None, None, None,
@@ -277,3 +280,16 @@ def test_flags_roundtrip_and_environment():
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
                        timeout=300)
     assert r.stdout.strip().splitlines()[-1] == "0"
+
+
+def test_workspace_falls_with_tile_v():
+    """The tiled backward holds one vocabulary part of a chunk's logit
+    gradients: its workspace shrinks by B*tile_t*tile_u*(V - tile_v)
+    elements as tile_v narrows; the untiled mode ignores tile_v."""
+    B, T, U, H, V = 8, 1500, 300, 640, 4096
+    full = _ws(B, T, U, H, V, 1, 64, 64, 0)[1]
+    for tv in (128, 256, 1024):
+        part = _ws(B, T, U, H, V, 1, 64, 64, tv)[1]
+        assert full - part >= 2 * B * 64 * 64 * (V - tv) - 4096
+    assert _ws(B, T, U, H, V, 1, 64, 64, 8192)[1] == full
+    assert _ws(2, 20, 5, 64, 32, 0, 0, 0, 128)[1] == _ws(2, 20, 5, 64, 32, 0, 0, 0, 0)[1]

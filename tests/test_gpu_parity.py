@@ -550,3 +550,32 @@ def test_backward_checks_the_state_it_is_given():
     _, small = rj.rnnt_joint_loss_fwd(**d, tile_t=16, tile_u=8)
     with pytest.raises(ValueError, match="saved"):
         rj.rnnt_joint_loss_bwd(**d, saved=small)
+
+
+# ------------------------------------------------------------------ vocabulary parts
+
+@pytest.mark.parametrize("tile_v", [128, 256, 384])
+def test_vocabulary_parts_short(tile_v):
+    """The tiled backward in vocabulary parts of tile_v columns (V = 512: four,
+    two, or a part of 384 and one of 128): every output against the oracle."""
+    inp = make_config("short")
+    print(f"[vocabulary parts short tiles=(64, 64, {tile_v})]", flush=True)
+    g = run_gpu(inp, 64, 64, tile_v)
+    assert g["status"] == 0
+    _compare_all(inp, g, _oracle_full(inp))
+
+
+@pytest.mark.parametrize("dtype,H", [("fp32", 48), ("bf16", 64), ("bf16", 640)])
+def test_vocabulary_parts_ragged(dtype, H):
+    """V = 200 in parts of 128 (a last part of 72 columns, not a multiple of
+    any kernel's vocabulary step), ragged lengths and signed cost weights;
+    H = 64 bf16 uses the 64-column joint step, H = 640 the 128-column one."""
+    inp = make_inputs(4, 37, 11, H, 200, dtype=dtype, sigma=0.3, seed=71, t_range=(1, 37),
+                      u_range=(0, 11))
+    gcs = [1.0, -0.5, 2.0, 0.25]
+    ref = _oracle_full(inp, grad_costs=gcs)
+    for tiles in [(16, 8, 128), (32, 0, 128)]:
+        print(f"[vocabulary parts ragged {dtype} H={H} tiles={tiles}]", flush=True)
+        g = run_gpu(inp, *tiles, grad_costs=gcs)
+        assert g["status"] == 0
+        _compare_all(inp, g, ref)
