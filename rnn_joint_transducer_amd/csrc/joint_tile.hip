@@ -533,6 +533,40 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   }
   float mrow = -kInf, srow = 0.f;
 
+  // bias of a vocabulary step's columns, loaded one step ahead and kept
+  // unconverted until the step starts: its wait then comes long after the
+  // load and never covers a slice copy issued after it
+  T bnx[NBLK];
+  auto load_bias = [&](int vt) {
+#pragma unroll
+    for (int blk = 0; blk < NBLK; ++blk) {
+      const int col = vt + blk * 32 + lc;
+      bnx[blk] = bias[(EXACT || col < V) ? col : V - 1];
+    }
+  };
+  load_bias(vt_begin * VT);
+
+  // B-fragment reads: row lc of each 32-row block; hidden chunk c of that
+  // row is stored at slot c ^ (lc & 15).  bf16: a fragment is one 16-byte
+  // chunk (2*kk + kh); fp32: two chunks (4*kk + 2*kh, +1), each at its own
+  // swizzled slot
+  const int xm = lc & 15;
+  auto bfrag = [&](const char* slice, int blk, int kk) {
+    const char* rb = slice + lc * C::ROWB + blk * 32 * C::ROWB;
+    Frag8<T> f;
+    if constexpr (kBf16) {
+      f.v = *reinterpret_cast<const u32x4*>(rb + (((2 * kk + kh) ^ xm) << 4));
+    } else {
+      f.lo = *reinterpret_cast<const f32x4*>(rb + (((4 * kk + 2 * kh) ^ xm) << 4));
+      f.hi = *reinterpret_cast<const f32x4*>(rb + (((4 * kk + 2 * kh + 1) ^ xm) << 4));
+    }
+    return f;
+  };
+  // fragments of the current k-step; after the first slice of the item
+  // they were read by the previous slice (below)
+  Frag8<T> bcur[NBLK];
+  bool have_b = false;
+
   int s = 0;
   for (int vti = vt_begin; vti < vt_end; ++vti) {
     const int vt = vti * VT;
@@ -541,16 +575,15 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     bool cvalid[NBLK];
 #pragma unroll
     for (int blk = 0; blk < NBLK; ++blk) {
-      const int col = vt + blk * 32 + lc;
-      cvalid[blk] = EXACT || col < V;
-      const float bc = cvalid[blk] ? ElemTraits<T>::to_f32(bias[col]) : 0.f;
+      cvalid[blk] = EXACT || vt + blk * 32 + lc < V;
+      const float bc = cvalid[blk] ? ElemTraits<T>::to_f32(bnx[blk]) : 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[blk][r] = bc;
     }
+    if (vti + 1 < vt_end) load_bias(vt + VT);
+    // the bias is consumed before this step's first slice copy is issued
+    __builtin_amdgcn_sched_barrier(0);
 
-    // B-fragment reads: row lc of each 32-row block; hidden chunk c of that
-    // row is stored at slot c ^ (lc & 15)
-    const int xm = lc & 15;
 #pragma unroll
     for (int kc = 0; kc < KC_MAX; ++kc) {
       if (EXACT || kc < nkc) {
@@ -559,54 +592,51 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
         const int ns = s + 1;
         const int nvt = has_next ? (vt_begin + ns / nkc) * VT : next_vb * VT;
         const int nkc0 = has_next ? (ns % nkc) * C::BK : 0;
+        const char* src = par ? Ws1 : Ws0;
+        char* nxt = par ? Ws0 : Ws1;
         // one stage: start the copy of the next slice into `nxt`, run the
-        // MFMAs of this slice from `src` (B fragments one k-step ahead)
-        auto stage = [&](const char* src, char* nxt) {
-          if (has_next || cross) dma_slice<T, NBLK, EXACT>(Wt, H, V, nvt, nkc0, voff, nxt);
-          const char* wrow = src + lc * C::ROWB;
-          // bf16: a fragment is one 16-byte chunk (2*kk + kh); fp32: two
-          // chunks (4*kk + 2*kh, +1), each at its own swizzled slot
-          auto bfrag = [&](int blk, int kk) {
-            const char* rb = wrow + blk * 32 * C::ROWB;
-            Frag8<T> f;
-            if constexpr (kBf16) {
-              f.v = *reinterpret_cast<const u32x4*>(rb + (((2 * kk + kh) ^ xm) << 4));
-            } else {
-              f.lo = *reinterpret_cast<const f32x4*>(rb + (((4 * kk + 2 * kh) ^ xm) << 4));
-              f.hi = *reinterpret_cast<const f32x4*>(rb + (((4 * kk + 2 * kh + 1) ^ xm) << 4));
-            }
-            return f;
-          };
-          Frag8<T> bcur[NBLK], bnxt[NBLK];
+        // MFMAs of this slice from `src` with the B fragments one k-step
+        // ahead.  The slice barrier sits before the last k-step's MFMAs:
+        // once every wave's reads of `src` are done and its part of `nxt`
+        // has landed, the next slice's first fragments load while those
+        // MFMAs run.
+        if (has_next || cross) dma_slice<T, NBLK, EXACT>(Wt, H, V, nvt, nkc0, voff, nxt);
+        if (!have_b) {
 #pragma unroll
-          for (int blk = 0; blk < NBLK; ++blk) bcur[blk] = bfrag(blk, 0);
+          for (int blk = 0; blk < NBLK; ++blk) bcur[blk] = bfrag(src, blk, 0);
+        }
+        Frag8<T> bnxt[NBLK];
 #pragma unroll
-          for (int kk = 0; kk < C::KK; ++kk) {
-            const int ks = kc * C::KK + kk;
-            const bool live = ks < KS && (EXACT || ks < nks);
-            const bool nlive = kk + 1 < C::KK && ks + 1 < KS && (EXACT || ks + 1 < nks);
+        for (int kk = 0; kk < C::KK; ++kk) {
+          const int ks = kc * C::KK + kk;
+          const bool live = ks < KS && (EXACT || ks < nks);
+          if (kk + 1 < C::KK) {
+            const bool nlive = ks + 1 < KS && (EXACT || ks + 1 < nks);
             if (nlive) {
 #pragma unroll
-              for (int blk = 0; blk < NBLK; ++blk) bnxt[blk] = bfrag(blk, kk + 1);
+              for (int blk = 0; blk < NBLK; ++blk) bnxt[blk] = bfrag(src, blk, kk + 1);
             }
-            // keep the reads for k-step kk+1 issued ahead of this k-step's MFMAs
-            __builtin_amdgcn_sched_barrier(0);
-            if (live) {
+          } else {
+            wait_lgkm0();  // this wave's reads of `src` are done
+            wait_vmem();   // and its part of `nxt` has landed
+            __syncthreads();
+            if (has_next) {
 #pragma unroll
-              for (int blk = 0; blk < NBLK; ++blk)
-                mma_step(acc[blk], hA[ks < KS ? ks : 0], bcur[blk]);
+              for (int blk = 0; blk < NBLK; ++blk) bnxt[blk] = bfrag(nxt, blk, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int blk = 0; blk < NBLK; ++blk) bcur[blk] = bnxt[blk];
           }
-        };
-        if (par == 0)
-          stage(Ws0, Ws1);
-        else
-          stage(Ws1, Ws0);
-        wait_vmem();
-        __syncthreads();
+          // keep the reads for the next k-step issued ahead of this one's MFMAs
+          __builtin_amdgcn_sched_barrier(0);
+          if (live) {
+#pragma unroll
+            for (int blk = 0; blk < NBLK; ++blk)
+              mma_step(acc[blk], hA[ks < KS ? ks : 0], bcur[blk]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int blk = 0; blk < NBLK; ++blk) bcur[blk] = bnxt[blk];
+        }
+        have_b = has_next;
         ++s;
         par ^= 1;
       }
