@@ -39,10 +39,12 @@ MFMA_KERNELS = ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
 PROJ_KERNELS = ("proj_fwd", "proj_dx", "proj_dw")
 # Tiled defaults: medium takes the lowest-memory tiling within 95 % of the
 # best tiled throughput of a full tile sweep (`--sweep`); medium_lv keeps its
-# configured vocabulary parts of 256 columns and long its configured 64 x 64
-# chunks (over the whole vocabulary: the long configuration fixes no tile_v).
+# configured vocabulary parts of 256 columns and takes the same choice among
+# the tilings with those parts (one chunk of all frames and label positions);
+# long keeps its configured 64 x 64 chunks (over the whole vocabulary: the
+# long configuration fixes no tile_v).
 DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (128, 0, 0),
-                 "medium_lv": (32, 0, 256), "long": (64, 64, 0)}
+                 "medium_lv": (0, 128, 256), "long": (64, 64, 0)}
 
 
 def parse():
