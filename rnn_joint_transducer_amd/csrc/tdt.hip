@@ -75,52 +75,96 @@ __device__ __forceinline__ float bdur(const TdtArgs& a, int j) {
 
 // ------------------------------------------------------------ duration head
 //
-// One workgroup per (b, t), one thread per cell u; W_dur (float32) and the
-// frame's e^{2 enc} row in LDS.
+// One workgroup per (b, t); wave w takes the cells u = w, w + 4, ...; the 64
+// lanes of a wave split the hidden units (lane l: l, l + 64, ...), so each
+// e^{2 pred} row is read in coalesced 256-byte pieces, and the K partial
+// sums of the lanes meet in a butterfly.  W_dur (float32, [K][H]) and the
+// frame's e^{2 enc} row are in LDS.
 __global__ __launch_bounds__(256) void dur_head_kernel(TdtArgs a) {
-  extern __shared__ float sm[];  // W_dur [H][K], then the e^{2 enc} row [H]
+  extern __shared__ float sm[];  // W_dur [K][H], then the e^{2 enc} row [H]
   const Dims d = a.d;
   const int b = blockIdx.y, t = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   if (t >= Tl) return;  // uniform
   const int H = d.H, K = a.K;
   float* w = sm;
   float* er = sm + H * K;
   const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
-  for (int i = tid; i < H * K; i += 256) w[i] = wdur(a, i / K, i % K);
+  for (int i = tid; i < H * K; i += 256) w[(i % K) * H + i / K] = wdur(a, i / K, i % K);
   for (int k = tid; k < H; k += 256) er[k] = a.Eexp[((size_t)b * d.T + t) * H + k];
   __syncthreads();
-  for (int u = tid; u <= Ul; u += 256) {
+  for (int u = wv; u <= Ul; u += 4) {
     float z[kTdtMaxK];
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j) z[j] = j < K ? bdur(a, j) : 0.f;
+    for (int j = 0; j < kTdtMaxK; ++j) z[j] = 0.f;
     const float* pr = a.Pexp + ((size_t)b * d.U1 + u) * H;
-    for (int k = 0; k < H; ++k) {
+    for (int k = lane; k < H; k += 64) {
       const float h = h_round(a, use_ep ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + er[k] * pr[k])
                                         : h_of(a, b, t, u, k, false));
 #pragma unroll
       for (int j = 0; j < kTdtMaxK; ++j)
-        if (j < K) z[j] = fmaf(h, w[k * K + j], z[j]);
+        if (j < K) z[j] = fmaf(h, w[j * H + k], z[j]);
     }
-    float m = -__builtin_inff();
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j)
-      if (j < K) m = fmaxf(m, z[j]);
-    float s = 0.f;
+    for (int off = 32; off >= 1; off >>= 1)
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j)
-      if (j < K) s += __expf(z[j] - m);
-    const float lse = m + __logf(s);
-    float* ld = a.LD + skew_idx(d, b, t, u) * K;
+      for (int j = 0; j < kTdtMaxK; ++j)
+        if (j < K) z[j] += __shfl_xor(z[j], off);
+    if (lane == 0) {
+      float m = -__builtin_inff();
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j)
-      if (j < K) ld[j] = z[j] - lse;
+      for (int j = 0; j < kTdtMaxK; ++j)
+        if (j < K) {
+          z[j] += bdur(a, j);
+          m = fmaxf(m, z[j]);
+        }
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j)
+        if (j < K) s += __expf(z[j] - m);
+      const float lse = m + __logf(s);
+      float* ld = a.LD + skew_idx(d, b, t, u) * K;
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j)
+        if (j < K) ld[j] = z[j] - lse;
+    }
   }
 }
 
 // ------------------------------------------------------------ lattice
 //
 // blockIdx.y == 0: alpha, == 1: beta; thread u owns label position u.
+//
+// A cell's value is the log of a sum over up to 2K incoming (alpha) or
+// outgoing (beta) steps.  It is formed as the largest term, in float64, plus
+// the natural log of the sum of exp(term - largest) taken in float32: every
+// difference is <= 0 and the sum lies in [1, 2K], so the float32 part adds a
+// few 1e-8 of absolute error per cell to a float64 state (no difference is
+// rounded before it is taken).  A NaN term makes the cell NaN.
+//
+// The step weights a diagonal needs (float32 LB, LE, LD of the source cells)
+// do not depend on the recursion: each lane loads the next diagonal's while
+// the current one is computed.  The loads are a fixed set of kTdtMaxK per
+// kind (unused durations read a valid cell and are masked), so the wait
+// before their use never has to cover the loads issued after them.
+// (absent steps hold -inf)
+__device__ __forceinline__ double lse_terms(const double (&x)[2 * kTdtMaxK]) {
+  double m = kNegInfD;
+  bool nan = false;
+#pragma unroll
+  for (int i = 0; i < 2 * kTdtMaxK; ++i) {
+    nan |= x[i] != x[i];
+    m = x[i] > m ? x[i] : m;
+  }
+  if (nan) return __builtin_nan("");
+  if (m == kNegInfD) return kNegInfD;
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 2 * kTdtMaxK; ++i) sum += exp2_fast((float)(x[i] - m) * kLog2e);
+  return m + (double)(__builtin_amdgcn_logf(sum) * kLn2);
+}
+
 __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
   __shared__ double ring[kRing][513];
   const Dims d = a.d;
@@ -141,11 +185,41 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
   __syncthreads();
   const bool lane_on = u <= Ul;
   const int nd = Tl + Ul;  // diagonals 0 .. Tl-1+Ul
-  auto LBv = [&](int t, int uu) { return (double)a.LB[skew_idx(d, b, t, uu)]; };
-  auto LEv = [&](int t, int uu) { return (double)a.LE[skew_idx(d, b, t, uu)]; };
-  auto LDv = [&](int t, int uu, int j) { return (double)a.LD[skew_idx(d, b, t, uu) * K + j]; };
+  int dur[kTdtMaxK];
+#pragma unroll
+  for (int j = 0; j < kTdtMaxK; ++j) dur[j] = a.dur[j < K ? j : K - 1];
+  const size_t base = (size_t)b * d.DG * d.U1;
+  // cell (t, uu) of this utterance, t + uu <= DG - 1 and uu <= U1 - 1
+  auto idx = [&](int t, int uu) { return base + (size_t)(t + uu) * d.U1 + uu; };
   if (fwd) {
+    // weights of the cell this lane computes on diagonal k: blank from
+    // (t - d_j, u), label from (t - d_j, u - 1); invalid sources read (0, 0)
+    float wlb[kTdtMaxK], wlbd[kTdtMaxK], wle[kTdtMaxK], wled[kTdtMaxK];
+    auto load_w = [&](int k) {
+      const int t = k - u;
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j) {
+        const int s = t - dur[j];
+        const bool okb = lane_on && t < Tl && s >= 0;
+        const bool oke = okb && u >= 1;
+        const size_t ib = okb ? idx(s, u) : base, ie = oke ? idx(s, u - 1) : base;
+        wlb[j] = a.LB[ib];
+        wlbd[j] = a.LD[ib * K + (j < K ? j : 0)];
+        wle[j] = a.LE[ie];
+        wled[j] = a.LD[ie * K + (j < K ? j : 0)];
+      }
+    };
+    load_w(0);
     for (int k = 0; k < nd; ++k) {
+      float clb[kTdtMaxK], clbd[kTdtMaxK], cle[kTdtMaxK], cled[kTdtMaxK];
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j) {
+        clb[j] = wlb[j];
+        clbd[j] = wlbd[j];
+        cle[j] = wle[j];
+        cled[j] = wled[j];
+      }
+      if (k + 1 < nd) load_w(k + 1);
       const int t = k - u;
       const bool on = lane_on && t >= 0 && t < Tl;
       double v = kNegInfD;
@@ -153,46 +227,80 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
         if (k == 0) {
           v = 0.0;
         } else {
-          for (int j = 0; j < K; ++j) {
-            const int dj = a.dur[j], s = t - dj;
-            if (s < 0) continue;
-            if (dj >= 1)  // blank (s,u) -> (t,u), on diagonal k - dj
-              v = lae(v, ring[(k - dj) % kRing][u] + LBv(s, u) + LDv(s, u, j));
-            if (u >= 1)   // label (s,u-1) -> (t,u), on diagonal k - dj - 1
-              v = lae(v, ring[(k - dj - 1) % kRing][u - 1] + LEv(s, u - 1) + LDv(s, u - 1, j));
+          double x[2 * kTdtMaxK];
+#pragma unroll
+          for (int j = 0; j < kTdtMaxK; ++j) {
+            const int dj = dur[j], s = t - dj;
+            const bool ok = j < K && s >= 0;
+            // blank (s,u) -> (t,u), on diagonal k - dj
+            x[2 * j] = ok && dj >= 1 ? ring[(k - dj) % kRing][u] + ((double)clb[j] + (double)clbd[j])
+                                     : kNegInfD;
+            // label (s,u-1) -> (t,u), on diagonal k - dj - 1
+            x[2 * j + 1] = ok && u >= 1
+                               ? ring[(k - dj - 1) % kRing][u - 1] + ((double)cle[j] + (double)cled[j])
+                               : kNegInfD;
           }
+          v = lse_terms(x);
         }
-        a.alpha[skew_idx(d, b, t, u)] = v;
+        a.alpha[idx(t, u)] = v;
       }
       ring[k % kRing][u] = on ? v : kNegInfD;
       __syncthreads();
     }
     if (u == Ul) {  // the final blank lands exactly on frame T'
-      double lp = kNegInfD;
-      for (int j = 0; j < K; ++j) {
-        const int dj = a.dur[j], s = Tl - dj;
-        if (dj >= 1 && s >= 0) lp = lae(lp, a.alpha[skew_idx(d, b, s, Ul)] + LBv(s, Ul) + LDv(s, Ul, j));
+      double x[2 * kTdtMaxK];
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j) {
+        const int dj = dur[j], s = Tl - dj;
+        x[2 * j] = j < K && dj >= 1 && s >= 0
+                       ? a.alpha[idx(s, Ul)] + ((double)a.LB[idx(s, Ul)] + (double)a.LD[idx(s, Ul) * K + j])
+                       : kNegInfD;
+        x[2 * j + 1] = kNegInfD;
       }
+      const double lp = lse_terms(x);
       a.logP[b] = lp;
       a.costs[b] = (float)(-lp);
     }
   } else {
+    // the weights of a cell's outgoing steps are its own LB, LE, LD
+    float wlb = 0.f, wle = 0.f, wld[kTdtMaxK];
+    auto load_w = [&](int k) {
+      const int t = k - u;
+      const bool ok = lane_on && t >= 0 && t < Tl;
+      const size_t i = ok ? idx(t, u) : base;
+      wlb = a.LB[i];
+      wle = a.LE[i];
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j) wld[j] = a.LD[i * K + (j < K ? j : 0)];
+    };
+    load_w(nd - 1);
     for (int k = nd - 1; k >= 0; --k) {
+      const float clb = wlb, cle = wle;
+      float cld[kTdtMaxK];
+#pragma unroll
+      for (int j = 0; j < kTdtMaxK; ++j) cld[j] = wld[j];
+      if (k > 0) load_w(k - 1);
       const int t = k - u;
       const bool on = lane_on && t >= 0 && t < Tl;
       double v = kNegInfD;
       if (on) {
-        const double lb = LBv(t, u), le = u < Ul ? LEv(t, u) : 0.0;
-        for (int j = 0; j < K; ++j) {
-          const int dj = a.dur[j];
-          const double ldj = LDv(t, u, j);
-          if (dj >= 1) {
-            if (t + dj == Tl && u == Ul) v = lae(v, lb + ldj);
-            else if (t + dj < Tl) v = lae(v, lb + ldj + ring[(k + dj) % kRing][u]);
+        const double lb = clb, le = u < Ul ? (double)cle : 0.0;
+        double x[2 * kTdtMaxK];
+#pragma unroll
+        for (int j = 0; j < kTdtMaxK; ++j) {
+          const int dj = dur[j];
+          const double ldj = cld[j];
+          double xb = kNegInfD, xe = kNegInfD;
+          if (j < K && dj >= 1) {
+            if (t + dj == Tl && u == Ul) xb = lb + ldj;
+            else if (t + dj < Tl) xb = lb + ldj + ring[(k + dj) % kRing][u];
           }
-          if (u < Ul && t + dj < Tl) v = lae(v, le + ldj + ring[(k + dj + 1) % kRing][u + 1]);
+          if (j < K && u < Ul && t + dj < Tl) xe = le + ldj + ring[(k + dj + 1) % kRing][u + 1];
+          x[2 * j] = xb;
+          x[2 * j + 1] = xe;
         }
-        a.beta[skew_idx(d, b, t, u)] = v;
+        v = lse_terms(x);
+        a.beta[idx(t, u)] = v;
       }
       ring[k % kRing][u] = on ? v : kNegInfD;
       __syncthreads();
@@ -295,8 +403,11 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
     for (int i = 0; i < kHPer; ++i) dw[i][j] = 0.f;
   }
   float acc[kHPer] = {0.f, 0.f, 0.f};  // mode 1: the d_pred row
+  // (unrolled so that several cells' loads are in flight together)
+#pragma unroll 4
   for (int t = t_lo; t < t_hi; ++t) {
     float ae[kHPer] = {0.f, 0.f, 0.f};  // mode 0: this frame's d_enc row
+#pragma unroll 4
     for (int u = u_lo; u <= u_hi; ++u) {
       const size_t ix = skew_idx(d, b, t, u);
       float z[kTdtMaxK];
