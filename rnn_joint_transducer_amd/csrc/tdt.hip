@@ -14,10 +14,10 @@
 //                        (the token head's backward reads them in place of
 //                        alpha / beta) and the duration-logit gradient
 //                        dzd(t,u,k) = gc ((gB + gE) q_k - (gB_k + gE_k))
-//   dur_bwd_kernel       the duration head's share of d_enc (over a block of
-//                        frames) or d_pred (over one label position):
-//                        (1 - h^2) (W_dur dzd) summed over the lattice, plus
-//                        d_W_dur = sum h dzd^T and d_b_dur = sum dzd.
+//   dur_bwd_kernel       the duration head's share of d_enc and d_pred,
+//                        (1 - h^2) (W_dur dzd) summed over label positions
+//                        and over frames, from one pass over blocks of
+//                        frames, plus d_W_dur = sum h dzd^T, d_b_dur = sum dzd.
 // The lattice runs in float64 with one anti-diagonal per step: every
 // predecessor of a cell lies on one of the dmax + 1 previous diagonals, which
 // a ring of diagonals in LDS holds.
@@ -360,110 +360,117 @@ __global__ __launch_bounds__(256) void tdt_post_kernel(TdtArgs a) {
 
 // ------------------------------------------------------------ duration head backward
 //
-// mode 0: one workgroup per (b, block of kFrames frames): the frames' d_enc
-// rows and the block's share of d_W_dur, d_b_dur; mode 1: one workgroup per
-// (b, u): the d_pred row.  Threads over hidden units k.
+// One workgroup per (b, block of kFrames frames); thread k0 owns the hidden
+// units k0, k0 + 256, k0 + 512 (H <= 768), with those units' W_dur entries
+// and the block's e^{2 enc} values in registers.  The duration-logit
+// gradients of the block go through LDS in chunks of kUChunk label
+// positions.  Per cell and unit, h is formed once and
+//   dp = (1 - h^2) sum_j W_dur[k][j] dzd(t,u,j)
+// is summed over the block's frames into the d_pred row of u (one float32
+// atomic per unit and label position) and over the label positions into
+// the frames' d_enc rows (atomics at the end); d_W_dur += h dzd and
+// d_b_dur += dzd are summed over the block's cells.
 constexpr int kFrames = 16;
 constexpr int kHPer = 3;  // hidden units per thread (H <= 768)
+constexpr int kUChunk = 32;
 
-template <int MODE>
 __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
+  __shared__ float zs[kUChunk][kFrames][kTdtMaxK];
   const Dims d = a.d;
   const int b = blockIdx.y, tid = threadIdx.x, K = a.K;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   const int H = d.H;
   const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
-  int t_lo, t_hi, u_lo, u_hi;
-  if (MODE == 0) {
-    t_lo = blockIdx.x * kFrames;
-    t_hi = min(t_lo + kFrames, Tl);
-    u_lo = 0;
-    u_hi = Ul;
-    if (t_lo >= Tl) return;
-  } else {
-    u_lo = u_hi = blockIdx.x;
-    t_lo = 0;
-    t_hi = Tl;
-    if (u_lo > Ul || Tl == 0) return;
-  }
-  float w[kHPer][kTdtMaxK];
+  const int t_lo = blockIdx.x * kFrames;
+  if (t_lo >= Tl) return;  // uniform
+  const int nt = min(kFrames, Tl - t_lo);
+  float w[kHPer][kTdtMaxK], dw[kHPer][kTdtMaxK], db[kTdtMaxK];
+  float e[kFrames][kHPer], ae[kFrames][kHPer];
 #pragma unroll
-  for (int i = 0; i < kHPer; ++i)
+  for (int i = 0; i < kHPer; ++i) {
+    const int k = tid + 256 * i;
 #pragma unroll
     for (int j = 0; j < kTdtMaxK; ++j) {
-      const int k = tid + 256 * i;
       w[i][j] = (k < H && j < K) ? wdur(a, k, j) : 0.f;
+      dw[i][j] = 0.f;
     }
-  float dw[kHPer][kTdtMaxK];
-  float db[kTdtMaxK];
 #pragma unroll
-  for (int j = 0; j < kTdtMaxK; ++j) {
-    db[j] = 0.f;
-#pragma unroll
-    for (int i = 0; i < kHPer; ++i) dw[i][j] = 0.f;
+    for (int q = 0; q < kFrames; ++q) {
+      const int t = t_lo + (q < nt ? q : 0);
+      e[q][i] = (use_ep && k < H) ? a.Eexp[((size_t)b * d.T + t) * H + k] : 0.f;
+      ae[q][i] = 0.f;
+    }
   }
-  float acc[kHPer] = {0.f, 0.f, 0.f};  // mode 1: the d_pred row
-  // (unrolled so that several cells' loads are in flight together)
-#pragma unroll 4
-  for (int t = t_lo; t < t_hi; ++t) {
-    float ae[kHPer] = {0.f, 0.f, 0.f};  // mode 0: this frame's d_enc row
-#pragma unroll 4
-    for (int u = u_lo; u <= u_hi; ++u) {
-      const size_t ix = skew_idx(d, b, t, u);
-      float z[kTdtMaxK];
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j) z[j] = j < K ? ld_const(a.dzd + ix * K + j) : 0.f;
-      if (MODE == 0) {
-#pragma unroll
-        for (int j = 0; j < kTdtMaxK; ++j) db[j] += z[j];
-      }
+  for (int j = 0; j < kTdtMaxK; ++j) db[j] = 0.f;
+
+  for (int u0 = 0; u0 <= Ul; u0 += kUChunk) {
+    const int nu = min(kUChunk, Ul + 1 - u0);
+    __syncthreads();  // the previous chunk's reads are done
+    for (int i = tid; i < kUChunk * kFrames * kTdtMaxK; i += 256) {
+      const int j = i % kTdtMaxK, q = (i / kTdtMaxK) % kFrames, uu = i / (kTdtMaxK * kFrames);
+      float v = 0.f;
+      if (uu < nu && q < nt && j < K) v = a.dzd[skew_idx(d, b, t_lo + q, u0 + uu) * K + j];
+      zs[uu][q][j] = v;
+    }
+    __syncthreads();
+    for (int uu = 0; uu < nu; ++uu) {
+      const int u = u0 + uu;
+      float p[kHPer], ap[kHPer];
 #pragma unroll
       for (int i = 0; i < kHPer; ++i) {
         const int k = tid + 256 * i;
-        if (k >= H) continue;
-        const float h = h_of(a, b, t, u, k, use_ep);
-        float s = 0.f;
+        p[i] = (use_ep && k < H) ? a.Pexp[((size_t)b * d.U1 + u) * H + k] : 0.f;
+        ap[i] = 0.f;
+      }
 #pragma unroll
-        for (int j = 0; j < kTdtMaxK; ++j) s = fmaf(w[i][j], z[j], s);
-        const float dp = (1.0f - h * h) * s;
-        if (MODE == 0) {
-          ae[i] += dp;
+      for (int q = 0; q < kFrames; ++q) {
+        if (q >= nt) continue;  // uniform
+        float z[kTdtMaxK];
+#pragma unroll
+        for (int j = 0; j < kTdtMaxK; ++j) {
+          z[j] = zs[uu][q][j];
+          db[j] += tid == 0 ? z[j] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kHPer; ++i) {
+          const int k = tid + 256 * i;
+          if (k >= H) continue;
+          const float h = use_ep ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e[q][i] * p[i])
+                                 : h_of(a, b, t_lo + q, u, k, false);
+          float sacc = 0.f;
+#pragma unroll
+          for (int j = 0; j < kTdtMaxK; ++j) sacc = fmaf(w[i][j], z[j], sacc);
+          const float dp = (1.0f - h * h) * sacc;
+          ae[q][i] += dp;
+          ap[i] += dp;
           const float hr = h_round(a, h);
 #pragma unroll
           for (int j = 0; j < kTdtMaxK; ++j) dw[i][j] = fmaf(hr, z[j], dw[i][j]);
-        } else {
-          acc[i] += dp;
         }
       }
-    }
-    if (MODE == 0) {
 #pragma unroll
       for (int i = 0; i < kHPer; ++i) {
         const int k = tid + 256 * i;
-        if (k < H) atomicAdd(&a.d_enc[((size_t)b * d.T + t) * H + k], ae[i]);
+        if (k < H) atomicAdd(&a.d_pred[((size_t)b * d.U1 + u) * H + k], ap[i]);
       }
     }
   }
-  if (MODE == 0) {
 #pragma unroll
-    for (int i = 0; i < kHPer; ++i) {
-      const int k = tid + 256 * i;
-      if (k >= H) continue;
+  for (int i = 0; i < kHPer; ++i) {
+    const int k = tid + 256 * i;
+    if (k >= H) continue;
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j)
-        if (j < K) atomicAdd(&a.d_Wd[(size_t)k * K + j], dw[i][j]);
-    }
-    if (tid == 0) {
+    for (int q = 0; q < kFrames; ++q)
+      if (q < nt) atomicAdd(&a.d_enc[((size_t)b * d.T + t_lo + q) * H + k], ae[q][i]);
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j)
-        if (j < K) atomicAdd(&a.d_bd[j], db[j]);
-    }
-  } else {
+    for (int j = 0; j < kTdtMaxK; ++j)
+      if (j < K) atomicAdd(&a.d_Wd[(size_t)k * K + j], dw[i][j]);
+  }
+  if (tid == 0) {
 #pragma unroll
-    for (int i = 0; i < kHPer; ++i) {
-      const int k = tid + 256 * i;
-      if (k < H) atomicAdd(&a.d_pred[((size_t)b * d.U1 + u_lo) * H + k], acc[i]);
-    }
+    for (int j = 0; j < kTdtMaxK; ++j)
+      if (j < K) atomicAdd(&a.d_bd[j], db[j]);
   }
 }
 
@@ -486,9 +493,8 @@ hipError_t launch_tdt_post(const TdtArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tdt_dur_bwd(const TdtArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(dur_bwd_kernel<0>, dim3((a.d.T + kFrames - 1) / kFrames, a.d.B), dim3(256),
-                     0, st, a);
-  hipLaunchKernelGGL(dur_bwd_kernel<1>, dim3(a.d.U1, a.d.B), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(dur_bwd_kernel, dim3((a.d.T + kFrames - 1) / kFrames, a.d.B), dim3(256), 0,
+                     st, a);
   return hipGetLastError();
 }
 
