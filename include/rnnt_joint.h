@@ -55,7 +55,8 @@
  *     ignores tile_v.
  *   - Limits (else RNNTJ_ERR_UNSUPPORTED): H a multiple of 16 with
  *     16 <= H <= 768 for bf16 and H <= 256 for fp32; V a multiple of 8,
- *     8 <= V <= 262144; U + 1 <= 512; B <= 8191; T <= 65520.
+ *     8 <= V <= 262144; U + 1 <= 1024 (512 for the pruned and the
+ *     token-and-duration entry points); B <= 8191; T <= 65520.
  *   - Host-side argument errors (null pointers, bad shapes, blank outside
  *     [0,V), unsupported tiles, workspace too small) return a nonzero code
  *     before anything is enqueued; outputs are untouched.

@@ -80,7 +80,7 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   const bool bf16 = dtype == RNNTJ_BF16;
   if (H % 16 != 0 || H > (bf16 ? 768 : 256)) return RNNTJ_ERR_UNSUPPORTED;
   if (V % 8 != 0 || V < 8 || V > kMaxV) return RNNTJ_ERR_UNSUPPORTED;
-  if (U + 1 > 512) return RNNTJ_ERR_UNSUPPORTED;
+  if (U + 1 > kMaxU1) return RNNTJ_ERR_UNSUPPORTED;
   if (B > 8191 || T > 65520) return RNNTJ_ERR_UNSUPPORTED;  // packed tile coordinates
   if (tile_t % kTileT != 0 || tile_u % kTileU != 0) return RNNTJ_ERR_UNSUPPORTED;
   // tile_v: vocabulary columns of one part of the tiled backward (and an
@@ -116,10 +116,10 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_lse = o;    o = align_up(o + 4 * cells);
   q.o_lb = o;     o = align_up(o + 4 * cells);
   q.o_le = o;     o = align_up(o + 4 * cells);
-  // alpha / beta carry a trash area of 512 float64 past the cells (slots of
-  // the lattice sweep that fall outside the lattice are stored there)
-  q.o_alpha = o;  o = align_up(o + 8 * (cells + 512));
-  q.o_beta = o;   o = align_up(o + 8 * (cells + 512));
+  // alpha / beta carry a trash area of kMaxU1 float64 past the cells (slots
+  // of the lattice sweep that fall outside the lattice are stored there)
+  q.o_alpha = o;  o = align_up(o + 8 * (cells + kMaxU1));
+  q.o_beta = o;   o = align_up(o + 8 * (cells + kMaxU1));
   q.o_E = o;      o = align_up(o + 4 * (size_t)B * T * H);
   q.o_P = o;      o = align_up(o + 4 * (size_t)B * (U + 1) * H);
   q.cap_all = B * (q.d.Tpad / kTileT) * (q.d.U1pad / kTileU);
@@ -370,12 +370,14 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   if (tdt) {
     if ((rc = check_tdt(*tdt))) return rc;
     if (criterion != RNNTJ_CRIT_SUM || S != 0) return RNNTJ_ERR_ARG;
+    if (U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
   }
   if (criterion != RNNTJ_CRIT_SUM && criterion != RNNTJ_CRIT_MAX) return RNNTJ_ERR_ARG;
   const bool pruned = S > 0;
   if (S < 0) return RNNTJ_ERR_ARG;
   if (pruned) {
-    if (criterion != RNNTJ_CRIT_SUM || p.untiled || T > kMaxPrunedT) return RNNTJ_ERR_UNSUPPORTED;
+    if (criterion != RNNTJ_CRIT_SUM || p.untiled || T > kMaxPrunedT || U + 1 > kMaxU1Short)
+      return RNNTJ_ERR_UNSUPPORTED;
     if (workspace_bytes < p.ws_pruned || !workspace) return RNNTJ_ERR_WORKSPACE;
     if (misaligned(workspace) || misaligned(simple_costs)) return RNNTJ_ERR_ARG;
   }
@@ -561,6 +563,7 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   size_t o_gB = 0, o_gE = 0, o_dzd = 0, ws_need = p.bwd_ws();
   if (tdt) {
     if ((rc = check_tdt(*tdt))) return rc;
+    if (U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
     if (!d_Wd || !d_bd || misaligned(d_Wd) || misaligned(d_bd)) return RNNTJ_ERR_ARG;
     tdt_ws(p, tdt->K, o_gB, o_gE, o_dzd, ws_need);
   }
@@ -899,7 +902,7 @@ int rnnt_joint_loss_pruned_workspace_bytes(int B, int T, int U, int H, int V, in
   Plan p;
   const int rc = make_plan(B, T, U, H, V, dtype, kTileT, kTileU, 0, &p);
   if (rc) return rc;
-  if (T > kMaxPrunedT) return RNNTJ_ERR_UNSUPPORTED;
+  if (T > kMaxPrunedT || U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
   *out = p.ws_pruned;
   return RNNTJ_OK;
 }
@@ -951,6 +954,7 @@ int rnnt_joint_loss_tdt_saved_bytes(int B, int T, int U, int H, int V, int dtype
   Plan p;
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
+  if (U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
   *out = p.saved_bytes + tdt_ld_bytes(p, K);
   return RNNTJ_OK;
 }
@@ -961,6 +965,7 @@ int rnnt_joint_loss_tdt_workspace_bytes(int B, int T, int U, int H, int V, int d
   Plan p;
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
+  if (U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
   size_t a, b, c, total;
   tdt_ws(p, K, a, b, c, total);
   *out = pass == 0 ? p.ws_fwd : total;

@@ -35,8 +35,9 @@ constexpr int kTileT = 16;
 constexpr int kTileU = 8;
 constexpr int kTileCells = kTileT * kTileU;
 constexpr int kVocabTile = 128;  // vocabulary columns per pass of one wave
-// Largest vocabulary: keeps 32-bit element offsets inside a 16-frame tile of
-// logit rows (16 x 512 rows x V) and a label + 1 inside 30 bits.
+// Largest vocabulary: keeps the 32-bit element offsets inside one 16 x 8
+// cell tile of logit rows (at most (15 x 1024 + 7) x V + V, below 2^32) and
+// a label + 1 inside 30 bits.
 constexpr int kMaxV = 262144;
 constexpr int kMaxProj = 65536;  // largest input / output width of a joint input projection
 

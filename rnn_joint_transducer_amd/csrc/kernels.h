@@ -36,13 +36,18 @@ constexpr int kErrPruneInfeasible = 16;
 // positions cu0 .. cu0+CU-1) is covered by 16 x 8 cell tiles; a tile is
 // active when it holds at least one cell t < T'_b, u <= U'_b.  The active
 // tiles of chunk c are list[c * cap + i], i < count[c], utterance by
-// utterance, each packed as b << 18 | tt << 6 | tu (tile row / column inside
-// the chunk).
-__host__ __device__ inline int tile_pack(int b, int tt, int tu) { return (b << 18) | (tt << 6) | tu; }
+// utterance, each packed into the 32 bits of an int32 entry as
+// b << 19 | tt << 7 | tu (tile row / column inside the chunk): 13 bits of
+// utterance (B <= 8191), 12 of 16-frame tile row (T <= 65520), 7 of 8-label
+// tile column (U + 1 <= 1024).
+__host__ __device__ inline int tile_pack(int b, int tt, int tu) {
+  return (int)(((uint32_t)b << 19) | ((uint32_t)tt << 7) | (uint32_t)tu);
+}
 __device__ inline void tile_unpack(int v, int& b, int& tt, int& tu) {
-  b = v >> 18;
-  tt = (v >> 6) & 0xfff;
-  tu = v & 63;
+  const uint32_t x = (uint32_t)v;
+  b = (int)(x >> 19);
+  tt = (int)((x >> 7) & 0xfffu);
+  tu = (int)(x & 127u);
 }
 // With a pruned forward's state (hdr[kHdrBand] = S > 0) only tiles holding a
 // cell of the band s_t <= u <= s_t + S - 1 (bounds [B, T]) are listed.
@@ -157,6 +162,13 @@ struct PruneArgs {
 hipError_t launch_pruning_bounds(const PruneArgs& p, hipStream_t st);
 // p[i] = v for i < n
 hipError_t launch_fill(float* p, size_t n, float v, hipStream_t st);
+
+// Largest U + 1: the lattice sweep blocks up to 16 label positions on each
+// lane of one wave (and alpha / beta carry one trash slot per position past
+// their cells); the token-and-duration and simple-joiner lattices put one
+// thread on each label position of a 512-thread workgroup.
+constexpr int kMaxU1 = 1024;
+constexpr int kMaxU1Short = 512;
 
 // Token-and-duration transducer (tdt.hip).  Up to kTdtMaxK durations, each
 // in [0, kTdtMaxDur].

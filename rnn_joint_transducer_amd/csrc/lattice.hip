@@ -307,20 +307,20 @@ __global__ __launch_bounds__(256) void lattice_kernel(const float* __restrict__ 
 // the walk crosses downwards once.  Each anti-diagonal n = t + u holds one
 // path cell, in the row u whose [t_lo(u) + u, t_hi(u) + u] contains n, so all
 // threads then write the marks at once.
-constexpr int kBtThreads = 512, kBtWords = 8192, kBtBatch = 16;
+constexpr int kBtThreads = kMaxU1, kBtWords = 8192, kBtBatch = 16;
 
 __global__ __launch_bounds__(kBtThreads) void backtrace_kernel(const int32_t* __restrict__ Teff,
                                                                const int32_t* __restrict__ Ueff,
                                                                Dims d, double* __restrict__ beta) {
   __shared__ uint32_t bits[kBtWords];
-  __shared__ int tlo[512], thi[512];
+  __shared__ int tlo[kMaxU1], thi[kMaxU1];
   __shared__ int s_t, s_u, s_more;
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int Tl = Teff[b], Ul = Ueff[b];
   if (Tl == 0) return;  // invalid utterance (uniform over the block)
   const int R = Ul + 1;  // rows u = 0..U'
   // W words (32 W frames) of a row per chunk, rows S = W | 1 words apart;
-  // R <= 512 gives W >= 15
+  // R <= kMaxU1 = 1024 gives W >= 7
   const int W = min((Tl + 31) >> 5, kBtWords / R - 1), S = W | 1;
   const int CT = W * 32;
   if (tid == 0) {
@@ -629,6 +629,14 @@ hipError_t launch_lattice(const float* LB, const float* LE, const int32_t* Teff,
     RNNTJ_LAT(6, 3)
     RNNTJ_LAT(7, 2)
     RNNTJ_LAT(8, 2)
+    RNNTJ_LAT(9, 1)
+    RNNTJ_LAT(10, 1)
+    RNNTJ_LAT(11, 1)
+    RNNTJ_LAT(12, 1)
+    RNNTJ_LAT(13, 1)
+    RNNTJ_LAT(14, 1)
+    RNNTJ_LAT(15, 1)
+    RNNTJ_LAT(16, 1)
     default:
       return hipErrorInvalidValue;
   }

@@ -79,13 +79,29 @@ def test_buffer_sizes():
     ((2, 10, 2, 60, 32, 0), 2),        # H not a multiple of 16
     ((2, 10, 2, 512, 32, 0), 2),       # fp32 H > 256
     ((2, 10, 2, 64, 30, 0), 2),        # V not a multiple of 8
-    ((2, 10, 600, 64, 32, 0), 2),      # U + 1 > 512
+    ((2, 10, 1024, 64, 32, 0), 2),     # U + 1 > 1024
     ((8192, 10, 2, 64, 32, 0), 2),     # B > 8191
     ((2, 65521, 2, 64, 32, 0), 2),     # T > 65520
     ((2, 10, 2, 64, 262152, 0), 2),    # V > 262144
 ])
 def test_shape_errors(args, code):
     assert _saved(*args)[0] == code
+
+
+def test_label_limit():
+    """U + 1 up to 1024 for the fused path; the token-and-duration and pruned
+    entry points keep U + 1 <= 512."""
+    assert _saved(2, 10, 1023, 64, 32, 0)[0] == 0
+    assert _saved(2, 10, 600, 64, 32, 0, 16, 8)[0] == 0
+    out = ctypes.c_size_t(0)
+    assert lib.rnnt_joint_loss_pruned_workspace_bytes(2, 20, 511, 64, 32, 0, ctypes.byref(out)) == 0
+    assert lib.rnnt_joint_loss_pruned_workspace_bytes(2, 20, 512, 64, 32, 0, ctypes.byref(out)) == 2
+    assert lib.rnnt_joint_loss_tdt_saved_bytes(2, 20, 511, 64, 32, 0, 16, 8, 0, 5,
+                                               ctypes.byref(out)) == 0
+    assert lib.rnnt_joint_loss_tdt_saved_bytes(2, 20, 512, 64, 32, 0, 16, 8, 0, 5,
+                                               ctypes.byref(out)) == 2
+    assert lib.rnnt_joint_loss_tdt_workspace_bytes(2, 20, 512, 64, 32, 0, 16, 8, 0, 5, 0,
+                                                   ctypes.byref(out)) == 2
 
 
 def test_tile_errors():

@@ -159,9 +159,10 @@ def test_nan_input_stays_in_its_utterance(criterion, tiles):
 
 
 @pytest.mark.parametrize("criterion", ["sum", "max"])
-@pytest.mark.parametrize("U1", [64, 65, 129, 192, 193, 256, 320, 321, 385, 448, 449, 512])
+@pytest.mark.parametrize("U1", [64, 65, 129, 192, 193, 256, 320, 321, 385, 448, 449, 512, 513,
+                                577, 640, 705, 768, 833, 896, 961, 1024])
 def test_lattice_label_blocking(U1, criterion):
-    """Every label-position blocking of the lattice sweep (1 to 8 positions
+    """Every label-position blocking of the lattice sweep (1 to 16 positions
     per lane, each with its own chunk length), at and just past each block
     boundary, with label counts up to the padded maximum: every output
     against the oracle."""
@@ -484,7 +485,7 @@ def test_max_zero_weights_closed_form_medium():
 @pytest.mark.parametrize("case", ["U_max", "V_max", "H_max_bf16", "B_max", "T_max"])
 def test_maximum_sizes(case):
     """Each size limit the library accepts, with the other sizes small enough
-    for the oracle: U + 1 = 512 (both criteria), V = 262144, H = 768 in bf16,
+    for the oracle: U + 1 = 1024 (both criteria), V = 262144, H = 768 in bf16,
     B = 8191, T = 65520.  Every output is compared.  The largest-B and
     longest-T cases weight their costs by 1e-3 and 1e-4: unweighted, d_b_out
     sums to ~1.1e4 over 8191 utterances (half an fp32 ulp there is 4.9e-4)
@@ -496,8 +497,8 @@ def test_maximum_sizes(case):
     gcs = None
     runs = [((0, 0, 0), "sum"), ((16, 8, 0), "sum")]
     if case == "U_max":
-        inp = make_inputs(2, 24, 511, 64, 40, sigma=0.2, seed=101)
-        inp.U_lens = np.array([511, 300], dtype=np.int32)
+        inp = make_inputs(2, 24, 1023, 64, 40, sigma=0.2, seed=101)
+        inp.U_lens = np.array([1023, 600], dtype=np.int32)
         runs += [((0, 0, 0), "max"), ((64, 64, 128), "max")]
     elif case == "V_max":
         inp = make_inputs(2, 5, 2, 32, 262144, sigma=0.2, seed=102)
