@@ -35,6 +35,7 @@ if ROOT not in sys.path:
 METRIC = "lattice cells/sec (B·T·U) fused joint+loss fwd+bwd"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2500.0}
 PEAK_HBM_GBS = 8000.0
+PEAK_F64_VECTOR = 78.6  # TFLOP/s: 256 CUs x 4 SIMDs x 16 lanes x 2 flops (FMA) x 2.4 GHz
 MFMA_KERNELS = ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
 PROJ_KERNELS = ("proj_fwd", "proj_dx", "proj_dw")
 # Tiled defaults: medium takes the lowest-memory tiling within 95 % of the
@@ -455,11 +456,30 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS[dt],
                 "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS[dt], "traffic": None,
                 "algorithmic_per_launch": per_launch}
+    elif dom == "pruning_bounds":
+        # float64 vector arithmetic: am = enc W_out and lm = pred W_out over the
+        # valid rows (2 H V flops per row), and the normaliser product
+        # EA EL^T of every utterance (2 V flops per valid cell)
+        rows = int(np.sum(inp.T_lens.astype(np.int64) + inp.U_lens.astype(np.int64) + 1))
+        per_launch = (2.0 * H * V * rows + 2.0 * V * valid) / launches
+        achieved = per_launch / (kd["ms_per_launch"] / 1e3) / 1e12
+        roof = {"kernel": dom, "bound": "alu", "achieved": achieved, "peak": PEAK_F64_VECTOR,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_F64_VECTOR, "traffic": None,
+                "algorithmic_per_launch": per_launch}
     else:
         # lattice: 32 B per valid cell (alpha and beta chains each read LB, LE and
-        # write one float64); grad_inplace: read + write the logits
+        # write one float64); token-and-duration lattice: the same plus the K
+        # float32 duration log-probabilities read by each chain; grad_inplace:
+        # read + write the logits
         elem = 2 if bf16 else 4
-        per_cell = 32.0 if dom == "lattice" else (2.0 * elem * V if dom == "grad_inplace" else 0.0)
+        if dom == "lattice":
+            per_cell = 32.0
+        elif dom == "tdt_lattice":
+            per_cell = 32.0 + 8.0 * len(args.tdt.split(","))
+        elif dom == "grad_inplace":
+            per_cell = 2.0 * elem * V
+        else:
+            per_cell = 0.0
         per_launch = per_cell * valid / launches
         achieved = per_launch / (kd["ms_per_launch"] / 1e3) / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
