@@ -54,7 +54,7 @@
  *     with H <= 256).  The untiled mode stores whole rows of logits and
  *     ignores tile_v.
  *   - Limits (else RNNTJ_ERR_UNSUPPORTED): H a multiple of 16 with
- *     16 <= H <= 768 for bf16 and H <= 256 for fp32; V a multiple of 8,
+ *     16 <= H <= 768; V a multiple of 8,
  *     8 <= V <= 262144; U + 1 <= 1024 (512 for the pruned and the
  *     token-and-duration entry points); B <= 8191; T <= 65520.
  *   - Host-side argument errors (null pointers, bad shapes, blank outside

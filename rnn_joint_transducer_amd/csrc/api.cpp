@@ -78,7 +78,7 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   if (dtype != RNNTJ_F32 && dtype != RNNTJ_BF16) return RNNTJ_ERR_ARG;
   if (tile_t < 0 || tile_u < 0 || tile_v < 0) return RNNTJ_ERR_ARG;
   const bool bf16 = dtype == RNNTJ_BF16;
-  if (H % 16 != 0 || H > (bf16 ? 768 : 256)) return RNNTJ_ERR_UNSUPPORTED;
+  if (H % 16 != 0 || H > 768) return RNNTJ_ERR_UNSUPPORTED;
   if (V % 8 != 0 || V < 8 || V > kMaxV) return RNNTJ_ERR_UNSUPPORTED;
   if (U + 1 > kMaxU1) return RNNTJ_ERR_UNSUPPORTED;
   if (B > 8191 || T > 65520) return RNNTJ_ERR_UNSUPPORTED;  // packed tile coordinates

@@ -236,7 +236,7 @@ __device__ __forceinline__ void band_mask(const JointArgs& a, int b, int t, int 
 // workgroups per compute unit the rows are read from global memory instead.
 template <typename T, int KS, int NBLK>
 struct EpCfg {
-  static constexpr int kMaxH = sizeof(T) == 2 ? 640 : 256;
+  static constexpr int kMaxH = sizeof(T) == 2 ? 640 : 768;
   static constexpr bool kStage = NBLK == 4 && KS * 16 <= kMaxH;
   // 16 e^{2 enc} rows then 8 e^{2 pred} rows (float32), plus one 1 KB copy
   // of slack for a partial last copy
@@ -250,6 +250,13 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   constexpr int VT = C::VT;
   constexpr bool kBf16 = C::kBf16;
   constexpr int KC_MAX = (KS * 16 + C::BK - 1) / C::BK;
+  // k-steps of h held in registers at a time.  fp32 rows above 256 hidden
+  // do not fit: there h is kept 16 k-steps (256 hidden) at a time and each
+  // part is rebuilt from the staged exponential rows when a vocabulary step
+  // reaches it (about 5 VALU per element against 256 MFMA flops)
+  constexpr int KR = (!kBf16 && KS > 16) ? 16 : KS;
+  constexpr int NCH = KS / KR;
+  static_assert(KS % KR == 0 && KR % C::KK == 0, "h parts are whole slices");
   constexpr bool kStores = (MODE == kStoreZ || MODE == kGrad) && kBf16;
   // two separately named slice buffers: the compiler then knows that the
   // copy into one does not alias the fragment reads of the other
@@ -321,19 +328,21 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   };
   // h = tanh(enc + pred) evaluated directly from the inputs (rows whose
   // e^{2x} could overflow)
-  auto build_h_direct = [&](Frag8<T>(&hA)[KS], int b, int tv, int uv, bool valid) {
+  // (k-steps c KR .. c KR + KR - 1)
+  auto build_h_direct = [&](Frag8<T>(&hA)[KR], int c, int b, int tv, int uv, bool valid) {
     const T* er = enc + ((size_t)b * d.T + tv) * H + 8 * kh;
     const T* pr = pred + ((size_t)b * d.U1 + uv) * H + 8 * kh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+    for (int j = 0; j < KR; ++j) {
+      const int ks = c * KR + j;
       if ((EXACT || ks < nks) && valid) {
         const Frag8<T> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
         float x[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) x[i] = fast_tanh(e.get(i) + p.get(i));
-        pack_frag(hA[ks], x);
+        pack_frag(hA[j], x);
       } else {
-        zero_frag(hA[ks]);
+        zero_frag(hA[j]);
       }
     }
   };
@@ -400,7 +409,9 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     pg = a.gcost ? (double)a.gcost[b] : 1.0;
   }
 
-  Frag8<T> hA[KS];
+  // h of this lane's tile row (k-steps c KR .. c KR + KR - 1 of it)
+  Frag8<T> hA[KR];
+  if constexpr (NCH == 1)
   {
     const int tt = lc >> 3, uu = lc & 7;
     const int t = t0 + 4 * w + tt, u = u0 + uu;
@@ -412,7 +423,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
       const T* hrow = static_cast<const T*>(a.hout) +
                       (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KR; ++ks) {
         if (EXACT || ks < nks) hA[ks] = load_frag(hrow + ks * 16);
         else zero_frag(hA[ks]);
       }
@@ -422,7 +433,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
         const float* er = reinterpret_cast<const float*>(Ep) + (4 * w + tt) * H + 8 * kh;
         const float* pr = reinterpret_cast<const float*>(Ep + 64 * H) + uu * H + 8 * kh;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KR; ++ks) {
           if ((EXACT || ks < nks) && valid) {
             const Frag8<float> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
             float x[8];
@@ -435,14 +446,14 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
           }
         }
       } else {
-        build_h_direct(hA, b, tv, uv, valid);
+        build_h_direct(hA, 0, b, tv, uv, valid);
       }
     } else if (use_ep) {
       // exponential rows straight from global memory
       const float* er = a.Eexp + ((size_t)b * d.T + tv) * H + 8 * kh;
       const float* pr = a.Pexp + ((size_t)b * d.U1 + uv) * H + 8 * kh;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int ks = 0; ks < KR; ++ks) {
         if ((EXACT || ks < nks) && valid) {
           const Frag8<float> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
           float x[8];
@@ -458,9 +469,63 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
         if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
       }
     } else {
-      build_h_direct(hA, b, tv, uv, valid);
+      build_h_direct(hA, 0, b, tv, uv, valid);
     }
   }
+  // h rebuilt in parts (fp32, more than 256 hidden; the exponential rows
+  // are always staged then): from the stored rows, the staged rows or the
+  // inputs
+  static_assert(NCH == 1 || EP::kStage, "parts of h are rebuilt from staged rows");
+  auto build_part = [&](int c) {
+    const int t = t0 + 4 * w + (lc >> 3), u = u0 + (lc & 7);
+    const bool valid = (t < Tl) && (u <= Ul);
+    if (h_from_mem) {
+      const T* hrow = static_cast<const T*>(a.hout) +
+                      (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        const int ks = c * KR + j;
+        if (EXACT || ks < nks) hA[j] = load_frag(hrow + ks * 16);
+        else zero_frag(hA[j]);
+      }
+    } else if (use_ep) {
+      const float* er = reinterpret_cast<const float*>(Ep) + (t - t0) * H + 8 * kh;
+      const float* pr = reinterpret_cast<const float*>(Ep + 64 * H) + (u - u0) * H + 8 * kh;
+#pragma unroll
+      for (int j = 0; j < KR; ++j) {
+        const int ks = c * KR + j;
+        if ((EXACT || ks < nks) && valid) {
+          const Frag8<float> e = load_frag(er + ks * 16), p = load_frag(pr + ks * 16);
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            x[i] = 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e.get(i) * p.get(i));
+          pack_frag(hA[j], x);
+        } else {
+          zero_frag(hA[j]);
+        }
+      }
+    } else {
+      build_h_direct(hA, c, b, valid ? t : 0, valid ? u : 0, valid);
+    }
+  };
+  // kStoreZ / kGrad: the weight-gradient GEMM reads these h rows back
+  // ([B, CT, CU, H]); every row of the tile is written (zero outside the
+  // lattice).  (Untiled forward: the h rows of the whole padded lattice,
+  // kept for the backward.)
+  const bool h_store = (MODE == kGrad || MODE == kStoreZ) && vr == 0 &&
+                       (MODE == kGrad ? a.gv0 == 0 : a.hout != nullptr);
+  // (parts of h: stored as each is built in the first vocabulary step)
+  auto store_part = [&](int c) {
+    const int t = t0 + 4 * w + (lc >> 3), u = u0 + (lc & 7);
+    T* hrow = static_cast<T*>(a.hout) +
+              (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
+#pragma unroll
+    for (int j = 0; j < KR; ++j) {
+      const int ks = c * KR + j;
+      if (EXACT || ks < nks) store_frag(hrow + ks * 16, hA[j]);
+    }
+  };
   // labels of this lane's accumulator rows: u = u0 + 4*kh + j
   int lab[4];
 #pragma unroll
@@ -497,23 +562,21 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   wait_vmem();
   __syncthreads();
   // every wave has built its h: the next item's exponential rows may load
-  if (stage_ep && item + (int)gridDim.x < n_items) {
+  // (h rebuilt in parts reads them until the item ends)
+  if (NCH == 1 && stage_ep && item + (int)gridDim.x < n_items) {
     int nb, nt0, nu0;
     item_tile(item + gridDim.x, nb, nt0, nu0);
     issue_ep(nb, nt0, nu0);
   }
-  if constexpr (MODE == kGrad || MODE == kStoreZ) {
-    // the weight-gradient GEMM reads these h rows back ([B, CT, CU, H]);
-    // every row of the tile is written (zero outside the lattice).  Issued
-    // after the barrier, so the first slice's MFMAs cover their completion
-    // instead of the barrier waiting for it.  (Untiled forward: the h rows
-    // of the whole padded lattice, kept for the backward.)
-    if (vr == 0 && (MODE == kGrad ? a.gv0 == 0 : a.hout != nullptr)) {
+  if constexpr ((MODE == kGrad || MODE == kStoreZ) && NCH == 1) {
+    // issued after the barrier, so the first slice's MFMAs cover their
+    // completion instead of the barrier waiting for it
+    if (h_store) {
       const int t = t0 + 4 * w + (lc >> 3), u = u0 + (lc & 7);
       T* hrow = static_cast<T*>(a.hout) +
                 (((size_t)b * a.CT + (t - a.ct0)) * a.CU + (u - a.cu0)) * H + 8 * kh;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+      for (int ks = 0; ks < KR; ++ks)
         if (EXACT || ks < nks) store_frag(hrow + ks * 16, hA[ks]);
     }
   }
@@ -584,8 +647,19 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
     // the bias is consumed before this step's first slice copy is issued
     __builtin_amdgcn_sched_barrier(0);
 
+    // slices in parts of h (one part unless h is rebuilt in parts); the
+    // slices of a part are unrolled, so every h fragment index is a constant
+    constexpr int KCR = KR / C::KK;
+    for (int c = 0; c < NCH; ++c) {
+    if constexpr (NCH > 1) {
+      if (!EXACT && c * KR >= nks) break;
+      build_part(c);
+      if constexpr (MODE == kGrad || MODE == kStoreZ)
+        if (h_store && vti == vt_begin) store_part(c);
+    }
 #pragma unroll
-    for (int kc = 0; kc < KC_MAX; ++kc) {
+    for (int kq = 0; kq < KCR; ++kq) {
+      const int kc = c * KCR + kq;
       if (EXACT || kc < nkc) {
         const bool has_next = (s + 1) < nstage;
         const bool cross = !has_next && next_ns > 0;  // the next item's first slice
@@ -630,7 +704,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
           if (live) {
 #pragma unroll
             for (int blk = 0; blk < NBLK; ++blk)
-              mma_step(acc[blk], hA[ks < KS ? ks : 0], bcur[blk]);
+              mma_step(acc[blk], hA[kq * C::KK + kk], bcur[blk]);
           }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -641,6 +715,7 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
         par ^= 1;
       }
     }
+    }  // parts of h
 
     // ---- epilogue for vocabulary columns vt .. vt+VT-1
     if constexpr ((MODE == kLse || MODE == kStoreZ) && NBLK == 2) {
@@ -949,6 +1024,14 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
   }
   // the next item rewrites the captures, row constants and store staging
   __syncthreads();
+  if constexpr (NCH > 1) {
+    // every wave is done with this item's exponential rows
+    if (stage_ep && item + (int)gridDim.x < n_items) {
+      int nb, nt0, nu0;
+      item_tile(item + gridDim.x, nb, nt0, nu0);
+      issue_ep(nb, nt0, nu0);
+    }
+  }
   }  // item loop
 }
 
@@ -1001,6 +1084,8 @@ static hipError_t launch_mode(const JointArgs& a, int n_items, hipStream_t st) {
     if (nks <= 4) launch_ks<T, 4, MODE>(a, n_items, st);
     else if (nks <= 8) launch_ks<T, 8, MODE>(a, n_items, st);
     else if (nks <= 16) launch_ks<T, 16, MODE>(a, n_items, st);
+    else if (nks <= 32) launch_ks<T, 32, MODE>(a, n_items, st);
+    else if (nks <= 48) launch_ks<T, 48, MODE>(a, n_items, st);
     else return hipErrorInvalidValue;
   } else {
     if (nks <= 8) launch_ks<T, 8, MODE>(a, n_items, st);

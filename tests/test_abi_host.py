@@ -77,7 +77,8 @@ def test_buffer_sizes():
     ((2, 10, -1, 64, 32, 0), 1),       # U < 0
     ((2, 10, 2, 64, 32, 7), 1),        # dtype
     ((2, 10, 2, 60, 32, 0), 2),        # H not a multiple of 16
-    ((2, 10, 2, 512, 32, 0), 2),       # fp32 H > 256
+    ((2, 10, 2, 784, 32, 0), 2),       # fp32 H > 768
+    ((2, 10, 2, 784, 32, 1), 2),       # bf16 H > 768
     ((2, 10, 2, 64, 30, 0), 2),        # V not a multiple of 8
     ((2, 10, 1024, 64, 32, 0), 2),     # U + 1 > 1024
     ((8192, 10, 2, 64, 32, 0), 2),     # B > 8191

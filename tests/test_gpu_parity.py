@@ -115,6 +115,33 @@ def test_bf16_wide_hidden_partial_tiles(tiles):
     _compare_all(inp, g, _oracle_full(inp))
 
 
+@pytest.mark.parametrize("H,V,big", [
+    (272, 200, False),  # two 256-wide parts of h, one live k-step in the second
+    (512, 256, False),  # two whole parts, exact shape
+    (640, 200, False),  # three parts, the last half used
+    (768, 256, False),  # three whole parts, exact shape (the largest hidden size)
+    (640, 200, True),   # one |enc| > 40: h evaluated from the inputs, part by part
+])
+def test_fp32_wide_hidden(H, V, big):
+    """fp32 above 256 hidden: h is held in registers 256 hidden at a time and
+    each part is rebuilt when a vocabulary step reaches it.  Untiled, tiled,
+    and tiled in vocabulary parts (the later parts read the first part's
+    stored h rows back); every output against the oracle."""
+    inp = make_inputs(3, 40, 13, H, V, dtype="fp32", sigma=0.05, seed=13, t_range=(17, 40),
+                      u_range=(3, 13))
+    inp.U_lens[:] = [13, 9, 4]
+    if big:
+        inp.enc[1, 2, 5] = 45.0
+        inp.enc_f64[1, 2, 5] = 45.0
+    gcs = [1.0, -0.5, 2.0]
+    ref = _oracle_full(inp, grad_costs=gcs)
+    for tiles in [(0, 0, 0), (16, 8, 0), (16, 8, 128)]:
+        print(f"[fp32 wide hidden H={H} V={V} big={big} tiles={tiles}]", flush=True)
+        g = run_gpu(inp, *tiles, grad_costs=gcs)
+        assert g["status"] == 0
+        _compare_all(inp, g, ref)
+
+
 def test_data_errors_flagged():
     inp = make_inputs(4, 12, 5, 32, 24, sigma=0.4, seed=5, t_range=(4, 12), u_range=(1, 5))
     good = make_inputs(4, 12, 5, 32, 24, sigma=0.4, seed=5, t_range=(4, 12), u_range=(1, 5))

@@ -139,6 +139,16 @@ def test_pruned_ragged_and_infeasible(dtype, sigma):
     assert g["status"] == 16
 
 
+def test_pruned_fp32_wide_hidden():
+    """fp32 at H = 640 (h rebuilt in 256-wide parts by the joint kernel),
+    S = 4: every output against the oracle."""
+    inp = make_inputs(3, 30, 9, 640, 200, dtype="fp32", sigma=0.05, seed=29, t_range=(12, 30),
+                      u_range=(2, 9))
+    print("[pruned fp32 H=640 S=4 tiles=(16, 8, 0)]", flush=True)
+    g, _ = _full(inp, 4, (16, 8, 0), gcs=[1.0, -0.5, 2.0])
+    assert g["status"] == 0
+
+
 def test_pruned_medium():
     """The medium workload (bf16, H = 640, V = 1024) with S = 5: every
     utterance's bounds, simple and pruned cost; the gradients of one

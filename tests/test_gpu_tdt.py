@@ -115,6 +115,21 @@ def test_tdt_ragged_and_unreachable(dtype, sigma):
     assert 3 not in live and len(live) == inp.B - 1
 
 
+@pytest.mark.parametrize("tiles", [(0, 0, 0), (16, 8, 0)])
+def test_tdt_fp32_wide_hidden(tiles):
+    """fp32 at H = 640 (h rebuilt in 256-wide parts by the joint kernel):
+    every cost and gradient, durations 0..4."""
+    inp = make_inputs(3, 30, 9, 640, 200, dtype="fp32", sigma=0.05, seed=23, t_range=(12, 30),
+                      u_range=(2, 9))
+    head = make_duration_head(inp, (0, 1, 2, 3, 4), seed=4, sigma=0.1)
+    gcs = [1.0, -0.5, 2.0]
+    print(f"[tdt fp32 H=640 tiles={tiles}]", flush=True)
+    g = _run(inp, head, tiles, gcs=gcs)
+    assert g["status"] == 0
+    refs = tdt_oracle(inp, head, range(inp.B), WORKERS, grad_costs=gcs)
+    assert len(_compare(inp, g, refs)) == inp.B
+
+
 def test_tdt_medium():
     """Medium workload (bf16, H = 640, V = 1024), durations 0..4: every cost,
     one utterance's gradients, the weight gradients of a two-utterance
