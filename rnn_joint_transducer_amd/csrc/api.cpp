@@ -719,7 +719,9 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   // reduction kernels add after each GEMM, in place of float atomics
   auto reduce_dh = [&]() -> hipError_t {
     if (!det) return hipSuccess;
-    return timed("dh_reduce", st, [&] { return launch_dh_reduce(h, st); });
+    return timed("dh_reduce", st, [&] {
+      return launch_dh_reduce(h, p.untiled ? p.cap_all : p.cap_chunk, st);
+    });
   };
   auto reduce_dw = [&]() -> hipError_t {
     if (!det) return hipSuccess;

@@ -864,30 +864,80 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
   }
 }
 
-// Deterministic d_enc / d_pred of one chunk: thread n of workgroup
-// (b, n-block) walks the chunk's tile list in order and adds the stored
-// per-tile rows of utterance b (each output element has one writer).
+// First index of the sorted tile list [lo, hi) whose word is not below key
+// (the words order by utterance, tile row, tile column; uniform scalar loads).
+__device__ __forceinline__ int tile_lower_bound(const int32_t* tiles, int lo, int hi, uint32_t key) {
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((uint32_t)ld_const(tiles + mid) < key) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ bool tile_present(const int32_t* tiles, int lo, int hi, uint32_t key) {
+  const int j = tile_lower_bound(tiles, lo, hi, key);
+  return j < hi && (uint32_t)ld_const(tiles + j) == key;
+}
+
+// Deterministic d_enc / d_pred of one chunk, from the per-tile rows dh
+// stored (enc_part / pred_part, indexed by list entry).  Workgroup (i, hidden
+// block) belongs to list entry i = tile (b, tt, tu).  If i is the first entry
+// of tile row (b, tt), it sums that row's entries' d_enc rows in list order
+// and adds the sums to d_enc.  If no entry of an earlier tile row of
+// utterance b has column tu, it sums the d_pred rows of column (b, tu) over
+// the tile rows in order and adds them to d_pred.  Each output element of
+// the chunk gets one addition, and every sum has a fixed order.
 __global__ __launch_bounds__(256) void dh_reduce_kernel(DhArgs a) {
   if (ld_const(a.hdr + kHdrRefuse)) return;
+  const int count = ld_const(a.tile_count);
+  const int i = blockIdx.x;
+  if (i >= count) return;
   const Dims d = a.d;
-  const int b = blockIdx.x, n = blockIdx.y * 256 + threadIdx.x, H = d.H;
-  if (n >= H) return;
-  const int Tl = a.Teff[b], Ul = a.Ueff[b];
-  const int count = a.tile_count[0];
-  for (int i = 0; i < count; ++i) {
-    int tb, tt, tu;
-    tile_unpack(a.tiles[i], tb, tt, tu);
-    if (tb != b) continue;
-    const int t0 = a.ct0 + tt * kTileT, u0 = a.cu0 + tu * kTileU;
-    for (int r = 0; r < kTileT; ++r) {
-      const int t = t0 + r;
-      if (t < Tl)
-        a.d_enc[((size_t)b * d.T + t) * H + n] += a.enc_part[((size_t)i * kTileT + r) * H + n];
+  const int H = d.H, n = blockIdx.y * 256 + threadIdx.x;
+  const int32_t* tiles = a.tiles;
+  const uint32_t key = (uint32_t)ld_const(tiles + i);
+  int b, tt, tu;
+  tile_unpack((int)key, b, tt, tu);
+  const int Tl = ld_const(a.Teff + b), Ul = ld_const(a.Ueff + b);
+  // d_enc: the run of tile row (b, tt) starts at i
+  if (i == 0 || ((uint32_t)ld_const(tiles + i - 1) >> 7) != (key >> 7)) {
+    int e = i + 1;
+    while (e < count && ((uint32_t)ld_const(tiles + e) >> 7) == (key >> 7)) ++e;
+    if (n < H) {
+      for (int r = 0; r < kTileT; ++r) {
+        const int t = a.ct0 + tt * kTileT + r;
+        if (t >= Tl) break;
+        float sum = 0.f;
+        for (int j = i; j < e; ++j) sum += a.enc_part[((size_t)j * kTileT + r) * H + n];
+        a.d_enc[((size_t)b * d.T + t) * H + n] += sum;
+      }
     }
+  }
+  // d_pred: utterance b's entries are [ub, ue); column tu's first tile row
+  // owns the column
+  const int ub = tile_lower_bound(tiles, 0, count, (uint32_t)tile_pack(b, 0, 0));
+  const int ue = tile_lower_bound(tiles, ub, count, (uint32_t)tile_pack(b + 1, 0, 0));
+  int fb_, tt_first, tt_last, fu_;
+  tile_unpack(ld_const(tiles + ub), fb_, tt_first, fu_);
+  tile_unpack(ld_const(tiles + ue - 1), fb_, tt_last, fu_);
+  for (int r = tt_first; r < tt; ++r)
+    if (tile_present(tiles, ub, ue, (uint32_t)tile_pack(b, r, tu))) return;
+  float sum[kTileU];
+#pragma unroll
+  for (int q = 0; q < kTileU; ++q) sum[q] = 0.f;
+  for (int r = tt; r <= tt_last; ++r) {
+    const int j = tile_lower_bound(tiles, ub, ue, (uint32_t)tile_pack(b, r, tu));
+    if (j >= ue || (uint32_t)ld_const(tiles + j) != (uint32_t)tile_pack(b, r, tu)) continue;
+    if (n < H) {
+#pragma unroll
+      for (int q = 0; q < kTileU; ++q) sum[q] += a.pred_part[((size_t)j * kTileU + q) * H + n];
+    }
+  }
+  if (n < H) {
+#pragma unroll
     for (int q = 0; q < kTileU; ++q) {
-      const int u = u0 + q;
-      if (u <= Ul)
-        a.d_pred[((size_t)b * d.U1 + u) * H + n] += a.pred_part[((size_t)i * kTileU + q) * H + n];
+      const int u = a.cu0 + tu * kTileU + q;
+      if (u <= Ul) a.d_pred[((size_t)b * d.U1 + u) * H + n] += sum[q];
     }
   }
 }
@@ -942,8 +992,9 @@ hipError_t launch_grad_inplace(void* z, bool bf16, const JointArgs& a, int max_t
   return hipGetLastError();
 }
 
-hipError_t launch_dh_reduce(const DhArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(dh_reduce_kernel, dim3(a.d.B, (a.d.H + 255) / 256), dim3(256), 0, st, a);
+hipError_t launch_dh_reduce(const DhArgs& a, int max_tiles, hipStream_t st) {
+  if (max_tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL(dh_reduce_kernel, dim3(max_tiles, (a.d.H + 255) / 256), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

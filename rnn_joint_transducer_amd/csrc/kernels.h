@@ -253,7 +253,8 @@ struct DhArgs {
   float* d_pred;
   // deterministic reductions (both set, ksplit 1): each tile's d_enc rows
   // [tiles, 16, H] and d_pred rows [tiles, 8, H] are stored here instead of
-  // being added with atomics; launch_dh_reduce then adds them in list order
+  // being added with atomics; launch_dh_reduce then adds them, each sum in a
+  // fixed order
   float* enc_part;
   float* pred_part;
 };
@@ -287,7 +288,7 @@ struct DwArgs {
   float* w_part;
   double* b_part;
 };
-hipError_t launch_dh_reduce(const DhArgs& a, hipStream_t st);
+hipError_t launch_dh_reduce(const DhArgs& a, int max_tiles, hipStream_t st);
 hipError_t launch_dw_reduce(const DwArgs& a, hipStream_t st);
 hipError_t launch_dw(const DwArgs& a, bool bf16, hipStream_t st);
 

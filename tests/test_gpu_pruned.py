@@ -149,6 +149,31 @@ def test_pruned_fp32_wide_hidden():
     assert g["status"] == 0
 
 
+@pytest.mark.parametrize("tiles", [(64, 64, 0), (16, 0, 0)])
+def test_pruned_deterministic_mode(tiles):
+    """Deterministic mode over a banded tile list (rows of the chunk hold
+    different tile columns): bitwise identical outputs run after run, and
+    still the oracle's."""
+    from rnn_joint_transducer_amd import _lib
+    inp = make_inputs(4, 70, 23, 48, 40, dtype="fp32", sigma=0.4, seed=31, t_range=(40, 70),
+                      u_range=(10, 23))
+    gcs = [1.0, -0.5, 2.0, 0.25]
+    old = _lib.get_flags()
+    try:
+        _lib.set_flags(_lib.FLAG_DETERMINISTIC)
+        print(f"[pruned deterministic S=3 tiles={tiles}]", flush=True)
+        runs = [_run(inp, 3, tiles, grad_costs=gcs) for _ in range(2)]
+    finally:
+        _lib.set_flags(old)
+    for k in ("costs", "simple", "bounds", "dEnc", "dPred", "dW", "db"):
+        assert np.array_equal(runs[0][k], runs[1][k], equal_nan=True), k
+    refs = pruned_oracle(inp, 3, range(inp.B), WORKERS, grad_costs=gcs)
+    cmp = _check_utts(inp, 3, runs[0], refs, range(inp.B))
+    assert len(cmp) == inp.B
+    check_grad("d_W_out", runs[0]["dW"], sum(o["dW"] for o in refs), inp.dtype)
+    check_grad("d_b_out", runs[0]["db"], sum(o["db"] for o in refs), inp.dtype)
+
+
 def test_pruned_medium():
     """The medium workload (bf16, H = 640, V = 1024) with S = 5: every
     utterance's bounds, simple and pruned cost; the gradients of one
