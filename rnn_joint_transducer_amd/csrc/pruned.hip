@@ -51,11 +51,15 @@ __device__ __forceinline__ double to_f64(T x) {
 
 // ------------------------------------------------------------ float64 GEMM
 //
-// One 64 x 64 output tile per workgroup of 256 threads, each thread 4 x 4
-// outputs (rows 4 (tid / 16) + i, columns 4 (tid % 16) + j), k-steps of 16
-// staged in LDS as float64 (operands converted on load).  A is row-major
-// [M, K]; B is row-major [K, N] (kProj) or [N, K] (kScore, the product with
-// B transposed).
+// One 64 x 64 output tile per workgroup of 4 waves; wave w computes rows
+// 32 (w / 2) .. +31 and columns 32 (w % 2) .. +31 as 2 x 2 blocks of
+// v_mfma_f64_16x16x4_f64.  k-steps of 16 are staged in LDS as float64
+// (operands converted as they are written); the next step's global loads
+// are in flight while the current step's MFMAs run.  A is row-major [M, K];
+// B is row-major [K, N] (kProj) or [N, K] (kScore, the product with B
+// transposed).  MFMA operand layout (lane l): A[l % 16][l / 16] of a 16 x 4
+// block, B[l / 16][l % 16] of a 4 x 16 block; output value i of lane l is
+// D[4 i + l / 16][l % 16].
 constexpr int kProj = 0, kScore = 1;
 
 struct F64GemmArgs {
@@ -79,11 +83,16 @@ struct F64GemmArgs {
   double* LEs;
 };
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
 template <typename TA, typename TB, int MODE>
 __global__ __launch_bounds__(256) void f64_gemm_kernel(F64GemmArgs g) {
-  __shared__ __align__(16) double As[16][64];
-  __shared__ __align__(16) double Bs[16][64];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  __shared__ __align__(16) double As[2][16][64];
+  __shared__ __align__(16) double Bs[2][16][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r0 = 32 * (w >> 1), c0 = 32 * (w & 1);
+  const int lm = lane & 15, lk4 = lane >> 4;
   const int m0 = blockIdx.x * 64, n0 = blockIdx.y * 64;
   int M = g.M, N = g.N, K = g.K;
   const TA* A = static_cast<const TA*>(g.A);
@@ -100,95 +109,124 @@ __global__ __launch_bounds__(256) void f64_gemm_kernel(F64GemmArgs g) {
     A += (size_t)b * g.d.T * K;
     B += (size_t)b * g.d.U1 * K;
   }
-  double acc[4][4];
+  f64x4 acc[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
 
   // loader roles: A (and B of kScore) 4 consecutive k of row tid / 4;
-  // B of kProj 4 consecutive n of k-row tid / 16
+  // B of kProj 4 consecutive n of k-row tid / 16.  Raw values are held
+  // across the MFMAs and converted as they are written to LDS.
   const int lr = tid >> 2, lk = (tid & 3) * 4;
   const int bk = tid >> 4, bn = (tid & 15) * 4;
-  for (int k0 = 0; k0 < K; k0 += 16) {
+  TA xa[4];
+  TB xb[4];
+  // (sources clamped into the operands, the values outside them zeroed:
+  // no branches around the loads; K and N are multiples of 4)
+  auto load = [&](int k0) {
     {
-      const int m = m0 + lr, k = k0 + lk;
-      double x[4] = {0.0, 0.0, 0.0, 0.0};
-      if (m < M && k < K) {  // K is a multiple of 4
-        const TA* p = A + (size_t)m * K + k;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = to_f64(p[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) As[lk + i][lr] = x[i];
-    }
-    if constexpr (MODE == kProj) {
-      const int k = k0 + bk, n = n0 + bn;
-      double x[4] = {0.0, 0.0, 0.0, 0.0};
-      if (k < K && n < N) {  // N is a multiple of 4
-        const TB* p = B + (size_t)k * N + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = to_f64(p[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Bs[bk][bn + i] = x[i];
-    } else {
-      const int n = n0 + lr, k = k0 + lk;
-      double x[4] = {0.0, 0.0, 0.0, 0.0};
-      if (n < N && k < K) {
-        const TB* p = B + (size_t)n * K + k;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = to_f64(p[i]);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Bs[lk + i][lr] = x[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      double a[4], bb[4];
+      const bool ok = m0 + lr < M && k0 + lk < K;
+      const TA* p = A + (size_t)min(m0 + lr, M - 1) * K + min(k0 + lk, K - 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = As[k][4 * ty + i];
-        bb[i] = Bs[k][4 * tx + i];
+        const TA v = p[i];
+        xa[i] = ok ? v : TA(0);
+      }
+    }
+    if constexpr (MODE == kProj) {
+      const bool ok = k0 + bk < K && n0 + bn < N;
+      const TB* p = B + (size_t)min(k0 + bk, K - 1) * N + min(n0 + bn, N - 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const TB v = p[i];
+        xb[i] = ok ? v : TB(0);
+      }
+    } else {
+      const bool ok = n0 + lr < N && k0 + lk < K;
+      const TB* p = B + (size_t)min(n0 + lr, N - 1) * K + min(k0 + lk, K - 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const TB v = p[i];
+        xb[i] = ok ? v : TB(0);
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) As[buf][lk + i][lr] = to_f64(xa[i]);
+    if constexpr (MODE == kProj) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Bs[buf][bk][bn + i] = to_f64(xb[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Bs[buf][lk + i][lr] = to_f64(xb[i]);
+    }
+  };
+  // two LDS stages: step s computes from buffer s % 2 while step s + 1's
+  // operands load and are then written to the other buffer, whose last
+  // reader (step s - 1) finished before the previous barrier
+  load(0);
+  store(0);
+  __syncthreads();
+  int k0 = 0, buf = 0;
+  do {  // K >= 4: at least one step
+    // (the last step reloads its own operands into the idle buffer)
+    load(k0 + 16 < K ? k0 + 16 : k0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      double a[2], bb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = As[buf][4 * kk + lk4][r0 + 16 * i + lm];
+        bb[i] = Bs[buf][4 * kk + lk4][c0 + 16 * i + lm];
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], bb[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], bb[j], acc[i][j], 0, 0, 0);
     }
+    store(buf ^ 1);
     __syncthreads();
-  }
+    k0 += 16;
+    buf ^= 1;
+  } while (k0 < K);
 
   if constexpr (MODE == kProj) {
     const TB* bias = static_cast<const TB*>(g.bias);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = m0 + 4 * ty + i;
-      if (m >= M) continue;
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + c0 + 16 * j + lm;
+      if (n >= N) continue;
+      const double bn_ = bias ? to_f64(bias[n]) : 0.0;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 4 * tx + j;
-        if (n < N) g.C[(size_t)m * N + n] = acc[i][j] + (bias ? to_f64(bias[n]) : 0.0);
-      }
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + r0 + 16 * i + 4 * q + lk4;
+          if (m < M) g.C[(size_t)m * N + n] = acc[i][j][q] + bn_;
+        }
     }
   } else {
     const Dims d = g.d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = m0 + 4 * ty + i;
-      if (t >= Tl) continue;
-      const size_t rt = (size_t)b * d.T + t;
+    for (int j = 0; j < 2; ++j) {
+      const int u = n0 + c0 + 16 * j + lm;
+      if (u > Ul) continue;
+      const size_t ru = (size_t)b * d.U1 + u;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int u = n0 + 4 * tx + j;
-        if (u > Ul) continue;
-        const size_t ru = (size_t)b * d.U1 + u;
-        const double lse = g.ma[rt] + g.ml[ru] + log(acc[i][j]);
-        const size_t ix = skew_idx(d, b, t, u);
-        g.LBs[ix] = g.amB[rt] + g.lmB[ru] - lse;
-        g.LEs[ix] = u < Ul ? g.amY[rt * d.U + u] + g.lmY[ru] - lse : 0.0;
-      }
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int t = m0 + r0 + 16 * i + 4 * q + lk4;
+          if (t >= Tl) continue;
+          const size_t rt = (size_t)b * d.T + t;
+          const double lse = g.ma[rt] + g.ml[ru] + log(acc[i][j][q]);
+          const size_t ix = skew_idx(d, b, t, u);
+          g.LBs[ix] = g.amB[rt] + g.lmB[ru] - lse;
+          g.LEs[ix] = u < Ul ? g.amY[rt * d.U + u] + g.lmY[ru] - lse : 0.0;
+        }
     }
   }
 }
