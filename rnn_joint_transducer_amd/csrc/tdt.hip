@@ -80,6 +80,8 @@ __device__ __forceinline__ float bdur(const TdtArgs& a, int j) {
 // e^{2 pred} row is read in coalesced 256-byte pieces, and the K partial
 // sums of the lanes meet in a butterfly.  W_dur (float32, [K][H]) and the
 // frame's e^{2 enc} row are in LDS.
+// (KK = the number of durations, a.K)
+template <int KK>
 __global__ __launch_bounds__(256) void dur_head_kernel(TdtArgs a) {
   extern __shared__ float sm[];  // W_dur [K][H], then the e^{2 enc} row [H]
   const Dims d = a.d;
@@ -87,7 +89,8 @@ __global__ __launch_bounds__(256) void dur_head_kernel(TdtArgs a) {
   const int lane = tid & 63, wv = tid >> 6;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   if (t >= Tl) return;  // uniform
-  const int H = d.H, K = a.K;
+  const int H = d.H;
+  constexpr int K = KK;
   float* w = sm;
   float* er = sm + H * K;
   const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
@@ -95,38 +98,38 @@ __global__ __launch_bounds__(256) void dur_head_kernel(TdtArgs a) {
   for (int k = tid; k < H; k += 256) er[k] = a.Eexp[((size_t)b * d.T + t) * H + k];
   __syncthreads();
   for (int u = wv; u <= Ul; u += 4) {
-    float z[kTdtMaxK];
+    float z[KK];
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j) z[j] = 0.f;
+    for (int j = 0; j < KK; ++j) z[j] = 0.f;
     const float* pr = a.Pexp + ((size_t)b * d.U1 + u) * H;
     for (int k = lane; k < H; k += 64) {
       const float h = h_round(a, use_ep ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + er[k] * pr[k])
                                         : h_of(a, b, t, u, k, false));
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j)
-        if (j < K) z[j] = fmaf(h, w[j * H + k], z[j]);
+      for (int j = 0; j < KK; ++j)
+        z[j] = fmaf(h, w[j * H + k], z[j]);
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1)
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j)
-        if (j < K) z[j] += __shfl_xor(z[j], off);
+      for (int j = 0; j < KK; ++j)
+        z[j] += __shfl_xor(z[j], off);
     if (lane == 0) {
       float m = -__builtin_inff();
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j)
+      for (int j = 0; j < KK; ++j)
         if (j < K) {
           z[j] += bdur(a, j);
           m = fmaxf(m, z[j]);
         }
       float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j)
+      for (int j = 0; j < KK; ++j)
         if (j < K) s += __expf(z[j] - m);
       const float lse = m + __logf(s);
       float* ld = a.LD + skew_idx(d, b, t, u) * K;
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j)
+      for (int j = 0; j < KK; ++j)
         if (j < K) ld[j] = z[j] - lse;
     }
   }
@@ -145,15 +148,18 @@ __global__ __launch_bounds__(256) void dur_head_kernel(TdtArgs a) {
 //
 // The step weights a diagonal needs (float32 LB, LE, LD of the source cells)
 // do not depend on the recursion: each lane loads the next diagonal's while
-// the current one is computed.  The loads are a fixed set of kTdtMaxK per
-// kind (unused durations read a valid cell and are masked), so the wait
-// before their use never has to cover the loads issued after them.
+// the current one is computed.  The loads are a fixed set of K per kind
+// (a source outside the lattice reads a valid cell and is masked), so the
+// wait before their use never has to cover the loads issued after them.
+// The kernel is instantiated for each duration count, so no work is spent on
+// unused duration slots.
 // (absent steps hold -inf)
-__device__ __forceinline__ double lse_terms(const double (&x)[2 * kTdtMaxK]) {
+template <int N>
+__device__ __forceinline__ double lse_terms(const double (&x)[N]) {
   double m = kNegInfD;
   bool nan = false;
 #pragma unroll
-  for (int i = 0; i < 2 * kTdtMaxK; ++i) {
+  for (int i = 0; i < N; ++i) {
     nan |= x[i] != x[i];
     m = x[i] > m ? x[i] : m;
   }
@@ -161,14 +167,17 @@ __device__ __forceinline__ double lse_terms(const double (&x)[2 * kTdtMaxK]) {
   if (m == kNegInfD) return kNegInfD;
   float sum = 0.f;
 #pragma unroll
-  for (int i = 0; i < 2 * kTdtMaxK; ++i) sum += exp2_fast((float)(x[i] - m) * kLog2e);
+  for (int i = 0; i < N; ++i) sum += exp2_fast((float)(x[i] - m) * kLog2e);
   return m + (double)(__builtin_amdgcn_logf(sum) * kLn2);
 }
 
+// (KK = the number of durations, a.K)
+template <int KK>
 __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
   __shared__ double ring[kRing][513];
   const Dims d = a.d;
-  const int b = blockIdx.x, u = threadIdx.x, K = a.K;
+  const int b = blockIdx.x, u = threadIdx.x;
+  constexpr int K = KK;
   const bool fwd = blockIdx.y == 0;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   if (Tl == 0) {
@@ -185,35 +194,35 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
   __syncthreads();
   const bool lane_on = u <= Ul;
   const int nd = Tl + Ul;  // diagonals 0 .. Tl-1+Ul
-  int dur[kTdtMaxK];
+  int dur[KK];
 #pragma unroll
-  for (int j = 0; j < kTdtMaxK; ++j) dur[j] = a.dur[j < K ? j : K - 1];
+  for (int j = 0; j < KK; ++j) dur[j] = a.dur[j];
   const size_t base = (size_t)b * d.DG * d.U1;
   // cell (t, uu) of this utterance, t + uu <= DG - 1 and uu <= U1 - 1
   auto idx = [&](int t, int uu) { return base + (size_t)(t + uu) * d.U1 + uu; };
   if (fwd) {
     // weights of the cell this lane computes on diagonal k: blank from
     // (t - d_j, u), label from (t - d_j, u - 1); invalid sources read (0, 0)
-    float wlb[kTdtMaxK], wlbd[kTdtMaxK], wle[kTdtMaxK], wled[kTdtMaxK];
+    float wlb[KK], wlbd[KK], wle[KK], wled[KK];
     auto load_w = [&](int k) {
       const int t = k - u;
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j) {
+      for (int j = 0; j < KK; ++j) {
         const int s = t - dur[j];
         const bool okb = lane_on && t < Tl && s >= 0;
         const bool oke = okb && u >= 1;
         const size_t ib = okb ? idx(s, u) : base, ie = oke ? idx(s, u - 1) : base;
         wlb[j] = a.LB[ib];
-        wlbd[j] = a.LD[ib * K + (j < K ? j : 0)];
+        wlbd[j] = a.LD[ib * K + j];
         wle[j] = a.LE[ie];
-        wled[j] = a.LD[ie * K + (j < K ? j : 0)];
+        wled[j] = a.LD[ie * K + j];
       }
     };
     load_w(0);
     for (int k = 0; k < nd; ++k) {
-      float clb[kTdtMaxK], clbd[kTdtMaxK], cle[kTdtMaxK], cled[kTdtMaxK];
+      float clb[KK], clbd[KK], cle[KK], cled[KK];
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j) {
+      for (int j = 0; j < KK; ++j) {
         clb[j] = wlb[j];
         clbd[j] = wlbd[j];
         cle[j] = wle[j];
@@ -227,9 +236,9 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
         if (k == 0) {
           v = 0.0;
         } else {
-          double x[2 * kTdtMaxK];
+          double x[2 * KK];
 #pragma unroll
-          for (int j = 0; j < kTdtMaxK; ++j) {
+          for (int j = 0; j < KK; ++j) {
             const int dj = dur[j], s = t - dj;
             const bool ok = j < K && s >= 0;
             // blank (s,u) -> (t,u), on diagonal k - dj
@@ -248,9 +257,9 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
       __syncthreads();
     }
     if (u == Ul) {  // the final blank lands exactly on frame T'
-      double x[2 * kTdtMaxK];
+      double x[2 * KK];
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j) {
+      for (int j = 0; j < KK; ++j) {
         const int dj = dur[j], s = Tl - dj;
         x[2 * j] = j < K && dj >= 1 && s >= 0
                        ? a.alpha[idx(s, Ul)] + ((double)a.LB[idx(s, Ul)] + (double)a.LD[idx(s, Ul) * K + j])
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
     }
   } else {
     // the weights of a cell's outgoing steps are its own LB, LE, LD
-    float wlb = 0.f, wle = 0.f, wld[kTdtMaxK];
+    float wlb = 0.f, wle = 0.f, wld[KK];
     auto load_w = [&](int k) {
       const int t = k - u;
       const bool ok = lane_on && t >= 0 && t < Tl;
@@ -271,23 +280,23 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
       wlb = a.LB[i];
       wle = a.LE[i];
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j) wld[j] = a.LD[i * K + (j < K ? j : 0)];
+      for (int j = 0; j < KK; ++j) wld[j] = a.LD[i * K + j];
     };
     load_w(nd - 1);
     for (int k = nd - 1; k >= 0; --k) {
       const float clb = wlb, cle = wle;
-      float cld[kTdtMaxK];
+      float cld[KK];
 #pragma unroll
-      for (int j = 0; j < kTdtMaxK; ++j) cld[j] = wld[j];
+      for (int j = 0; j < KK; ++j) cld[j] = wld[j];
       if (k > 0) load_w(k - 1);
       const int t = k - u;
       const bool on = lane_on && t >= 0 && t < Tl;
       double v = kNegInfD;
       if (on) {
         const double lb = clb, le = u < Ul ? (double)cle : 0.0;
-        double x[2 * kTdtMaxK];
+        double x[2 * KK];
 #pragma unroll
-        for (int j = 0; j < kTdtMaxK; ++j) {
+        for (int j = 0; j < KK; ++j) {
           const int dj = dur[j];
           const double ldj = cld[j];
           double xb = kNegInfD, xe = kNegInfD;
@@ -374,23 +383,26 @@ constexpr int kFrames = 16;
 constexpr int kHPer = 3;  // hidden units per thread (H <= 768)
 constexpr int kUChunk = 32;
 
+// (KK = the number of durations, a.K)
+template <int KK>
 __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
-  __shared__ float zs[kUChunk][kFrames][kTdtMaxK];
+  __shared__ float zs[kUChunk][kFrames][KK];
   const Dims d = a.d;
-  const int b = blockIdx.y, tid = threadIdx.x, K = a.K;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  constexpr int K = KK;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   const int H = d.H;
   const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
   const int t_lo = blockIdx.x * kFrames;
   if (t_lo >= Tl) return;  // uniform
   const int nt = min(kFrames, Tl - t_lo);
-  float w[kHPer][kTdtMaxK], dw[kHPer][kTdtMaxK], db[kTdtMaxK];
+  float w[kHPer][KK], dw[kHPer][KK], db[KK];
   float e[kFrames][kHPer], ae[kFrames][kHPer];
 #pragma unroll
   for (int i = 0; i < kHPer; ++i) {
     const int k = tid + 256 * i;
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j) {
+    for (int j = 0; j < KK; ++j) {
       w[i][j] = (k < H && j < K) ? wdur(a, k, j) : 0.f;
       dw[i][j] = 0.f;
     }
@@ -402,13 +414,13 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
     }
   }
 #pragma unroll
-  for (int j = 0; j < kTdtMaxK; ++j) db[j] = 0.f;
+  for (int j = 0; j < KK; ++j) db[j] = 0.f;
 
   for (int u0 = 0; u0 <= Ul; u0 += kUChunk) {
     const int nu = min(kUChunk, Ul + 1 - u0);
     __syncthreads();  // the previous chunk's reads are done
-    for (int i = tid; i < kUChunk * kFrames * kTdtMaxK; i += 256) {
-      const int j = i % kTdtMaxK, q = (i / kTdtMaxK) % kFrames, uu = i / (kTdtMaxK * kFrames);
+    for (int i = tid; i < kUChunk * kFrames * KK; i += 256) {
+      const int j = i % KK, q = (i / KK) % kFrames, uu = i / (KK * kFrames);
       float v = 0.f;
       if (uu < nu && q < nt && j < K) v = a.dzd[skew_idx(d, b, t_lo + q, u0 + uu) * K + j];
       zs[uu][q][j] = v;
@@ -426,9 +438,9 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
 #pragma unroll
       for (int q = 0; q < kFrames; ++q) {
         if (q >= nt) continue;  // uniform
-        float z[kTdtMaxK];
+        float z[KK];
 #pragma unroll
-        for (int j = 0; j < kTdtMaxK; ++j) {
+        for (int j = 0; j < KK; ++j) {
           z[j] = zs[uu][q][j];
           db[j] += tid == 0 ? z[j] : 0.f;
         }
@@ -440,13 +452,13 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
                                  : h_of(a, b, t_lo + q, u, k, false);
           float sacc = 0.f;
 #pragma unroll
-          for (int j = 0; j < kTdtMaxK; ++j) sacc = fmaf(w[i][j], z[j], sacc);
+          for (int j = 0; j < KK; ++j) sacc = fmaf(w[i][j], z[j], sacc);
           const float dp = (1.0f - h * h) * sacc;
           ae[q][i] += dp;
           ap[i] += dp;
           const float hr = h_round(a, h);
 #pragma unroll
-          for (int j = 0; j < kTdtMaxK; ++j) dw[i][j] = fmaf(hr, z[j], dw[i][j]);
+          for (int j = 0; j < KK; ++j) dw[i][j] = fmaf(hr, z[j], dw[i][j]);
         }
       }
 #pragma unroll
@@ -464,12 +476,12 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
     for (int q = 0; q < kFrames; ++q)
       if (q < nt) atomicAdd(&a.d_enc[((size_t)b * d.T + t_lo + q) * H + k], ae[q][i]);
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j)
+    for (int j = 0; j < KK; ++j)
       if (j < K) atomicAdd(&a.d_Wd[(size_t)k * K + j], dw[i][j]);
   }
   if (tid == 0) {
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j)
+    for (int j = 0; j < KK; ++j)
       if (j < K) atomicAdd(&a.d_bd[j], db[j]);
   }
 }
@@ -478,12 +490,34 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
 
 hipError_t launch_tdt_dur_head(const TdtArgs& a, hipStream_t st) {
   const size_t lds = sizeof(float) * (size_t)a.d.H * (a.K + 1);
-  hipLaunchKernelGGL(dur_head_kernel, dim3(a.d.T, a.d.B), dim3(256), lds, st, a);
+  const dim3 g(a.d.T, a.d.B), blk(256);
+  switch (a.K) {
+    case 1: hipLaunchKernelGGL(dur_head_kernel<1>, g, blk, lds, st, a); break;
+    case 2: hipLaunchKernelGGL(dur_head_kernel<2>, g, blk, lds, st, a); break;
+    case 3: hipLaunchKernelGGL(dur_head_kernel<3>, g, blk, lds, st, a); break;
+    case 4: hipLaunchKernelGGL(dur_head_kernel<4>, g, blk, lds, st, a); break;
+    case 5: hipLaunchKernelGGL(dur_head_kernel<5>, g, blk, lds, st, a); break;
+    case 6: hipLaunchKernelGGL(dur_head_kernel<6>, g, blk, lds, st, a); break;
+    case 7: hipLaunchKernelGGL(dur_head_kernel<7>, g, blk, lds, st, a); break;
+    case 8: hipLaunchKernelGGL(dur_head_kernel<8>, g, blk, lds, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_tdt_lattice(const TdtArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(tdt_lattice_kernel, dim3(a.d.B, 2), dim3(512), 0, st, a);
+  const dim3 g(a.d.B, 2), blk(512);
+  switch (a.K) {
+    case 1: hipLaunchKernelGGL(tdt_lattice_kernel<1>, g, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(tdt_lattice_kernel<2>, g, blk, 0, st, a); break;
+    case 3: hipLaunchKernelGGL(tdt_lattice_kernel<3>, g, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL(tdt_lattice_kernel<4>, g, blk, 0, st, a); break;
+    case 5: hipLaunchKernelGGL(tdt_lattice_kernel<5>, g, blk, 0, st, a); break;
+    case 6: hipLaunchKernelGGL(tdt_lattice_kernel<6>, g, blk, 0, st, a); break;
+    case 7: hipLaunchKernelGGL(tdt_lattice_kernel<7>, g, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL(tdt_lattice_kernel<8>, g, blk, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -493,8 +527,18 @@ hipError_t launch_tdt_post(const TdtArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tdt_dur_bwd(const TdtArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(dur_bwd_kernel, dim3((a.d.T + kFrames - 1) / kFrames, a.d.B), dim3(256), 0,
-                     st, a);
+  const dim3 g((a.d.T + kFrames - 1) / kFrames, a.d.B), blk(256);
+  switch (a.K) {
+    case 1: hipLaunchKernelGGL(dur_bwd_kernel<1>, g, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(dur_bwd_kernel<2>, g, blk, 0, st, a); break;
+    case 3: hipLaunchKernelGGL(dur_bwd_kernel<3>, g, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL(dur_bwd_kernel<4>, g, blk, 0, st, a); break;
+    case 5: hipLaunchKernelGGL(dur_bwd_kernel<5>, g, blk, 0, st, a); break;
+    case 6: hipLaunchKernelGGL(dur_bwd_kernel<6>, g, blk, 0, st, a); break;
+    case 7: hipLaunchKernelGGL(dur_bwd_kernel<7>, g, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL(dur_bwd_kernel<8>, g, blk, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
