@@ -322,9 +322,12 @@ __global__ __launch_bounds__(512) void tdt_lattice_kernel(TdtArgs a) {
 // One thread per cell: gbt = sum_k gB, get = sum_k gE (float64; the token
 // head's backward reads them as its transition posteriors), dzd (float32,
 // the grad_costs weight included).
+// (KK = the number of durations, a.K)
+template <int KK>
 __global__ __launch_bounds__(256) void tdt_post_kernel(TdtArgs a) {
   const Dims d = a.d;
-  const int b = blockIdx.y, t = blockIdx.x, K = a.K;
+  const int b = blockIdx.y, t = blockIdx.x;
+  constexpr int K = KK;
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   if (t >= Tl) return;
   const double lp = a.logP[b];
@@ -341,9 +344,9 @@ __global__ __launch_bounds__(256) void tdt_post_kernel(TdtArgs a) {
     }
     const double al = a.alpha[ix];
     const double lb = a.LB[ix], le = u < Ul ? (double)a.LE[ix] : 0.0;
-    double sB = 0.0, sE = 0.0, g[kTdtMaxK];
+    double sB = 0.0, sE = 0.0, g[KK];
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j) {
+    for (int j = 0; j < KK; ++j) {
       g[j] = 0.0;
       if (j >= K) continue;
       const int dj = a.dur[j];
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(256) void tdt_post_kernel(TdtArgs a) {
     a.gE[ix] = sE;
     const double occ = sB + sE;
 #pragma unroll
-    for (int j = 0; j < kTdtMaxK; ++j)
+    for (int j = 0; j < KK; ++j)
       if (j < K) a.dzd[ix * K + j] = (float)(gc * (occ * exp((double)a.LD[ix * K + j]) - g[j]));
   }
 }
@@ -522,7 +525,18 @@ hipError_t launch_tdt_lattice(const TdtArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tdt_post(const TdtArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(tdt_post_kernel, dim3(a.d.T, a.d.B), dim3(256), 0, st, a);
+  const dim3 g(a.d.T, a.d.B), blk(256);
+  switch (a.K) {
+    case 1: hipLaunchKernelGGL(tdt_post_kernel<1>, g, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(tdt_post_kernel<2>, g, blk, 0, st, a); break;
+    case 3: hipLaunchKernelGGL(tdt_post_kernel<3>, g, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL(tdt_post_kernel<4>, g, blk, 0, st, a); break;
+    case 5: hipLaunchKernelGGL(tdt_post_kernel<5>, g, blk, 0, st, a); break;
+    case 6: hipLaunchKernelGGL(tdt_post_kernel<6>, g, blk, 0, st, a); break;
+    case 7: hipLaunchKernelGGL(tdt_post_kernel<7>, g, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL(tdt_post_kernel<8>, g, blk, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

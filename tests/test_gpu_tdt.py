@@ -84,6 +84,26 @@ def test_tdt_tiny(durations, tiles):
     assert len(_compare(inp, g, refs)) == inp.B
 
 
+@pytest.mark.parametrize("durations", [(1,), (0, 2), (1, 2, 3, 5), (0, 1, 2, 3, 4, 5),
+                                       (1, 2, 3, 4, 5, 6, 7), (0, 1, 3, 4, 6, 7, 8, 9)])
+def test_tdt_every_duration_count(durations):
+    """The token-and-duration kernels are instantiated per duration count:
+    every count from the ones the other tests leave out (1, 2, 4, 6, 7) and
+    8 with gaps in the set, with and without the zero duration, against the
+    oracle (every cost and gradient, tiled)."""
+    inp = make_inputs(3, 23, 6, 32, 24, dtype="fp32", sigma=0.3, seed=41, t_range=(9, 23),
+                      u_range=(1, 6))
+    head = make_duration_head(inp, durations, seed=5, sigma=0.3)
+    gcs = [1.0, -0.5, 2.0]
+    print(f"[tdt durations={durations}]", flush=True)
+    g = _run(inp, head, (16, 8, 0), gcs=gcs)
+    refs = tdt_oracle(inp, head, range(inp.B), WORKERS, grad_costs=gcs)
+    live = _compare(inp, g, refs)
+    # (durations {0, 2} reach only even frame counts: an odd T' has no
+    # alignment, cost +inf on both sides)
+    assert len(live) >= 1
+
+
 @pytest.mark.parametrize("tiles", [(0, 0, 0), (64, 64, 128)])
 def test_tdt_short(tiles):
     inp = make_config("short")
