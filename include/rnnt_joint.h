@@ -320,7 +320,9 @@ int rnnt_joint_loss_pruned_fwd(const void* enc, const void* pred, const void* W_
  * plus the duration log-probabilities, float32 [cells, K]); the backward's
  * workspace of rnnt_joint_loss_tdt_workspace_bytes (pass 1) bytes (the plain
  * one plus the summed step posteriors, float64, and the duration-logit
- * gradients, float32); the forward needs none (pass 0).  Untiled and tiled
+ * gradients, float32; in deterministic mode also each 16-frame block's
+ * d_W_dur / d_b_dur sums, so query it with the mode already set); the
+ * forward needs none (pass 0).  Untiled and tiled
  * modes as in rnnt_joint_loss_fwd / _bwd; full sum over alignments.  The
  * backward overwrites d_enc, d_pred, d_W_out, d_b_out, d_W_dur [H, K] and
  * d_b_dur [K] (float32) and checks, like rnnt_joint_loss_bwd, that `saved`

@@ -247,13 +247,26 @@ size_t tdt_ld_bytes(const Plan& p, int K) {
 }
 // backward workspace of a token-and-duration call: the plain one, then the
 // summed step posteriors (float64, two arrays) and the duration-logit
-// gradients (float32 [cells, K])
-void tdt_ws(const Plan& p, int K, size_t& o_gB, size_t& o_gE, size_t& o_dzd, size_t& total) {
+// gradients (float32 [cells, K]); in deterministic mode also the duration
+// head's per-frame-block d_W_dur / d_b_dur sums
+struct TdtWs {
+  size_t gB, gE, dzd, part_w, part_b, total;
+};
+TdtWs tdt_ws(const Plan& p, int K) {
   const size_t cells = (size_t)p.d.B * p.d.DG * p.d.U1;
-  o_gB = align_up(p.bwd_ws());
-  o_gE = o_gB + align_up(8 * cells);
-  o_dzd = o_gE + align_up(8 * cells);
-  total = o_dzd + align_up(4 * cells * K);
+  const size_t blocks = (size_t)p.d.B * ((p.d.T + kTdtFrames - 1) / kTdtFrames);
+  TdtWs w;
+  w.gB = align_up(p.bwd_ws());
+  w.gE = w.gB + align_up(8 * cells);
+  w.dzd = w.gE + align_up(8 * cells);
+  w.part_w = w.dzd + align_up(4 * cells * K);
+  w.part_b = w.part_w;
+  w.total = w.part_w;
+  if (deterministic_on()) {
+    w.part_b = w.part_w + align_up(4 * blocks * p.d.H * K);
+    w.total = w.part_b + align_up(4 * blocks * K);
+  }
+  return w;
 }
 
 // ---- optional per-kernel event timing (rnnt_joint_loss_timing)
@@ -560,12 +573,14 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   Plan p;
   int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
-  size_t o_gB = 0, o_gE = 0, o_dzd = 0, ws_need = p.bwd_ws();
+  TdtWs tw = {};
+  size_t ws_need = p.bwd_ws();
   if (tdt) {
     if ((rc = check_tdt(*tdt))) return rc;
     if (U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
     if (!d_Wd || !d_bd || misaligned(d_Wd) || misaligned(d_bd)) return RNNTJ_ERR_ARG;
-    tdt_ws(p, tdt->K, o_gB, o_gE, o_dzd, ws_need);
+    tw = tdt_ws(p, tdt->K);
+    ws_need = tw.total;
   }
   if (!enc || !pred || !W_out || !b_out || !saved || !d_enc || !d_pred || !d_W_out || !d_b_out)
     return RNNTJ_ERR_ARG;
@@ -650,9 +665,13 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
     g.beta = at<double>(saved, p.o_beta);
     g.logP = logP;
     g.gcost = grad_costs;
-    g.gB = at<double>(workspace, o_gB);
-    g.gE = at<double>(workspace, o_gE);
-    g.dzd = at<float>(workspace, o_dzd);
+    g.gB = at<double>(workspace, tw.gB);
+    g.gE = at<double>(workspace, tw.gE);
+    g.dzd = at<float>(workspace, tw.dzd);
+    if (deterministic_on()) {
+      g.part_w = at<float>(workspace, tw.part_w);
+      g.part_b = at<float>(workspace, tw.part_b);
+    }
     g.d_enc = d_enc;
     g.d_pred = d_pred;
     g.d_Wd = d_Wd;
@@ -968,9 +987,7 @@ int rnnt_joint_loss_tdt_workspace_bytes(int B, int T, int U, int H, int V, int d
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
   if (U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
-  size_t a, b, c, total;
-  tdt_ws(p, K, a, b, c, total);
-  *out = pass == 0 ? p.ws_fwd : total;
+  *out = pass == 0 ? p.ws_fwd : tdt_ws(p, K).total;
   return RNNTJ_OK;
 }
 

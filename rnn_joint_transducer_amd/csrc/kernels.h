@@ -203,7 +203,14 @@ struct TdtArgs {
   float* d_pred;
   float* d_Wd;
   float* d_bd;
+  // deterministic mode (both set): the duration-head backward stores each
+  // frame block's d_W_dur / d_b_dur sums here ([blocks, H, K], [blocks, K];
+  // blocks = B ceil(T / kTdtFrames)) instead of adding them with atomics,
+  // and d_pred is formed by a pass with one writer per element
+  float* part_w;
+  float* part_b;
 };
+constexpr int kTdtFrames = 16;  // frames per block of the duration-head backward
 hipError_t launch_tdt_dur_head(const TdtArgs& a, hipStream_t st);
 hipError_t launch_tdt_lattice(const TdtArgs& a, hipStream_t st);
 hipError_t launch_tdt_post(const TdtArgs& a, hipStream_t st);

@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void tdt_post_kernel(TdtArgs a) {
 // atomic per unit and label position) and over the label positions into
 // the frames' d_enc rows (atomics at the end); d_W_dur += h dzd and
 // d_b_dur += dzd are summed over the block's cells.
-constexpr int kFrames = 16;
+constexpr int kFrames = kTdtFrames;
 constexpr int kHPer = 3;  // hidden units per thread (H <= 768)
 constexpr int kUChunk = 32;
 
@@ -396,6 +396,7 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
   const int Tl = a.Teff[b], Ul = a.Ueff[b];
   const int H = d.H;
   const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
+  const bool det = a.part_w != nullptr;
   const int t_lo = blockIdx.x * kFrames;
   if (t_lo >= Tl) return;  // uniform
   const int nt = min(kFrames, Tl - t_lo);
@@ -464,10 +465,12 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
           for (int j = 0; j < KK; ++j) dw[i][j] = fmaf(hr, z[j], dw[i][j]);
         }
       }
+      if (!det) {
 #pragma unroll
-      for (int i = 0; i < kHPer; ++i) {
-        const int k = tid + 256 * i;
-        if (k < H) atomicAdd(&a.d_pred[((size_t)b * d.U1 + u) * H + k], ap[i]);
+        for (int i = 0; i < kHPer; ++i) {
+          const int k = tid + 256 * i;
+          if (k < H) atomicAdd(&a.d_pred[((size_t)b * d.U1 + u) * H + k], ap[i]);
+        }
       }
     }
   }
@@ -478,14 +481,112 @@ __global__ __launch_bounds__(256) void dur_bwd_kernel(TdtArgs a) {
 #pragma unroll
     for (int q = 0; q < kFrames; ++q)
       if (q < nt) atomicAdd(&a.d_enc[((size_t)b * d.T + t_lo + q) * H + k], ae[q][i]);
+    const size_t blk = (size_t)b * gridDim.x + blockIdx.x;
 #pragma unroll
-    for (int j = 0; j < KK; ++j)
-      if (j < K) atomicAdd(&a.d_Wd[(size_t)k * K + j], dw[i][j]);
+    for (int j = 0; j < KK; ++j) {
+      if (det) a.part_w[(blk * H + k) * K + j] = dw[i][j];
+      else atomicAdd(&a.d_Wd[(size_t)k * K + j], dw[i][j]);
+    }
   }
   if (tid == 0) {
+    const size_t blk = (size_t)b * gridDim.x + blockIdx.x;
 #pragma unroll
-    for (int j = 0; j < KK; ++j)
-      if (j < K) atomicAdd(&a.d_bd[j], db[j]);
+    for (int j = 0; j < KK; ++j) {
+      if (det) a.part_b[blk * K + j] = db[j];
+      else atomicAdd(&a.d_bd[j], db[j]);
+    }
+  }
+}
+
+// Deterministic mode: d_pred's share of the duration head, one writer per
+// element.  Workgroup (u block, b): thread k0 owns hidden units k0, k0 + 256,
+// k0 + 512; for kUPer label positions it sums
+//   dp = (1 - h^2) sum_j W_dur[k][j] dzd(t,u,j)
+// over the frames in order and adds the sums to d_pred.
+constexpr int kUPer = 4;
+template <int KK>
+__global__ __launch_bounds__(256) void dur_pred_kernel(TdtArgs a) {
+  const Dims d = a.d;
+  const int b = blockIdx.y, tid = threadIdx.x;
+  constexpr int K = KK;
+  const int Tl = a.Teff[b], Ul = a.Ueff[b];
+  const int H = d.H;
+  const int u0 = blockIdx.x * kUPer;
+  if (Tl == 0 || u0 > Ul) return;  // uniform
+  const bool use_ep = (a.hdr[1] & kFlagEpBad) == 0;
+  float w[kHPer][KK], ap[kUPer][kHPer], p[kUPer][kHPer];
+#pragma unroll
+  for (int i = 0; i < kHPer; ++i) {
+    const int k = tid + 256 * i;
+#pragma unroll
+    for (int j = 0; j < KK; ++j) w[i][j] = k < H ? wdur(a, k, j) : 0.f;
+#pragma unroll
+    for (int q = 0; q < kUPer; ++q) {
+      const int u = min(u0 + q, Ul);
+      ap[q][i] = 0.f;
+      p[q][i] = (use_ep && k < H) ? a.Pexp[((size_t)b * d.U1 + u) * H + k] : 0.f;
+    }
+  }
+  for (int t = 0; t < Tl; ++t) {
+    float e[kHPer];
+#pragma unroll
+    for (int i = 0; i < kHPer; ++i) {
+      const int k = tid + 256 * i;
+      e[i] = (use_ep && k < H) ? a.Eexp[((size_t)b * d.T + t) * H + k] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < kUPer; ++q) {
+      const int u = u0 + q;
+      if (u > Ul) continue;  // uniform
+      float z[KK];
+      const float* zp = a.dzd + skew_idx(d, b, t, u) * K;
+#pragma unroll
+      for (int j = 0; j < KK; ++j) z[j] = zp[j];
+#pragma unroll
+      for (int i = 0; i < kHPer; ++i) {
+        const int k = tid + 256 * i;
+        if (k >= H) continue;
+        const float h = use_ep ? 1.0f - 2.0f * __builtin_amdgcn_rcpf(1.0f + e[i] * p[q][i])
+                               : h_of(a, b, t, u, k, false);
+        float sacc = 0.f;
+#pragma unroll
+        for (int j = 0; j < KK; ++j) sacc = fmaf(w[i][j], z[j], sacc);
+        ap[q][i] += (1.0f - h * h) * sacc;
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kUPer; ++q) {
+    const int u = u0 + q;
+    if (u > Ul) continue;
+#pragma unroll
+    for (int i = 0; i < kHPer; ++i) {
+      const int k = tid + 256 * i;
+      if (k < H) a.d_pred[((size_t)b * d.U1 + u) * H + k] += ap[q][i];
+    }
+  }
+}
+
+// Deterministic mode: d_W_dur and d_b_dur from the frame blocks' partial
+// sums, added in block order (blocks past an utterance's length hold none).
+__global__ __launch_bounds__(256) void dur_reduce_kernel(TdtArgs a, int nfb) {
+  const int H = a.d.H, K = a.K;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < H * K) {
+    float s = 0.f;
+    for (int b = 0; b < a.d.B; ++b) {
+      const int nb = (a.Teff[b] + kFrames - 1) / kFrames;
+      for (int f = 0; f < nb; ++f) s += a.part_w[((size_t)b * nfb + f) * H * K + i];
+    }
+    a.d_Wd[i] += s;
+  }
+  if (i < K) {
+    float s = 0.f;
+    for (int b = 0; b < a.d.B; ++b) {
+      const int nb = (a.Teff[b] + kFrames - 1) / kFrames;
+      for (int f = 0; f < nb; ++f) s += a.part_b[((size_t)b * nfb + f) * K + i];
+    }
+    a.d_bd[i] += s;
   }
 }
 
@@ -541,7 +642,8 @@ hipError_t launch_tdt_post(const TdtArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_tdt_dur_bwd(const TdtArgs& a, hipStream_t st) {
-  const dim3 g((a.d.T + kFrames - 1) / kFrames, a.d.B), blk(256);
+  const int nfb = (a.d.T + kFrames - 1) / kFrames;
+  const dim3 g(nfb, a.d.B), blk(256);
   switch (a.K) {
     case 1: hipLaunchKernelGGL(dur_bwd_kernel<1>, g, blk, 0, st, a); break;
     case 2: hipLaunchKernelGGL(dur_bwd_kernel<2>, g, blk, 0, st, a); break;
@@ -553,6 +655,21 @@ hipError_t launch_tdt_dur_bwd(const TdtArgs& a, hipStream_t st) {
     case 8: hipLaunchKernelGGL(dur_bwd_kernel<8>, g, blk, 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
+  if (!a.part_w) return hipGetLastError();
+  // deterministic mode: d_pred by its own pass, then the ordered reduction
+  const dim3 gp((a.d.U1 + kUPer - 1) / kUPer, a.d.B);
+  switch (a.K) {
+    case 1: hipLaunchKernelGGL(dur_pred_kernel<1>, gp, blk, 0, st, a); break;
+    case 2: hipLaunchKernelGGL(dur_pred_kernel<2>, gp, blk, 0, st, a); break;
+    case 3: hipLaunchKernelGGL(dur_pred_kernel<3>, gp, blk, 0, st, a); break;
+    case 4: hipLaunchKernelGGL(dur_pred_kernel<4>, gp, blk, 0, st, a); break;
+    case 5: hipLaunchKernelGGL(dur_pred_kernel<5>, gp, blk, 0, st, a); break;
+    case 6: hipLaunchKernelGGL(dur_pred_kernel<6>, gp, blk, 0, st, a); break;
+    case 7: hipLaunchKernelGGL(dur_pred_kernel<7>, gp, blk, 0, st, a); break;
+    case 8: hipLaunchKernelGGL(dur_pred_kernel<8>, gp, blk, 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipLaunchKernelGGL(dur_reduce_kernel, dim3((a.d.H * a.K + 255) / 256), blk, 0, st, a, nfb);
   return hipGetLastError();
 }
 

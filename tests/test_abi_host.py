@@ -275,12 +275,21 @@ def test_flags_roundtrip_and_environment():
         _lib.set_flags(0)
         assert _lib.get_flags() == 0
         plain = _ws(8, 200, 50, 256, 512, 0, 64, 64, 128)[1]
+        out = ctypes.c_size_t(0)
+        assert lib.rnnt_joint_loss_tdt_workspace_bytes(8, 200, 50, 256, 512, 0, 64, 64, 128, 5, 1,
+                                                       ctypes.byref(out)) == 0
+        tdt_plain = out.value
         _lib.set_flags(_lib.FLAG_DETERMINISTIC)
         assert _lib.get_flags() == _lib.FLAG_DETERMINISTIC
         det = _ws(8, 200, 50, 256, 512, 0, 64, 64, 128)[1]
         # per-tile d_enc / d_pred rows of a 64 x 64 chunk (8 x 4 x 8 tiles) and
         # at least one split-K part of d_W_out
         assert det >= plain + 4 * 256 * 24 * 256 + 4 * 256 * 512
+        # token-and-duration: also each 16-frame block's d_W_dur / d_b_dur sums
+        # (8 utterances x 13 blocks)
+        assert lib.rnnt_joint_loss_tdt_workspace_bytes(8, 200, 50, 256, 512, 0, 64, 64, 128, 5, 1,
+                                                       ctypes.byref(out)) == 0
+        assert out.value >= tdt_plain + (det - plain) + 4 * 8 * 13 * 256 * 5
         assert lib.rnnt_joint_loss_set_flags(4) == 1
         assert _lib.get_flags() == _lib.FLAG_DETERMINISTIC
     finally:

@@ -150,6 +150,30 @@ def test_tdt_fp32_wide_hidden(tiles):
     assert len(_compare(inp, g, refs)) == inp.B
 
 
+@pytest.mark.parametrize("tiles", [(16, 8, 0), (0, 0, 0)])
+def test_tdt_deterministic_mode(tiles):
+    """Deterministic mode with the duration head: three runs bitwise equal in
+    every output (the duration head's d_pred by its own pass, d_W_dur /
+    d_b_dur from per-block sums added in order), and the oracle's values."""
+    from rnn_joint_transducer_amd import _lib
+    inp = make_inputs(4, 40, 9, 64, 40, dtype="fp32", sigma=0.3, seed=43, t_range=(20, 40),
+                      u_range=(2, 9))
+    head = make_duration_head(inp, (0, 1, 2, 3), seed=6, sigma=0.3)
+    gcs = [1.0, -0.5, 2.0, 0.25]
+    old = _lib.get_flags()
+    try:
+        _lib.set_flags(_lib.FLAG_DETERMINISTIC)
+        print(f"[tdt deterministic tiles={tiles}]", flush=True)
+        runs = [_run(inp, head, tiles, gcs=gcs) for _ in range(3)]
+    finally:
+        _lib.set_flags(old)
+    for g in runs[1:]:
+        for k in ("costs", "dEnc", "dPred", "dW", "db", "dWd", "dbd"):
+            assert np.array_equal(g[k], runs[0][k]), k
+    refs = tdt_oracle(inp, head, range(inp.B), WORKERS, grad_costs=gcs)
+    assert len(_compare(inp, runs[0], refs)) == inp.B
+
+
 def test_tdt_medium():
     """Medium workload (bf16, H = 640, V = 1024), durations 0..4: every cost,
     one utterance's gradients, the weight gradients of a two-utterance
