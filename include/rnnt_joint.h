@@ -380,7 +380,10 @@ int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error)
  * rnnt_joint_proj_bwd: from dy[M,N] (float32) writes dx[M,K] = dy @ W^T,
  * dW[K,N] = x^T @ dy and db[N] = sum of the rows of dy, all float32 and
  * overwritten (dx and db may be NULL to skip them).  x and W as in the
- * forward; the outputs must not overlap each other or the inputs.
+ * forward; the outputs must not overlap each other or the inputs.  In
+ * deterministic mode the row splits of dW and db run one after another, so
+ * each element's partial sums are added in a fixed order (bitwise
+ * repeatable; fewer workgroups at a time).
  *
  * Both: x, W, y / dy, dx, dW 16-byte aligned; K and N multiples of 16 and at
  * most 65536, M >= 1 (else RNNTJ_ERR_UNSUPPORTED / RNNTJ_ERR_ARG, returned

@@ -1083,7 +1083,8 @@ int rnnt_joint_proj_bwd(const void* x, const void* W, int dtype, int M, int K, i
                 hipSuccess)
     return RNNTJ_ERR_HIP;
   if (timed("proj_dw", st, [&] {
-        return launch_proj_dw(x, dy, bf16, M, K, N, dW, db, device_cu_count(), st);
+        return launch_proj_dw(x, dy, bf16, M, K, N, dW, db, device_cu_count(), deterministic_on(),
+                              st);
       }) != hipSuccess)
     return RNNTJ_ERR_HIP;
   return RNNTJ_OK;

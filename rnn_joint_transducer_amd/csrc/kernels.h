@@ -315,6 +315,6 @@ hipError_t launch_proj_fwd(const void* x, const void* W, const void* b, bool bf1
 hipError_t launch_proj_dx(const float* dy, const void* W, bool bf16, int M, int K, int N,
                           float* dx, hipStream_t st);
 hipError_t launch_proj_dw(const void* x, const float* dy, bool bf16, int M, int K, int N,
-                          float* dW, float* db, int cus, hipStream_t st);
+                          float* dW, float* db, int cus, bool in_order, hipStream_t st);
 
 }  // namespace rnntj

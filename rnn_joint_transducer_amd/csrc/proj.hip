@@ -72,6 +72,7 @@ struct GemmArgs {
   long long ldc;
   int M, N, K, kchunk;
   float* colsum;
+  int zbase;  // k split of blockIdx.z == 0 (launches of one split at a time)
 };
 
 template <typename TA, typename TB, bool AK, bool BJ, int OUT, typename TO>
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const TB* __restrict__ Bm = static_cast<const TB*>(g.b);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int i0 = blockIdx.x * kPT, j0 = blockIdx.y * kPT;
-  const int kb = blockIdx.z * g.kchunk;
+  const int kb = (g.zbase + (int)blockIdx.z) * g.kchunk;
   const int ke = min(g.K, kb + g.kchunk);
   // this thread's 8-element piece of the A and B tiles
   const int ai = AK ? tid >> 2 : (tid & 7) * 8, ak = AK ? (tid & 3) * 8 : tid >> 3;
@@ -228,10 +229,20 @@ __global__ __launch_bounds__(256) void proj_fwd_bf16_kernel(GemmArgs g) {
   }
 }
 
+// (in_order: the k splits as consecutive launches, so that the atomic sums
+// of each output element come in split order)
 template <typename TA, typename TB, bool AK, bool BJ, int OUT, typename TO>
-hipError_t gemm(const GemmArgs& g, int splits, hipStream_t st) {
-  const dim3 grid((g.M + kPT - 1) / kPT, (g.N + kPT - 1) / kPT, splits);
-  hipLaunchKernelGGL((gemm_kernel<TA, TB, AK, BJ, OUT, TO>), grid, dim3(256), 0, st, g);
+hipError_t gemm(const GemmArgs& g, int splits, hipStream_t st, bool in_order = false) {
+  const dim3 grid((g.M + kPT - 1) / kPT, (g.N + kPT - 1) / kPT, in_order ? 1 : splits);
+  if (!in_order) {
+    hipLaunchKernelGGL((gemm_kernel<TA, TB, AK, BJ, OUT, TO>), grid, dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
+  GemmArgs gs = g;
+  for (int z = 0; z < splits; ++z) {
+    gs.zbase = z;
+    hipLaunchKernelGGL((gemm_kernel<TA, TB, AK, BJ, OUT, TO>), grid, dim3(256), 0, st, gs);
+  }
   return hipGetLastError();
 }
 
@@ -257,10 +268,11 @@ hipError_t launch_proj_dx(const float* dy, const void* W, bool bf16, int M, int 
 }
 
 hipError_t launch_proj_dw(const void* x, const float* dy, bool bf16, int M, int K, int N,
-                          float* dW, float* db, int cus, hipStream_t st) {
+                          float* dW, float* db, int cus, bool in_order, hipStream_t st) {
   // dW[K,N] += x[M,K]^T dy[M,N] and db[N] += column sums of dy: k runs over
   // the M rows, split so that the grid holds about four workgroups per
-  // compute unit
+  // compute unit (in_order: the splits run one launch after another, so the
+  // atomic sums of each element come in a fixed order)
   const int tiles = ((K + kPT - 1) / kPT) * ((N + kPT - 1) / kPT);
   int splits = (4 * cus + tiles - 1) / tiles;
   const int max_splits = (M + kPK - 1) / kPK;
@@ -268,9 +280,9 @@ hipError_t launch_proj_dw(const void* x, const float* dy, bool bf16, int M, int 
   int kchunk = (M + splits - 1) / splits;
   kchunk = (kchunk + kPK - 1) / kPK * kPK;
   splits = (M + kchunk - 1) / kchunk;
-  GemmArgs g{x, K, dy, N, nullptr, dW, N, K, N, M, kchunk, db};
-  if (bf16) return gemm<uint16_t, float, false, true, 1, float>(g, splits, st);
-  return gemm<float, float, false, true, 1, float>(g, splits, st);
+  GemmArgs g{x, K, dy, N, nullptr, dW, N, K, N, M, kchunk, db, 0};
+  if (bf16) return gemm<uint16_t, float, false, true, 1, float>(g, splits, st, in_order);
+  return gemm<float, float, false, true, 1, float>(g, splits, st, in_order);
 }
 
 

@@ -184,3 +184,33 @@ def test_projection_without_bias_and_skipped_outputs(dtype):
     assert dx is None and db is None
     _, rdW, _ = proj.linear_grads(x64, W64, dy.astype(np.float64))
     assert float(np.max(np.abs(_np(dW) - rdW))) <= FP32_GRAD_ABS
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_projection_gradients_deterministic_mode(dtype):
+    """Deterministic mode: the row splits of the projection gradients run
+    one after another, so three runs are bitwise equal, and still match
+    float64 to the same bound."""
+    import rnn_joint_transducer_amd as rj
+    from rnn_joint_transducer_amd import _lib
+    from synth import _cast
+    rng = np.random.default_rng(93)
+    M, K, N = 16 * 101, 640, 640
+    x_s, x64 = _cast(rng.normal(0, 0.5, (M, K)), dtype)
+    W_s, W64 = _cast(rng.normal(0, 1 / np.sqrt(K), (K, N)), dtype)
+    dy = rng.normal(0, 1.0, (M, N)).astype(np.float32)
+    old = _lib.get_flags()
+    try:
+        _lib.set_flags(_lib.FLAG_DETERMINISTIC)
+        print(f"[proj deterministic {dtype}]", flush=True)
+        runs = [[_np(t) for t in rj.rnnt_joint_proj_bwd(_dev(x_s, dtype), _dev(W_s, dtype),
+                                                        _dev(dy, "fp32"))] for _ in range(3)]
+    finally:
+        _lib.set_flags(old)
+    for r in runs[1:]:
+        for a, b in zip(r, runs[0]):
+            assert np.array_equal(a, b)
+    rdx, rdW, rdb = proj.linear_grads(x64, W64, dy.astype(np.float64))
+    for name, gv, rv in zip(("dx", "dW", "db"), runs[0], (rdx, rdW, rdb)):
+        err = float(np.max(np.abs(gv - rv)))
+        assert err <= FP32_GRAD_ABS * max(1.0, float(np.max(np.abs(rv))) / 100), (name, err)
