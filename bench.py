@@ -70,6 +70,10 @@ def parse():
     ap.add_argument("--tile-u", type=int, default=None)
     ap.add_argument("--tile-v", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--min-workspace", action="store_true",
+                    help="give the backward its least workspace (one chunk buffer pair: every "
+                         "kernel in order on one stream) instead of the size for the "
+                         "overlapped chunk schedule")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--sweep", action="store_true",
@@ -236,7 +240,7 @@ def tile_sweep(args, rj, torch, tensors, inp, dev, dc):
                 saved = torch.empty(rj.rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tt, tu, tv),
                                     dtype=torch.uint8, device=dev)
                 ws = torch.empty(rj.rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tt, tu,
-                                                                     tv, 1),
+                                                                     tv, ws_pass(args)),
                                  dtype=torch.uint8, device=dev)
 
                 def step():
@@ -283,6 +287,11 @@ def tile_sweep(args, rj, torch, tensors, inp, dev, dc):
     print(json.dumps({"metric": METRIC, "workload": args.workload, "steps": args.steps,
                       "warmup": max(1, args.warmup), "data": "synthetic", "sweep": rows,
                       "frontier": frontier, "lowest_memory_within_95pct": pick}), flush=True)
+
+
+def ws_pass(args):
+    """Backward workspace query: 1 = the overlapped chunk schedule, 2 = the least."""
+    return 2 if args.min_workspace else 1
 
 
 def main():
@@ -337,7 +346,7 @@ def main():
     base_mem = torch.cuda.memory_allocated(dev)
     saved = torch.empty(rj.rnnt_joint_loss_saved_bytes(B, T, U, H, V, dc, tt, tu, tv),
                         dtype=torch.uint8, device=dev)
-    wsb = rj.rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tt, tu, tv, 1)
+    wsb = rj.rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tt, tu, tv, ws_pass(args))
     ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
     costs = torch.empty(B, dtype=torch.float32, device=dev)
     grads = (torch.empty(B, T, H, device=dev), torch.empty(B, U + 1, H, device=dev),
@@ -355,7 +364,8 @@ def main():
                                                                ctypes.byref(sz)), "tdt_saved")
         saved = torch.empty(sz.value, dtype=torch.uint8, device=dev)
         _lib.check(_lib.load().rnnt_joint_loss_tdt_workspace_bytes(B, T, U, H, V, dc, tt, tu, tv,
-                                                                   K, 1, ctypes.byref(sz)),
+                                                                   K, ws_pass(args),
+                                                                   ctypes.byref(sz)),
                    "tdt_ws")
         ws = torch.empty(sz.value, dtype=torch.uint8, device=dev)
     if args.pruned:
@@ -489,6 +499,19 @@ def main():
 
     mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
     roof["traffic"] = measured_traffic(args.workload, dom, mode, args.criterion)
+    # the whole step against the matrix peak: the joint projection's
+    # algorithmic flops (forward 2HV, dh 2HV, dW 2HV per cell) and those the
+    # kernels execute (the tiled backward recomputes the forward's 2HV), over
+    # the step time (kernels on the side stream overlap the others, so the
+    # per-kernel rates above do not add up to this)
+    n_mm = sum(1 for k in ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
+               if k in kernels)
+    useful = 6.0 * H * V * work_cells
+    executed = 2.0 * H * V * work_cells * n_mm
+    step_mfma = {"useful_tflops": useful / (ms / 1e3) / 1e12,
+                 "executed_tflops": executed / (ms / 1e3) / 1e12, "peak": PEAK_TFLOPS[dt]}
+    step_mfma["useful_frac"] = step_mfma["useful_tflops"] / PEAK_TFLOPS[dt]
+    step_mfma["executed_frac"] = step_mfma["executed_tflops"] / PEAK_TFLOPS[dt]
     # the lattice pass against HBM peak (32 B per valid cell: the alpha and beta
     # chains each read LB, LE and write one float64) and per anti-diagonal step
     lat = None
@@ -515,9 +538,11 @@ def main():
                    "pruned_S": args.pruned or None, "band_cells": band_cells,
                    "tdt_durations": None if head is None else list(head.durations),
                    "tile_t": tt, "tile_u": tu, "tile_v": tv,
+                   "workspace": "least" if args.min_workspace else "overlapped",
                    "valid_cells": valid, "valid_cells_per_s": valid / (ms / 1e3),
                    "peak_gb": round(peak_gb, 3), "peak_gb_above_inputs": round(extra_gb, 3)},
         "roofline": roof,
+        "step_mfma": step_mfma,
         "lattice": lat,
         "kernels": {k: {kk: round(vv, 6) for kk, vv in v.items()} for k, v in kernels.items()},
         "cpu_baseline": cpu,

@@ -152,14 +152,24 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype,
 
 /*
  * Bytes of scratch `workspace` needed by the forward (pass = 0) or the
- * backward (pass = 1).  The forward needs none.  The backward needs a float64
- * accumulator for d_b_out [V] and, in the tiled mode, the joint activations
- * h of one lattice chunk [B, tile_t, tile_u, H] in dtype (untiled: none,
- * they are in `saved`), that chunk's logit gradients of one vocabulary part
- * [B, tile_t, tile_u, min(tile_v, V)] (tile_v = 0: V) in dtype plus the
- * active-tile list of every chunk (int32, one word per 16 x 8 tile); in the
- * deterministic mode (rnnt_joint_loss_set_flags) also its partial-sum
- * buffers.  Writes *out; returns a status code.
+ * backward (pass = 1: the size for the fastest schedule; pass = 2: the
+ * least the backward accepts).  The forward needs none.  The backward needs
+ * a float64 accumulator for d_b_out [V] and, in the tiled mode, the joint
+ * activations h of one lattice chunk [B, tile_t, tile_u, H] in dtype
+ * (untiled: none, they are in `saved`), that chunk's logit gradients of one
+ * vocabulary part [B, tile_t, tile_u, min(tile_v, V)] (tile_v = 0: V) in
+ * dtype plus the active-tile list of every chunk (int32, one word per
+ * 16 x 8 tile); in the deterministic mode (rnnt_joint_loss_set_flags) also
+ * its partial-sum buffers.  That is pass 2.  Pass 1 adds, in the tiled mode,
+ * a second pair of chunk buffers: given that much, the tiled backward
+ * alternates the pairs between consecutive chunks and runs each chunk's dW
+ * GEMM on a library-owned side stream of the same device (created once,
+ * default priority), so that it overlaps that chunk's dh GEMM and the next
+ * chunk's logit gradients; events join the side stream back to `stream`
+ * before the call returns, so the results are ordered on `stream` as
+ * always.  Given less than pass 1 (and at least pass 2), every kernel runs
+ * on `stream` in order.  The results are the same either way.  Writes *out;
+ * returns a status code.
  */
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype,
                                     int tile_t, int tile_u, int tile_v, int pass,
@@ -231,12 +241,13 @@ int rnnt_joint_loss_bwd(const void* enc, const void* pred, const void* W_out,
  * backward's scratch is instead a static device array of
  * RNNTJ_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
  * the process ends.  Sizes whose backward workspace
- * (rnnt_joint_loss_workspace_bytes, pass 1) exceeds it return
+ * (rnnt_joint_loss_workspace_bytes, pass 2) exceeds it return
  * RNNTJ_ERR_WORKSPACE before anything is enqueued: this covers the untiled
  * mode at every accepted size and the tiled mode while one chunk's logit
  * gradients and activations fit.  `stream` must belong to the calling
  * thread's current device (else RNNTJ_ERR_ARG).  No hipMalloc / hipFree or
- * allocating library call is made.  Every call on one GPU shares that GPU's
+ * allocating library call is made, and every kernel runs on `stream` (no
+ * side stream).  Every call on one GPU shares that GPU's
  * array, which keeps the last call's contents (the backward clears what it
  * needs zeroed itself): calls that overlap on one GPU race, so serialise
  * them (for example, issue them on one stream).
@@ -318,7 +329,8 @@ int rnnt_joint_loss_pruned_fwd(const void* enc, const void* pred, const void* W_
  *
  * Buffers: `saved` of rnnt_joint_loss_tdt_saved_bytes bytes (the plain state
  * plus the duration log-probabilities, float32 [cells, K]); the backward's
- * workspace of rnnt_joint_loss_tdt_workspace_bytes (pass 1) bytes (the plain
+ * workspace of rnnt_joint_loss_tdt_workspace_bytes (pass 1, or at least
+ * pass 2, as for rnnt_joint_loss_workspace_bytes) bytes (the plain
  * one plus the summed step posteriors, float64, and the duration-logit
  * gradients, float32; in deterministic mode also each 16-frame block's
  * d_W_dur / d_b_dur sums, so query it with the mode already set); the

@@ -217,13 +217,15 @@ def rnnt_joint_loss_tdt_bwd(enc, pred, W_out, b_out, W_dur, b_dur, labels, T_len
     if saved.dtype != torch.uint8 or saved.device != dev or saved.numel() < need.value:
         raise ValueError(f"saved: expected a uint8 buffer of at least {need.value} bytes on {dev}")
     ws = ctypes.c_size_t(0)
-    check(load().rnnt_joint_loss_tdt_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v,
-                                                     K, 1, ctypes.byref(ws)),
-          "rnnt_joint_loss_tdt_workspace_bytes")
+    least = ctypes.c_size_t(0)
+    for pass_, out_ in ((1, ws), (2, least)):
+        check(load().rnnt_joint_loss_tdt_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u,
+                                                         tile_v, K, pass_, ctypes.byref(out_)),
+              "rnnt_joint_loss_tdt_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(ws.value, dtype=torch.uint8, device=dev)
-    elif workspace.numel() < ws.value:
-        raise ValueError(f"workspace too small ({workspace.numel()} < {ws.value})")
+    elif workspace.numel() < least.value:
+        raise ValueError(f"workspace too small ({workspace.numel()} < {least.value})")
     if grad_costs is not None:
         if grad_costs.dtype != torch.float32 or tuple(grad_costs.shape) != (B,):
             raise ValueError("grad_costs must be float32 [B]")
@@ -258,11 +260,14 @@ def rnnt_joint_loss_bwd(enc, pred, W_out, b_out, labels, T_lens, U_lens, saved, 
         raise ValueError(f"saved: expected a uint8 buffer of at least {need} bytes on {dev} "
                          f"(the forward's state for these sizes and tiles), got "
                          f"{saved.numel()} {saved.dtype} on {saved.device}")
-    ws = rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, 1)
     if workspace is None:
+        # the size for the overlapped chunk schedule (pass 1)
+        ws = rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, 1)
         workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
-    elif workspace.numel() < ws:
-        raise ValueError(f"workspace too small ({workspace.numel()} < {ws})")
+    else:
+        least = rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tile_t, tile_u, tile_v, 2)
+        if workspace.numel() < least:
+            raise ValueError(f"workspace too small ({workspace.numel()} < {least})")
     if out is None:
         out = (torch.empty(B, T, H, dtype=torch.float32, device=dev),
                torch.empty(B, U + 1, H, dtype=torch.float32, device=dev),

@@ -70,6 +70,14 @@ struct Plan {
   size_t o_ws_encp, o_ws_predp, o_ws_wpart, o_ws_bpart, ws_bwd_det;
   int kparts_det;
   size_t bwd_ws() const { return deterministic_on() ? ws_bwd_det : ws_bwd; }
+  // tiled: bytes of a second chunk buffer pair (logit gradients, h rows),
+  // placed after the rest of a backward workspace of `need` bytes; with it
+  // consecutive chunks alternate buffers and a chunk's dW overlaps the next
+  // chunk's logit gradients
+  size_t ws_g = 0, ws_h = 0;
+  size_t overlap_bytes(size_t need) const {
+    return untiled ? need : align_up(need) + ws_g + ws_h;
+  }
 };
 
 int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile_u, int tile_v,
@@ -170,9 +178,11 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.cap_chunk = B * (q.CT / kTileT) * (q.CU / kTileU);
   q.o_ws_db = 0;
   q.o_ws_g = align_up(8 * (size_t)V);
-  q.o_ws_h = q.o_ws_g + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * q.Vp));
+  q.ws_g = q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * q.Vp);
+  q.ws_h = q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * H);
+  q.o_ws_h = q.o_ws_g + q.ws_g;
   // (untiled: the h rows are part of the saved state instead)
-  q.o_ws_tiles = q.o_ws_h + (q.untiled ? 0 : align_up(q.elem * (size_t)B * q.CT * q.CU * H));
+  q.o_ws_tiles = q.o_ws_h + q.ws_h;
   q.o_ws_tcount = q.o_ws_tiles + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks * q.cap_chunk));
   q.ws_bwd = q.o_ws_tcount + (q.untiled ? 0 : align_up(4 * (size_t)q.n_chunks));
   // deterministic reductions: per-tile d_enc / d_pred rows of one chunk and
@@ -355,6 +365,42 @@ int scratch_for(hipStream_t st, void** out) {
   }
   *out = g_scratch_ptr[dev];
   return RNNTJ_OK;
+}
+
+// ---- side stream of the tiled backward, one per device (default priority,
+// not blocking on the null stream).  A chunk's dW GEMM runs on it, so that it
+// overlaps that chunk's dh GEMM and the next chunk's logit gradients; events
+// fork it from and join it to the caller's stream.  dw_done[k & 1] marks the
+// end of the dW of vocabulary pass k.  The lock is held while a backward
+// enqueues its chunks, so that two host threads never re-record these events
+// at once.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t jg_done[2] = {}, dw_done[2] = {};
+  std::mutex mu;
+  bool tried = false;
+};
+SideStream g_side[kMaxDevices];
+
+// The side stream of the current device (NULL if it cannot be created: the
+// backward then runs its chunks on the caller's stream alone).
+SideStream* side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& s = g_side[dev];
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!s.tried) {
+    s.tried = true;
+    bool ok = hipStreamCreateWithFlags(&s.s, hipStreamNonBlocking) == hipSuccess;
+    for (int i = 0; i < 2 && ok; ++i)
+      ok = hipEventCreateWithFlags(&s.jg_done[i], hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&s.dw_done[i], hipEventDisableTiming) == hipSuccess;
+    if (!ok) {
+      (void)hipGetLastError();
+      s.s = nullptr;
+    }
+  }
+  return s.s ? &s : nullptr;
 }
 
 // Debug mode: wait for the call's kernels and report a nonzero data-error
@@ -569,7 +615,7 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
              int tile_u, int tile_v, const float* grad_costs, void* saved, float* d_enc,
              float* d_pred, float* d_W_out, float* d_b_out, void* workspace,
              size_t workspace_bytes, void* stream, const TdtIn* tdt = nullptr,
-             float* d_Wd = nullptr, float* d_bd = nullptr) {
+             float* d_Wd = nullptr, float* d_bd = nullptr, bool side_ok = true) {
   Plan p;
   int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
@@ -742,9 +788,9 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
       return launch_dh_reduce(h, p.untiled ? p.cap_all : p.cap_chunk, st);
     });
   };
-  auto reduce_dw = [&]() -> hipError_t {
+  auto reduce_dw = [&](hipStream_t s) -> hipError_t {
     if (!det) return hipSuccess;
-    return timed("dw_reduce", st, [&] { return launch_dw_reduce(w, st); });
+    return timed("dw_reduce", s, [&] { return launch_dw_reduce(w, s); });
   };
   auto finalize = [&](int32_t* mark) {
     if (tdt) {
@@ -769,17 +815,17 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
     h.ct0 = 0; h.cu0 = 0; h.CT = p.d.Tpad; h.CU = p.d.U1pad;
     h.tiles = a.tiles;
     h.tile_count = a.tile_count;
-    if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
-      return RNNTJ_ERR_HIP;
     w.g = z;
     w.h = at<char>(saved, p.o_h);  // written by the forward
     w.ct0 = 0; w.cu0 = 0; w.CT = p.d.Tpad; w.CU = p.d.U1pad;
     w.tiles = a.tiles;
     w.tile_count = a.tile_count;
     w.kparts = kparts_for(p.cap_all);
+    if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_all, st); })) != hipSuccess)
+      return RNNTJ_ERR_HIP;
     if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
       return RNNTJ_ERR_HIP;
-    if (reduce_dh() != hipSuccess || reduce_dw() != hipSuccess) return RNNTJ_ERR_HIP;
+    if (reduce_dh() != hipSuccess || reduce_dw(st) != hipSuccess) return RNNTJ_ERR_HIP;
     if (finalize(a.hdr) != hipSuccess) return RNNTJ_ERR_HIP;
     return debug_data_check(hdr, st);
   }
@@ -802,7 +848,34 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
                                  st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
-  int chunk = 0;
+  // Chunk schedule.  With room for a second buffer pair after the workspace
+  // proper, vocabulary pass k (one chunk's vocabulary part) writes buffer
+  // pair k & 1 (the h rows: pair c & 1 of its chunk c) and its dW runs on the
+  // side stream: it overlaps the pass's dh and the next pass's logit
+  // gradients, and pass k + 2 first waits for it, since it overwrites what
+  // that dW reads.  Otherwise every kernel runs in order on the caller's
+  // stream over one buffer pair.
+  SideStream* ss = nullptr;
+  std::unique_lock<std::mutex> side_lk;
+  void* gbuf[2] = {gchunk, gchunk};
+  void* hbuf[2] = {hchunk, hchunk};
+  if (side_ok && workspace_bytes >= p.overlap_bytes(ws_need) && p.n_chunks * ((V + p.Vp - 1) / p.Vp) > 1 &&
+      (ss = side_stream()) != nullptr) {
+    side_lk = std::unique_lock<std::mutex>(ss->mu);
+    char* second = at<char>(workspace, align_up(ws_need));
+    gbuf[1] = second;
+    hbuf[1] = second + p.ws_g;
+  }
+  hipStream_t sw = ss ? ss->s : st;  // stream of the dW GEMMs
+  int chunk = 0, pass = 0;
+  // on an error after the fork, the caller's stream still waits for the dW
+  // GEMMs already enqueued on the side stream
+  int joined_to = -1;  // last pass whose dW end was recorded
+  auto fail = [&](const char* what, hipError_t err) {
+    if (what) note_error(what, err);
+    if (ss && joined_to >= 0) (void)hipStreamWaitEvent(st, ss->dw_done[joined_to & 1], 0);
+    return RNNTJ_ERR_HIP;
+  };
   for (int ct0 = 0; ct0 < p.d.Tpad; ct0 += p.CT) {
     for (int cu0 = 0; cu0 < p.d.U1pad; cu0 += p.CU, ++chunk) {
       a.ct0 = ct0;
@@ -811,15 +884,13 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
       a.CU = p.CU;
       a.n_tu = p.CU / kTileU;
       a.vsplit = vsplit;
-      a.gout = gchunk;
-      a.hout = hchunk;
+      a.hout = hbuf[chunk & 1];
       a.tiles = ctiles + (size_t)chunk * p.cap_chunk;
       a.tile_count = ccount + chunk;
-      h.g = gchunk;
       h.ct0 = ct0; h.cu0 = cu0; h.CT = p.CT; h.CU = p.CU;
       h.tiles = a.tiles;
       h.tile_count = a.tile_count;
-      w.g = gchunk;
+      w.h = hbuf[chunk & 1];
       w.ct0 = ct0; w.cu0 = cu0; w.CT = p.CT; w.CU = p.CU;
       w.tiles = a.tiles;
       w.tile_count = a.tile_count;
@@ -827,25 +898,44 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
       // the chunk's vocabulary in parts of Vp columns: the logit gradients
       // of one part, that part's share of dh (linear in dz, so the parts'
       // d_enc / d_pred contributions add) and its columns of dW
-      for (int v0 = 0; v0 < V; v0 += p.Vp) {
+      for (int v0 = 0; v0 < V; v0 += p.Vp, ++pass) {
         const int vw = V - v0 < p.Vp ? V - v0 : p.Vp;
+        void* g = gbuf[pass & 1];
+        a.gout = g;
+        h.g = g;
+        w.g = g;
         a.gv0 = v0; a.gvw = vw; a.gld = p.Vp;
         h.v0 = v0; h.vw = vw; h.ldg = p.Vp;
         w.v0 = v0; w.vw = vw; w.ldg = p.Vp;
+        // buffer pair pass & 1 (and the h rows of chunk pair chunk & 1, last
+        // read by a dW at or before pass - 2) are free once the dW of pass - 2 is done
+        if (ss && pass >= 2 && (e = hipStreamWaitEvent(st, ss->dw_done[pass & 1], 0)) != hipSuccess)
+          return fail("stream wait", e);
         if ((e = timed("joint_grad", st, [&] {
                return launch_joint_tile(a, kGrad, p.bf16, p.cap_chunk * vsplit, st);
              })) != hipSuccess)
-          return RNNTJ_ERR_HIP;
+          return fail(nullptr, e);
+        if (ss && ((e = hipEventRecord(ss->jg_done[pass & 1], st)) != hipSuccess ||
+                   (e = hipStreamWaitEvent(sw, ss->jg_done[pass & 1], 0)) != hipSuccess))
+          return fail("stream fork", e);
         if ((e = timed("dh", st, [&] { return launch_dh(h, p.bf16, p.cap_chunk, st); })) !=
             hipSuccess)
-          return RNNTJ_ERR_HIP;
-        if (reduce_dh() != hipSuccess) return RNNTJ_ERR_HIP;
-        if ((e = timed("dw", st, [&] { return launch_dw(w, p.bf16, st); })) != hipSuccess)
-          return RNNTJ_ERR_HIP;
-        if (reduce_dw() != hipSuccess) return RNNTJ_ERR_HIP;
+          return fail(nullptr, e);
+        if (reduce_dh() != hipSuccess) return fail(nullptr, hipSuccess);
+        if ((e = timed("dw", sw, [&] { return launch_dw(w, p.bf16, sw); })) != hipSuccess)
+          return fail(nullptr, e);
+        if (reduce_dw(sw) != hipSuccess) return fail(nullptr, hipSuccess);
+        if (ss) {
+          if ((e = hipEventRecord(ss->dw_done[pass & 1], sw)) != hipSuccess)
+            return fail("stream event", e);
+          joined_to = pass;
+        }
       }
     }
   }
+  // join: the caller's stream waits for the last dW (the side stream runs in order)
+  if (ss && joined_to >= 0 && (e = hipStreamWaitEvent(st, ss->dw_done[joined_to & 1], 0)) != hipSuccess)
+    return note_error("stream join", e), RNNTJ_ERR_HIP;
   if (finalize(nullptr) != hipSuccess) return RNNTJ_ERR_HIP;
   return debug_data_check(hdr, st);
 }
@@ -888,11 +978,11 @@ int rnnt_joint_loss_saved_bytes(int B, int T, int U, int H, int V, int dtype, in
 
 int rnnt_joint_loss_workspace_bytes(int B, int T, int U, int H, int V, int dtype, int tile_t,
                                     int tile_u, int tile_v, int pass, size_t* out) {
-  if (!out || (pass != 0 && pass != 1)) return RNNTJ_ERR_ARG;
+  if (!out || pass < 0 || pass > 2) return RNNTJ_ERR_ARG;
   Plan p;
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
-  *out = pass == 0 ? p.ws_fwd : p.bwd_ws();
+  *out = pass == 0 ? p.ws_fwd : pass == 1 ? p.overlap_bytes(p.bwd_ws()) : p.bwd_ws();
   return RNNTJ_OK;
 }
 
@@ -982,12 +1072,13 @@ int rnnt_joint_loss_tdt_saved_bytes(int B, int T, int U, int H, int V, int dtype
 
 int rnnt_joint_loss_tdt_workspace_bytes(int B, int T, int U, int H, int V, int dtype, int tile_t,
                                         int tile_u, int tile_v, int K, int pass, size_t* out) {
-  if (!out || K < 1 || K > kTdtMaxK || (pass != 0 && pass != 1)) return RNNTJ_ERR_ARG;
+  if (!out || K < 1 || K > kTdtMaxK || pass < 0 || pass > 2) return RNNTJ_ERR_ARG;
   Plan p;
   const int rc = make_plan(B, T, U, H, V, dtype, tile_t, tile_u, tile_v, &p);
   if (rc) return rc;
   if (U + 1 > kMaxU1Short) return RNNTJ_ERR_UNSUPPORTED;
-  *out = pass == 0 ? p.ws_fwd : tdt_ws(p, K).total;
+  const size_t need = tdt_ws(p, K).total;
+  *out = pass == 0 ? p.ws_fwd : pass == 1 ? p.overlap_bytes(need) : need;
   return RNNTJ_OK;
 }
 
@@ -1035,9 +1126,12 @@ int rnnt_joint_loss_bwd_noalloc(const void* enc, const void* pred, const void* W
   void* ws = nullptr;
   const int src = scratch_for(static_cast<hipStream_t>(stream), &ws);
   if (src) return src;
-  return rnnt_joint_loss_bwd(enc, pred, W_out, b_out, dtype, labels, T_lens, U_lens, B, T, U, H,
-                             V, blank, tile_t, tile_u, tile_v, grad_costs, saved, d_enc, d_pred,
-                             d_W_out, d_b_out, ws, kScratchBytes, stream);
+  (void)T_lens;
+  (void)U_lens;
+  // one stream: creating the side stream could allocate
+  return bwd_impl(enc, pred, W_out, b_out, dtype, labels, B, T, U, H, V, blank, tile_t, tile_u,
+                  tile_v, grad_costs, saved, d_enc, d_pred, d_W_out, d_b_out, ws, kScratchBytes,
+                  stream, nullptr, nullptr, nullptr, false);
 }
 
 int rnnt_joint_loss_status(const void* saved, void* stream, int32_t* data_error) {

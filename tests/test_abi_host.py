@@ -64,10 +64,15 @@ def test_buffer_sizes():
     chunk = 16 * 64 * 64
     # 8 x 2 chunks, each with a list of 16 * 4 * 8 tiles, and 16 tile counts
     lists = 16 * (16 * 4 * 8) * 4 + 256
-    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, 8 * 1024 + chunk * (1024 + 640) * 2 + lists)
+    least = 8 * 1024 + chunk * (1024 + 640) * 2 + lists
+    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, p=2) == (0, least)
+    # pass 1: a second chunk buffer pair, for the overlapped chunk schedule
+    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64) == (0, least + chunk * (1024 + 640) * 2)
+    assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, p=3)[0] == 1
     # untiled: only the bias-gradient accumulator (the h rows are in the saved
     # state, and the logit gradients replace the stored logits in place)
     assert _ws(16, 500, 100, 640, 1024, 1) == (0, 8 * 1024)
+    assert _ws(16, 500, 100, 640, 1024, 1, p=2) == (0, 8 * 1024)
     assert _ws(16, 500, 100, 640, 1024, 1, 64, 64, 0, 0) == (0, 0)
 
 
@@ -207,7 +212,9 @@ def test_noalloc_backward_rejects_sizes_beyond_its_scratch():
                                          300, 640, 4096, 0, 64, 64, 0, None, None, None, None,
                                          None, None, None)
     assert rc == 3
-    assert _ws(8, 1500, 300, 640, 4096, 1, 64, 64, 256)[1] <= (64 << 20)
+    # the least workspace (pass 2) is what the scratch must hold: the
+    # no-allocation backward runs every kernel on one stream
+    assert _ws(8, 1500, 300, 640, 4096, 1, 64, 64, 256, p=2)[1] <= (64 << 20)
     rc = lib.rnnt_joint_loss_bwd_noalloc(None, None, None, None, 1, None, None, None, 8, 1500,
                                          300, 640, 4096, 0, 64, 64, 256, None, None, None, None,
                                          None, None, None)
