@@ -52,6 +52,7 @@ struct Plan {
   size_t elem;
   // saved layout (byte offsets)
   size_t o_h;  // untiled: h rows [B, Tpad, U1pad, H]
+  size_t o_wb;  // W_out in 32-column blocks [ceil(V / 32), H, 32] (dh's copies)
   size_t o_status, o_teff, o_ueff, o_logp, o_wt, o_lse, o_lb, o_le, o_alpha, o_beta, o_E, o_P,
       o_tiles, o_tcount, o_z;
   size_t o_zm;  // untiled bf16: the per-(row, vocabulary step) logit offsets
@@ -121,6 +122,7 @@ int make_plan(int B, int T, int U, int H, int V, int dtype, int tile_t, int tile
   q.o_ueff = o;   o = align_up(o + 4 * (size_t)B);
   q.o_logp = o;   o = align_up(o + 8 * (size_t)B);
   q.o_wt = o;     o = align_up(o + q.elem * (size_t)H * V);
+  q.o_wb = o;     o = align_up(o + q.elem * (size_t)H * ((V + 31) / 32 * 32));
   q.o_lse = o;    o = align_up(o + 4 * cells);
   q.o_lb = o;     o = align_up(o + 4 * cells);
   q.o_le = o;     o = align_up(o + 4 * cells);
@@ -474,7 +476,8 @@ int fwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   float* Eexp = at<float>(saved, p.o_E);
   float* Pexp = at<float>(saved, p.o_P);
   if ((e = timed("prep", st, [&] {
-         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Wt, Eexp, Pexp, status, st);
+         return launch_prep(enc, pred, W_out, b_out, p.bf16, p.d, Wt, at<char>(saved, p.o_wb),
+                            Eexp, Pexp, status, st);
        })) != hipSuccess)
     return RNNTJ_ERR_HIP;
 
@@ -734,7 +737,7 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   }
 
   DhArgs h = {};
-  h.W = W_out;
+  h.W = at<char>(saved, p.o_wb);  // written by the forward
   h.enc = enc;
   h.pred = pred;
   h.Teff = Teff;

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   // slot l%CPR, holding 16-byte chunk slot_of(row, l%CPR).  Rows below 128 are dz
   // rows of the tile (cells outside the lattice read the tile's first cell,
   // which is always inside; their results are never used), the rest W_out
-  // rows n0 + r - 128 (clamped to H - 1).  Each copy's source is formed from
+  // rows n0 + r - 128 (clamped to H - 1), read from the blocked copy.  Each copy's source is formed from
   // the item's (uniform) coordinates as it is issued, so no per-copy offsets
   // occupy registers between slices.  Chunks past V (last slice, V not a
   // multiple of KB) are clamped to the row's last chunk; their fragments are
@@ -300,8 +300,12 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
       du = ok ? du : 0;
       return (uint32_t)((dt * a.CU + du) * LG + col);
     }
+    // W_out rows from the blocked copy: vocabulary entry g of row n is at
+    // (g / 32, n, g % 32); a slice starts on a block (V0 and k0 are
+    // multiples of 32), so its RPC consecutive rows form one contiguous 1 KB
     const int n = min(src_it.n0 + r - kTileCells, H - 1);
-    return (uint32_t)(n * V + V0 + col);
+    const int g = V0 + col;
+    return (uint32_t)(((g >> 5) * H + n) * 32 + (g & 31));
   };
   auto set_sources = [&](ItemRef ref) {
     src_it = decode(ref);
@@ -320,8 +324,14 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
     for (int q = 0; q < C::CPW; ++q) {
       const T* base = (C::CPW * w + q < kTileCells / C::RPC) ? gbase : W;
       uint32_t off;
-      if constexpr (C::OCC == 1) off = tail ? copy_off(q, k0) : coff[q] + (uint32_t)k0;
-      else off = copy_off(q, k0);
+      if constexpr (C::OCC == 1) {
+        // a dz row moves k0 entries; a blocked W_out row k0 / 32 blocks
+        const bool dz_row = C::CPW * w + q < kTileCells / C::RPC;
+        off = tail ? copy_off(q, k0)
+                   : coff[q] + (dz_row ? (uint32_t)k0 : (uint32_t)(k0 >> 5) * (uint32_t)(H * 32));
+      } else {
+        off = copy_off(q, k0);
+      }
       dma16(base + off, st + q * 1024);
     }
   };

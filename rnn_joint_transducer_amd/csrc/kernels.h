@@ -119,11 +119,13 @@ hipError_t launch_validate(const int32_t* T_lens, const int32_t* U_lens,
 // Backward's first check of the state header (see kErrPlan).
 hipError_t launch_guard(int32_t* hdr, int32_t tag, int need_logits, hipStream_t st);
 
-// One launch: Wt[V, H] = W_out transposed; Eexp = e^{2 enc}, Pexp = e^{2 pred}
+// One launch: Wt[V, H] = W_out transposed; Wb = W_out in blocks of 32
+// vocabulary columns, [ceil(V / 32), H, 32], columns past V zero (each slice
+// row that dh copies is then contiguous); Eexp = e^{2 enc}, Pexp = e^{2 pred}
 // (float32), hdr[1] |= kFlagEpBad if some finite |enc| or |pred| exceeds 40;
 // hdr[2] = max(hdr[2], bits of max_v sum_k |W[k,v]| + |b[v]|), hdr[2] zero on entry.
 hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
-                       bool bf16, const Dims& d, void* Wt, float* Eexp, float* Pexp,
+                       bool bf16, const Dims& d, void* Wt, void* Wb, float* Eexp, float* Pexp,
                        int32_t* hdr, hipStream_t st);
 
 // Pruning bounds of the pruned transducer loss (pruned.hip): the simple
@@ -241,7 +243,7 @@ int device_cu_count();
 
 struct DhArgs {
   const void* g;      // [B, CT, CU, ldg] logit gradients of the chunk's vocabulary part
-  const void* W;      // [H, V]
+  const void* W;      // W_out in 32-column blocks [ceil(V / 32), H, 32] (launch_prep's Wb)
   const void* enc;
   const void* pred;
   const int32_t* Teff;

@@ -472,7 +472,8 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ enc,
                                                    const E* __restrict__ pred,
                                                    const E* __restrict__ W,
                                                    const E* __restrict__ bias, Dims d,
-                                                   E* __restrict__ Wt, float* __restrict__ Eexp,
+                                                   E* __restrict__ Wt, E* __restrict__ Wb,
+                                                   float* __restrict__ Eexp,
                                                    float* __restrict__ Pexp,
                                                    int32_t* __restrict__ hdr, int n_tr, int n_cb) {
   __shared__ float sh[32 * 33];
@@ -486,7 +487,11 @@ __global__ __launch_bounds__(256) void prep_kernel(const E* __restrict__ enc,
     const int tx = tid & 31, ty = tid >> 5;  // 32 x 8
     for (int i = ty; i < 32; i += 8) {
       const int h = h0 + i, v = v0 + tx;
-      if (h < H && v < V) tile[i * 33 + tx] = W[(size_t)h * V + v];
+      if (h < H) {
+        const E x = v < V ? W[(size_t)h * V + v] : E(0);
+        if (v < V) tile[i * 33 + tx] = x;
+        Wb[((size_t)(v0 >> 5) * H + h) * 32 + tx] = x;  // block v0 / 32, row h, column tx
+      }
     }
     __syncthreads();
     for (int i = ty; i < 32; i += 8) {
@@ -683,7 +688,7 @@ hipError_t launch_guard(int32_t* hdr, int32_t tag, int need_logits, hipStream_t 
 }
 
 hipError_t launch_prep(const void* enc, const void* pred, const void* W, const void* bias,
-                       bool bf16, const Dims& d, void* Wt, float* Eexp, float* Pexp,
+                       bool bf16, const Dims& d, void* Wt, void* Wb, float* Eexp, float* Pexp,
                        int32_t* hdr, hipStream_t st) {
   const size_t n = (size_t)d.B * (d.T + d.U1) * d.H;
   size_t n_ep = (n + 255) / 256;
@@ -693,13 +698,13 @@ hipError_t launch_prep(const void* enc, const void* pred, const void* W, const v
   if (bf16)
     hipLaunchKernelGGL(prep_kernel<uint16_t>, grid, block, 0, st, static_cast<const uint16_t*>(enc),
                        static_cast<const uint16_t*>(pred), static_cast<const uint16_t*>(W),
-                       static_cast<const uint16_t*>(bias), d, static_cast<uint16_t*>(Wt), Eexp, Pexp,
-                       hdr, n_tr, n_cb);
+                       static_cast<const uint16_t*>(bias), d, static_cast<uint16_t*>(Wt),
+                       static_cast<uint16_t*>(Wb), Eexp, Pexp, hdr, n_tr, n_cb);
   else
     hipLaunchKernelGGL(prep_kernel<float>, grid, block, 0, st, static_cast<const float*>(enc),
                        static_cast<const float*>(pred), static_cast<const float*>(W),
-                       static_cast<const float*>(bias), d, static_cast<float*>(Wt), Eexp, Pexp, hdr,
-                       n_tr, n_cb);
+                       static_cast<const float*>(bias), d, static_cast<float*>(Wt),
+                       static_cast<float*>(Wb), Eexp, Pexp, hdr, n_tr, n_cb);
   return hipGetLastError();
 }
 

@@ -50,13 +50,14 @@ def _ws(B, T, U, H, V, dt, tt=0, tu=0, tv=0, p=1):
 
 def test_buffer_sizes():
     # medium workload, bf16: per cell lse/LB/LE (12 B) + alpha/beta (16 B) over
-    # the skewed [B, T+U, U+1] layout, W^T, and e^{2 enc}, e^{2 pred} (float32);
+    # the skewed [B, T+U, U+1] layout, W^T and W_out in 32-column blocks, and
+    # e^{2 enc}, e^{2 pred} (float32);
     # untiled adds the logits and the h rows of the padded lattice.
     rc, tiled = _saved(16, 500, 100, 640, 1024, 1, 64, 64, 0)
     assert rc == 0
     cells = 16 * 600 * 101
     tiles = 16 * 32 * 13  # 16 x 8 tiles of the padded lattice, one int32 each
-    fixed = cells * 28 + 640 * 1024 * 2 + 4 * 16 * (500 + 101) * 640 + 4 * tiles
+    fixed = cells * 28 + 2 * 640 * 1024 * 2 + 4 * 16 * (500 + 101) * 640 + 4 * tiles
     assert fixed <= tiled <= fixed + 64 * 1024
     rc, untiled = _saved(16, 500, 100, 640, 1024, 1)
     assert rc == 0
