@@ -39,20 +39,21 @@ PEAK_F64 = 78.6  # TFLOP/s, float64 MFMA (dense) = float64 vector: 256 CUs x 4 S
 MFMA_KERNELS = ("joint_fwd", "joint_fwd_store", "joint_grad", "dh", "dw")
 PROJ_KERNELS = ("proj_fwd", "proj_dx", "proj_dw")
 # Tiled defaults: medium takes the lowest-memory tiling within 95 % of the
-# best tiled throughput of a full tile sweep (`--sweep`); medium_lv keeps its
+# best tiled throughput of a full tile sweep (`--sweep`, overlapped chunk
+# schedule: 64 frames x all label positions); medium_lv keeps its
 # configured vocabulary parts of 256 columns and takes the same choice among
 # the tilings with those parts (one chunk of all frames and label positions);
 # long keeps its configured 64 x 64 chunks (over the whole vocabulary: the
 # long configuration fixes no tile_v).
-DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (128, 0, 0),
+DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (64, 0, 0),
                  "medium_lv": (0, 128, 256), "long": (64, 64, 0)}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long",
                     choices=["tiny", "short", "medium", "medium_lv", "long"])
     ap.add_argument("--criterion", default="sum", choices=["sum", "max"],
