@@ -82,3 +82,43 @@ def test_schedules_agree_bitwise_in_deterministic_mode(name, tiles):
     for k in ("costs", "dEnc", "dPred", "dW", "db"):
         assert np.array_equal(a[k], b[k]), k
         assert np.array_equal(a[k], c[k]), k
+
+
+def test_two_threads_on_two_streams():
+    """Two host threads run tiled forward + backward calls at once, each on a
+    stream of its own; the library's side stream and its events are shared
+    per device.  Each thread's gradients must match those of the same call run
+    alone, to the parity bar of its dtype."""
+    import threading
+
+    import torch
+    inps = [make_config("short"),
+            make_inputs(4, 60, 17, 128, 200, dtype="bf16", sigma=0.3, seed=29,
+                        t_range=(20, 60), u_range=(5, 17))]
+    tiles = [(16, 16, 256), (16, 8, 0)]
+    alone = [_run(inp, t, False, [1.0] * inp.B) for inp, t in zip(inps, tiles)]
+    results = [None, None]
+    errors = []
+
+    def worker(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                outs = [_run(inps[i], tiles[i], False, [1.0] * inps[i].B) for _ in range(3)]
+            s.synchronize()
+            results[i] = outs
+        except Exception as e:  # reported below, in the test's own thread
+            errors.append(repr(e))
+
+    print("[schedule two threads]", flush=True)
+    th = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    assert not errors, errors
+    for i, inp in enumerate(inps):
+        for g in results[i]:
+            check_costs(g["costs"], alone[i]["costs"], inp.dtype)
+            for k in ("dEnc", "dPred", "dW", "db"):
+                check_grad(k, g[k], alone[i][k], inp.dtype)
