@@ -275,21 +275,17 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   // slot l%CPR, holding 16-byte chunk slot_of(row, l%CPR).  Rows below 128 are dz
   // rows of the tile (cells outside the lattice read the tile's first cell,
   // which is always inside; their results are never used), the rest W_out
-  // rows n0 + r - 128 (clamped to H - 1), read from the blocked copy.  Each copy's source is formed from
-  // the item's (uniform) coordinates as it is issued, so no per-copy offsets
-  // occupy registers between slices.  Chunks past V (last slice, V not a
-  // multiple of KB) are clamped to the row's last chunk; their fragments are
-  // zeroed before the MFMAs.  Element offsets fit 32 bits (a tile spans 16
-  // frames of one chunk; W_out is at most 768 rows).
-  // (Two workgroups per CU leave no registers for per-copy offsets: there
-  // they are formed at issue time from the item's uniform coordinates; with
-  // one per CU they are set once per item.)
+  // rows n0 + r - 128 (clamped to H - 1), read from the blocked copy.  Chunks
+  // past V (last slice, V not a multiple of KB) are clamped to the row's last
+  // chunk; their fragments are zeroed before the MFMAs.  Element offsets fit
+  // 32 bits (a tile spans 16 frames of one chunk; W_out is at most 768 rows).
   const int lr = lane / C::CPR, lcc = lane % C::CPR;
   const T* gbase = G;
   Item src_it = {};
   int src_k0 = 0;  // first vocabulary entry of the issuing item's part
-  uint32_t coff[C::OCC == 1 ? C::CPW : 1];
-  auto copy_off = [&](int q, int k0) -> uint32_t {  // element offset of copy q
+  // General form (vocabulary tails, or tiles whose byte span exceeds 32
+  // bits): element offset of copy q from the copy's base, formed at issue.
+  auto copy_off = [&](int q, int k0) -> uint32_t {
     const int ins = C::CPW * w + q;  // uniform
     const int r = C::RPC * ins + lr;
     const int col = min(k0 + slot_of<C::RB>(r, lcc) * C::CE, VW - C::CE);
@@ -307,32 +303,52 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
     const int g = V0 + col;
     return (uint32_t)(((g >> 5) * H + n) * 32 + (g & 31));
   };
+  // Usual form: each copy is a wave-uniform base (dz rows: the slice's first
+  // entry of the tile's first row; W_out rows: the slice's block) plus a
+  // per-lane byte offset that stays fixed over the item's slices, set once
+  // per item, so a slice's copies cost no vector arithmetic.  A tile's dz
+  // rows span fewer than 16 frame rows of the chunk, which bounds the offsets.
+  const bool soff = (uint64_t)kTileT * (uint64_t)a.CU * (uint64_t)LG * sizeof(T) < (1ull << 32);
+  uint32_t coff[C::CPW];
+  auto lane_off = [&](int q) -> uint32_t {  // bytes from the copy's base
+    const int ins = C::CPW * w + q;  // uniform
+    const int r = C::RPC * ins + lr;
+    const uint32_t c = (uint32_t)(slot_of<C::RB>(r, lcc) * C::CE);
+    if (ins < kTileCells / C::RPC) {
+      int dt = r >> 3, du = r & 7;
+      const bool ok = src_it.t0 + dt < src_it.Tl && src_it.u0 + du <= src_it.Ul;
+      dt = ok ? dt : 0;
+      du = ok ? du : 0;
+      return ((uint32_t)(dt * a.CU + du) * (uint32_t)LG + c) * (uint32_t)sizeof(T);
+    }
+    const int n = min(src_it.n0 + r - kTileCells, H - 1);
+    return ((uint32_t)n * 32u + c) * (uint32_t)sizeof(T);
+  };
   auto set_sources = [&](ItemRef ref) {
     src_it = decode(ref);
     src_k0 = ref.kp * nks * C::KB;
     gbase = G + (((size_t)src_it.b * a.CT + (src_it.t0 - a.ct0)) * a.CU + (src_it.u0 - a.cu0)) * LG;
-    if constexpr (C::OCC == 1) {
+    if (soff) {
 #pragma unroll
-      for (int q = 0; q < C::CPW; ++q) coff[q] = copy_off(q, 0);
+      for (int q = 0; q < C::CPW; ++q) coff[q] = lane_off(q);
     }
   };
   auto issue = [&](int s, int buf) {
     const int k0 = src_k0 + s * C::KB;
     const uint32_t st = lbase + buf * C::SLICE + C::CPW * w * 1024;
     const bool tail = k0 + C::KB > VW;
+    if (soff && !tail) {
+      const T* gb = gbase + k0;
+      const T* wb = W + (size_t)((V0 + k0) >> 5) * H * 32;
 #pragma unroll
-    for (int q = 0; q < C::CPW; ++q) {
-      const T* base = (C::CPW * w + q < kTileCells / C::RPC) ? gbase : W;
-      uint32_t off;
-      if constexpr (C::OCC == 1) {
-        // a dz row moves k0 entries; a blocked W_out row k0 / 32 blocks
-        const bool dz_row = C::CPW * w + q < kTileCells / C::RPC;
-        off = tail ? copy_off(q, k0)
-                   : coff[q] + (dz_row ? (uint32_t)k0 : (uint32_t)(k0 >> 5) * (uint32_t)(H * 32));
-      } else {
-        off = copy_off(q, k0);
+      for (int q = 0; q < C::CPW; ++q)
+        dma16s((C::CPW * w + q < kTileCells / C::RPC) ? gb : wb, coff[q], st + q * 1024);
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::CPW; ++q) {
+        const T* base = (C::CPW * w + q < kTileCells / C::RPC) ? gbase : W;
+        dma16(base + copy_off(q, k0), st + q * 1024);
       }
-      dma16(base + off, st + q * 1024);
     }
   };
   constexpr int kCopies = C::CPW;  // per wave per slice
