@@ -198,7 +198,10 @@ __device__ __forceinline__ int slot_of(int r, int c) {
 // else is in flight.
 __device__ __forceinline__ void touch(float x) { asm volatile("" ::"v"(x)); }
 
-template <typename T>
+// VTAIL: the vocabulary part is not a multiple of the slice width, so the
+// fragments past its end are zeroed (a separate instantiation: otherwise the
+// test would cost a select per fragment register at every k-step).
+template <typename T, bool VTAIL>
 __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
   using C = DhCfg<T>;
   __shared__ __align__(16) char lds[C::NST * C::SLICE];
@@ -363,7 +366,7 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
 
   Frag8<T> fa[2][2], fb[2][4];
   // fragments of k-step kk of stream slice g (buffer g % NST)
-  const bool has_vtail = VW % C::KB != 0;
+  const bool has_vtail = VTAIL && VW % C::KB != 0;
   auto rd = [&](int g, int kk, int fbuf) {
     const char* sl = lds + (g % C::NST) * C::SLICE;
     const int s = g % nks;  // slice of the item (ks == 1 whenever V has a tail)
@@ -379,7 +382,8 @@ __global__ __launch_bounds__(256, DhCfg<T>::OCC) void dh_kernel(DhArgs a) {
         fa[fbuf][i].lo = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh) << 4));
         fa[fbuf][i].hi = *reinterpret_cast<const f32x4*>(row + (slot_of<C::RB>(r, 4 * kk + 2 * kh + 1) << 4));
       }
-      if (vtail && kbase >= VW) zero_frag(fa[fbuf][i]);  // vocabulary tail
+      if constexpr (VTAIL)
+        if (vtail && kbase >= VW) zero_frag(fa[fbuf][i]);  // vocabulary tail
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -1049,8 +1053,14 @@ hipError_t launch_dh(const DhArgs& a, bool bf16, int max_tiles, hipStream_t st) 
   if (items <= 0) return hipSuccess;
   const long long g8 = (items + 7) / 8 * 8;
   dim3 grid((unsigned)(g8 < gmax ? g8 : gmax)), block(256);
-  if (bf16) hipLaunchKernelGGL(dh_kernel<uint16_t>, grid, block, 0, st, b);
-  else hipLaunchKernelGGL(dh_kernel<float>, grid, block, 0, st, b);
+  const bool vtail = a.vw % kb != 0;
+  if (bf16) {
+    if (vtail) hipLaunchKernelGGL((dh_kernel<uint16_t, true>), grid, block, 0, st, b);
+    else hipLaunchKernelGGL((dh_kernel<uint16_t, false>), grid, block, 0, st, b);
+  } else {
+    if (vtail) hipLaunchKernelGGL((dh_kernel<float, true>), grid, block, 0, st, b);
+    else hipLaunchKernelGGL((dh_kernel<float, false>), grid, block, 0, st, b);
+  }
   return hipGetLastError();
 }
 
