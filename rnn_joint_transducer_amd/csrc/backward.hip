@@ -137,8 +137,7 @@ __global__ __launch_bounds__(256) void grad_inplace_kernel(JointArgs a, T* __res
         u32x4 y;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          y[q] = (uint32_t)ElemTraits<uint16_t>::from_f32(g[2 * q]) |
-                 ((uint32_t)ElemTraits<uint16_t>::from_f32(g[2 * q + 1]) << 16);
+          y[q] = pack_bf16x2(g[2 * q], g[2 * q + 1]);
         *reinterpret_cast<u32x4*>(ptr[k]) = y;
       } else {
 #pragma unroll
@@ -761,10 +760,8 @@ __global__ __launch_bounds__(256, DwCfg<T>::OCC) void dw_kernel(DwArgs a) {
       const char* p = sl + off + 16 * kk * rowb;
       const i16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
       const i16x4 y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 4 * rowb));
-      f.v[0] = (uint32_t)(uint16_t)x[0] | ((uint32_t)(uint16_t)x[1] << 16);
-      f.v[1] = (uint32_t)(uint16_t)x[2] | ((uint32_t)(uint16_t)x[3] << 16);
-      f.v[2] = (uint32_t)(uint16_t)y[0] | ((uint32_t)(uint16_t)y[1] << 16);
-      f.v[3] = (uint32_t)(uint16_t)y[2] | ((uint32_t)(uint16_t)y[3] << 16);
+      const u32x2_t x2 = __builtin_bit_cast(u32x2_t, x), y2 = __builtin_bit_cast(u32x2_t, y);
+      f.v = u32x4{x2[0], x2[1], y2[0], y2[1]};
     } else {
       const int col = col0 + lc;
       float x[8];

@@ -76,6 +76,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 __device__ __forceinline__ uint16_t f32_to_bf16_hw(float f) {
   return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
+// Two floats to two bf16 (round to nearest even) in one 32-bit word, lo in
+// the low half: one packed conversion instead of two conversions and a merge.
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<float> {
@@ -130,7 +137,7 @@ __device__ __forceinline__ void zero_frag(Frag8<float>& f) {
 __device__ __forceinline__ void pack_frag(Frag8<uint16_t>& f, const float* x) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    f.v[i] = (uint32_t)f32_to_bf16_hw(x[2 * i]) | ((uint32_t)f32_to_bf16_hw(x[2 * i + 1]) << 16);
+    f.v[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
 }
 __device__ __forceinline__ void pack_frag(Frag8<float>& f, const float* x) {
   f.lo = f32x4{x[0], x[1], x[2], x[3]};
@@ -169,6 +176,9 @@ __device__ __forceinline__ void mma_step(f32x16& acc, const Frag8<float>& a,
 // every lane of the wave active.  fp32 uses eight scalar reads.
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+// the four 16-bit values of a transposing read, as the two 32-bit words they
+// occupy (element 2i in the low half of word i)
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 __device__ __forceinline__ Frag8<uint16_t> load_frag_T(const uint16_t* tile, int ld, int row0,
                                                        int col0) {
   const int l = threadIdx.x & 63;
@@ -180,10 +190,8 @@ __device__ __forceinline__ Frag8<uint16_t> load_frag_T(const uint16_t* tile, int
   const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p1));
   Frag8<uint16_t> f;
-  f.v[0] = (uint32_t)(uint16_t)a[0] | ((uint32_t)(uint16_t)a[1] << 16);
-  f.v[1] = (uint32_t)(uint16_t)a[2] | ((uint32_t)(uint16_t)a[3] << 16);
-  f.v[2] = (uint32_t)(uint16_t)b[0] | ((uint32_t)(uint16_t)b[1] << 16);
-  f.v[3] = (uint32_t)(uint16_t)b[2] | ((uint32_t)(uint16_t)b[3] << 16);
+  const u32x2_t a2 = __builtin_bit_cast(u32x2_t, a), b2 = __builtin_bit_cast(u32x2_t, b);
+  f.v = u32x4{a2[0], a2[1], b2[0], b2[1]};
   return f;
 }
 __device__ __forceinline__ Frag8<float> load_frag_T(const float* tile, int ld, int row0,

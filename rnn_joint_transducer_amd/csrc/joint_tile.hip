@@ -871,10 +871,8 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             uint2 pk;
-            pk.x = (uint32_t)f32_to_bf16_hw(acc[blk][4 * i]) |
-                   ((uint32_t)f32_to_bf16_hw(acc[blk][4 * i + 1]) << 16);
-            pk.y = (uint32_t)f32_to_bf16_hw(acc[blk][4 * i + 2]) |
-                   ((uint32_t)f32_to_bf16_hw(acc[blk][4 * i + 3]) << 16);
+            pk.x = pack_bf16x2(acc[blk][4 * i], acc[blk][4 * i + 1]);
+            pk.y = pack_bf16x2(acc[blk][4 * i + 2], acc[blk][4 * i + 3]);
             *reinterpret_cast<uint2*>(&ts[ts_idx(col, 8 * i + 4 * kh)]) = pk;
           }
         }
@@ -919,11 +917,8 @@ __global__ __launch_bounds__(256, NBLK == 2 ? 2 : 1) void joint_tile_kernel(Join
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0, cb)]));
           const i16x4 hi =
               __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&ts[ts_idx(k0 + 4, cb)]));
-          u32x4 pk;
-          pk[0] = (uint32_t)(uint16_t)lo[0] | ((uint32_t)(uint16_t)lo[1] << 16);
-          pk[1] = (uint32_t)(uint16_t)lo[2] | ((uint32_t)(uint16_t)lo[3] << 16);
-          pk[2] = (uint32_t)(uint16_t)hi[0] | ((uint32_t)(uint16_t)hi[1] << 16);
-          pk[3] = (uint32_t)(uint16_t)hi[2] | ((uint32_t)(uint16_t)hi[3] << 16);
+          const u32x2_t lo2 = __builtin_bit_cast(u32x2_t, lo), hi2 = __builtin_bit_cast(u32x2_t, hi);
+          u32x4 pk = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
           const int colo = 16 * f + 8 * kh;
           if (!row_ok) pk = u32x4{0u, 0u, 0u, 0u};
           if (row_st && (EXACT || vt + colo < V)) *reinterpret_cast<u32x4*>(orow + colo) = pk;
