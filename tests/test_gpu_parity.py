@@ -510,11 +510,16 @@ def test_max_zero_weights_closed_form_medium():
 
 # ------------------------------------------------------------------ maximum sizes
 
-@pytest.mark.parametrize("case", ["U_max", "V_max", "H_max_bf16", "B_max", "T_max"])
+@pytest.mark.parametrize("case", ["U_max", "V_max", "H_max_bf16", "B_max", "T_max",
+                                  "wide_rows"])
 def test_maximum_sizes(case):
     """Each size limit the library accepts, with the other sizes small enough
     for the oracle: U + 1 = 1024 (both criteria), V = 262144, H = 768 in bf16,
-    B = 8191, T = 65520.  Every output is compared.  The largest-B and
+    B = 8191, T = 65520.  Every output is compared.  "wide_rows" pairs
+    U + 1 = 1024 with V = 131072 (fp32): the logit rows of one 16-frame tile
+    then span 8 GiB, beyond the 32-bit per-lane offsets of dh's usual copy
+    form, so dh takes its general address form (untiled, and tiled with every
+    label position in one chunk).  The largest-B and
     longest-T cases weight their costs by 1e-3 and 1e-4: unweighted, d_b_out
     sums to ~1.1e4 over 8191 utterances (half an fp32 ulp there is 4.9e-4)
     and d_W_out to ~40 over 65520 frames, beyond what an fp32 value can hold
@@ -532,6 +537,9 @@ def test_maximum_sizes(case):
         inp = make_inputs(2, 5, 2, 32, 262144, sigma=0.2, seed=102)
     elif case == "H_max_bf16":
         inp = make_inputs(2, 20, 6, 768, 96, dtype="bf16", sigma=0.05, seed=103)
+    elif case == "wide_rows":
+        inp = make_inputs(1, 2, 1023, 16, 131072, sigma=0.2, seed=106)
+        runs = [((0, 0, 0), "sum"), ((16, 0, 0), "sum")]
     elif case == "B_max":
         inp = make_inputs(8191, 2, 1, 16, 16, sigma=0.3, seed=104, t_range=(1, 2), u_range=(0, 1))
         gcs = [1e-3] * inp.B
