@@ -376,7 +376,8 @@ def main():
                           dtype=torch.uint8, device=dev)
         simple = torch.empty(B, dtype=torch.float32, device=dev)
 
-    def step():
+    def step(wsx=None):
+        wsx = ws if wsx is None else wsx
         if pj is not None:
             tensors["enc"] = rj.rnnt_joint_proj_fwd(ptens["enc_in"], ptens["W_enc"], ptens["b_enc"])
             tensors["pred"] = rj.rnnt_joint_proj_fwd(ptens["pred_in"], ptens["W_pred"],
@@ -385,7 +386,7 @@ def main():
             rj.rnnt_joint_loss_tdt_fwd(**tensors, W_dur=Wd, b_dur=bd, durations=head.durations,
                                        tile_t=tt, tile_u=tu, tile_v=tv, costs=costs, saved=saved)
             rj.rnnt_joint_loss_tdt_bwd(**tensors, W_dur=Wd, b_dur=bd, durations=head.durations,
-                                       saved=saved, tile_t=tt, tile_u=tu, tile_v=tv, workspace=ws)
+                                       saved=saved, tile_t=tt, tile_u=tu, tile_v=tv, workspace=wsx)
             return
         if args.pruned:
             rj.rnnt_joint_loss_pruned_fwd(**tensors, S=args.pruned, tile_t=tt, tile_u=tu,
@@ -395,11 +396,12 @@ def main():
             rj.rnnt_joint_loss_fwd(**tensors, tile_t=tt, tile_u=tu, tile_v=tv, costs=costs,
                                    saved=saved, criterion=args.criterion)
         rj.rnnt_joint_loss_bwd(**tensors, saved=saved, tile_t=tt, tile_u=tu, tile_v=tv,
-                               workspace=ws, out=grads)
+                               workspace=wsx, out=grads)
         if pj is not None:
             rj.rnnt_joint_proj_bwd(ptens["enc_in"], ptens["W_enc"], grads[0])
             rj.rnnt_joint_proj_bwd(ptens["pred_in"], ptens["W_pred"], grads[1])
 
+    mode_tiled = not (tt == 0 and tu == 0)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -434,6 +436,29 @@ def main():
     torch.cuda.synchronize()
     rep = _lib.timing_report()
     _lib.timing(False)
+    # In the overlapped chunk schedule the launches above share the compute
+    # units with the side stream's dW, so their durations include shared
+    # time.  Two more steps with the least workspace (every kernel in order
+    # on one stream) give each kernel's duration alone.
+    rep_alone = None
+    if mode_tiled and not args.min_workspace:
+        if head is not None:
+            import ctypes
+            sz = ctypes.c_size_t(0)
+            _lib.check(_lib.load().rnnt_joint_loss_tdt_workspace_bytes(
+                B, T, U, H, V, dc, tt, tu, tv, len(head.durations), 2, ctypes.byref(sz)), "tdt_ws")
+            least = sz.value
+        else:
+            least = rj.rnnt_joint_loss_workspace_bytes(B, T, U, H, V, dc, tt, tu, tv, 2)
+        ws_least = ws[:least]
+        step(ws_least)
+        torch.cuda.synchronize()
+        _lib.timing(True)
+        for _ in range(2):
+            step(ws_least)
+        torch.cuda.synchronize()
+        rep_alone = _lib.timing_report()
+        _lib.timing(False)
     valid = int(np.sum(inp.T_lens.astype(np.int64) * (inp.U_lens.astype(np.int64) + 1)))
     band_cells = None
     if args.pruned:
@@ -500,6 +525,15 @@ def main():
 
     mode = "untiled" if (tt == 0 and tu == 0) else "tiled"
     roof["traffic"] = measured_traffic(args.workload, dom, mode, args.criterion)
+    alone = None
+    if rep_alone is not None:
+        alone = {"schedule": "least workspace: every kernel in order on one stream, 2 steps"}
+        for name, (n, tot) in rep_alone.items():
+            if name in MFMA_KERNELS:
+                per_launch = 2.0 * H * V * work_cells / (n / 2.0)
+                tf = per_launch / (tot / n / 1e3) / 1e12
+                alone[name] = {"ms_per_launch": round(tot / n, 6), "tflops": round(tf, 2),
+                               "frac": round(tf / PEAK_TFLOPS[dt], 4)}
     # the whole step against the matrix peak: the joint projection's
     # algorithmic flops (forward 2HV, dh 2HV, dW 2HV per cell) and those the
     # kernels execute (the tiled backward recomputes the forward's 2HV), over
@@ -543,6 +577,7 @@ def main():
                    "valid_cells": valid, "valid_cells_per_s": valid / (ms / 1e3),
                    "peak_gb": round(peak_gb, 3), "peak_gb_above_inputs": round(extra_gb, 3)},
         "roofline": roof,
+        "kernels_alone": alone,
         "step_mfma": step_mfma,
         "lattice": lat,
         "kernels": {k: {kk: round(vv, 6) for kk, vv in v.items()} for k, v in kernels.items()},
