@@ -42,11 +42,11 @@ PROJ_KERNELS = ("proj_fwd", "proj_dx", "proj_dw")
 # best tiled throughput of a full tile sweep (`--sweep`, overlapped chunk
 # schedule: 64 frames x all label positions); medium_lv keeps its
 # configured vocabulary parts of 256 columns and takes the same choice among
-# the tilings with those parts (one chunk of all frames and label positions);
+# the tilings with those parts (chunks of all frames x 64 label positions);
 # long keeps its configured 64 x 64 chunks (over the whole vocabulary: the
 # long configuration fixes no tile_v).
 DEFAULT_TILES = {"tiny": (0, 0, 0), "short": (0, 0, 0), "medium": (64, 0, 0),
-                 "medium_lv": (0, 128, 256), "long": (64, 64, 0)}
+                 "medium_lv": (0, 64, 256), "long": (64, 64, 0)}
 
 
 def parse():

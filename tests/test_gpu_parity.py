@@ -342,10 +342,10 @@ def test_medium(tiles):
     _sub_batch_weights(inp, tiles, [3, 11])
 
 
-@pytest.mark.parametrize("tiles", [(0, 128, 256), (64, 64, 256), (32, 0, 256)])
+@pytest.mark.parametrize("tiles", [(0, 64, 256), (0, 128, 256), (64, 64, 256), (32, 0, 256)])
 def test_medium_large_vocab(tiles):
-    """(0, 128, 256) -- one chunk of the whole lattice, vocabulary parts of 256
-    columns -- is the tiling the benchmark times."""
+    """(0, 64, 256) -- chunks of all frames x 64 label positions, vocabulary
+    parts of 256 columns -- is the tiling the benchmark times."""
     inp = make_config("medium_lv")
     print(f"[medium_lv tiles={tiles}]", flush=True)
     _sampled(inp, tiles, cost_utts=list(range(inp.B)), grad_utts=[9], key="medium_lv")
