@@ -862,7 +862,8 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
   std::unique_lock<std::mutex> side_lk;
   void* gbuf[2] = {gchunk, gchunk};
   void* hbuf[2] = {hchunk, hchunk};
-  if (side_ok && workspace_bytes >= p.overlap_bytes(ws_need) && p.n_chunks * ((V + p.Vp - 1) / p.Vp) > 1 &&
+  const int n_passes = p.n_chunks * ((V + p.Vp - 1) / p.Vp);
+  if (side_ok && workspace_bytes >= p.overlap_bytes(ws_need) && n_passes > 1 &&
       (ss = side_stream()) != nullptr) {
     side_lk = std::unique_lock<std::mutex>(ss->mu);
     char* second = at<char>(workspace, align_up(ws_need));
@@ -912,7 +913,8 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
         w.v0 = v0; w.vw = vw; w.ldg = p.Vp;
         // buffer pair pass & 1 (and the h rows of chunk pair chunk & 1, last
         // read by a dW at or before pass - 2) are free once the dW of pass - 2 is done
-        if (ss && pass >= 2 && (e = hipStreamWaitEvent(st, ss->dw_done[pass & 1], 0)) != hipSuccess)
+        if (ss && pass >= 2 &&
+            (e = hipStreamWaitEvent(st, ss->dw_done[pass & 1], 0)) != hipSuccess)
           return fail("stream wait", e);
         if ((e = timed("joint_grad", st, [&] {
                return launch_joint_tile(a, kGrad, p.bf16, p.cap_chunk * vsplit, st);
@@ -937,7 +939,8 @@ int bwd_impl(const void* enc, const void* pred, const void* W_out, const void* b
     }
   }
   // join: the caller's stream waits for the last dW (the side stream runs in order)
-  if (ss && joined_to >= 0 && (e = hipStreamWaitEvent(st, ss->dw_done[joined_to & 1], 0)) != hipSuccess)
+  if (ss && joined_to >= 0 &&
+      (e = hipStreamWaitEvent(st, ss->dw_done[joined_to & 1], 0)) != hipSuccess)
     return note_error("stream join", e), RNNTJ_ERR_HIP;
   if (finalize(nullptr) != hipSuccess) return RNNTJ_ERR_HIP;
   return debug_data_check(hdr, st);
